@@ -1,0 +1,143 @@
+"""fp64 CPU oracle of the Gaussian Mixture Attention forward mixer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(the HIP library and its Python binding) never imports, links or calls it, and
+this package imports nothing from the product path.
+
+The arithmetic lives in ``gma_oracle.c`` (plain C, fp64, OpenMP over
+independent rows/columns, sequential sums over the sequence); this module only
+compiles it with gcc and marshals numpy arrays.  Formulas follow the page
+"Attention par Mélange Gaussien (GMA)", section "Méthodologie", sub-section
+"Mécanisme Central" (items 1-3); see the C file for the per-function mapping.
+
+Parity pins for every function are in ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gma_oracle.c")
+_LIB = os.path.join(_HERE, "libgma_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+__all__ = ["build", "params", "responsibilities", "forward", "set_threads", "max_threads"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2 -fopenmp, no fast-math)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            dp = ctypes.POINTER(ctypes.c_double)
+            i64, i32 = ctypes.c_int64, ctypes.c_int32
+            lib.gma_oracle_params.argtypes = [i64, i32, i32, dp, dp, dp, dp]
+            lib.gma_oracle_params.restype = None
+            lib.gma_oracle_responsibilities.argtypes = [i64, i64, i64, i32, i32, dp, dp, dp, dp, dp]
+            lib.gma_oracle_responsibilities.restype = ctypes.c_int
+            lib.gma_oracle_forward.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32,
+                                               ctypes.c_double, dp, dp, dp, dp, dp, dp, dp]
+            lib.gma_oracle_forward.restype = ctypes.c_int
+            lib.gma_oracle_set_threads.argtypes = [ctypes.c_int]
+            lib.gma_oracle_set_threads.restype = None
+            lib.gma_oracle_max_threads.argtypes = []
+            lib.gma_oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    """Exact upcast to a C-contiguous fp64 array (bf16 and fp32 values are exact in fp64)."""
+    if hasattr(a, "detach"):  # torch tensor: go through fp32, exact for bf16/fp32
+        import torch
+        a = a.detach().to("cpu")
+        if a.dtype != torch.float64:
+            a = a.to(torch.float64)
+        a = a.numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def set_threads(n: int) -> None:
+    _load().gma_oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().gma_oracle_max_threads())
+
+
+def params(raw_var, prior_logits):
+    """(sigma^2 [H, K, d_r], log pi [H, K]) from the raw learned parameters."""
+    rv, pl = _f64(raw_var), _f64(prior_logits)
+    H, K, dr = rv.shape
+    assert pl.shape == (H, K)
+    var = np.empty_like(rv)
+    logp = np.empty_like(pl)
+    _load().gma_oracle_params(H, K, dr, _ptr(rv), _ptr(pl), _ptr(var), _ptr(logp))
+    return var, logp
+
+
+def responsibilities(x, mu, raw_var, prior_logits) -> np.ndarray:
+    """Gamma [B, H, N, K] for x [B, H, N, d_r] (x may also be [H, N, d_r] or [N, d_r] with H = 1)."""
+    x, mu, rv, pl = _f64(x), _f64(mu), _f64(raw_var), _f64(prior_logits)
+    shape = x.shape
+    if x.ndim == 2:
+        x = x[None, None]
+    elif x.ndim == 3:
+        x = x[None]
+    B, H, N, dr = x.shape
+    K = mu.shape[1]
+    assert mu.shape == (H, K, dr) and rv.shape == (H, K, dr) and pl.shape == (H, K)
+    g = np.empty((B, H, N, K), dtype=np.float64)
+    rc = _load().gma_oracle_responsibilities(B, H, N, dr, K, _ptr(x), _ptr(mu), _ptr(rv), _ptr(pl), _ptr(g))
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return g.reshape(shape[:-1] + (K,))
+
+
+def forward(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, causal: bool = False,
+            threads: Optional[int] = None) -> np.ndarray:
+    """O [B, H, N, d_v] in fp64.  qx, kx [B, H, N, d_r]; v [B, H, N, d_v]."""
+    qx, kx, v = _f64(qx), _f64(kx), _f64(v)
+    mu, rv, pl = _f64(mu), _f64(raw_var), _f64(prior_logits)
+    squeeze = qx.ndim == 2
+    if squeeze:
+        qx, kx, v = qx[None, None], kx[None, None], v[None, None]
+    B, H, N, dr = qx.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    assert kx.shape == qx.shape and v.shape == (B, H, N, dv)
+    assert mu.shape == (H, K, dr) and rv.shape == (H, K, dr) and pl.shape == (H, K)
+    o = np.empty((B, H, N, dv), dtype=np.float64)
+    lib = _load()
+    if threads is not None:
+        lib.gma_oracle_set_threads(int(threads))
+    rc = lib.gma_oracle_forward(1 if causal else 0, B, H, N, dr, K, dv, float(eps), _ptr(qx), _ptr(kx),
+                                _ptr(v), _ptr(mu), _ptr(rv), _ptr(pl), _ptr(o))
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return o[0, 0] if squeeze else o

@@ -1,0 +1,245 @@
+/*
+ * gma_oracle.c -- plain fp64 CPU oracle of the Gaussian Mixture Attention
+ * (GMA) forward mixer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header or constant with the HIP
+ * library.
+ *
+ * Source of every formula: the page "Attention par Melange Gaussien (GMA)"
+ * (gist.science, paper 2606.18283), section "Methodologie: Attention par
+ * Melange Gaussien (GMA)", sub-section "Mecanisme Central":
+ *   item 1 "Routage Latent Probabiliste"  -> gma_oracle_responsibilities
+ *   item 2 "Routage de Memoire Latente"   -> gma_oracle_forward (write phase,
+ *                                            read phase equation)
+ *   item 3 "Variantes et Entrainement"    -> gma_oracle_params (softplus
+ *                                            variances, softmax priors) and
+ *                                            the causal prefix-sum variant.
+ *
+ * Everything is the plain definition, in fp64, in the pages' order:
+ *   sigma2_kd = softplus(rho_kd) = log(1 + e^rho)
+ *   log pi_k  = lambda_k - log sum_j e^lambda_j
+ *   l_k(x)    = log pi_k - 1/2 sum_d [ log(2 pi sigma2_kd) + (x_d - mu_kd)^2 / sigma2_kd ]
+ *   gamma_k   = e^{l_k} / sum_j e^{l_j}           (posterior p(z = k | x))
+ *   Vt = Gamma_K^T V, Z = Gamma_K^T 1             (bidirectional write)
+ *   O  = Gamma_Q Vt / (Gamma_Q Z + eps)           (read; one scalar per row)
+ *   causal: Vt and Z are running sums over j <= i (the diagonal included).
+ *
+ * The Gaussian is taken in its direct form (x - mu)^2 / sigma2, not the
+ * expanded quadratic the GPU uses.  Sums over n run sequentially in n; each
+ * output element is produced by one thread in a fixed order, so results are
+ * bitwise independent of the OpenMP thread count.
+ *
+ * Memory: Gamma rows are produced one block of rows at a time and consumed
+ * in row order.  Rows are independent, so this only bounds memory (a head of
+ * one million tokens would need gigabytes of Gamma otherwise); the arithmetic
+ * of every element is unchanged.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_ROW_BLOCK 4096
+
+static const double TWO_PI = 6.283185307179586476925286766559;
+
+/* softplus(r) = log(1 + e^r), written so that it neither overflows nor loses
+ * the small-r tail: max(r, 0) + log1p(e^{-|r|}). */
+static double softplus(double r) { return fmax(r, 0.0) + log1p(exp(-fabs(r))); }
+
+void gma_oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int gma_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Reparameterisation ("Variantes et Entrainement"): variances by softplus,
+ * priors by softmax (returned as log pi).  Shapes: raw_var, var [H, K, d_r];
+ * prior_logits, log_prior [H, K]. */
+void gma_oracle_params(int64_t H, int32_t K, int32_t dr, const double* raw_var,
+                       const double* prior_logits, double* var, double* log_prior) {
+    for (int64_t i = 0; i < H * K * dr; ++i) var[i] = softplus(raw_var[i]);
+    for (int64_t h = 0; h < H; ++h) {
+        const double* lam = prior_logits + h * K;
+        double m = lam[0];
+        for (int k = 1; k < K; ++k) m = fmax(m, lam[k]);
+        double s = 0.0;
+        for (int k = 0; k < K; ++k) s += exp(lam[k] - m);
+        double lse = m + log(s);
+        for (int k = 0; k < K; ++k) log_prior[h * K + k] = lam[k] - lse;
+    }
+}
+
+/* Posterior responsibilities of one row x[d_r] under one head's mixture
+ * ("Routage Latent Probabiliste").  mu, var [K, d_r]; log_prior [K];
+ * logdet[k] = sum_d log(2 pi var_kd) (a per-component constant).
+ * gamma[K] receives p(z = k | x). */
+static void row_responsibilities(int32_t K, int32_t dr, const double* x, const double* mu,
+                                 const double* var, const double* log_prior,
+                                 const double* logdet, double* gamma) {
+    double m = -INFINITY;
+    for (int k = 0; k < K; ++k) {
+        double q = 0.0;
+        for (int d = 0; d < dr; ++d) {
+            double diff = x[d] - mu[(int64_t)k * dr + d];
+            q += diff * diff / var[(int64_t)k * dr + d];
+        }
+        double l = log_prior[k] - 0.5 * (logdet[k] + q);
+        gamma[k] = l;
+        if (l > m) m = l;
+    }
+    double s = 0.0;
+    for (int k = 0; k < K; ++k) {
+        gamma[k] = exp(gamma[k] - m);
+        s += gamma[k];
+    }
+    for (int k = 0; k < K; ++k) gamma[k] /= s;
+}
+
+static void head_logdet(int32_t K, int32_t dr, const double* var, double* logdet) {
+    for (int k = 0; k < K; ++k) {
+        double s = 0.0;
+        for (int d = 0; d < dr; ++d) s += log(TWO_PI * var[(int64_t)k * dr + d]);
+        logdet[k] = s;
+    }
+}
+
+/* Responsibilities of every row of x [B, H, N, d_r] -> gamma [B, H, N, K].
+ * Parameters are the raw learned ones: mu, raw_var [H, K, d_r], prior_logits [H, K]. */
+int gma_oracle_responsibilities(int64_t B, int64_t H, int64_t N, int32_t dr, int32_t K,
+                                const double* x, const double* mu, const double* raw_var,
+                                const double* prior_logits, double* gamma) {
+    double* var = (double*)malloc(sizeof(double) * H * K * dr);
+    double* logp = (double*)malloc(sizeof(double) * H * K);
+    double* logdet = (double*)malloc(sizeof(double) * H * K);
+    if (!var || !logp || !logdet) { free(var); free(logp); free(logdet); return 1; }
+    gma_oracle_params(H, K, dr, raw_var, prior_logits, var, logp);
+    for (int64_t h = 0; h < H; ++h) head_logdet(K, dr, var + h * K * dr, logdet + h * K);
+    int64_t rows = B * H * N;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t h = (r / N) % H;
+        row_responsibilities(K, dr, x + r * dr, mu + h * K * dr, var + h * K * dr, logp + h * K,
+                             logdet + h * K, gamma + r * K);
+    }
+    free(var); free(logp); free(logdet);
+    return 0;
+}
+
+/* Forward mixer ("Routage de Memoire Latente" and "Variantes et Entrainement").
+ * qx, kx [B, H, N, d_r]; v [B, H, N, d_v]; o [B, H, N, d_v]; causal = 0 or 1.
+ * Returns 0, or 1 if memory could not be allocated. */
+int gma_oracle_forward(int causal, int64_t B, int64_t H, int64_t N, int32_t dr, int32_t K,
+                       int32_t dv, double eps, const double* qx, const double* kx,
+                       const double* v, const double* mu, const double* raw_var,
+                       const double* prior_logits, double* o) {
+    double* var = (double*)malloc(sizeof(double) * H * K * dr);
+    double* logp = (double*)malloc(sizeof(double) * H * K);
+    double* logdet = (double*)malloc(sizeof(double) * H * K);
+    double* gq = (double*)malloc(sizeof(double) * ORACLE_ROW_BLOCK * K);
+    double* gk = (double*)malloc(sizeof(double) * ORACLE_ROW_BLOCK * K);
+    double* vt = (double*)malloc(sizeof(double) * (int64_t)K * dv);   /* latent memory Vt [K, d_v] */
+    double* z = (double*)malloc(sizeof(double) * K);                  /* normaliser Z [K] */
+    double* den = (double*)malloc(sizeof(double) * ORACLE_ROW_BLOCK);
+    int rc = 0;
+    if (!var || !logp || !logdet || !gq || !gk || !vt || !z || !den) { rc = 1; goto done; }
+    gma_oracle_params(H, K, dr, raw_var, prior_logits, var, logp);
+    for (int64_t h = 0; h < H; ++h) head_logdet(K, dr, var + h * K * dr, logdet + h * K);
+
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const int64_t h = bh % H;
+        const double* mu_h = mu + h * K * dr;
+        const double* var_h = var + h * K * dr;
+        const double* lp_h = logp + h * K;
+        const double* ld_h = logdet + h * K;
+        const double* q_bh = qx + bh * N * dr;
+        const double* k_bh = kx + bh * N * dr;
+        const double* v_bh = v + bh * N * dv;
+        double* o_bh = o + bh * N * dv;
+        memset(vt, 0, sizeof(double) * (size_t)K * dv);
+        memset(z, 0, sizeof(double) * (size_t)K);
+
+        if (!causal) {
+            /* Write phase over the whole sequence: Vt = Gamma_K^T V, Z = Gamma_K^T 1. */
+            for (int64_t n0 = 0; n0 < N; n0 += ORACLE_ROW_BLOCK) {
+                int64_t nb = (N - n0 < ORACLE_ROW_BLOCK) ? N - n0 : ORACLE_ROW_BLOCK;
+#pragma omp parallel for schedule(static)
+                for (int64_t r = 0; r < nb; ++r)
+                    row_responsibilities(K, dr, k_bh + (n0 + r) * dr, mu_h, var_h, lp_h, ld_h, gk + r * K);
+                for (int64_t r = 0; r < nb; ++r)
+                    for (int k = 0; k < K; ++k) z[k] += gk[r * K + k];
+#pragma omp parallel for schedule(static)
+                for (int c = 0; c < dv; ++c)
+                    for (int64_t r = 0; r < nb; ++r)
+                        for (int k = 0; k < K; ++k)
+                            vt[(int64_t)k * dv + c] += gk[r * K + k] * v_bh[(n0 + r) * dv + c];
+            }
+            /* Read phase: O_n = (Gamma_Q[n] Vt) / (Gamma_Q[n] . Z + eps). */
+            for (int64_t n0 = 0; n0 < N; n0 += ORACLE_ROW_BLOCK) {
+                int64_t nb = (N - n0 < ORACLE_ROW_BLOCK) ? N - n0 : ORACLE_ROW_BLOCK;
+#pragma omp parallel for schedule(static)
+                for (int64_t r = 0; r < nb; ++r) {
+                    double* g = gq + r * K;
+                    row_responsibilities(K, dr, q_bh + (n0 + r) * dr, mu_h, var_h, lp_h, ld_h, g);
+                    double d = 0.0;
+                    for (int k = 0; k < K; ++k) d += g[k] * z[k];
+                    d += eps;
+                    for (int c = 0; c < dv; ++c) {
+                        double num = 0.0;
+                        for (int k = 0; k < K; ++k) num += g[k] * vt[(int64_t)k * dv + c];
+                        o_bh[(n0 + r) * dv + c] = num / d;
+                    }
+                }
+            }
+        } else {
+            /* Causal: for n = 0 .. N-1 in order, Vt += gamma_K[n] (x) v[n], Z += gamma_K[n],
+             * then O_n = (gamma_Q[n] Vt) / (gamma_Q[n] . Z + eps).  Inclusive of j = n. */
+            for (int64_t n0 = 0; n0 < N; n0 += ORACLE_ROW_BLOCK) {
+                int64_t nb = (N - n0 < ORACLE_ROW_BLOCK) ? N - n0 : ORACLE_ROW_BLOCK;
+#pragma omp parallel for schedule(static)
+                for (int64_t r = 0; r < nb; ++r) {
+                    row_responsibilities(K, dr, q_bh + (n0 + r) * dr, mu_h, var_h, lp_h, ld_h, gq + r * K);
+                    row_responsibilities(K, dr, k_bh + (n0 + r) * dr, mu_h, var_h, lp_h, ld_h, gk + r * K);
+                }
+                /* Denominators: Z as a running sum, one scalar per row. */
+                for (int64_t r = 0; r < nb; ++r) {
+                    for (int k = 0; k < K; ++k) z[k] += gk[r * K + k];
+                    double d = 0.0;
+                    for (int k = 0; k < K; ++k) d += gq[r * K + k] * z[k];
+                    den[r] = d + eps;
+                }
+                /* Numerators: column c of Vt is a running sum of its own. */
+#pragma omp parallel for schedule(static)
+                for (int c = 0; c < dv; ++c) {
+                    for (int64_t r = 0; r < nb; ++r) {
+                        const double vc = v_bh[(n0 + r) * dv + c];
+                        double num = 0.0;
+                        for (int k = 0; k < K; ++k) {
+                            vt[(int64_t)k * dv + c] += gk[r * K + k] * vc;
+                            num += gq[r * K + k] * vt[(int64_t)k * dv + c];
+                        }
+                        o_bh[(n0 + r) * dv + c] = num / den[r];
+                    }
+                }
+            }
+        }
+    }
+done:
+    free(var); free(logp); free(logdet); free(gq); free(gk); free(vt); free(z); free(den);
+    return rc;
+}

@@ -1,0 +1,331 @@
+"""Pins for the fp64 oracle, checked against things other than itself.
+
+Every definition comes from the page "Attention par Mélange Gaussien (GMA)",
+section "Méthodologie", sub-section "Mécanisme Central":
+  item 1  responsibilities are GMM posteriors (non-negative, rows sum to 1);
+  item 2  write Vt = Gamma_K^T V, Z = Gamma_K^T 1, read O = Gamma_Q Vt / (Gamma_Q Z + eps),
+          identical (by associativity) to the materialised affinity A = Gamma_Q Gamma_K^T;
+  item 3  causal prefix sums (O_i depends on j <= i only); softplus variances and
+          softmax priors.
+Section "Contributions Clés", item 3 ("Interprétation de l'Affinité"): A is
+non-negative with rank <= K.
+
+Independent references used here: SciPy's multivariate normal log-density and
+softmax, scikit-learn's GaussianMixture posterior, a hand-derived closed-form
+fixture (tests/golden/two_component_1d.txt), closed forms for K = 1 and for
+identical components, brute-force materialised affinities, and structural
+invariants (linearity, convexity bound, permutation symmetry, causal masking).
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+from scipy.special import log_softmax, softmax
+from scipy.stats import multivariate_normal
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "two_component_1d.txt")
+
+
+def rand_params(rng, H, K, dr):
+    mu = rng.normal(0.0, 1.0, (H, K, dr))
+    rv = rng.uniform(-1.0, 1.0, (H, K, dr))
+    pl = rng.normal(0.0, 0.5, (H, K))
+    return mu, rv, pl
+
+
+def scipy_gamma(x, mu, rv, pl):
+    """Posterior from SciPy: log N(x; mu_k, diag(var_k)) + log pi_k, then softmax over k.
+    x [N, dr]; mu, rv [K, dr]; pl [K].  var = log(1 + e^rho) via numpy's logaddexp."""
+    var = np.logaddexp(0.0, rv)
+    logpi = log_softmax(pl)
+    L = np.stack([multivariate_normal(mean=mu[k], cov=np.diag(var[k])).logpdf(x).reshape(-1)
+                  for k in range(mu.shape[0])], axis=-1) + logpi
+    return softmax(L, axis=-1)
+
+
+def brute_force(gq, gk, v, eps, causal):
+    """Materialised affinity A = Gamma_Q Gamma_K^T (lower-triangular incl. diagonal when causal)."""
+    A = gq @ gk.T
+    if causal:
+        A = np.tril(A)
+    return (A @ v) / (A.sum(axis=1, keepdims=True) + eps)
+
+
+# ----------------------------------------------------------------------------- parameters
+
+
+def test_softplus_closed_forms(oracle_mod):
+    rv = np.array([[[0.0, 1.5, -1.5, 40.0, -40.0, 1e-8]]])
+    var, _ = oracle_mod.params(rv, np.zeros((1, 1)))
+    v = var[0, 0]
+    assert v[0] == pytest.approx(math.log(2.0), rel=1e-15)
+    assert v[1] - v[2] == pytest.approx(1.5, rel=1e-14)          # softplus(x) - softplus(-x) = x
+    assert v[3] == pytest.approx(40.0, rel=1e-15)
+    assert v[4] == pytest.approx(math.exp(-40.0), rel=1e-12)     # small tail kept, not flushed
+    assert v[5] == pytest.approx(math.log(2.0) + 0.5e-8, rel=1e-15)
+
+
+def test_prior_softmax(oracle_mod):
+    rng = np.random.default_rng(0)
+    pl = rng.normal(0, 3.0, (3, 7))
+    _, logp = oracle_mod.params(np.zeros((3, 7, 2)), pl)
+    np.testing.assert_allclose(np.exp(logp).sum(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(logp - logp[:, :1], pl - pl[:, :1], atol=1e-13)
+    _, logp_eq = oracle_mod.params(np.zeros((1, 5, 1)), np.full((1, 5), 3.7))
+    np.testing.assert_allclose(logp_eq, -math.log(5.0), rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------- responsibilities
+
+
+def test_gamma_nonnegative_rows_sum_to_one(oracle_mod):
+    rng = np.random.default_rng(1)
+    mu, rv, pl = rand_params(rng, 2, 9, 6)
+    x = rng.normal(0, 2.0, (2, 2, 50, 6))
+    g = oracle_mod.responsibilities(x, mu, rv, pl)
+    assert g.shape == (2, 2, 50, 9)
+    assert (g >= 0).all()
+    np.testing.assert_allclose(g.sum(-1), 1.0, rtol=1e-14)
+
+
+def test_gamma_matches_scipy(oracle_mod):
+    rng = np.random.default_rng(2)
+    H, K, dr = 3, 6, 5
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    x = rng.normal(0, 1.0, (1, H, 40, dr))
+    g = oracle_mod.responsibilities(x, mu, rv, pl)
+    for h in range(H):
+        ref = scipy_gamma(x[0, h], mu[h], rv[h], pl[h])
+        np.testing.assert_allclose(g[0, h], ref, rtol=1e-10, atol=1e-14)
+
+
+def test_gamma_matches_sklearn(oracle_mod):
+    from sklearn.mixture import GaussianMixture
+    rng = np.random.default_rng(3)
+    K, dr = 4, 3
+    mu, rv, pl = rand_params(rng, 1, K, dr)
+    var = np.logaddexp(0.0, rv[0])
+    gm = GaussianMixture(n_components=K, covariance_type="diag")
+    gm.means_ = mu[0]
+    gm.covariances_ = var
+    gm.precisions_cholesky_ = 1.0 / np.sqrt(var)
+    gm.weights_ = softmax(pl[0])
+    gm.converged_, gm.n_iter_, gm.lower_bound_ = True, 0, 0.0
+    x = rng.normal(0, 1.5, (64, dr))
+    g = oracle_mod.responsibilities(x, mu, rv, pl)
+    np.testing.assert_allclose(g, gm.predict_proba(x), rtol=1e-9, atol=1e-13)
+
+
+def test_gamma_two_component_sigmoid(oracle_mod):
+    # d_r = 1, K = 2, equal variance s and equal priors:
+    # gamma_1(x) = sigmoid((mu_1 - mu_2)(x - (mu_1 + mu_2)/2) / s).
+    m1, m2, rho = 0.3, -1.1, 0.25
+    s = math.log1p(math.exp(rho))
+    x = np.linspace(-4, 4, 33).reshape(-1, 1)
+    g = oracle_mod.responsibilities(x, np.array([[[m1], [m2]]]), np.full((1, 2, 1), rho), np.zeros((1, 2)))
+    t = (m1 - m2) * (x[:, 0] - (m1 + m2) / 2) / s
+    np.testing.assert_allclose(g[:, 0], 1.0 / (1.0 + np.exp(-t)), rtol=1e-13)
+
+
+def test_gamma_single_component_is_one(oracle_mod):
+    rng = np.random.default_rng(4)
+    mu, rv, pl = rand_params(rng, 1, 1, 4)
+    g = oracle_mod.responsibilities(rng.normal(0, 5, (20, 4)), mu, rv, pl)
+    assert (g == 1.0).all()
+
+
+def test_gamma_far_rows_are_one_hot_not_nan(oracle_mod):
+    mu = np.array([[[0.0], [10.0]]])
+    g = oracle_mod.responsibilities(np.array([[-1e3], [1e3]]), mu, np.zeros((1, 2, 1)), np.zeros((1, 2)))
+    assert np.isfinite(g).all()
+    np.testing.assert_array_equal(g, [[1.0, 0.0], [0.0, 1.0]])
+
+
+# ----------------------------------------------------------------------------- golden fixture
+
+
+def _golden():
+    out = {}
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split(":", 1)
+            rows = [[Fraction(t) if "/" in t else float(t) for t in r.split()] for r in val.split("|")]
+            out[key.strip()] = rows
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_golden_two_component(oracle_mod, causal):
+    gd = _golden()
+    mu = np.array(gd["mu"][0], dtype=float).reshape(1, 2, 1)
+    rv = np.full((1, 2, 1), gd["raw_var"][0][0])
+    pl = np.array(gd["prior_logits"][0], dtype=float).reshape(1, 2)
+    eps = gd["eps"][0][0]
+    xq = np.array([r[0] for r in gd["x_q"]], dtype=float).reshape(3, 1)
+    xk = np.array([r[0] for r in gd["x_k"]], dtype=float).reshape(3, 1)
+    v = np.array(gd["v"], dtype=float)
+    gq = oracle_mod.responsibilities(xq, mu, rv, pl)
+    gk = oracle_mod.responsibilities(xk, mu, rv, pl)
+    np.testing.assert_allclose(gq, np.array(gd["gamma_q"], dtype=float), rtol=1e-14)
+    np.testing.assert_allclose(gk, np.array(gd["gamma_k"], dtype=float), rtol=1e-14)
+    tag = "causal" if causal else "bidir"
+    num = np.array(gd[tag + "_num"], dtype=float)
+    den = np.array([r[0] for r in gd[tag + "_den"]], dtype=float)
+    expect = num / (den + eps)[:, None]
+    o = oracle_mod.forward(xq, xk, v, mu, rv, pl, eps=eps, causal=causal)
+    np.testing.assert_allclose(o, expect, rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- forward
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_matches_brute_force_affinity(oracle_mod, causal):
+    rng = np.random.default_rng(5)
+    B, H, N, dr, K, dv = 2, 2, 37, 3, 5, 4
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    qx, kx = rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dr))
+    v = rng.normal(0, 1, (B, H, N, dv))
+    eps = 1e-3
+    o = oracle_mod.forward(qx, kx, v, mu, rv, pl, eps=eps, causal=causal)
+    for b in range(B):
+        for h in range(H):
+            gq = scipy_gamma(qx[b, h], mu[h], rv[h], pl[h])
+            gk = scipy_gamma(kx[b, h], mu[h], rv[h], pl[h])
+            np.testing.assert_allclose(o[b, h], brute_force(gq, gk, v[b, h], eps, causal), rtol=1e-10, atol=1e-12)
+
+
+def test_affinity_nonnegative_rank_at_most_K(oracle_mod):
+    rng = np.random.default_rng(6)
+    N, dr, K = 60, 4, 5
+    mu, rv, pl = rand_params(rng, 1, K, dr)
+    gq = oracle_mod.responsibilities(rng.normal(0, 1, (N, dr)), mu, rv, pl)
+    gk = oracle_mod.responsibilities(rng.normal(0, 1, (N, dr)), mu, rv, pl)
+    A = gq @ gk.T
+    assert (A >= 0).all()
+    s = np.linalg.svd(A, compute_uv=False)
+    assert (s[K:] <= 1e-12 * s[0]).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_component_closed_form(oracle_mod, causal):
+    rng = np.random.default_rng(7)
+    N, dr, dv, eps = 25, 3, 4, 0.25
+    mu, rv, pl = rand_params(rng, 1, 1, dr)
+    v = rng.normal(0, 1, (N, dv))
+    o = oracle_mod.forward(rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dr)), v, mu, rv, pl,
+                           eps=eps, causal=causal)
+    if causal:
+        expect = np.cumsum(v, axis=0) / (np.arange(1, N + 1)[:, None] + eps)
+    else:
+        expect = np.broadcast_to(v.sum(0) / (N + eps), v.shape)
+    np.testing.assert_allclose(o, expect, rtol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_components_closed_form(oracle_mod, causal):
+    # K identical components with equal priors: gamma = 1/K everywhere, so
+    # O_n = sum_j v_j / (count + K eps).
+    rng = np.random.default_rng(8)
+    N, dr, dv, K, eps = 19, 2, 3, 4, 0.5
+    mu = np.broadcast_to(rng.normal(0, 1, (1, 1, dr)), (1, K, dr)).copy()
+    rv = np.broadcast_to(rng.uniform(-1, 1, (1, 1, dr)), (1, K, dr)).copy()
+    v = rng.normal(0, 1, (N, dv))
+    o = oracle_mod.forward(rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dr)), v, mu, rv,
+                           np.zeros((1, K)), eps=eps, causal=causal)
+    if causal:
+        expect = np.cumsum(v, axis=0) / (np.arange(1, N + 1)[:, None] + K * eps)
+    else:
+        expect = np.broadcast_to(v.sum(0) / (N + K * eps), v.shape)
+    np.testing.assert_allclose(o, expect, rtol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_linear_in_values_and_convexity_bound(oracle_mod, causal):
+    rng = np.random.default_rng(9)
+    B, H, N, dr, K, dv = 1, 2, 45, 4, 6, 5
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    qx, kx = rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dr))
+    v1, v2 = rng.normal(0, 1, (B, H, N, dv)), rng.normal(0, 1, (B, H, N, dv))
+    f = lambda v: oracle_mod.forward(qx, kx, v, mu, rv, pl, eps=1e-6, causal=causal)
+    o1, o2, o12 = f(v1), f(v2), f(2.0 * v1 - 3.0 * v2)
+    np.testing.assert_allclose(o12, 2.0 * o1 - 3.0 * o2, rtol=1e-11, atol=1e-12)
+    # |O_nc| <= max_j |V_jc|: the weights A_nj / (sum_j A_nj + eps) are >= 0 and sum to < 1.
+    bound = np.abs(v1).max(axis=2, keepdims=True)
+    assert (np.abs(o1) <= bound * (1 + 1e-12)).all()
+
+
+def test_bidir_permutation_symmetry(oracle_mod):
+    rng = np.random.default_rng(10)
+    N, dr, K, dv = 30, 3, 4, 2
+    mu, rv, pl = rand_params(rng, 1, K, dr)
+    qx, kx, v = rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dv))
+    o = oracle_mod.forward(qx, kx, v, mu, rv, pl)
+    p = rng.permutation(N)
+    np.testing.assert_allclose(oracle_mod.forward(qx[p], kx, v, mu, rv, pl), o[p], rtol=1e-13)  # queries: equivariant
+    np.testing.assert_allclose(oracle_mod.forward(qx, kx[p], v[p], mu, rv, pl), o, rtol=1e-12)  # keys+values: invariant
+
+
+def test_causal_ignores_future_tokens_bitwise(oracle_mod):
+    rng = np.random.default_rng(11)
+    B, H, N, dr, K, dv = 1, 2, 64, 3, 5, 4
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    qx, kx, v = rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dv))
+    o = oracle_mod.forward(qx, kx, v, mu, rv, pl, causal=True)
+    for i in (0, 17, 40):
+        q2, k2, v2 = qx.copy(), kx.copy(), v.copy()
+        q2[:, :, i + 1:] = rng.normal(0, 3, q2[:, :, i + 1:].shape)
+        k2[:, :, i + 1:] = rng.normal(0, 3, k2[:, :, i + 1:].shape)
+        v2[:, :, i + 1:] = rng.normal(0, 3, v2[:, :, i + 1:].shape)
+        o2 = oracle_mod.forward(q2, k2, v2, mu, rv, pl, causal=True)
+        np.testing.assert_array_equal(o2[:, :, : i + 1], o[:, :, : i + 1])
+        assert not np.array_equal(o2[:, :, i + 1:], o[:, :, i + 1:])
+
+
+def test_causal_is_bidir_on_prefix(oracle_mod):
+    rng = np.random.default_rng(12)
+    N, dr, K, dv = 48, 3, 4, 3
+    mu, rv, pl = rand_params(rng, 1, K, dr)
+    qx, kx, v = rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dv))
+    oc = oracle_mod.forward(qx, kx, v, mu, rv, pl, causal=True)
+    ob = oracle_mod.forward(qx, kx, v, mu, rv, pl, causal=False)
+    np.testing.assert_allclose(oc[-1], ob[-1], rtol=1e-14)
+    for i in (0, 1, 13, 29):
+        obi = oracle_mod.forward(qx[: i + 1], kx[: i + 1], v[: i + 1], mu, rv, pl, causal=False)
+        np.testing.assert_allclose(oc[i], obi[i], rtol=1e-13)
+
+
+def test_thread_count_does_not_change_bits(oracle_mod):
+    rng = np.random.default_rng(13)
+    B, H, N, dr, K, dv = 1, 2, 5000, 4, 6, 8
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    args = (rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dv)), mu, rv, pl)
+    n = oracle_mod.max_threads()
+    try:
+        for causal in (False, True):
+            a = oracle_mod.forward(*args, causal=causal, threads=1)
+            b = oracle_mod.forward(*args, causal=causal, threads=max(2, n))
+            np.testing.assert_array_equal(a, b)
+    finally:
+        oracle_mod.set_threads(n)
+
+
+@settings(max_examples=25, deadline=None)
+@given(N=st.integers(1, 24), dr=st.integers(1, 5), K=st.integers(1, 6), dv=st.integers(1, 4),
+       causal=st.booleans(), seed=st.integers(0, 2**31 - 1))
+def test_property_random_shapes_match_brute_force(N, dr, K, dv, causal, seed):
+    import oracle
+    rng = np.random.default_rng(seed)
+    mu, rv, pl = rand_params(rng, 1, K, dr)
+    qx, kx, v = rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dv))
+    o = oracle.forward(qx, kx, v, mu, rv, pl, eps=1e-6, causal=causal)
+    gq, gk = scipy_gamma(qx, mu[0], rv[0], pl[0]), scipy_gamma(kx, mu[0], rv[0], pl[0])
+    np.testing.assert_allclose(o, brute_force(gq, gk, v, 1e-6, causal), rtol=1e-9, atol=1e-11)
