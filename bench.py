@@ -1,0 +1,210 @@
+"""Throughput of the GMA forward mixer on one MI355X.
+
+A step is one call of the full forward (parameter prep, segment aggregates, segment scan and
+the chunked causal output pass) over one batch of synthetic inputs already resident in HBM.
+Default workload: causal, bf16 storage / fp32 accumulation, B=1, H=16, N=65536, d_r=128,
+K=128, d_v=128.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix peaks
+METRIC = "GMA fwd tokens/sec (causal, N=64K, K=128) + % of HBM/MFMA roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gaussian_mixture_token_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes_per_token_head(w) -> int:
+    # read Q_X, K_X, V once and write O once
+    es = 2 if w.dtype == "bf16" else 4
+    return es * (2 * w.d_route + 2 * w.d_value)
+
+
+def algorithmic_flops_per_token_head(w) -> int:
+    # logits of Q and K: 2 * (2 d_r) * K * 2; write Gamma_K^T V and read Gamma_Q Vt: 2 * 2 K d_v
+    return 8 * w.n_comp * w.d_route + 4 * w.n_comp * w.d_value
+
+
+def load_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = t.get(kernel)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, heads):
+    import oracle
+    sub_w = w
+    from gaussian_mixture_token_amd import make_inputs
+    inp = make_inputs(sub_w, heads=heads)
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.forward(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"], inp["prior_logits"],
+                   eps=w.eps, causal=w.causal)
+    dt = time.perf_counter() - t0
+    token_heads = w.batch * len(heads) * w.seq_len
+    return {"value": token_heads / dt / w.heads, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d heads, full N=%d, %s fp64 oracle, %.1f s wall" %
+                      (len(heads), w.heads, w.seq_len, "causal" if w.causal else "bidirectional", dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+              "(each (batch, head) or sequence shard would run the same single-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gaussian_mixture_token_amd as gma
+    from gaussian_mixture_token_amd import _lib
+
+    lib = _lib.load()
+    dev = torch.device("cuda:0")
+    w = gma.workload(args.workload)
+    print("bench: workload %s" % w.name, file=sys.stderr, flush=True)
+    inp = gma.make_inputs(w)
+    t = {k: v.to(dev) for k, v in inp.items()}
+    del inp
+    out = torch.empty(w.batch, w.heads, w.seq_len, w.d_value, dtype=w.torch_dtype, device=dev)
+    prob = gma.problem(w.batch, w.heads, w.seq_len, w.d_route, w.n_comp, w.d_value, w.torch_dtype, w.eps)
+    op = _lib.GMA_OP_FORWARD_CAUSAL if w.causal else _lib.GMA_OP_FORWARD_BIDIR
+    ws = torch.empty(gma.workspace_size(prob, op), dtype=torch.uint8, device=dev)
+
+    def step():
+        gma.forward(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps,
+                    causal=w.causal, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("bench: warmup done", file=sys.stderr, flush=True)
+
+    # timed region 1: whole steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / args.steps
+    tokens = w.batch * w.seq_len
+    value = tokens / (ms_per_step / 1e3)
+    print("bench: %.3f ms/step (wall %.3f s)" % (ms_per_step, wall), file=sys.stderr, flush=True)
+
+    # timed region 2: the same steps with per-kernel HIP events on the launch stream
+    lib.gma_timing_enable(1)
+    for k in range(lib.gma_kernel_count()):
+        lib.gma_timing_read(k, ctypes_double(), ctypes_int64())
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    lib.gma_timing_enable(0)
+    kernels = {}
+    for k in range(lib.gma_kernel_count()):
+        tot, n = ctypes_double(), ctypes_int64()
+        _lib.check(lib.gma_timing_read(k, tot, n))
+        if n.value:
+            kernels[lib.gma_kernel_name(k).decode()] = {"avg_us": 1e3 * tot.value / n.value, "launches": n.value}
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    avg_s = kernels[dominant]["avg_us"] * 1e-6
+    T = w.batch * w.heads * w.seq_len
+    alg_bytes = algorithmic_bytes_per_token_head(w) * T
+    alg_flops = algorithmic_flops_per_token_head(w) * T
+    hbm_frac = alg_bytes / avg_s / 1e9 / HBM_PEAK_GBS
+    mfma_frac = alg_flops / avg_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(dominant, src_hash)
+    if hbm_frac >= mfma_frac:
+        roof = {"bound": "hbm", "achieved": alg_bytes / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": hbm_frac, "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": alg_flops / avg_s / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": mfma_frac, "traffic": traffic}
+    roof.update({"kernel": dominant, "kernel_avg_us": kernels[dominant]["avg_us"],
+                 "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": alg_flops,
+                 "hbm_frac": hbm_frac, "mfma_frac": mfma_frac})
+    # whole-step fractions (all kernels of the step against the same algorithmic work)
+    step_s = ms_per_step * 1e-3
+    step_roof = {"hbm_frac": alg_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+                 "mfma_frac": alg_flops / step_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        heads = list(range(min(args.cpu_heads, w.heads)))
+        cpu = cpu_baseline(w, heads)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, N(0,1) means, U(-1,1) raw variances, N(0,0.5^2) prior logits)",
+        "config": {"workload": w.name, "mode": "causal" if w.causal else "bidirectional", "batch": w.batch,
+                   "heads": w.heads, "seq_len": w.seq_len, "d_route": w.d_route, "n_comp": w.n_comp,
+                   "d_value": w.d_value, "eps": w.eps, "global_batch": w.batch, "parallelism": "single GPU"},
+        "roofline": roof,
+        "step_roofline": step_roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "source_hash": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def ctypes_double():
+    import ctypes
+    return ctypes.c_double()
+
+
+def ctypes_int64():
+    import ctypes
+    return ctypes.c_int64()
+
+
+if __name__ == "__main__":
+    main()

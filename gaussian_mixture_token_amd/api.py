@@ -1,0 +1,123 @@
+"""PyTorch-facing binding of libgma.so.
+
+Tensors supply device memory and the current HIP stream; every step of the computation runs
+in the library's HIP kernels.  There is no CPU or PyTorch fallback: a missing library or a
+non-GPU tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+__all__ = ["problem", "workspace_size", "responsibilities", "forward_bidir", "forward_causal",
+           "forward", "GmaError"]
+
+GmaError = _lib.GmaError
+
+_DTYPES = {torch.float32: _lib.GMA_DTYPE_F32, torch.bfloat16: _lib.GMA_DTYPE_BF16}
+
+
+def problem(B: int, H: int, N: int, d_r: int, K: int, d_v: int, dtype: torch.dtype, eps: float = 1e-6) -> _lib.Problem:
+    if dtype not in _DTYPES:
+        raise TypeError("dtype must be torch.float32 or torch.bfloat16")
+    return _lib.Problem(B, H, N, d_r, K, d_v, _DTYPES[dtype], float(eps))
+
+
+def workspace_size(prob: _lib.Problem, op: int) -> int:
+    return int(_lib.load().gma_workspace_size(ctypes.byref(prob), op))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_gpu(*ts: torch.Tensor) -> torch.device:
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if t.device != dev:
+            raise ValueError("all tensors must be on one device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    return dev
+
+
+def _params(mu, raw_var, prior_logits, H, K, d_r):
+    for name, t, shape in (("mu", mu, (H, K, d_r)), ("raw_var", raw_var, (H, K, d_r)),
+                           ("prior_logits", prior_logits, (H, K))):
+        if t.dtype != torch.float32:
+            raise TypeError("%s must be float32" % name)
+        if tuple(t.shape) != shape:
+            raise ValueError("%s must have shape %s, got %s" % (name, shape, tuple(t.shape)))
+
+
+def _workspace(nbytes: int, device: torch.device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small: need %d bytes" % nbytes)
+        return workspace
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def responsibilities(x: torch.Tensor, mu: torch.Tensor, raw_var: torch.Tensor, prior_logits: torch.Tensor,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gamma [B, H, N, K] fp32 for x [B, H, N, d_r] (fp32 or bf16)."""
+    B, H, N, d_r = x.shape
+    K = mu.shape[1]
+    _params(mu, raw_var, prior_logits, H, K, d_r)
+    dev = _check_gpu(x, mu, raw_var, prior_logits)
+    prob = problem(B, H, N, d_r, K, 1, x.dtype)
+    if out is None:
+        out = torch.empty(B, H, N, K, dtype=torch.float32, device=dev)
+    _check_gpu(out)
+    ws = _workspace(workspace_size(prob, _lib.GMA_OP_RESPONSIBILITIES), dev, workspace)
+    _lib.check(_lib.load().gma_responsibilities(ctypes.byref(prob), _ptr(x), _ptr(mu), _ptr(raw_var), _ptr(prior_logits),
+                                                _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return out
+
+
+def _forward(fn_name: str, op: int, qx, kx, v, mu, raw_var, prior_logits, eps, out, workspace):
+    B, H, N, d_r = qx.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    if tuple(kx.shape) != (B, H, N, d_r) or tuple(v.shape[:3]) != (B, H, N):
+        raise ValueError("qx, kx must be [B, H, N, d_r] and v [B, H, N, d_v]")
+    if not (qx.dtype == kx.dtype == v.dtype):
+        raise TypeError("qx, kx and v must share one dtype")
+    _params(mu, raw_var, prior_logits, H, K, d_r)
+    dev = _check_gpu(qx, kx, v, mu, raw_var, prior_logits)
+    prob = problem(B, H, N, d_r, K, d_v, qx.dtype, eps)
+    if out is None:
+        out = torch.empty(B, H, N, d_v, dtype=qx.dtype, device=dev)
+    _check_gpu(out)
+    ws = _workspace(workspace_size(prob, op), dev, workspace)
+    fn = getattr(_lib.load(), fn_name)
+    _lib.check(fn(ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu), _ptr(raw_var), _ptr(prior_logits),
+                  _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+    return out
+
+
+def forward_bidir(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=None, workspace=None):
+    """O = Gamma_Q (Gamma_K^T V) / (Gamma_Q (Gamma_K^T 1) + eps); qx, kx [B, H, N, d_r], v [B, H, N, d_v]."""
+    return _forward("gma_forward_bidir", _lib.GMA_OP_FORWARD_BIDIR, qx, kx, v, mu, raw_var, prior_logits, eps,
+                    out, workspace)
+
+
+def forward_causal(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=None, workspace=None):
+    """Causal O (prefix sums of Gamma_K^T V and Gamma_K^T 1, inclusive of the current token)."""
+    return _forward("gma_forward_causal", _lib.GMA_OP_FORWARD_CAUSAL, qx, kx, v, mu, raw_var, prior_logits, eps,
+                    out, workspace)
+
+
+def forward(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, causal: bool = False, out=None, workspace=None):
+    f = forward_causal if causal else forward_bidir
+    return f(qx, kx, v, mu, raw_var, prior_logits, eps=eps, out=out, workspace=workspace)

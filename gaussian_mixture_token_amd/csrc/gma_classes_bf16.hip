@@ -1,0 +1,18 @@
+// Compiled shape classes for bf16 storage (fp16 logits operands, bf16 contraction operands).
+// Columns: fp32?, padded K, padded d_v, padded d_r, wavefronts per workgroup, tokens per chunk.
+#include "gma_registry.hpp"
+
+namespace gma {
+
+static const ShapeClass kClassesBf16[] = {
+    GMA_SHAPE_CLASS(false, 32, 64, 64, 2, 64),
+    GMA_SHAPE_CLASS(false, 128, 128, 128, 4, 64),
+    GMA_SHAPE_CLASS(false, 256, 64, 64, 4, 32),
+};
+
+const ShapeClass* classes_bf16(int* count) {
+    *count = (int)(sizeof(kClassesBf16) / sizeof(kClassesBf16[0]));
+    return kClassesBf16;
+}
+
+}  // namespace gma

@@ -1,0 +1,434 @@
+// Host side of libgma.so: argument validation, shape-class selection, workspace layout,
+// kernel launches and optional per-kernel event timing.  Declared in include/gma.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/gma.h"
+#include "gma_registry.hpp"
+
+namespace gma {
+namespace {
+
+thread_local std::string g_last_error;
+
+gma_status_t fail(gma_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gma_status_t fail(gma_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+// Workgroups the segment split aims for: two per compute unit of a 256-CU MI355X.  A fixed
+// constant (not a device query) keeps the decomposition, and therefore every result bit,
+// independent of the device and of the HIP runtime state.
+constexpr int64_t kTargetWorkgroups = 512;
+
+int next_pow2(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+enum KernelId { K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_COUNT };
+const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan",
+                                     "causal_output", "bidir_output", "responsibilities"};
+
+struct Plan {
+    const ShapeClass* cls = nullptr;
+    int64_t B = 0, H = 0, N = 0;
+    int d_r = 0, K = 0, d_v = 0;
+    bool f32 = false;
+    float eps = 0.f;
+    int64_t n_chunks = 0;
+    int P = 1;
+    int seg_chunks = 1;
+    size_t off_ab = 0, off_c = 0, off_seg = 0, total = 0;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// vc < 0: any d_v class (the responsibilities kernel does not touch V).
+const ShapeClass* find_class(bool f32, int kc, int vc, int drc) {
+    int n = 0;
+    const ShapeClass* tab = f32 ? classes_f32(&n) : classes_bf16(&n);
+    for (int i = 0; i < n; ++i)
+        if (tab[i].kc == kc && (vc < 0 || tab[i].vc == vc) && tab[i].drc == drc) return &tab[i];
+    return nullptr;
+}
+
+// Validates sizes (pure host) and fills the plan.  No HIP call.
+gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan) {
+    if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
+    if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_FORWARD_CAUSAL)
+        return fail(GMA_ERROR_INVALID_VALUE, "unknown op %d", op);
+    if (p->batch < 1 || p->heads < 1 || p->seq_len < 1)
+        return fail(GMA_ERROR_INVALID_VALUE, "batch, heads and seq_len must be >= 1 (got %lld, %lld, %lld)",
+                    (long long)p->batch, (long long)p->heads, (long long)p->seq_len);
+    if (p->d_route < 1 || p->n_comp < 1 || p->d_value < 1)
+        return fail(GMA_ERROR_INVALID_VALUE, "d_route, n_comp and d_value must be >= 1");
+    if (p->dtype != GMA_DTYPE_F32 && p->dtype != GMA_DTYPE_BF16)
+        return fail(GMA_ERROR_INVALID_VALUE, "dtype must be GMA_DTYPE_F32 or GMA_DTYPE_BF16 (got %d)", p->dtype);
+    if (!std::isfinite(p->eps) || p->eps < 0.f)
+        return fail(GMA_ERROR_INVALID_VALUE, "eps must be finite and >= 0");
+    if (p->d_route > 256 || p->n_comp > 256 || p->d_value > 256)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "d_route, n_comp and d_value must be <= 256");
+    const int64_t maxd = std::max(std::max(p->d_route, p->d_value), p->n_comp);
+    if (p->batch > (int64_t(1) << 40) / p->heads ||
+        p->batch * p->heads > (int64_t(1) << 52) / p->seq_len / maxd)
+        return fail(GMA_ERROR_INVALID_VALUE, "tensor sizes overflow");
+    if (p->batch * p->heads > INT32_MAX / 2)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "batch * heads too large");
+
+    plan->f32 = p->dtype == GMA_DTYPE_F32;
+    plan->B = p->batch;
+    plan->H = p->heads;
+    plan->N = p->seq_len;
+    plan->d_r = p->d_route;
+    plan->K = p->n_comp;
+    plan->d_v = p->d_value;
+    plan->eps = p->eps;
+
+    const int kmin = plan->f32 ? 16 : 32;
+    const int kc = std::max(kmin, next_pow2(p->n_comp));
+    const int w = std::min(4, kc / 16);
+    const int vc = std::max(next_pow2(p->d_value), 16 * w);
+    const int drc = std::max(plan->f32 ? 16 : 32, next_pow2(p->d_route));
+    plan->cls = find_class(plan->f32, kc, op == GMA_OP_RESPONSIBILITIES ? -1 : vc, drc);
+    if (!plan->cls)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "no compiled kernel class for dtype=%s K=%d d_v=%d d_r=%d (padded %d/%d/%d)",
+                    plan->f32 ? "f32" : "bf16", p->n_comp, p->d_value, p->d_route, kc, vc, drc);
+    const int C = plan->cls->c;
+    const int64_t BH = plan->B * plan->H;
+    plan->n_chunks = (plan->N + C - 1) / C;
+    if (op == GMA_OP_RESPONSIBILITIES) {
+        plan->P = (int)std::min<int64_t>(plan->n_chunks, INT32_MAX / 4);
+        plan->seg_chunks = (int)((plan->n_chunks + plan->P - 1) / plan->P);
+    } else {
+        int64_t P = (kTargetWorkgroups + BH - 1) / BH;
+        if (P > plan->n_chunks) P = plan->n_chunks;
+        if (P < 1) P = 1;
+        const int64_t sc = (plan->n_chunks + P - 1) / P;
+        plan->seg_chunks = (int)sc;
+        plan->P = (int)((plan->n_chunks + sc - 1) / sc);
+    }
+    if (BH * plan->P > INT32_MAX)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "grid too large");
+
+    // workspace: [a | b] fragments, c, segment records
+    const int ks = plan->f32 ? 16 : 32;
+    const int nks = 2 * plan->cls->drc / ks;
+    const size_t ab_bytes = (size_t)plan->H * (plan->cls->kc / 16) * nks * 64 * 16;
+    const size_t c_bytes = (size_t)plan->H * plan->cls->kc * sizeof(float);
+    size_t seg_bytes = 0;
+    const bool need_seg = (op == GMA_OP_FORWARD_BIDIR) || (op == GMA_OP_FORWARD_CAUSAL && plan->P > 1);
+    if (need_seg)
+        seg_bytes = (size_t)BH * plan->P * ((size_t)plan->cls->kc * plan->cls->vc + plan->cls->kc) * sizeof(float);
+    plan->off_ab = 0;
+    plan->off_c = align_up(ab_bytes, 256);
+    plan->off_seg = align_up(plan->off_c + c_bytes, 256);
+    plan->total = align_up(plan->off_seg + seg_bytes, 256);
+    return GMA_SUCCESS;
+}
+
+bool misaligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// ---------------------------------------------------------------------------------- timing
+struct Timing {
+    std::mutex mu;
+    bool enabled = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded[K_COUNT];
+    std::vector<hipEvent_t> pool;
+} g_timing;
+
+hipEvent_t take_event() {
+    if (!g_timing.pool.empty()) {
+        hipEvent_t e = g_timing.pool.back();
+        g_timing.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+gma_status_t timed_launch(int kid, hipStream_t s, F&& launch) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    bool timing = false;
+    {
+        std::lock_guard<std::mutex> lk(g_timing.mu);
+        if (g_timing.enabled) {
+            e0 = take_event();
+            e1 = take_event();
+            timing = e0 && e1;
+        }
+    }
+    if (timing) (void)hipEventRecord(e0, s);
+    launch();
+    const hipError_t err = hipGetLastError();
+    if (timing) {
+        (void)hipEventRecord(e1, s);
+        std::lock_guard<std::mutex> lk(g_timing.mu);
+        g_timing.recorded[kid].emplace_back(e0, e1);
+    }
+    if (err != hipSuccess)
+        return fail(GMA_ERROR_LAUNCH, "launch of %s failed: %s", kKernelNames[kid], hipGetErrorString(err));
+    return GMA_SUCCESS;
+}
+
+// ---------------------------------------------------------------------------------- launches
+// scan over the P segment aggregates of each (batch, head), fixed order (deterministic).
+// causal: seg[bh][s] <- sum_{t < s} seg[bh][t] (exclusive prefix, in place)
+// bidir : seg[bh][0] <- sum_{t < P} seg[bh][t]
+__global__ void __launch_bounds__(256) scan_kernel(float* seg, int P, int64_t rec, int causal) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= rec) return;
+    float* base = seg + (int64_t)blockIdx.y * P * rec + e;
+    float run = 0.f;
+    if (causal) {
+        for (int s = 0; s < P; ++s) {
+            const float x = base[(int64_t)s * rec];
+            base[(int64_t)s * rec] = run;
+            run += x;
+        }
+    } else {
+        for (int s = 0; s < P; ++s) run += base[(int64_t)s * rec];
+        base[0] = run;
+    }
+}
+
+gma_status_t launch_prep(const Plan& pl, const float* mu, const float* rv, const float* pr, char* ws, hipStream_t s) {
+    PrepArgs pa;
+    pa.mu = mu;
+    pa.raw_var = rv;
+    pa.prior = pr;
+    pa.ab = ws + pl.off_ab;
+    pa.cvec = reinterpret_cast<float*>(ws + pl.off_c);
+    pa.H = (int)pl.H;
+    pa.K = pl.K;
+    pa.d_r = pl.d_r;
+    return timed_launch(K_PREP, s, [&] { pl.cls->prep(pa, (int)pl.H, s); });
+}
+
+MainArgs base_args(const Plan& pl, char* ws) {
+    MainArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.ab = ws + pl.off_ab;
+    a.cvec = reinterpret_cast<const float*>(ws + pl.off_c);
+    a.seg = reinterpret_cast<float*>(ws + pl.off_seg);
+    a.N = pl.N;
+    a.H = (int)pl.H;
+    a.P = pl.P;
+    a.d_r = pl.d_r;
+    a.d_v = pl.d_v;
+    a.K = pl.K;
+    a.seg_chunks = pl.seg_chunks;
+    a.eps = pl.eps;
+    return a;
+}
+
+int vec_ok(const void* ptr, int d, bool f32) {
+    const int vec = f32 ? 4 : 8;  // elements per 16 bytes
+    return (d % vec == 0) && !misaligned(ptr, 16);
+}
+
+int vec_o_ok(const void* ptr, int d, bool f32) {
+    return (d % 4 == 0) && !misaligned(ptr, f32 ? 16 : 8);
+}
+
+gma_status_t check_common(const gma_problem_t* p, const void* const* ptrs, int nptrs, void* ws, size_t ws_bytes,
+                          const Plan& pl) {
+    for (int i = 0; i < nptrs; ++i)
+        if (!ptrs[i]) return fail(GMA_ERROR_INVALID_VALUE, "pointer argument %d is NULL", i);
+    if (ws_bytes < pl.total)
+        return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                    ws_bytes, pl.total);
+    if (pl.total > 0 && !ws) return fail(GMA_ERROR_INVALID_VALUE, "workspace is NULL");
+    if (ws && misaligned(ws, 16)) return fail(GMA_ERROR_INVALID_VALUE, "workspace must be 16-byte aligned");
+    (void)p;
+    return GMA_SUCCESS;
+}
+
+gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const void* kx, const void* v,
+                     const float* mu, const float* rv, const float* pr, void* o, void* ws, size_t ws_bytes,
+                     void* stream) {
+    g_last_error.clear();
+    Plan pl;
+    gma_status_t st = make_plan(p, causal ? GMA_OP_FORWARD_CAUSAL : GMA_OP_FORWARD_BIDIR, &pl);
+    if (st != GMA_SUCCESS) return st;
+    const void* ptrs[] = {qx, kx, v, mu, rv, pr, o};
+    st = check_common(p, ptrs, 7, ws, ws_bytes, pl);
+    if (st != GMA_SUCCESS) return st;
+    const size_t es = pl.f32 ? 4 : 2;
+    for (const void* ptr : {qx, kx, v, (const void*)o})
+        if (misaligned(ptr, es)) return fail(GMA_ERROR_INVALID_VALUE, "tensor pointers must be %zu-byte aligned", es);
+    for (const void* ptr : {(const void*)mu, (const void*)rv, (const void*)pr})
+        if (misaligned(ptr, 4)) return fail(GMA_ERROR_INVALID_VALUE, "parameter pointers must be 4-byte aligned");
+    const size_t nx = (size_t)(pl.B * pl.H * pl.N) * pl.d_r * es;
+    const size_t nv = (size_t)(pl.B * pl.H * pl.N) * pl.d_v * es;
+    if (overlaps(o, nv, qx, nx) || overlaps(o, nv, kx, nx) || overlaps(o, nv, v, nv))
+        return fail(GMA_ERROR_INVALID_VALUE, "o must not overlap qx, kx or v");
+    if (ws && (overlaps(ws, pl.total, qx, nx) || overlaps(ws, pl.total, kx, nx) ||
+               overlaps(ws, pl.total, v, nv) || overlaps(ws, pl.total, o, nv)))
+        return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* w = reinterpret_cast<char*>(ws);
+    st = launch_prep(pl, mu, rv, pr, w, s);
+    if (st != GMA_SUCCESS) return st;
+    MainArgs a = base_args(pl, w);
+    a.qx = qx;
+    a.kx = kx;
+    a.v = v;
+    a.o = o;
+    a.vec_x = vec_ok(qx, pl.d_r, pl.f32) && vec_ok(kx, pl.d_r, pl.f32);
+    a.vec_v = vec_ok(v, pl.d_v, pl.f32);
+    a.vec_o = vec_o_ok(o, pl.d_v, pl.f32);
+    const int grid = (int)(pl.B * pl.H * pl.P);
+    const int64_t rec = (int64_t)pl.cls->kc * pl.cls->vc + pl.cls->kc;
+    const bool need_agg = !causal || pl.P > 1;
+    if (need_agg) {
+        st = timed_launch(K_AGG, s, [&] { pl.cls->agg(a, grid, s); });
+        if (st != GMA_SUCCESS) return st;
+        if (pl.P > 1) {
+            st = timed_launch(K_SCAN, s, [&] {
+                hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), (unsigned)(pl.B * pl.H)), dim3(256),
+                                   0, s, a.seg, pl.P, rec, causal);
+            });
+            if (st != GMA_SUCCESS) return st;
+        }
+    }
+    if (causal) {
+        a.has_carry = pl.P > 1;
+        return timed_launch(K_OUT_CAUSAL, s, [&] { pl.cls->out_causal(a, grid, s); });
+    }
+    return timed_launch(K_OUT_BIDIR, s, [&] { pl.cls->out_bidir(a, grid, s); });
+}
+
+}  // namespace
+}  // namespace gma
+
+using namespace gma;
+
+extern "C" {
+
+size_t gma_workspace_size(const gma_problem_t* problem, int op) {
+    Plan pl;
+    if (make_plan(problem, op, &pl) != GMA_SUCCESS) return 0;
+    return pl.total;
+}
+
+gma_status_t gma_responsibilities(const gma_problem_t* p, const void* x, const float* mu, const float* raw_var,
+                                  const float* prior_logits, float* gamma, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    Plan pl;
+    gma_status_t st = make_plan(p, GMA_OP_RESPONSIBILITIES, &pl);
+    if (st != GMA_SUCCESS) return st;
+    const void* ptrs[] = {x, mu, raw_var, prior_logits, gamma};
+    st = check_common(p, ptrs, 5, ws, ws_bytes, pl);
+    if (st != GMA_SUCCESS) return st;
+    const size_t es = pl.f32 ? 4 : 2;
+    if (misaligned(x, es) || misaligned(gamma, 4) || misaligned(mu, 4) || misaligned(raw_var, 4) ||
+        misaligned(prior_logits, 4))
+        return fail(GMA_ERROR_INVALID_VALUE, "misaligned pointer");
+    const size_t nx = (size_t)(pl.B * pl.H * pl.N) * pl.d_r * es;
+    const size_t ng = (size_t)(pl.B * pl.H * pl.N) * pl.K * 4;
+    if (overlaps(gamma, ng, x, nx)) return fail(GMA_ERROR_INVALID_VALUE, "gamma must not overlap x");
+    if (ws && (overlaps(ws, pl.total, x, nx) || overlaps(ws, pl.total, gamma, ng)))
+        return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* w = reinterpret_cast<char*>(ws);
+    st = launch_prep(pl, mu, raw_var, prior_logits, w, s);
+    if (st != GMA_SUCCESS) return st;
+    MainArgs a = base_args(pl, w);
+    a.qx = x;
+    a.gamma = gamma;
+    a.vec_x = vec_ok(x, pl.d_r, pl.f32);
+    const int grid = (int)(pl.B * pl.H * pl.P);
+    return timed_launch(K_RESP, s, [&] { pl.cls->resp(a, grid, s); });
+}
+
+gma_status_t gma_forward_bidir(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,
+                               const float* raw_var, const float* prior_logits, void* o, void* ws, size_t ws_bytes,
+                               void* stream) {
+    return forward(p, 0, qx, kx, v, mu, raw_var, prior_logits, o, ws, ws_bytes, stream);
+}
+
+gma_status_t gma_forward_causal(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,
+                                const float* raw_var, const float* prior_logits, void* o, void* ws, size_t ws_bytes,
+                                void* stream) {
+    return forward(p, 1, qx, kx, v, mu, raw_var, prior_logits, o, ws, ws_bytes, stream);
+}
+
+const char* gma_status_string(gma_status_t s) {
+    switch (s) {
+        case GMA_SUCCESS: return "success";
+        case GMA_ERROR_INVALID_VALUE: return "invalid value";
+        case GMA_ERROR_NOT_SUPPORTED: return "not supported";
+        case GMA_ERROR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case GMA_ERROR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char* gma_last_error(void) { return g_last_error.c_str(); }
+
+gma_status_t gma_timing_enable(int enabled) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.enabled = enabled != 0;
+    return GMA_SUCCESS;
+}
+
+gma_status_t gma_timing_read(int kernel_id, double* total_ms, int64_t* launches) {
+    if (kernel_id < 0 || kernel_id >= K_COUNT || !total_ms || !launches)
+        return fail(GMA_ERROR_INVALID_VALUE, "bad timing query");
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> rec;
+    {
+        std::lock_guard<std::mutex> lk(g_timing.mu);
+        rec.swap(g_timing.recorded[kernel_id]);
+    }
+    double sum = 0.0;
+    gma_status_t st = GMA_SUCCESS;
+    for (auto& pr : rec) {
+        float ms = 0.f;
+        if (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess)
+            st = fail(GMA_ERROR_LAUNCH, "event query failed");
+        sum += ms;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_timing.mu);
+        for (auto& pr : rec) {
+            g_timing.pool.push_back(pr.first);
+            g_timing.pool.push_back(pr.second);
+        }
+    }
+    *total_ms = sum;
+    *launches = (int64_t)rec.size();
+    return st;
+}
+
+int gma_kernel_count(void) { return K_COUNT; }
+
+const char* gma_kernel_name(int kernel_id) {
+    return (kernel_id >= 0 && kernel_id < K_COUNT) ? kKernelNames[kernel_id] : "";
+}
+
+}  // extern "C"

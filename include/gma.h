@@ -1,0 +1,126 @@
+/*
+ * gma.h -- C ABI of libgma.so, the MI355X (gfx950) forward pass of Gaussian Mixture
+ * Attention (GMA).
+ *
+ * The operation (page "Attention par Mélange Gaussien (GMA)", gist.science paper
+ * 2606.18283, section "Méthodologie", sub-section "Mécanisme Central"):
+ *   item 1 "Routage Latent Probabiliste": for a routing vector x (a row of Q_X or K_X) the
+ *          responsibility gamma_k(x) = p(z = k | x) is the posterior of a K-component GMM with
+ *          means mu_k, diagonal covariances Sigma_k and mixing priors pi_k; rows of Gamma_Q and
+ *          Gamma_K (N x K) are these posteriors.  One mixture per head routes both Q and K.
+ *   item 2 "Routage de Mémoire Latente": write Vt = Gamma_K^T V (K x d_v), Z = Gamma_K^T 1 (K);
+ *          read O = Gamma_Q Vt / (Gamma_Q Z + eps), one scalar denominator per query row.
+ *          The N x N affinity Gamma_Q Gamma_K^T is never formed.
+ *   item 3 "Variantes et Entraînement": bidirectional and causal variants (causal: prefix sums
+ *          of Vt and Z, so O_i depends on j <= i only, the diagonal included); variances are
+ *          softplus(raw) and priors are softmax(prior logits).
+ *
+ * Conventions shared by every entry point
+ *   Layout     tensors are contiguous row-major: x, qx, kx [B, H, N, d_r]; v, o [B, H, N, d_v];
+ *              gamma [B, H, N, K]; mu, raw_var [H, K, d_r] (fp32); prior_logits [H, K] (fp32).
+ *              Parameters are the raw learned ones (softplus / softmax are applied inside).
+ *   Dtypes     GMA_DTYPE_F32: x, qx, kx, v and o are fp32; all arithmetic is fp32.
+ *              GMA_DTYPE_BF16: x, qx, kx, v and o are bf16; logits use fp16 matrix-core
+ *              operands, responsibilities / values / states use bf16 operands, every sum and
+ *              the softmax accumulate in fp32.  Domain of the bf16 path: |x| < 256 (x^2 must
+ *              fit fp16) and |mu| / sigma^2 < 40000.
+ *   Memory     every tensor pointer is a device pointer owned by the caller; the workspace is a
+ *              caller-owned device buffer of at least gma_workspace_size() bytes, 16-byte
+ *              aligned, whose contents need not be initialised and are clobbered.  The library
+ *              never allocates, frees or synchronises device memory.  o and gamma must not
+ *              overlap any input.
+ *   Streams    `stream` is a hipStream_t (NULL = the legacy default stream).  Every call only
+ *              enqueues kernels and returns; results are ready when the stream reaches them.
+ *   Errors     invalid arguments are reported by status code before any HIP call is made.
+ *              GMA_ERROR_LAUNCH reports a failed kernel launch.  gma_last_error() gives a
+ *              human-readable message for the last failing call on the calling thread.
+ *   Limits     1 <= d_r, K, d_v <= 256 with, per head, padded K * padded d_v <= 32768; B, H, N >= 1.
+ *              Shapes are padded internally to power-of-two tile classes; unsupported classes
+ *              return GMA_ERROR_NOT_SUPPORTED.
+ *   Results    deterministic: repeated calls give bitwise identical outputs (no atomics; every
+ *              reduction runs in a fixed order independent of the device).
+ */
+#ifndef GMA_H_
+#define GMA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GMA_DTYPE_F32 = 0, GMA_DTYPE_BF16 = 1 } gma_dtype_t;
+
+typedef enum {
+    GMA_SUCCESS = 0,
+    GMA_ERROR_INVALID_VALUE = 1,
+    GMA_ERROR_NOT_SUPPORTED = 2,
+    GMA_ERROR_WORKSPACE_TOO_SMALL = 3,
+    GMA_ERROR_LAUNCH = 4
+} gma_status_t;
+
+typedef enum {
+    GMA_OP_RESPONSIBILITIES = 0,
+    GMA_OP_FORWARD_BIDIR = 1,
+    GMA_OP_FORWARD_CAUSAL = 2
+} gma_op_t;
+
+/* Problem sizes.  eps >= 0 and finite; it is added to each row's denominator Gamma_Q Z. */
+typedef struct {
+    int64_t batch;     /* B */
+    int64_t heads;     /* H */
+    int64_t seq_len;   /* N */
+    int32_t d_route;   /* d_r: width of the routing projections Q_X, K_X */
+    int32_t n_comp;    /* K: number of Gaussian components */
+    int32_t d_value;   /* d_v: width of V and O */
+    int32_t dtype;     /* gma_dtype_t of x / qx / kx / v / o / (not gamma: always fp32) */
+    float eps;
+} gma_problem_t;
+
+/* Bytes of workspace `op` needs for `problem`; 0 if the problem is invalid or unsupported.
+ * Pure host computation. */
+size_t gma_workspace_size(const gma_problem_t* problem, int op);
+
+/* Responsibilities (item 1 above) of every row of x [B, H, N, d_r] under head h's mixture:
+ * gamma [B, H, N, K] fp32, each row non-negative and summing to 1. */
+gma_status_t gma_responsibilities(const gma_problem_t* problem, const void* x, const float* mu,
+                                  const float* raw_var, const float* prior_logits, float* gamma,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bidirectional forward (items 1-2): O = Gamma_Q (Gamma_K^T V) / (Gamma_Q (Gamma_K^T 1) + eps)
+ * over the whole sequence of each (b, h).  qx, kx [B, H, N, d_r]; v, o [B, H, N, d_v]. */
+gma_status_t gma_forward_bidir(const gma_problem_t* problem, const void* qx, const void* kx,
+                               const void* v, const float* mu, const float* raw_var,
+                               const float* prior_logits, void* o, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Causal forward (item 3): O_i = Gamma_Q[i] Vt_i / (Gamma_Q[i] . Z_i + eps) with
+ * Vt_i = sum_{j <= i} gamma_K[j] (x) v_j and Z_i = sum_{j <= i} gamma_K[j].  Same arguments as
+ * gma_forward_bidir. */
+gma_status_t gma_forward_causal(const gma_problem_t* problem, const void* qx, const void* kx,
+                                const void* v, const float* mu, const float* raw_var,
+                                const float* prior_logits, void* o, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* gma_status_string(gma_status_t status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* gma_last_error(void);
+
+/* Measurement support.  When enabled, every kernel launch is bracketed by a pair of HIP
+ * events recorded on the launch stream.  gma_timing_read() waits for the recorded events of
+ * kernel `kernel_id` (0 <= id < gma_kernel_count()), returns their summed elapsed time and
+ * launch count, and forgets them.  Disabled by default; enabling costs two event records per
+ * launch. */
+gma_status_t gma_timing_enable(int enabled);
+gma_status_t gma_timing_read(int kernel_id, double* total_ms, int64_t* launches);
+int gma_kernel_count(void);
+const char* gma_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMA_H_ */

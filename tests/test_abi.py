@@ -1,0 +1,137 @@
+"""C-ABI contract of libgma.so, checked on the CPU (no kernel is launched).
+
+Validation is pure host code that returns before any HIP call, so every error path is
+exercised here without a GPU.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gma.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gaussian_mixture_token_amd import _lib
+    if not os.path.exists(_lib.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gma_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gma_responsibilities", "gma_forward_bidir", "gma_forward_causal", "gma_workspace_size",
+              "gma_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _prob(**kw):
+    from gaussian_mixture_token_amd import _lib
+    d = dict(batch=1, heads=16, seq_len=65536, d_route=128, n_comp=128, d_value=128, dtype=1, eps=1e-6)
+    d.update(kw)
+    return _lib.Problem(**d)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, fn, prob, ws_bytes=1 << 40, **override):
+    args = dict(qx=FAKE, kx=ctypes.c_void_p(0x20000000), v=ctypes.c_void_p(0x40000000), mu=FAKE, rv=FAKE, pl=FAKE,
+                o=ctypes.c_void_p(0x80000000000), ws=ctypes.c_void_p(0x100000000000))
+    args.update(override)
+    return getattr(lib, fn)(ctypes.byref(prob), args["qx"], args["kx"], args["v"], args["mu"], args["rv"], args["pl"],
+                            args["o"], args["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["gma_forward_bidir", "gma_forward_causal"])
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, 1), ("heads", -1, 1), ("seq_len", 0, 1), ("d_route", 0, 1), ("n_comp", 0, 1),
+    ("d_value", 0, 1), ("dtype", 7, 1), ("eps", -1.0, 1), ("eps", float("nan"), 1), ("eps", float("inf"), 1),
+    ("n_comp", 257, 2), ("d_route", 300, 2), ("d_value", 257, 2),
+])
+def test_invalid_problem_rejected(lib, fn, field, value, status):
+    assert _fwd(lib, fn, _prob(**{field: value})) == status
+    assert lib.gma_last_error()
+
+
+@pytest.mark.parametrize("fn", ["gma_forward_bidir", "gma_forward_causal"])
+def test_null_pointers_rejected(lib, fn):
+    for name in ("qx", "kx", "v", "mu", "rv", "pl", "o"):
+        assert _fwd(lib, fn, _prob(), **{name: None}) == 1, name
+
+
+@pytest.mark.parametrize("fn", ["gma_forward_bidir", "gma_forward_causal"])
+def test_workspace_too_small_and_null(lib, fn):
+    prob = _prob()
+    need = lib.gma_workspace_size(ctypes.byref(prob), 2 if fn.endswith("causal") else 1)
+    assert need > 0
+    assert _fwd(lib, fn, prob, ws_bytes=need - 1) == 3
+    assert _fwd(lib, fn, prob, ws_bytes=need, ws=None) == 1
+
+
+def test_misaligned_and_aliasing_rejected(lib):
+    prob = _prob()
+    assert _fwd(lib, "gma_forward_causal", prob, qx=ctypes.c_void_p(0x10001)) == 1        # odd address for bf16
+    assert _fwd(lib, "gma_forward_causal", prob, ws=ctypes.c_void_p(0x100000000008)) == 1  # workspace not 16-B aligned
+    assert _fwd(lib, "gma_forward_causal", prob, o=ctypes.c_void_p(0x40000000)) == 1       # o aliases v
+
+
+def test_null_problem_and_bad_op(lib):
+    assert lib.gma_workspace_size(None, 2) == 0
+    assert lib.gma_workspace_size(ctypes.byref(_prob()), 9) == 0
+    assert lib.gma_forward_causal(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+
+
+def test_responsibilities_validation(lib):
+    prob = _prob(d_value=1)
+    f = lib.gma_responsibilities
+    assert f(ctypes.byref(prob), None, FAKE, FAKE, FAKE, ctypes.c_void_p(0x80000000000), FAKE, 1 << 40, None) == 1
+    assert f(ctypes.byref(_prob(n_comp=0)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    need = lib.gma_workspace_size(ctypes.byref(prob), 0)
+    assert need > 0
+    assert f(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x80000000000),
+             ctypes.c_void_p(0x100000000000), need - 1, None) == 3
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.gma_status_string(s)
+    assert lib.gma_kernel_count() >= 5
+    assert lib.gma_kernel_name(0) and lib.gma_kernel_name(999) == b""
+
+
+def test_workspace_is_linear_memory_not_quadratic(lib):
+    # The N x N affinity is never formed (page "Attention par Mélange Gaussien (GMA)",
+    # "Mécanisme Central" item 2): workspace depends on the segment count and K x d_v only.
+    sizes = [lib.gma_workspace_size(ctypes.byref(_prob(seq_len=n)), 2) for n in (1 << 14, 1 << 17, 1 << 20)]
+    assert sizes[0] > 0
+    assert sizes[2] == sizes[1] == sizes[0]  # segment count saturates; no N-dependence at all beyond it
+    per_head_state = (128 * 128 + 128) * 4
+    assert sizes[2] < 64 * 16 * per_head_state + (1 << 22)
+    # the bidirectional read never needs more than one [Vt | Z] per segment either
+    assert lib.gma_workspace_size(ctypes.byref(_prob(seq_len=1 << 20)), 1) == sizes[2]
+
+
+def test_small_causal_problem_needs_no_segment_records(lib):
+    # one segment per head: no carried state, workspace holds only the prepared parameters
+    small = lib.gma_workspace_size(ctypes.byref(_prob(seq_len=64, heads=1024)), 2)
+    big = lib.gma_workspace_size(ctypes.byref(_prob(seq_len=64, heads=1024)), 1)
+    assert 0 < small < big

@@ -1,0 +1,215 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Tolerance (from the method's precision contract): max |O_gpu - O_ref| / max |O_ref| <= 1e-4
+for fp32 storage and <= 1e-2 for bf16 storage with fp32 accumulation.  Responsibilities:
+max |Gamma_gpu - Gamma_ref| <= 1e-4 (fp32) / 1e-2 (bf16), an absolute bound on probabilities.
+
+Inputs come from gaussian_mixture_token_amd.workloads (seeded; shapes of the five workloads).
+Full-size workloads that the oracle cannot finish in seconds are compared on sampled heads:
+(batch, head) slices are independent, so the oracle on a slice is exact for that slice.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.conftest import gpu_available
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module")
+def gma():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import gaussian_mixture_token_amd as g
+    from gaussian_mixture_token_amd import _lib
+    _lib.load()
+    oracle.build(force=False)
+    return g
+
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def gpu_forward(g, w, inp, causal=None, **kw):
+    causal = w.causal if causal is None else causal
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    o = g.forward(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps, causal=causal, **kw)
+    torch.cuda.synchronize()
+    return o
+
+
+def ref_forward(w, inp, causal=None):
+    causal = w.causal if causal is None else causal
+    return oracle.forward(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"], inp["prior_logits"],
+                          eps=w.eps, causal=causal)
+
+
+def rel_err(o, ref):
+    o = o.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(o) else o
+    return float(np.abs(o - ref).max() / np.abs(ref).max())
+
+
+# ------------------------------------------------------------------------------------ responsibilities
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_responsibilities_match_oracle(gma, cfg):
+    w = gma.workload(cfg)
+    w = w.with_(batch=1, heads=min(w.heads, 2), seq_len=min(w.seq_len, 1000))
+    say("responsibilities cfg%d %s" % (cfg, w))
+    inp = gma.make_inputs(w)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    gq = gma.responsibilities(t["qx"], t["mu"], t["raw_var"], t["prior_logits"])
+    torch.cuda.synchronize()
+    ref = oracle.responsibilities(inp["qx"], inp["mu"], inp["raw_var"], inp["prior_logits"])
+    got = gq.cpu().numpy().astype(np.float64)
+    assert (got >= 0).all()
+    np.testing.assert_allclose(got.sum(-1), 1.0, atol=1e-5)
+    err = np.abs(got - ref).max()
+    say("  max |dGamma| = %.3e" % err)
+    assert err <= TOL[w.dtype]
+
+
+# ------------------------------------------------------------------------------------ forward parity
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_full_size_fp32(gma, cfg, causal):
+    w = gma.workload(cfg)
+    say("forward cfg%d causal=%s %s" % (cfg, causal, w))
+    inp = gma.make_inputs(w)
+    err = rel_err(gpu_forward(gma, w, inp, causal), ref_forward(w, inp, causal))
+    say("  rel err %.3e" % err)
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_cfg2_full_size_sampled_slices(gma, causal):
+    # B=32, H=8, N=4096: the GPU runs everything; the oracle checks 3 (batch, head) slices.
+    w = gma.workload(2)
+    say("forward cfg2 causal=%s %s" % (causal, w))
+    inp = gma.make_inputs(w)
+    o = gpu_forward(gma, w, inp, causal).float().cpu()
+    for b, h in ((0, 0), (17, 3), (31, 7)):
+        sl = {k: inp[k][b:b + 1, h:h + 1] for k in ("qx", "kx", "v")}
+        sl.update({k: inp[k][h:h + 1] for k in ("mu", "raw_var", "prior_logits")})
+        err = rel_err(o[b:b + 1, h:h + 1], ref_forward(w, sl, causal))
+        say("  slice b=%d h=%d rel err %.3e" % (b, h, err))
+        assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("cfg,N", [(3, 5000), (4, 3001)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_bf16_reduced_length_all_heads(gma, cfg, N, causal):
+    # all heads, many segments per head and a ragged last chunk
+    w = gma.workload(cfg, seq_len=N)
+    say("forward cfg%d N=%d causal=%s" % (cfg, N, causal))
+    inp = gma.make_inputs(w)
+    err = rel_err(gpu_forward(gma, w, inp, causal), ref_forward(w, inp, causal))
+    say("  rel err %.3e" % err)
+    assert err <= TOL[w.dtype]
+
+
+def test_forward_cfg3_full_size_sampled_heads(gma):
+    w = gma.workload(3)
+    say("forward cfg3 full size %s" % (w,))
+    inp = gma.make_inputs(w)
+    o = gpu_forward(gma, w, inp).float().cpu()
+    heads = [0, 11]
+    sub = gma.make_inputs(w, heads=heads)
+    ref = ref_forward(w, sub)
+    for j, h in enumerate(heads):
+        err = rel_err(o[:, h:h + 1], ref[:, j:j + 1])
+        say("  head %d rel err %.3e" % (h, err))
+        assert err <= TOL[w.dtype]
+
+
+def test_forward_cfg4_full_size_one_head(gma):
+    w = gma.workload(4)
+    say("forward cfg4 full size %s" % (w,))
+    inp = gma.make_inputs(w)
+    o = gpu_forward(gma, w, inp).float().cpu()
+    del inp
+    sub = gma.make_inputs(w, heads=[5])
+    ref = ref_forward(w, sub)
+    err = rel_err(o[:, 5:6], ref)
+    say("  head 5 rel err %.3e" % err)
+    assert err <= TOL[w.dtype]
+
+
+# ------------------------------------------------------------------------------------ edge cases
+
+
+@pytest.mark.parametrize("base", [0, 3])
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 257, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tails_and_tiny_lengths(gma, base, N, causal):
+    w = gma.workload(base, batch=1, heads=3 if base else 1, seq_len=N)
+    inp = gma.make_inputs(w)
+    err = rel_err(gpu_forward(gma, w, inp, causal), ref_forward(w, inp, causal))
+    assert err <= TOL[w.dtype], err
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bitwise_deterministic(gma, causal):
+    w = gma.workload(3, seq_len=20000)
+    inp = gma.make_inputs(w)
+    a = gpu_forward(gma, w, inp, causal)
+    b = gpu_forward(gma, w, inp, causal)
+    assert torch.equal(a, b)
+
+
+def test_causal_output_ignores_future_tokens_bitwise(gma):
+    w = gma.workload(3, heads=2, seq_len=9000)
+    inp = gma.make_inputs(w)
+    o = gpu_forward(gma, w, inp)
+    gen = torch.Generator().manual_seed(123)
+    for i in (0, 100, 4099, 8000):
+        pert = dict(inp)
+        for k in ("qx", "kx", "v"):
+            x = inp[k].clone()
+            x[:, :, i + 1:] = (3.0 * torch.randn(x[:, :, i + 1:].shape, generator=gen)).to(x.dtype)
+            pert[k] = x
+        o2 = gpu_forward(gma, w, pert)
+        assert torch.equal(o2[:, :, : i + 1], o[:, :, : i + 1]), i
+        assert not torch.equal(o2[:, :, i + 1:], o[:, :, i + 1:])
+
+
+def test_causal_last_row_equals_bidirectional(gma):
+    w = gma.workload(1, heads=2, batch=1)
+    inp = gma.make_inputs(w)
+    oc = gpu_forward(gma, w, inp, True).double().cpu()
+    ob = gpu_forward(gma, w, inp, False).double().cpu()
+    err = (oc[:, :, -1] - ob[:, :, -1]).abs().max() / ob.abs().max()
+    assert err <= 1e-5
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_poisoned_workspace_and_guard_bands(gma, causal):
+    # a NaN-filled workspace must be fully overwritten before it is read; writes stay inside O
+    w = gma.workload(3, seq_len=6000, heads=4)
+    inp = gma.make_inputs(w)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    prob = gma.problem(w.batch, w.heads, w.seq_len, w.d_route, w.n_comp, w.d_value, torch.bfloat16, w.eps)
+    nws = gma.workspace_size(prob, 2 if causal else 1)
+    ws = torch.full((nws // 4 + 1,), float("nan"), dtype=torch.float32, device=DEV)
+    numel = w.batch * w.heads * w.seq_len * w.d_value
+    guard = 4096
+    buf = torch.full((numel + 2 * guard,), 4096.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[guard:guard + numel].view(w.batch, w.heads, w.seq_len, w.d_value)
+    gma.forward(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps, causal=causal,
+                out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    assert (buf[:guard] == 4096.0).all() and (buf[guard + numel:] == 4096.0).all()
+    err = rel_err(out, ref_forward(w, inp, causal))
+    assert err <= TOL[w.dtype]
