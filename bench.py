@@ -81,6 +81,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) and exit; "
+                         "its FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
@@ -91,8 +94,17 @@ def main():
     import gaussian_mixture_token_amd as gma
     from gaussian_mixture_token_amd import _lib
 
-    lib = _lib.load()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(max(args.steps, 1)):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": x.numel() * 4, "copy_calibration_bytes_written": y.numel() * 4,
+                          "launches": max(args.steps, 1)}), flush=True)
+        return
+    lib = _lib.load()
     w = gma.workload(args.workload)
     print("bench: workload %s" % w.name, file=sys.stderr, flush=True)
     inp = gma.make_inputs(w)

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,17 +35,67 @@ def sources():
     return out
 
 
+RESOURCE_REMARK = "-Rpass-analysis=kernel-resource-usage"
+
+
+def _check_resources(src: str, remarks: str) -> None:
+    """Every kernel must run without register spills or scratch memory: the DMA-staged kernels
+    count their outstanding vector-memory operations exactly (s_waitcnt vmcnt(N)), and a spill
+    would add scratch loads and stores to that count."""
+    cur = None
+    bad = []
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            continue
+        m = re.search(r"remark: (VGPRs Spill|SGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
+        if m and cur and int(m.group(2)) != 0:
+            bad.append("%s: %s = %s" % (cur, m.group(1), m.group(2)))
+    if bad:
+        raise RuntimeError("kernels in %s use scratch memory:\n  %s" % (src, "\n  ".join(bad)))
+
+
+def _check_store_counts(asm_path: str) -> int:
+    """The DMA output kernels wait with vmcnt(NSTORE) for the prefetch, which is exact only if each
+    chunk body issues exactly NSTORE = (d_v tiles per wave) x (token tiles) buffer stores."""
+    text = open(asm_path).read()
+    n_checked = 0
+    for m in re.finditer(r"^(_ZN3gma11main_kernelILb0ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi([23])ELb1ELi\d+EEEvNS_8MainArgsE):",
+                         text, re.M):
+        name, kc, vc, drc, w, c, mode = m.group(1), *map(int, m.groups()[1:])
+        body = text[m.end(): text.index("s_endpgm", m.end())]
+        stores = len(re.findall(r"^\s*buffer_store_dwordx2", body, re.M))
+        nstore = (vc // 16 // w) * (c // 16)
+        if stores != 2 * nstore:
+            raise RuntimeError("%s: %d buffer stores in the chunk loop, expected %d" % (name, stores, 2 * nstore))
+        n_checked += 1
+    return n_checked
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON_FLAGS + DEVICE_FLAGS + ["-c", src, "-o", obj]
+    extra = [RESOURCE_REMARK]
+    if src.endswith(".hip"):
+        extra += ["-save-temps=obj"]
+    cmd = [HIPCC] + COMMON_FLAGS + DEVICE_FLAGS + extra + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC, "-x", "hip"] + COMMON_FLAGS + DEVICE_FLAGS + ["-c", src, "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in r.stderr.splitlines() if "not a recognized feature" not in l)
+        cmd = [HIPCC, "-x", "hip"] + COMMON_FLAGS + DEVICE_FLAGS + extra + ["-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD_DIR)
+    lines = [l for l in r.stderr.splitlines() if "not a recognized feature" not in l]
+    remarks = "\n".join(l for l in lines if "kernel-resource-usage" in l)
+    err = "\n".join(l for l in lines if "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, err))
-    if err.strip():
-        sys.stderr.write(err + "\n")
+    warnings = [l for l in err.splitlines() if "warning:" in l]
+    if warnings:
+        sys.stderr.write("\n".join(warnings) + "\n")
+    _check_resources(src, remarks)
+    if src.endswith(".hip"):
+        base = os.path.splitext(os.path.basename(obj))[0]
+        for name in os.listdir(BUILD_DIR):
+            if name.startswith(base.replace(".hip", "")) and name.endswith("gfx950.s"):
+                _check_store_counts(os.path.join(BUILD_DIR, name))
     return obj
 
 

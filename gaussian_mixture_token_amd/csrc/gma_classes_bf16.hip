@@ -1,13 +1,14 @@
 // Compiled shape classes for bf16 storage (fp16 logits operands, bf16 contraction operands).
-// Columns: fp32?, padded K, padded d_v, padded d_r, wavefronts per workgroup, tokens per chunk.
+// Columns: padded K, padded d_v, padded d_r, wavefronts per workgroup, tokens per chunk,
+// wavefronts per SIMD the DMA kernels are register-budgeted for.
 #include "gma_registry.hpp"
 
 namespace gma {
 
 static const ShapeClass kClassesBf16[] = {
-    GMA_SHAPE_CLASS(false, 32, 64, 64, 2, 64),
-    GMA_SHAPE_CLASS(false, 128, 128, 128, 4, 64),
-    GMA_SHAPE_CLASS(false, 256, 64, 64, 4, 32),
+    GMA_SHAPE_CLASS_BF16(32, 64, 64, 2, 32, 2),
+    GMA_SHAPE_CLASS_BF16(128, 128, 128, 4, 32, 2),
+    GMA_SHAPE_CLASS_BF16(256, 64, 64, 4, 32, 1),
 };
 
 const ShapeClass* classes_bf16(int* count) {

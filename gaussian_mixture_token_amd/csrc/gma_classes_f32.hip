@@ -1,12 +1,12 @@
 // Compiled shape classes for fp32 storage and arithmetic.
-// Columns: fp32?, padded K, padded d_v, padded d_r, wavefronts per workgroup, tokens per chunk.
+// Columns: padded K, padded d_v, padded d_r, wavefronts per workgroup, tokens per chunk.
 #include "gma_registry.hpp"
 
 namespace gma {
 
 static const ShapeClass kClassesF32[] = {
-    GMA_SHAPE_CLASS(true, 16, 16, 16, 1, 64),
-    GMA_SHAPE_CLASS(true, 64, 64, 64, 4, 64),
+    GMA_SHAPE_CLASS_F32(16, 16, 16, 1, 64),
+    GMA_SHAPE_CLASS_F32(64, 64, 64, 4, 64),
 };
 
 const ShapeClass* classes_f32(int* count) {

@@ -46,6 +46,9 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
+// x rounded to the nearest bf16 value, returned as fp32
+__device__ __forceinline__ float round_bf16(float x) { return __uint_as_float((uint32_t)bf16_bits(x) << 16); }
+
 // Two accumulator tiles -> one bf16 operand fragment whose contraction slots are
 // (tile lo rows 4g..4g+3, tile hi rows 4g..4g+3).
 __device__ __forceinline__ bf16x8 pack_pair(const f32x4& lo, const f32x4& hi) {
@@ -84,5 +87,102 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// v_rcp_f32 (about 1 ulp)
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ---- bf16 -> fp16 (8 values).  Exact for every bf16 value whose magnitude lies in the fp16
+// normal range: bf16 carries 8 significant bits, fp16 11, so the round-toward-zero pack
+// conversion never rounds there.
+__device__ __forceinline__ f16x8 bf16x8_bits_to_f16x8(const u32x4& r) {
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const auto p = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(r[e] << 16), __uint_as_float(r[e] & 0xffff0000u));
+        h[2 * e] = p[0];
+        h[2 * e + 1] = p[1];
+    }
+    return h;
+}
+
+// ---- buffer descriptors, LDS DMA, transposed LDS reads, bounds-checked stores
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define GMA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + bytes): loads past the end return 0, stores are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The same descriptor as four scalar dwords (base, stride 0, byte count, gfx9 format word), for
+// the inline-assembly DMA below.
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane from global (base + soff + voff) into LDS at lds + 16 * lane (1 KiB per
+// wave): buffer_load_dwordx4 ... lds.  Issued from inline assembly so that the compiler does not
+// track the LDS write: the kernels wait for it explicitly (wait_vmcnt + barrier) before reading
+// the buffer, and an implicit wait would otherwise serialise the prefetch with the compute of
+// the current chunk.  M0 (the LDS destination) is saved and restored around the load.
+__device__ __forceinline__ void dma16(const i32x4& rs, char* lds, uint32_t voff, uint32_t soff) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)GMA_LDS(lds)));
+    i32x4 srs;
+    srs[0] = __builtin_amdgcn_readfirstlane(rs[0]);
+    srs[1] = __builtin_amdgcn_readfirstlane(rs[1]);
+    srs[2] = __builtin_amdgcn_readfirstlane(rs[2]);
+    srs[3] = __builtin_amdgcn_readfirstlane(rs[3]);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(dst), "v"(voff), "s"(srs), "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory");
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane r receives element (r % 4) of the 8-byte
+// rows addressed by lanes 4i + r/4 of its group, i = 0..3 (a 4 x 16 transpose).
+__device__ __forceinline__ u32x2 ds_read_tr16(const char* lds) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(GMA_LDS(lds)));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ void store_b64(__amdgpu_buffer_rsrc_t rs, u32x2 v, uint32_t voff) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, rs, voff, 0, 0);
+}
+
+// ---- explicit waits and barriers.  A plain __syncthreads() would also wait for the LDS DMA
+// prefetch in flight; these wait only for what they name.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]; lgkmcnt 0
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | (((N >> 4) & 3) << 14));
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS writes of this wave complete, then barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    block_barrier();
+}
 
 }  // namespace gma

@@ -31,10 +31,11 @@ gma_status_t fail(gma_status_t st, const char* fmt, ...) {
     return st;
 }
 
-// Workgroups the segment split aims for: two per compute unit of a 256-CU MI355X.  A fixed
-// constant (not a device query) keeps the decomposition, and therefore every result bit,
-// independent of the device and of the HIP runtime state.
-constexpr int64_t kTargetWorkgroups = 512;
+// The segment split aims for one full round of workgroups on a 256-CU MI355X: 256 x the
+// workgroups per CU that the shape class's LDS and register budgets allow.  A fixed constant
+// (not a device query) keeps the decomposition, and therefore every result bit, independent of
+// the device and of the HIP runtime state.
+constexpr int64_t kComputeUnits = 256;
 
 int next_pow2(int x) {
     int p = 1;
@@ -55,6 +56,7 @@ struct Plan {
     int64_t n_chunks = 0;
     int P = 1;
     int seg_chunks = 1;
+    bool dma = false;
     size_t off_ab = 0, off_c = 0, off_seg = 0, total = 0;
 };
 
@@ -117,7 +119,8 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan) {
         plan->P = (int)std::min<int64_t>(plan->n_chunks, INT32_MAX / 4);
         plan->seg_chunks = (int)((plan->n_chunks + plan->P - 1) / plan->P);
     } else {
-        int64_t P = (kTargetWorkgroups + BH - 1) / BH;
+        const int64_t target = kComputeUnits * plan->cls->wg_per_cu;
+        int64_t P = (target + BH - 1) / BH;
         if (P > plan->n_chunks) P = plan->n_chunks;
         if (P < 1) P = 1;
         const int64_t sc = (plan->n_chunks + P - 1) / P;
@@ -204,11 +207,13 @@ __global__ void __launch_bounds__(256) scan_kernel(float* seg, int P, int64_t re
     float* base = seg + (int64_t)blockIdx.y * P * rec + e;
     float run = 0.f;
     if (causal) {
-        for (int s = 0; s < P; ++s) {
+        // the last segment's aggregate is never produced (nothing follows it)
+        for (int s = 0; s + 1 < P; ++s) {
             const float x = base[(int64_t)s * rec];
             base[(int64_t)s * rec] = run;
             run += x;
         }
+        base[(int64_t)(P - 1) * rec] = run;
     } else {
         for (int s = 0; s < P; ++s) run += base[(int64_t)s * rec];
         base[0] = run;
@@ -237,6 +242,7 @@ MainArgs base_args(const Plan& pl, char* ws) {
     a.N = pl.N;
     a.H = (int)pl.H;
     a.P = pl.P;
+    a.Pg = pl.P;
     a.d_r = pl.d_r;
     a.d_v = pl.d_v;
     a.K = pl.K;
@@ -302,11 +308,22 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
     a.vec_x = vec_ok(qx, pl.d_r, pl.f32) && vec_ok(kx, pl.d_r, pl.f32);
     a.vec_v = vec_ok(v, pl.d_v, pl.f32);
     a.vec_o = vec_o_ok(o, pl.d_v, pl.f32);
+    // LDS-DMA staging: bf16, 16-byte rows chunks, aligned bases, 31-bit byte offsets per slice
+    const bool dma = !pl.f32 && pl.cls->dma_out_causal && pl.d_r % 8 == 0 && pl.d_v % 8 == 0 &&
+                     !misaligned(qx, 16) && !misaligned(kx, 16) && !misaligned(v, 16) && !misaligned(o, 16) &&
+                     pl.N * std::max(pl.d_r, pl.d_v) * 2 < (int64_t(1) << 31);
+    const main_launch_t f_agg = dma ? pl.cls->dma_agg : pl.cls->agg;
+    const main_launch_t f_causal = dma ? pl.cls->dma_out_causal : pl.cls->out_causal;
+    const main_launch_t f_bidir = dma ? pl.cls->dma_out_bidir : pl.cls->out_bidir;
     const int grid = (int)(pl.B * pl.H * pl.P);
     const int64_t rec = (int64_t)pl.cls->kc * pl.cls->vc + pl.cls->kc;
     const bool need_agg = !causal || pl.P > 1;
     if (need_agg) {
-        st = timed_launch(K_AGG, s, [&] { pl.cls->agg(a, grid, s); });
+        // causal: the last segment's aggregate is not needed by anyone
+        MainArgs ag = a;
+        ag.Pg = causal ? pl.P - 1 : pl.P;
+        const int agrid = (int)(pl.B * pl.H * ag.Pg);
+        st = timed_launch(K_AGG, s, [&] { f_agg(ag, agrid, s); });
         if (st != GMA_SUCCESS) return st;
         if (pl.P > 1) {
             st = timed_launch(K_SCAN, s, [&] {
@@ -318,9 +335,9 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
     }
     if (causal) {
         a.has_carry = pl.P > 1;
-        return timed_launch(K_OUT_CAUSAL, s, [&] { pl.cls->out_causal(a, grid, s); });
+        return timed_launch(K_OUT_CAUSAL, s, [&] { f_causal(a, grid, s); });
     }
-    return timed_launch(K_OUT_BIDIR, s, [&] { pl.cls->out_bidir(a, grid, s); });
+    return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, grid, s); });
 }
 
 }  // namespace
@@ -362,8 +379,11 @@ gma_status_t gma_responsibilities(const gma_problem_t* p, const void* x, const f
     a.qx = x;
     a.gamma = gamma;
     a.vec_x = vec_ok(x, pl.d_r, pl.f32);
+    const bool dma = !pl.f32 && pl.cls->dma_resp && pl.d_r % 8 == 0 && !misaligned(x, 16) &&
+                     pl.N * pl.d_r * 2 < (int64_t(1) << 31);
+    const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
     const int grid = (int)(pl.B * pl.H * pl.P);
-    return timed_launch(K_RESP, s, [&] { pl.cls->resp(a, grid, s); });
+    return timed_launch(K_RESP, s, [&] { f_resp(a, grid, s); });
 }
 
 gma_status_t gma_forward_bidir(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,

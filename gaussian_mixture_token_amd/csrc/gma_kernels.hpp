@@ -16,7 +16,7 @@
 //
 // Kernels:
 //   prep_kernel      raw parameters -> [a | b] operand fragments (fp16 or fp32) and c.
-//   main_kernel<..., MODE>
+//   main_kernel<..., MODE, DMA>
 //     MODE_RESP        Gamma of every row, written out in fp32.
 //     MODE_AGG         per sequence segment: [Vt | Z] = sum over the segment of gamma_K (x) [v | 1].
 //     MODE_OUT_BIDIR   O = Gamma_Q Vt / (Gamma_Q Z + eps) with the whole-sequence [Vt | Z].
@@ -32,7 +32,17 @@
 // contraction phase splits d_v across waves (each wave owns state columns for all K
 // components).  Gamma moves between the two splits through LDS as ready-made operand
 // fragments.
+//
+// Input staging.  DMA = true (bf16 with 8-aligned widths): chunk c+1 is fetched straight from
+// HBM into the second half of a double-buffered LDS area (buffer_load_dwordx4 ... lds, 1 KiB per
+// instruction, bounds-checked by the buffer descriptor so rows past N read as zeros) while chunk
+// c is computed.  X is laid out in MFMA-fragment order (each 1 KiB block is one operand
+// fragment); V is kept row-major with a 16-byte-chunk XOR swizzle and read as transposed
+// operand fragments with ds_read_b64_tr_b16.  DMA = false: synchronous staging through
+// registers (fp32 path and unaligned shapes).
 #pragma once
+#include <type_traits>
+
 #include "gma_device.hpp"
 
 namespace gma {
@@ -56,7 +66,7 @@ template <> struct Tr<false> {
     static constexpr int KS = 32;
     static constexpr int ES = 2;
     static constexpr int XES = 2;   // staged X in fp16
-    static constexpr int GES = 2;   // staged Gamma / V in bf16
+    static constexpr int GES = 2;   // staged Gamma / V element in bf16
 };
 
 struct MainArgs {
@@ -69,10 +79,12 @@ struct MainArgs {
     const float* cvec;     // [H, KC]
     float* seg;            // [BH, P, KC*VC + KC]
     int64_t N;
-    int H, P;
+    int H;
+    int P;                 // segments per head (record stride)
+    int Pg;                // segments per head launched by this grid (P, or P - 1 for causal aggregates)
     int d_r, d_v, K;
     int seg_chunks;        // chunks of C tokens per segment
-    int vec_x, vec_v, vec_o;  // 16-byte (x, v) / 4-element (o) vector access allowed
+    int vec_x, vec_v, vec_o;  // 16-byte (x, v) / 4-element (o) vector access allowed (register staging)
     int has_carry;         // causal: load the carried state (P > 1)
     float eps;
 };
@@ -88,10 +100,12 @@ struct PrepArgs {
 
 // ---------------------------------------------------------------------------------------------
 // prep: softplus variances, log-softmax priors, expanded-quadratic coefficients.
-// One workgroup per head.  [a | b] is written in the exact per-lane fragment order the main
-// kernel loads: ab[h][ct][ks][lane][j] = A[comp = 16 ct + lane % 16][k = ks*KS + (lane/16)*(KS/4) + j]
+// Grid (H, KC/16): one workgroup per 16 components of a head.  [a | b] is written in the exact
+// per-lane fragment order the main kernel loads:
+//   ab[h][ct][ks][lane][j] = A[comp = 16 ct + lane % 16][k = ks*KS + (lane/16)*(KS/4) + j]
 // with A = [a | b] (k < DRC: a_{comp,k}; k >= DRC: b_{comp,k-DRC}).  Pad components get
 // a = b = 0 and c = -inf (their posterior is exactly 0); pad dimensions get a = b = 0.
+// Arithmetic in fp64; the sum over d of each c_k runs in a fixed order.
 template <bool F32, int KC, int DRC>
 __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
     using T = Tr<F32>;
@@ -99,10 +113,11 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
     constexpr int NKS = 2 * DRC / KS;
     constexpr int EPL = KS / 4;  // elements per lane per fragment
     const int h = blockIdx.x;
+    const int ct = blockIdx.y;
     const int tid = threadIdx.x;
     const double LOG2E = 1.4426950408889634073599246810019;
     __shared__ double s_red[256];
-    __shared__ double s_lse;
+    __shared__ double s_t[16][DRC];
 
     // log-sum-exp of the prior logits of this head
     double m = -INFINITY;
@@ -123,57 +138,56 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
         if (tid < s) s_red[tid] += s_red[tid + s];
         __syncthreads();
     }
-    if (tid == 0) s_lse = mx + log(s_red[0]);
-    __syncthreads();
-    const double lse = s_lse;
+    const double lse = mx + log(s_red[0]);
 
-    // c_k
-    for (int k = tid; k < KC; k += 256) {
-        float c = -INFINITY;
-        if (k < p.K) {
-            double sum = 0.0;
-            for (int d = 0; d < p.d_r; ++d) {
-                const int64_t i = ((int64_t)h * p.K + k) * p.d_r + d;
-                const double r = p.raw_var[i];
-                const double var = fmax(r, 0.0) + log1p(exp(-fabs(r)));
-                const double mu = p.mu[i];
-                sum += log(var) + mu * mu / var;
-            }
-            const double logpi = (double)p.prior[(int64_t)h * p.K + k] - lse;
-            c = (float)(LOG2E * (logpi - 0.5 * sum));
-        }
-        p.cvec[(int64_t)h * KC + k] = c;
-    }
-
-    // [a | b] fragments
-    constexpr int TOTAL = (KC / 16) * NKS * 64 * EPL;
-    for (int idx = tid; idx < TOTAL; idx += 256) {
-        const int j = idx % EPL;
-        const int lane = (idx / EPL) % 64;
-        const int ks = (idx / (EPL * 64)) % NKS;
-        const int ct = idx / (EPL * 64 * NKS);
-        const int comp = ct * 16 + (lane & 15);
-        const int kk = ks * KS + (lane >> 4) * EPL + j;
-        const bool is_b = kk >= DRC;
-        const int d = is_b ? kk - DRC : kk;
-        double val = 0.0;
+    // a, b and the per-dimension terms of c for the 16 components of this tile
+    for (int e = tid; e < 16 * DRC; e += 256) {
+        const int cl = e / DRC;
+        const int d = e % DRC;
+        const int comp = ct * 16 + cl;
+        double a = 0.0, b = 0.0, t = 0.0;
         if (comp < p.K && d < p.d_r) {
             const int64_t i = ((int64_t)h * p.K + comp) * p.d_r + d;
             const double r = p.raw_var[i];
-            const double var = fmax(r, 0.0) + log1p(exp(-fabs(r)));
-            val = is_b ? LOG2E * (double)p.mu[i] / var : -0.5 * LOG2E / var;
+            const double var = fmax(r, 0.0) + log1p(exp(-fabs(r)));   // softplus
+            const double mu = p.mu[i];
+            a = -0.5 * LOG2E / var;
+            b = LOG2E * mu / var;
+            t = log(var) + mu * mu / var;
         }
-        const int64_t out = (int64_t)h * TOTAL + idx;
-        if constexpr (F32) {
-            reinterpret_cast<float*>(p.ab)[out] = (float)val;
-        } else {
-            reinterpret_cast<_Float16*>(p.ab)[out] = (_Float16)(float)val;
+        s_t[cl][d] = t;
+        // fragment positions of k = d (a part) and k = DRC + d (b part)
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            const int kk = part * DRC + d;
+            const int ks = kk / KS;
+            const int lane = (comp & 15) + 16 * ((kk % KS) / EPL);
+            const int j = kk % EPL;
+            const int64_t idx = (((int64_t)h * (KC / 16) + ct) * NKS + ks) * 64 * EPL + lane * EPL + j;
+            const double val = part ? b : a;
+            if constexpr (F32) {
+                reinterpret_cast<float*>(p.ab)[idx] = (float)val;
+            } else {
+                reinterpret_cast<_Float16*>(p.ab)[idx] = (_Float16)(float)val;
+            }
         }
+    }
+    __syncthreads();
+    if (tid < 16) {
+        const int comp = ct * 16 + tid;
+        float c = -INFINITY;
+        if (comp < p.K) {
+            double sum = 0.0;
+            for (int d = 0; d < p.d_r; ++d) sum += s_t[tid][d];
+            const double logpi = (double)p.prior[(int64_t)h * p.K + comp] - lse;
+            c = (float)(LOG2E * (logpi - 0.5 * sum));
+        }
+        p.cvec[(int64_t)h * KC + comp] = c;
     }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Staging helpers (global -> LDS).
+// Synchronous staging helpers (global -> registers -> LDS).
 
 // X rows [C][DRC] -> LDS (fp16 for bf16 inputs, fp32 otherwise), zero-padded in d and in rows.
 template <bool F32, int C, int DRC, int NTHR>
@@ -210,12 +224,7 @@ __device__ __forceinline__ void stage_x(char* lds, const typename Tr<F32>::elem_
                     for (int e = 0; e < 4; ++e) raw[e] = (uint32_t)tmp[2 * e] | ((uint32_t)tmp[2 * e + 1] << 16);
                 }
             }
-            f16x8 h;
-            for (int e = 0; e < 4; ++e) {
-                h[2 * e] = (_Float16)bf16_bits_to_f32(raw[e] & 0xffffu);
-                h[2 * e + 1] = (_Float16)bf16_bits_to_f32(raw[e] >> 16);
-            }
-            *reinterpret_cast<f16x8*>(dst) = h;
+            *reinterpret_cast<f16x8*>(dst) = bf16x8_bits_to_f16x8(raw);
         }
     }
 }
@@ -279,9 +288,20 @@ __device__ __forceinline__ void stage_vt(char* lds, const typename Tr<F32>::elem
 }
 
 // ---------------------------------------------------------------------------------------------
-// Main kernel.  Grid: BH * P workgroups (segment-major inside a head); block: W wavefronts.
-template <bool F32, int KC, int VC, int DRC, int W, int C, int MODE>
-__global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
+// Main kernel.  Grid: BH * Pg workgroups (segment-major inside a head); block: W wavefronts.
+//
+// Per chunk of C tokens:
+//   B0  inputs in LDS (DMA: wait for this wave's prefetch, convert its X blocks bf16 -> fp16 in
+//       place, barrier, then start the prefetch of the next chunk)
+//       logits^T tiles of the wave's own components for Q and/or K (MFMA), local softmax
+//   B1  combine the per-wave (max, sum) pairs -> Gamma; Gamma_Q as operand fragments and
+//       Gamma_K as a row-major [token][component] bf16 tile into LDS; denominators over own
+//       components; Z update
+//   B2  contraction over the wave's own d_v tiles: O = (Gamma_Q Vt + tril(Gamma_Q Gamma_K^T) V) /
+//       (Gamma_Q Z + rowsum tril(..) + eps); state += Gamma_K^T [V | 1]
+template <bool F32, int KC, int VC, int DRC, int W, int C, int MODE, bool DMA, int WPE>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+main_kernel(const MainArgs a) {
     using T = Tr<F32>;
     using elem_t = typename T::elem_t;
     using xfrag_t = typename T::xfrag_t;
@@ -297,33 +317,60 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
     constexpr int NKS2 = NKS / 2;
     constexpr int NKQ = KC / KS;             // fragment steps over components
     constexpr int NTK = C / KS;              // fragment steps over tokens
-    constexpr int XS = DRC * T::XES + 16;    // staged X row stride (bytes)
-    constexpr int VTS = C * T::GES + 16;     // staged V^T row stride (bytes)
+    constexpr int XS = DRC * T::XES + 16;    // register-staged X row stride (bytes)
+    constexpr int VTS = C * T::GES + 16;     // register-staged V^T row stride (bytes)
     constexpr bool NEED_Q = (MODE == MODE_RESP) || (MODE == MODE_OUT_BIDIR) || (MODE == MODE_OUT_CAUSAL);
     constexpr bool NEED_K = (MODE == MODE_AGG) || (MODE == MODE_OUT_CAUSAL);
     constexpr bool NEED_V = NEED_K;
     constexpr bool HAS_STATE = (MODE != MODE_RESP);
+    constexpr bool OUT = (MODE == MODE_OUT_BIDIR) || (MODE == MODE_OUT_CAUSAL);
     static_assert(NCT % W == 0, "components must split evenly across waves");
     static_assert(MODE == MODE_RESP || NVT % W == 0, "d_v must split evenly across waves");
     static_assert(KC % KS == 0 && C % KS == 0 && (2 * DRC) % KS == 0, "tile shapes");
-    static_assert(F32 || KT_W % 2 == 0 || W >= 1, "");
+    static_assert(!DMA || !F32, "LDS DMA staging is the bf16 path");
 
-    __shared__ __attribute__((aligned(16))) char s_xq[NEED_Q ? C * XS : 16];
-    __shared__ __attribute__((aligned(16))) char s_xk[NEED_K ? C * XS : 16];
-    __shared__ __attribute__((aligned(16))) char s_vt[NEED_V ? VC * VTS : 16];
-    __shared__ __attribute__((aligned(16))) char s_gq[(MODE == MODE_OUT_BIDIR || MODE == MODE_OUT_CAUSAL) ? NT * NKQ * 1024 : 16];
-    __shared__ __attribute__((aligned(16))) char s_gk[(MODE == MODE_OUT_CAUSAL) ? NT * NKQ * 1024 : 16];
-    __shared__ __attribute__((aligned(16))) char s_gkc[NEED_K ? NCT * NTK * 1024 : 16];
+    // DMA layout of one staging buffer: [X_Q fragments][X_K fragments][V rows]
+    constexpr int XFRAG_BYTES = NT * NKS2 * 1024;
+    constexpr int VROW_BYTES = C * VC * 2;
+    constexpr int OFF_XQ = 0;
+    constexpr int OFF_XK = OFF_XQ + (NEED_Q ? XFRAG_BYTES : 0);
+    constexpr int OFF_V = OFF_XK + (NEED_K ? XFRAG_BYTES : 0);
+    constexpr int RAW_BYTES = OFF_V + (NEED_V ? VROW_BYTES : 0);
+    constexpr int CPR = VC / 8;              // 16-byte chunks per V row
+    constexpr int RPB = 1024 / (VC * 2);     // V rows per 1 KiB DMA block
+    constexpr int NF_X = NT * NKS2;
+    constexpr int NF_V = VROW_BYTES / 1024;
+    constexpr int NF_XALL = (NEED_Q ? NF_X : 0) + (NEED_K ? NF_X : 0);
+    constexpr int NF = NF_XALL + (NEED_V ? NF_V : 0);
+    // buffer stores per chunk per wave (unconditional, so the count is exact)
+    constexpr int NSTORE = OUT ? VT_W * NT : 0;
+    static_assert(!DMA || !NEED_V || (VROW_BYTES % 1024 == 0 && 1024 % (VC * 2) == 0), "V DMA blocks");
+    // Gamma_K tile in LDS: bf16 path row-major [token][component], rows padded by 32 bytes so that
+    // the 16 rows a transposed read touches fall in distinct banks within each half-wave and every
+    // address is affine in the component index; fp32 path as ready operand fragments (token rows,
+    // and component rows for the state update)
+    constexpr int GKR = KC * 2 + 32;         // bytes per Gamma_K row (bf16 path)
+    constexpr int GK_BYTES = NEED_K ? (F32 ? (NT * NKQ + NCT * NTK) * 1024 : C * GKR) : 16;
+
+    __shared__ __attribute__((aligned(16))) char s_raw0[DMA ? RAW_BYTES : 16];
+    __shared__ __attribute__((aligned(16))) char s_raw1[DMA ? RAW_BYTES : 16];
+    __shared__ __attribute__((aligned(16))) char s_xq[(!DMA && NEED_Q) ? C * XS : 16];
+    __shared__ __attribute__((aligned(16))) char s_xk[(!DMA && NEED_K) ? C * XS : 16];
+    __shared__ __attribute__((aligned(16))) char s_vt[(!DMA && NEED_V) ? VC * VTS : 16];
+    __shared__ __attribute__((aligned(16))) char s_gq[OUT ? NT * NKQ * 1024 : 16];
+    __shared__ __attribute__((aligned(16))) char s_gk[GK_BYTES];
     __shared__ float s_ms[2][W][C][2];
     __shared__ float s_den[W][C];
+    __shared__ __attribute__((aligned(16))) float s_c[KC];   // per-component logit constants c_k
+    __shared__ __attribute__((aligned(16))) float s_z[KC];   // running Z (each wave owns its components)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
     const int lr = lane & 15;
     const int lg = lane >> 4;
-    const int bh = blockIdx.x / a.P;
-    const int sidx = blockIdx.x % a.P;
+    const int bh = blockIdx.x / a.Pg;
+    const int sidx = blockIdx.x % a.Pg;
     const int h = bh % a.H;
     const int64_t N = a.N;
     const int64_t n_chunks = (N + C - 1) / C;
@@ -333,10 +380,54 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
     const elem_t* qx = reinterpret_cast<const elem_t*>(a.qx) + (int64_t)bh * N * a.d_r;
     const elem_t* kx = reinterpret_cast<const elem_t*>(a.kx) + (int64_t)bh * N * a.d_r;
     const elem_t* vv = reinterpret_cast<const elem_t*>(a.v) + (int64_t)bh * N * a.d_v;
+    elem_t* oo = reinterpret_cast<elem_t*>(a.o) + (int64_t)bh * N * a.d_v;
 
-    // ---- per-wave constants: [a | b] fragments and c for the wave's own components
+    // buffer descriptors over this (batch, head) slice: reads past the end return 0, stores past
+    // the end are dropped
+    i32x4 rs_q, rs_k, rs_v;
+    __amdgpu_buffer_rsrc_t rs_o;
+    if constexpr (DMA) {
+        rs_q = make_rsrc_words(qx, (uint32_t)(N * a.d_r * 2));
+        rs_k = make_rsrc_words(kx, (uint32_t)(N * a.d_r * 2));
+        rs_v = make_rsrc_words(vv, (uint32_t)(N * a.d_v * 2));
+        rs_o = make_rsrc(oo, (uint32_t)(N * a.d_v * 2));
+    }
+
+    // ---- DMA issue of chunk ch into a staging buffer (each wave issues every W-th block)
+    auto issue_dma = [&](int64_t ch, char* raw) {
+        const int64_t n0 = ch * C;
+        for (int f = w; f < NF; f += W) {
+            if (f < NF_XALL) {
+                const bool isq = NEED_Q && f < NF_X;
+                const int fx = (NEED_Q && !isq) ? f - NF_X : f;
+                const int tt = fx / NKS2, ks2 = fx % NKS2;
+                const uint32_t soff = (uint32_t)((n0 + tt * 16) * a.d_r * 2);
+                const uint32_t voff = (uint32_t)((lr * a.d_r + ks2 * 32 + lg * 8) * 2);
+                dma16(isq ? rs_q : rs_k, raw + (isq ? OFF_XQ : OFF_XK) + fx * 1024, voff, soff);
+            } else if constexpr (NEED_V) {
+                const int fv = f - NF_XALL;
+                const int r0 = fv * RPB;
+                const int rl = lane / CPR;
+                const int row = r0 + rl;
+                const int gch = (lane % CPR) ^ (row % CPR);
+                const uint32_t soff = (uint32_t)((n0 + r0) * a.d_v * 2);
+                const uint32_t voff = (uint32_t)((rl * a.d_v + gch * 8) * 2);
+                dma16(rs_v, raw + OFF_V + fv * 1024, voff, soff);
+            }
+        }
+    };
+    // In-place bf16 -> fp16 conversion of the X blocks this wave fetched (same byte layout).
+    auto convert_own_x = [&](char* raw) {
+        for (int f = w; f < NF_XALL; f += W) {
+            char* p = raw + f * 1024 + lane * 16;   // X_Q blocks then X_K blocks, contiguous
+            const u32x4 r = *reinterpret_cast<const u32x4*>(p);
+            *reinterpret_cast<f16x8*>(p) = bf16x8_bits_to_f16x8(r);
+        }
+    };
+
+    // ---- per-wave constants: [a | b] fragments of the wave's own components (registers) and the
+    // logit constants c (LDS)
     xfrag_t abf[KT_W][NKS];
-    f32x4 cinit[KT_W];
     {
         const xfrag_t* abg = reinterpret_cast<const xfrag_t*>(a.ab) + (int64_t)h * NCT * NKS * 64;
 #pragma unroll
@@ -344,16 +435,14 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
             const int ct = w * KT_W + kt;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) abf[kt][ks] = abg[((int64_t)ct * NKS + ks) * 64 + lane];
-            const float* cv = a.cvec + (int64_t)h * KC + ct * 16 + lg * 4;
-            cinit[kt] = f32x4{cv[0], cv[1], cv[2], cv[3]};
         }
+        for (int k = tid; k < KC; k += NTHR) s_c[k] = a.cvec[(int64_t)h * KC + k];
     }
 
     // ---- running state: [Vt | Z] columns owned by this wave (all components), Z of own components
     constexpr int ST_T = HAS_STATE ? NCT : 1;
     constexpr int ST_V = HAS_STATE ? VT_W : 1;
     f32x4 st[ST_T][ST_V];
-    f32x4 zown[KT_W];
     const int64_t rec = (int64_t)KC * VC + KC;
     float* segrec = a.seg + ((int64_t)bh * a.P + sidx) * rec;
     if constexpr (HAS_STATE) {
@@ -367,38 +456,60 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
                 st[ct][vt] = load ? *reinterpret_cast<const f32x4*>(src + ((int64_t)(ct * NVT + gvt) * 64 + lane) * 4)
                                   : f32x4{0.f, 0.f, 0.f, 0.f};
             }
-#pragma unroll
-        for (int kt = 0; kt < KT_W; ++kt) {
-            const int ct = w * KT_W + kt;
-            zown[kt] = load ? *reinterpret_cast<const f32x4*>(src + (int64_t)KC * VC + ct * 16 + lg * 4)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int k = tid; k < KC; k += NTHR) s_z[k] = load ? src[(int64_t)KC * VC + k] : 0.f;
+    }
+    lds_barrier();   // s_c and s_z visible to every wave
+
+    if constexpr (DMA) {
+        if (ch0 < ch1) issue_dma(ch0, s_raw0);
     }
 
-    for (int64_t ch = ch0; ch < ch1; ++ch) {
+    // byte offset of (row, column) in the bf16 Gamma_K tile
+    auto gk_off = [&](int row, int col) -> int { return row * GKR + col * 2; };
+
+    // ---- one chunk; BUF selects the DMA staging buffer (compile-time, so the two buffers are
+    // distinct LDS objects)
+    auto body = [&](auto buf_tag, int64_t ch) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        char* raw = BUF ? s_raw1 : s_raw0;
+        char* raw_next = BUF ? s_raw0 : s_raw1;
         const int64_t n0 = ch * C;
         const int rows_valid = (int)((N - n0 < C) ? N - n0 : C);
 
-        // ---- stage inputs of this chunk
-        if constexpr (NEED_Q) stage_x<F32, C, DRC, NTHR>(s_xq, qx + n0 * a.d_r, rows_valid, a.d_r, a.vec_x, tid);
-        if constexpr (NEED_K) stage_x<F32, C, DRC, NTHR>(s_xk, kx + n0 * a.d_r, rows_valid, a.d_r, a.vec_x, tid);
-        if constexpr (NEED_V) stage_vt<F32, C, VC, NTHR>(s_vt, vv + n0 * a.d_v, rows_valid, a.d_v, a.vec_v, tid);
-        __syncthreads();
+        // ---- inputs of this chunk in LDS
+        if constexpr (DMA) {
+            if (ch == ch0) wait_vmcnt<0>();
+            else wait_vmcnt<NSTORE>();
+            convert_own_x(raw);
+            lds_barrier();
+            if (ch + 1 < ch1) issue_dma(ch + 1, raw_next);
+        } else {
+            if constexpr (NEED_Q) stage_x<F32, C, DRC, NTHR>(s_xq, qx + n0 * a.d_r, rows_valid, a.d_r, a.vec_x, tid);
+            if constexpr (NEED_K) stage_x<F32, C, DRC, NTHR>(s_xk, kx + n0 * a.d_r, rows_valid, a.d_r, a.vec_x, tid);
+            if constexpr (NEED_V) stage_vt<F32, C, VC, NTHR>(s_vt, vv + n0 * a.d_v, rows_valid, a.d_v, a.vec_v, tid);
+            lds_barrier();
+        }
 
-        // ---- logits^T tiles for own components: lq[kt][tt] (rows: comps 4g+i of tile ct, col: token 16tt+r)
-        f32x4 lq[NEED_Q ? KT_W : 1][NT];
-        f32x4 lk[NEED_K ? KT_W : 1][NT];
-        auto logits = [&](const char* sx, f32x4 (&acc)[KT_W][NT]) {
+        // ---- logits^T tiles for own components: acc[kt][tt] (rows: comps 4g+i of tile ct, col: token 16tt+r)
+        auto logits = [&](int which, f32x4 (&acc)[KT_W][NT]) {
 #pragma unroll
-            for (int kt = 0; kt < KT_W; ++kt)
+            for (int kt = 0; kt < KT_W; ++kt) {
+                const f32x4 cinit = *reinterpret_cast<const f32x4*>(&s_c[(w * KT_W + kt) * 16 + lg * 4]);
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) acc[kt][tt] = cinit[kt];
+                for (int tt = 0; tt < NT; ++tt) acc[kt][tt] = cinit;
+            }
 #pragma unroll
             for (int ks = 0; ks < NKS2; ++ks) {
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
-                    const xfrag_t xf = *reinterpret_cast<const xfrag_t*>(
-                        sx + (tt * 16 + lr) * XS + (ks * KS + lg * (KS / 4)) * T::XES);
+                    xfrag_t xf;
+                    if constexpr (DMA) {
+                        xf = *reinterpret_cast<const xfrag_t*>(raw + (which ? OFF_XK : OFF_XQ) +
+                                                               ((tt * NKS2 + ks) * 64 + lane) * 16);
+                    } else {
+                        xf = *reinterpret_cast<const xfrag_t*>((which ? s_xk : s_xq) + (tt * 16 + lr) * XS +
+                                                               (ks * KS + lg * (KS / 4)) * T::XES);
+                    }
                     const xfrag_t x2 = xf * xf;
 #pragma unroll
                     for (int kt = 0; kt < KT_W; ++kt) {
@@ -408,8 +519,10 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
                 }
             }
         };
-        if constexpr (NEED_Q) logits(s_xq, lq);
-        if constexpr (NEED_K) logits(s_xk, lk);
+        f32x4 lq[NEED_Q ? KT_W : 1][NT];
+        f32x4 lk[NEED_K ? KT_W : 1][NT];
+        if constexpr (NEED_Q) logits(0, lq);
+        if constexpr (NEED_K) logits(1, lk);
 
         // ---- softmax over K, part 1: per-wave max and sum of exp2 over own components
         float mq[NT], mk[NT];
@@ -442,9 +555,11 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
         };
         if constexpr (NEED_Q) local_softmax(lq, mq, 0);
         if constexpr (NEED_K) local_softmax(lk, mk, 1);
-        __syncthreads();
+        lds_barrier();
 
-        // ---- softmax part 2: combine the W partial (max, sum) pairs; scale to posteriors
+        // ---- softmax part 2: combine the W partial (max, sum) pairs; scale to posteriors.
+        // Rows past the end of the sequence get the factor 0 (their logits are finite: the
+        // staged inputs of those rows are zeros).
         auto finish_softmax = [&](f32x4 (&acc)[KT_W][NT], const float (&mloc)[NT], int which) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -455,7 +570,8 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
                 float S = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < W; ++ww) S += s_ms[which][ww][tok][1] * fast_exp2(s_ms[which][ww][tok][0] - M);
-                float f = (mloc[tt] == -INFINITY || tok >= rows_valid) ? 0.f : fast_exp2(mloc[tt] - M) / S;
+                const bool live = mloc[tt] != -INFINITY && tok < rows_valid;
+                const float f = live ? fast_exp2(mloc[tt] - M) * fast_rcp(S) : 0.f;
 #pragma unroll
                 for (int kt = 0; kt < KT_W; ++kt) acc[kt][tt] *= f;
             }
@@ -481,12 +597,12 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
                     }
                 }
             }
-            __syncthreads();  // s_xq / s_ms reuse by the next chunk
-            continue;
+            if constexpr (!DMA) lds_barrier();  // staging buffers are rewritten by the next chunk
+            return;
         }
 
-        // ---- Gamma to LDS as operand fragments; denominators from the carried Z
-        if constexpr (MODE == MODE_OUT_BIDIR || MODE == MODE_OUT_CAUSAL) {
+        // ---- Gamma to LDS; denominators from the carried Z
+        if constexpr (OUT) {
             // token-row fragments of Gamma_Q: frag[tt][kq][lane] holds comps of step kq for token 16tt + r
 #pragma unroll
             for (int kt = 0; kt < KT_W; ++kt) {
@@ -502,6 +618,10 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
                 }
             }
             // partial denominators over own components: sum_k gamma_Q[n,k] Z[k]
+            f32x4 zown[KT_W];
+#pragma unroll
+            for (int kt = 0; kt < KT_W; ++kt)
+                zown[kt] = *reinterpret_cast<const f32x4*>(&s_z[(w * KT_W + kt) * 16 + lg * 4]);
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 float d = 0.f;
@@ -514,100 +634,115 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
             }
         }
         if constexpr (NEED_K) {
-            if constexpr (MODE == MODE_OUT_CAUSAL) {
-#pragma unroll
-                for (int kt = 0; kt < KT_W; ++kt) {
-                    const int ct = w * KT_W + kt;
-#pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) {
-                        if constexpr (F32) {
-                            *reinterpret_cast<f32x4*>(s_gk + ((tt * NKQ + ct) * 64 + lane) * 16) = lk[kt][tt];
-                        } else {
-                            *reinterpret_cast<bf16x4*>(s_gk + ((tt * NKQ + (ct >> 1)) * 64 + lane) * 16 + (ct & 1) * 8) =
-                                pack4(lk[kt][tt]);
-                        }
-                    }
-                }
-            }
-            // comp-row fragments of Gamma_K^T: frag[ct][tk][lane'] holds, for component 16ct + (lane' % 16),
-            // the tokens of step tk in slots matching the V^T fragments (4 consecutive tokens per group).
 #pragma unroll
             for (int kt = 0; kt < KT_W; ++kt) {
                 const int ct = w * KT_W + kt;
 #pragma unroll
                 for (int tt = 0; tt < NT; ++tt) {
+                    if constexpr (F32) {
+                        // token-row fragments (for S^T) ...
+                        if constexpr (MODE == MODE_OUT_CAUSAL)
+                            *reinterpret_cast<f32x4*>(s_gk + ((tt * NKQ + ct) * 64 + lane) * 16) = lk[kt][tt];
+                        // ... and component-row fragments (for the state update), slots matching the V
+                        // fragments (4 consecutive tokens per lane group)
+                        char* gkc = s_gk + NT * NKQ * 1024;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int lane2 = (lg * 4 + i) + 16 * (lr >> 2);
-                        if constexpr (F32) {
-                            const int slot = lr & 3;
-                            reinterpret_cast<float*>(s_gkc + ((ct * NTK + tt) * 64 + lane2) * 16)[slot] = lk[kt][tt][i];
-                        } else {
-                            const int slot = (lr & 3) + 4 * (tt & 1);
-                            reinterpret_cast<__bf16*>(s_gkc + ((ct * NTK + (tt >> 1)) * 64 + lane2) * 16)[slot] =
-                                to_bf16(lk[kt][tt][i]);
+                        for (int i = 0; i < 4; ++i) {
+                            const int lane2 = (lg * 4 + i) + 16 * (lr >> 2);
+                            reinterpret_cast<float*>(gkc + ((ct * NTK + tt) * 64 + lane2) * 16)[lr & 3] = lk[kt][tt][i];
                         }
+                    } else {
+                        // row-major bf16: token 16tt + r, components 16ct + 4g .. +3
+                        *reinterpret_cast<bf16x4*>(s_gk + gk_off(tt * 16 + lr, ct * 16 + lg * 4)) = pack4(lk[kt][tt]);
                     }
                 }
+                // Z over the chunk's tokens (fp32); each wave updates only its own components
+                f32x4 zs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) zs += lk[kt][tt];
+                f32x4 zn = *reinterpret_cast<const f32x4*>(&s_z[ct * 16 + lg * 4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zn[i] += row16_sum(zs[i]);
+                if (lr == 0) *reinterpret_cast<f32x4*>(&s_z[ct * 16 + lg * 4]) = zn;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- contraction phase: this wave owns d_v tiles [w*VT_W, (w+1)*VT_W)
         gfrag_t vf[NEED_V ? VT_W : 1][NTK];
         if constexpr (NEED_V) {
 #pragma unroll
             for (int vt = 0; vt < VT_W; ++vt) {
-                const int row = (w * VT_W + vt) * 16 + lr;
+                const int gvt = w * VT_W + vt;
 #pragma unroll
                 for (int tk = 0; tk < NTK; ++tk) {
-                    if constexpr (F32) {
-                        vf[vt][tk] = *reinterpret_cast<const f32x4*>(s_vt + row * VTS + (tk * 16 + lg * 4) * 4);
+                    if constexpr (DMA) {
+                        // transposed reads of the swizzled row-major V: lane 16g + 4i + q supplies row
+                        // 4g + i of the token tile and the 4 columns 16 gvt + 4q .. +3
+                        const int q = lane & 3, i4 = (lane >> 2) & 3;
+                        u32x2 part[2];
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const int row = (2 * tk + hf) * 16 + lg * 4 + i4;
+                            const int chunk = (2 * gvt + (q >> 1)) ^ (row % CPR);
+                            part[hf] = ds_read_tr16(raw + OFF_V + row * (VC * 2) + chunk * 16 + (q & 1) * 8);
+                        }
+                        vf[vt][tk] = __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
                     } else {
-                        const u32x2 lo = *reinterpret_cast<const u32x2*>(s_vt + row * VTS + ((2 * tk) * 16 + lg * 4) * 2);
-                        const u32x2 hi = *reinterpret_cast<const u32x2*>(s_vt + row * VTS + ((2 * tk + 1) * 16 + lg * 4) * 2);
-                        u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
-                        vf[vt][tk] = __builtin_bit_cast(bf16x8, both);
+                        const int row = gvt * 16 + lr;
+                        if constexpr (F32) {
+                            vf[vt][tk] = *reinterpret_cast<const f32x4*>(s_vt + row * VTS + (tk * 16 + lg * 4) * 4);
+                        } else {
+                            const u32x2 lo = *reinterpret_cast<const u32x2*>(s_vt + row * VTS + ((2 * tk) * 16 + lg * 4) * 2);
+                            const u32x2 hi = *reinterpret_cast<const u32x2*>(s_vt + row * VTS + ((2 * tk + 1) * 16 + lg * 4) * 2);
+                            vf[vt][tk] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                        }
                     }
                 }
             }
         }
 
-        if constexpr (MODE == MODE_OUT_BIDIR || MODE == MODE_OUT_CAUSAL) {
-            f32x4 oacc[VT_W][NT];
+        // Gamma_K operand fragments
+        // token rows (A of S^T = Gamma_K Gamma_Q^T): lane = token 16J + r, slots = components of step kq
+        auto gk_token_frag = [&](int J, int kq) -> gfrag_t {
+            if constexpr (F32) {
+                return *reinterpret_cast<const gfrag_t*>(s_gk + ((J * NKQ + kq) * 64 + lane) * 16);
+            } else {
+                const int row = J * 16 + lr;
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(s_gk + gk_off(row, (2 * kq) * 16 + lg * 4));
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(s_gk + gk_off(row, (2 * kq + 1) * 16 + lg * 4));
+                return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+        };
+        // component rows (A of the state update Gamma_K^T V): lane = component 16ct + r, slots =
+        // tokens of step tk in the V-fragment order
+        auto gk_comp_frag = [&](int ct, int tk) -> gfrag_t {
+            if constexpr (F32) {
+                return *reinterpret_cast<const gfrag_t*>(s_gk + NT * NKQ * 1024 + ((ct * NTK + tk) * 64 + lane) * 16);
+            } else {
+                const int q = lane & 3, i4 = (lane >> 2) & 3;
+                u32x2 part[2];
 #pragma unroll
-            for (int vt = 0; vt < VT_W; ++vt)
-#pragma unroll
-                for (int I = 0; I < NT; ++I) oacc[vt][I] = f32x4{0.f, 0.f, 0.f, 0.f};
-            float den[NT];
-
-            // state operand fragments (A: rows d_v, contraction over components)
-            gfrag_t sf[VT_W][NKQ];
-#pragma unroll
-            for (int vt = 0; vt < VT_W; ++vt)
-#pragma unroll
-                for (int kq = 0; kq < NKQ; ++kq) {
-                    if constexpr (F32) sf[vt][kq] = st[kq][vt];
-                    else sf[vt][kq] = pack_pair(st[2 * kq][vt], st[2 * kq + 1][vt]);
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int row = (2 * tk + hf) * 16 + lg * 4 + i4;
+                    part[hf] = ds_read_tr16(s_gk + gk_off(row, ct * 16 + 4 * q));
                 }
+                return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+            }
+        };
 
+        if constexpr (OUT) {
+            // intra-chunk affinities (causal): S^T(J, I) = Gamma_K[J] Gamma_Q[I]^T for J <= I, masked
+            // j <= i, as operand fragments over the token steps; row sums go to the denominators
+            constexpr int NSF = (MODE == MODE_OUT_CAUSAL) ? (F32 ? NT * NT : NT * NTK) : 1;
+            gfrag_t sfr[NSF];
+            float den[NT];
 #pragma unroll
             for (int I = 0; I < NT; ++I) {
-                gfrag_t gqf[NKQ];
-#pragma unroll
-                for (int kq = 0; kq < NKQ; ++kq)
-                    gqf[kq] = *reinterpret_cast<const gfrag_t*>(s_gq + ((I * NKQ + kq) * 64 + lane) * 16);
-                // inter: O^T(vt, I) += state^T . Gamma_Q^T
-#pragma unroll
-                for (int vt = 0; vt < VT_W; ++vt)
-#pragma unroll
-                    for (int kq = 0; kq < NKQ; ++kq) mma(oacc[vt][I], sf[vt][kq], gqf[kq]);
                 float d = 0.f;
 #pragma unroll
                 for (int ww = 0; ww < W; ++ww) d += s_den[ww][I * 16 + lr];
-
                 if constexpr (MODE == MODE_OUT_CAUSAL) {
-                    // intra: S^T(J, I) = Gamma_K[J] Gamma_Q[I]^T for J <= I, masked j <= i
                     f32x4 sacc[NT];
                     float dsum = 0.f;
 #pragma unroll
@@ -616,8 +751,8 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
                         if (J > I) continue;
 #pragma unroll
                         for (int kq = 0; kq < NKQ; ++kq) {
-                            const gfrag_t gkf = *reinterpret_cast<const gfrag_t*>(s_gk + ((J * NKQ + kq) * 64 + lane) * 16);
-                            mma(sacc[J], gkf, gqf[kq]);
+                            const gfrag_t gqi = *reinterpret_cast<const gfrag_t*>(s_gq + ((I * NKQ + kq) * 64 + lane) * 16);
+                            mma(sacc[J], gk_token_frag(J, kq), gqi);
                         }
                         if (J == I) {
 #pragma unroll
@@ -627,52 +762,78 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
                         if constexpr (!F32) {
                             // round to the operand precision so numerator and denominator agree
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) sacc[J][i] = (float)to_bf16(sacc[J][i]);
+                            for (int i = 0; i < 4; ++i) sacc[J][i] = round_bf16(sacc[J][i]);
                         }
 #pragma unroll
                         for (int i = 0; i < 4; ++i) dsum += sacc[J][i];
                     }
                     d += group4_sum(dsum);
-                    // O^T(vt, I) += V^T(vt, tokens) . S^T(tokens, I)
+                    if constexpr (F32) {
 #pragma unroll
-                    for (int tk = 0; tk < NTK; ++tk) {
-                        if constexpr (F32) {
-                            if (tk > I) continue;
+                        for (int J = 0; J < NT; ++J) sfr[I * NT + J] = sacc[J];
+                    } else {
 #pragma unroll
-                            for (int vt = 0; vt < VT_W; ++vt) mma(oacc[vt][I], vf[vt][tk], sacc[tk]);
-                        } else {
-                            if (2 * tk > I) continue;
-                            const bf16x8 sfr = pack_pair(sacc[2 * tk], sacc[2 * tk + 1]);
-#pragma unroll
-                            for (int vt = 0; vt < VT_W; ++vt) mma(oacc[vt][I], vf[vt][tk], sfr);
-                        }
+                        for (int tk = 0; tk < NTK; ++tk) sfr[I * NTK + tk] = pack_pair(sacc[2 * tk], sacc[2 * tk + 1]);
                     }
                 }
                 den[I] = d + a.eps;
             }
 
-            // ---- write O: lane holds d_v 16vt' + 4g .. +3 of token 16I + r
 #pragma unroll
-            for (int I = 0; I < NT; ++I) {
-                const int tok = I * 16 + lr;
-                if (tok >= rows_valid) continue;
-                const float inv = 1.0f / den[I];
-                elem_t* orow = reinterpret_cast<elem_t*>(a.o) + ((int64_t)bh * N + n0 + tok) * a.d_v;
+            for (int vt = 0; vt < VT_W; ++vt) {
+                f32x4 oacc[NT];
 #pragma unroll
-                for (int vt = 0; vt < VT_W; ++vt) {
-                    const int c0 = (w * VT_W + vt) * 16 + lg * 4;
-                    f32x4 ov = oacc[vt][I] * inv;
-                    if (a.vec_o && c0 + 4 <= a.d_v) {
+                for (int I = 0; I < NT; ++I) oacc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+                // inter: O^T(vt, I) += state^T . Gamma_Q^T, state operands packed on the fly
+#pragma unroll
+                for (int kq = 0; kq < NKQ; ++kq) {
+                    gfrag_t sf;
+                    if constexpr (F32) sf = st[kq][vt];
+                    else sf = pack_pair(st[2 * kq][vt], st[2 * kq + 1][vt]);
+#pragma unroll
+                    for (int I = 0; I < NT; ++I)
+                        mma(oacc[I], sf, *reinterpret_cast<const gfrag_t*>(s_gq + ((I * NKQ + kq) * 64 + lane) * 16));
+                }
+                // intra: O^T(vt, I) += V^T(vt, tokens) . S^T(tokens, I)
+                if constexpr (MODE == MODE_OUT_CAUSAL) {
+#pragma unroll
+                    for (int I = 0; I < NT; ++I) {
                         if constexpr (F32) {
-                            *reinterpret_cast<f32x4*>(orow + c0) = ov;
+#pragma unroll
+                            for (int J = 0; J < NT; ++J)
+                                if (J <= I) mma(oacc[I], vf[vt][J], sfr[I * NT + J]);
                         } else {
-                            *reinterpret_cast<bf16x4*>(orow + c0) = pack4(ov);
+#pragma unroll
+                            for (int tk = 0; tk < NTK; ++tk)
+                                if (2 * tk <= I) mma(oacc[I], vf[vt][tk], sfr[I * NTK + tk]);
                         }
+                    }
+                }
+                // ---- write O: lane holds d_v 16vt' + 4g .. +3 of token 16I + r
+                const int c0 = (w * VT_W + vt) * 16 + lg * 4;
+#pragma unroll
+                for (int I = 0; I < NT; ++I) {
+                    const int tok = I * 16 + lr;
+                    const f32x4 ov = oacc[I] * fast_rcp(den[I]);
+                    if constexpr (DMA) {
+                        // unconditional bounds-checked store: rows past N and pad columns are dropped
+                        const uint32_t off = (c0 < a.d_v) ? (uint32_t)(((n0 + tok) * a.d_v + c0) * 2) : 0x80000000u;
+                        store_b64(rs_o, __builtin_bit_cast(u32x2, pack4(ov)), off);
                     } else {
-                        for (int i = 0; i < 4; ++i) {
-                            if (c0 + i < a.d_v) {
-                                if constexpr (F32) orow[c0 + i] = ov[i];
-                                else orow[c0 + i] = bf16_bits(ov[i]);
+                        if (tok >= rows_valid) continue;
+                        elem_t* orow = oo + (n0 + tok) * a.d_v;
+                        if (a.vec_o && c0 + 4 <= a.d_v) {
+                            if constexpr (F32) {
+                                *reinterpret_cast<f32x4*>(orow + c0) = ov;
+                            } else {
+                                *reinterpret_cast<bf16x4*>(orow + c0) = pack4(ov);
+                            }
+                        } else {
+                            for (int i = 0; i < 4; ++i) {
+                                if (c0 + i < a.d_v) {
+                                    if constexpr (F32) orow[c0 + i] = ov[i];
+                                    else orow[c0 + i] = bf16_bits(ov[i]);
+                                }
                             }
                         }
                     }
@@ -680,26 +841,23 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
             }
         }
 
-        // ---- advance the state: [Vt | Z] += Gamma_K^T [V | 1]
+        // ---- advance the state: Vt += Gamma_K^T V (Z was advanced with the softmax)
         if constexpr (NEED_K) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int tk = 0; tk < NTK; ++tk) {
-                    const gfrag_t gkc = *reinterpret_cast<const gfrag_t*>(s_gkc + ((ct * NTK + tk) * 64 + lane) * 16);
+                    const gfrag_t gkc = gk_comp_frag(ct, tk);
 #pragma unroll
                     for (int vt = 0; vt < VT_W; ++vt) mma(st[ct][vt], gkc, vf[vt][tk]);
                 }
-#pragma unroll
-            for (int kt = 0; kt < KT_W; ++kt) {
-                f32x4 zs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int tt = 0; tt < NT; ++tt) zs += lk[kt][tt];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) zown[kt][i] += row16_sum(zs[i]);
-            }
         }
-        __syncthreads();  // LDS buffers are restaged by the next chunk
+        if constexpr (!DMA) lds_barrier();  // staging buffers are rewritten by the next chunk
+    };
+
+    for (int64_t ch = ch0; ch < ch1; ch += 2) {
+        body(std::integral_constant<int, 0>{}, ch);
+        if (ch + 1 < ch1) body(std::integral_constant<int, 1>{}, ch + 1);
     }
 
     if constexpr (MODE == MODE_AGG) {
@@ -714,7 +872,8 @@ __global__ void __launch_bounds__(W * 64) main_kernel(const MainArgs a) {
 #pragma unroll
             for (int kt = 0; kt < KT_W; ++kt) {
                 const int ct = w * KT_W + kt;
-                *reinterpret_cast<f32x4*>(segrec + (int64_t)KC * VC + ct * 16 + lg * 4) = zown[kt];
+                *reinterpret_cast<f32x4*>(segrec + (int64_t)KC * VC + ct * 16 + lg * 4) =
+                    *reinterpret_cast<const f32x4*>(&s_z[ct * 16 + lg * 4]);
             }
         }
     }
