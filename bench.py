@@ -43,14 +43,16 @@ def algorithmic_flops_per_token_head(w) -> int:
     return 8 * w.n_comp * w.d_route + 4 * w.n_comp * w.d_value
 
 
-def load_traffic(kernel: str, src_hash: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+def load_traffic(workload_name: str, kernel: str, src_hash: str):
+    """HBM bytes per launch (reads + writes) of `kernel` from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE scaled by a copy-kernel calibration), or None if they were taken on a
+    different kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = t.get(kernel)
+    ent = t.get(workload_name, {}).get(kernel)
     if not ent or ent.get("source_hash") != src_hash:
         return None
     return ent.get("bytes_per_launch")
@@ -98,7 +100,9 @@ def main():
     if args.copy_calibration:
         x = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         y = torch.empty_like(x)
+        flush = torch.empty(1 << 29, dtype=torch.float32, device=dev)   # 2 GiB, evicts the 256 MB last-level cache
         for _ in range(max(args.steps, 1)):
+            flush.fill_(0.0)
             torch.mul(x, 1.0, out=y)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": x.numel() * 4, "copy_calibration_bytes_written": y.numel() * 4,
@@ -162,7 +166,7 @@ def main():
     hbm_frac = alg_bytes / avg_s / 1e9 / HBM_PEAK_GBS
     mfma_frac = alg_flops / avg_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]
     src_hash = kernel_source_hash()
-    traffic = load_traffic(dominant, src_hash)
+    traffic = load_traffic(w.name, dominant, src_hash)
     if hbm_frac >= mfma_frac:
         roof = {"bound": "hbm", "achieved": alg_bytes / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": hbm_frac, "traffic": traffic}

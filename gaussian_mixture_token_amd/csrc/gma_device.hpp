@@ -58,6 +58,13 @@ __device__ __forceinline__ bf16x8 pack_pair(const f32x4& lo, const f32x4& hi) {
     return r;
 }
 
+template <class F> __device__ __forceinline__ F ones_frag();
+template <> __device__ __forceinline__ f32x4 ones_frag<f32x4>() { return f32x4{1.f, 1.f, 1.f, 1.f}; }
+template <> __device__ __forceinline__ bf16x8 ones_frag<bf16x8>() {
+    const __bf16 o = (__bf16)1.0f;
+    return bf16x8{o, o, o, o, o, o, o, o};
+}
+
 __device__ __forceinline__ bf16x4 pack4(const f32x4& v) {
     bf16x4 r;
     r[0] = to_bf16(v[0]); r[1] = to_bf16(v[1]); r[2] = to_bf16(v[2]); r[3] = to_bf16(v[3]);
@@ -66,16 +73,20 @@ __device__ __forceinline__ bf16x4 pack4(const f32x4& v) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
-// Sum / max over the four lane groups g (lanes r, r+16, r+32, r+48).
+// Sum / max over the four 16-lane rows (lanes r, r+16, r+32, r+48), in VALU: with both operands
+// equal, v_permlane16_swap returns rows (0,0,2,2) and (1,1,3,3) and v_permlane32_swap returns rows
+// (0,1,0,1) and (2,3,2,3).
 __device__ __forceinline__ float group4_sum(float v) {
-    v += shfl_xor(v, 16);
-    v += shfl_xor(v, 32);
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ __forceinline__ float group4_max(float v) {
-    v = fmaxf(v, shfl_xor(v, 16));
-    v = fmaxf(v, shfl_xor(v, 32));
-    return v;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 // Sum over the 16 lanes of one row group (lanes 16g .. 16g+15).
 __device__ __forceinline__ float row16_sum(float v) {

@@ -12,7 +12,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/gma.h"
+#include "gma.h"
 #include "gma_registry.hpp"
 
 namespace gma {

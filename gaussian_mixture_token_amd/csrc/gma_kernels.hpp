@@ -328,6 +328,7 @@ main_kernel(const MainArgs a) {
     static_assert(MODE == MODE_RESP || NVT % W == 0, "d_v must split evenly across waves");
     static_assert(KC % KS == 0 && C % KS == 0 && (2 * DRC) % KS == 0, "tile shapes");
     static_assert(!DMA || !F32, "LDS DMA staging is the bf16 path");
+    static_assert(W <= 4, "the softmax combine maps one wave per lane group");
 
     // DMA layout of one staging buffer: [X_Q fragments][X_K fragments][V rows]
     constexpr int XFRAG_BYTES = NT * NKS2 * 1024;
@@ -339,6 +340,11 @@ main_kernel(const MainArgs a) {
     constexpr int CPR = VC / 8;              // 16-byte chunks per V row
     constexpr int RPB = 1024 / (VC * 2);     // V rows per 1 KiB DMA block
     constexpr int NF_X = NT * NKS2;
+    // X staging by whole 128-byte row segments (8 rows x 128 B per DMA block) when rows are at least
+    // that long: every fetched line is used by one instruction.  Shorter rows (DRC = 32) keep one
+    // fragment per block (16 rows x 64 B, which is then a contiguous 1 KiB).
+    constexpr bool XSEG = DRC >= 64;
+    constexpr int NSEG = DRC / 64;           // 128-byte segments per row
     constexpr int NF_V = VROW_BYTES / 1024;
     constexpr int NF_XALL = (NEED_Q ? NF_X : 0) + (NEED_K ? NF_X : 0);
     constexpr int NF = NF_XALL + (NEED_V ? NF_V : 0);
@@ -393,6 +399,19 @@ main_kernel(const MainArgs a) {
         rs_o = make_rsrc(oo, (uint32_t)(N * a.d_v * 2));
     }
 
+    // XOR swizzle of the 16-byte chunks of a staged X row: rows r and r + 8 of a 16-row fragment use
+    // disjoint bank halves, so fragment reads are conflict-free
+    auto xswz = [](int row) -> int { return (row & 7) ^ ((row >> 3) & 1); };
+    // LDS byte offset, within one matrix's X area, of this lane's fragment for (tt, ks)
+    const int xlane0 = ((lr >> 3) * NSEG) * 1024 + (lr & 7) * 128 +
+                       (((lg ^ ((lr & 3) ^ ((lr >> 3) & 1))) | (((lr >> 2) & 1) << 2)) << 4);
+    const int xlane1 = ((lr >> 3) * NSEG) * 1024 + (lr & 7) * 128 +
+                       (((lg ^ ((lr & 3) ^ ((lr >> 3) & 1))) | ((((lr >> 2) & 1) ^ 1) << 2)) << 4);
+    auto xfrag_off = [&](int tt, int ks) -> int {
+        if constexpr (XSEG) return ((ks & 1) ? xlane1 : xlane0) + (tt * 2 * NSEG + (ks >> 1)) * 1024;
+        else return ((tt * NKS2 + ks) * 64 + lane) * 16;
+    };
+
     // ---- DMA issue of chunk ch into a staging buffer (each wave issues every W-th block)
     auto issue_dma = [&](int64_t ch, char* raw) {
         const int64_t n0 = ch * C;
@@ -400,10 +419,22 @@ main_kernel(const MainArgs a) {
             if (f < NF_XALL) {
                 const bool isq = NEED_Q && f < NF_X;
                 const int fx = (NEED_Q && !isq) ? f - NF_X : f;
-                const int tt = fx / NKS2, ks2 = fx % NKS2;
-                const uint32_t soff = (uint32_t)((n0 + tt * 16) * a.d_r * 2);
-                const uint32_t voff = (uint32_t)((lr * a.d_r + ks2 * 32 + lg * 8) * 2);
-                dma16(isq ? rs_q : rs_k, raw + (isq ? OFF_XQ : OFF_XK) + fx * 1024, voff, soff);
+                uint32_t soff, voff;
+                if constexpr (XSEG) {
+                    // block fx = (8-row group rb, 128-byte segment sg); lane l -> row rb*8 + l/8, LDS
+                    // chunk l%8 holding global chunk (l%8) ^ xswz(row)
+                    const int rb = fx / NSEG, sg = fx % NSEG;
+                    const int rl = lane >> 3;
+                    const int gc = (lane & 7) ^ xswz(rb * 8 + rl);
+                    soff = (uint32_t)((n0 + rb * 8) * a.d_r * 2);
+                    voff = (uint32_t)((rl * a.d_r + sg * 64 + gc * 8) * 2);
+                } else {
+                    const int tt = fx / NKS2, ks2 = fx % NKS2;
+                    soff = (uint32_t)((n0 + tt * 16) * a.d_r * 2);
+                    voff = (uint32_t)((lr * a.d_r + ks2 * 32 + lg * 8) * 2);
+                }
+                if (isq) dma16(rs_q, raw + OFF_XQ + fx * 1024, voff, soff);
+                else dma16(rs_k, raw + OFF_XK + fx * 1024, voff, soff);
             } else if constexpr (NEED_V) {
                 const int fv = f - NF_XALL;
                 const int r0 = fv * RPB;
@@ -504,8 +535,7 @@ main_kernel(const MainArgs a) {
                 for (int tt = 0; tt < NT; ++tt) {
                     xfrag_t xf;
                     if constexpr (DMA) {
-                        xf = *reinterpret_cast<const xfrag_t*>(raw + (which ? OFF_XK : OFF_XQ) +
-                                                               ((tt * NKS2 + ks) * 64 + lane) * 16);
+                        xf = *reinterpret_cast<const xfrag_t*>(raw + (which ? OFF_XK : OFF_XQ) + xfrag_off(tt, ks));
                     } else {
                         xf = *reinterpret_cast<const xfrag_t*>((which ? s_xk : s_xq) + (tt * 16 + lr) * XS +
                                                                (ks * KS + lg * (KS / 4)) * T::XES);
@@ -564,12 +594,12 @@ main_kernel(const MainArgs a) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 const int tok = tt * 16 + lr;
-                float M = -INFINITY;
-#pragma unroll
-                for (int ww = 0; ww < W; ++ww) M = fmaxf(M, s_ms[which][ww][tok][0]);
-                float S = 0.f;
-#pragma unroll
-                for (int ww = 0; ww < W; ++ww) S += s_ms[which][ww][tok][1] * fast_exp2(s_ms[which][ww][tok][0] - M);
+                // lane group g combines the partial of wave g (W <= 4): M = max_g m_g,
+                // S = sum_g s_g 2^(m_g - M)
+                const float mg = (lg < W) ? s_ms[which][lg < W ? lg : 0][tok][0] : -INFINITY;
+                const float sg = (lg < W) ? s_ms[which][lg < W ? lg : 0][tok][1] : 0.f;
+                const float M = group4_max(mg);
+                const float S = group4_sum(mg == -INFINITY ? 0.f : sg * fast_exp2(mg - M));
                 const bool live = mloc[tt] != -INFINITY && tok < rows_valid;
                 const float f = live ? fast_exp2(mloc[tt] - M) * fast_rcp(S) : 0.f;
 #pragma unroll
@@ -656,14 +686,6 @@ main_kernel(const MainArgs a) {
                         *reinterpret_cast<bf16x4*>(s_gk + gk_off(tt * 16 + lr, ct * 16 + lg * 4)) = pack4(lk[kt][tt]);
                     }
                 }
-                // Z over the chunk's tokens (fp32); each wave updates only its own components
-                f32x4 zs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int tt = 0; tt < NT; ++tt) zs += lk[kt][tt];
-                f32x4 zn = *reinterpret_cast<const f32x4*>(&s_z[ct * 16 + lg * 4]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) zn[i] += row16_sum(zs[i]);
-                if (lr == 0) *reinterpret_cast<f32x4*>(&s_z[ct * 16 + lg * 4]) = zn;
             }
         }
         lds_barrier();
@@ -744,7 +766,6 @@ main_kernel(const MainArgs a) {
                 for (int ww = 0; ww < W; ++ww) d += s_den[ww][I * 16 + lr];
                 if constexpr (MODE == MODE_OUT_CAUSAL) {
                     f32x4 sacc[NT];
-                    float dsum = 0.f;
 #pragma unroll
                     for (int J = 0; J < NT; ++J) {
                         sacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -759,22 +780,25 @@ main_kernel(const MainArgs a) {
                             for (int i = 0; i < 4; ++i)
                                 if (lg * 4 + i > lr) sacc[J][i] = 0.f;
                         }
-                        if constexpr (!F32) {
-                            // round to the operand precision so numerator and denominator agree
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) sacc[J][i] = round_bf16(sacc[J][i]);
-                        }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) dsum += sacc[J][i];
                     }
-                    d += group4_sum(dsum);
+                    // operand fragments over the token steps, and their column sums (an all-ones
+                    // product, so the denominator sees the same rounded weights as the numerator)
+                    const gfrag_t ones = ones_frag<gfrag_t>();
+                    f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
                     if constexpr (F32) {
 #pragma unroll
-                        for (int J = 0; J < NT; ++J) sfr[I * NT + J] = sacc[J];
+                        for (int J = 0; J < NT; ++J) {
+                            sfr[I * NT + J] = sacc[J];
+                            if (J <= I) mma(dacc, ones, sacc[J]);
+                        }
                     } else {
 #pragma unroll
-                        for (int tk = 0; tk < NTK; ++tk) sfr[I * NTK + tk] = pack_pair(sacc[2 * tk], sacc[2 * tk + 1]);
+                        for (int tk = 0; tk < NTK; ++tk) {
+                            sfr[I * NTK + tk] = pack_pair(sacc[2 * tk], sacc[2 * tk + 1]);
+                            if (2 * tk <= I) mma(dacc, ones, sfr[I * NTK + tk]);
+                        }
                     }
+                    d += dacc[0];
                 }
                 den[I] = d + a.eps;
             }
@@ -841,16 +865,27 @@ main_kernel(const MainArgs a) {
             }
         }
 
-        // ---- advance the state: Vt += Gamma_K^T V (Z was advanced with the softmax)
+        // ---- advance the state: Vt += Gamma_K^T V for the wave's d_v tiles, and Z += Gamma_K^T 1 for
+        // its own components (a product with an all-ones operand: lane (r, g) receives the column
+        // sums for components 16ct + 4g .. +3, the same bf16 Gamma_K the state sees)
         if constexpr (NEED_K) {
+            const gfrag_t ones = ones_frag<gfrag_t>();
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+            for (int ct = 0; ct < NCT; ++ct) {
+                const bool own = (ct / KT_W) == w;
+                f32x4 zi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int tk = 0; tk < NTK; ++tk) {
                     const gfrag_t gkc = gk_comp_frag(ct, tk);
 #pragma unroll
                     for (int vt = 0; vt < VT_W; ++vt) mma(st[ct][vt], gkc, vf[vt][tk]);
+                    if (own) mma(zi, gkc, ones);
                 }
+                if (own && lr == 0) {
+                    f32x4* zp = reinterpret_cast<f32x4*>(&s_z[ct * 16 + lg * 4]);
+                    *zp = *zp + zi;
+                }
+            }
         }
         if constexpr (!DMA) lds_barrier();  // staging buffers are rewritten by the next chunk
     };
