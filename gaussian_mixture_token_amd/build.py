@@ -22,7 +22,9 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Matrix-core results stay in VGPRs (the token-split kernels keep their [a | b] operands in AGPRs,
+# where the MFMAs read them directly).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-Wno-unused-function", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
@@ -56,19 +58,29 @@ def _check_resources(src: str, remarks: str) -> None:
         raise RuntimeError("kernels in %s use scratch memory:\n  %s" % (src, "\n  ".join(bad)))
 
 
-def _check_store_counts(asm_path: str) -> int:
-    """The DMA output kernels wait with vmcnt(NSTORE) for the prefetch, which is exact only if each
-    chunk body issues exactly NSTORE = (d_v tiles per wave) x (token tiles) buffer stores."""
+def _check_vmem_in_loops(asm_path: str) -> int:
+    """The token-split kernels wait for their LDS-DMA prefetch with exact vmcnt counts, which hold
+    only if the chunk loop issues no vector-memory operation other than the DMA loads (buffer_load
+    ... lds) and the output stores (buffer_store).  Checked on the assembly after the first barrier
+    (everything before it is the prologue): no scratch access, no other loads."""
     text = open(asm_path).read()
     n_checked = 0
-    for m in re.finditer(r"^(_ZN3gma11main_kernelILb0ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi([23])ELb1ELi\d+EEEvNS_8MainArgsE):",
-                         text, re.M):
-        name, kc, vc, drc, w, c, mode = m.group(1), *map(int, m.groups()[1:])
+    for m in re.finditer(r"^(_ZN3gma10tok_kernel\S*):", text, re.M):
+        name = m.group(1)
         body = text[m.end(): text.index("s_endpgm", m.end())]
-        stores = len(re.findall(r"^\s*buffer_store_dwordx2", body, re.M))
-        nstore = (vc // 16 // w) * (c // 16)
-        if stores != 2 * nstore:
-            raise RuntimeError("%s: %d buffer stores in the chunk loop, expected %d" % (name, stores, 2 * nstore))
+        loop = body[body.index("s_barrier"):] if "s_barrier" in body else ""
+        bad = []
+        for line in loop.splitlines():
+            t = line.strip().split()
+            if not t:
+                continue
+            op = t[0]
+            # (global stores: only the aggregate epilogue, after the loop)
+            if op.startswith(("global_load", "global_atomic", "flat_", "scratch_")) or \
+                    (op.startswith("buffer_load") and not line.rstrip().endswith(" lds")):
+                bad.append(line.strip())
+        if bad:
+            raise RuntimeError("%s: unexpected vector-memory operations in the chunk loop:\n  %s" % (name, "\n  ".join(bad[:8])))
         n_checked += 1
     return n_checked
 
@@ -95,7 +107,7 @@ def _compile(src: str) -> str:
         base = os.path.splitext(os.path.basename(obj))[0]
         for name in os.listdir(BUILD_DIR):
             if name.startswith(base.replace(".hip", "")) and name.endswith("gfx950.s"):
-                _check_store_counts(os.path.join(BUILD_DIR, name))
+                _check_vmem_in_loops(os.path.join(BUILD_DIR, name))
     return obj
 
 

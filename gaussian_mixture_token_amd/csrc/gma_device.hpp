@@ -36,6 +36,34 @@ __device__ __forceinline__ void mma(f32x4& c, const f32x4& a, const f32x4& b) {
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
 }
 
+// Keeps an MFMA operand in accumulation registers (AGPRs): with one wavefront per SIMD a wave has
+// 256 VGPRs and 256 AGPRs, and matrix-core operands may be read from either file.
+template <class T>
+__device__ __forceinline__ void pin_agpr(T& v) {
+    asm volatile("" : "+a"(v));
+}
+
+// Scheduling hints for one scheduling region (the code since the last sched_barrier): interleave
+// N matrix-core instructions with V vector-ALU instructions after each, so that the ALU work
+// issues while the matrix cores are busy.  fence() ends a region.
+template <int N, int V>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    }
+}
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Makes v opaque to the optimiser at this point, so that values computed from it inside a loop are
+// recomputed there instead of being hoisted out and held in registers across the loop.
+template <class T>
+__device__ __forceinline__ T opaque_v(T v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
@@ -44,6 +72,13 @@ __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
     __bf16 b = (__bf16)x;
     return __builtin_bit_cast(uint16_t, b);
+}
+
+// Two fp32 values rounded to bf16 (nearest even), packed: a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 t = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, t);
 }
 
 // x rounded to the nearest bf16 value, returned as fp32
@@ -142,7 +177,8 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t byte
 // wave): buffer_load_dwordx4 ... lds.  Issued from inline assembly so that the compiler does not
 // track the LDS write: the kernels wait for it explicitly (wait_vmcnt + barrier) before reading
 // the buffer, and an implicit wait would otherwise serialise the prefetch with the compute of
-// the current chunk.  M0 (the LDS destination) is saved and restored around the load.
+// the current chunk.  M0 (the LDS destination) is saved and restored around the load; an SALU
+// write of M0 needs one wait state before an LDS-DMA load reads it (s_nop 0).
 __device__ __forceinline__ void dma16(const i32x4& rs, char* lds, uint32_t voff, uint32_t soff) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)GMA_LDS(lds)));
@@ -155,11 +191,81 @@ __device__ __forceinline__ void dma16(const i32x4& rs, char* lds, uint32_t voff,
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
         "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "s"(dst), "v"(voff), "s"(srs), "s"(__builtin_amdgcn_readfirstlane(soff))
         : "memory");
+}
+
+// LDS (address space 3) byte pointers and their 32-bit addresses.
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
+
+// Four LDS-DMA loads of 16 bytes per lane: global (rsrc, voff[i]) -> LDS at m0[i] + 16 * lane.
+// rs and the LDS addresses must be wave-uniform (SGPRs).  One M0 save / restore for the four.
+__device__ __forceinline__ void dma16x4(const i32x4& rs, uint32_t m0a, uint32_t m0b, uint32_t m0c, uint32_t m0d,
+                                        uint32_t va, uint32_t vb, uint32_t vc, uint32_t vd) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %5, %9, 0 offen lds\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %6, %9, 0 offen lds\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %7, %9, 0 offen lds\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %8, %9, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0a), "s"(m0b), "s"(m0c), "s"(m0d), "v"(va), "v"(vb), "v"(vc), "v"(vd), "s"(rs)
+        : "memory");
+}
+__device__ __forceinline__ void dma16x2(const i32x4& rs, uint32_t m0a, uint32_t m0b, uint32_t va, uint32_t vb) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %3, %5, 0 offen lds\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %4, %5, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0a), "s"(m0b), "v"(va), "v"(vb), "s"(rs)
+        : "memory");
+}
+
+// Uniform (SGPR) copy of a buffer descriptor.
+__device__ __forceinline__ i32x4 uniform_rsrc(const i32x4& rs) {
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(rs[0]);
+    r[1] = __builtin_amdgcn_readfirstlane(rs[1]);
+    r[2] = __builtin_amdgcn_readfirstlane(rs[2]);
+    r[3] = __builtin_amdgcn_readfirstlane(rs[3]);
+    return r;
+}
+
+// Typed accesses through LDS (address space 3) pointers.
+template <class T>
+__device__ __forceinline__ T lds_ld(const lds_char* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) T*>(p);
+}
+template <class T>
+__device__ __forceinline__ void lds_st(lds_char* p, const T& v) {
+    *reinterpret_cast<__attribute__((address_space(3))) T*>(p) = v;
+}
+__device__ __forceinline__ u32x2 ds_read_tr16_at(const lds_char* p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_char*>(p)));
+    return __builtin_bit_cast(u32x2, v);
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane r receives element (r % 4) of the 8-byte

@@ -71,8 +71,9 @@ const ShapeClass* find_class(bool f32, int kc, int vc, int drc) {
     return nullptr;
 }
 
-// Validates sizes (pure host) and fills the plan.  No HIP call.
-gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan) {
+// Validates sizes (pure host) and fills the plan for the register-staged kernels or, with tok, for
+// the token-split LDS-DMA kernels (chunks of kTokChunk tokens).  No HIP call.
+gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = false) {
     if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
     if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_FORWARD_CAUSAL)
         return fail(GMA_ERROR_INVALID_VALUE, "unknown op %d", op);
@@ -112,14 +113,18 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan) {
     if (!plan->cls)
         return fail(GMA_ERROR_NOT_SUPPORTED, "no compiled kernel class for dtype=%s K=%d d_v=%d d_r=%d (padded %d/%d/%d)",
                     plan->f32 ? "f32" : "bf16", p->n_comp, p->d_value, p->d_route, kc, vc, drc);
-    const int C = plan->cls->c;
+    if (tok && !plan->cls->tok_out_causal)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "no token-split kernels for this class");
+    plan->dma = tok;
+    const int C = tok ? kTokChunk : plan->cls->c;
+    const int wg_per_cu = tok ? plan->cls->tok_wg_per_cu : plan->cls->wg_per_cu;
     const int64_t BH = plan->B * plan->H;
     plan->n_chunks = (plan->N + C - 1) / C;
     if (op == GMA_OP_RESPONSIBILITIES) {
         plan->P = (int)std::min<int64_t>(plan->n_chunks, INT32_MAX / 4);
         plan->seg_chunks = (int)((plan->n_chunks + plan->P - 1) / plan->P);
     } else {
-        const int64_t target = kComputeUnits * plan->cls->wg_per_cu;
+        const int64_t target = kComputeUnits * wg_per_cu;
         int64_t P = (target + BH - 1) / BH;
         if (P > plan->n_chunks) P = plan->n_chunks;
         if (P < 1) P = 1;
@@ -296,6 +301,19 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
                overlaps(ws, pl.total, v, nv) || overlaps(ws, pl.total, o, nv)))
         return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
 
+    // Token-split LDS-DMA kernels: bf16, rows in whole 16-byte chunks, 16-byte aligned bases, byte
+    // offsets within one (batch, head) slice (one chunk past the end included) below 2^31.
+    const bool dma = !pl.f32 && pl.cls->tok_out_causal && pl.d_r % 8 == 0 && pl.d_v % 8 == 0 &&
+                     !misaligned(qx, 16) && !misaligned(kx, 16) && !misaligned(v, 16) && !misaligned(o, 16) &&
+                     (pl.N + kTokChunk) * std::max(pl.d_r, pl.d_v) * 2 < (int64_t(1) << 31);
+    if (dma) {
+        st = make_plan(p, causal ? GMA_OP_FORWARD_CAUSAL : GMA_OP_FORWARD_BIDIR, &pl, true);
+        if (st != GMA_SUCCESS) return st;
+        if (ws_bytes < pl.total)
+            return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                        ws_bytes, pl.total);
+    }
+
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* w = reinterpret_cast<char*>(ws);
     st = launch_prep(pl, mu, rv, pr, w, s);
@@ -308,13 +326,9 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
     a.vec_x = vec_ok(qx, pl.d_r, pl.f32) && vec_ok(kx, pl.d_r, pl.f32);
     a.vec_v = vec_ok(v, pl.d_v, pl.f32);
     a.vec_o = vec_o_ok(o, pl.d_v, pl.f32);
-    // LDS-DMA staging: bf16, 16-byte rows chunks, aligned bases, 31-bit byte offsets per slice
-    const bool dma = !pl.f32 && pl.cls->dma_out_causal && pl.d_r % 8 == 0 && pl.d_v % 8 == 0 &&
-                     !misaligned(qx, 16) && !misaligned(kx, 16) && !misaligned(v, 16) && !misaligned(o, 16) &&
-                     pl.N * std::max(pl.d_r, pl.d_v) * 2 < (int64_t(1) << 31);
-    const main_launch_t f_agg = dma ? pl.cls->dma_agg : pl.cls->agg;
-    const main_launch_t f_causal = dma ? pl.cls->dma_out_causal : pl.cls->out_causal;
-    const main_launch_t f_bidir = dma ? pl.cls->dma_out_bidir : pl.cls->out_bidir;
+    const main_launch_t f_agg = dma ? pl.cls->tok_agg : pl.cls->agg;
+    const main_launch_t f_causal = dma ? pl.cls->tok_out_causal : pl.cls->out_causal;
+    const main_launch_t f_bidir = dma ? pl.cls->tok_out_bidir : pl.cls->out_bidir;
     const int grid = (int)(pl.B * pl.H * pl.P);
     const int64_t rec = (int64_t)pl.cls->kc * pl.cls->vc + pl.cls->kc;
     const bool need_agg = !causal || pl.P > 1;
@@ -350,7 +364,13 @@ extern "C" {
 size_t gma_workspace_size(const gma_problem_t* problem, int op) {
     Plan pl;
     if (make_plan(problem, op, &pl) != GMA_SUCCESS) return 0;
-    return pl.total;
+    size_t total = pl.total;
+    // the forward passes may take the token-split path (decided per call from pointer alignment)
+    Plan pt;
+    if (op != GMA_OP_RESPONSIBILITIES && pl.cls->tok_out_causal && make_plan(problem, op, &pt, true) == GMA_SUCCESS)
+        total = std::max(total, pt.total);
+    g_last_error.clear();
+    return total;
 }
 
 gma_status_t gma_responsibilities(const gma_problem_t* p, const void* x, const float* mu, const float* raw_var,
@@ -380,7 +400,7 @@ gma_status_t gma_responsibilities(const gma_problem_t* p, const void* x, const f
     a.gamma = gamma;
     a.vec_x = vec_ok(x, pl.d_r, pl.f32);
     const bool dma = !pl.f32 && pl.cls->dma_resp && pl.d_r % 8 == 0 && !misaligned(x, 16) &&
-                     pl.N * pl.d_r * 2 < (int64_t(1) << 31);
+                     (pl.N + pl.cls->c) * pl.d_r * 2 < (int64_t(1) << 31);
     const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
     const int grid = (int)(pl.B * pl.H * pl.P);
     return timed_launch(K_RESP, s, [&] { f_resp(a, grid, s); });

@@ -388,8 +388,9 @@ main_kernel(const MainArgs a) {
     const elem_t* vv = reinterpret_cast<const elem_t*>(a.v) + (int64_t)bh * N * a.d_v;
     elem_t* oo = reinterpret_cast<elem_t*>(a.o) + (int64_t)bh * N * a.d_v;
 
-    // buffer descriptors over this (batch, head) slice: reads past the end return 0, stores past
-    // the end are dropped
+    // buffer descriptors over this (batch, head) slice.  Every offset is passed as a vector offset
+    // (the range check covers only that part), so reads past the end return 0 and stores past the
+    // end are dropped.
     i32x4 rs_q, rs_k, rs_v;
     __amdgpu_buffer_rsrc_t rs_o;
     if constexpr (DMA) {
@@ -426,12 +427,12 @@ main_kernel(const MainArgs a) {
                     const int rb = fx / NSEG, sg = fx % NSEG;
                     const int rl = lane >> 3;
                     const int gc = (lane & 7) ^ xswz(rb * 8 + rl);
-                    soff = (uint32_t)((n0 + rb * 8) * a.d_r * 2);
-                    voff = (uint32_t)((rl * a.d_r + sg * 64 + gc * 8) * 2);
+                    soff = 0;
+                    voff = (uint32_t)(((n0 + rb * 8 + rl) * a.d_r + sg * 64 + gc * 8) * 2);
                 } else {
                     const int tt = fx / NKS2, ks2 = fx % NKS2;
-                    soff = (uint32_t)((n0 + tt * 16) * a.d_r * 2);
-                    voff = (uint32_t)((lr * a.d_r + ks2 * 32 + lg * 8) * 2);
+                    soff = 0;
+                    voff = (uint32_t)(((n0 + tt * 16 + lr) * a.d_r + ks2 * 32 + lg * 8) * 2);
                 }
                 if (isq) dma16(rs_q, raw + OFF_XQ + fx * 1024, voff, soff);
                 else dma16(rs_k, raw + OFF_XK + fx * 1024, voff, soff);
@@ -441,9 +442,8 @@ main_kernel(const MainArgs a) {
                 const int rl = lane / CPR;
                 const int row = r0 + rl;
                 const int gch = (lane % CPR) ^ (row % CPR);
-                const uint32_t soff = (uint32_t)((n0 + r0) * a.d_v * 2);
-                const uint32_t voff = (uint32_t)((rl * a.d_v + gch * 8) * 2);
-                dma16(rs_v, raw + OFF_V + fv * 1024, voff, soff);
+                const uint32_t voff = (uint32_t)(((n0 + row) * a.d_v + gch * 8) * 2);
+                dma16(rs_v, raw + OFF_V + fv * 1024, voff, 0);
             }
         }
     };

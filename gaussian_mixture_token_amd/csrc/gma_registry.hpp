@@ -3,6 +3,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include "gma_kernels.hpp"
+#include "gma_tok.hpp"
 
 namespace gma {
 
@@ -15,9 +16,15 @@ struct ShapeClass {
     int f32, kc, vc, drc, w, c;
     int wg_per_cu;   // workgroups per compute unit the LDS and register budgets allow
     prep_launch_t prep;
-    main_launch_t resp, agg, out_bidir, out_causal;              // register-staged inputs
-    main_launch_t dma_resp, dma_agg, dma_out_bidir, dma_out_causal;  // LDS-DMA staged (bf16 only)
+    main_launch_t resp, agg, out_bidir, out_causal;   // main_kernel, register-staged inputs
+    main_launch_t dma_resp;                           // main_kernel, LDS-DMA staged (bf16 only)
+    // token-split kernels (bf16, LDS-DMA staged, 4 wavefronts, chunks of 64 tokens); null where the
+    // class has none
+    int tok_wg_per_cu;
+    main_launch_t tok_agg, tok_out_bidir, tok_out_causal;
 };
+
+constexpr int kTokChunk = 64;
 
 const ShapeClass* classes_f32(int* count);
 const ShapeClass* classes_bf16(int* count);
@@ -33,6 +40,11 @@ void launch_main(const MainArgs& a, int grid, hipStream_t s) {
     hipLaunchKernelGGL((main_kernel<F32, KC, VC, DRC, W, C, MODE, DMA, WPE>), dim3(grid), dim3(W * 64), 0, s, a);
 }
 
+template <int KC, int VC, int DRC, int MODE, int WPE>
+void launch_tok(const MainArgs& a, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((tok_kernel<KC, VC, DRC, MODE, WPE>), dim3(grid), dim3(256), 0, s, a);
+}
+
 #define GMA_MAIN_SET(F32, KC, VC, DRC, W, C, DMA, WPE)                                        \
     &launch_main<F32, KC, 16 * W, DRC, W, C, MODE_RESP, DMA, WPE>,                            \
         &launch_main<F32, KC, VC, DRC, W, C, MODE_AGG, DMA, WPE>,                             \
@@ -42,13 +54,25 @@ void launch_main(const MainArgs& a, int grid, hipStream_t s) {
 #define GMA_SHAPE_CLASS_F32(KC, VC, DRC, W, C)                                                \
     ShapeClass {                                                                              \
         1, KC, VC, DRC, W, C, 1, &launch_prep<true, KC, DRC>, GMA_MAIN_SET(true, KC, VC, DRC, W, C, false, 1), \
-            nullptr, nullptr, nullptr, nullptr                                                \
+            nullptr, 0, nullptr, nullptr, nullptr                                             \
     }
 
-#define GMA_SHAPE_CLASS_BF16(KC, VC, DRC, W, C, WPE)                                          \
+// WPE: wavefronts per SIMD of the LDS-DMA responsibilities kernel; TWPE: of the token-split kernels
+#define GMA_SHAPE_CLASS_BF16(KC, VC, DRC, W, C, WPE, TWPE)                                    \
     ShapeClass {                                                                              \
         0, KC, VC, DRC, W, C, WPE, &launch_prep<false, KC, DRC>,                              \
-            GMA_MAIN_SET(false, KC, VC, DRC, W, C, false, 1), GMA_MAIN_SET(false, KC, VC, DRC, W, C, true, WPE) \
+            GMA_MAIN_SET(false, KC, VC, DRC, W, C, false, 1),                                 \
+            &launch_main<false, KC, 16 * W, DRC, W, C, MODE_RESP, true, WPE>, TWPE,           \
+            &launch_tok<KC, VC, DRC, MODE_AGG, TWPE>, &launch_tok<KC, VC, DRC, MODE_OUT_BIDIR, TWPE>, \
+            &launch_tok<KC, VC, DRC, MODE_OUT_CAUSAL, TWPE>                                   \
+    }
+
+// the same without token-split kernels
+#define GMA_SHAPE_CLASS_BF16_NOTOK(KC, VC, DRC, W, C, WPE)                                    \
+    ShapeClass {                                                                              \
+        0, KC, VC, DRC, W, C, WPE, &launch_prep<false, KC, DRC>,                              \
+            GMA_MAIN_SET(false, KC, VC, DRC, W, C, false, 1),                                 \
+            &launch_main<false, KC, 16 * W, DRC, W, C, MODE_RESP, true, WPE>, 0, nullptr, nullptr, nullptr \
     }
 
 }  // namespace gma

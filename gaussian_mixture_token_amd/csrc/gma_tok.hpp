@@ -1,0 +1,671 @@
+// Token-split kernels of the bf16 forward path (LDS-DMA staging, one workgroup of four
+// wavefronts, chunks of 64 tokens).
+//
+// Method: page "Attention par Mélange Gaussien (GMA)", section "Méthodologie", sub-section
+// "Mécanisme Central", items 1-3 (responsibilities of a diagonal GMM, write Vt = Gamma_K^T V and
+// Z = Gamma_K^T 1, read O = Gamma_Q Vt / (Gamma_Q Z + eps), causal variant by prefix sums).
+//
+// Work split.  Wave w owns tokens 16w .. 16w+15 of every chunk for everything that is per token:
+// the logits of all K components (one MFMA GEMM [a | b] . [x^2 ; x]; the [a | b] operand
+// fragments of every component stay in AGPRs for the whole kernel), the softmax over K (inside
+// the wave: no exchange) and the output rows.  The state [Vt | Z] is split by components (pairs
+// of 16-row tiles) and, where there are fewer pairs than waves, by d_v tiles; each wave keeps its
+// share in fp32 registers and publishes it once per chunk to LDS as bf16 operand fragments.
+//
+// Causal chunk c:
+//   B0   barrier: the previous chunk's LDS reads are done.  Start the DMA of chunk c+1 (own X
+//        rows, a quarter of V).
+//   P1   publish the state before chunk c (bf16 state^T fragments, Z fragments); logits and
+//        softmax of own tokens for K and Q.  Gamma_K (normalised) goes to LDS as bf16 rows;
+//        Gamma_Q stays in registers as operand fragments, unnormalised: the row scale cancels
+//        between numerator and denominator except in eps, which gets eps * rowsum.
+//   B1   barrier: Gamma_K rows, V of the chunk and the published state are visible.
+//   P2   own query rows: O^T = state^T Gamma_Q^T (inter-chunk) + V^T tril(Gamma_Q Gamma_K^T)^T
+//        (intra-chunk), denominators Gamma_Q . Z + rowsum(tril) + eps * rowsum(Gamma_Q); state
+//        update of the owned share from Gamma_K^T [V | 1].
+// The denominator Gamma_Q . Z uses Z split into two bf16 halves (hi + lo, about 16 significant
+// bits) and a row of ones in one extra MFMA tile, so it sees exactly the bf16 Gamma_Q the
+// numerator sees.
+#pragma once
+#include <type_traits>
+
+#include "gma_kernels.hpp"
+
+namespace gma {
+
+template <int KC, int VC, int DRC, int MODE, int WPE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
+tok_kernel(const MainArgs a) {
+    constexpr int W = 4;
+    constexpr int C = 16 * W;
+    constexpr int NCT = KC / 16;   // component tiles
+    constexpr int NKQ = KC / 32;   // component fragment steps (pairs of tiles)
+    constexpr int NVT = VC / 16;   // d_v tiles
+    constexpr int NKS2 = DRC / 32; // fragment steps over d_r (x^2 part; the x part follows)
+    constexpr int NSEG = DRC / 64; // 128-byte segments per staged X row
+    constexpr bool NEED_Q = (MODE == MODE_OUT_BIDIR) || (MODE == MODE_OUT_CAUSAL);
+    constexpr bool NEED_K = (MODE == MODE_AGG) || (MODE == MODE_OUT_CAUSAL);
+    constexpr bool NEED_V = NEED_K;
+    constexpr bool CAUSAL = MODE == MODE_OUT_CAUSAL;
+    constexpr bool OUT = NEED_Q;
+    static_assert(MODE != MODE_RESP, "responsibilities use main_kernel");
+    static_assert(DRC >= 64 && DRC % 64 == 0 && NSEG <= 2, "X rows are staged in one or two 128-byte segments");
+    static_assert(KC % 32 == 0 && VC % 16 == 0, "tile shapes");
+    // state ownership: wave w owns component pairs kq0 .. kq0+KQW-1 and d_v tiles vt0 .. vt0+VTW-1
+    constexpr int KQW = (NKQ >= W) ? NKQ / W : 1;
+    constexpr int WPK = (NKQ >= W) ? 1 : W / NKQ;   // waves sharing one component pair
+    constexpr int VTW = NVT / WPK;
+    static_assert((NKQ >= W) ? (NKQ % W == 0) : (W % NKQ == 0), "component pairs must split across waves");
+    static_assert(NVT % WPK == 0 && VTW >= 1, "d_v tiles must split across the waves of a pair");
+
+    // ---- LDS
+    constexpr int NSIDE = (NEED_Q ? 1 : 0) + (NEED_K ? 1 : 0);
+    constexpr int XSIDE = 16 * DRC * 2;            // one wave's 16 rows of Q_X or K_X
+    constexpr int XWAVE = NSIDE * XSIDE;
+    constexpr int XBUF = W * XWAVE;
+    constexpr int VBUF = C * VC * 2;
+    constexpr int NXB = 2 * NSEG;                  // X DMA blocks per wave, side and chunk
+    constexpr int NXD = NSIDE * NXB;               // X DMA blocks per wave and chunk
+    constexpr int NVB = NEED_V ? VBUF / 1024 : 0;  // V DMA blocks per chunk
+    constexpr int NVD = NVB / W;                   // ... per wave
+    constexpr int NST = OUT ? NVT : 0;             // O stores per wave and chunk
+    static_assert(NVB % W == 0 && (NVD == 0 || NVD == 2 || NVD == 4), "V blocks must split across waves");
+    static_assert(NXD + NVD + NST < 64, "vmcnt range");
+    constexpr int CPR = VC / 8;                    // 16-byte chunks per V row
+    constexpr int RPB = 1024 / (VC * 2);           // V rows per DMA block
+    static_assert((RPB == 4 || RPB == 8) && RPB * CPR == 64, "V DMA blocks");
+    constexpr int GKR = KC * 2 + 32;               // bytes per Gamma_K row (padded)
+    constexpr int OFF_XQ = 0;
+    constexpr int OFF_XK = NEED_Q ? XSIDE : 0;
+
+    __shared__ __attribute__((aligned(16))) char s_x[2 * XBUF];
+    __shared__ __attribute__((aligned(16))) char s_v[NEED_V ? 2 * VBUF : 16];
+    __shared__ __attribute__((aligned(16))) char s_gk[NEED_K ? C * GKR : 16];
+    __shared__ __attribute__((aligned(16))) char s_st[OUT ? NVT * NKQ * 1024 : 16];   // state^T fragments
+    __shared__ __attribute__((aligned(16))) char s_zx[OUT ? NKQ * 1024 : 16];         // [Z_hi; Z_lo; 1; 0] fragments
+    __shared__ __attribute__((aligned(16))) float s_c[KC];
+    __shared__ __attribute__((aligned(16))) float s_z[KC];   // Z of the state before the current chunk
+    lds_char* const LX = (lds_char*)s_x;
+    lds_char* const LV = (lds_char*)s_v;
+    lds_char* const LGK = (lds_char*)s_gk;
+    lds_char* const LST = (lds_char*)s_st;
+    lds_char* const LZX = (lds_char*)s_zx;
+    lds_char* const LC = (lds_char*)s_c;
+    lds_char* const LZ = (lds_char*)s_z;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    [[maybe_unused]] const int lr = lane & 15;
+    [[maybe_unused]] const int lg = lane >> 4;
+    const int bh = blockIdx.x / a.Pg;
+    const int sidx = blockIdx.x % a.Pg;
+    const int h = bh % a.H;
+    const int64_t N = a.N;
+    const int64_t n_chunks = (N + C - 1) / C;
+    const int64_t ch0 = (int64_t)sidx * a.seg_chunks;
+    const int64_t ch1 = (ch0 + a.seg_chunks < n_chunks) ? ch0 + a.seg_chunks : n_chunks;
+    const int kq0 = (NKQ >= W) ? w * KQW : w / WPK;
+    const int vt0 = (NKQ >= W) ? 0 : (w % WPK) * VTW;
+    const bool zown = (NKQ >= W) || (w % WPK == 0);   // this wave keeps Z of its components
+    const uint32_t d_r = (uint32_t)a.d_r, d_v = (uint32_t)a.d_v;
+
+    const uint16_t* qx = reinterpret_cast<const uint16_t*>(a.qx) + (int64_t)bh * N * a.d_r;
+    const uint16_t* kx = reinterpret_cast<const uint16_t*>(a.kx) + (int64_t)bh * N * a.d_r;
+    const uint16_t* vv = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)bh * N * a.d_v;
+    uint16_t* oo = reinterpret_cast<uint16_t*>(a.o) + (int64_t)bh * N * a.d_v;
+    // buffer descriptors over this (batch, head) slice.  Every byte offset is a vector offset (the
+    // range check covers only that part), so rows past N read as zeros and their stores are dropped.
+    i32x4 rs_q, rs_k, rs_v;
+    __amdgpu_buffer_rsrc_t rs_o;
+    if constexpr (NEED_Q) rs_q = uniform_rsrc(make_rsrc_words(qx, (uint32_t)(N * a.d_r * 2)));
+    if constexpr (NEED_K) rs_k = uniform_rsrc(make_rsrc_words(kx, (uint32_t)(N * a.d_r * 2)));
+    if constexpr (NEED_V) rs_v = uniform_rsrc(make_rsrc_words(vv, (uint32_t)(N * a.d_v * 2)));
+    if constexpr (OUT) rs_o = make_rsrc(oo, (uint32_t)(N * a.d_v * 2));
+
+    // Lane id as seen inside the chunk loop: reassigned (opaque to the optimiser) at the start of every
+    // chunk, so that lane-dependent offsets are recomputed there rather than held in registers
+    // across the loop.  Every lambda below derives its lane quantities from it.
+    int lane_v = lane;
+
+    // ---- staged X: per wave and side, 16 rows in blocks of 8 rows x 128 bytes (block rb * NSEG + sg
+    // = rows 8 rb .. 8 rb + 7, dims 64 sg .. 64 sg + 63).  The 16-byte chunks of row r are
+    // XOR-swizzled by (r & 7) ^ (r >> 3) so that fragment reads are conflict-free.  Fragment step ks
+    // (32 dims) of row lr for lane group lg is chunk 4 (ks & 1) + lg of segment ks / 2.
+    auto xoff = [&](int ks) -> int {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        const int xsw = lg ^ ((lr & 3) ^ ((lr >> 3) & 1));
+        const int hi = (((lr >> 2) & 1) ^ (ks & 1)) << 2;
+        return ((lr >> 3) * NSEG) * 1024 + (lr & 7) * 128 + ((xsw | hi) << 4) + (ks >> 1) * 1024;
+    };
+    // DMA: lane l of block (rb, sg) fetches row 8 rb + l/8, global chunk (l % 8) ^ (l/8) ^ rb of
+    // segment sg; the vector part of its byte offset below, the rest is per block and chunk
+    // V: block fv holds rows RPB fv .. RPB fv + RPB - 1 chunk-major: 16-byte chunk c of row r of the
+    // block at (c RPB + r) 16.  Lane l fetches row l % RPB, chunk l / RPB.
+    const uint32_t lx_base = lds_addr(LX), lv_base = lds_addr(LV);
+
+    auto issue = [&](int64_t ch, int buf) {
+        const uint32_t lane = (uint32_t)lane_v, rl = lane >> 3;
+        const uint32_t xl[2] = {(rl * d_r + (((lane & 7) ^ rl) * 8)) * 2, (rl * d_r + (((lane & 7) ^ rl ^ 1) * 8)) * 2};
+        const uint32_t n0 = (uint32_t)(ch * C);
+        const uint32_t xrow = (n0 + 16 * w) * d_r * 2;   // byte offset of the wave's first row
+        const uint32_t m0x = lx_base + buf * XBUF + w * XWAVE;
+        // lane parts made opaque here, so that the per-block sums are formed per chunk (one add each)
+        // rather than kept in registers across the loop
+        const uint32_t x0 = xl[0] + xrow, x1 = xl[1] + xrow + 16 * d_r;
+#pragma unroll
+        for (int sd = 0; sd < NSIDE; ++sd) {
+            const i32x4& rs = (NEED_Q && sd == 0) ? rs_q : rs_k;
+            const uint32_t m0 = m0x + sd * XSIDE;
+            if constexpr (NSEG == 2) dma16x4(rs, m0, m0 + 1024, m0 + 2048, m0 + 3072, x0, x0 + 128, x1, x1 + 128);
+            else dma16x2(rs, m0, m0 + 1024, x0, x1);
+        }
+        if constexpr (NEED_V) {
+            const uint32_t vstep = W * RPB * d_v * 2;
+            const uint32_t vl = ((lane % RPB) * d_v + (lane / RPB) * 8) * 2;
+            const uint32_t v0 = vl + (n0 + w * RPB) * d_v * 2;
+            const uint32_t m0 = lv_base + buf * VBUF + w * 1024;
+            if constexpr (NVD == 4)
+                dma16x4(rs_v, m0, m0 + W * 1024, m0 + 2 * W * 1024, m0 + 3 * W * 1024, v0, v0 + vstep, v0 + 2 * vstep,
+                        v0 + 3 * vstep);
+            else dma16x2(rs_v, m0, m0 + W * 1024, v0, v0 + vstep);
+        }
+    };
+
+    // ---- [a | b] operand fragments of every component (AGPRs), logit constants c (LDS)
+    f16x8 abf[NCT][2 * NKS2];
+    {
+        const f16x8* abg = reinterpret_cast<const f16x8*>(a.ab) + (int64_t)h * NCT * 2 * NKS2 * 64;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int ks = 0; ks < 2 * NKS2; ++ks) {
+                abf[ct][ks] = abg[((int64_t)ct * 2 * NKS2 + ks) * 64 + lane];
+                pin_agpr(abf[ct][ks]);
+            }
+        for (int k = tid; k < KC; k += 256) s_c[k] = a.cvec[(int64_t)h * KC + k];
+    }
+
+    // ---- state share: st[kqi][hh][vti] = rows (components) of tile 2(kq0+kqi)+hh, columns of d_v
+    // tile vt0+vti, in accumulator layout; Z in LDS (s_z), updated by the wave owning the components
+    constexpr bool HAS_STATE = NEED_K || OUT;
+    f32x4 st[HAS_STATE ? KQW : 1][2][HAS_STATE ? VTW : 1];
+    const int64_t rec = (int64_t)KC * VC + KC;
+    float* segrec = a.seg + ((int64_t)bh * a.P + sidx) * rec;
+    if constexpr (HAS_STATE) {
+        const bool load = (MODE == MODE_OUT_BIDIR) || (CAUSAL && a.has_carry);
+        const float* src = (MODE == MODE_OUT_BIDIR) ? a.seg + (int64_t)bh * a.P * rec : segrec;
+#pragma unroll
+        for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int ct = 2 * (kq0 + kqi) + hh;
+#pragma unroll
+                for (int vti = 0; vti < VTW; ++vti) {
+                    const int vt = vt0 + vti;
+                    st[kqi][hh][vti] = load ? *reinterpret_cast<const f32x4*>(src + ((int64_t)(ct * NVT + vt) * 64 + lane) * 4)
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        for (int k = tid; k < KC; k += 256) s_z[k] = load ? src[(int64_t)KC * VC + k] : 0.f;
+    }
+    // bf16 state^T fragments: (vt, kq) is the A operand of O^T(vt) += state^T(vt, kq) . Gamma_Q^T(kq);
+    // lane (r, g) holds d_v column 16 vt + r, components 32 kq + 4g + i and 32 kq + 16 + 4g + i
+    auto write_state = [&]() {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+            for (int vti = 0; vti < VTW; ++vti)
+                lds_st<bf16x8>(LST + ((vt0 + vti) * NKQ + kq0 + kqi) * 1024 + lane * 16,
+                               pack_pair(st[kqi][0][vti], st[kqi][1][vti]));
+    };
+    // Z fragments for the denominators: row 4m + 0 holds Z rounded to bf16, row 4m + 1 the bf16 of
+    // the remainder, row 4m + 2 ones (the row sum of Gamma_Q), row 4m + 3 zeros.  Branch-free: both
+    // halves are formed on every lane and the lane's row type selects by bit masks.
+    auto write_z = [&]() {
+        if (!zown) return;
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        const uint32_t typ = (uint32_t)lr & 3u;
+        const uint32_t mh = (typ == 0u) ? 0xffffffffu : 0u;
+        const uint32_t ml = (typ == 1u) ? 0xffffffffu : 0u;
+        const uint32_t mo = (typ == 2u) ? 0x3f803f80u : 0u;   // two bf16 ones
+#pragma unroll
+        for (int kqi = 0; kqi < KQW; ++kqi) {
+            u32x4 f;
+            const f32x4 zq[2] = {lds_ld<f32x4>(LZ + ((kq0 + kqi) * 32 + lg * 4) * 4),
+                                 lds_ld<f32x4>(LZ + ((kq0 + kqi) * 32 + 16 + lg * 4) * 4)};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float z0 = zq[p >> 1][2 * (p & 1)], z1 = zq[p >> 1][2 * (p & 1) + 1];
+                const uint32_t hb = pack2_bf16(z0, z1);
+                const uint32_t lb = pack2_bf16(z0 - __uint_as_float(hb << 16), z1 - __uint_as_float(hb & 0xffff0000u));
+                f[p] = (hb & mh) | (lb & ml) | mo;
+            }
+            lds_st<u32x4>(LZX + (kq0 + kqi) * 1024 + lane * 16, f);
+        }
+    };
+    // the bidirectional pass reads the fixed total state; the causal pass publishes the state before
+    // each chunk at the start of that chunk (after barrier B0, read after B1)
+    if constexpr (MODE == MODE_OUT_BIDIR) {
+        lds_barrier();   // s_z
+        write_state();
+        write_z();
+    }
+
+    if (ch0 < ch1) issue(ch0, 0);
+    lds_barrier();   // s_c (and the bidirectional state) visible
+
+    // ---- Gamma_K rows: row-major [token][component] bf16, rows padded by 32 bytes (transposed
+    // reads of 16 rows fall in distinct banks; addresses stay affine in the component)
+    auto gk_off = [](int row, int col) -> int { return row * GKR + col * 2; };
+    // A of S^T = Gamma_K Gamma_Q^T: lane = token 16 J + r, slots = components of pair kq
+    auto gk_token_frag = [&](int J, int kq) -> bf16x8 {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        const int row = J * 16 + lr;
+        const u32x2 lo = lds_ld<u32x2>(LGK + gk_off(row, (2 * kq) * 16 + lg * 4));
+        const u32x2 hi = lds_ld<u32x2>(LGK + gk_off(row, (2 * kq + 1) * 16 + lg * 4));
+        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    // A of the state update Gamma_K^T V: lane = component 16 ct + r, slots = tokens of step tk
+    // (tokens 32 tk + 4g + i and 32 tk + 16 + 4g + i, the order of the V fragments)
+    auto gk_comp_frag = [&](int ct, int tk) -> bf16x8 {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        const int q = lane & 3, i4 = (lane >> 2) & 3;
+        u32x2 part[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int row = (2 * tk + hf) * 16 + lg * 4 + i4;
+            part[hf] = ds_read_tr16_at(LGK + gk_off(row, ct * 16 + 4 * q));
+        }
+        return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+    };
+    // V^T fragment (d_v tile vt, token step tk) from the chunk-major V blocks: A of O^T += V^T S^T
+    // and, with the same contents, B of the state update.  Lane 16g + 4 i4 + q reads row
+    // 32 tk + 16 hf + 4g + i4, chunk 2 vt + q/2, half q % 2; a 16-lane group covers 128 contiguous
+    // bytes (conflict-free) and the address is affine in vt and tk.
+    auto v_frag = [&](const lds_char* vb, int vt, int tk) -> bf16x8 {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        const int v_lane_off = (((lg * 4 + ((lane >> 2) & 3)) / RPB) * 1024) +
+                               ((((lane & 3) >> 1) * RPB + (lg * 4 + ((lane >> 2) & 3)) % RPB) * 16) + (lane & 1) * 8;
+        u32x2 part[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            part[hf] = ds_read_tr16_at(vb + v_lane_off + ((2 * tk + hf) * (16 / RPB)) * 1024 + (2 * vt) * RPB * 16);
+        return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+    };
+
+    // fp16 operand fragments [x ; x^2] of own tokens (bf16 -> fp16 is exact in the supported range)
+    auto x_frags = [&](const lds_char* xs, f16x8 (&xf)[NKS2], f16x8 (&x2)[NKS2]) {
+        u32x4 raw[NKS2];
+#pragma unroll
+        for (int ks = 0; ks < NKS2; ++ks) raw[ks] = lds_ld<u32x4>(xs + xoff(ks));
+#pragma unroll
+        for (int ks = 0; ks < NKS2; ++ks) {
+            xf[ks] = bf16x8_bits_to_f16x8(raw[ks]);
+            x2[ks] = xf[ks] * xf[ks];
+        }
+    };
+    // logits^T of own tokens: acc[ct] rows = components 16 ct + 4g + i, column = token 16 w + r
+    auto logits = [&](const f16x8 (&xf)[NKS2], const f16x8 (&x2)[NKS2], f32x4 (&acc)[NCT]) {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
+#pragma unroll
+        for (int ks = 0; ks < NKS2; ++ks) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                pin_agpr(abf[ct][ks]);
+                mma(acc[ct], abf[ct][ks], x2[ks]);
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                pin_agpr(abf[ct][ks + NKS2]);
+                mma(acc[ct], abf[ct][ks + NKS2], xf[ks]);
+            }
+        }
+    };
+    // 2^(l - max_k l) in place (base-2 logits)
+    auto exp_rows = [&](f32x4 (&acc)[NCT]) {
+        float m = acc[0][0];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, acc[ct][i]);
+        m = group4_max(m);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[ct][i] = fast_exp2(acc[ct][i] - m);
+    };
+    // own Gamma_K rows (normalised; rows past N are zero) into LDS
+    auto write_gk = [&](f32x4 (&acc)[NCT], bool valid) {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        float s = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s += acc[ct][i];
+        s = group4_sum(s);
+        const float r = valid ? fast_rcp(s) : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) lds_st<bf16x4>(LGK + gk_off(16 * w + lr, ct * 16 + lg * 4), pack4(acc[ct] * r));
+    };
+    // own output rows: lane (r, g) holds d_v 16 vt + 4g .. +3 of token 16 w + r.  Without d_v padding
+    // the column offsets are instruction immediates; with padding, pad columns get an offset past
+    // the end of the buffer (dropped), computed without compares.
+    auto store_tile = [&](const f32x4& o, float inv, uint32_t base, int vt) {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        const u32x2 v = __builtin_bit_cast(u32x2, pack4(o * inv));
+        if (d_v == VC) {
+            __builtin_amdgcn_raw_buffer_store_b64(v, rs_o, base, vt * 32, 0);
+        } else {
+            const int spare = (int)d_v - 1 - (lg * 4) - vt * 16;   // < 0 for pad columns
+            store_b64(rs_o, v, (base + vt * 32) | ((uint32_t)(spare >> 31) & 0x80000000u));
+        }
+    };
+    auto row_base = [&](uint32_t tok) -> uint32_t { return (tok * d_v + (lane_v >> 4) * 4) * 2; };
+
+    // causal mask of the intra-chunk tiles: key 16 J + 4g + i is kept for query 16 w + r when
+    // 16 J + i <= 16 w + r - 4g; as a factor 0 / 1 from a clamped difference (no per-element compare)
+    auto keep = [&](int k) -> float {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        return __builtin_amdgcn_fmed3f((float)(16 * w + lr - 4 * lg + 1 - k), 0.f, 1.f);
+    };
+    const uint32_t N32 = (uint32_t)N;
+
+    auto body = [&](auto buf_tag, int64_t ch) {
+        constexpr int BUF = decltype(buf_tag)::value;
+        lane_v = opaque_v(lane);
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        const uint32_t n0 = (uint32_t)(ch * C);
+        const bool first = ch == ch0;
+        const bool has_next = ch + 1 < ch1;
+        const lds_char* xw = LX + BUF * XBUF + w * XWAVE;
+        const lds_char* vb = LV + (NEED_V ? BUF * VBUF : 0);
+        const uint32_t tok = n0 + 16 * w + lr;
+
+        // own X rows of this chunk landed (V of the chunk and the previous chunk's stores may
+        // still be in flight)
+        if (first) wait_vmcnt<NVD>();
+        else wait_vmcnt<NVD + NST>();
+        if constexpr (NEED_K) lds_barrier();   // B0
+        if (has_next) issue(ch + 1, BUF ^ 1);
+
+        if constexpr (MODE == MODE_OUT_BIDIR) {
+            // Gamma_Q of own tokens, then O^T = state^T Gamma_Q^T with the fixed total state
+            f16x8 xf[NKS2], x2[NKS2];
+            x_frags(xw + OFF_XQ, xf, x2);
+            f32x4 acc[NCT];
+            logits(xf, x2, acc);
+            exp_rows(acc);
+            bf16x8 pq[NKQ];
+#pragma unroll
+            for (int kq = 0; kq < NKQ; ++kq) pq[kq] = pack_pair(acc[2 * kq], acc[2 * kq + 1]);
+            f32x4 oacc[NVT];
+            f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) oacc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kq = 0; kq < NKQ; ++kq) {
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt)
+                    mma(oacc[vt], lds_ld<bf16x8>(LST + (vt * NKQ + kq) * 1024 + lane * 16), pq[kq]);
+                mma(dx, lds_ld<bf16x8>(LZX + kq * 1024 + lane * 16), pq[kq]);
+            }
+            const float inv = fast_rcp(dx[0] + dx[1] + a.eps * dx[2]);
+            const uint32_t base = row_base(tok);
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) store_tile(oacc[vt], inv, base, vt);
+            return;
+        } else {
+            // ---- P1
+            bf16x8 pq[CAUSAL ? NKQ : 1];
+            if constexpr (CAUSAL) {
+                // Step ks of region A issues the K-side logits MFMAs of fragment step ks and, beside them,
+                // the fp16 conversion of Q_X step ks and a share of the state publication; step ks of
+                // region B issues the Q-side logits MFMAs of step ks beside a quarter of the K-side
+                // softmax.  Region C (the Q-side softmax) has no matrix work beside it.
+                f16x8 kxf[NKS2], kx2[NKS2];
+                x_frags(xw + OFF_XK, kxf, kx2);
+                u32x4 qraw[NKS2];
+#pragma unroll
+                for (int ks = 0; ks < NKS2; ++ks) qraw[ks] = lds_ld<u32x4>(xw + OFF_XQ + xoff(ks));
+                f32x4 acck[NCT], accq[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) acck[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
+                f16x8 qxf[NKS2], qx2[NKS2];
+                fence();
+                constexpr int NPUB = KQW * VTW;   // state fragments to publish
+#pragma unroll
+                for (int ks = 0; ks < NKS2; ++ks) {
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        pin_agpr(abf[ct][ks]);
+                        mma(acck[ct], abf[ct][ks], kx2[ks]);
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        pin_agpr(abf[ct][ks + NKS2]);
+                        mma(acck[ct], abf[ct][ks + NKS2], kxf[ks]);
+                    }
+                    qxf[ks] = bf16x8_bits_to_f16x8(qraw[ks]);
+                    qx2[ks] = qxf[ks] * qxf[ks];
+#pragma unroll
+                    for (int j = ks; j < NPUB; j += NKS2) {
+                        const int kqi = j / VTW, vti = j % VTW;
+                        lds_st<bf16x8>(LST + ((vt0 + vti) * NKQ + kq0 + kqi) * 1024 + lane * 16,
+                                       pack_pair(st[kqi][0][vti], st[kqi][1][vti]));
+                    }
+                    if (ks == NKS2 - 1) write_z();
+                    fence();
+                }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) accq[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
+                // K-side softmax in four parts: max; exp of the first half; exp of the second half;
+                // row sum, normalisation and the Gamma_K rows to LDS
+                float mk = 0.f, sk = 0.f;
+                auto ksoft = [&](int part) {
+                    if (part == 0) {
+                        float m = acck[0][0];
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) m = fmaxf(m, acck[ct][i]);
+                        mk = group4_max(m);
+                    } else if (part == 1 || part == 2) {
+                        const int c0 = (part - 1) * (NCT / 2);
+#pragma unroll
+                        for (int ct = c0; ct < c0 + NCT / 2; ++ct)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acck[ct][i] = fast_exp2(acck[ct][i] - mk);
+                    } else {
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) sk += acck[ct][i];
+                        sk = group4_sum(sk);
+                        const float r = (tok < N32) ? fast_rcp(sk) : 0.f;
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+                            lds_st<bf16x4>(LGK + gk_off(16 * w + lr, ct * 16 + lg * 4), pack4(acck[ct] * r));
+                    }
+                };
+                fence();
+#pragma unroll
+                for (int ks = 0; ks < NKS2; ++ks) {
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        pin_agpr(abf[ct][ks]);
+                        mma(accq[ct], abf[ct][ks], qx2[ks]);
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        pin_agpr(abf[ct][ks + NKS2]);
+                        mma(accq[ct], abf[ct][ks + NKS2], qxf[ks]);
+                    }
+#pragma unroll
+                    for (int part = ks * 4 / NKS2; part < (ks + 1) * 4 / NKS2; ++part) ksoft(part);
+                    interleave_mfma_valu<2 * NCT, 3>();
+                    fence();
+                }
+                exp_rows(accq);
+#pragma unroll
+                for (int kq = 0; kq < NKQ; ++kq) pq[kq] = pack_pair(accq[2 * kq], accq[2 * kq + 1]);
+            } else {
+                f16x8 kxf[NKS2], kx2[NKS2];
+                x_frags(xw + OFF_XK, kxf, kx2);
+                f32x4 acck[NCT];
+                logits(kxf, kx2, acck);
+                exp_rows(acck);
+                write_gk(acck, tok < N32);
+            }
+
+            // own V blocks of this chunk landed, then B1
+            if (first) {
+                if (has_next) wait_vmcnt<NXD + NVD>();
+                else wait_vmcnt<0>();
+            } else {
+                if (has_next) wait_vmcnt<NST + NXD + NVD>();
+                else wait_vmcnt<NST>();
+            }
+            lds_barrier();   // B1
+
+            // ---- P2
+            bf16x8 gkc[KQW][2][2];
+#pragma unroll
+            for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int tk = 0; tk < 2; ++tk) gkc[kqi][hh][tk] = gk_comp_frag(2 * (kq0 + kqi) + hh, tk);
+
+            bf16x8 sfr[2];
+            float inv = 0.f;
+            if constexpr (CAUSAL) {
+                // intra-chunk affinities of own queries S^T(J, w) = Gamma_K[J] Gamma_Q[w]^T for all four
+                // key blocks (the same work on every wave), causally masked; operand fragments over
+                // the two token steps and their column sums.  Component steps outermost, so that
+                // consecutive MFMAs go to independent accumulators.
+                f32x4 sacc[4];
+                f32x4 dx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int J = 0; J < 4; ++J) sacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kq = 0; kq < NKQ; ++kq) {
+#pragma unroll
+                    for (int J = 0; J < 4; ++J) mma(sacc[J], gk_token_frag(J, kq), pq[kq]);
+                    // denominators: Gamma_Q . Z (hi + lo) and eps * rowsum(Gamma_Q)
+                    mma(dx, lds_ld<bf16x8>(LZX + kq * 1024 + lane * 16), pq[kq]);
+                }
+#pragma unroll
+                for (int J = 0; J < 4; ++J)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sacc[J][i] *= keep(16 * J + i);
+                const bf16x8 ones = ones_frag<bf16x8>();
+                f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    sfr[t] = pack_pair(sacc[2 * t], sacc[2 * t + 1]);
+                    mma(dacc, ones, sfr[t]);
+                }
+                inv = fast_rcp(dx[0] + dx[1] + a.eps * dx[2] + dacc[0]);
+            }
+            const uint32_t obase = row_base(tok);
+
+            // groups of d_v tiles: inter (state before the chunk) and intra output of own queries, state
+            // update of the owned share; within a group consecutive MFMAs use independent accumulators
+            constexpr bool ALL_VT = (VTW == NVT);
+            constexpr int VG = (NVT >= 4) ? 4 : NVT;
+            static_assert(NVT % VG == 0, "d_v tile groups");
+            if constexpr (CAUSAL || ALL_VT) {
+#pragma unroll
+                for (int vg = 0; vg < NVT; vg += VG) {
+                    bf16x8 vf[VG][2];
+#pragma unroll
+                    for (int j = 0; j < VG; ++j) {
+                        vf[j][0] = v_frag(vb, vg + j, 0);
+                        vf[j][1] = v_frag(vb, vg + j, 1);
+                    }
+                    if constexpr (CAUSAL) {
+                        f32x4 o[VG];
+#pragma unroll
+                        for (int j = 0; j < VG; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kq = 0; kq < NKQ; ++kq)
+#pragma unroll
+                            for (int j = 0; j < VG; ++j)
+                                mma(o[j], lds_ld<bf16x8>(LST + ((vg + j) * NKQ + kq) * 1024 + lane * 16), pq[kq]);
+#pragma unroll
+                        for (int t = 0; t < 2; ++t)
+#pragma unroll
+                            for (int j = 0; j < VG; ++j) mma(o[j], vf[j][t], sfr[t]);
+#pragma unroll
+                        for (int j = 0; j < VG; ++j) store_tile(o[j], inv, obase, vg + j);
+                    }
+                    if constexpr (ALL_VT) {
+#pragma unroll
+                        for (int tk = 0; tk < 2; ++tk)
+#pragma unroll
+                            for (int j = 0; j < VG; ++j)
+#pragma unroll
+                                for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+                                    for (int hh = 0; hh < 2; ++hh) mma(st[kqi][hh][vg + j], gkc[kqi][hh][tk], vf[j][tk]);
+                    }
+                }
+            }
+            if constexpr (!ALL_VT) {
+                // the owned d_v tiles are a slice: fetch their V fragments again
+#pragma unroll
+                for (int vti = 0; vti < VTW; ++vti) {
+                    const bf16x8 vf0 = v_frag(vb, vt0 + vti, 0);
+                    const bf16x8 vf1 = v_frag(vb, vt0 + vti, 1);
+#pragma unroll
+                    for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            mma(st[kqi][hh][vti], gkc[kqi][hh][0], vf0);
+                            mma(st[kqi][hh][vti], gkc[kqi][hh][1], vf1);
+                        }
+                }
+            }
+            // Z of the owned components: column sums of the same bf16 Gamma_K (all-ones operand)
+            if (zown) {
+                const bf16x8 ones = ones_frag<bf16x8>();
+#pragma unroll
+                for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        f32x4 zi = {0.f, 0.f, 0.f, 0.f};
+                        mma(zi, gkc[kqi][hh][0], ones);
+                        mma(zi, gkc[kqi][hh][1], ones);
+                        const int zo = ((2 * (kq0 + kqi) + hh) * 16 + lg * 4) * 4;
+                        const f32x4 z = lds_ld<f32x4>(LZ + zo) + zi;
+                        if (lr == 0) lds_st<f32x4>(LZ + zo, z);
+                    }
+            }
+        }
+    };
+
+    for (int64_t ch = ch0; ch < ch1; ch += 2) {
+        body(std::integral_constant<int, 0>{}, ch);
+        if (ch + 1 < ch1) body(std::integral_constant<int, 1>{}, ch + 1);
+    }
+
+    if constexpr (MODE == MODE_AGG) {
+#pragma unroll
+        for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int ct = 2 * (kq0 + kqi) + hh;
+#pragma unroll
+                for (int vti = 0; vti < VTW; ++vti)
+                    *reinterpret_cast<f32x4*>(segrec + ((int64_t)(ct * NVT + vt0 + vti) * 64 + lane) * 4) = st[kqi][hh][vti];
+            }
+        lds_barrier();   // Z updates of the last chunk
+        for (int k = tid; k < KC; k += 256) segrec[(int64_t)KC * VC + k] = s_z[k];
+    }
+}
+
+}  // namespace gma
