@@ -144,25 +144,23 @@ tok_kernel(const MainArgs a) {
     // block at (c RPB + r) 16.  Lane l fetches row l % RPB, chunk l / RPB.
     const uint32_t lx_base = lds_addr(LX), lv_base = lds_addr(LV);
 
-    auto issue = [&](int64_t ch, int buf) {
+    // DMA of chunk ch into staging buffer buf, in parts: part sd < NSIDE = own X rows of one side,
+    // part NSIDE = this wave's quarter of V
+    auto issue_part = [&](int64_t ch, int buf, int part) {
         const uint32_t lane = (uint32_t)lane_v, rl = lane >> 3;
-        const uint32_t xl[2] = {(rl * d_r + (((lane & 7) ^ rl) * 8)) * 2, (rl * d_r + (((lane & 7) ^ rl ^ 1) * 8)) * 2};
         const uint32_t n0 = (uint32_t)(ch * C);
-        const uint32_t xrow = (n0 + 16 * w) * d_r * 2;   // byte offset of the wave's first row
-        const uint32_t m0x = lx_base + buf * XBUF + w * XWAVE;
-        // lane parts made opaque here, so that the per-block sums are formed per chunk (one add each)
-        // rather than kept in registers across the loop
-        const uint32_t x0 = xl[0] + xrow, x1 = xl[1] + xrow + 16 * d_r;
-#pragma unroll
-        for (int sd = 0; sd < NSIDE; ++sd) {
+        if (part < NSIDE) {
+            const int sd = part;
+            const uint32_t xl0 = (rl * d_r + (((lane & 7) ^ rl) * 8)) * 2, xl1 = (rl * d_r + (((lane & 7) ^ rl ^ 1) * 8)) * 2;
+            const uint32_t xrow = (n0 + 16 * w) * d_r * 2;   // byte offset of the wave's first row
+            const uint32_t m0 = lx_base + buf * XBUF + w * XWAVE + sd * XSIDE;
+            const uint32_t x0 = xl0 + xrow, x1 = xl1 + xrow + 16 * d_r;
             const i32x4& rs = (NEED_Q && sd == 0) ? rs_q : rs_k;
-            const uint32_t m0 = m0x + sd * XSIDE;
             if constexpr (NSEG == 2) dma16x4(rs, m0, m0 + 1024, m0 + 2048, m0 + 3072, x0, x0 + 128, x1, x1 + 128);
             else dma16x2(rs, m0, m0 + 1024, x0, x1);
-        }
-        if constexpr (NEED_V) {
-            const uint32_t vstep = W * RPB * d_v * 2;
+        } else if constexpr (NEED_V) {
             const uint32_t vl = ((lane % RPB) * d_v + (lane / RPB) * 8) * 2;
+            const uint32_t vstep = W * RPB * d_v * 2;
             const uint32_t v0 = vl + (n0 + w * RPB) * d_v * 2;
             const uint32_t m0 = lv_base + buf * VBUF + w * 1024;
             if constexpr (NVD == 4)
@@ -170,6 +168,11 @@ tok_kernel(const MainArgs a) {
                         v0 + 3 * vstep);
             else dma16x2(rs_v, m0, m0 + W * 1024, v0, v0 + vstep);
         }
+    };
+    constexpr int NPARTS = NSIDE + (NEED_V ? 1 : 0);
+    auto issue = [&](int64_t ch, int buf) {
+#pragma unroll
+        for (int part = 0; part < NPARTS; ++part) issue_part(ch, buf, part);
     };
 
     // ---- [a | b] operand fragments of every component (AGPRs), logit constants c (LDS)
@@ -368,9 +371,9 @@ tok_kernel(const MainArgs a) {
 
     // causal mask of the intra-chunk tiles: key 16 J + 4g + i is kept for query 16 w + r when
     // 16 J + i <= 16 w + r - 4g; as a factor 0 / 1 from a clamped difference (no per-element compare)
-    auto keep = [&](int k) -> float {
+    auto keep_base = [&]() -> float {
         [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
-        return __builtin_amdgcn_fmed3f((float)(16 * w + lr - 4 * lg + 1 - k), 0.f, 1.f);
+        return (float)(16 * w + lr - 4 * lg + 1);
     };
     const uint32_t N32 = (uint32_t)N;
 
@@ -390,7 +393,9 @@ tok_kernel(const MainArgs a) {
         if (first) wait_vmcnt<NVD>();
         else wait_vmcnt<NVD + NST>();
         if constexpr (NEED_K) lds_barrier();   // B0
-        if (has_next) issue(ch + 1, BUF ^ 1);
+        if constexpr (!CAUSAL) {
+            if (has_next) issue(ch + 1, BUF ^ 1);
+        }
 
         if constexpr (MODE == MODE_OUT_BIDIR) {
             // Gamma_Q of own tokens, then O^T = state^T Gamma_Q^T with the fixed total state
@@ -422,92 +427,117 @@ tok_kernel(const MainArgs a) {
             // ---- P1
             bf16x8 pq[CAUSAL ? NKQ : 1];
             if constexpr (CAUSAL) {
-                // Step ks of region A issues the K-side logits MFMAs of fragment step ks and, beside them,
-                // the fp16 conversion of Q_X step ks and a share of the state publication; step ks of
-                // region B issues the Q-side logits MFMAs of step ks beside a quarter of the K-side
-                // softmax.  Region C (the Q-side softmax) has no matrix work beside it.
-                f16x8 kxf[NKS2], kx2[NKS2];
-                x_frags(xw + OFF_XK, kxf, kx2);
-                u32x4 qraw[NKS2];
-#pragma unroll
-                for (int ks = 0; ks < NKS2; ++ks) qraw[ks] = lds_ld<u32x4>(xw + OFF_XQ + xoff(ks));
+                // Region A: the K-side logits MFMAs, each pair followed by one small piece of independent
+                // vector work: one 32-bit word of the fp16 conversion of the next K_X step or of a Q_X
+                // step, one fragment of the state publication, a part of the next chunk's DMA.  Region B:
+                // the Q-side logits MFMAs, each pair followed by a piece of the K-side softmax (running
+                // max, exp per tile, sum per tile, normalisation and the Gamma_K row per tile).  The
+                // pieces are fenced one by one so that the issue order stays interleaved.
+                u32x4 kraw[NKS2], qraw[NKS2];
                 f32x4 acck[NCT], accq[NCT];
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) acck[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
-                f16x8 qxf[NKS2], qx2[NKS2];
+#pragma unroll
+                for (int ks = 0; ks < NKS2; ++ks) kraw[ks] = lds_ld<u32x4>(xw + OFF_XK + xoff(ks));
+#pragma unroll
+                for (int ks = 0; ks < NKS2; ++ks) qraw[ks] = lds_ld<u32x4>(xw + OFF_XQ + xoff(ks));
+                f16x8 kxf[NKS2], kx2[NKS2], qxf[NKS2], qx2[NKS2];
+                auto cvt_word = [](const u32x4& raw, int e, f16x8& xf, f16x8& x2) {
+                    const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(raw[e] << 16), __uint_as_float(raw[e] & 0xffff0000u));
+                    xf[2 * e] = h[0];
+                    xf[2 * e + 1] = h[1];
+                    x2[2 * e] = h[0] * h[0];
+                    x2[2 * e + 1] = h[1] * h[1];
+                };
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cvt_word(kraw[0], e, kxf[0], kx2[0]);
                 fence();
                 constexpr int NPUB = KQW * VTW;   // state fragments to publish
+                // pieces of step ks, in order: K_X words of step ks+1, Q_X words of step ks, state
+                // fragments j = ks (mod NKS2), the Z fragments (last step), the DMA parts (steps 0..)
+                auto piece_a = [&](int ks, int p) {
+                    const int nk = (ks + 1 < NKS2) ? 4 : 0;
+                    if (p < nk) { cvt_word(kraw[ks + 1], p, kxf[ks + 1], kx2[ks + 1]); return; }
+                    p -= nk;
+                    if (p < 4) { cvt_word(qraw[ks], p, qxf[ks], qx2[ks]); return; }
+                    p -= 4;
+                    const int npub = (NPUB - ks + NKS2 - 1) / NKS2;   // j = ks, ks + NKS2, ...
+                    if (p < npub) {
+                        const int jj = ks + p * NKS2;
+                        const int kqi = jj / VTW, vti = jj % VTW;
+                        lds_st<bf16x8>(LST + ((vt0 + vti) * NKQ + kq0 + kqi) * 1024 + lane * 16,
+                                       pack_pair(st[kqi][0][vti], st[kqi][1][vti]));
+                        return;
+                    }
+                    p -= npub;
+                    if (ks == NKS2 - 1) {
+                        if (p == 0) { write_z(); return; }
+                        p -= 1;
+                    }
+                    // DMA parts: step ks issues the parts ks * NPARTS / NKS2 .. (ks + 1) * NPARTS / NKS2 - 1
+                    const int d0 = ks * NPARTS / NKS2, d1 = (ks + 1) * NPARTS / NKS2;
+                    if (p < d1 - d0 && has_next) issue_part(ch + 1, BUF ^ 1, d0 + p);
+                };
+                // most pieces in one step: K and Q words, state fragments, Z, DMA parts
+                constexpr int NPA = 4 + 4 + (NPUB + NKS2 - 1) / NKS2 + 1 + (NPARTS + NKS2 - 1) / NKS2;
+                constexpr int PPA = (NPA + NCT - 1) / NCT;   // pieces per MFMA pair
 #pragma unroll
                 for (int ks = 0; ks < NKS2; ++ks) {
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) {
-                        pin_agpr(abf[ct][ks]);
                         mma(acck[ct], abf[ct][ks], kx2[ks]);
-                    }
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        pin_agpr(abf[ct][ks + NKS2]);
                         mma(acck[ct], abf[ct][ks + NKS2], kxf[ks]);
-                    }
-                    qxf[ks] = bf16x8_bits_to_f16x8(qraw[ks]);
-                    qx2[ks] = qxf[ks] * qxf[ks];
 #pragma unroll
-                    for (int j = ks; j < NPUB; j += NKS2) {
-                        const int kqi = j / VTW, vti = j % VTW;
-                        lds_st<bf16x8>(LST + ((vt0 + vti) * NKQ + kq0 + kqi) * 1024 + lane * 16,
-                                       pack_pair(st[kqi][0][vti], st[kqi][1][vti]));
+                        for (int t = 0; t < PPA; ++t) piece_a(ks, ct * PPA + t);
+                        fence();
                     }
-                    if (ks == NKS2 - 1) write_z();
-                    fence();
                 }
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) accq[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
-                // K-side softmax in four parts: max; exp of the first half; exp of the second half;
-                // row sum, normalisation and the Gamma_K rows to LDS
-                float mk = 0.f, sk = 0.f;
-                auto ksoft = [&](int part) {
-                    if (part == 0) {
-                        float m = acck[0][0];
-#pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) m = fmaxf(m, acck[ct][i]);
-                        mk = group4_max(m);
-                    } else if (part == 1 || part == 2) {
-                        const int c0 = (part - 1) * (NCT / 2);
-#pragma unroll
-                        for (int ct = c0; ct < c0 + NCT / 2; ++ct)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) acck[ct][i] = fast_exp2(acck[ct][i] - mk);
-                    } else {
-#pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) sk += acck[ct][i];
-                        sk = group4_sum(sk);
-                        const float r = (tok < N32) ? fast_rcp(sk) : 0.f;
-#pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct)
-                            lds_st<bf16x4>(LGK + gk_off(16 * w + lr, ct * 16 + lg * 4), pack4(acck[ct] * r));
-                    }
-                };
                 fence();
+                // K-side softmax pieces: 0: running max over tiles 0..NCT-1 (one piece per two tiles),
+                // then the cross-lane max; exp per tile; row-sum per two tiles, cross-lane sum and
+                // reciprocal; normalisation, bf16 pack and LDS row write per tile
+                float mk = -INFINITY, sk = 0.f, rk = 0.f;
+                constexpr int NMAXP = NCT / 2, NSUMP = NCT / 2;
+                constexpr int NKSOFT = NMAXP + 1 + NCT + NSUMP + 1 + NCT;
+                auto piece_b = [&](int p) {
+                    if (p < NMAXP) {
+#pragma unroll
+                        for (int c = 2 * p; c < 2 * p + 2; ++c)
+                            mk = fmaxf(mk, fmaxf(fmaxf(acck[c][0], acck[c][1]), fmaxf(acck[c][2], acck[c][3])));
+                        return;
+                    }
+                    p -= NMAXP;
+                    if (p == 0) { mk = group4_max(mk); return; }
+                    p -= 1;
+                    if (p < NCT) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acck[p][i] = fast_exp2(acck[p][i] - mk);
+                        return;
+                    }
+                    p -= NCT;
+                    if (p < NSUMP) {
+#pragma unroll
+                        for (int c = 2 * p; c < 2 * p + 2; ++c) sk += (acck[c][0] + acck[c][1]) + (acck[c][2] + acck[c][3]);
+                        return;
+                    }
+                    p -= NSUMP;
+                    if (p == 0) { sk = group4_sum(sk); rk = (tok < N32) ? fast_rcp(sk) : 0.f; return; }
+                    p -= 1;
+                    if (p < NCT) lds_st<bf16x4>(LGK + gk_off(16 * w + lr, p * 16 + lg * 4), pack4(acck[p] * rk));
+                };
+                constexpr int PPB = (NKSOFT + NCT * NKS2 - 1) / (NCT * NKS2);   // pieces per MFMA pair
 #pragma unroll
                 for (int ks = 0; ks < NKS2; ++ks) {
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) {
-                        pin_agpr(abf[ct][ks]);
                         mma(accq[ct], abf[ct][ks], qx2[ks]);
-                    }
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        pin_agpr(abf[ct][ks + NKS2]);
                         mma(accq[ct], abf[ct][ks + NKS2], qxf[ks]);
-                    }
 #pragma unroll
-                    for (int part = ks * 4 / NKS2; part < (ks + 1) * 4 / NKS2; ++part) ksoft(part);
-                    interleave_mfma_valu<2 * NCT, 3>();
-                    fence();
+                        for (int t = 0; t < PPB; ++t) piece_b((ks * NCT + ct) * PPB + t);
+                        fence();
+                    }
                 }
                 exp_rows(accq);
 #pragma unroll
@@ -532,6 +562,7 @@ tok_kernel(const MainArgs a) {
             lds_barrier();   // B1
 
             // ---- P2
+            constexpr bool ALL_VT = (VTW == NVT);
             bf16x8 gkc[KQW][2][2];
 #pragma unroll
             for (int kqi = 0; kqi < KQW; ++kqi)
@@ -540,28 +571,70 @@ tok_kernel(const MainArgs a) {
 #pragma unroll
                     for (int tk = 0; tk < 2; ++tk) gkc[kqi][hh][tk] = gk_comp_frag(2 * (kq0 + kqi) + hh, tk);
 
+            // Software pipeline over stages: each stage first issues the LDS reads of the next stage,
+            // then the matrix work of the current one (fences keep the order), so that LDS latency
+            // is covered by MFMAs.
+            constexpr int VP = (NKQ >= 8) ? 1 : ((8 / NKQ < NVT) ? 8 / NKQ : NVT);   // d_v tiles per stage
+            static_assert(NVT % VP == 0, "d_v tile stages");
+            bf16x8 vfr[2][VP][2];
+            bf16x8 sst[2][VP][CAUSAL ? NKQ : 1];
+            auto load_vstage = [&](int buf, int vs) {
+#pragma unroll
+                for (int j = 0; j < VP; ++j) {
+                    const int vt = vs * VP + j;
+                    if constexpr (CAUSAL || ALL_VT) {
+                        vfr[buf][j][0] = v_frag(vb, vt, 0);
+                        vfr[buf][j][1] = v_frag(vb, vt, 1);
+                    }
+                    if constexpr (CAUSAL) {
+#pragma unroll
+                        for (int kq = 0; kq < NKQ; ++kq) sst[buf][j][kq] = lds_ld<bf16x8>(LST + (vt * NKQ + kq) * 1024 + lane * 16);
+                    }
+                }
+            };
+
             bf16x8 sfr[2];
             float inv = 0.f;
             if constexpr (CAUSAL) {
                 // intra-chunk affinities of own queries S^T(J, w) = Gamma_K[J] Gamma_Q[w]^T for all four
                 // key blocks (the same work on every wave), causally masked; operand fragments over
-                // the two token steps and their column sums.  Component steps outermost, so that
-                // consecutive MFMAs go to independent accumulators.
+                // the two token steps and their column sums.  Denominators: Gamma_Q . Z (hi + lo) and
+                // eps * rowsum(Gamma_Q) from the Z fragments.
+                constexpr int SKQ = (NKQ >= 2) ? 2 : 1;   // component steps per stage
+                bf16x8 gt[2][SKQ][4];
+                bf16x8 zx[2][SKQ];
+                auto load_sstage = [&](int buf, int k0) {
+#pragma unroll
+                    for (int sq = 0; sq < SKQ; ++sq) {
+#pragma unroll
+                        for (int J = 0; J < 4; ++J) gt[buf][sq][J] = gk_token_frag(J, k0 + sq);
+                        zx[buf][sq] = lds_ld<bf16x8>(LZX + (k0 + sq) * 1024 + lane * 16);
+                    }
+                };
                 f32x4 sacc[4];
                 f32x4 dx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int J = 0; J < 4; ++J) sacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+                load_sstage(0, 0);
+                fence();
 #pragma unroll
-                for (int kq = 0; kq < NKQ; ++kq) {
+                for (int k0 = 0; k0 < NKQ; k0 += SKQ) {
+                    const int cb = (k0 / SKQ) & 1;
+                    if (k0 + SKQ < NKQ) load_sstage(cb ^ 1, k0 + SKQ);
+                    else load_vstage(0, 0);
 #pragma unroll
-                    for (int J = 0; J < 4; ++J) mma(sacc[J], gk_token_frag(J, kq), pq[kq]);
-                    // denominators: Gamma_Q . Z (hi + lo) and eps * rowsum(Gamma_Q)
-                    mma(dx, lds_ld<bf16x8>(LZX + kq * 1024 + lane * 16), pq[kq]);
+                    for (int sq = 0; sq < SKQ; ++sq) {
+#pragma unroll
+                        for (int J = 0; J < 4; ++J) mma(sacc[J], gt[cb][sq][J], pq[k0 + sq]);
+                        mma(dx, zx[cb][sq], pq[k0 + sq]);
+                    }
+                    fence();
                 }
+                const float kb = keep_base();
 #pragma unroll
                 for (int J = 0; J < 4; ++J)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sacc[J][i] *= keep(16 * J + i);
+                    for (int i = 0; i < 4; ++i) sacc[J][i] *= __builtin_amdgcn_fmed3f(kb - (float)(16 * J + i), 0.f, 1.f);
                 const bf16x8 ones = ones_frag<bf16x8>();
                 f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -570,49 +643,57 @@ tok_kernel(const MainArgs a) {
                     mma(dacc, ones, sfr[t]);
                 }
                 inv = fast_rcp(dx[0] + dx[1] + a.eps * dx[2] + dacc[0]);
+            } else {
+                if constexpr (ALL_VT) load_vstage(0, 0);
             }
             const uint32_t obase = row_base(tok);
+            fence();
 
-            // groups of d_v tiles: inter (state before the chunk) and intra output of own queries, state
-            // update of the owned share; within a group consecutive MFMAs use independent accumulators
-            constexpr bool ALL_VT = (VTW == NVT);
-            constexpr int VG = (NVT >= 4) ? 4 : NVT;
-            static_assert(NVT % VG == 0, "d_v tile groups");
+            // stages of VP d_v tiles: inter (state before the chunk) and intra output of own queries,
+            // state update of the owned share; each stage's output tiles are stored during the next
             if constexpr (CAUSAL || ALL_VT) {
+                f32x4 oprev[VP];
 #pragma unroll
-                for (int vg = 0; vg < NVT; vg += VG) {
-                    bf16x8 vf[VG][2];
-#pragma unroll
-                    for (int j = 0; j < VG; ++j) {
-                        vf[j][0] = v_frag(vb, vg + j, 0);
-                        vf[j][1] = v_frag(vb, vg + j, 1);
-                    }
+                for (int vs = 0; vs < NVT / VP; ++vs) {
+                    const int cb = vs & 1;
+                    if (vs + 1 < NVT / VP) load_vstage(cb ^ 1, vs + 1);
+                    f32x4 o[VP];
                     if constexpr (CAUSAL) {
-                        f32x4 o[VG];
 #pragma unroll
-                        for (int j = 0; j < VG; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int j = 0; j < VP; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int kq = 0; kq < NKQ; ++kq)
 #pragma unroll
-                            for (int j = 0; j < VG; ++j)
-                                mma(o[j], lds_ld<bf16x8>(LST + ((vg + j) * NKQ + kq) * 1024 + lane * 16), pq[kq]);
+                            for (int j = 0; j < VP; ++j) mma(o[j], sst[cb][j][kq], pq[kq]);
 #pragma unroll
                         for (int t = 0; t < 2; ++t)
 #pragma unroll
-                            for (int j = 0; j < VG; ++j) mma(o[j], vf[j][t], sfr[t]);
-#pragma unroll
-                        for (int j = 0; j < VG; ++j) store_tile(o[j], inv, obase, vg + j);
+                            for (int j = 0; j < VP; ++j) mma(o[j], vfr[cb][j][t], sfr[t]);
                     }
                     if constexpr (ALL_VT) {
 #pragma unroll
                         for (int tk = 0; tk < 2; ++tk)
 #pragma unroll
-                            for (int j = 0; j < VG; ++j)
+                            for (int j = 0; j < VP; ++j)
 #pragma unroll
                                 for (int kqi = 0; kqi < KQW; ++kqi)
 #pragma unroll
-                                    for (int hh = 0; hh < 2; ++hh) mma(st[kqi][hh][vg + j], gkc[kqi][hh][tk], vf[j][tk]);
+                                    for (int hh = 0; hh < 2; ++hh)
+                                        mma(st[kqi][hh][vs * VP + j], gkc[kqi][hh][tk], vfr[cb][j][tk]);
                     }
+                    if constexpr (CAUSAL) {
+                        if (vs > 0) {
+#pragma unroll
+                            for (int j = 0; j < VP; ++j) store_tile(oprev[j], inv, obase, (vs - 1) * VP + j);
+                        }
+#pragma unroll
+                        for (int j = 0; j < VP; ++j) oprev[j] = o[j];
+                    }
+                    fence();
+                }
+                if constexpr (CAUSAL) {
+#pragma unroll
+                    for (int j = 0; j < VP; ++j) store_tile(oprev[j], inv, obase, (NVT / VP - 1) * VP + j);
                 }
             }
             if constexpr (!ALL_VT) {
