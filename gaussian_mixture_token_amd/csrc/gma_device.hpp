@@ -227,6 +227,18 @@ __device__ __forceinline__ void dma16x4(const i32x4& rs, uint32_t m0a, uint32_t 
         : "s"(m0a), "s"(m0b), "s"(m0c), "s"(m0d), "v"(va), "v"(vb), "v"(vc), "v"(vd), "s"(rs)
         : "memory");
 }
+__device__ __forceinline__ void dma16x1(const i32x4& rs, uint32_t m0a, uint32_t va) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0a), "v"(va), "s"(rs)
+        : "memory");
+}
 __device__ __forceinline__ void dma16x2(const i32x4& rs, uint32_t m0a, uint32_t m0b, uint32_t va, uint32_t vb) {
     uint32_t saved;
     asm volatile(

@@ -57,7 +57,8 @@ struct Plan {
     int P = 1;
     int seg_chunks = 1;
     bool dma = false;
-    size_t off_ab = 0, off_c = 0, off_seg = 0, total = 0;
+    bool gtiles = false;   // causal token-split pair through stored Gamma_K tiles
+    size_t off_ab = 0, off_c = 0, off_seg = 0, off_gk = 0, total = 0;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -135,19 +136,28 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     if (BH * plan->P > INT32_MAX)
         return fail(GMA_ERROR_NOT_SUPPORTED, "grid too large");
 
-    // workspace: [a | b] fragments, c, segment records
+    // Causal token-split path through stored Gamma_K tiles: taken where a tile row (K bf16) is no
+    // wider than an X row (d_r bf16), so the output pass reads no more bytes than it would for K_X,
+    // and the tiles of one (batch, head) stay within 32-bit byte offsets.
+    const int64_t tile_bytes = (int64_t)C * plan->cls->kc * 2;
+    plan->gtiles = tok && op == GMA_OP_FORWARD_CAUSAL && plan->cls->tok_out_causal_g && plan->cls->kc <= plan->cls->drc &&
+                   plan->n_chunks * tile_bytes < (int64_t(1) << 31);
+
+    // workspace: [a | b] fragments, c, segment records, Gamma_K tiles
     const int ks = plan->f32 ? 16 : 32;
     const int nks = 2 * plan->cls->drc / ks;
     const size_t ab_bytes = (size_t)plan->H * (plan->cls->kc / 16) * nks * 64 * 16;
     const size_t c_bytes = (size_t)plan->H * plan->cls->kc * sizeof(float);
     size_t seg_bytes = 0;
-    const bool need_seg = (op == GMA_OP_FORWARD_BIDIR) || (op == GMA_OP_FORWARD_CAUSAL && plan->P > 1);
+    const bool need_seg = (op == GMA_OP_FORWARD_BIDIR) || (op == GMA_OP_FORWARD_CAUSAL && (plan->P > 1 || plan->gtiles));
     if (need_seg)
         seg_bytes = (size_t)BH * plan->P * ((size_t)plan->cls->kc * plan->cls->vc + plan->cls->kc) * sizeof(float);
+    const size_t gk_bytes = plan->gtiles ? (size_t)BH * plan->n_chunks * tile_bytes : 0;
     plan->off_ab = 0;
     plan->off_c = align_up(ab_bytes, 256);
     plan->off_seg = align_up(plan->off_c + c_bytes, 256);
-    plan->total = align_up(plan->off_seg + seg_bytes, 256);
+    plan->off_gk = align_up(plan->off_seg + seg_bytes, 256);
+    plan->total = align_up(plan->off_gk + gk_bytes, 256);
     return GMA_SUCCESS;
 }
 
@@ -244,6 +254,7 @@ MainArgs base_args(const Plan& pl, char* ws) {
     a.ab = ws + pl.off_ab;
     a.cvec = reinterpret_cast<const float*>(ws + pl.off_c);
     a.seg = reinterpret_cast<float*>(ws + pl.off_seg);
+    a.gk = pl.gtiles ? ws + pl.off_gk : nullptr;
     a.N = pl.N;
     a.H = (int)pl.H;
     a.P = pl.P;
@@ -312,6 +323,9 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
         if (ws_bytes < pl.total)
             return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
                         ws_bytes, pl.total);
+        if (overlaps(ws, pl.total, qx, nx) || overlaps(ws, pl.total, kx, nx) || overlaps(ws, pl.total, v, nv) ||
+            overlaps(ws, pl.total, o, nv))
+            return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
     }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -326,16 +340,18 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
     a.vec_x = vec_ok(qx, pl.d_r, pl.f32) && vec_ok(kx, pl.d_r, pl.f32);
     a.vec_v = vec_ok(v, pl.d_v, pl.f32);
     a.vec_o = vec_o_ok(o, pl.d_v, pl.f32);
-    const main_launch_t f_agg = dma ? pl.cls->tok_agg : pl.cls->agg;
-    const main_launch_t f_causal = dma ? pl.cls->tok_out_causal : pl.cls->out_causal;
+    const bool gt = dma && pl.gtiles;
+    const main_launch_t f_agg = gt ? pl.cls->tok_agg_g : dma ? pl.cls->tok_agg : pl.cls->agg;
+    const main_launch_t f_causal = gt ? pl.cls->tok_out_causal_g : dma ? pl.cls->tok_out_causal : pl.cls->out_causal;
     const main_launch_t f_bidir = dma ? pl.cls->tok_out_bidir : pl.cls->out_bidir;
     const int grid = (int)(pl.B * pl.H * pl.P);
     const int64_t rec = (int64_t)pl.cls->kc * pl.cls->vc + pl.cls->kc;
-    const bool need_agg = !causal || pl.P > 1;
+    const bool need_agg = !causal || pl.P > 1 || gt;
     if (need_agg) {
-        // causal: the last segment's aggregate is not needed by anyone
+        // causal: the last segment's aggregate is not needed by anyone, but with stored tiles its
+        // Gamma_K tiles are
         MainArgs ag = a;
-        ag.Pg = causal ? pl.P - 1 : pl.P;
+        ag.Pg = (causal && !gt) ? pl.P - 1 : pl.P;
         const int agrid = (int)(pl.B * pl.H * ag.Pg);
         st = timed_launch(K_AGG, s, [&] { f_agg(ag, agrid, s); });
         if (st != GMA_SUCCESS) return st;

@@ -47,7 +47,10 @@
 
 namespace gma {
 
-enum { MODE_RESP = 0, MODE_AGG = 1, MODE_OUT_BIDIR = 2, MODE_OUT_CAUSAL = 3 };
+enum { MODE_RESP = 0, MODE_AGG = 1, MODE_OUT_BIDIR = 2, MODE_OUT_CAUSAL = 3,
+       // token-split kernels only: the aggregate pass also stores every chunk's Gamma_K tile, and the
+       // causal output pass reads those tiles instead of recomputing the K-side responsibilities
+       MODE_AGG_G = 4, MODE_OUT_CAUSAL_G = 5 };
 
 template <bool F32> struct Tr;
 template <> struct Tr<true> {
@@ -78,6 +81,7 @@ struct MainArgs {
     const void* ab;        // [H, KC/16, NKS, 64] x 16 bytes
     const float* cvec;     // [H, KC]
     float* seg;            // [BH, P, KC*VC + KC]
+    void* gk;              // [BH, n_chunks, 64 * KC] bf16 Gamma_K chunk tiles (MODE_AGG_G / MODE_OUT_CAUSAL_G)
     int64_t N;
     int H;
     int P;                 // segments per head (record stride)

@@ -22,6 +22,9 @@ struct ShapeClass {
     // class has none
     int tok_wg_per_cu;
     main_launch_t tok_agg, tok_out_bidir, tok_out_causal;
+    // causal pair through stored Gamma_K tiles: aggregate pass that also writes the tiles, output
+    // pass that reads them
+    main_launch_t tok_agg_g, tok_out_causal_g;
 };
 
 constexpr int kTokChunk = 64;
@@ -54,7 +57,7 @@ void launch_tok(const MainArgs& a, int grid, hipStream_t s) {
 #define GMA_SHAPE_CLASS_F32(KC, VC, DRC, W, C)                                                \
     ShapeClass {                                                                              \
         1, KC, VC, DRC, W, C, 1, &launch_prep<true, KC, DRC>, GMA_MAIN_SET(true, KC, VC, DRC, W, C, false, 1), \
-            nullptr, 0, nullptr, nullptr, nullptr                                             \
+            nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr                           \
     }
 
 // WPE: wavefronts per SIMD of the LDS-DMA responsibilities kernel; TWPE: of the token-split kernels
@@ -64,7 +67,8 @@ void launch_tok(const MainArgs& a, int grid, hipStream_t s) {
             GMA_MAIN_SET(false, KC, VC, DRC, W, C, false, 1),                                 \
             &launch_main<false, KC, 16 * W, DRC, W, C, MODE_RESP, true, WPE>, TWPE,           \
             &launch_tok<KC, VC, DRC, MODE_AGG, TWPE>, &launch_tok<KC, VC, DRC, MODE_OUT_BIDIR, TWPE>, \
-            &launch_tok<KC, VC, DRC, MODE_OUT_CAUSAL, TWPE>                                   \
+            &launch_tok<KC, VC, DRC, MODE_OUT_CAUSAL, TWPE>,                                  \
+            &launch_tok<KC, VC, DRC, MODE_AGG_G, TWPE>, &launch_tok<KC, VC, DRC, MODE_OUT_CAUSAL_G, TWPE> \
     }
 
 // the same without token-split kernels
@@ -72,7 +76,8 @@ void launch_tok(const MainArgs& a, int grid, hipStream_t s) {
     ShapeClass {                                                                              \
         0, KC, VC, DRC, W, C, WPE, &launch_prep<false, KC, DRC>,                              \
             GMA_MAIN_SET(false, KC, VC, DRC, W, C, false, 1),                                 \
-            &launch_main<false, KC, 16 * W, DRC, W, C, MODE_RESP, true, WPE>, 0, nullptr, nullptr, nullptr \
+            &launch_main<false, KC, 16 * W, DRC, W, C, MODE_RESP, true, WPE>, 0, nullptr, nullptr, nullptr, \
+            nullptr, nullptr                                                                  \
     }
 
 }  // namespace gma

@@ -43,10 +43,13 @@ tok_kernel(const MainArgs a) {
     constexpr int NVT = VC / 16;   // d_v tiles
     constexpr int NKS2 = DRC / 32; // fragment steps over d_r (x^2 part; the x part follows)
     constexpr int NSEG = DRC / 64; // 128-byte segments per staged X row
-    constexpr bool NEED_Q = (MODE == MODE_OUT_BIDIR) || (MODE == MODE_OUT_CAUSAL);
-    constexpr bool NEED_K = (MODE == MODE_AGG) || (MODE == MODE_OUT_CAUSAL);
-    constexpr bool NEED_V = NEED_K;
-    constexpr bool CAUSAL = MODE == MODE_OUT_CAUSAL;
+    constexpr bool GSTORE = MODE == MODE_AGG_G;         // aggregate pass storing the Gamma_K tiles
+    constexpr bool GLOAD = MODE == MODE_OUT_CAUSAL_G;   // causal output pass reading them
+    constexpr bool AGG = (MODE == MODE_AGG) || GSTORE;
+    constexpr bool CAUSAL = (MODE == MODE_OUT_CAUSAL) || GLOAD;
+    constexpr bool NEED_Q = (MODE == MODE_OUT_BIDIR) || CAUSAL;
+    constexpr bool NEED_K = AGG || (MODE == MODE_OUT_CAUSAL);   // K_X staged, Gamma_K computed
+    constexpr bool NEED_V = AGG || CAUSAL;
     constexpr bool OUT = NEED_Q;
     static_assert(MODE != MODE_RESP, "responsibilities use main_kernel");
     static_assert(DRC >= 64 && DRC % 64 == 0 && NSEG <= 2, "X rows are staged in one or two 128-byte segments");
@@ -68,19 +71,26 @@ tok_kernel(const MainArgs a) {
     constexpr int NXD = NSIDE * NXB;               // X DMA blocks per wave and chunk
     constexpr int NVB = NEED_V ? VBUF / 1024 : 0;  // V DMA blocks per chunk
     constexpr int NVD = NVB / W;                   // ... per wave
-    constexpr int NST = OUT ? NVT : 0;             // O stores per wave and chunk
+    // Gamma_K tile of a chunk: C rows x KC components bf16, stored and staged as one image
+    constexpr int GKR = KC * 2;                    // bytes per Gamma_K row
+    constexpr int GKBUF = C * GKR;                 // bytes per tile
+    constexpr int GKWAVE = GKBUF / W;              // one wave's share (its own 16 rows)
+    constexpr int NGD = GLOAD ? GKWAVE / 1024 : 0; // Gamma_K DMA blocks per wave and chunk
+    constexpr int NGS = GSTORE ? GKWAVE / 1024 : 0;   // Gamma_K tile stores per wave and chunk
+    // vector-memory stores per wave and chunk, issued after the DMA of the next chunk
+    constexpr int NST = OUT ? NVT : NGS;
     static_assert(NVB % W == 0 && (NVD == 0 || NVD == 2 || NVD == 4), "V blocks must split across waves");
-    static_assert(NXD + NVD + NST < 64, "vmcnt range");
+    static_assert(GKWAVE % 1024 == 0, "Gamma_K tile blocks");
+    static_assert(NXD + NVD + NGD + NST < 64, "vmcnt range");
     constexpr int CPR = VC / 8;                    // 16-byte chunks per V row
     constexpr int RPB = 1024 / (VC * 2);           // V rows per DMA block
     static_assert((RPB == 4 || RPB == 8) && RPB * CPR == 64, "V DMA blocks");
-    constexpr int GKR = KC * 2 + 32;               // bytes per Gamma_K row (padded)
     constexpr int OFF_XQ = 0;
     constexpr int OFF_XK = NEED_Q ? XSIDE : 0;
 
     __shared__ __attribute__((aligned(16))) char s_x[2 * XBUF];
     __shared__ __attribute__((aligned(16))) char s_v[NEED_V ? 2 * VBUF : 16];
-    __shared__ __attribute__((aligned(16))) char s_gk[NEED_K ? C * GKR : 16];
+    __shared__ __attribute__((aligned(16))) char s_gk[GLOAD ? 2 * GKBUF : (NEED_K ? GKBUF : 16)];
     __shared__ __attribute__((aligned(16))) char s_st[OUT ? NVT * NKQ * 1024 : 16];   // state^T fragments
     __shared__ __attribute__((aligned(16))) char s_zx[OUT ? NKQ * 1024 : 16];         // [Z_hi; Z_lo; 1; 0] fragments
     __shared__ __attribute__((aligned(16))) float s_c[KC];
@@ -122,6 +132,12 @@ tok_kernel(const MainArgs a) {
     if constexpr (NEED_K) rs_k = uniform_rsrc(make_rsrc_words(kx, (uint32_t)(N * a.d_r * 2)));
     if constexpr (NEED_V) rs_v = uniform_rsrc(make_rsrc_words(vv, (uint32_t)(N * a.d_v * 2)));
     if constexpr (OUT) rs_o = make_rsrc(oo, (uint32_t)(N * a.d_v * 2));
+    // Gamma_K tiles of this (batch, head): n_chunks images of GKBUF bytes
+    char* gkt = reinterpret_cast<char*>(a.gk) + (int64_t)bh * n_chunks * GKBUF;
+    i32x4 rs_g;
+    __amdgpu_buffer_rsrc_t rs_gs;
+    if constexpr (GLOAD) rs_g = uniform_rsrc(make_rsrc_words(gkt, (uint32_t)(n_chunks * GKBUF)));
+    if constexpr (GSTORE) rs_gs = make_rsrc(gkt, (uint32_t)(n_chunks * GKBUF));
 
     // Lane id as seen inside the chunk loop: reassigned (opaque to the optimiser) at the start of every
     // chunk, so that lane-dependent offsets are recomputed there rather than held in registers
@@ -142,10 +158,11 @@ tok_kernel(const MainArgs a) {
     // segment sg; the vector part of its byte offset below, the rest is per block and chunk
     // V: block fv holds rows RPB fv .. RPB fv + RPB - 1 chunk-major: 16-byte chunk c of row r of the
     // block at (c RPB + r) 16.  Lane l fetches row l % RPB, chunk l / RPB.
-    const uint32_t lx_base = lds_addr(LX), lv_base = lds_addr(LV);
+    const uint32_t lx_base = lds_addr(LX), lv_base = lds_addr(LV), lg_base = lds_addr(LGK);
 
     // DMA of chunk ch into staging buffer buf, in parts: part sd < NSIDE = own X rows of one side,
-    // part NSIDE = this wave's quarter of V
+    // part NSIDE = this wave's quarter of V, part NSIDE + 1 = this wave's quarter of the Gamma_K tile
+    // (a verbatim copy of the stored image)
     auto issue_part = [&](int64_t ch, int buf, int part) {
         const uint32_t lane = (uint32_t)lane_v, rl = lane >> 3;
         const uint32_t n0 = (uint32_t)(ch * C);
@@ -158,18 +175,34 @@ tok_kernel(const MainArgs a) {
             const i32x4& rs = (NEED_Q && sd == 0) ? rs_q : rs_k;
             if constexpr (NSEG == 2) dma16x4(rs, m0, m0 + 1024, m0 + 2048, m0 + 3072, x0, x0 + 128, x1, x1 + 128);
             else dma16x2(rs, m0, m0 + 1024, x0, x1);
-        } else if constexpr (NEED_V) {
-            const uint32_t vl = ((lane % RPB) * d_v + (lane / RPB) * 8) * 2;
-            const uint32_t vstep = W * RPB * d_v * 2;
-            const uint32_t v0 = vl + (n0 + w * RPB) * d_v * 2;
-            const uint32_t m0 = lv_base + buf * VBUF + w * 1024;
-            if constexpr (NVD == 4)
-                dma16x4(rs_v, m0, m0 + W * 1024, m0 + 2 * W * 1024, m0 + 3 * W * 1024, v0, v0 + vstep, v0 + 2 * vstep,
-                        v0 + 3 * vstep);
-            else dma16x2(rs_v, m0, m0 + W * 1024, v0, v0 + vstep);
+        } else if (part == NSIDE) {
+            if constexpr (NEED_V) {
+                const uint32_t vl = ((lane % RPB) * d_v + (lane / RPB) * 8) * 2;
+                const uint32_t vstep = W * RPB * d_v * 2;
+                const uint32_t v0 = vl + (n0 + w * RPB) * d_v * 2;
+                const uint32_t m0 = lv_base + buf * VBUF + w * 1024;
+                if constexpr (NVD == 4)
+                    dma16x4(rs_v, m0, m0 + W * 1024, m0 + 2 * W * 1024, m0 + 3 * W * 1024, v0, v0 + vstep,
+                            v0 + 2 * vstep, v0 + 3 * vstep);
+                else dma16x2(rs_v, m0, m0 + W * 1024, v0, v0 + vstep);
+            }
+        } else {
+            if constexpr (GLOAD) {
+                const uint32_t g0 = (uint32_t)(ch * GKBUF) + w * GKWAVE + lane * 16;
+                const uint32_t m0 = lg_base + buf * GKBUF + w * GKWAVE;
+#pragma unroll
+                for (int j = 0; j < NGD; j += 4) {
+                    if constexpr (NGD % 4 == 0)
+                        dma16x4(rs_g, m0 + j * 1024, m0 + (j + 1) * 1024, m0 + (j + 2) * 1024, m0 + (j + 3) * 1024,
+                                g0 + j * 1024, g0 + (j + 1) * 1024, g0 + (j + 2) * 1024, g0 + (j + 3) * 1024);
+                    else if constexpr (NGD == 2) dma16x2(rs_g, m0, m0 + 1024, g0, g0 + 1024);
+                    else dma16x1(rs_g, m0, g0);
+                }
+            }
         }
     };
-    constexpr int NPARTS = NSIDE + (NEED_V ? 1 : 0);
+    constexpr int NPARTS = NSIDE + (NEED_V ? 1 : 0) + (GLOAD ? 1 : 0);
+    static_assert(!GLOAD || NGD % 4 == 0 || NGD <= 2, "Gamma_K DMA parts");
     auto issue = [&](int64_t ch, int buf) {
 #pragma unroll
         for (int part = 0; part < NPARTS; ++part) issue_part(ch, buf, part);
@@ -191,7 +224,7 @@ tok_kernel(const MainArgs a) {
 
     // ---- state share: st[kqi][hh][vti] = rows (components) of tile 2(kq0+kqi)+hh, columns of d_v
     // tile vt0+vti, in accumulator layout; Z in LDS (s_z), updated by the wave owning the components
-    constexpr bool HAS_STATE = NEED_K || OUT;
+    constexpr bool HAS_STATE = AGG || OUT;
     f32x4 st[HAS_STATE ? KQW : 1][2][HAS_STATE ? VTW : 1];
     const int64_t rec = (int64_t)KC * VC + KC;
     float* segrec = a.seg + ((int64_t)bh * a.P + sidx) * rec;
@@ -259,27 +292,34 @@ tok_kernel(const MainArgs a) {
     if (ch0 < ch1) issue(ch0, 0);
     lds_barrier();   // s_c (and the bidirectional state) visible
 
-    // ---- Gamma_K rows: row-major [token][component] bf16, rows padded by 32 bytes (transposed
-    // reads of 16 rows fall in distinct banks; addresses stay affine in the component)
-    auto gk_off = [](int row, int col) -> int { return row * GKR + col * 2; };
+    // ---- Gamma_K tile: row-major [token][component] bf16 without padding; the 8-byte slots (four
+    // components) of row r are XOR-swizzled within each 128-byte span by
+    //   KC >= 64: 4 (r & 3) + ((r >> 2) & 3)       KC = 32: 4 ((r >> 1) & 1) + ((r >> 2) & 3)
+    // so that a 16-lane group reading one slot of 16 consecutive rows, or four slots of four
+    // consecutive rows (transposed reads), touches every bank once.  The stored tiles use the same
+    // image, so the causal output pass copies them into LDS unchanged.
+    auto gk_off = [](int row, int slot) -> int {
+        const int sw = (KC >= 64) ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+        return row * GKR + ((slot ^ sw) << 3);
+    };
     // A of S^T = Gamma_K Gamma_Q^T: lane = token 16 J + r, slots = components of pair kq
-    auto gk_token_frag = [&](int J, int kq) -> bf16x8 {
+    auto gk_token_frag = [&](const lds_char* gkb, int J, int kq) -> bf16x8 {
         [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
         const int row = J * 16 + lr;
-        const u32x2 lo = lds_ld<u32x2>(LGK + gk_off(row, (2 * kq) * 16 + lg * 4));
-        const u32x2 hi = lds_ld<u32x2>(LGK + gk_off(row, (2 * kq + 1) * 16 + lg * 4));
+        const u32x2 lo = lds_ld<u32x2>(gkb + gk_off(row, 8 * kq + lg));
+        const u32x2 hi = lds_ld<u32x2>(gkb + gk_off(row, 8 * kq + 4 + lg));
         return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
     // A of the state update Gamma_K^T V: lane = component 16 ct + r, slots = tokens of step tk
     // (tokens 32 tk + 4g + i and 32 tk + 16 + 4g + i, the order of the V fragments)
-    auto gk_comp_frag = [&](int ct, int tk) -> bf16x8 {
+    auto gk_comp_frag = [&](const lds_char* gkb, int ct, int tk) -> bf16x8 {
         [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
         const int q = lane & 3, i4 = (lane >> 2) & 3;
         u32x2 part[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int row = (2 * tk + hf) * 16 + lg * 4 + i4;
-            part[hf] = ds_read_tr16_at(LGK + gk_off(row, ct * 16 + 4 * q));
+            part[hf] = ds_read_tr16_at(gkb + gk_off(row, 4 * ct + q));
         }
         return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
     };
@@ -352,7 +392,7 @@ tok_kernel(const MainArgs a) {
         s = group4_sum(s);
         const float r = valid ? fast_rcp(s) : 0.f;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) lds_st<bf16x4>(LGK + gk_off(16 * w + lr, ct * 16 + lg * 4), pack4(acc[ct] * r));
+        for (int ct = 0; ct < NCT; ++ct) lds_st<bf16x4>(LGK + gk_off(16 * w + lr, 4 * ct + lg), pack4(acc[ct] * r));
     };
     // own output rows: lane (r, g) holds d_v 16 vt + 4g .. +3 of token 16 w + r.  Without d_v padding
     // the column offsets are instruction immediates; with padding, pad columns get an offset past
@@ -388,11 +428,11 @@ tok_kernel(const MainArgs a) {
         const lds_char* vb = LV + (NEED_V ? BUF * VBUF : 0);
         const uint32_t tok = n0 + 16 * w + lr;
 
-        // own X rows of this chunk landed (V of the chunk and the previous chunk's stores may
-        // still be in flight)
-        if (first) wait_vmcnt<NVD>();
-        else wait_vmcnt<NVD + NST>();
-        if constexpr (NEED_K) lds_barrier();   // B0
+        // own X rows of this chunk landed (V and the Gamma_K tile of the chunk and the previous
+        // chunk's stores may still be in flight)
+        if (first) wait_vmcnt<NVD + NGD>();
+        else wait_vmcnt<NVD + NGD + NST>();
+        if constexpr (NEED_V) lds_barrier();   // B0
         if constexpr (!CAUSAL) {
             if (has_next) issue(ch + 1, BUF ^ 1);
         }
@@ -426,7 +466,67 @@ tok_kernel(const MainArgs a) {
         } else {
             // ---- P1
             bf16x8 pq[CAUSAL ? NKQ : 1];
-            if constexpr (CAUSAL) {
+            // one 32-bit word (two bf16) of staged X to fp16 x and x^2 (exact in the supported range)
+            auto cvt_word = [](const u32x4& raw, int e, f16x8& xf, f16x8& x2) {
+                const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(raw[e] << 16), __uint_as_float(raw[e] & 0xffff0000u));
+                xf[2 * e] = h[0];
+                xf[2 * e + 1] = h[1];
+                x2[2 * e] = h[0] * h[0];
+                x2[2 * e + 1] = h[1] * h[1];
+            };
+            constexpr int NPUB = KQW * VTW;   // state fragments to publish
+            if constexpr (GLOAD) {
+                // Gamma_K of the chunk arrives as a stored tile.  The Q-side logits MFMAs, each pair
+                // followed by one small piece of independent vector work: one 32-bit word of the
+                // fp16 conversion of the next Q_X step, one fragment of the state publication, the
+                // Z fragments, a part of the next chunk's DMA.
+                u32x4 qraw[NKS2];
+                f32x4 accq[NCT];
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) accq[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
+#pragma unroll
+                for (int ks = 0; ks < NKS2; ++ks) qraw[ks] = lds_ld<u32x4>(xw + OFF_XQ + xoff(ks));
+                f16x8 qxf[NKS2], qx2[NKS2];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cvt_word(qraw[0], e, qxf[0], qx2[0]);
+                fence();
+                auto piece_q = [&](int ks, int p) {
+                    const int nq = (ks + 1 < NKS2) ? 4 : 0;
+                    if (p < nq) { cvt_word(qraw[ks + 1], p, qxf[ks + 1], qx2[ks + 1]); return; }
+                    p -= nq;
+                    const int npub = (NPUB - ks + NKS2 - 1) / NKS2;   // j = ks, ks + NKS2, ...
+                    if (p < npub) {
+                        const int jj = ks + p * NKS2;
+                        const int kqi = jj / VTW, vti = jj % VTW;
+                        lds_st<bf16x8>(LST + ((vt0 + vti) * NKQ + kq0 + kqi) * 1024 + lane * 16,
+                                       pack_pair(st[kqi][0][vti], st[kqi][1][vti]));
+                        return;
+                    }
+                    p -= npub;
+                    if (ks == NKS2 - 1) {
+                        if (p == 0) { write_z(); return; }
+                        p -= 1;
+                    }
+                    const int d0 = ks * NPARTS / NKS2, d1 = (ks + 1) * NPARTS / NKS2;
+                    if (p < d1 - d0 && has_next) issue_part(ch + 1, BUF ^ 1, d0 + p);
+                };
+                constexpr int NPQ = 4 + (NPUB + NKS2 - 1) / NKS2 + 1 + (NPARTS + NKS2 - 1) / NKS2;
+                constexpr int PPQ = (NPQ + NCT - 1) / NCT;   // pieces per MFMA pair
+#pragma unroll
+                for (int ks = 0; ks < NKS2; ++ks) {
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        mma(accq[ct], abf[ct][ks], qx2[ks]);
+                        mma(accq[ct], abf[ct][ks + NKS2], qxf[ks]);
+#pragma unroll
+                        for (int t = 0; t < PPQ; ++t) piece_q(ks, ct * PPQ + t);
+                        fence();
+                    }
+                }
+                exp_rows(accq);
+#pragma unroll
+                for (int kq = 0; kq < NKQ; ++kq) pq[kq] = pack_pair(accq[2 * kq], accq[2 * kq + 1]);
+            } else if constexpr (CAUSAL) {
                 // Region A: the K-side logits MFMAs, each pair followed by one small piece of independent
                 // vector work: one 32-bit word of the fp16 conversion of the next K_X step or of a Q_X
                 // step, one fragment of the state publication, a part of the next chunk's DMA.  Region B:
@@ -442,17 +542,9 @@ tok_kernel(const MainArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < NKS2; ++ks) qraw[ks] = lds_ld<u32x4>(xw + OFF_XQ + xoff(ks));
                 f16x8 kxf[NKS2], kx2[NKS2], qxf[NKS2], qx2[NKS2];
-                auto cvt_word = [](const u32x4& raw, int e, f16x8& xf, f16x8& x2) {
-                    const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(raw[e] << 16), __uint_as_float(raw[e] & 0xffff0000u));
-                    xf[2 * e] = h[0];
-                    xf[2 * e + 1] = h[1];
-                    x2[2 * e] = h[0] * h[0];
-                    x2[2 * e + 1] = h[1] * h[1];
-                };
 #pragma unroll
                 for (int e = 0; e < 4; ++e) cvt_word(kraw[0], e, kxf[0], kx2[0]);
                 fence();
-                constexpr int NPUB = KQW * VTW;   // state fragments to publish
                 // pieces of step ks, in order: K_X words of step ks+1, Q_X words of step ks, state
                 // fragments j = ks (mod NKS2), the Z fragments (last step), the DMA parts (steps 0..)
                 auto piece_a = [&](int ks, int p) {
@@ -525,7 +617,7 @@ tok_kernel(const MainArgs a) {
                     p -= NSUMP;
                     if (p == 0) { sk = group4_sum(sk); rk = (tok < N32) ? fast_rcp(sk) : 0.f; return; }
                     p -= 1;
-                    if (p < NCT) lds_st<bf16x4>(LGK + gk_off(16 * w + lr, p * 16 + lg * 4), pack4(acck[p] * rk));
+                    if (p < NCT) lds_st<bf16x4>(LGK + gk_off(16 * w + lr, 4 * p + lg), pack4(acck[p] * rk));
                 };
                 constexpr int PPB = (NKSOFT + NCT * NKS2 - 1) / (NCT * NKS2);   // pieces per MFMA pair
 #pragma unroll
@@ -551,15 +643,24 @@ tok_kernel(const MainArgs a) {
                 write_gk(acck, tok < N32);
             }
 
-            // own V blocks of this chunk landed, then B1
+            // own V blocks (and Gamma_K blocks) of this chunk landed, then B1
             if (first) {
-                if (has_next) wait_vmcnt<NXD + NVD>();
+                if (has_next) wait_vmcnt<NXD + NVD + NGD>();
                 else wait_vmcnt<0>();
             } else {
-                if (has_next) wait_vmcnt<NST + NXD + NVD>();
+                if (has_next) wait_vmcnt<NST + NXD + NVD + NGD>();
                 else wait_vmcnt<NST>();
             }
             lds_barrier();   // B1
+            const lds_char* gkb = LGK + (GLOAD ? BUF * GKBUF : 0);
+            if constexpr (GSTORE) {
+                // this wave's quarter of the chunk's Gamma_K tile to HBM, verbatim
+#pragma unroll
+                for (int j = 0; j < NGS; ++j) {
+                    const int off = w * GKWAVE + j * 1024 + lane * 16;
+                    __builtin_amdgcn_raw_buffer_store_b128(lds_ld<u32x4>(LGK + off), rs_gs, (uint32_t)(ch * GKBUF) + off, 0, 0);
+                }
+            }
 
             // ---- P2
             constexpr bool ALL_VT = (VTW == NVT);
@@ -569,7 +670,7 @@ tok_kernel(const MainArgs a) {
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                    for (int tk = 0; tk < 2; ++tk) gkc[kqi][hh][tk] = gk_comp_frag(2 * (kq0 + kqi) + hh, tk);
+                    for (int tk = 0; tk < 2; ++tk) gkc[kqi][hh][tk] = gk_comp_frag(gkb, 2 * (kq0 + kqi) + hh, tk);
 
             // Software pipeline over stages: each stage first issues the LDS reads of the next stage,
             // then the matrix work of the current one (fences keep the order), so that LDS latency
@@ -607,7 +708,7 @@ tok_kernel(const MainArgs a) {
 #pragma unroll
                     for (int sq = 0; sq < SKQ; ++sq) {
 #pragma unroll
-                        for (int J = 0; J < 4; ++J) gt[buf][sq][J] = gk_token_frag(J, k0 + sq);
+                        for (int J = 0; J < 4; ++J) gt[buf][sq][J] = gk_token_frag(gkb, J, k0 + sq);
                         zx[buf][sq] = lds_ld<bf16x8>(LZX + (k0 + sq) * 1024 + lane * 16);
                     }
                 };
@@ -734,7 +835,7 @@ tok_kernel(const MainArgs a) {
         if (ch + 1 < ch1) body(std::integral_constant<int, 1>{}, ch + 1);
     }
 
-    if constexpr (MODE == MODE_AGG) {
+    if constexpr (AGG) {
 #pragma unroll
         for (int kqi = 0; kqi < KQW; ++kqi)
 #pragma unroll

@@ -118,20 +118,41 @@ def test_status_strings(lib):
     assert lib.gma_kernel_name(0) and lib.gma_kernel_name(999) == b""
 
 
+def _ws(lib, op, **kw):
+    return lib.gma_workspace_size(ctypes.byref(_prob(**kw)), op)
+
+
 def test_workspace_is_linear_memory_not_quadratic(lib):
     # The N x N affinity is never formed (page "Attention par Mélange Gaussien (GMA)",
-    # "Mécanisme Central" item 2): workspace depends on the segment count and K x d_v only.
-    sizes = [lib.gma_workspace_size(ctypes.byref(_prob(seq_len=n)), 2) for n in (1 << 14, 1 << 17, 1 << 20)]
-    assert sizes[0] > 0
-    assert sizes[2] == sizes[1] == sizes[0]  # segment count saturates; no N-dependence at all beyond it
+    # "Mécanisme Central" item 2).  Bidirectional: the workspace depends on the segment count and
+    # K x d_v only.  Causal with K <= d_r: in addition, one bf16 Gamma_K row per token and head
+    # (the stored responsibility tiles), i.e. linear in N.
+    ns = (1 << 14, 1 << 17, 1 << 20)
+    bidir = [_ws(lib, 1, seq_len=n) for n in ns]
+    assert bidir[0] > 0
+    assert bidir[2] == bidir[1] == bidir[0]  # segment count saturates; no N-dependence at all beyond it
     per_head_state = (128 * 128 + 128) * 4
-    assert sizes[2] < 64 * 16 * per_head_state + (1 << 22)
-    # the bidirectional read never needs more than one [Vt | Z] per segment either
-    assert lib.gma_workspace_size(ctypes.byref(_prob(seq_len=1 << 20)), 1) == sizes[2]
+    assert bidir[2] < 64 * 16 * per_head_state + (1 << 22)
+    causal = [_ws(lib, 2, seq_len=n) for n in ns]
+    row = 128 * 2   # one bf16 Gamma_K row
+    for n, c in zip(ns, causal):
+        assert 16 * n * row <= c <= bidir[0] + 16 * n * row + 4096
+    assert causal[2] - causal[1] == 16 * (ns[2] - ns[1]) * row
 
 
 def test_small_causal_problem_needs_no_segment_records(lib):
-    # one segment per head: no carried state, workspace holds only the prepared parameters
-    small = lib.gma_workspace_size(ctypes.byref(_prob(seq_len=64, heads=1024)), 2)
-    big = lib.gma_workspace_size(ctypes.byref(_prob(seq_len=64, heads=1024)), 1)
+    # one segment per head: no carried state.  With K wider than d_r the Gamma_K tiles are not
+    # stored, and the workspace holds only the prepared parameters.
+    kw = dict(seq_len=64, heads=1024, d_route=64, n_comp=256, d_value=64)
+    small = _ws(lib, 2, **kw)
+    big = _ws(lib, 1, **kw)
     assert 0 < small < big
+
+
+def test_causal_tiles_cover_the_padded_sequence(lib):
+    # K <= d_r: one tile of 64 rows x K bf16 per chunk of 64 tokens (the last chunk padded)
+    n = 64 * 1000 + 5
+    c = _ws(lib, 2, seq_len=n)
+    b = _ws(lib, 1, seq_len=n)
+    tiles = 16 * 1001 * 64 * 128 * 2
+    assert tiles <= c <= b + tiles + 4096
