@@ -94,14 +94,17 @@ tok_kernel(const MainArgs a) {
     __shared__ __attribute__((aligned(16))) char s_st[OUT ? NVT * NKQ * 1024 : 16];   // state^T fragments
     __shared__ __attribute__((aligned(16))) char s_zx[OUT ? NKQ * 1024 : 16];         // [Z_hi; Z_lo; 1; 0] fragments
     __shared__ __attribute__((aligned(16))) float s_c[KC];
-    __shared__ __attribute__((aligned(16))) float s_z[KC];   // Z of the state before the current chunk
+    // Z of the state before the current chunk: in registers of the owning wave, except in the pass
+    // that computes both the K and the Q side (its registers are full), which keeps Z in LDS
+    constexpr bool ZREG = MODE != MODE_OUT_CAUSAL;
+    __shared__ __attribute__((aligned(16))) float s_z[ZREG ? 4 : KC];
     lds_char* const LX = (lds_char*)s_x;
     lds_char* const LV = (lds_char*)s_v;
     lds_char* const LGK = (lds_char*)s_gk;
     lds_char* const LST = (lds_char*)s_st;
     lds_char* const LZX = (lds_char*)s_zx;
-    lds_char* const LC = (lds_char*)s_c;
     lds_char* const LZ = (lds_char*)s_z;
+    lds_char* const LC = (lds_char*)s_c;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -223,9 +226,11 @@ tok_kernel(const MainArgs a) {
     }
 
     // ---- state share: st[kqi][hh][vti] = rows (components) of tile 2(kq0+kqi)+hh, columns of d_v
-    // tile vt0+vti, in accumulator layout; Z in LDS (s_z), updated by the wave owning the components
+    // tile vt0+vti, in accumulator layout; Z of the owned components (zst[kqi][hh], every column of
+    // the accumulator tile holds Z of its rows) in the wave that owns them
     constexpr bool HAS_STATE = AGG || OUT;
     f32x4 st[HAS_STATE ? KQW : 1][2][HAS_STATE ? VTW : 1];
+    f32x4 zst[(HAS_STATE && ZREG) ? KQW : 1][2];
     const int64_t rec = (int64_t)KC * VC + KC;
     float* segrec = a.seg + ((int64_t)bh * a.P + sidx) * rec;
     if constexpr (HAS_STATE) {
@@ -243,7 +248,18 @@ tok_kernel(const MainArgs a) {
                                             : f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             }
-        for (int k = tid; k < KC; k += 256) s_z[k] = load ? src[(int64_t)KC * VC + k] : 0.f;
+        if constexpr (ZREG) {
+#pragma unroll
+            for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int ct = 2 * (kq0 + kqi) + hh;
+                    zst[kqi][hh] = (load && zown) ? *reinterpret_cast<const f32x4*>(src + (int64_t)KC * VC + ct * 16 + lg * 4)
+                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        } else {
+            for (int k = tid; k < KC; k += 256) s_z[k] = load ? src[(int64_t)KC * VC + k] : 0.f;
+        }
     }
     // bf16 state^T fragments: (vt, kq) is the A operand of O^T(vt) += state^T(vt, kq) . Gamma_Q^T(kq);
     // lane (r, g) holds d_v column 16 vt + r, components 32 kq + 4g + i and 32 kq + 16 + 4g + i
@@ -269,8 +285,14 @@ tok_kernel(const MainArgs a) {
 #pragma unroll
         for (int kqi = 0; kqi < KQW; ++kqi) {
             u32x4 f;
-            const f32x4 zq[2] = {lds_ld<f32x4>(LZ + ((kq0 + kqi) * 32 + lg * 4) * 4),
-                                 lds_ld<f32x4>(LZ + ((kq0 + kqi) * 32 + 16 + lg * 4) * 4)};
+            f32x4 zq[2];
+            if constexpr (ZREG) {
+                zq[0] = zst[kqi][0];
+                zq[1] = zst[kqi][1];
+            } else {
+                zq[0] = lds_ld<f32x4>(LZ + ((kq0 + kqi) * 32 + lg * 4) * 4);
+                zq[1] = lds_ld<f32x4>(LZ + ((kq0 + kqi) * 32 + 16 + lg * 4) * 4);
+            }
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const float z0 = zq[p >> 1][2 * (p & 1)], z1 = zq[p >> 1][2 * (p & 1) + 1];
@@ -284,13 +306,29 @@ tok_kernel(const MainArgs a) {
     // the bidirectional pass reads the fixed total state; the causal pass publishes the state before
     // each chunk at the start of that chunk (after barrier B0, read after B1)
     if constexpr (MODE == MODE_OUT_BIDIR) {
-        lds_barrier();   // s_z
         write_state();
         write_z();
     }
 
     if (ch0 < ch1) issue(ch0, 0);
     lds_barrier();   // s_c (and the bidirectional state) visible
+
+    // Stored-tile causal pass: the Q_X operand words and the logit constants of the next chunk are
+    // read from LDS at the end of the current one (its X rows have landed by then), so that their
+    // latency overlaps the chunk boundary instead of the start of the logits
+    u32x4 qraw_n[GLOAD ? NKS2 : 1];
+    f32x4 accq_n[GLOAD ? NCT : 1];
+    auto prefetch_q = [&](const lds_char* xw) {
+        [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < NKS2; ++ks) qraw_n[ks] = lds_ld<u32x4>(xw + OFF_XQ + xoff(ks));
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) accq_n[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
+    };
+    if constexpr (GLOAD) {
+        wait_vmcnt<NVD + NGD>();   // own X rows of the first chunk
+        prefetch_q(LX + w * XWAVE);
+    }
 
     // ---- Gamma_K tile: row-major [token][component] bf16 without padding; the 8-byte slots (four
     // components) of row r are XOR-swizzled within each 128-byte span by
@@ -430,9 +468,15 @@ tok_kernel(const MainArgs a) {
 
         // own X rows of this chunk landed (V and the Gamma_K tile of the chunk and the previous
         // chunk's stores may still be in flight)
-        if (first) wait_vmcnt<NVD + NGD>();
-        else wait_vmcnt<NVD + NGD + NST>();
-        if constexpr (NEED_V) lds_barrier();   // B0
+        if constexpr (GLOAD) {
+            // own X rows waited for and read at the end of the previous chunk.  B0 needs no LDS
+            // wait: every read of the previous chunk's shared buffers has been consumed.
+            block_barrier();   // B0
+        } else {
+            if (first) wait_vmcnt<NVD + NGD>();
+            else wait_vmcnt<NVD + NGD + NST>();
+            if constexpr (NEED_V) lds_barrier();   // B0
+        }
         if constexpr (!CAUSAL) {
             if (has_next) issue(ch + 1, BUF ^ 1);
         }
@@ -483,9 +527,9 @@ tok_kernel(const MainArgs a) {
                 u32x4 qraw[NKS2];
                 f32x4 accq[NCT];
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) accq[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
+                for (int ct = 0; ct < NCT; ++ct) accq[ct] = accq_n[ct];
 #pragma unroll
-                for (int ks = 0; ks < NKS2; ++ks) qraw[ks] = lds_ld<u32x4>(xw + OFF_XQ + xoff(ks));
+                for (int ks = 0; ks < NKS2; ++ks) qraw[ks] = qraw_n[ks];
                 f16x8 qxf[NKS2], qx2[NKS2];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) cvt_word(qraw[0], e, qxf[0], qx2[0]);
@@ -819,13 +863,26 @@ tok_kernel(const MainArgs a) {
                 for (int kqi = 0; kqi < KQW; ++kqi)
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
-                        f32x4 zi = {0.f, 0.f, 0.f, 0.f};
-                        mma(zi, gkc[kqi][hh][0], ones);
-                        mma(zi, gkc[kqi][hh][1], ones);
-                        const int zo = ((2 * (kq0 + kqi) + hh) * 16 + lg * 4) * 4;
-                        const f32x4 z = lds_ld<f32x4>(LZ + zo) + zi;
-                        if (lr == 0) lds_st<f32x4>(LZ + zo, z);
+                        if constexpr (ZREG) {
+                            mma(zst[kqi][hh], gkc[kqi][hh][0], ones);
+                            mma(zst[kqi][hh], gkc[kqi][hh][1], ones);
+                        } else {
+                            f32x4 zi = {0.f, 0.f, 0.f, 0.f};
+                            mma(zi, gkc[kqi][hh][0], ones);
+                            mma(zi, gkc[kqi][hh][1], ones);
+                            const int zo = ((2 * (kq0 + kqi) + hh) * 16 + lg * 4) * 4;
+                            const f32x4 z = lds_ld<f32x4>(LZ + zo) + zi;
+                            if (lr == 0) lds_st<f32x4>(LZ + zo, z);
+                        }
                     }
+            }
+            if constexpr (GLOAD) {
+                // own X rows of the next chunk: after them only its V and Gamma_K blocks and this
+                // chunk's stores were issued.  Done after the last chunk too (the reads then see
+                // stale LDS and are never used): an unconditional update keeps the carried
+                // registers dead through the chunk.
+                wait_vmcnt<NVD + NGD + NST>();
+                prefetch_q(LX + (BUF ^ 1) * XBUF + w * XWAVE);
             }
         }
     };
@@ -845,8 +902,13 @@ tok_kernel(const MainArgs a) {
                 for (int vti = 0; vti < VTW; ++vti)
                     *reinterpret_cast<f32x4*>(segrec + ((int64_t)(ct * NVT + vt0 + vti) * 64 + lane) * 4) = st[kqi][hh][vti];
             }
-        lds_barrier();   // Z updates of the last chunk
-        for (int k = tid; k < KC; k += 256) segrec[(int64_t)KC * VC + k] = s_z[k];
+        if (zown && lr == 0) {
+#pragma unroll
+            for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    *reinterpret_cast<f32x4*>(segrec + (int64_t)KC * VC + (2 * (kq0 + kqi) + hh) * 16 + lg * 4) = zst[kqi][hh];
+        }
     }
 }
 
