@@ -220,19 +220,21 @@ __global__ void __launch_bounds__(256) scan_kernel(float* seg, int P, int64_t re
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= rec) return;
     float* base = seg + (int64_t)blockIdx.y * P * rec + e;
+    // the last segment's causal aggregate is never produced (nothing follows it)
+    const int n = causal ? P - 1 : P;
     float run = 0.f;
-    if (causal) {
-        // the last segment's aggregate is never produced (nothing follows it)
-        for (int s = 0; s + 1 < P; ++s) {
-            const float x = base[(int64_t)s * rec];
-            base[(int64_t)s * rec] = run;
-            run += x;
+    // groups of 16 independent loads, then the sequential sum over the group
+    for (int s0 = 0; s0 < n; s0 += 16) {
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = (s0 + j < n) ? base[(int64_t)(s0 + j) * rec] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (causal && s0 + j < n) base[(int64_t)(s0 + j) * rec] = run;
+            run += x[j];
         }
-        base[(int64_t)(P - 1) * rec] = run;
-    } else {
-        for (int s = 0; s < P; ++s) run += base[(int64_t)s * rec];
-        base[0] = run;
     }
+    base[causal ? (int64_t)(P - 1) * rec : 0] = run;
 }
 
 gma_status_t launch_prep(const Plan& pl, const float* mu, const float* rv, const float* pr, char* ws, hipStream_t s) {

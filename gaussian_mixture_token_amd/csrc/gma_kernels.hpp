@@ -149,15 +149,19 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
         const int cl = e / DRC;
         const int d = e % DRC;
         const int comp = ct * 16 + cl;
+        // softplus and log in fp32 (about one ulp each); the per-dimension terms of c are summed in
+        // fp64 below
         double a = 0.0, b = 0.0, t = 0.0;
         if (comp < p.K && d < p.d_r) {
             const int64_t i = ((int64_t)h * p.K + comp) * p.d_r + d;
-            const double r = p.raw_var[i];
-            const double var = fmax(r, 0.0) + log1p(exp(-fabs(r)));   // softplus
+            const float r = p.raw_var[i];
+            const float varf = fmaxf(r, 0.f) + log1pf(expf(-fabsf(r)));   // softplus
+            const double var = varf;
             const double mu = p.mu[i];
-            a = -0.5 * LOG2E / var;
-            b = LOG2E * mu / var;
-            t = log(var) + mu * mu / var;
+            const double inv = 1.0 / var;
+            a = -0.5 * LOG2E * inv;
+            b = LOG2E * mu * inv;
+            t = (double)logf(varf) + mu * mu * inv;
         }
         s_t[cl][d] = t;
         // fragment positions of k = d (a part) and k = DRC + d (b part)

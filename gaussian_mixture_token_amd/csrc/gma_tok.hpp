@@ -313,21 +313,24 @@ tok_kernel(const MainArgs a) {
     if (ch0 < ch1) issue(ch0, 0);
     lds_barrier();   // s_c (and the bidirectional state) visible
 
-    // Stored-tile causal pass: the Q_X operand words and the logit constants of the next chunk are
-    // read from LDS at the end of the current one (its X rows have landed by then), so that their
-    // latency overlaps the chunk boundary instead of the start of the logits
-    u32x4 qraw_n[GLOAD ? NKS2 : 1];
-    f32x4 accq_n[GLOAD ? NCT : 1];
-    auto prefetch_q = [&](const lds_char* xw) {
+    // Passes with one logits side (the aggregate passes: K; the stored-tile causal pass: Q) read the
+    // X operand words and the logit constants of the next chunk from LDS at the end of the current
+    // one (its X rows have landed by then), so that their latency overlaps the chunk boundary
+    // instead of the start of the logits
+    constexpr bool PIPE = AGG || GLOAD;
+    constexpr int OFF_P = GLOAD ? OFF_XQ : OFF_XK;
+    u32x4 xraw_n[PIPE ? NKS2 : 1];
+    f32x4 acc_n[PIPE ? NCT : 1];
+    auto prefetch_x = [&](const lds_char* xw) {
         [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-        for (int ks = 0; ks < NKS2; ++ks) qraw_n[ks] = lds_ld<u32x4>(xw + OFF_XQ + xoff(ks));
+        for (int ks = 0; ks < NKS2; ++ks) xraw_n[ks] = lds_ld<u32x4>(xw + OFF_P + xoff(ks));
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) accq_n[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
+        for (int ct = 0; ct < NCT; ++ct) acc_n[ct] = lds_ld<f32x4>(LC + (ct * 16 + lg * 4) * 4);
     };
-    if constexpr (GLOAD) {
+    if constexpr (PIPE) {
         wait_vmcnt<NVD + NGD>();   // own X rows of the first chunk
-        prefetch_q(LX + w * XWAVE);
+        prefetch_x(LX + w * XWAVE);
     }
 
     // ---- Gamma_K tile: row-major [token][component] bf16 without padding; the 8-byte slots (four
@@ -468,7 +471,7 @@ tok_kernel(const MainArgs a) {
 
         // own X rows of this chunk landed (V and the Gamma_K tile of the chunk and the previous
         // chunk's stores may still be in flight)
-        if constexpr (GLOAD) {
+        if constexpr (PIPE) {
             // own X rows waited for and read at the end of the previous chunk.  B0 needs no LDS
             // wait: every read of the previous chunk's shared buffers has been consumed.
             block_barrier();   // B0
@@ -477,7 +480,7 @@ tok_kernel(const MainArgs a) {
             else wait_vmcnt<NVD + NGD + NST>();
             if constexpr (NEED_V) lds_barrier();   // B0
         }
-        if constexpr (!CAUSAL) {
+        if constexpr (!CAUSAL && !AGG) {
             if (has_next) issue(ch + 1, BUF ^ 1);
         }
 
@@ -519,57 +522,65 @@ tok_kernel(const MainArgs a) {
                 x2[2 * e + 1] = h[1] * h[1];
             };
             constexpr int NPUB = KQW * VTW;   // state fragments to publish
-            if constexpr (GLOAD) {
-                // Gamma_K of the chunk arrives as a stored tile.  The Q-side logits MFMAs, each pair
-                // followed by one small piece of independent vector work: one 32-bit word of the
-                // fp16 conversion of the next Q_X step, one fragment of the state publication, the
-                // Z fragments, a part of the next chunk's DMA.
-                u32x4 qraw[NKS2];
-                f32x4 accq[NCT];
+            if constexpr (PIPE) {
+                // One logits side (stored-tile causal pass: Q, Gamma_K of the chunk arrives as a stored
+                // tile; aggregate passes: K).  The logits MFMAs, each pair followed by one small piece
+                // of independent vector work: one 32-bit word of the fp16 conversion of the next X
+                // step, (causal) one fragment of the state publication or the Z fragments, a part of
+                // the next chunk's DMA.
+                u32x4 xraw[NKS2];
+                f32x4 acc[NCT];
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) accq[ct] = accq_n[ct];
+                for (int ct = 0; ct < NCT; ++ct) acc[ct] = acc_n[ct];
 #pragma unroll
-                for (int ks = 0; ks < NKS2; ++ks) qraw[ks] = qraw_n[ks];
-                f16x8 qxf[NKS2], qx2[NKS2];
+                for (int ks = 0; ks < NKS2; ++ks) xraw[ks] = xraw_n[ks];
+                f16x8 xf[NKS2], x2[NKS2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) cvt_word(qraw[0], e, qxf[0], qx2[0]);
+                for (int e = 0; e < 4; ++e) cvt_word(xraw[0], e, xf[0], x2[0]);
                 fence();
-                auto piece_q = [&](int ks, int p) {
+                constexpr int NPUBP = GLOAD ? NPUB : 0;
+                auto piece = [&](int ks, int p) {
                     const int nq = (ks + 1 < NKS2) ? 4 : 0;
-                    if (p < nq) { cvt_word(qraw[ks + 1], p, qxf[ks + 1], qx2[ks + 1]); return; }
+                    if (p < nq) { cvt_word(xraw[ks + 1], p, xf[ks + 1], x2[ks + 1]); return; }
                     p -= nq;
-                    const int npub = (NPUB - ks + NKS2 - 1) / NKS2;   // j = ks, ks + NKS2, ...
-                    if (p < npub) {
-                        const int jj = ks + p * NKS2;
-                        const int kqi = jj / VTW, vti = jj % VTW;
-                        lds_st<bf16x8>(LST + ((vt0 + vti) * NKQ + kq0 + kqi) * 1024 + lane * 16,
-                                       pack_pair(st[kqi][0][vti], st[kqi][1][vti]));
-                        return;
-                    }
-                    p -= npub;
-                    if (ks == NKS2 - 1) {
-                        if (p == 0) { write_z(); return; }
-                        p -= 1;
+                    if constexpr (GLOAD) {
+                        const int npub = (NPUBP - ks + NKS2 - 1) / NKS2;   // j = ks, ks + NKS2, ...
+                        if (p < npub) {
+                            const int jj = ks + p * NKS2;
+                            const int kqi = jj / VTW, vti = jj % VTW;
+                            lds_st<bf16x8>(LST + ((vt0 + vti) * NKQ + kq0 + kqi) * 1024 + lane * 16,
+                                           pack_pair(st[kqi][0][vti], st[kqi][1][vti]));
+                            return;
+                        }
+                        p -= npub;
+                        if (ks == NKS2 - 1) {
+                            if (p == 0) { write_z(); return; }
+                            p -= 1;
+                        }
                     }
                     const int d0 = ks * NPARTS / NKS2, d1 = (ks + 1) * NPARTS / NKS2;
                     if (p < d1 - d0 && has_next) issue_part(ch + 1, BUF ^ 1, d0 + p);
                 };
-                constexpr int NPQ = 4 + (NPUB + NKS2 - 1) / NKS2 + 1 + (NPARTS + NKS2 - 1) / NKS2;
+                constexpr int NPQ = 4 + (NPUBP + NKS2 - 1) / NKS2 + (GLOAD ? 1 : 0) + (NPARTS + NKS2 - 1) / NKS2;
                 constexpr int PPQ = (NPQ + NCT - 1) / NCT;   // pieces per MFMA pair
 #pragma unroll
                 for (int ks = 0; ks < NKS2; ++ks) {
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) {
-                        mma(accq[ct], abf[ct][ks], qx2[ks]);
-                        mma(accq[ct], abf[ct][ks + NKS2], qxf[ks]);
+                        mma(acc[ct], abf[ct][ks], x2[ks]);
+                        mma(acc[ct], abf[ct][ks + NKS2], xf[ks]);
 #pragma unroll
-                        for (int t = 0; t < PPQ; ++t) piece_q(ks, ct * PPQ + t);
+                        for (int t = 0; t < PPQ; ++t) piece(ks, ct * PPQ + t);
                         fence();
                     }
                 }
-                exp_rows(accq);
+                exp_rows(acc);
+                if constexpr (GLOAD) {
 #pragma unroll
-                for (int kq = 0; kq < NKQ; ++kq) pq[kq] = pack_pair(accq[2 * kq], accq[2 * kq + 1]);
+                    for (int kq = 0; kq < NKQ; ++kq) pq[kq] = pack_pair(acc[2 * kq], acc[2 * kq + 1]);
+                } else {
+                    write_gk(acc, tok < N32);
+                }
             } else if constexpr (CAUSAL) {
                 // Region A: the K-side logits MFMAs, each pair followed by one small piece of independent
                 // vector work: one 32-bit word of the fp16 conversion of the next K_X step or of a Q_X
@@ -678,13 +689,6 @@ tok_kernel(const MainArgs a) {
                 exp_rows(accq);
 #pragma unroll
                 for (int kq = 0; kq < NKQ; ++kq) pq[kq] = pack_pair(accq[2 * kq], accq[2 * kq + 1]);
-            } else {
-                f16x8 kxf[NKS2], kx2[NKS2];
-                x_frags(xw + OFF_XK, kxf, kx2);
-                f32x4 acck[NCT];
-                logits(kxf, kx2, acck);
-                exp_rows(acck);
-                write_gk(acck, tok < N32);
             }
 
             // own V blocks (and Gamma_K blocks) of this chunk landed, then B1
@@ -876,13 +880,13 @@ tok_kernel(const MainArgs a) {
                         }
                     }
             }
-            if constexpr (GLOAD) {
-                // own X rows of the next chunk: after them only its V and Gamma_K blocks and this
+            if constexpr (PIPE) {
+                // own X rows of the next chunk: after them only its V (and Gamma_K) blocks and this
                 // chunk's stores were issued.  Done after the last chunk too (the reads then see
                 // stale LDS and are never used): an unconditional update keeps the carried
                 // registers dead through the chunk.
                 wait_vmcnt<NVD + NGD + NST>();
-                prefetch_q(LX + (BUF ^ 1) * XBUF + w * XWAVE);
+                prefetch_x(LX + (BUF ^ 1) * XBUF + w * XWAVE);
             }
         }
     };
