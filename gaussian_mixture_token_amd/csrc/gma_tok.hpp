@@ -160,7 +160,8 @@ tok_kernel(const MainArgs a) {
     // DMA: lane l of block (rb, sg) fetches row 8 rb + l/8, global chunk (l % 8) ^ (l/8) ^ rb of
     // segment sg; the vector part of its byte offset below, the rest is per block and chunk
     // V: block fv holds rows RPB fv .. RPB fv + RPB - 1 chunk-major: 16-byte chunk c of row r of the
-    // block at (c RPB + r) 16.  Lane l fetches row l % RPB, chunk l / RPB.
+    // block at (c RPB + r) 16 (with RPB = 4, odd blocks hold chunk c ^ 2 there).  Lane l fetches row
+    // l % RPB of its block.
     const uint32_t lx_base = lds_addr(LX), lv_base = lds_addr(LV), lg_base = lds_addr(LGK);
 
     // DMA of chunk ch into staging buffer buf, in parts: part sd < NSIDE = own X rows of one side,
@@ -180,7 +181,11 @@ tok_kernel(const MainArgs a) {
             else dma16x2(rs, m0, m0 + 1024, x0, x1);
         } else if (part == NSIDE) {
             if constexpr (NEED_V) {
-                const uint32_t vl = ((lane % RPB) * d_v + (lane / RPB) * 8) * 2;
+                // with four rows per block, the blocks of odd waves (odd blocks) are rotated by 128
+                // bytes (chunk index ^ 2) so that the transposed reads of two adjacent blocks do not
+                // share banks
+                const uint32_t vch = (lane / RPB) ^ ((RPB == 4 && (w & 1)) ? 2u : 0u);
+                const uint32_t vl = ((lane % RPB) * d_v + vch * 8) * 2;
                 const uint32_t vstep = W * RPB * d_v * 2;
                 const uint32_t v0 = vl + (n0 + w * RPB) * d_v * 2;
                 const uint32_t m0 = lv_base + buf * VBUF + w * 1024;
@@ -334,13 +339,19 @@ tok_kernel(const MainArgs a) {
     }
 
     // ---- Gamma_K tile: row-major [token][component] bf16 without padding; the 8-byte slots (four
-    // components) of row r are XOR-swizzled within each 128-byte span by
-    //   KC >= 64: 4 (r & 3) + ((r >> 2) & 3)       KC = 32: 4 ((r >> 1) & 1) + ((r >> 2) & 3)
-    // so that a 16-lane group reading one slot of 16 consecutive rows, or four slots of four
-    // consecutive rows (transposed reads), touches every bank once.  The stored tiles use the same
-    // image, so the causal output pass copies them into LDS unchanged.
+    // components) of row r are XOR-swizzled by (bits of r & 15 written r3 r2 r1 r0)
+    //   KC >= 128: r2 r1 r0 r3 r2      KC = 64: r2 r1 r3 r0      KC = 32: r2 r3 r1
+    // LDS serves 8-byte reads 32 lanes at a time over 256 bytes of banks, and 8-byte writes 16 lanes
+    // at a time over 128 bytes.  With this swizzle the row reads of S^T (one or two slots of 16
+    // consecutive rows per 32 lanes), the transposed reads of the state update (four slots of eight
+    // consecutive rows per 32 lanes) and the row writes (one slot of 16 rows per 16 lanes) each touch
+    // every bank once.  The stored tiles use the same image, so the causal output pass copies them
+    // into LDS unchanged.
     auto gk_off = [](int row, int slot) -> int {
-        const int sw = (KC >= 64) ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+        const int r = row & 15;
+        const int sw = (KC >= 128) ? (((r & 7) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1))
+                     : (KC == 64)  ? ((((r >> 1) & 3) << 2) | (((r >> 3) & 1) << 1) | (r & 1))
+                                   : ((((r >> 2) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 1) & 1));
         return row * GKR + ((slot ^ sw) << 3);
     };
     // A of S^T = Gamma_K Gamma_Q^T: lane = token 16 J + r, slots = components of pair kq
@@ -370,8 +381,11 @@ tok_kernel(const MainArgs a) {
     // bytes (conflict-free) and the address is affine in vt and tk.
     auto v_frag = [&](const lds_char* vb, int vt, int tk) -> bf16x8 {
         [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
+        // odd blocks (four rows per block: lane group lg reads block lg of its token step) are
+        // rotated by 128 bytes: there d_v tile vt sits where tile vt ^ 1 sits in even blocks
+        const int rot = (RPB == 4) ? (lg & 1) * ((vt & 1) ? -128 : 128) : 0;
         const int v_lane_off = (((lg * 4 + ((lane >> 2) & 3)) / RPB) * 1024) +
-                               ((((lane & 3) >> 1) * RPB + (lg * 4 + ((lane >> 2) & 3)) % RPB) * 16) + (lane & 1) * 8;
+                               ((((lane & 3) >> 1) * RPB + (lg * 4 + ((lane >> 2) & 3)) % RPB) * 16) + (lane & 1) * 8 + rot;
         u32x2 part[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
