@@ -159,6 +159,19 @@ def test_tails_and_tiny_lengths(gma, base, N, causal):
     assert err <= TOL[w.dtype], err
 
 
+@pytest.mark.parametrize("shape", [(96, 100, 120), (128, 96, 128), (40, 20, 48), (40, 30, 56), (64, 200, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_padded_shapes(gma, shape, causal):
+    # d_r, K and d_v below the kernels' tile sizes: padding dimensions, padding value columns and
+    # padding components (K = 96 leaves two whole tiles of them; K = 200 uses the K = 256 kernels)
+    d_r, K, d_v = shape
+    w = gma.workload(3, batch=1, heads=2, seq_len=1500, d_route=d_r, n_comp=K, d_value=d_v)
+    say("padded shape d_r=%d K=%d d_v=%d causal=%s" % (d_r, K, d_v, causal))
+    inp = gma.make_inputs(w)
+    err = rel_err(gpu_forward(gma, w, inp, causal), ref_forward(w, inp, causal))
+    assert err <= TOL[w.dtype], err
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bitwise_deterministic(gma, causal):
     w = gma.workload(3, seq_len=20000)
