@@ -73,8 +73,9 @@ const ShapeClass* find_class(bool f32, int kc, int vc, int drc) {
 }
 
 // Validates sizes (pure host) and fills the plan for the register-staged kernels or, with tok, for
-// the token-split LDS-DMA kernels (chunks of kTokChunk tokens).  No HIP call.
-gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = false) {
+// the token-split LDS-DMA kernels (chunks of kTokChunk tokens; with tiles, the causal pair through
+// stored Gamma_K tiles where it applies).  No HIP call.
+gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = false, bool tiles = true) {
     if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
     if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_FORWARD_CAUSAL)
         return fail(GMA_ERROR_INVALID_VALUE, "unknown op %d", op);
@@ -136,12 +137,15 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     if (BH * plan->P > INT32_MAX)
         return fail(GMA_ERROR_NOT_SUPPORTED, "grid too large");
 
-    // Causal token-split path through stored Gamma_K tiles: taken where a tile row (K bf16) is no
-    // wider than an X row (d_r bf16), so the output pass reads no more bytes than it would for K_X,
-    // and the tiles of one (batch, head) stay within 32-bit byte offsets.
+    // Causal token-split path through stored Gamma_K tiles.  Storing Gamma_K (K bf16 per token)
+    // instead of recomputing it from K_X (d_r bf16 per token) in the output pass saves the K-side
+    // logits GEMM and softmax at the price of 2 K bytes written and read per token-head.  Measured
+    // on MI355X it wins at K = d_r = 128 (0.62 -> 0.55 ms per step) and at K = 4 d_r = 256 (4.01 ->
+    // 3.74 ms), so it is taken up to K = 4 d_r, while the tiles of one (batch, head) stay within
+    // 32-bit byte offsets.
     const int64_t tile_bytes = (int64_t)C * plan->cls->kc * 2;
-    plan->gtiles = tok && op == GMA_OP_FORWARD_CAUSAL && plan->cls->tok_out_causal_g && plan->cls->kc <= plan->cls->drc &&
-                   plan->n_chunks * tile_bytes < (int64_t(1) << 31);
+    plan->gtiles = tiles && tok && op == GMA_OP_FORWARD_CAUSAL && plan->cls->tok_out_causal_g &&
+                   plan->cls->kc <= 4 * plan->cls->drc && plan->n_chunks * tile_bytes < (int64_t(1) << 31);
 
     // workspace: [a | b] fragments, c, segment records, Gamma_K tiles
     const int ks = plan->f32 ? 16 : 32;
@@ -159,6 +163,18 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     plan->off_gk = align_up(plan->off_seg + seg_bytes, 256);
     plan->total = align_up(plan->off_gk + gk_bytes, 256);
     return GMA_SUCCESS;
+}
+
+// Workspace bytes advertised for (problem, op): the register-staged plan or the token-split plan,
+// whichever is larger (which one runs is decided per call from pointer alignment).  0 if invalid.
+size_t advertised_workspace(const gma_problem_t* problem, int op) {
+    Plan pl;
+    if (make_plan(problem, op, &pl) != GMA_SUCCESS) return 0;
+    size_t total = pl.total;
+    Plan pt;
+    if (op != GMA_OP_RESPONSIBILITIES && pl.cls->tok_out_causal && make_plan(problem, op, &pt, true) == GMA_SUCCESS)
+        total = std::max(total, pt.total);
+    return total;
 }
 
 bool misaligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) != 0; }
@@ -278,11 +294,12 @@ int vec_o_ok(const void* ptr, int d, bool f32) {
     return (d % 4 == 0) && !misaligned(ptr, f32 ? 16 : 8);
 }
 
+// size_check = false: the caller checks the workspace size against the plan it finally runs
 gma_status_t check_common(const gma_problem_t* p, const void* const* ptrs, int nptrs, void* ws, size_t ws_bytes,
-                          const Plan& pl) {
+                          const Plan& pl, bool size_check = true) {
     for (int i = 0; i < nptrs; ++i)
         if (!ptrs[i]) return fail(GMA_ERROR_INVALID_VALUE, "pointer argument %d is NULL", i);
-    if (ws_bytes < pl.total)
+    if (size_check && ws_bytes < pl.total)
         return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
                     ws_bytes, pl.total);
     if (pl.total > 0 && !ws) return fail(GMA_ERROR_INVALID_VALUE, "workspace is NULL");
@@ -299,7 +316,7 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
     gma_status_t st = make_plan(p, causal ? GMA_OP_FORWARD_CAUSAL : GMA_OP_FORWARD_BIDIR, &pl);
     if (st != GMA_SUCCESS) return st;
     const void* ptrs[] = {qx, kx, v, mu, rv, pr, o};
-    st = check_common(p, ptrs, 7, ws, ws_bytes, pl);
+    st = check_common(p, ptrs, 7, ws, ws_bytes, pl, false);
     if (st != GMA_SUCCESS) return st;
     const size_t es = pl.f32 ? 4 : 2;
     for (const void* ptr : {qx, kx, v, (const void*)o})
@@ -310,9 +327,6 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
     const size_t nv = (size_t)(pl.B * pl.H * pl.N) * pl.d_v * es;
     if (overlaps(o, nv, qx, nx) || overlaps(o, nv, kx, nx) || overlaps(o, nv, v, nv))
         return fail(GMA_ERROR_INVALID_VALUE, "o must not overlap qx, kx or v");
-    if (ws && (overlaps(ws, pl.total, qx, nx) || overlaps(ws, pl.total, kx, nx) ||
-               overlaps(ws, pl.total, v, nv) || overlaps(ws, pl.total, o, nv)))
-        return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
 
     // Token-split LDS-DMA kernels: bf16, rows in whole 16-byte chunks, 16-byte aligned bases, byte
     // offsets within one (batch, head) slice (one chunk past the end included) below 2^31.
@@ -322,13 +336,20 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
     if (dma) {
         st = make_plan(p, causal ? GMA_OP_FORWARD_CAUSAL : GMA_OP_FORWARD_BIDIR, &pl, true);
         if (st != GMA_SUCCESS) return st;
-        if (ws_bytes < pl.total)
-            return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
-                        ws_bytes, pl.total);
-        if (overlaps(ws, pl.total, qx, nx) || overlaps(ws, pl.total, kx, nx) || overlaps(ws, pl.total, v, nv) ||
-            overlaps(ws, pl.total, o, nv))
-            return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
+        if (pl.gtiles && ws_bytes < advertised_workspace(p, GMA_OP_FORWARD_CAUSAL)) {
+            // less than the advertised workspace: no stored Gamma_K tiles, the causal output pass
+            // recomputes Gamma_K
+            st = make_plan(p, GMA_OP_FORWARD_CAUSAL, &pl, true, false);
+            if (st != GMA_SUCCESS) return st;
+        }
     }
+    // the workspace against the plan that runs
+    if (ws_bytes < pl.total)
+        return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                    ws_bytes, pl.total);
+    if (ws && (overlaps(ws, pl.total, qx, nx) || overlaps(ws, pl.total, kx, nx) || overlaps(ws, pl.total, v, nv) ||
+               overlaps(ws, pl.total, o, nv)))
+        return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* w = reinterpret_cast<char*>(ws);
@@ -380,13 +401,7 @@ using namespace gma;
 extern "C" {
 
 size_t gma_workspace_size(const gma_problem_t* problem, int op) {
-    Plan pl;
-    if (make_plan(problem, op, &pl) != GMA_SUCCESS) return 0;
-    size_t total = pl.total;
-    // the forward passes may take the token-split path (decided per call from pointer alignment)
-    Plan pt;
-    if (op != GMA_OP_RESPONSIBILITIES && pl.cls->tok_out_causal && make_plan(problem, op, &pt, true) == GMA_SUCCESS)
-        total = std::max(total, pt.total);
+    const size_t total = advertised_workspace(problem, op);
     g_last_error.clear();
     return total;
 }

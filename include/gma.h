@@ -78,8 +78,12 @@ typedef struct {
     float eps;
 } gma_problem_t;
 
-/* Bytes of workspace `op` needs for `problem`; 0 if the problem is invalid or unsupported.
- * Pure host computation. */
+/* Bytes of workspace `op` needs for `problem` on its fastest path; 0 if the problem is invalid or
+ * unsupported.  Pure host computation.  For GMA_OP_FORWARD_CAUSAL with bf16 storage this includes
+ * the stored responsibility tiles of the keys, B * H * ceil(N / 64) * 64 * K_padded * 2 bytes
+ * (K_padded: K rounded up to a power of two, at least 32).  The tiles are used only with a
+ * workspace of at least this size; a smaller one is still accepted where it holds the rest, and
+ * the causal pass then recomputes Gamma_K from K_X (slower). */
 size_t gma_workspace_size(const gma_problem_t* problem, int op);
 
 /* Responsibilities (item 1 above) of every row of x [B, H, N, d_r] under head h's mixture:

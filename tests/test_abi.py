@@ -83,7 +83,10 @@ def test_workspace_too_small_and_null(lib, fn):
     prob = _prob()
     need = lib.gma_workspace_size(ctypes.byref(prob), 2 if fn.endswith("causal") else 1)
     assert need > 0
-    assert _fwd(lib, fn, prob, ws_bytes=need - 1) == 3
+    # gma_workspace_size() is what the fastest applicable path needs; a somewhat smaller workspace
+    # may still fit the path that runs (which then launches kernels: covered on the GPU).  One
+    # smaller than every path's need is rejected before any HIP call.
+    assert _fwd(lib, fn, prob, ws_bytes=4096) == 3
     assert _fwd(lib, fn, prob, ws_bytes=need, ws=None) == 1
 
 
@@ -141,9 +144,9 @@ def test_workspace_is_linear_memory_not_quadratic(lib):
 
 
 def test_small_causal_problem_needs_no_segment_records(lib):
-    # one segment per head: no carried state.  With K wider than d_r the Gamma_K tiles are not
-    # stored, and the workspace holds only the prepared parameters.
-    kw = dict(seq_len=64, heads=1024, d_route=64, n_comp=256, d_value=64)
+    # one segment per head: no carried state.  On the fp32 path (no stored Gamma_K tiles) the
+    # workspace holds only the prepared parameters.
+    kw = dict(seq_len=64, heads=1024, d_route=64, n_comp=64, d_value=64, dtype=0)
     small = _ws(lib, 2, **kw)
     big = _ws(lib, 1, **kw)
     assert 0 < small < big

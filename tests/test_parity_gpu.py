@@ -172,6 +172,19 @@ def test_bf16_padded_shapes(gma, shape, causal):
     assert err <= TOL[w.dtype], err
 
 
+@pytest.mark.parametrize("cfg,N", [(3, 5000), (4, 3001), (2, 2000)])
+def test_causal_without_room_for_stored_tiles(gma, cfg, N):
+    # less than the advertised workspace: no stored Gamma_K tiles, the causal output pass recomputes
+    # Gamma_K from K_X
+    w = gma.workload(cfg, batch=1, heads=2, seq_len=N)
+    say("causal, reduced workspace, cfg %d N=%d" % (cfg, N))
+    inp = gma.make_inputs(w)
+    prob = gma.problem(w.batch, w.heads, w.seq_len, w.d_route, w.n_comp, w.d_value, w.torch_dtype, w.eps)
+    ws = torch.empty(gma.workspace_size(prob, 2) - 1, dtype=torch.uint8, device=DEV)
+    err = rel_err(gpu_forward(gma, w, inp, True, workspace=ws), ref_forward(w, inp, True))
+    assert err <= TOL[w.dtype], err
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bitwise_deterministic(gma, causal):
     w = gma.workload(3, seq_len=20000)
