@@ -575,18 +575,46 @@ tok_kernel(const MainArgs a) {
                     const int d0 = ks * NPARTS / NKS2, d1 = (ks + 1) * NPARTS / NKS2;
                     if (p < d1 - d0 && has_next) issue_part(ch + 1, BUF ^ 1, d0 + p);
                 };
-                constexpr int NPQ = 4 + (NPUBP + NKS2 - 1) / NKS2 + (GLOAD ? 1 : 0) + (NPARTS + NKS2 - 1) / NKS2;
-                constexpr int PPQ = (NPQ + NCT - 1) / NCT;   // pieces per MFMA pair
-#pragma unroll
-                for (int ks = 0; ks < NKS2; ++ks) {
+                if constexpr (AGG) {
+                    // Aggregate passes: tile order.  Component tile ct's chain of 2 NKS2 MFMAs accumulates
+                    // in place (measured faster here; the step order below is faster in the causal pass);
+                    // the fp16 conversion of the next X steps rides on tile 0, the DMA parts on tiles >= 1.
+                    constexpr int NXS = (NCT - 1) * NKS2;
+                    constexpr int EPS = (NPARTS + NXS - 1) / NXS;   // DMA parts per slot
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) {
-                        mma(acc[ct], abf[ct][ks], x2[ks]);
-                        mma(acc[ct], abf[ct][ks + NKS2], xf[ks]);
 #pragma unroll
-                        for (int t = 0; t < PPQ; ++t) piece(ks, ct * PPQ + t);
-                        fence();
+                        for (int ks = 0; ks < NKS2; ++ks) {
+                            mma(acc[ct], abf[ct][ks], x2[ks]);
+                            mma(acc[ct], abf[ct][ks + NKS2], xf[ks]);
+                            if (ct == 0) {
+                                if (ks + 1 < NKS2) {
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) cvt_word(xraw[ks + 1], e, xf[ks + 1], x2[ks + 1]);
+                                }
+                            } else {
+                                const int sl = (ct - 1) * NKS2 + ks;
+#pragma unroll
+                                for (int t = 0; t < EPS; ++t)
+                                    if (sl * EPS + t < NPARTS && has_next) issue_part(ch + 1, BUF ^ 1, sl * EPS + t);
+                            }
+                            fence();
+                        }
                     }
+                } else {
+                    constexpr int NPQ = 4 + (NPUBP + NKS2 - 1) / NKS2 + (GLOAD ? 1 : 0) + (NPARTS + NKS2 - 1) / NKS2;
+                    constexpr int PPQ = (NPQ + NCT - 1) / NCT;   // pieces per MFMA pair
+#pragma unroll
+                    for (int ks = 0; ks < NKS2; ++ks) {
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct) {
+                            mma(acc[ct], abf[ct][ks], x2[ks]);
+                            mma(acc[ct], abf[ct][ks + NKS2], xf[ks]);
+#pragma unroll
+                            for (int t = 0; t < PPQ; ++t) piece(ks, ct * PPQ + t);
+                            fence();
+                        }
+                }
                 }
                 exp_rows(acc);
                 if constexpr (GLOAD) {
