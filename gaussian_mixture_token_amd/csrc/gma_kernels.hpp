@@ -109,9 +109,11 @@ struct PrepArgs {
 //   ab[h][ct][ks][lane][j] = A[comp = 16 ct + lane % 16][k = ks*KS + (lane/16)*(KS/4) + j]
 // with A = [a | b] (k < DRC: a_{comp,k}; k >= DRC: b_{comp,k-DRC}).  Pad components get
 // a = b = 0 and c = -inf (their posterior is exactly 0); pad dimensions get a = b = 0.
-// Arithmetic in fp64; the sum over d of each c_k runs in a fixed order.
+// Softplus and log in fp32 (about one ulp); a, b, the per-dimension terms of c and their sum in
+// fp64; every reduction runs in a fixed order.
+constexpr int kPrepThreads = 512;
 template <bool F32, int KC, int DRC>
-__global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
+__global__ void __launch_bounds__(kPrepThreads) prep_kernel(const PrepArgs p) {
     using T = Tr<F32>;
     constexpr int KS = T::KS;
     constexpr int NKS = 2 * DRC / KS;
@@ -120,32 +122,24 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
     const int ct = blockIdx.y;
     const int tid = threadIdx.x;
     const double LOG2E = 1.4426950408889634073599246810019;
-    __shared__ double s_red[256];
     __shared__ double s_t[16][DRC];
+    __shared__ double s_lse;
 
-    // log-sum-exp of the prior logits of this head
-    double m = -INFINITY;
-    for (int k = tid; k < p.K; k += 256) m = fmax(m, (double)p.prior[(int64_t)h * p.K + k]);
-    s_red[tid] = m;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) s_red[tid] = fmax(s_red[tid], s_red[tid + s]);
-        __syncthreads();
+    // log-sum-exp of the prior logits of this head, by wave 0 (butterfly reductions, fixed order)
+    if (tid < 64) {
+        double m = -INFINITY;
+        for (int k = tid; k < p.K; k += 64) m = fmax(m, (double)p.prior[(int64_t)h * p.K + k]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
+        double acc = 0.0;
+        for (int k = tid; k < p.K; k += 64) acc += exp((double)p.prior[(int64_t)h * p.K + k] - m);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (tid == 0) s_lse = m + log(acc);
     }
-    const double mx = s_red[0];
-    __syncthreads();
-    double acc = 0.0;
-    for (int k = tid; k < p.K; k += 256) acc += exp((double)p.prior[(int64_t)h * p.K + k] - mx);
-    s_red[tid] = acc;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) s_red[tid] += s_red[tid + s];
-        __syncthreads();
-    }
-    const double lse = mx + log(s_red[0]);
 
     // a, b and the per-dimension terms of c for the 16 components of this tile
-    for (int e = tid; e < 16 * DRC; e += 256) {
+    for (int e = tid; e < 16 * DRC; e += kPrepThreads) {
         const int cl = e / DRC;
         const int d = e % DRC;
         const int comp = ct * 16 + cl;
@@ -187,7 +181,7 @@ __global__ void __launch_bounds__(256) prep_kernel(const PrepArgs p) {
         if (comp < p.K) {
             double sum = 0.0;
             for (int d = 0; d < p.d_r; ++d) sum += s_t[tid][d];
-            const double logpi = (double)p.prior[(int64_t)h * p.K + comp] - lse;
+            const double logpi = (double)p.prior[(int64_t)h * p.K + comp] - s_lse;
             c = (float)(LOG2E * (logpi - 0.5 * sum));
         }
         p.cvec[(int64_t)h * KC + comp] = c;
