@@ -29,7 +29,7 @@ _LIB = os.path.join(_HERE, "libgma_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-__all__ = ["build", "params", "responsibilities", "forward", "set_threads", "max_threads"]
+__all__ = ["build", "params", "responsibilities", "forward", "forward_causal_state", "set_threads", "max_threads"]
 
 
 def build(force: bool = True) -> str:
@@ -59,6 +59,9 @@ def _load():
             lib.gma_oracle_forward.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32,
                                                ctypes.c_double, dp, dp, dp, dp, dp, dp, dp]
             lib.gma_oracle_forward.restype = ctypes.c_int
+            lib.gma_oracle_forward_causal_state.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.c_double,
+                                                            dp, dp, dp, dp, dp, dp, dp, dp, dp]
+            lib.gma_oracle_forward_causal_state.restype = ctypes.c_int
             lib.gma_oracle_set_threads.argtypes = [ctypes.c_int]
             lib.gma_oracle_set_threads.restype = None
             lib.gma_oracle_max_threads.argtypes = []
@@ -141,3 +144,30 @@ def forward(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, causal: boo
     if rc != 0:
         raise MemoryError("oracle: allocation failed")
     return o[0, 0] if squeeze else o
+
+
+def forward_causal_state(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, state_in=None,
+                         threads: Optional[int] = None):
+    """Causal O [B, H, N, d_v] and the latent memory after the last token, [B, H, K, d_v + 1]
+    (row k: Vt[k, :] then Z[k]), starting from state_in (same layout; None = zero)."""
+    qx, kx, v = _f64(qx), _f64(kx), _f64(v)
+    mu, rv, pl = _f64(mu), _f64(raw_var), _f64(prior_logits)
+    B, H, N, dr = qx.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    assert kx.shape == qx.shape and v.shape == (B, H, N, dv)
+    assert mu.shape == (H, K, dr) and rv.shape == (H, K, dr) and pl.shape == (H, K)
+    sin = None if state_in is None else _f64(state_in)
+    if sin is not None:
+        assert sin.shape == (B, H, K, dv + 1)
+    o = np.empty((B, H, N, dv), dtype=np.float64)
+    sout = np.empty((B, H, K, dv + 1), dtype=np.float64)
+    lib = _load()
+    if threads is not None:
+        lib.gma_oracle_set_threads(int(threads))
+    rc = lib.gma_oracle_forward_causal_state(B, H, N, dr, K, dv, float(eps), _ptr(qx), _ptr(kx), _ptr(v),
+                                             _ptr(mu), _ptr(rv), _ptr(pl),
+                                             None if sin is None else _ptr(sin), _ptr(sout), _ptr(o))
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return o, sout

@@ -143,11 +143,15 @@ int gma_oracle_responsibilities(int64_t B, int64_t H, int64_t N, int32_t dr, int
 
 /* Forward mixer ("Routage de Memoire Latente" and "Variantes et Entrainement").
  * qx, kx [B, H, N, d_r]; v [B, H, N, d_v]; o [B, H, N, d_v]; causal = 0 or 1.
+ * Causal only: state_in (or NULL = zero) is the latent memory before the first token and
+ * state_out (or NULL) receives it after the last one, both [B, H, K, d_v + 1]: row k holds
+ * Vt[k, 0 .. d_v-1] and then Z[k].  The running sums simply start from state_in.
  * Returns 0, or 1 if memory could not be allocated. */
-int gma_oracle_forward(int causal, int64_t B, int64_t H, int64_t N, int32_t dr, int32_t K,
-                       int32_t dv, double eps, const double* qx, const double* kx,
-                       const double* v, const double* mu, const double* raw_var,
-                       const double* prior_logits, double* o) {
+static int forward_impl(int causal, int64_t B, int64_t H, int64_t N, int32_t dr, int32_t K,
+                        int32_t dv, double eps, const double* qx, const double* kx,
+                        const double* v, const double* mu, const double* raw_var,
+                        const double* prior_logits, const double* state_in, double* state_out,
+                        double* o) {
     double* var = (double*)malloc(sizeof(double) * H * K * dr);
     double* logp = (double*)malloc(sizeof(double) * H * K);
     double* logdet = (double*)malloc(sizeof(double) * H * K);
@@ -173,6 +177,13 @@ int gma_oracle_forward(int causal, int64_t B, int64_t H, int64_t N, int32_t dr, 
         double* o_bh = o + bh * N * dv;
         memset(vt, 0, sizeof(double) * (size_t)K * dv);
         memset(z, 0, sizeof(double) * (size_t)K);
+        if (causal && state_in) {
+            const double* s = state_in + bh * K * (dv + 1);
+            for (int k = 0; k < K; ++k) {
+                for (int c = 0; c < dv; ++c) vt[(int64_t)k * dv + c] = s[(int64_t)k * (dv + 1) + c];
+                z[k] = s[(int64_t)k * (dv + 1) + dv];
+            }
+        }
 
         if (!causal) {
             /* Write phase over the whole sequence: Vt = Gamma_K^T V, Z = Gamma_K^T 1. */
@@ -237,9 +248,33 @@ int gma_oracle_forward(int causal, int64_t B, int64_t H, int64_t N, int32_t dr, 
                     }
                 }
             }
+            if (state_out) {
+                double* s = state_out + bh * K * (dv + 1);
+                for (int k = 0; k < K; ++k) {
+                    for (int c = 0; c < dv; ++c) s[(int64_t)k * (dv + 1) + c] = vt[(int64_t)k * dv + c];
+                    s[(int64_t)k * (dv + 1) + dv] = z[k];
+                }
+            }
         }
     }
 done:
     free(var); free(logp); free(logdet); free(gq); free(gk); free(vt); free(z); free(den);
     return rc;
+}
+
+int gma_oracle_forward(int causal, int64_t B, int64_t H, int64_t N, int32_t dr, int32_t K,
+                       int32_t dv, double eps, const double* qx, const double* kx,
+                       const double* v, const double* mu, const double* raw_var,
+                       const double* prior_logits, double* o) {
+    return forward_impl(causal, B, H, N, dr, K, dv, eps, qx, kx, v, mu, raw_var, prior_logits, NULL, NULL, o);
+}
+
+/* Causal forward with the latent memory carried in (state_in, NULL = zero) and out (state_out,
+ * NULL = not wanted); layouts as above. */
+int gma_oracle_forward_causal_state(int64_t B, int64_t H, int64_t N, int32_t dr, int32_t K,
+                                    int32_t dv, double eps, const double* qx, const double* kx,
+                                    const double* v, const double* mu, const double* raw_var,
+                                    const double* prior_logits, const double* state_in,
+                                    double* state_out, double* o) {
+    return forward_impl(1, B, H, N, dr, K, dv, eps, qx, kx, v, mu, raw_var, prior_logits, state_in, state_out, o);
 }

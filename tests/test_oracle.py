@@ -329,3 +329,65 @@ def test_property_random_shapes_match_brute_force(N, dr, K, dv, causal, seed):
     o = oracle.forward(qx, kx, v, mu, rv, pl, eps=1e-6, causal=causal)
     gq, gk = scipy_gamma(qx, mu[0], rv[0], pl[0]), scipy_gamma(kx, mu[0], rv[0], pl[0])
     np.testing.assert_allclose(o, brute_force(gq, gk, v, 1e-6, causal), rtol=1e-9, atol=1e-11)
+
+
+# ----------------------------------------------------------------------------- carried state
+# Causal variant with the latent memory carried in and out (page "Attention par Mélange Gaussien
+# (GMA)", "Mécanisme Central" item 3: the causal output is a prefix sum, so the prefix before the
+# first token enters only through [Vt | Z]).
+
+
+def test_state_zero_initial_state_is_plain_causal(oracle_mod):
+    rng = np.random.default_rng(21)
+    B, H, N, dr, K, dv = 2, 2, 300, 5, 7, 6
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    qx, kx, v = rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dv))
+    o, _ = oracle_mod.forward_causal_state(qx, kx, v, mu, rv, pl)
+    np.testing.assert_array_equal(o, oracle_mod.forward(qx, kx, v, mu, rv, pl, causal=True))
+
+
+def test_state_final_state_is_the_write_phase(oracle_mod):
+    # from a zero state, the final [Vt | Z] is Gamma_K^T [V | 1] over the sequence, with Gamma_K
+    # from SciPy (an independent computation)
+    rng = np.random.default_rng(22)
+    H, N, dr, K, dv = 2, 200, 4, 5, 3
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    qx, kx, v = rng.normal(0, 1, (1, H, N, dr)), rng.normal(0, 1, (1, H, N, dr)), rng.normal(0, 1, (1, H, N, dv))
+    _, s = oracle_mod.forward_causal_state(qx, kx, v, mu, rv, pl)
+    for h in range(H):
+        gk = scipy_gamma(kx[0, h], mu[h], rv[h], pl[h])
+        np.testing.assert_allclose(s[0, h, :, :dv], gk.T @ v[0, h], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(s[0, h, :, dv], gk.sum(axis=0), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("m", [1, 97, 299])
+def test_state_split_sequence_equals_one_pass(oracle_mod, m):
+    # running [0, m) and then [m, N) from the carried state reproduces the one-pass result bitwise
+    rng = np.random.default_rng(23)
+    B, H, N, dr, K, dv = 1, 3, 300, 4, 6, 5
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    qx, kx, v = rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dv))
+    o, s = oracle_mod.forward_causal_state(qx, kx, v, mu, rv, pl)
+    o1, s1 = oracle_mod.forward_causal_state(qx[:, :, :m], kx[:, :, :m], v[:, :, :m], mu, rv, pl)
+    o2, s2 = oracle_mod.forward_causal_state(qx[:, :, m:], kx[:, :, m:], v[:, :, m:], mu, rv, pl, state_in=s1)
+    np.testing.assert_array_equal(np.concatenate([o1, o2], axis=2), o)
+    np.testing.assert_array_equal(s2, s)
+
+
+def test_state_initial_state_acts_as_a_prefix(oracle_mod):
+    # an initial state built by hand from prefix tokens (SciPy posteriors) gives the outputs that the
+    # brute-force causal form gives for those rows after the prefix
+    rng = np.random.default_rng(24)
+    P, N, dr, K, dv = 40, 60, 3, 4, 3
+    mu, rv, pl = rand_params(rng, 1, K, dr)
+    kx_p, v_p = rng.normal(0, 1, (P, dr)), rng.normal(0, 1, (P, dv))
+    qx, kx, v = rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dr)), rng.normal(0, 1, (N, dv))
+    gk_p = scipy_gamma(kx_p, mu[0], rv[0], pl[0])
+    s0 = np.concatenate([gk_p.T @ v_p, gk_p.sum(axis=0)[:, None]], axis=1)[None, None]
+    o, _ = oracle_mod.forward_causal_state(qx[None, None], kx[None, None], v[None, None], mu, rv, pl, eps=1e-6,
+                                           state_in=s0)
+    # brute force over [prefix; x]: queries of the prefix rows are irrelevant (take the x rows only)
+    qa = np.concatenate([rng.normal(0, 1, (P, dr)), qx])
+    ka, va = np.concatenate([kx_p, kx]), np.concatenate([v_p, v])
+    gq, gk = scipy_gamma(qa, mu[0], rv[0], pl[0]), scipy_gamma(ka, mu[0], rv[0], pl[0])
+    np.testing.assert_allclose(o[0, 0], brute_force(gq, gk, va, 1e-6, True)[P:], rtol=1e-9, atol=1e-11)
