@@ -12,6 +12,7 @@ GMA_DTYPE_BF16 = 1
 GMA_OP_RESPONSIBILITIES = 0
 GMA_OP_FORWARD_BIDIR = 1
 GMA_OP_FORWARD_CAUSAL = 2
+GMA_OP_FORWARD_CAUSAL_STATE = 3
 STATUS = {0: "GMA_SUCCESS", 1: "GMA_ERROR_INVALID_VALUE", 2: "GMA_ERROR_NOT_SUPPORTED",
           3: "GMA_ERROR_WORKSPACE_TOO_SMALL", 4: "GMA_ERROR_LAUNCH"}
 
@@ -38,6 +39,8 @@ _SIGS = [
     ("gma_responsibilities", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     ("gma_forward_bidir", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     ("gma_forward_causal", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    ("gma_forward_causal_state", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                ctypes.c_size_t, _VP]),
     ("gma_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("gma_last_error", ctypes.c_char_p, []),
     ("gma_timing_enable", ctypes.c_int, [ctypes.c_int]),

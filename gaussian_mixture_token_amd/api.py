@@ -85,7 +85,7 @@ def responsibilities(x: torch.Tensor, mu: torch.Tensor, raw_var: torch.Tensor, p
     return out
 
 
-def _forward(fn_name: str, op: int, qx, kx, v, mu, raw_var, prior_logits, eps, out, workspace):
+def _forward(fn_name: str, op: int, qx, kx, v, mu, raw_var, prior_logits, eps, out, workspace, states=None):
     B, H, N, d_r = qx.shape
     d_v = v.shape[-1]
     K = mu.shape[1]
@@ -101,8 +101,16 @@ def _forward(fn_name: str, op: int, qx, kx, v, mu, raw_var, prior_logits, eps, o
     _check_gpu(out)
     ws = _workspace(workspace_size(prob, op), dev, workspace)
     fn = getattr(_lib.load(), fn_name)
+    extra = []
+    if states is not None:
+        for name, t in zip(("state_in", "state_out"), states):
+            if t is not None:
+                if t.dtype != torch.float32 or tuple(t.shape) != (B, H, K, d_v + 1) or not t.is_contiguous():
+                    raise ValueError("%s must be a contiguous float32 [B, H, K, d_v + 1] tensor" % name)
+                _check_gpu(t)
+        extra = [_ptr(t) if t is not None else None for t in states]
     _lib.check(fn(ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu), _ptr(raw_var), _ptr(prior_logits),
-                  _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
+                  *extra, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
     return out
 
 
@@ -112,10 +120,18 @@ def forward_bidir(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=N
                     out, workspace)
 
 
-def forward_causal(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=None, workspace=None):
-    """Causal O (prefix sums of Gamma_K^T V and Gamma_K^T 1, inclusive of the current token)."""
-    return _forward("gma_forward_causal", _lib.GMA_OP_FORWARD_CAUSAL, qx, kx, v, mu, raw_var, prior_logits, eps,
-                    out, workspace)
+def forward_causal(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=None, workspace=None,
+                   state_in=None, state_out=None):
+    """Causal O (prefix sums of Gamma_K^T V and Gamma_K^T 1, inclusive of the current token).
+
+    With state_in and/or state_out (float32 [B, H, K, d_v + 1]: row k holds Vt[k, :] then Z[k]) the
+    latent memory is carried across calls: state_in is the memory after all earlier tokens (None =
+    zero), state_out receives it after this call's last token (it may be state_in itself)."""
+    if state_in is None and state_out is None:
+        return _forward("gma_forward_causal", _lib.GMA_OP_FORWARD_CAUSAL, qx, kx, v, mu, raw_var, prior_logits, eps,
+                        out, workspace)
+    return _forward("gma_forward_causal_state", _lib.GMA_OP_FORWARD_CAUSAL_STATE, qx, kx, v, mu, raw_var,
+                    prior_logits, eps, out, workspace, states=(state_in, state_out))
 
 
 def forward(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, causal: bool = False, out=None, workspace=None):

@@ -43,9 +43,9 @@ int next_pow2(int x) {
     return p;
 }
 
-enum KernelId { K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_COUNT };
+enum KernelId { K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_COUNT };
 const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan",
-                                     "causal_output", "bidir_output", "responsibilities"};
+                                     "causal_output", "bidir_output", "responsibilities", "state_convert"};
 
 struct Plan {
     const ShapeClass* cls = nullptr;
@@ -58,7 +58,7 @@ struct Plan {
     int seg_chunks = 1;
     bool dma = false;
     bool gtiles = false;   // causal token-split pair through stored Gamma_K tiles
-    size_t off_ab = 0, off_c = 0, off_seg = 0, off_gk = 0, total = 0;
+    size_t off_ab = 0, off_c = 0, off_seg = 0, off_gk = 0, off_state = 0, total = 0;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -77,7 +77,7 @@ const ShapeClass* find_class(bool f32, int kc, int vc, int drc) {
 // stored Gamma_K tiles where it applies).  No HIP call.
 gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = false, bool tiles = true) {
     if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
-    if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_FORWARD_CAUSAL)
+    if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_FORWARD_CAUSAL_STATE)
         return fail(GMA_ERROR_INVALID_VALUE, "unknown op %d", op);
     if (p->batch < 1 || p->heads < 1 || p->seq_len < 1)
         return fail(GMA_ERROR_INVALID_VALUE, "batch, heads and seq_len must be >= 1 (got %lld, %lld, %lld)",
@@ -144,24 +144,29 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     // 3.74 ms), so it is taken up to K = 4 d_r, while the tiles of one (batch, head) stay within
     // 32-bit byte offsets.
     const int64_t tile_bytes = (int64_t)C * plan->cls->kc * 2;
-    plan->gtiles = tiles && tok && op == GMA_OP_FORWARD_CAUSAL && plan->cls->tok_out_causal_g &&
+    const bool causal = op == GMA_OP_FORWARD_CAUSAL || op == GMA_OP_FORWARD_CAUSAL_STATE;
+    plan->gtiles = tiles && tok && causal && plan->cls->tok_out_causal_g &&
                    plan->cls->kc <= 4 * plan->cls->drc && plan->n_chunks * tile_bytes < (int64_t(1) << 31);
 
-    // workspace: [a | b] fragments, c, segment records, Gamma_K tiles
+    // workspace: [a | b] fragments, c, segment records, Gamma_K tiles, (carried state) the
+    // initial and the final state as records
     const int ks = plan->f32 ? 16 : 32;
     const int nks = 2 * plan->cls->drc / ks;
     const size_t ab_bytes = (size_t)plan->H * (plan->cls->kc / 16) * nks * 64 * 16;
     const size_t c_bytes = (size_t)plan->H * plan->cls->kc * sizeof(float);
+    const size_t rec_bytes = ((size_t)plan->cls->kc * plan->cls->vc + plan->cls->kc) * sizeof(float);
+    const bool stateful = op == GMA_OP_FORWARD_CAUSAL_STATE;
     size_t seg_bytes = 0;
-    const bool need_seg = (op == GMA_OP_FORWARD_BIDIR) || (op == GMA_OP_FORWARD_CAUSAL && (plan->P > 1 || plan->gtiles));
-    if (need_seg)
-        seg_bytes = (size_t)BH * plan->P * ((size_t)plan->cls->kc * plan->cls->vc + plan->cls->kc) * sizeof(float);
+    const bool need_seg = (op == GMA_OP_FORWARD_BIDIR) || (causal && (plan->P > 1 || plan->gtiles || stateful));
+    if (need_seg) seg_bytes = (size_t)BH * plan->P * rec_bytes;
     const size_t gk_bytes = plan->gtiles ? (size_t)BH * plan->n_chunks * tile_bytes : 0;
+    const size_t state_bytes = stateful ? 2 * (size_t)BH * rec_bytes : 0;
     plan->off_ab = 0;
     plan->off_c = align_up(ab_bytes, 256);
     plan->off_seg = align_up(plan->off_c + c_bytes, 256);
     plan->off_gk = align_up(plan->off_seg + seg_bytes, 256);
-    plan->total = align_up(plan->off_gk + gk_bytes, 256);
+    plan->off_state = align_up(plan->off_gk + gk_bytes, 256);
+    plan->total = align_up(plan->off_state + state_bytes, 256);
     return GMA_SUCCESS;
 }
 
@@ -230,27 +235,63 @@ gma_status_t timed_launch(int kid, hipStream_t s, F&& launch) {
 
 // ---------------------------------------------------------------------------------- launches
 // scan over the P segment aggregates of each (batch, head), fixed order (deterministic).
-// causal: seg[bh][s] <- sum_{t < s} seg[bh][t] (exclusive prefix, in place)
+// causal: seg[bh][s] <- init[bh] + sum_{t < s} seg[bh][t] (exclusive prefix, in place; init = 0 if
+//         NULL); n_agg = aggregates present (P, or P - 1 when the last one was not computed);
+//         total[bh] <- init[bh] + sum of all P aggregates (only when n_agg = P and total != NULL)
 // bidir : seg[bh][0] <- sum_{t < P} seg[bh][t]
-__global__ void __launch_bounds__(256) scan_kernel(float* seg, int P, int64_t rec, int causal) {
+__global__ void __launch_bounds__(256) scan_kernel(float* seg, int P, int64_t rec, int causal, int n_agg,
+                                                   const float* init, float* total) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= rec) return;
     float* base = seg + (int64_t)blockIdx.y * P * rec + e;
-    // the last segment's causal aggregate is never produced (nothing follows it)
-    const int n = causal ? P - 1 : P;
-    float run = 0.f;
+    const int n = causal ? n_agg : P;
+    float run = (causal && init) ? init[(int64_t)blockIdx.y * rec + e] : 0.f;
     // groups of 16 independent loads, then the sequential sum over the group
-    for (int s0 = 0; s0 < n; s0 += 16) {
+    for (int s0 = 0; s0 < P; s0 += 16) {
         float x[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) x[j] = (s0 + j < n) ? base[(int64_t)(s0 + j) * rec] : 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            if (causal && s0 + j < n) base[(int64_t)(s0 + j) * rec] = run;
+            if (causal && s0 + j < P) base[(int64_t)(s0 + j) * rec] = run;
             run += x[j];
         }
     }
-    base[causal ? (int64_t)(P - 1) * rec : 0] = run;
+    if (!causal) base[0] = run;
+    else if (total && n_agg == P) total[(int64_t)blockIdx.y * rec + e] = run;
+}
+
+// Carried state [B*H, K, d_v + 1] (row k: Vt[k, 0 .. d_v-1], then Z[k]) <-> state record in the
+// kernels' accumulator-fragment order: element (component c, column j) of Vt at
+// ((c/16 * VC/16 + j/16) * 64 + (c%16)/4 * 16 + j%16) * 4 + c%4, then Z[c] at KC*VC + c.
+// Padding components and columns are zero in a record.
+__global__ void __launch_bounds__(256) state_to_record(const float* state, float* recs, int K, int dv, int KC,
+                                                       int VC, int64_t rec) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= rec) return;
+    const float* sb = state + (int64_t)blockIdx.y * K * (dv + 1);
+    int c, j;
+    if (e < (int64_t)KC * VC) {
+        const int i = (int)(e & 3), lane = (int)((e >> 2) & 63), t = (int)(e >> 8);
+        const int ct = t / (VC / 16), vt = t % (VC / 16);
+        c = ct * 16 + (lane >> 4) * 4 + i;
+        j = vt * 16 + (lane & 15);
+    } else {
+        c = (int)(e - (int64_t)KC * VC);
+        j = dv;
+    }
+    const bool in = (e < (int64_t)KC * VC) ? (c < K && j < dv) : (c < K);
+    recs[(int64_t)blockIdx.y * rec + e] = in ? sb[(int64_t)c * (dv + 1) + j] : 0.f;
+}
+
+__global__ void __launch_bounds__(256) record_to_state(const float* recs, float* state, int K, int dv, int KC,
+                                                       int VC, int64_t rec) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;   // element (c, j) of the state
+    if (e >= (int64_t)K * (dv + 1)) return;
+    const int c = (int)(e / (dv + 1)), j = (int)(e % (dv + 1));
+    const int64_t r = (j < dv) ? (((int64_t)(c / 16) * (VC / 16) + j / 16) * 64 + (c % 16) / 4 * 16 + j % 16) * 4 + c % 4
+                               : (int64_t)KC * VC + c;
+    state[(int64_t)blockIdx.y * K * (dv + 1) + e] = recs[(int64_t)blockIdx.y * rec + r];
 }
 
 gma_status_t launch_prep(const Plan& pl, const float* mu, const float* rv, const float* pr, char* ws, hipStream_t s) {
@@ -308,12 +349,16 @@ gma_status_t check_common(const gma_problem_t* p, const void* const* ptrs, int n
     return GMA_SUCCESS;
 }
 
-gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const void* kx, const void* v,
-                     const float* mu, const float* rv, const float* pr, void* o, void* ws, size_t ws_bytes,
-                     void* stream) {
+// op: GMA_OP_FORWARD_BIDIR, GMA_OP_FORWARD_CAUSAL or GMA_OP_FORWARD_CAUSAL_STATE (state_in /
+// state_out used only by the last; either may be NULL)
+gma_status_t forward(const gma_problem_t* p, int op, const void* qx, const void* kx, const void* v,
+                     const float* mu, const float* rv, const float* pr, const float* state_in, float* state_out,
+                     void* o, void* ws, size_t ws_bytes, void* stream) {
     g_last_error.clear();
+    const bool causal = op != GMA_OP_FORWARD_BIDIR;
+    const bool stateful = op == GMA_OP_FORWARD_CAUSAL_STATE;
     Plan pl;
-    gma_status_t st = make_plan(p, causal ? GMA_OP_FORWARD_CAUSAL : GMA_OP_FORWARD_BIDIR, &pl);
+    gma_status_t st = make_plan(p, op, &pl);
     if (st != GMA_SUCCESS) return st;
     const void* ptrs[] = {qx, kx, v, mu, rv, pr, o};
     st = check_common(p, ptrs, 7, ws, ws_bytes, pl, false);
@@ -327,6 +372,18 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
     const size_t nv = (size_t)(pl.B * pl.H * pl.N) * pl.d_v * es;
     if (overlaps(o, nv, qx, nx) || overlaps(o, nv, kx, nx) || overlaps(o, nv, v, nv))
         return fail(GMA_ERROR_INVALID_VALUE, "o must not overlap qx, kx or v");
+    const size_t ns = (size_t)(pl.B * pl.H) * pl.K * (pl.d_v + 1) * sizeof(float);
+    if (stateful) {
+        if (misaligned(state_in, 4) || misaligned(state_out, 4))
+            return fail(GMA_ERROR_INVALID_VALUE, "state pointers must be 4-byte aligned");
+        for (const void* sp : {(const void*)state_in, (const void*)state_out}) {
+            if (sp && (overlaps(sp, ns, qx, nx) || overlaps(sp, ns, kx, nx) || overlaps(sp, ns, v, nv) ||
+                       overlaps(sp, ns, o, nv)))
+                return fail(GMA_ERROR_INVALID_VALUE, "states must not overlap qx, kx, v or o");
+        }
+        if (state_in && state_out && state_in != state_out && overlaps(state_in, ns, state_out, ns))
+            return fail(GMA_ERROR_INVALID_VALUE, "state_in and state_out must be the same buffer or disjoint");
+    }
 
     // Token-split LDS-DMA kernels: bf16, rows in whole 16-byte chunks, 16-byte aligned bases, byte
     // offsets within one (batch, head) slice (one chunk past the end included) below 2^31.
@@ -334,12 +391,12 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
                      !misaligned(qx, 16) && !misaligned(kx, 16) && !misaligned(v, 16) && !misaligned(o, 16) &&
                      (pl.N + kTokChunk) * std::max(pl.d_r, pl.d_v) * 2 < (int64_t(1) << 31);
     if (dma) {
-        st = make_plan(p, causal ? GMA_OP_FORWARD_CAUSAL : GMA_OP_FORWARD_BIDIR, &pl, true);
+        st = make_plan(p, op, &pl, true);
         if (st != GMA_SUCCESS) return st;
-        if (pl.gtiles && ws_bytes < advertised_workspace(p, GMA_OP_FORWARD_CAUSAL)) {
+        if (pl.gtiles && ws_bytes < advertised_workspace(p, op)) {
             // less than the advertised workspace: no stored Gamma_K tiles, the causal output pass
             // recomputes Gamma_K
-            st = make_plan(p, GMA_OP_FORWARD_CAUSAL, &pl, true, false);
+            st = make_plan(p, op, &pl, true, false);
             if (st != GMA_SUCCESS) return st;
         }
     }
@@ -348,7 +405,8 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
         return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
                     ws_bytes, pl.total);
     if (ws && (overlaps(ws, pl.total, qx, nx) || overlaps(ws, pl.total, kx, nx) || overlaps(ws, pl.total, v, nv) ||
-               overlaps(ws, pl.total, o, nv)))
+               overlaps(ws, pl.total, o, nv) || (stateful && (overlaps(ws, pl.total, state_in, state_in ? ns : 0) ||
+                                                              overlaps(ws, pl.total, state_out, state_out ? ns : 0)))))
         return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -369,28 +427,43 @@ gma_status_t forward(const gma_problem_t* p, int causal, const void* qx, const v
     const main_launch_t f_bidir = dma ? pl.cls->tok_out_bidir : pl.cls->out_bidir;
     const int grid = (int)(pl.B * pl.H * pl.P);
     const int64_t rec = (int64_t)pl.cls->kc * pl.cls->vc + pl.cls->kc;
-    const bool need_agg = !causal || pl.P > 1 || gt;
-    if (need_agg) {
-        // causal: the last segment's aggregate is not needed by anyone, but with stored tiles its
-        // Gamma_K tiles are
+    const unsigned BH = (unsigned)(pl.B * pl.H);
+    // carried state: the initial and the final state as records in the workspace
+    float* rec_in = (stateful && state_in) ? reinterpret_cast<float*>(w + pl.off_state) : nullptr;
+    float* rec_out = (stateful && state_out) ? reinterpret_cast<float*>(w + pl.off_state) + BH * rec : nullptr;
+    if (rec_in) {
+        st = timed_launch(K_STATE, s, [&] {
+            hipLaunchKernelGGL(state_to_record, dim3((unsigned)((rec + 255) / 256), BH), dim3(256), 0, s, state_in,
+                               rec_in, pl.K, pl.d_v, pl.cls->kc, pl.cls->vc, rec);
+        });
+        if (st != GMA_SUCCESS) return st;
+    }
+    // causal: the last segment's aggregate is needed only for the final state, but with stored tiles
+    // its Gamma_K tiles are
+    const int n_agg = (!causal || gt || rec_out) ? (int)pl.P : (int)pl.P - 1;
+    if (n_agg > 0) {
         MainArgs ag = a;
-        ag.Pg = (causal && !gt) ? pl.P - 1 : pl.P;
+        ag.Pg = n_agg;
         const int agrid = (int)(pl.B * pl.H * ag.Pg);
         st = timed_launch(K_AGG, s, [&] { f_agg(ag, agrid, s); });
         if (st != GMA_SUCCESS) return st;
-        if (pl.P > 1) {
-            st = timed_launch(K_SCAN, s, [&] {
-                hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), (unsigned)(pl.B * pl.H)), dim3(256),
-                                   0, s, a.seg, pl.P, rec, causal);
-            });
-            if (st != GMA_SUCCESS) return st;
-        }
     }
-    if (causal) {
-        a.has_carry = pl.P > 1;
-        return timed_launch(K_OUT_CAUSAL, s, [&] { f_causal(a, grid, s); });
+    if (pl.P > 1 || rec_in || rec_out) {
+        st = timed_launch(K_SCAN, s, [&] {
+            hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), BH), dim3(256), 0, s, a.seg, pl.P, rec,
+                               causal ? 1 : 0, n_agg, (const float*)rec_in, rec_out);
+        });
+        if (st != GMA_SUCCESS) return st;
     }
-    return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, grid, s); });
+    if (!causal) return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, grid, s); });
+    a.has_carry = pl.P > 1 || rec_in;
+    st = timed_launch(K_OUT_CAUSAL, s, [&] { f_causal(a, grid, s); });
+    if (st != GMA_SUCCESS || !rec_out) return st;
+    const int64_t nstate = (int64_t)pl.K * (pl.d_v + 1);
+    return timed_launch(K_STATE, s, [&] {
+        hipLaunchKernelGGL(record_to_state, dim3((unsigned)((nstate + 255) / 256), BH), dim3(256), 0, s,
+                           (const float*)rec_out, state_out, pl.K, pl.d_v, pl.cls->kc, pl.cls->vc, rec);
+    });
 }
 
 }  // namespace
@@ -442,13 +515,23 @@ gma_status_t gma_responsibilities(const gma_problem_t* p, const void* x, const f
 gma_status_t gma_forward_bidir(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,
                                const float* raw_var, const float* prior_logits, void* o, void* ws, size_t ws_bytes,
                                void* stream) {
-    return forward(p, 0, qx, kx, v, mu, raw_var, prior_logits, o, ws, ws_bytes, stream);
+    return forward(p, GMA_OP_FORWARD_BIDIR, qx, kx, v, mu, raw_var, prior_logits, nullptr, nullptr, o, ws, ws_bytes,
+                   stream);
 }
 
 gma_status_t gma_forward_causal(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,
                                 const float* raw_var, const float* prior_logits, void* o, void* ws, size_t ws_bytes,
                                 void* stream) {
-    return forward(p, 1, qx, kx, v, mu, raw_var, prior_logits, o, ws, ws_bytes, stream);
+    return forward(p, GMA_OP_FORWARD_CAUSAL, qx, kx, v, mu, raw_var, prior_logits, nullptr, nullptr, o, ws, ws_bytes,
+                   stream);
+}
+
+gma_status_t gma_forward_causal_state(const gma_problem_t* p, const void* qx, const void* kx, const void* v,
+                                      const float* mu, const float* raw_var, const float* prior_logits,
+                                      const float* state_in, float* state_out, void* o, void* ws, size_t ws_bytes,
+                                      void* stream) {
+    return forward(p, GMA_OP_FORWARD_CAUSAL_STATE, qx, kx, v, mu, raw_var, prior_logits, state_in, state_out, o, ws,
+                   ws_bytes, stream);
 }
 
 const char* gma_status_string(gma_status_t s) {

@@ -63,7 +63,8 @@ typedef enum {
 typedef enum {
     GMA_OP_RESPONSIBILITIES = 0,
     GMA_OP_FORWARD_BIDIR = 1,
-    GMA_OP_FORWARD_CAUSAL = 2
+    GMA_OP_FORWARD_CAUSAL = 2,
+    GMA_OP_FORWARD_CAUSAL_STATE = 3
 } gma_op_t;
 
 /* Problem sizes.  eps >= 0 and finite; it is added to each row's denominator Gamma_Q Z. */
@@ -106,6 +107,24 @@ gma_status_t gma_forward_causal(const gma_problem_t* problem, const void* qx, co
                                 const void* v, const float* mu, const float* raw_var,
                                 const float* prior_logits, void* o, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* Causal forward with the latent memory carried across calls (item 3: the causal output is a
+ * prefix sum, so everything before this call's first token enters only through [Vt | Z]).  Lets a
+ * sequence be processed in consecutive pieces (streaming, or one-token decode steps) with results
+ * identical, up to rounding order, to one call over the whole sequence.
+ *   state_in   [B, H, K, d_v + 1] fp32 or NULL (zero): row k of (b, h) holds Vt[k, 0 .. d_v-1] and
+ *              then Z[k], the memory after all earlier tokens.
+ *   state_out  [B, H, K, d_v + 1] fp32 or NULL: receives the memory after this call's last token
+ *              (state_in plus this call's Gamma_K^T [V | 1]).
+ * state_in and state_out may be the same buffer (updated in place); otherwise they must be
+ * disjoint, and neither may overlap qx, kx, v, o or the workspace.  4-byte aligned.  Other
+ * arguments as gma_forward_causal; workspace: gma_workspace_size(problem,
+ * GMA_OP_FORWARD_CAUSAL_STATE) bytes. */
+gma_status_t gma_forward_causal_state(const gma_problem_t* problem, const void* qx, const void* kx,
+                                      const void* v, const float* mu, const float* raw_var,
+                                      const float* prior_logits, const float* state_in,
+                                      float* state_out, void* o, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* gma_status_string(gma_status_t status);

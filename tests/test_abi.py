@@ -159,3 +159,29 @@ def test_causal_tiles_cover_the_padded_sequence(lib):
     b = _ws(lib, 1, seq_len=n)
     tiles = 16 * 1001 * 64 * 128 * 2
     assert tiles <= c <= b + tiles + 4096
+
+
+def _fwd_state(lib, prob, state_in, state_out, ws_bytes=1 << 40, **override):
+    args = dict(qx=FAKE, kx=ctypes.c_void_p(0x20000000), v=ctypes.c_void_p(0x40000000), mu=FAKE, rv=FAKE, pl=FAKE,
+                o=ctypes.c_void_p(0x80000000000), ws=ctypes.c_void_p(0x100000000000))
+    args.update(override)
+    return lib.gma_forward_causal_state(ctypes.byref(prob), args["qx"], args["kx"], args["v"], args["mu"], args["rv"],
+                                        args["pl"], state_in, state_out, args["o"], args["ws"], ws_bytes, None)
+
+
+def test_causal_state_validation(lib):
+    prob = _prob()
+    ns = 16 * 128 * 129 * 4
+    s1, s2 = 0x200000000000, 0x300000000000
+    # misaligned state pointers
+    assert _fwd_state(lib, prob, ctypes.c_void_p(s1 + 2), None) == 1
+    assert _fwd_state(lib, prob, None, ctypes.c_void_p(s2 + 1)) == 1
+    # partial overlap of state_in and state_out (identical buffers are allowed: in-place update)
+    assert _fwd_state(lib, prob, ctypes.c_void_p(s1), ctypes.c_void_p(s1 + ns // 2)) == 1
+    # a state overlapping o or the workspace
+    assert _fwd_state(lib, prob, ctypes.c_void_p(0x80000000000 + 64), None) == 1
+    assert _fwd_state(lib, prob, None, ctypes.c_void_p(0x100000000000 + 256)) == 1
+    # workspace too small for every path
+    assert _fwd_state(lib, prob, ctypes.c_void_p(s1), ctypes.c_void_p(s1), ws_bytes=4096) == 3
+    # the stateful op needs at least the causal workspace
+    assert lib.gma_workspace_size(ctypes.byref(prob), 3) >= lib.gma_workspace_size(ctypes.byref(prob), 2)

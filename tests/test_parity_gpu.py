@@ -185,6 +185,85 @@ def test_causal_without_room_for_stored_tiles(gma, cfg, N):
     assert err <= TOL[w.dtype], err
 
 
+# ------------------------------------------------------------------------------ carried state
+
+
+def _state_tol(w):
+    return TOL[w.dtype]
+
+
+def _rel(a, b):
+    a = a.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(a) else a
+    return float(np.abs(a - b).max() / np.abs(b).max())
+
+
+@pytest.mark.parametrize("cfg,N,m", [(3, 3000, 1100), (4, 2500, 700), (2, 2000, 64), (1, 1500, 333)])
+@pytest.mark.parametrize("reduced_ws", [False, True])
+def test_causal_state_continues_a_sequence(gma, cfg, N, m, reduced_ws):
+    # the oracle runs tokens [0, m) and hands its state over; the GPU runs [m, N) from it and must
+    # give the oracle's one-pass outputs of those rows and its final state
+    w = gma.workload(cfg, batch=1, heads=2, seq_len=N)
+    say("carried state cfg %d N=%d m=%d reduced workspace %s" % (cfg, N, m, reduced_ws))
+    inp = gma.make_inputs(w)
+    o_ref, s_ref = oracle.forward_causal_state(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"],
+                                               inp["prior_logits"], eps=w.eps)
+    _, s_m = oracle.forward_causal_state(inp["qx"][:, :, :m], inp["kx"][:, :, :m], inp["v"][:, :, :m], inp["mu"],
+                                         inp["raw_var"], inp["prior_logits"], eps=w.eps)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    tail = {k: t[k][:, :, m:].contiguous() for k in ("qx", "kx", "v")}
+    s_in = torch.from_numpy(s_m).float().to(DEV)
+    s_out = torch.empty_like(s_in)
+    kw = {}
+    if reduced_ws:
+        if w.dtype != "bf16":
+            pytest.skip("the recompute path exists for bf16 storage only")
+        prob = gma.problem(1, 2, N - m, w.d_route, w.n_comp, w.d_value, w.torch_dtype, w.eps)
+        kw["workspace"] = torch.empty(gma.workspace_size(prob, 3) - 1, dtype=torch.uint8, device=DEV)
+    o = gma.forward_causal(tail["qx"], tail["kx"], tail["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps,
+                           state_in=s_in, state_out=s_out, **kw)
+    torch.cuda.synchronize()
+    err_o = _rel(o, o_ref[:, :, m:])
+    err_s = _rel(s_out, s_ref)
+    say("  O err %.2e, state err %.2e" % (err_o, err_s))
+    assert err_o <= TOL[w.dtype], err_o
+    assert err_s <= _state_tol(w), err_s
+
+
+def test_causal_state_split_on_gpu_and_decode_steps(gma):
+    w = gma.workload(3, batch=1, heads=2, seq_len=2024)
+    inp = gma.make_inputs(w)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    q, k, v = t["qx"], t["kx"], t["v"]
+    o_ref, s_ref = oracle.forward_causal_state(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"],
+                                               inp["prior_logits"], eps=w.eps)
+    st = torch.zeros(1, 2, w.n_comp, w.d_value + 1, dtype=torch.float32, device=DEV)
+    outs = []
+    # a long first piece, then 24 one-token decode steps updating the state in place
+    cuts = [0, 2000] + list(range(2001, 2025))
+    for a_, b_ in zip(cuts[:-1], cuts[1:]):
+        outs.append(gma.forward_causal(q[:, :, a_:b_].contiguous(), k[:, :, a_:b_].contiguous(),
+                                       v[:, :, a_:b_].contiguous(), t["mu"], t["raw_var"], t["prior_logits"],
+                                       eps=w.eps, state_in=st, state_out=st))
+    torch.cuda.synchronize()
+    o = torch.cat(outs, dim=2)
+    err_o, err_s = _rel(o, o_ref), _rel(st, s_ref)
+    say("split + decode: O err %.2e, state err %.2e" % (err_o, err_s))
+    assert err_o <= TOL[w.dtype], err_o
+    assert err_s <= TOL[w.dtype], err_s
+
+
+def test_causal_state_without_state_equals_plain_causal(gma):
+    w = gma.workload(3, batch=1, heads=2, seq_len=3000)
+    inp = gma.make_inputs(w)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    a = gma.forward_causal(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps)
+    s = torch.empty(1, 2, w.n_comp, w.d_value + 1, dtype=torch.float32, device=DEV)
+    b = gma.forward_causal(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps,
+                           state_out=s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bitwise_deterministic(gma, causal):
     w = gma.workload(3, seq_len=20000)
