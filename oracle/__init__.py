@@ -29,7 +29,7 @@ _LIB = os.path.join(_HERE, "libgma_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-__all__ = ["build", "params", "responsibilities", "forward", "forward_causal_state", "set_threads", "max_threads"]
+__all__ = ["build", "params", "responsibilities", "forward", "forward_causal_state", "forward_bidir_kv", "set_threads", "max_threads"]
 
 
 def build(force: bool = True) -> str:
@@ -62,6 +62,9 @@ def _load():
             lib.gma_oracle_forward_causal_state.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.c_double,
                                                             dp, dp, dp, dp, dp, dp, dp, dp, dp]
             lib.gma_oracle_forward_causal_state.restype = ctypes.c_int
+            lib.gma_oracle_forward_bidir_kv.argtypes = [i64, i64, i64, i64, i32, i32, i32, ctypes.c_double,
+                                                        dp, dp, dp, dp, dp, dp, dp]
+            lib.gma_oracle_forward_bidir_kv.restype = ctypes.c_int
             lib.gma_oracle_set_threads.argtypes = [ctypes.c_int]
             lib.gma_oracle_set_threads.restype = None
             lib.gma_oracle_max_threads.argtypes = []
@@ -171,3 +174,26 @@ def forward_causal_state(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6
     if rc != 0:
         raise MemoryError("oracle: allocation failed")
     return o, sout
+
+
+def forward_bidir_kv(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6,
+                     threads: Optional[int] = None) -> np.ndarray:
+    """Bidirectional O [B, H, Nq, d_v] with queries qx [B, H, Nq, d_r] and keys / values kx
+    [B, H, Nk, d_r], v [B, H, Nk, d_v] (cross-attention)."""
+    qx, kx, v = _f64(qx), _f64(kx), _f64(v)
+    mu, rv, pl = _f64(mu), _f64(raw_var), _f64(prior_logits)
+    B, H, Nq, dr = qx.shape
+    Nk = kx.shape[2]
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    assert kx.shape == (B, H, Nk, dr) and v.shape == (B, H, Nk, dv)
+    assert mu.shape == (H, K, dr) and rv.shape == (H, K, dr) and pl.shape == (H, K)
+    o = np.empty((B, H, Nq, dv), dtype=np.float64)
+    lib = _load()
+    if threads is not None:
+        lib.gma_oracle_set_threads(int(threads))
+    rc = lib.gma_oracle_forward_bidir_kv(B, H, Nq, Nk, dr, K, dv, float(eps), _ptr(qx), _ptr(kx), _ptr(v),
+                                         _ptr(mu), _ptr(rv), _ptr(pl), _ptr(o))
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return o

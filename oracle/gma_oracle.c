@@ -269,6 +269,74 @@ int gma_oracle_forward(int causal, int64_t B, int64_t H, int64_t N, int32_t dr, 
     return forward_impl(causal, B, H, N, dr, K, dv, eps, qx, kx, v, mu, raw_var, prior_logits, NULL, NULL, o);
 }
 
+/* Bidirectional forward with separate query and key/value sequences (cross-attention): the write
+ * phase runs over the Nk rows of kx [B, H, Nk, d_r] and v [B, H, Nk, d_v], the read phase over the
+ * Nq rows of qx [B, H, Nq, d_r]; o [B, H, Nq, d_v].  The same definitions as the bidirectional
+ * forward above; one GMM per head routes both sides.  Returns 0, or 1 if memory could not be
+ * allocated. */
+int gma_oracle_forward_bidir_kv(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int32_t dr, int32_t K,
+                                int32_t dv, double eps, const double* qx, const double* kx,
+                                const double* v, const double* mu, const double* raw_var,
+                                const double* prior_logits, double* o) {
+    double* var = (double*)malloc(sizeof(double) * H * K * dr);
+    double* logp = (double*)malloc(sizeof(double) * H * K);
+    double* logdet = (double*)malloc(sizeof(double) * H * K);
+    double* g = (double*)malloc(sizeof(double) * ORACLE_ROW_BLOCK * K);
+    double* vt = (double*)malloc(sizeof(double) * (int64_t)K * dv);
+    double* z = (double*)malloc(sizeof(double) * K);
+    int rc = 0;
+    if (!var || !logp || !logdet || !g || !vt || !z) { rc = 1; goto done; }
+    gma_oracle_params(H, K, dr, raw_var, prior_logits, var, logp);
+    for (int64_t h = 0; h < H; ++h) head_logdet(K, dr, var + h * K * dr, logdet + h * K);
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const int64_t h = bh % H;
+        const double* mu_h = mu + h * K * dr;
+        const double* var_h = var + h * K * dr;
+        const double* lp_h = logp + h * K;
+        const double* ld_h = logdet + h * K;
+        const double* q_bh = qx + bh * Nq * dr;
+        const double* k_bh = kx + bh * Nk * dr;
+        const double* v_bh = v + bh * Nk * dv;
+        double* o_bh = o + bh * Nq * dv;
+        memset(vt, 0, sizeof(double) * (size_t)K * dv);
+        memset(z, 0, sizeof(double) * (size_t)K);
+        /* write phase over the key/value rows: Vt = Gamma_K^T V, Z = Gamma_K^T 1 */
+        for (int64_t n0 = 0; n0 < Nk; n0 += ORACLE_ROW_BLOCK) {
+            int64_t nb = (Nk - n0 < ORACLE_ROW_BLOCK) ? Nk - n0 : ORACLE_ROW_BLOCK;
+#pragma omp parallel for schedule(static)
+            for (int64_t r = 0; r < nb; ++r)
+                row_responsibilities(K, dr, k_bh + (n0 + r) * dr, mu_h, var_h, lp_h, ld_h, g + r * K);
+            for (int64_t r = 0; r < nb; ++r)
+                for (int k = 0; k < K; ++k) z[k] += g[r * K + k];
+#pragma omp parallel for schedule(static)
+            for (int c = 0; c < dv; ++c)
+                for (int64_t r = 0; r < nb; ++r)
+                    for (int k = 0; k < K; ++k)
+                        vt[(int64_t)k * dv + c] += g[r * K + k] * v_bh[(n0 + r) * dv + c];
+        }
+        /* read phase over the query rows: O_n = (Gamma_Q[n] Vt) / (Gamma_Q[n] . Z + eps) */
+        for (int64_t n0 = 0; n0 < Nq; n0 += ORACLE_ROW_BLOCK) {
+            int64_t nb = (Nq - n0 < ORACLE_ROW_BLOCK) ? Nq - n0 : ORACLE_ROW_BLOCK;
+#pragma omp parallel for schedule(static)
+            for (int64_t r = 0; r < nb; ++r) {
+                double* gr = g + r * K;
+                row_responsibilities(K, dr, q_bh + (n0 + r) * dr, mu_h, var_h, lp_h, ld_h, gr);
+                double d = 0.0;
+                for (int k = 0; k < K; ++k) d += gr[k] * z[k];
+                d += eps;
+                for (int c = 0; c < dv; ++c) {
+                    double num = 0.0;
+                    for (int k = 0; k < K; ++k) num += gr[k] * vt[(int64_t)k * dv + c];
+                    o_bh[(n0 + r) * dv + c] = num / d;
+                }
+            }
+        }
+    }
+done:
+    free(var); free(logp); free(logdet); free(g); free(vt); free(z);
+    return rc;
+}
+
 /* Causal forward with the latent memory carried in (state_in, NULL = zero) and out (state_out,
  * NULL = not wanted); layouts as above. */
 int gma_oracle_forward_causal_state(int64_t B, int64_t H, int64_t N, int32_t dr, int32_t K,

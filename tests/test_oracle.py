@@ -391,3 +391,43 @@ def test_state_initial_state_acts_as_a_prefix(oracle_mod):
     ka, va = np.concatenate([kx_p, kx]), np.concatenate([v_p, v])
     gq, gk = scipy_gamma(qa, mu[0], rv[0], pl[0]), scipy_gamma(ka, mu[0], rv[0], pl[0])
     np.testing.assert_allclose(o[0, 0], brute_force(gq, gk, va, 1e-6, True)[P:], rtol=1e-9, atol=1e-11)
+
+
+# ----------------------------------------------------------------------------- cross-attention
+# Bidirectional form with separate query and key/value sequences (N_q != N_k); the pages name it
+# as future work; the definitions of the write and read phases are unchanged.
+
+
+def test_cross_equal_lengths_is_bidirectional(oracle_mod):
+    rng = np.random.default_rng(31)
+    B, H, N, dr, K, dv = 2, 2, 150, 4, 5, 3
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    qx, kx, v = rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dr)), rng.normal(0, 1, (B, H, N, dv))
+    np.testing.assert_array_equal(oracle_mod.forward_bidir_kv(qx, kx, v, mu, rv, pl),
+                                  oracle_mod.forward(qx, kx, v, mu, rv, pl, causal=False))
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 200), (37, 5), (120, 80)])
+def test_cross_matches_rectangular_brute_force(oracle_mod, Nq, Nk):
+    # A = Gamma_Q Gamma_K^T is N_q x N_k; O = A V / (A 1 + eps), posteriors from SciPy
+    rng = np.random.default_rng(32 + Nq)
+    dr, K, dv = 3, 4, 2
+    mu, rv, pl = rand_params(rng, 1, K, dr)
+    qx, kx, v = rng.normal(0, 1, (Nq, dr)), rng.normal(0, 1, (Nk, dr)), rng.normal(0, 1, (Nk, dv))
+    o = oracle_mod.forward_bidir_kv(qx[None, None], kx[None, None], v[None, None], mu, rv, pl, eps=1e-6)
+    gq, gk = scipy_gamma(qx, mu[0], rv[0], pl[0]), scipy_gamma(kx, mu[0], rv[0], pl[0])
+    np.testing.assert_allclose(o[0, 0], brute_force(gq, gk, v, 1e-6, False), rtol=1e-9, atol=1e-11)
+
+
+def test_cross_key_order_and_query_subsets(oracle_mod):
+    # invariant to a joint permutation of the key/value rows; each query row depends on itself only
+    rng = np.random.default_rng(33)
+    Nq, Nk, dr, K, dv = 50, 90, 4, 6, 3
+    mu, rv, pl = rand_params(rng, 1, K, dr)
+    qx, kx, v = rng.normal(0, 1, (1, 1, Nq, dr)), rng.normal(0, 1, (1, 1, Nk, dr)), rng.normal(0, 1, (1, 1, Nk, dv))
+    o = oracle_mod.forward_bidir_kv(qx, kx, v, mu, rv, pl)
+    perm = rng.permutation(Nk)
+    np.testing.assert_allclose(oracle_mod.forward_bidir_kv(qx, kx[:, :, perm], v[:, :, perm], mu, rv, pl), o,
+                               rtol=1e-12, atol=1e-14)
+    sub = [3, 17, 49]
+    np.testing.assert_array_equal(oracle_mod.forward_bidir_kv(qx[:, :, sub], kx, v, mu, rv, pl), o[:, :, sub])
