@@ -115,9 +115,35 @@ def _forward(fn_name: str, op: int, qx, kx, v, mu, raw_var, prior_logits, eps, o
 
 
 def forward_bidir(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=None, workspace=None):
-    """O = Gamma_Q (Gamma_K^T V) / (Gamma_Q (Gamma_K^T 1) + eps); qx, kx [B, H, N, d_r], v [B, H, N, d_v]."""
+    """O = Gamma_Q (Gamma_K^T V) / (Gamma_Q (Gamma_K^T 1) + eps); qx [B, H, N_q, d_r], kx [B, H, N_kv, d_r],
+    v [B, H, N_kv, d_v] (N_kv may differ from N_q: cross-attention)."""
+    if kx.dim() == 4 and qx.dim() == 4 and kx.shape[2] != qx.shape[2]:
+        return _forward_kv(qx, kx, v, mu, raw_var, prior_logits, eps, out, workspace)
     return _forward("gma_forward_bidir", _lib.GMA_OP_FORWARD_BIDIR, qx, kx, v, mu, raw_var, prior_logits, eps,
                     out, workspace)
+
+
+def _forward_kv(qx, kx, v, mu, raw_var, prior_logits, eps, out, workspace):
+    B, H, Nq, d_r = qx.shape
+    Nk = kx.shape[2]
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    if tuple(kx.shape) != (B, H, Nk, d_r) or tuple(v.shape[:3]) != (B, H, Nk):
+        raise ValueError("qx must be [B, H, N_q, d_r], kx [B, H, N_kv, d_r] and v [B, H, N_kv, d_v]")
+    if not (qx.dtype == kx.dtype == v.dtype):
+        raise TypeError("qx, kx and v must share one dtype")
+    _params(mu, raw_var, prior_logits, H, K, d_r)
+    dev = _check_gpu(qx, kx, v, mu, raw_var, prior_logits)
+    prob = problem(B, H, Nq, d_r, K, d_v, qx.dtype, eps)
+    if out is None:
+        out = torch.empty(B, H, Nq, d_v, dtype=qx.dtype, device=dev)
+    _check_gpu(out)
+    ws = _workspace(workspace_size(problem(B, H, Nk, d_r, K, d_v, qx.dtype, eps), _lib.GMA_OP_FORWARD_BIDIR), dev,
+                    workspace)
+    _lib.check(_lib.load().gma_forward_bidir_kv(ctypes.byref(prob), Nk, _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu),
+                                                _ptr(raw_var), _ptr(prior_logits), _ptr(out), _ptr(ws),
+                                                ws.numel() * ws.element_size(), _stream(dev)))
+    return out
 
 
 def forward_causal(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=None, workspace=None,

@@ -466,6 +466,85 @@ gma_status_t forward(const gma_problem_t* p, int op, const void* qx, const void*
     });
 }
 
+// Bidirectional forward with N_q query rows (problem->seq_len) and N_kv key/value rows: the
+// aggregate pass and the workspace follow the key/value sequence, the read pass the queries (its
+// grid has its own segments; it reads the total [Vt | Z] at the key side's record stride).
+gma_status_t forward_bidir_kv(const gma_problem_t* p, int64_t n_kv, const void* qx, const void* kx, const void* v,
+                              const float* mu, const float* rv, const float* pr, void* o, void* ws, size_t ws_bytes,
+                              void* stream) {
+    g_last_error.clear();
+    if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
+    if (n_kv < 1) return fail(GMA_ERROR_INVALID_VALUE, "seq_len_kv must be >= 1 (got %lld)", (long long)n_kv);
+    gma_problem_t pk = *p;
+    pk.seq_len = n_kv;
+    Plan plq, plk;
+    gma_status_t st = make_plan(p, GMA_OP_FORWARD_BIDIR, &plq);
+    if (st != GMA_SUCCESS) return st;
+    st = make_plan(&pk, GMA_OP_FORWARD_BIDIR, &plk);
+    if (st != GMA_SUCCESS) return st;
+    const void* ptrs[] = {qx, kx, v, mu, rv, pr, o};
+    st = check_common(p, ptrs, 7, ws, ws_bytes, plk, false);
+    if (st != GMA_SUCCESS) return st;
+    const size_t es = plq.f32 ? 4 : 2;
+    for (const void* ptr : {qx, kx, v, (const void*)o})
+        if (misaligned(ptr, es)) return fail(GMA_ERROR_INVALID_VALUE, "tensor pointers must be %zu-byte aligned", es);
+    for (const void* ptr : {(const void*)mu, (const void*)rv, (const void*)pr})
+        if (misaligned(ptr, 4)) return fail(GMA_ERROR_INVALID_VALUE, "parameter pointers must be 4-byte aligned");
+    const int64_t BH = plq.B * plq.H;
+    const size_t nq = (size_t)(BH * plq.N) * plq.d_r * es, nk = (size_t)(BH * n_kv) * plq.d_r * es;
+    const size_t nv = (size_t)(BH * n_kv) * plq.d_v * es, no = (size_t)(BH * plq.N) * plq.d_v * es;
+    if (overlaps(o, no, qx, nq) || overlaps(o, no, kx, nk) || overlaps(o, no, v, nv))
+        return fail(GMA_ERROR_INVALID_VALUE, "o must not overlap qx, kx or v");
+    const bool dma = !plq.f32 && plq.cls->tok_out_causal && plq.d_r % 8 == 0 && plq.d_v % 8 == 0 &&
+                     !misaligned(qx, 16) && !misaligned(kx, 16) && !misaligned(v, 16) && !misaligned(o, 16) &&
+                     (std::max(plq.N, n_kv) + kTokChunk) * std::max(plq.d_r, plq.d_v) * 2 < (int64_t(1) << 31);
+    if (dma) {
+        st = make_plan(p, GMA_OP_FORWARD_BIDIR, &plq, true);
+        if (st != GMA_SUCCESS) return st;
+        st = make_plan(&pk, GMA_OP_FORWARD_BIDIR, &plk, true);
+        if (st != GMA_SUCCESS) return st;
+    }
+    if (ws_bytes < plk.total)
+        return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                    ws_bytes, plk.total);
+    if (ws && (overlaps(ws, plk.total, qx, nq) || overlaps(ws, plk.total, kx, nk) || overlaps(ws, plk.total, v, nv) ||
+               overlaps(ws, plk.total, o, no)))
+        return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* w = reinterpret_cast<char*>(ws);
+    st = launch_prep(plk, mu, rv, pr, w, s);
+    if (st != GMA_SUCCESS) return st;
+    // write phase over the key/value rows
+    MainArgs ag = base_args(plk, w);
+    ag.kx = kx;
+    ag.v = v;
+    ag.vec_x = vec_ok(kx, plk.d_r, plk.f32);
+    ag.vec_v = vec_ok(v, plk.d_v, plk.f32);
+    const main_launch_t f_agg = dma ? plk.cls->tok_agg : plk.cls->agg;
+    st = timed_launch(K_AGG, s, [&] { f_agg(ag, (int)(BH * plk.P), s); });
+    if (st != GMA_SUCCESS) return st;
+    const int64_t rec = (int64_t)plk.cls->kc * plk.cls->vc + plk.cls->kc;
+    if (plk.P > 1) {
+        st = timed_launch(K_SCAN, s, [&] {
+            hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), (unsigned)BH), dim3(256), 0, s, ag.seg,
+                               plk.P, rec, 0, plk.P, (const float*)nullptr, (float*)nullptr);
+        });
+        if (st != GMA_SUCCESS) return st;
+    }
+    // read phase over the query rows, the total at record stride P of the key side
+    MainArgs a = base_args(plk, w);
+    a.N = plq.N;
+    a.Pg = plq.P;
+    a.seg_chunks = plq.seg_chunks;
+    a.qx = qx;
+    a.o = o;
+    a.vec_x = vec_ok(qx, plq.d_r, plq.f32);
+    a.vec_o = vec_o_ok(o, plq.d_v, plq.f32);
+    const main_launch_t f_bidir = dma ? plq.cls->tok_out_bidir : plq.cls->out_bidir;
+    return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, (int)(BH * plq.P), s); });
+}
+
 }  // namespace
 }  // namespace gma
 
@@ -524,6 +603,12 @@ gma_status_t gma_forward_causal(const gma_problem_t* p, const void* qx, const vo
                                 void* stream) {
     return forward(p, GMA_OP_FORWARD_CAUSAL, qx, kx, v, mu, raw_var, prior_logits, nullptr, nullptr, o, ws, ws_bytes,
                    stream);
+}
+
+gma_status_t gma_forward_bidir_kv(const gma_problem_t* p, int64_t seq_len_kv, const void* qx, const void* kx,
+                                  const void* v, const float* mu, const float* raw_var, const float* prior_logits,
+                                  void* o, void* ws, size_t ws_bytes, void* stream) {
+    return forward_bidir_kv(p, seq_len_kv, qx, kx, v, mu, raw_var, prior_logits, o, ws, ws_bytes, stream);
 }
 
 gma_status_t gma_forward_causal_state(const gma_problem_t* p, const void* qx, const void* kx, const void* v,

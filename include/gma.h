@@ -108,6 +108,16 @@ gma_status_t gma_forward_causal(const gma_problem_t* problem, const void* qx, co
                                 const float* prior_logits, void* o, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Bidirectional forward with separate query and key/value sequences (cross-attention; the pages
+ * name N_q != N_k as future work, and the write / read equations of item 2 apply unchanged):
+ * qx [B, H, N_q, d_r] and o [B, H, N_q, d_v] with N_q = problem->seq_len; kx [B, H, N_kv, d_r] and
+ * v [B, H, N_kv, d_v] with N_kv = seq_len_kv >= 1.  Workspace: gma_workspace_size() of the same
+ * problem with seq_len = seq_len_kv and op GMA_OP_FORWARD_BIDIR.  Otherwise as gma_forward_bidir. */
+gma_status_t gma_forward_bidir_kv(const gma_problem_t* problem, int64_t seq_len_kv, const void* qx,
+                                  const void* kx, const void* v, const float* mu, const float* raw_var,
+                                  const float* prior_logits, void* o, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Causal forward with the latent memory carried across calls (item 3: the causal output is a
  * prefix sum, so everything before this call's first token enters only through [Vt | Z]).  Lets a
  * sequence be processed in consecutive pieces (streaming, or one-token decode steps) with results

@@ -185,3 +185,17 @@ def test_causal_state_validation(lib):
     assert _fwd_state(lib, prob, ctypes.c_void_p(s1), ctypes.c_void_p(s1), ws_bytes=4096) == 3
     # the stateful op needs at least the causal workspace
     assert lib.gma_workspace_size(ctypes.byref(prob), 3) >= lib.gma_workspace_size(ctypes.byref(prob), 2)
+
+
+def test_cross_validation(lib):
+    prob = _prob()
+    f = lib.gma_forward_bidir_kv
+    args = [FAKE, ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x40000000), FAKE, FAKE, FAKE,
+            ctypes.c_void_p(0x80000000000), ctypes.c_void_p(0x100000000000)]
+    assert f(None, 100, *args, 1 << 40, None) == 1
+    assert f(ctypes.byref(prob), 0, *args, 1 << 40, None) == 1                   # seq_len_kv < 1
+    assert f(ctypes.byref(_prob(n_comp=0)), 100, *args, 1 << 40, None) == 1
+    assert f(ctypes.byref(prob), 100, *args, 4096, None) == 3                    # workspace too small
+    bad = list(args)
+    bad[6] = ctypes.c_void_p(0x40000000 + 64)                                    # o overlaps v
+    assert f(ctypes.byref(prob), 1 << 20, *bad, 1 << 40, None) == 1

@@ -185,6 +185,25 @@ def test_causal_without_room_for_stored_tiles(gma, cfg, N):
     assert err <= TOL[w.dtype], err
 
 
+# ------------------------------------------------------------------------------ cross-attention
+
+
+@pytest.mark.parametrize("cfg,Nq,Nk", [(3, 1, 5000), (3, 3000, 700), (3, 64, 1285), (2, 2000, 300), (4, 900, 2500),
+                                       (1, 700, 2100), (0, 256, 37)])
+def test_cross_attention_lengths(gma, cfg, Nq, Nk):
+    # bidirectional form with N_q query rows and N_kv key/value rows
+    wq = gma.workload(cfg, batch=1, heads=2, seq_len=Nq)
+    wk = gma.workload(cfg, batch=1, heads=2, seq_len=Nk)
+    say("cross cfg %d N_q=%d N_kv=%d" % (cfg, Nq, Nk))
+    iq, ik = gma.make_inputs(wq), gma.make_inputs(wk)   # same parameters (per-head seeds), different rows
+    ref = oracle.forward_bidir_kv(iq["qx"], ik["kx"], ik["v"], iq["mu"], iq["raw_var"], iq["prior_logits"], eps=wq.eps)
+    o = gma.forward_bidir(iq["qx"].to(DEV), ik["kx"].to(DEV), ik["v"].to(DEV), iq["mu"].to(DEV),
+                          iq["raw_var"].to(DEV), iq["prior_logits"].to(DEV), eps=wq.eps)
+    torch.cuda.synchronize()
+    err = rel_err(o, ref)
+    assert err <= TOL[wq.dtype], err
+
+
 # ------------------------------------------------------------------------------ carried state
 
 
