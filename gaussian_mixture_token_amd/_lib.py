@@ -41,6 +41,7 @@ _SIGS = [
     ("gma_forward_causal", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     ("gma_forward_bidir_kv", ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             _VP, ctypes.c_size_t, _VP]),
+    ("gma_decode_step", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     ("gma_forward_causal_state", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                 ctypes.c_size_t, _VP]),
     ("gma_status_string", ctypes.c_char_p, [ctypes.c_int]),

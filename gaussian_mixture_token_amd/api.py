@@ -163,3 +163,34 @@ def forward_causal(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=
 def forward(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, causal: bool = False, out=None, workspace=None):
     f = forward_causal if causal else forward_bidir
     return f(qx, kx, v, mu, raw_var, prior_logits, eps=eps, out=out, workspace=workspace)
+
+
+def decode_step(qx, kx, v, mu, raw_var, prior_logits, state, eps: float = 1e-6, out=None, state_out=None):
+    """One causal decode step: qx, kx [B, H, 1, d_r] (or [B, H, d_r]), v [B, H, 1, d_v]; state float32
+    [B, H, K, d_v + 1] (row k: Vt[k, :] then Z[k]) is the memory after all earlier tokens and is
+    updated in place unless state_out is given.  Returns the output row o [B, H, 1, d_v]."""
+    if qx.dim() == 3:
+        qx, kx, v = qx.unsqueeze(2), kx.unsqueeze(2), v.unsqueeze(2)
+    qx, kx, v = qx.contiguous(), kx.contiguous(), v.contiguous()   # one-token slices of a longer sequence
+    B, H, N, d_r = qx.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    if N != 1 or tuple(kx.shape) != (B, H, 1, d_r) or tuple(v.shape[:3]) != (B, H, 1):
+        raise ValueError("a decode step takes one token: qx, kx [B, H, 1, d_r], v [B, H, 1, d_v]")
+    if not (qx.dtype == kx.dtype == v.dtype):
+        raise TypeError("qx, kx and v must share one dtype")
+    _params(mu, raw_var, prior_logits, H, K, d_r)
+    dev = _check_gpu(qx, kx, v, mu, raw_var, prior_logits)
+    for name, t in (("state", state), ("state_out", state_out)):
+        if t is not None:
+            if t.dtype != torch.float32 or tuple(t.shape) != (B, H, K, d_v + 1) or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous float32 [B, H, K, d_v + 1] tensor" % name)
+            _check_gpu(t)
+    prob = problem(B, H, 1, d_r, K, d_v, qx.dtype, eps)
+    if out is None:
+        out = torch.empty(B, H, 1, d_v, dtype=qx.dtype, device=dev)
+    _check_gpu(out)
+    dst = state if state_out is None else state_out
+    _lib.check(_lib.load().gma_decode_step(ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu), _ptr(raw_var),
+                                           _ptr(prior_logits), _ptr(state), _ptr(dst), _ptr(out), _stream(dev)))
+    return out

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "gma.h"
+#include "gma_decode.hpp"
 #include "gma_registry.hpp"
 
 namespace gma {
@@ -43,9 +44,9 @@ int next_pow2(int x) {
     return p;
 }
 
-enum KernelId { K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_COUNT };
-const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan",
-                                     "causal_output", "bidir_output", "responsibilities", "state_convert"};
+enum KernelId { K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_COUNT };
+const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan", "causal_output", "bidir_output",
+                                     "responsibilities", "state_convert", "decode_step"};
 
 struct Plan {
     const ShapeClass* cls = nullptr;
@@ -609,6 +610,63 @@ gma_status_t gma_forward_bidir_kv(const gma_problem_t* p, int64_t seq_len_kv, co
                                   const void* v, const float* mu, const float* raw_var, const float* prior_logits,
                                   void* o, void* ws, size_t ws_bytes, void* stream) {
     return forward_bidir_kv(p, seq_len_kv, qx, kx, v, mu, raw_var, prior_logits, o, ws, ws_bytes, stream);
+}
+
+gma_status_t gma_decode_step(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,
+                             const float* raw_var, const float* prior_logits, const float* state_in, float* state_out,
+                             void* o, void* stream) {
+    g_last_error.clear();
+    if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
+    if (p->batch < 1 || p->heads < 1) return fail(GMA_ERROR_INVALID_VALUE, "batch and heads must be >= 1");
+    if (p->seq_len != 1)
+        return fail(GMA_ERROR_INVALID_VALUE, "a decode step takes one token per (batch, head): seq_len must be 1");
+    if (p->d_route < 1 || p->n_comp < 1 || p->d_value < 1)
+        return fail(GMA_ERROR_INVALID_VALUE, "d_route, n_comp and d_value must be >= 1");
+    if (p->d_route > 256 || p->n_comp > 256 || p->d_value > 256)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "d_route, n_comp and d_value must be <= 256");
+    if (p->dtype != GMA_DTYPE_F32 && p->dtype != GMA_DTYPE_BF16)
+        return fail(GMA_ERROR_INVALID_VALUE, "dtype must be GMA_DTYPE_F32 or GMA_DTYPE_BF16 (got %d)", p->dtype);
+    if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(GMA_ERROR_INVALID_VALUE, "eps must be finite and >= 0");
+    if (p->batch > (int64_t(1) << 40) / p->heads || p->batch * p->heads > INT32_MAX / 2)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "batch * heads too large");
+    const void* ptrs[] = {qx, kx, v, mu, raw_var, prior_logits, o};
+    for (int i = 0; i < 7; ++i)
+        if (!ptrs[i]) return fail(GMA_ERROR_INVALID_VALUE, "pointer argument %d is NULL", i);
+    const bool f32 = p->dtype == GMA_DTYPE_F32;
+    const size_t es = f32 ? 4 : 2;
+    for (const void* ptr : {qx, kx, v, (const void*)o})
+        if (misaligned(ptr, es)) return fail(GMA_ERROR_INVALID_VALUE, "tensor pointers must be %zu-byte aligned", es);
+    for (const void* ptr : {(const void*)mu, (const void*)raw_var, (const void*)prior_logits, (const void*)state_in,
+                            (const void*)state_out})
+        if (misaligned(ptr, 4)) return fail(GMA_ERROR_INVALID_VALUE, "parameter and state pointers must be 4-byte aligned");
+    const int64_t BH = p->batch * p->heads;
+    const size_t nx = (size_t)BH * p->d_route * es, nv = (size_t)BH * p->d_value * es;
+    const size_t ns = (size_t)BH * p->n_comp * (p->d_value + 1) * sizeof(float);
+    if (overlaps(o, nv, qx, nx) || overlaps(o, nv, kx, nx) || overlaps(o, nv, v, nv))
+        return fail(GMA_ERROR_INVALID_VALUE, "o must not overlap qx, kx or v");
+    for (const void* sp : {(const void*)state_in, (const void*)state_out})
+        if (sp && (overlaps(sp, ns, qx, nx) || overlaps(sp, ns, kx, nx) || overlaps(sp, ns, v, nv) ||
+                   overlaps(sp, ns, o, nv)))
+            return fail(GMA_ERROR_INVALID_VALUE, "states must not overlap qx, kx, v or o");
+    if (state_in && state_out && state_in != state_out && overlaps(state_in, ns, state_out, ns))
+        return fail(GMA_ERROR_INVALID_VALUE, "state_in and state_out must be the same buffer or disjoint");
+    DecodeArgs a;
+    a.qx = qx;
+    a.kx = kx;
+    a.v = v;
+    a.o = o;
+    a.mu = mu;
+    a.raw_var = raw_var;
+    a.prior = prior_logits;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.H = (int)p->heads;
+    a.K = p->n_comp;
+    a.d_r = p->d_route;
+    a.d_v = p->d_value;
+    a.eps = p->eps;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return timed_launch(K_DECODE, s, [&] { launch_decode(a, BH, f32, s); });
 }
 
 gma_status_t gma_forward_causal_state(const gma_problem_t* p, const void* qx, const void* kx, const void* v,

@@ -136,6 +136,18 @@ gma_status_t gma_forward_causal_state(const gma_problem_t* problem, const void* 
                                       float* state_out, void* o, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* One causal decode step (item 3, streaming): one new token per (b, h), problem->seq_len = 1.
+ * qx, kx [B, H, 1, d_r]; v, o [B, H, 1, d_v]; state_in / state_out as gma_forward_causal_state
+ * (either may be NULL: zero initial state / state not written; they may be the same buffer).
+ * Updates [Vt | Z] with the token's gamma_K (x) [v | 1] and writes its output row, which includes
+ * the token itself; the same result, up to rounding, as gma_forward_causal_state over one token.
+ * Any 1 <= d_r, K, d_v <= 256 (no tile classes); needs no workspace.  Arithmetic in fp32 with
+ * the log-density sums in fp64 (more precise than the bulk path's matrix-core logits). */
+gma_status_t gma_decode_step(const gma_problem_t* problem, const void* qx, const void* kx,
+                             const void* v, const float* mu, const float* raw_var,
+                             const float* prior_logits, const float* state_in, float* state_out,
+                             void* o, void* stream);
+
 /* Static description of a status code. */
 const char* gma_status_string(gma_status_t status);
 

@@ -199,3 +199,17 @@ def test_cross_validation(lib):
     bad = list(args)
     bad[6] = ctypes.c_void_p(0x40000000 + 64)                                    # o overlaps v
     assert f(ctypes.byref(prob), 1 << 20, *bad, 1 << 40, None) == 1
+
+
+def test_decode_step_validation(lib):
+    f = lib.gma_decode_step
+    ptrs = [FAKE, ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x40000000), FAKE, FAKE, FAKE]
+    s, o = ctypes.c_void_p(0x200000000000), ctypes.c_void_p(0x80000000000)
+    one = _prob(seq_len=1)
+    assert f(None, *ptrs, s, s, o, None) == 1
+    assert f(ctypes.byref(_prob(seq_len=2)), *ptrs, s, s, o, None) == 1            # one token per (b, h)
+    assert f(ctypes.byref(_prob(seq_len=1, n_comp=257)), *ptrs, s, s, o, None) == 2
+    assert f(ctypes.byref(one), *ptrs, s, s, None, None) == 1                      # o NULL
+    assert f(ctypes.byref(one), *ptrs, ctypes.c_void_p(0x200000000002), s, o, None) == 1   # misaligned state
+    assert f(ctypes.byref(one), *ptrs, s, ctypes.c_void_p(0x200000000000 + 4096), o, None) == 1   # partial overlap
+    assert f(ctypes.byref(one), *ptrs, ctypes.c_void_p(0x80000000000 + 64), None, o, None) == 1   # state over o

@@ -283,6 +283,51 @@ def test_causal_state_without_state_equals_plain_causal(gma):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("cfg,shape", [(3, None), (1, None), (4, None), (2, (37, 29, 45)), (0, (5, 3, 7))])
+def test_decode_steps_match_the_oracle(gma, cfg, shape):
+    # one-token steps from a zero state, updated in place, against the oracle's one pass over the
+    # same tokens (outputs and final state); any d_r, K, d_v <= 256
+    T = 30
+    kw = dict(batch=2, heads=2, seq_len=T)
+    if shape:
+        kw.update(d_route=shape[0], n_comp=shape[1], d_value=shape[2])
+    w = gma.workload(cfg, **kw)
+    say("decode cfg %d shape %s" % (cfg, shape))
+    inp = gma.make_inputs(w)
+    o_ref, s_ref = oracle.forward_causal_state(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"],
+                                               inp["prior_logits"], eps=w.eps)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    st = torch.zeros(2, 2, w.n_comp, w.d_value + 1, dtype=torch.float32, device=DEV)
+    outs = [gma.decode_step(t["qx"][:, :, i:i + 1], t["kx"][:, :, i:i + 1], t["v"][:, :, i:i + 1], t["mu"],
+                            t["raw_var"], t["prior_logits"], st, eps=w.eps) for i in range(T)]
+    torch.cuda.synchronize()
+    err_o, err_s = _rel(torch.cat(outs, dim=2), o_ref), _rel(st, s_ref)
+    say("  O err %.2e, state err %.2e" % (err_o, err_s))
+    assert err_o <= TOL[w.dtype], err_o
+    assert err_s <= TOL[w.dtype], err_s
+
+
+def test_decode_after_a_bulk_prefix(gma):
+    # the bulk causal pass over a prefix hands its state to decode steps; against one oracle pass
+    w = gma.workload(3, batch=1, heads=4, seq_len=3016)
+    inp = gma.make_inputs(w)
+    o_ref, s_ref = oracle.forward_causal_state(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"],
+                                               inp["prior_logits"], eps=w.eps)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    n0 = 3000
+    st = torch.empty(1, 4, w.n_comp, w.d_value + 1, dtype=torch.float32, device=DEV)
+    outs = [gma.forward_causal(t["qx"][:, :, :n0].contiguous(), t["kx"][:, :, :n0].contiguous(),
+                               t["v"][:, :, :n0].contiguous(), t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps,
+                               state_out=st)]
+    for i in range(n0, 3016):
+        outs.append(gma.decode_step(t["qx"][:, :, i:i + 1], t["kx"][:, :, i:i + 1], t["v"][:, :, i:i + 1], t["mu"],
+                                    t["raw_var"], t["prior_logits"], st, eps=w.eps))
+    torch.cuda.synchronize()
+    err_o, err_s = _rel(torch.cat(outs, dim=2), o_ref), _rel(st, s_ref)
+    assert err_o <= TOL[w.dtype], err_o
+    assert err_s <= TOL[w.dtype], err_s
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bitwise_deterministic(gma, causal):
     w = gma.workload(3, seq_len=20000)
