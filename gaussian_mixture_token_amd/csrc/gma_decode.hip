@@ -6,9 +6,9 @@
 // Z += gamma_K; read O = gamma_Q Vt / (gamma_Q . Z + eps)) and item 3 (causal: the read includes the
 // new token, and everything earlier enters through the carried [Vt | Z]).
 //
-// A step touches K (d_r + d_v + 1) numbers per head, so it is bound by launch latency and the state
-// traffic, not by arithmetic: plain vector code, no matrix cores.  Softplus, log and exp in fp32;
-// the log-density sums over d_r and the prior log-sum-exp in fp64; the state in fp32.
+// A step touches K (d_r + d_v + 1) numbers per head: plain vector code, no matrix cores, 16 waves per
+// (batch, head).  Per-dimension terms (softplus, log, reciprocal) in fp32; the log-density sums
+// over d_r and the prior log-sum-exp in fp64; the state in fp32.
 #include "gma_decode.hpp"
 #include "gma_device.hpp"
 
@@ -17,6 +17,8 @@ namespace gma {
 namespace {
 
 constexpr int kMax = 256;   // d_r, K, d_v <= 256
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
 
 template <bool F32>
 __device__ __forceinline__ float load_elem(const void* base, int64_t i) {
@@ -49,7 +51,7 @@ __device__ __forceinline__ double wave_max(double x) {
 }  // namespace
 
 template <bool F32>
-__global__ void __launch_bounds__(256) decode_kernel(const DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % a.H);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -57,14 +59,15 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecodeArgs a) {
     __shared__ float s_xq[kMax], s_xk[kMax], s_v[kMax];
     __shared__ double s_lq[kMax], s_lk[kMax];
     __shared__ float s_gq[kMax], s_gk[kMax];
-    __shared__ double s_red[8];
-    __shared__ float s_redf[8];
+    __shared__ double s_red[2 * kWaves];
+    __shared__ float s_redf[2 * kWaves];
+    __shared__ float s_num[kThreads];
 
-    for (int d = tid; d < dr; d += 256) {
+    for (int d = tid; d < dr; d += kThreads) {
         s_xq[d] = load_elem<F32>(a.qx, bh * dr + d);
         s_xk[d] = load_elem<F32>(a.kx, bh * dr + d);
     }
-    for (int j = tid; j < dv; j += 256) s_v[j] = load_elem<F32>(a.v, bh * dv + j);
+    for (int j = tid; j < dv; j += kThreads) s_v[j] = load_elem<F32>(a.v, bh * dv + j);
 
     // log pi = prior - log-sum-exp(prior), by wave 0 (fixed-order butterflies)
     if (w == 0) {
@@ -80,34 +83,52 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecodeArgs a) {
     const double lse = s_red[0];
 
     // log-densities of the query and the key: l_k(x) = log pi_k - 1/2 sum_d [log var + (x - mu)^2 / var]
-    // (the d_r/2 log 2 pi term is common to all components and cancels); components round-robin over
-    // the waves, dimensions over the lanes
-    for (int k = w; k < K; k += 4) {
-        double sq = 0.0, sk = 0.0;
-        for (int d = lane; d < dr; d += 64) {
-            const int64_t i = ((int64_t)h * K + k) * dr + d;
-            const float r = a.raw_var[i];
-            const float var = fmaxf(r, 0.f) + log1pf(expf(-fabsf(r)));   // softplus
-            const double inv = 1.0 / (double)var;
-            const double lv = (double)logf(var);
-            const double mu = a.mu[i];
-            const double dq = (double)s_xq[d] - mu, dk = (double)s_xk[d] - mu;
-            sq += lv + dq * dq * inv;
-            sk += lv + dk * dk * inv;
+    // (the d_r/2 log 2 pi term is common to all components and cancels).  Wave w takes components
+    // w, w + kWaves, ... in groups of G (their loads in flight together), lanes take dimensions.
+    constexpr int G = 4;
+    for (int k0 = w; k0 < K; k0 += kWaves * G) {
+        double sq[G], sk[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            sq[u] = 0.0;
+            sk[u] = 0.0;
         }
-        sq = wave_sum(sq);
-        sk = wave_sum(sk);
-        if (lane == 0) {
-            const double lp = (double)a.prior[(int64_t)h * K + k] - lse;
-            s_lq[k] = lp - 0.5 * sq;
-            s_lk[k] = lp - 0.5 * sk;
+        for (int d = lane; d < dr; d += 64) {
+            const double xq = s_xq[d], xk = s_xk[d];
+            float r[G], m[G];
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                const int k = k0 + kWaves * u;
+                const int64_t i = ((int64_t)h * K + (k < K ? k : 0)) * dr + d;
+                r[u] = a.raw_var[i];
+                m[u] = a.mu[i];
+            }
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                const float var = fmaxf(r[u], 0.f) + log1pf(expf(-fabsf(r[u])));   // softplus
+                const float inv = 1.f / var;
+                const float lv = logf(var);
+                const float dq = (float)xq - m[u], dk = (float)xk - m[u];
+                sq[u] += (double)(lv + dq * dq * inv);
+                sk[u] += (double)(lv + dk * dk * inv);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const int k = k0 + kWaves * u;
+            const double tq = wave_sum(sq[u]), tk = wave_sum(sk[u]);
+            if (lane == 0 && k < K) {
+                const double lp = (double)a.prior[(int64_t)h * K + k] - lse;
+                s_lq[k] = lp - 0.5 * tq;
+                s_lk[k] = lp - 0.5 * tk;
+            }
         }
     }
     __syncthreads();
 
     // softmax over the components (thread k), block reductions in a fixed order
     double mq = -INFINITY, mk = -INFINITY;
-    for (int k = tid; k < K; k += 256) {
+    for (int k = tid; k < K; k += kThreads) {
         mq = fmax(mq, s_lq[k]);
         mk = fmax(mk, s_lk[k]);
     }
@@ -115,14 +136,18 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecodeArgs a) {
     mk = wave_max(mk);
     if (lane == 0) {
         s_red[w] = mq;
-        s_red[4 + w] = mk;
+        s_red[kWaves + w] = mk;
     }
     __syncthreads();
-    mq = fmax(fmax(s_red[0], s_red[1]), fmax(s_red[2], s_red[3]));
-    mk = fmax(fmax(s_red[4], s_red[5]), fmax(s_red[6], s_red[7]));
+    mq = s_red[0];
+    mk = s_red[kWaves];
+    for (int q = 1; q < kWaves; ++q) {
+        mq = fmax(mq, s_red[q]);
+        mk = fmax(mk, s_red[kWaves + q]);
+    }
     __syncthreads();
     float eq = 0.f, ek = 0.f;
-    for (int k = tid; k < K; k += 256) {
+    for (int k = tid; k < K; k += kThreads) {
         const float xq = expf((float)(s_lq[k] - mq)), xk = expf((float)(s_lk[k] - mk));
         s_gq[k] = xq;
         s_gk[k] = xk;
@@ -133,47 +158,66 @@ __global__ void __launch_bounds__(256) decode_kernel(const DecodeArgs a) {
     ek = wave_sum(ek);
     if (lane == 0) {
         s_redf[w] = eq;
-        s_redf[4 + w] = ek;
+        s_redf[kWaves + w] = ek;
     }
     __syncthreads();
-    const float rq = 1.f / ((s_redf[0] + s_redf[1]) + (s_redf[2] + s_redf[3]));
-    const float rk = 1.f / ((s_redf[4] + s_redf[5]) + (s_redf[6] + s_redf[7]));
+    float tq = 0.f, tk = 0.f;
+    for (int q = 0; q < kWaves; ++q) {
+        tq += s_redf[q];
+        tk += s_redf[kWaves + q];
+    }
+    const float rq = 1.f / tq, rk = 1.f / tk;
     __syncthreads();
-    for (int k = tid; k < K; k += 256) {
+    for (int k = tid; k < K; k += kThreads) {
         s_gq[k] *= rq;
         s_gk[k] *= rk;
     }
     __syncthreads();
 
-    // memory update and read (the read sees the new token): column j of Vt by thread j, Z[k] by
-    // thread k; every element is read and written by the same thread, so in-place is safe
+    // memory update and read (the read sees the new token).  Z[k] by thread k; column j of Vt by the
+    // NP thread groups of NCOL threads, group g taking components g, g + NP, ...; every element is
+    // read and written by one thread, so in-place is safe.  Partial numerators meet in LDS.
     const int64_t sb = bh * K * (dv + 1);
     float den = 0.f;
-    for (int k = tid; k < K; k += 256) {
+    for (int k = tid; k < K; k += kThreads) {
         const float z = (a.state_in ? a.state_in[sb + (int64_t)k * (dv + 1) + dv] : 0.f) + s_gk[k];
         if (a.state_out) a.state_out[sb + (int64_t)k * (dv + 1) + dv] = z;
         den += s_gq[k] * z;
     }
     den = wave_sum(den);
     if (lane == 0) s_redf[w] = den;
-    __syncthreads();
-    den = ((s_redf[0] + s_redf[1]) + (s_redf[2] + s_redf[3])) + a.eps;
-    for (int j = tid; j < dv; j += 256) {
+    const int ncol = (dv <= 64) ? 64 : (dv <= 128 ? 128 : 256);   // threads per column group
+    const int np = kThreads / ncol;                                // column groups
+    const int g = tid / ncol, j = tid % ncol;
+    float num = 0.f;
+    if (j < dv) {
         const float vj = s_v[j];
-        float num = 0.f;
-        for (int k = 0; k < K; ++k) {
+#pragma unroll 8
+        for (int k = g; k < K; k += np) {
             const int64_t e = sb + (int64_t)k * (dv + 1) + j;
             const float sv = (a.state_in ? a.state_in[e] : 0.f) + s_gk[k] * vj;
             if (a.state_out) a.state_out[e] = sv;
             num += s_gq[k] * sv;
         }
-        store_elem<F32>(a.o, bh * dv + j, num / den);
+    }
+    s_num[tid] = num;
+    __syncthreads();
+    den = a.eps;
+    {
+        float t = 0.f;
+        for (int q = 0; q < kWaves; ++q) t += s_redf[q];
+        den += t;
+    }
+    if (tid < dv) {
+        float n = 0.f;
+        for (int q = 0; q < np; ++q) n += s_num[q * ncol + tid];
+        store_elem<F32>(a.o, bh * dv + tid, n / den);
     }
 }
 
 void launch_decode(const DecodeArgs& a, int64_t bh, bool f32, hipStream_t s) {
-    if (f32) hipLaunchKernelGGL((decode_kernel<true>), dim3((unsigned)bh), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<false>), dim3((unsigned)bh), dim3(256), 0, s, a);
+    if (f32) hipLaunchKernelGGL((decode_kernel<true>), dim3((unsigned)bh), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_kernel<false>), dim3((unsigned)bh), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace gma

@@ -19,7 +19,7 @@ struct DecodeArgs {
     float eps;
 };
 
-// grid: one workgroup of 256 threads per (batch, head)
+// grid: one workgroup of 1024 threads per (batch, head)
 void launch_decode(const DecodeArgs& a, int64_t bh, bool f32, hipStream_t s);
 
 }  // namespace gma
