@@ -29,7 +29,7 @@ _LIB = os.path.join(_HERE, "libgma_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-__all__ = ["build", "params", "responsibilities", "forward", "forward_causal_state", "forward_bidir_kv", "set_threads", "max_threads"]
+__all__ = ["build", "params", "responsibilities", "forward", "forward_causal_state", "forward_bidir_kv", "responsibility_stats", "set_threads", "max_threads"]
 
 
 def build(force: bool = True) -> str:
@@ -197,3 +197,25 @@ def forward_bidir_kv(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6,
     if rc != 0:
         raise MemoryError("oracle: allocation failed")
     return o
+
+
+def responsibility_stats(x, mu, raw_var, prior_logits):
+    """Diagnostics of the responsibilities of x [B, H, N, d_r] (reductions over the rows of Gamma):
+    usage [B, H, K] = sum_n gamma_nk; hard counts [B, H, K] = number of rows whose largest gamma is at
+    component k (ties to the lowest k); usage entropy [B, H] = -sum_k p_k ln p_k with p = usage / N
+    (0 ln 0 = 0).  Also returns the gap between each row's two largest responsibilities [B, H, N],
+    the margin by which its hard assignment is decided."""
+    g = responsibilities(x, mu, raw_var, prior_logits)          # [B, H, N, K] fp64
+    B, H, N, K = g.shape
+    usage = g.sum(axis=2)
+    arg = np.argmax(g, axis=-1)                                  # first maximum on ties
+    hard = np.zeros((B, H, K), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            hard[b, h] = np.bincount(arg[b, h], minlength=K)
+    p = usage / N
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ent = -np.where(p > 0, p * np.log(p), 0.0).sum(axis=-1)
+    top2 = np.sort(g, axis=-1)[..., -2:] if K > 1 else np.concatenate([np.zeros_like(g), g], axis=-1)
+    gap = top2[..., 1] - top2[..., 0]
+    return usage, hard, ent, gap

@@ -431,3 +431,40 @@ def test_cross_key_order_and_query_subsets(oracle_mod):
                                rtol=1e-12, atol=1e-14)
     sub = [3, 17, 49]
     np.testing.assert_array_equal(oracle_mod.forward_bidir_kv(qx[:, :, sub], kx, v, mu, rv, pl), o[:, :, sub])
+
+
+# ----------------------------------------------------------------------------- diagnostics
+# Component usage, hard assignments and usage entropy: reductions over the rows of Gamma.
+
+
+def test_stats_invariants(oracle_mod):
+    rng = np.random.default_rng(41)
+    B, H, N, dr, K = 2, 3, 400, 5, 7
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    x = rng.normal(0, 1.5, (B, H, N, dr))
+    usage, hard, ent, gap = oracle_mod.responsibility_stats(x, mu, rv, pl)
+    np.testing.assert_allclose(usage.sum(axis=-1), N, rtol=1e-12)      # rows of Gamma sum to one
+    assert (hard.sum(axis=-1) == N).all()
+    assert (ent >= 0).all() and (ent <= math.log(K) + 1e-12).all()
+    assert (gap >= 0).all() and (gap <= 1).all()
+
+
+def test_stats_single_component_and_separated_clusters(oracle_mod):
+    # K = 1: usage N, every row assigned, entropy 0
+    rng = np.random.default_rng(42)
+    mu, rv, pl = rand_params(rng, 1, 1, 3)
+    u, hd, e, _ = oracle_mod.responsibility_stats(rng.normal(0, 1, (1, 1, 50, 3)), mu, rv, pl)
+    assert u[0, 0, 0] == pytest.approx(50.0) and hd[0, 0, 0] == 50 and e[0, 0] == pytest.approx(0.0, abs=1e-12)
+    # three far-apart unit-variance clusters with equal priors, 10 / 20 / 30 points drawn at each mean:
+    # hard counts are the cluster sizes, usage is the same to within e^-(distance), entropy follows
+    dr = 2
+    means = np.array([[0.0, 0.0], [40.0, 0.0], [0.0, 40.0]])
+    mu = means[None]
+    rv = np.full((1, 3, dr), math.log(math.e - 1.0))                    # softplus(rho) = 1
+    pl = np.zeros((1, 3))
+    x = np.concatenate([means[c] + 0.1 * rng.normal(0, 1, (n, dr)) for c, n in enumerate((10, 20, 30))])
+    u, hd, e, _ = oracle_mod.responsibility_stats(x[None, None], mu, rv, pl)
+    assert list(hd[0, 0]) == [10, 20, 30]
+    np.testing.assert_allclose(u[0, 0], [10, 20, 30], atol=1e-9)
+    p = np.array([10, 20, 30]) / 60
+    assert e[0, 0] == pytest.approx(float(-(p * np.log(p)).sum()), rel=1e-9)
