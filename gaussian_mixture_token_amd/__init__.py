@@ -4,5 +4,5 @@ The computation lives in libgma.so (hand-written HIP kernels behind the C ABI of
 include/gma.h); this package only builds it, loads it and passes PyTorch tensors to it.
 """
 from .api import (GmaError, decode_step, forward, forward_bidir, forward_causal, problem,  # noqa: F401
-                  responsibilities, workspace_size)
+                  responsibilities, responsibility_stats, workspace_size)
 from .workloads import WORKLOADS, Workload, make_inputs, make_params, workload  # noqa: F401

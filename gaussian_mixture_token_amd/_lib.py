@@ -13,6 +13,7 @@ GMA_OP_RESPONSIBILITIES = 0
 GMA_OP_FORWARD_BIDIR = 1
 GMA_OP_FORWARD_CAUSAL = 2
 GMA_OP_FORWARD_CAUSAL_STATE = 3
+GMA_OP_RESPONSIBILITY_STATS = 4
 STATUS = {0: "GMA_SUCCESS", 1: "GMA_ERROR_INVALID_VALUE", 2: "GMA_ERROR_NOT_SUPPORTED",
           3: "GMA_ERROR_WORKSPACE_TOO_SMALL", 4: "GMA_ERROR_LAUNCH"}
 
@@ -41,6 +42,8 @@ _SIGS = [
     ("gma_forward_causal", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     ("gma_forward_bidir_kv", ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             _VP, ctypes.c_size_t, _VP]),
+    ("gma_responsibility_stats", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                ctypes.c_size_t, _VP]),
     ("gma_decode_step", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     ("gma_forward_causal_state", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                 ctypes.c_size_t, _VP]),

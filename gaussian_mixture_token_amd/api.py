@@ -194,3 +194,22 @@ def decode_step(qx, kx, v, mu, raw_var, prior_logits, state, eps: float = 1e-6, 
     _lib.check(_lib.load().gma_decode_step(ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu), _ptr(raw_var),
                                            _ptr(prior_logits), _ptr(state), _ptr(dst), _ptr(out), _stream(dev)))
     return out
+
+
+def responsibility_stats(x, mu, raw_var, prior_logits, workspace=None):
+    """Diagnostics of the responsibilities of x [B, H, N, d_r]: usage [B, H, K] fp32 (sum of Gamma over
+    the rows), hard counts [B, H, K] int32 view of uint32 (rows whose largest gamma is at k, ties to
+    the lowest k) and usage entropy [B, H] fp32 (of usage / N, natural log)."""
+    B, H, N, d_r = x.shape
+    K = mu.shape[1]
+    _params(mu, raw_var, prior_logits, H, K, d_r)
+    dev = _check_gpu(x, mu, raw_var, prior_logits)
+    prob = problem(B, H, N, d_r, K, 1, x.dtype)
+    usage = torch.empty(B, H, K, dtype=torch.float32, device=dev)
+    hard = torch.empty(B, H, K, dtype=torch.int32, device=dev)
+    ent = torch.empty(B, H, dtype=torch.float32, device=dev)
+    ws = _workspace(workspace_size(prob, _lib.GMA_OP_RESPONSIBILITY_STATS), dev, workspace)
+    _lib.check(_lib.load().gma_responsibility_stats(ctypes.byref(prob), _ptr(x), _ptr(mu), _ptr(raw_var),
+                                                    _ptr(prior_logits), _ptr(usage), _ptr(hard), _ptr(ent), _ptr(ws),
+                                                    ws.numel() * ws.element_size(), _stream(dev)))
+    return usage, hard, ent

@@ -44,9 +44,9 @@ int next_pow2(int x) {
     return p;
 }
 
-enum KernelId { K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_COUNT };
+enum KernelId { K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_STATS, K_COUNT };
 const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan", "causal_output", "bidir_output",
-                                     "responsibilities", "state_convert", "decode_step"};
+                                     "responsibilities", "state_convert", "decode_step", "responsibility_stats"};
 
 struct Plan {
     const ShapeClass* cls = nullptr;
@@ -60,6 +60,8 @@ struct Plan {
     bool dma = false;
     bool gtiles = false;   // causal token-split pair through stored Gamma_K tiles
     size_t off_ab = 0, off_c = 0, off_seg = 0, off_gk = 0, off_state = 0, total = 0;
+    int stat_segs = 0;                     // responsibility diagnostics: row segments per (batch, head)
+    size_t off_gamma = 0, off_part = 0;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -78,7 +80,7 @@ const ShapeClass* find_class(bool f32, int kc, int vc, int drc) {
 // stored Gamma_K tiles where it applies).  No HIP call.
 gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = false, bool tiles = true) {
     if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
-    if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_FORWARD_CAUSAL_STATE)
+    if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_RESPONSIBILITY_STATS)
         return fail(GMA_ERROR_INVALID_VALUE, "unknown op %d", op);
     if (p->batch < 1 || p->heads < 1 || p->seq_len < 1)
         return fail(GMA_ERROR_INVALID_VALUE, "batch, heads and seq_len must be >= 1 (got %lld, %lld, %lld)",
@@ -112,7 +114,8 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     const int w = std::min(4, kc / 16);
     const int vc = std::max(next_pow2(p->d_value), 16 * w);
     const int drc = std::max(plan->f32 ? 16 : 32, next_pow2(p->d_route));
-    plan->cls = find_class(plan->f32, kc, op == GMA_OP_RESPONSIBILITIES ? -1 : vc, drc);
+    const bool resp = op == GMA_OP_RESPONSIBILITIES || op == GMA_OP_RESPONSIBILITY_STATS;
+    plan->cls = find_class(plan->f32, kc, resp ? -1 : vc, drc);
     if (!plan->cls)
         return fail(GMA_ERROR_NOT_SUPPORTED, "no compiled kernel class for dtype=%s K=%d d_v=%d d_r=%d (padded %d/%d/%d)",
                     plan->f32 ? "f32" : "bf16", p->n_comp, p->d_value, p->d_route, kc, vc, drc);
@@ -123,7 +126,7 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     const int wg_per_cu = tok ? plan->cls->tok_wg_per_cu : plan->cls->wg_per_cu;
     const int64_t BH = plan->B * plan->H;
     plan->n_chunks = (plan->N + C - 1) / C;
-    if (op == GMA_OP_RESPONSIBILITIES) {
+    if (resp) {
         plan->P = (int)std::min<int64_t>(plan->n_chunks, INT32_MAX / 4);
         plan->seg_chunks = (int)((plan->n_chunks + plan->P - 1) / plan->P);
     } else {
@@ -168,6 +171,13 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     plan->off_gk = align_up(plan->off_seg + seg_bytes, 256);
     plan->off_state = align_up(plan->off_gk + gk_bytes, 256);
     plan->total = align_up(plan->off_state + state_bytes, 256);
+    if (op == GMA_OP_RESPONSIBILITY_STATS) {
+        // Gamma of every row, then per-segment partial usages and counts
+        plan->stat_segs = (int)std::max<int64_t>(1, std::min<int64_t>((1024 + BH - 1) / BH, (plan->N + 63) / 64));
+        plan->off_gamma = plan->total;
+        plan->off_part = align_up(plan->off_gamma + (size_t)BH * plan->N * plan->K * sizeof(float), 256);
+        plan->total = align_up(plan->off_part + (size_t)BH * plan->stat_segs * plan->K * 8, 256);
+    }
     return GMA_SUCCESS;
 }
 
@@ -178,7 +188,8 @@ size_t advertised_workspace(const gma_problem_t* problem, int op) {
     if (make_plan(problem, op, &pl) != GMA_SUCCESS) return 0;
     size_t total = pl.total;
     Plan pt;
-    if (op != GMA_OP_RESPONSIBILITIES && pl.cls->tok_out_causal && make_plan(problem, op, &pt, true) == GMA_SUCCESS)
+    if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_RESPONSIBILITY_STATS && pl.cls->tok_out_causal &&
+        make_plan(problem, op, &pt, true) == GMA_SUCCESS)
         total = std::max(total, pt.total);
     return total;
 }
@@ -293,6 +304,81 @@ __global__ void __launch_bounds__(256) record_to_state(const float* recs, float*
     const int64_t r = (j < dv) ? (((int64_t)(c / 16) * (VC / 16) + j / 16) * 64 + (c % 16) / 4 * 16 + j % 16) * 4 + c % 4
                                : (int64_t)KC * VC + c;
     state[(int64_t)blockIdx.y * K * (dv + 1) + e] = recs[(int64_t)blockIdx.y * rec + r];
+}
+
+// Responsibility diagnostics over Gamma [BH, N, K] fp32, first level: workgroup (s, bh) takes rows
+// [s rows_per_seg, (s + 1) rows_per_seg) of head bh, wave w every fourth of them; lane l holds
+// components l, l + 64, ...  Per row: the usage sums (sequential per lane) and the hard assignment
+// (largest gamma, ties to the lowest component, by butterflies).  Partials in a fixed order.
+__global__ void __launch_bounds__(256) stats_partial_kernel(const float* gamma, float* pu, uint32_t* pc, int64_t N, int K,
+                                                            int S, int64_t rows_per_seg) {
+    const int s = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t r0 = (int64_t)s * rows_per_seg, r1 = std::min<int64_t>(N, r0 + rows_per_seg);
+    float use[4] = {0.f, 0.f, 0.f, 0.f};
+    uint32_t cnt[4] = {0u, 0u, 0u, 0u};
+    __shared__ float s_u[4][256];
+    __shared__ uint32_t s_c[4][256];
+    for (int64_t r = r0 + w; r < r1; r += 4) {
+        const float* row = gamma + (bh * N + r) * K;
+        float best = -1.f;
+        int bi = K;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k = lane + 64 * u;
+            if (k < K) {
+                const float g = row[k];
+                use[u] += g;
+                if (g > best) { best = g; bi = k; }
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ob = __shfl_xor(best, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (bi == lane + 64 * u) ++cnt[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        s_u[w][lane + 64 * u] = use[u];
+        s_c[w][lane + 64 * u] = cnt[u];
+    }
+    __syncthreads();
+    for (int k = tid; k < K; k += 256) {
+        pu[(bh * S + s) * K + k] = ((s_u[0][k] + s_u[1][k]) + s_u[2][k]) + s_u[3][k];
+        pc[(bh * S + s) * K + k] = s_c[0][k] + s_c[1][k] + s_c[2][k] + s_c[3][k];
+    }
+}
+
+// Second level: usage and counts summed over the segments in order; usage entropy of usage / N.
+__global__ void __launch_bounds__(256) stats_final_kernel(const float* pu, const uint32_t* pc, float* usage,
+                                                          uint32_t* hard, float* entropy, int64_t N, int K, int S) {
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    __shared__ float s_e[4];
+    float e = 0.f;
+    for (int k = tid; k < K; k += 256) {
+        float u = 0.f;
+        uint32_t c = 0u;
+        for (int q = 0; q < S; ++q) {
+            u += pu[(bh * S + q) * K + k];
+            c += pc[(bh * S + q) * K + k];
+        }
+        usage[bh * K + k] = u;
+        hard[bh * K + k] = c;
+        const float p = u / (float)N;
+        if (p > 0.f) e -= p * logf(p);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o, 64);
+    if (lane == 0) s_e[w] = e;
+    __syncthreads();
+    if (tid == 0) entropy[bh] = ((s_e[0] + s_e[1]) + s_e[2]) + s_e[3];
 }
 
 gma_status_t launch_prep(const Plan& pl, const float* mu, const float* rv, const float* pr, char* ws, hipStream_t s) {
@@ -590,6 +676,60 @@ gma_status_t gma_responsibilities(const gma_problem_t* p, const void* x, const f
     const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
     const int grid = (int)(pl.B * pl.H * pl.P);
     return timed_launch(K_RESP, s, [&] { f_resp(a, grid, s); });
+}
+
+gma_status_t gma_responsibility_stats(const gma_problem_t* p, const void* x, const float* mu, const float* raw_var,
+                                      const float* prior_logits, float* usage, uint32_t* hard_counts,
+                                      float* usage_entropy, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    Plan pl;
+    gma_status_t st = make_plan(p, GMA_OP_RESPONSIBILITY_STATS, &pl);
+    if (st != GMA_SUCCESS) return st;
+    const void* ptrs[] = {x, mu, raw_var, prior_logits, usage, hard_counts, usage_entropy};
+    st = check_common(p, ptrs, 7, ws, ws_bytes, pl);
+    if (st != GMA_SUCCESS) return st;
+    const size_t es = pl.f32 ? 4 : 2;
+    if (misaligned(x, es) || misaligned(mu, 4) || misaligned(raw_var, 4) || misaligned(prior_logits, 4) ||
+        misaligned(usage, 4) || misaligned(hard_counts, 4) || misaligned(usage_entropy, 4))
+        return fail(GMA_ERROR_INVALID_VALUE, "misaligned pointer");
+    const int64_t BH = pl.B * pl.H;
+    const size_t nx = (size_t)(BH * pl.N) * pl.d_r * es, nk = (size_t)BH * pl.K * 4, nb = (size_t)BH * 4;
+    const void* outs[] = {usage, hard_counts, usage_entropy};
+    const size_t osz[] = {nk, nk, nb};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], osz[i], x, nx) || (ws && overlaps(outs[i], osz[i], ws, pl.total)))
+            return fail(GMA_ERROR_INVALID_VALUE, "outputs must not overlap x or the workspace");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], osz[i], outs[j], osz[j])) return fail(GMA_ERROR_INVALID_VALUE, "outputs must not overlap");
+    }
+    if (ws && overlaps(ws, pl.total, x, nx)) return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap x");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* w = reinterpret_cast<char*>(ws);
+    st = launch_prep(pl, mu, raw_var, prior_logits, w, s);
+    if (st != GMA_SUCCESS) return st;
+    // Gamma of every row into the workspace (the responsibilities kernels), then the reductions
+    MainArgs a = base_args(pl, w);
+    a.qx = x;
+    a.gamma = reinterpret_cast<float*>(w + pl.off_gamma);
+    a.vec_x = vec_ok(x, pl.d_r, pl.f32);
+    const bool dma = !pl.f32 && pl.cls->dma_resp && pl.d_r % 8 == 0 && !misaligned(x, 16) &&
+                     (pl.N + pl.cls->c) * pl.d_r * 2 < (int64_t(1) << 31);
+    const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
+    st = timed_launch(K_RESP, s, [&] { f_resp(a, (int)(BH * pl.P), s); });
+    if (st != GMA_SUCCESS) return st;
+    float* pu = reinterpret_cast<float*>(w + pl.off_part);
+    uint32_t* pc = reinterpret_cast<uint32_t*>(pu + (size_t)BH * pl.stat_segs * pl.K);
+    const int S = pl.stat_segs;
+    const int64_t rps = (pl.N + S - 1) / S;
+    st = timed_launch(K_STATS, s, [&] {
+        hipLaunchKernelGGL(stats_partial_kernel, dim3((unsigned)S, (unsigned)BH), dim3(256), 0, s,
+                           (const float*)a.gamma, pu, pc, pl.N, pl.K, S, rps);
+    });
+    if (st != GMA_SUCCESS) return st;
+    return timed_launch(K_STATS, s, [&] {
+        hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)BH), dim3(256), 0, s, (const float*)pu,
+                           (const uint32_t*)pc, usage, hard_counts, usage_entropy, pl.N, pl.K, S);
+    });
 }
 
 gma_status_t gma_forward_bidir(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,

@@ -64,7 +64,8 @@ typedef enum {
     GMA_OP_RESPONSIBILITIES = 0,
     GMA_OP_FORWARD_BIDIR = 1,
     GMA_OP_FORWARD_CAUSAL = 2,
-    GMA_OP_FORWARD_CAUSAL_STATE = 3
+    GMA_OP_FORWARD_CAUSAL_STATE = 3,
+    GMA_OP_RESPONSIBILITY_STATS = 4
 } gma_op_t;
 
 /* Problem sizes.  eps >= 0 and finite; it is added to each row's denominator Gamma_Q Z. */
@@ -92,6 +93,20 @@ size_t gma_workspace_size(const gma_problem_t* problem, int op);
 gma_status_t gma_responsibilities(const gma_problem_t* problem, const void* x, const float* mu,
                                   const float* raw_var, const float* prior_logits, float* gamma,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Responsibility diagnostics (item 1; the pages discuss how the components are used): for every
+ * row of x [B, H, N, d_r] under head h's mixture,
+ *   usage [B, H, K] fp32         sum over the rows of gamma_k (each row of Gamma sums to 1);
+ *   hard_counts [B, H, K] uint32 number of rows whose largest gamma is at component k (ties go to the
+ *                                lowest k; decided on the library's fp32 Gamma, so rows whose two
+ *                                largest responsibilities are within its rounding may go either way);
+ *   usage_entropy [B, H] fp32    -sum_k p_k ln p_k with p = usage / N (0 ln 0 = 0).
+ * Gamma of every row is formed in the workspace: gma_workspace_size(problem,
+ * GMA_OP_RESPONSIBILITY_STATS) bytes (about B * H * N * K * 4).  d_value is ignored. */
+gma_status_t gma_responsibility_stats(const gma_problem_t* problem, const void* x, const float* mu,
+                                      const float* raw_var, const float* prior_logits, float* usage,
+                                      uint32_t* hard_counts, float* usage_entropy, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* Bidirectional forward (items 1-2): O = Gamma_Q (Gamma_K^T V) / (Gamma_Q (Gamma_K^T 1) + eps)
  * over the whole sequence of each (b, h).  qx, kx [B, H, N, d_r]; v, o [B, H, N, d_v]. */

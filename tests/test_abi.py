@@ -213,3 +213,16 @@ def test_decode_step_validation(lib):
     assert f(ctypes.byref(one), *ptrs, ctypes.c_void_p(0x200000000002), s, o, None) == 1   # misaligned state
     assert f(ctypes.byref(one), *ptrs, s, ctypes.c_void_p(0x200000000000 + 4096), o, None) == 1   # partial overlap
     assert f(ctypes.byref(one), *ptrs, ctypes.c_void_p(0x80000000000 + 64), None, o, None) == 1   # state over o
+
+
+def test_responsibility_stats_validation(lib):
+    f = lib.gma_responsibility_stats
+    prob = _prob(d_value=1)
+    x, u, hc, e = FAKE, ctypes.c_void_p(0x80000000000), ctypes.c_void_p(0x90000000000), ctypes.c_void_p(0xa0000000000)
+    ws = ctypes.c_void_p(0x100000000000)
+    need = lib.gma_workspace_size(ctypes.byref(prob), 4)
+    assert need >= 16 * 65536 * 128 * 4                       # Gamma of every row is formed in the workspace
+    assert f(ctypes.byref(prob), None, FAKE, FAKE, FAKE, u, hc, e, ws, need, None) == 1
+    assert f(ctypes.byref(prob), x, FAKE, FAKE, FAKE, u, hc, e, ws, need - 1, None) == 3
+    assert f(ctypes.byref(prob), x, FAKE, FAKE, FAKE, u, u, e, ws, need, None) == 1       # outputs overlap
+    assert f(ctypes.byref(_prob(n_comp=300)), x, FAKE, FAKE, FAKE, u, hc, e, ws, need, None) == 2

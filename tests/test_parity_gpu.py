@@ -185,6 +185,31 @@ def test_causal_without_room_for_stored_tiles(gma, cfg, N):
     assert err <= TOL[w.dtype], err
 
 
+# ------------------------------------------------------------------------------ diagnostics
+
+
+@pytest.mark.parametrize("cfg,B,H,N", [(3, 1, 3, 7000), (4, 1, 2, 5000), (2, 2, 2, 3000), (1, 2, 2, 2000), (0, 1, 1, 256)])
+def test_responsibility_stats_match_the_oracle(gma, cfg, B, H, N):
+    # usage and entropy within the Gamma tolerance; hard counts exactly, except that rows whose two
+    # largest responsibilities (oracle) are closer than twice that tolerance may go either way
+    w = gma.workload(cfg, batch=B, heads=H, seq_len=N)
+    say("stats cfg %d B%d H%d N%d" % (cfg, B, H, N))
+    inp = gma.make_inputs(w)
+    u_ref, h_ref, e_ref, gap = oracle.responsibility_stats(inp["qx"], inp["mu"], inp["raw_var"], inp["prior_logits"])
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    u, hc, e = gma.responsibility_stats(t["qx"], t["mu"], t["raw_var"], t["prior_logits"])
+    torch.cuda.synchronize()
+    tol = 1e-4 if w.dtype == "f32" else 1e-2
+    u, hc, e = u.cpu().numpy().astype(np.float64), hc.cpu().numpy().astype(np.int64), e.cpu().numpy()
+    assert np.abs(u - u_ref).max() <= tol * N
+    assert (hc.sum(axis=-1) == N).all()
+    np.testing.assert_allclose(e, e_ref, atol=2 * tol)
+    ambiguous = (gap < 2 * tol).sum(axis=-1)                   # [B, H]
+    diff = np.abs(hc - h_ref).sum(axis=-1)
+    say("  usage err %.2e, hard-count moves %s (ambiguous rows %s)" % (np.abs(u - u_ref).max(), diff.ravel(), ambiguous.ravel()))
+    assert (diff <= 2 * ambiguous).all(), (diff, ambiguous)
+
+
 # ------------------------------------------------------------------------------ cross-attention
 
 
