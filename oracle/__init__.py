@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the Gaussian Mixture Attention forward mixer.
+"""fp64 CPU oracle of the Gaussian Mixture Attention mixer (forward and backward).
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product path
@@ -29,7 +29,7 @@ _LIB = os.path.join(_HERE, "libgma_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-__all__ = ["build", "params", "responsibilities", "forward", "forward_causal_state", "forward_bidir_kv", "responsibility_stats", "set_threads", "max_threads"]
+__all__ = ["build", "params", "responsibilities", "forward", "forward_causal_state", "forward_bidir_kv", "responsibility_stats", "backward", "set_threads", "max_threads"]
 
 
 def build(force: bool = True) -> str:
@@ -65,6 +65,9 @@ def _load():
             lib.gma_oracle_forward_bidir_kv.argtypes = [i64, i64, i64, i64, i32, i32, i32, ctypes.c_double,
                                                         dp, dp, dp, dp, dp, dp, dp]
             lib.gma_oracle_forward_bidir_kv.restype = ctypes.c_int
+            lib.gma_oracle_backward.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32, i32, ctypes.c_double,
+                                                dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp]
+            lib.gma_oracle_backward.restype = ctypes.c_int
             lib.gma_oracle_set_threads.argtypes = [ctypes.c_int]
             lib.gma_oracle_set_threads.restype = None
             lib.gma_oracle_max_threads.argtypes = []
@@ -197,6 +200,32 @@ def forward_bidir_kv(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6,
     if rc != 0:
         raise MemoryError("oracle: allocation failed")
     return o
+
+
+def backward(qx, kx, v, mu, raw_var, prior_logits, dout, eps: float = 1e-6, causal: bool = False,
+             threads: Optional[int] = None):
+    """Gradients of a loss through the mixer given dout = dL/dO [B, H, N, d_v]: a dict with dqx,
+    dkx [B, H, N, d_r], dv [B, H, N, d_v], dmu, draw_var [H, K, d_r] and dprior_logits [H, K], all
+    fp64 (the chain rule through the same definitions as ``forward``; see gma_oracle_backward)."""
+    qx, kx, v, do = _f64(qx), _f64(kx), _f64(v), _f64(dout)
+    mu, rv, pl = _f64(mu), _f64(raw_var), _f64(prior_logits)
+    B, H, N, dr = qx.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    assert kx.shape == qx.shape and v.shape == (B, H, N, dv) and do.shape == v.shape
+    assert mu.shape == (H, K, dr) and rv.shape == (H, K, dr) and pl.shape == (H, K)
+    out = {"dqx": np.empty_like(qx), "dkx": np.empty_like(kx), "dv": np.empty_like(v),
+           "dmu": np.empty_like(mu), "draw_var": np.empty_like(rv), "dprior_logits": np.empty_like(pl)}
+    lib = _load()
+    if threads is not None:
+        lib.gma_oracle_set_threads(int(threads))
+    rc = lib.gma_oracle_backward(1 if causal else 0, B, H, N, dr, K, dv, float(eps), _ptr(qx), _ptr(kx),
+                                 _ptr(v), _ptr(mu), _ptr(rv), _ptr(pl), _ptr(do), _ptr(out["dqx"]),
+                                 _ptr(out["dkx"]), _ptr(out["dv"]), _ptr(out["dmu"]), _ptr(out["draw_var"]),
+                                 _ptr(out["dprior_logits"]))
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return out
 
 
 def responsibility_stats(x, mu, raw_var, prior_logits):

@@ -1,6 +1,6 @@
 /*
  * gma_oracle.c -- plain fp64 CPU oracle of the Gaussian Mixture Attention
- * (GMA) forward mixer.
+ * (GMA) mixer: forward, and its backward (gma_oracle_backward).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
  * load this file: only the tests, the smoke check and the CPU-baseline leg of
@@ -345,4 +345,194 @@ int gma_oracle_forward_causal_state(int64_t B, int64_t H, int64_t N, int32_t dr,
                                     const double* prior_logits, const double* state_in,
                                     double* state_out, double* o) {
     return forward_impl(1, B, H, N, dr, K, dv, eps, qx, kx, v, mu, raw_var, prior_logits, state_in, state_out, o);
+}
+
+/* ---- Backward of the mixer: gradients of a loss L with respect to every input, given
+ * dout = dL/dO.  The pages train the layer end to end ("Variantes et Entrainement"), so the
+ * gradient is the chain rule through the definitions above, applied step by step:
+ *   read phase   O_i = num_i / den_i, num_i = Gamma_Q[i] Vt_i, den_i = Gamma_Q[i] . Z_i + eps
+ *                  g_i = dO_i / den_i                       (dL/dnum_i)
+ *                  h_i = -(dO_i . O_i) / den_i              (dL/dden_i)
+ *                  dGamma_Q[i][k] = Vt_i[k] . g_i + Z_i[k] h_i
+ *   write phase  Vt_i, Z_i = sums of gamma_K[j] (x) v_j and gamma_K[j] over j <= i (causal) or
+ *                over all j (bidirectional); every query i that sees key j contributes
+ *                  dGamma_K[j][k] = sum_{i sees j} Gamma_Q[i][k] (v_j . g_i + h_i)
+ *                  dv_j           = sum_{i sees j} (Gamma_Q[i] . gamma_K[j]) g_i
+ *   posterior    gamma = softmax_k(l_k): dl_k = gamma_k (dgamma_k - sum_j gamma_j dgamma_j)
+ *   log-density  l_k(x) = log pi_k - 1/2 sum_d [log(2 pi s_kd) + (x_d - mu_kd)^2 / s_kd]:
+ *                  dx_d   = sum_k dl_k (mu_kd - x_d) / s_kd
+ *                  dmu_kd = sum over rows of dl_k (x_d - mu_kd) / s_kd
+ *                  ds_kd  = sum over rows of dl_k ((x_d - mu_kd)^2 / s_kd^2 - 1 / s_kd) / 2
+ *                  dlog pi_k = sum over rows of dl_k
+ *   parameters   s = softplus(rho): drho = ds * sigmoid(rho);
+ *                log pi = lambda - logsumexp(lambda): dlambda_j = G_j - pi_j sum_k G_k with
+ *                G = dlog pi.
+ * Rows of both Q_X and K_X contribute to the parameter gradients (one mixture per head routes
+ * both).  Sums over the sequence run sequentially; the per-(b, h) parameter partials are added
+ * over b in order, so the result is independent of the thread count.
+ * dqx, dkx [B, H, N, d_r]; dv [B, H, N, d_v]; dmu, draw_var [H, K, d_r]; dprior_logits [H, K].
+ * Returns 0, or 1 if memory could not be allocated. */
+static void row_logit_backward(int32_t K, int32_t dr, const double* x, const double* mu,
+                               const double* var, const double* gamma, const double* dgamma,
+                               double* dx, double* dmu_acc, double* dvar_acc, double* dlogp_acc) {
+    double dot = 0.0;
+    for (int k = 0; k < K; ++k) dot += gamma[k] * dgamma[k];
+    for (int d = 0; d < dr; ++d) dx[d] = 0.0;
+    for (int k = 0; k < K; ++k) {
+        const double dl = gamma[k] * (dgamma[k] - dot);
+        dlogp_acc[k] += dl;
+        for (int d = 0; d < dr; ++d) {
+            const double s = var[(int64_t)k * dr + d];
+            const double diff = x[d] - mu[(int64_t)k * dr + d];
+            dx[d] += dl * (-diff) / s;
+            dmu_acc[(int64_t)k * dr + d] += dl * diff / s;
+            dvar_acc[(int64_t)k * dr + d] += dl * 0.5 * (diff * diff / (s * s) - 1.0 / s);
+        }
+    }
+}
+
+int gma_oracle_backward(int causal, int64_t B, int64_t H, int64_t N, int32_t dr, int32_t K,
+                        int32_t dv, double eps, const double* qx, const double* kx,
+                        const double* v, const double* mu, const double* raw_var,
+                        const double* prior_logits, const double* dout, double* dqx,
+                        double* dkx, double* dvv, double* dmu, double* draw_var,
+                        double* dprior_logits) {
+    const int64_t BH = B * H, KD = (int64_t)K * dr;
+    double* var = (double*)malloc(sizeof(double) * H * KD);
+    double* logp = (double*)malloc(sizeof(double) * H * K);
+    double* logdet = (double*)malloc(sizeof(double) * H * K);
+    double* pmu = (double*)calloc((size_t)(BH * KD), sizeof(double));    /* per-(b, h) partials */
+    double* pvar = (double*)calloc((size_t)(BH * KD), sizeof(double));
+    double* plogp = (double*)calloc((size_t)(BH * K), sizeof(double));
+    int rc = 0;
+    if (!var || !logp || !logdet || !pmu || !pvar || !plogp) { rc = 1; goto done; }
+    gma_oracle_params(H, K, dr, raw_var, prior_logits, var, logp);
+    for (int64_t h = 0; h < H; ++h) head_logdet(K, dr, var + h * KD, logdet + h * K);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const int64_t h = bh % H;
+        const double* mu_h = mu + h * KD;
+        const double* var_h = var + h * KD;
+        const double* q_bh = qx + bh * N * dr;
+        const double* k_bh = kx + bh * N * dr;
+        const double* v_bh = v + bh * N * dv;
+        const double* do_bh = dout + bh * N * dv;
+        double* gq = (double*)malloc(sizeof(double) * N * K);
+        double* gk = (double*)malloc(sizeof(double) * N * K);
+        double* dgq = (double*)malloc(sizeof(double) * N * K);
+        double* dgk = (double*)malloc(sizeof(double) * N * K);
+        double* gg = (double*)malloc(sizeof(double) * N * dv);   /* g_i */
+        double* hh = (double*)malloc(sizeof(double) * N);        /* h_i */
+        double* st = (double*)malloc(sizeof(double) * (int64_t)K * dv);
+        double* z = (double*)malloc(sizeof(double) * K);
+        if (!gq || !gk || !dgq || !dgk || !gg || !hh || !st || !z) {
+#pragma omp atomic write
+            rc = 1;
+            free(gq); free(gk); free(dgq); free(dgk); free(gg); free(hh); free(st); free(z);
+            continue;
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            row_responsibilities(K, dr, q_bh + n * dr, mu_h, var_h, logp + h * K, logdet + h * K, gq + n * K);
+            row_responsibilities(K, dr, k_bh + n * dr, mu_h, var_h, logp + h * K, logdet + h * K, gk + n * K);
+        }
+        /* read phase and its gradient, queries in order (the latent memory Vt, Z as of query i) */
+        memset(st, 0, sizeof(double) * (size_t)K * dv);
+        memset(z, 0, sizeof(double) * (size_t)K);
+        if (!causal) {
+            for (int64_t j = 0; j < N; ++j)
+                for (int k = 0; k < K; ++k) {
+                    z[k] += gk[j * K + k];
+                    for (int c = 0; c < dv; ++c) st[(int64_t)k * dv + c] += gk[j * K + k] * v_bh[j * dv + c];
+                }
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            if (causal) {
+                for (int k = 0; k < K; ++k) {
+                    z[k] += gk[i * K + k];
+                    for (int c = 0; c < dv; ++c) st[(int64_t)k * dv + c] += gk[i * K + k] * v_bh[i * dv + c];
+                }
+            }
+            double den = 0.0;
+            for (int k = 0; k < K; ++k) den += gq[i * K + k] * z[k];
+            den += eps;
+            double dot = 0.0;   /* dO_i . O_i */
+            for (int c = 0; c < dv; ++c) {
+                double num = 0.0;
+                for (int k = 0; k < K; ++k) num += gq[i * K + k] * st[(int64_t)k * dv + c];
+                dot += do_bh[i * dv + c] * (num / den);
+                gg[i * dv + c] = do_bh[i * dv + c] / den;
+            }
+            hh[i] = -dot / den;
+            for (int k = 0; k < K; ++k) {
+                double s = 0.0;
+                for (int c = 0; c < dv; ++c) s += st[(int64_t)k * dv + c] * gg[i * dv + c];
+                dgq[i * K + k] = s + z[k] * hh[i];
+            }
+        }
+        /* write phase gradient, keys in reverse order: R = sum over the queries that see key j of
+         * Gamma_Q[i] (x) g_i, r = the same sum of Gamma_Q[i] h_i */
+        memset(st, 0, sizeof(double) * (size_t)K * dv);
+        memset(z, 0, sizeof(double) * (size_t)K);
+        if (!causal) {
+            for (int64_t i = 0; i < N; ++i)
+                for (int k = 0; k < K; ++k) {
+                    z[k] += gq[i * K + k] * hh[i];
+                    for (int c = 0; c < dv; ++c) st[(int64_t)k * dv + c] += gq[i * K + k] * gg[i * dv + c];
+                }
+        }
+        double* dv_bh = dvv + bh * N * dv;
+        for (int64_t j = N - 1; j >= 0; --j) {
+            if (causal) {
+                for (int k = 0; k < K; ++k) {
+                    z[k] += gq[j * K + k] * hh[j];
+                    for (int c = 0; c < dv; ++c) st[(int64_t)k * dv + c] += gq[j * K + k] * gg[j * dv + c];
+                }
+            }
+            for (int k = 0; k < K; ++k) {
+                double s = 0.0;
+                for (int c = 0; c < dv; ++c) s += st[(int64_t)k * dv + c] * v_bh[j * dv + c];
+                dgk[j * K + k] = s + z[k];
+            }
+            for (int c = 0; c < dv; ++c) {
+                double s = 0.0;
+                for (int k = 0; k < K; ++k) s += gk[j * K + k] * st[(int64_t)k * dv + c];
+                dv_bh[j * dv + c] = s;
+            }
+        }
+        /* posterior and log-density gradients of every row of both sides */
+        for (int64_t n = 0; n < N; ++n) {
+            row_logit_backward(K, dr, q_bh + n * dr, mu_h, var_h, gq + n * K, dgq + n * K,
+                               dqx + bh * N * dr + n * dr, pmu + bh * KD, pvar + bh * KD, plogp + bh * K);
+            row_logit_backward(K, dr, k_bh + n * dr, mu_h, var_h, gk + n * K, dgk + n * K,
+                               dkx + bh * N * dr + n * dr, pmu + bh * KD, pvar + bh * KD, plogp + bh * K);
+        }
+        free(gq); free(gk); free(dgq); free(dgk); free(gg); free(hh); free(st); free(z);
+    }
+    if (rc) goto done;
+    /* parameter gradients: partials added over b in order, then the reparameterisations */
+    for (int64_t h = 0; h < H; ++h) {
+        for (int64_t e = 0; e < KD; ++e) {
+            double sm = 0.0, sv = 0.0;
+            for (int64_t b = 0; b < B; ++b) {
+                sm += pmu[(b * H + h) * KD + e];
+                sv += pvar[(b * H + h) * KD + e];
+            }
+            const double r = raw_var[h * KD + e];
+            dmu[h * KD + e] = sm;
+            draw_var[h * KD + e] = sv / (1.0 + exp(-r));   /* softplus'(r) = sigmoid(r) */
+        }
+        double tot = 0.0;
+        double* gsum = dprior_logits + h * K;
+        for (int k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t b = 0; b < B; ++b) s += plogp[(b * H + h) * K + k];
+            gsum[k] = s;
+            tot += s;
+        }
+        for (int k = 0; k < K; ++k) gsum[k] -= exp(logp[h * K + k]) * tot;
+    }
+done:
+    free(var); free(logp); free(logdet); free(pmu); free(pvar); free(plogp);
+    return rc;
 }

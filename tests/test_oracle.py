@@ -468,3 +468,116 @@ def test_stats_single_component_and_separated_clusters(oracle_mod):
     np.testing.assert_allclose(u[0, 0], [10, 20, 30], atol=1e-9)
     p = np.array([10, 20, 30]) / 60
     assert e[0, 0] == pytest.approx(float(-(p * np.log(p)).sum()), rel=1e-9)
+
+
+# ----------------------------------------------------------------------------- backward
+# The gradient of the mixer (the pages train it end to end, item 3) is pinned by central finite
+# differences of the forward oracle, by reverse-mode automatic differentiation of an independent
+# formulation (torch.distributions log-densities, materialised affinity), and by closed forms.
+
+def _bwd_case(seed, B, H, N, dr, K, dv):
+    rng = np.random.default_rng(seed)
+    mu, rv, pl = rand_params(rng, H, K, dr)
+    qx = rng.normal(0.0, 1.0, (B, H, N, dr))
+    kx = rng.normal(0.0, 1.0, (B, H, N, dr))
+    v = rng.normal(0.0, 1.0, (B, H, N, dv))
+    do = rng.normal(0.0, 1.0, (B, H, N, dv))
+    # shrink the routing inputs so that the posteriors are far from one-hot and every term matters
+    return dict(qx=0.4 * qx, kx=0.4 * kx, v=v, mu=0.4 * mu, raw_var=rv, prior_logits=pl), do
+
+
+_GRAD_OF = {"qx": "dqx", "kx": "dkx", "v": "dv", "mu": "dmu", "raw_var": "draw_var",
+            "prior_logits": "dprior_logits"}
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_finite_differences(oracle_mod, causal):
+    ins, do = _bwd_case(11, 2, 2, 7, 3, 4, 5)
+    eps = 0.05
+    g = oracle_mod.backward(**ins, dout=do, eps=eps, causal=causal)
+
+    def loss(d):
+        return float((oracle_mod.forward(**d, eps=eps, causal=causal) * do).sum())
+
+    step = 1e-5
+    for name, gname in _GRAD_OF.items():
+        x = ins[name]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            d = dict(ins)
+            xp = x.copy(); xp[idx] += step
+            xm = x.copy(); xm[idx] -= step
+            d[name] = xp
+            lp = loss(d)
+            d[name] = xm
+            fd[idx] = (lp - loss(d)) / (2 * step)
+        err = np.abs(fd - g[gname]).max()
+        assert err <= 1e-7 * max(1.0, np.abs(fd).max()), (name, err)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_autograd_of_materialised_affinity(oracle_mod, causal):
+    torch = pytest.importorskip("torch")
+    ins, do = _bwd_case(12, 2, 3, 19, 4, 5, 3)
+    eps = 1e-3
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in ins.items()}
+    var = torch.nn.functional.softplus(t["raw_var"])                       # [H, K, dr]
+    logpi = torch.log_softmax(t["prior_logits"], dim=-1)                   # [H, K]
+    dist = torch.distributions.Normal(t["mu"][None, :, None], var.sqrt()[None, :, None])
+
+    def gamma(x):                                                          # x [B, H, N, dr]
+        lp = dist.log_prob(x[:, :, :, None, :]).sum(-1) + logpi[None, :, None, :]
+        return torch.softmax(lp, dim=-1)
+
+    A = gamma(t["qx"]) @ gamma(t["kx"]).transpose(-1, -2)
+    if causal:
+        A = torch.tril(A)
+    O = (A @ t["v"]) / (A.sum(-1, keepdim=True) + eps)
+    grads = torch.autograd.grad((O * torch.tensor(do)).sum(), [t[k] for k in _GRAD_OF])
+    g = oracle_mod.backward(**ins, dout=do, eps=eps, causal=causal)
+    for (name, gname), ref in zip(_GRAD_OF.items(), grads):
+        ref = ref.numpy()
+        assert np.allclose(g[gname], ref, rtol=1e-9, atol=1e-11 * max(1.0, np.abs(ref).max())), name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_single_component_closed_form(oracle_mod, causal):
+    # K = 1: gamma == 1, so every routing and mixture gradient vanishes, and O is a (prefix) mean:
+    # bidirectional O_n = sum_j v_j / (N + eps), causal O_i = sum_{j <= i} v_j / (i + 1 + eps)
+    ins, do = _bwd_case(13, 1, 2, 9, 3, 1, 4)
+    eps = 0.25
+    g = oracle_mod.backward(**ins, dout=do, eps=eps, causal=causal)
+    for name in ("dqx", "dkx", "dmu", "draw_var", "dprior_logits"):
+        assert np.abs(g[name]).max() == 0.0, name
+    N = 9
+    if causal:
+        w = np.array([1.0 / (i + 1 + eps) for i in range(N)])
+        ref = np.flip(np.cumsum(np.flip(do * w[None, None, :, None], axis=2), axis=2), axis=2)
+    else:
+        ref = np.broadcast_to(do.sum(axis=2, keepdims=True) / (N + eps), do.shape)
+    assert np.allclose(g["dv"], ref, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_structure(oracle_mod, causal):
+    ins, do = _bwd_case(14, 2, 2, 16, 3, 4, 3)
+    g = oracle_mod.backward(**ins, dout=do, eps=1e-2, causal=causal)
+    # the priors enter through a softmax: its gradient sums to zero over the components
+    assert np.abs(g["dprior_logits"].sum(axis=-1)).max() < 1e-12 * max(1.0, np.abs(g["dprior_logits"]).max())
+    # O is linear in V and the loss is linear in dO: dv does not depend on V, and every gradient
+    # scales with dO
+    ins2 = dict(ins, v=3.0 * ins["v"] - 1.0)
+    assert np.allclose(oracle_mod.backward(**ins2, dout=do, eps=1e-2, causal=causal)["dv"], g["dv"],
+                       rtol=1e-12, atol=1e-14)
+    g3 = oracle_mod.backward(**ins, dout=-2.5 * do, eps=1e-2, causal=causal)
+    for name in _GRAD_OF.values():
+        assert np.allclose(g3[name], -2.5 * g[name], rtol=1e-12, atol=1e-14), name
+    if causal:
+        # a key j reaches the loss only through queries i >= j: with dO zero from row m on, the
+        # rows >= m of dv, dkx (and dqx, through their own queries) vanish exactly
+        m = 10
+        do2 = do.copy(); do2[:, :, m:] = 0.0
+        g2 = oracle_mod.backward(**ins, dout=do2, eps=1e-2, causal=True)
+        assert np.abs(g2["dv"][:, :, m:]).max() == 0.0
+        assert np.abs(g2["dkx"][:, :, m:]).max() == 0.0
+        assert np.abs(g2["dqx"][:, :, m:]).max() == 0.0
