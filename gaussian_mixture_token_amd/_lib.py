@@ -14,6 +14,8 @@ GMA_OP_FORWARD_BIDIR = 1
 GMA_OP_FORWARD_CAUSAL = 2
 GMA_OP_FORWARD_CAUSAL_STATE = 3
 GMA_OP_RESPONSIBILITY_STATS = 4
+GMA_OP_BACKWARD_BIDIR = 5
+GMA_OP_BACKWARD_CAUSAL = 6
 STATUS = {0: "GMA_SUCCESS", 1: "GMA_ERROR_INVALID_VALUE", 2: "GMA_ERROR_NOT_SUPPORTED",
           3: "GMA_ERROR_WORKSPACE_TOO_SMALL", 4: "GMA_ERROR_LAUNCH"}
 
@@ -47,6 +49,8 @@ _SIGS = [
     ("gma_decode_step", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     ("gma_forward_causal_state", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                 ctypes.c_size_t, _VP]),
+    ("gma_backward_bidir", ctypes.c_int, [ctypes.POINTER(Problem)] + [_VP] * 14 + [ctypes.c_size_t, _VP]),
+    ("gma_backward_causal", ctypes.c_int, [ctypes.POINTER(Problem)] + [_VP] * 14 + [ctypes.c_size_t, _VP]),
     ("gma_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("gma_last_error", ctypes.c_char_p, []),
     ("gma_timing_enable", ctypes.c_int, [ctypes.c_int]),

@@ -14,7 +14,7 @@ import torch
 from . import _lib
 
 __all__ = ["problem", "workspace_size", "responsibilities", "forward_bidir", "forward_causal",
-           "forward", "GmaError"]
+           "forward", "backward", "decode_step", "responsibility_stats", "GmaError"]
 
 GmaError = _lib.GmaError
 
@@ -213,3 +213,38 @@ def responsibility_stats(x, mu, raw_var, prior_logits, workspace=None):
                                                     _ptr(prior_logits), _ptr(usage), _ptr(hard), _ptr(ent), _ptr(ws),
                                                     ws.numel() * ws.element_size(), _stream(dev)))
     return usage, hard, ent
+
+
+def backward(qx, kx, v, mu, raw_var, prior_logits, dout, eps: float = 1e-6, causal: bool = False, workspace=None,
+             grads=None):
+    """Gradients of a loss through the bidirectional or causal forward, given dout = dL/dO [B, H, N, d_v]:
+    a dict with dqx, dkx [B, H, N, d_r] and dv [B, H, N, d_v] in the input dtype, and dmu, draw_var
+    [H, K, d_r], dprior_logits [H, K] fp32.  ``grads`` may supply that dict's tensors to write into."""
+    B, H, N, d_r = qx.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    if tuple(kx.shape) != (B, H, N, d_r) or tuple(v.shape[:3]) != (B, H, N) or tuple(dout.shape) != tuple(v.shape):
+        raise ValueError("qx, kx must be [B, H, N, d_r] and v, dout [B, H, N, d_v]")
+    if not (qx.dtype == kx.dtype == v.dtype == dout.dtype):
+        raise TypeError("qx, kx, v and dout must share one dtype")
+    _params(mu, raw_var, prior_logits, H, K, d_r)
+    dev = _check_gpu(qx, kx, v, dout, mu, raw_var, prior_logits)
+    prob = problem(B, H, N, d_r, K, d_v, qx.dtype, eps)
+    if grads is None:
+        grads = {"dqx": torch.empty_like(qx), "dkx": torch.empty_like(kx), "dv": torch.empty_like(v),
+                 "dmu": torch.empty_like(mu), "draw_var": torch.empty_like(raw_var),
+                 "dprior_logits": torch.empty_like(prior_logits)}
+    like = {"dqx": qx, "dkx": kx, "dv": v, "dmu": mu, "draw_var": raw_var, "dprior_logits": prior_logits}
+    for name, ref in like.items():
+        t = grads[name]
+        if t.dtype != ref.dtype or t.shape != ref.shape:
+            raise ValueError("%s must match its input's dtype and shape" % name)
+        _check_gpu(t)
+    op = _lib.GMA_OP_BACKWARD_CAUSAL if causal else _lib.GMA_OP_BACKWARD_BIDIR
+    ws = _workspace(workspace_size(prob, op), dev, workspace)
+    fn = _lib.load().gma_backward_causal if causal else _lib.load().gma_backward_bidir
+    _lib.check(fn(ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu), _ptr(raw_var), _ptr(prior_logits),
+                  _ptr(dout), _ptr(grads["dqx"]), _ptr(grads["dkx"]), _ptr(grads["dv"]), _ptr(grads["dmu"]),
+                  _ptr(grads["draw_var"]), _ptr(grads["dprior_logits"]), _ptr(ws), ws.numel() * ws.element_size(),
+                  _stream(dev)))
+    return grads

@@ -1,0 +1,69 @@
+// Backward of the mixer: argument blocks and launchers of the kernels in gma_backward.hip, driven
+// by the host library (gma_host.cpp), which owns validation, the workspace layout and timing.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace gma {
+
+// Batched fp32 matrix product on the matrix cores (v_mfma_f32_16x16x4_f32):
+//   C[b] = alpha op(A[b]) op(B[b]) (+ beta Cin[b]),  op(A) M x Kd, op(B) Kd x N, C M x N.
+// ta: A is stored Kd x M (op(A) = A^T), else M x Kd; tb: B is stored N x Kd, else Kd x N; rows of
+// every matrix are lda / ldb / ldc elements apart.  Batch b = outer * n_inner + inner; operand X
+// of batch b starts at X + outer * sX0 + inner * sX1 elements (B: outer taken modulo modB when
+// modB > 0).  Token axes: the bits of tok_flags mark M (1), N (2), Kd (4) as counting tokens of
+// the sequence; for batch b such an axis holds min(size, ntok - inner * tok_step) entries (the
+// ragged last chunk), and operand entries past it are read as zero and never stored.
+// tril: entry (i, j) of the product is kept only for j <= i (chunk-local token indices).
+// Cin (fp32, may be null) uses C's strides.  C is fp32, or bf16 with out_bf16.
+struct BwdGemm {
+    const float* A = nullptr;
+    const float* B = nullptr;
+    const float* Cin = nullptr;
+    void* C = nullptr;
+    int64_t sA0 = 0, sA1 = 0, sB0 = 0, sB1 = 0, sC0 = 0, sC1 = 0;
+    int64_t modB = 0;
+    int lda = 0, ldb = 0, ldc = 0;
+    int M = 0, N = 0, Kd = 0;
+    int n_inner = 1;
+    int64_t n_outer = 1;
+    int64_t ntok = 0;
+    int tok_step = 0;
+    int tok_flags = 0;
+    float alpha = 1.f, beta = 0.f;
+    int tril = 0;
+};
+void launch_bwd_gemm(const BwdGemm& g, bool ta, bool tb, bool out_bf16, hipStream_t s);
+
+// Mixture constants for the gradient: mw [H, K, 2 d_r] (row k: mu_kd / s_kd for d < d_r, then
+// 1 / s_kd), cp [H, K] = log pi_k - 1/2 sum_d log s_kd (s = softplus(raw_var)).
+void launch_bwd_prep(const float* mu, const float* raw_var, const float* prior, float* mw, float* cp, int H, int K,
+                     int d_r, hipStream_t s);
+
+// Responsibilities of rows x [BH, N, d_r] (bf16 or fp32) in fp32, from the direct form of the
+// log-density: gamma [BH, N, K].
+void launch_bwd_gamma(const void* x, bool f32, const float* mu, const float* mw, const float* cp, float* gamma,
+                      int64_t BH, int64_t N, int H, int K, int d_r, hipStream_t s);
+
+// [V | 1 | 0...] rows of width dva (fp32) from v [rows, d_v].
+void launch_bwd_vaug(const void* v, bool f32, float* vaug, int64_t rows, int d_v, int dva, hipStream_t s);
+// [x | x^2 | 1 | 0...] rows of width dxa (fp32) from x [rows, d_r].
+void launch_bwd_xaug(const void* x, bool f32, float* xaug, int64_t rows, int d_r, int dxa, hipStream_t s);
+// Read-phase gradient per row: p [rows, dva] holds (num | Gamma_Q . Z, the denominator without
+// eps); gh [rows, dva] <- (g = dO / den | h = -(dO . O) / den | 0...).
+void launch_bwd_gh(const float* p, const void* dout, bool f32, float* gh, int64_t rows, int d_v, int dva, float eps,
+                   hipStream_t s);
+// Softmax gradient in place: dl = gamma (dgamma - gamma . dgamma) per row of K.
+void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream_t s);
+// Routing-input gradient: dx = p12[:, :d_r] - x * p12[:, d_r:] (dx in the storage dtype).
+void launch_bwd_dx(const void* x, const float* p12, void* dx, bool f32, int64_t rows, int d_r, hipStream_t s);
+// Chunk-state scans over [n_outer][n][rec]: mode 0 exclusive prefix in place, 1 exclusive suffix in
+// place, 2 the total into entry 0.
+void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mode, hipStream_t s);
+// Mixture-parameter gradients from the partial sums gp [parts][K][dxa] (parts = 2 sides x B x
+// n_seg per head; columns x | x^2 | 1 of dl^T [x | x^2 | 1]).
+void launch_bwd_param(const float* gp, const float* mu, const float* raw_var, const float* prior, float* dmu,
+                      float* draw_var, float* dprior, int64_t B, int H, int K, int d_r, int dxa, int64_t n_seg,
+                      hipStream_t s);
+
+}  // namespace gma

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "gma.h"
+#include "gma_backward.hpp"
 #include "gma_decode.hpp"
 #include "gma_registry.hpp"
 
@@ -44,9 +45,14 @@ int next_pow2(int x) {
     return p;
 }
 
-enum KernelId { K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_STATS, K_COUNT };
+enum KernelId {
+    K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_STATS,
+    K_BWD_GAMMA, K_BWD_GEMM, K_BWD_ROWS, K_BWD_SCAN, K_BWD_PARAM, K_COUNT
+};
 const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan", "causal_output", "bidir_output",
-                                     "responsibilities", "state_convert", "decode_step", "responsibility_stats"};
+                                     "responsibilities", "state_convert", "decode_step", "responsibility_stats",
+                                     "backward_responsibilities", "backward_products", "backward_rows",
+                                     "backward_scan", "backward_parameters"};
 
 struct Plan {
     const ShapeClass* cls = nullptr;
@@ -78,10 +84,9 @@ const ShapeClass* find_class(bool f32, int kc, int vc, int drc) {
 // Validates sizes (pure host) and fills the plan for the register-staged kernels or, with tok, for
 // the token-split LDS-DMA kernels (chunks of kTokChunk tokens; with tiles, the causal pair through
 // stored Gamma_K tiles where it applies).  No HIP call.
-gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = false, bool tiles = true) {
+// Sizes, dtype and eps of a problem (pure host).
+gma_status_t validate_problem(const gma_problem_t* p) {
     if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
-    if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_RESPONSIBILITY_STATS)
-        return fail(GMA_ERROR_INVALID_VALUE, "unknown op %d", op);
     if (p->batch < 1 || p->heads < 1 || p->seq_len < 1)
         return fail(GMA_ERROR_INVALID_VALUE, "batch, heads and seq_len must be >= 1 (got %lld, %lld, %lld)",
                     (long long)p->batch, (long long)p->heads, (long long)p->seq_len);
@@ -99,6 +104,15 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
         return fail(GMA_ERROR_INVALID_VALUE, "tensor sizes overflow");
     if (p->batch * p->heads > INT32_MAX / 2)
         return fail(GMA_ERROR_NOT_SUPPORTED, "batch * heads too large");
+    return GMA_SUCCESS;
+}
+
+gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = false, bool tiles = true) {
+    if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
+    if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_RESPONSIBILITY_STATS)
+        return fail(GMA_ERROR_INVALID_VALUE, "unknown op %d", op);
+    gma_status_t vs = validate_problem(p);
+    if (vs != GMA_SUCCESS) return vs;
 
     plan->f32 = p->dtype == GMA_DTYPE_F32;
     plan->B = p->batch;
@@ -181,9 +195,91 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     return GMA_SUCCESS;
 }
 
+// Backward workspace: fp32 intermediates of the gradient, each region 256-byte aligned.
+//   mw [H, K, 2 d_r], cp [H, K]               mixture constants (mu / s | 1 / s; log pi - 1/2 sum log s)
+//   gq, gk, dgq, dgk [BH, N, K]               responsibilities and their gradients (then dl)
+//   va, gh, pp [BH, N, dva]                   [V | 1], [g | h], [num | Gamma_Q . Z]  (dva = d_v + 1 rounded
+//                                             up to a multiple of 4, zero padded)
+//   st, rt [BH, n_st, K, dva]                 states per chunk (causal) or segment (bidirectional):
+//                                             Gamma_K^T [V | 1] -> prefix, Gamma_Q^T [g | h] -> suffix
+//   ac, mt [BH, n_st, C, C] (causal)          tril(Gamma_Q Gamma_K^T), tril([g | h] [V | 1]^T) per chunk
+//   dvt [BH, N, d_v] (causal)                 intra-chunk part of dV
+//   p12 [BH, N, 2 d_r], xa [BH, N, dxa]       dl [mu / s | 1 / s], [x | x^2 | 1] (dxa = 2 d_r + 1 rounded up)
+//   gp [2, BH, n_sg, K, dxa]                  per-segment dl^T [x | x^2 | 1] of both sides
+constexpr int kBwdChunk = 64;    // causal chunk (tokens)
+constexpr int kBwdSeg = 1024;    // bidirectional state segments and parameter-partial segments (tokens)
+
+struct BwdPlan {
+    int64_t B = 0, H = 0, N = 0, BH = 0;
+    int d_r = 0, K = 0, d_v = 0, dva = 0, dxa = 0;
+    bool f32 = false, causal = false;
+    float eps = 0.f;
+    int st_step = 0;            // tokens per state entry
+    int64_t n_st = 0, n_sg = 0;  // state entries and parameter segments per (batch, head)
+    size_t off_mw = 0, off_cp = 0, off_gq = 0, off_gk = 0, off_dgq = 0, off_dgk = 0, off_va = 0, off_gh = 0,
+           off_pp = 0, off_st = 0, off_rt = 0, off_ac = 0, off_mt = 0, off_dvt = 0, off_p12 = 0, off_xa = 0,
+           off_gp = 0, total = 0;
+};
+
+gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
+    gma_status_t vs = validate_problem(p);
+    if (vs != GMA_SUCCESS) return vs;
+    b->B = p->batch;
+    b->H = p->heads;
+    b->N = p->seq_len;
+    b->BH = b->B * b->H;
+    b->d_r = p->d_route;
+    b->K = p->n_comp;
+    b->d_v = p->d_value;
+    b->dva = (p->d_value + 1 + 3) / 4 * 4;
+    b->dxa = (2 * p->d_route + 1 + 3) / 4 * 4;
+    b->f32 = p->dtype == GMA_DTYPE_F32;
+    b->causal = causal;
+    b->eps = p->eps;
+    b->st_step = causal ? kBwdChunk : kBwdSeg;
+    b->n_st = (b->N + b->st_step - 1) / b->st_step;
+    b->n_sg = (b->N + kBwdSeg - 1) / kBwdSeg;
+    const int64_t rows = b->BH * b->N;
+    const int64_t rec = (int64_t)b->K * b->dva;
+    // one product's grid: tiles x batches must fit a 32-bit launch
+    const int64_t widest = std::max<int64_t>(std::max<int64_t>(b->K, b->dva), std::max<int64_t>(2 * b->d_r, b->dxa));
+    if (b->BH * std::max(b->n_st, b->n_sg) * ((kBwdSeg + 63) / 64) * ((widest + 63) / 64) > INT32_MAX ||
+        rows * std::max<int64_t>(b->dxa, b->dva) / 256 > INT32_MAX)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "problem too large for the backward grids");
+    const int64_t C = b->st_step;
+    size_t off = 0;
+    auto take = [&](size_t* o, int64_t floats) {
+        *o = off;
+        off = align_up(off + (size_t)floats * sizeof(float), 256);
+    };
+    take(&b->off_mw, b->H * b->K * 2 * b->d_r);
+    take(&b->off_cp, b->H * b->K);
+    take(&b->off_gq, rows * b->K);
+    take(&b->off_gk, rows * b->K);
+    take(&b->off_dgq, rows * b->K);
+    take(&b->off_dgk, rows * b->K);
+    take(&b->off_va, rows * b->dva);
+    take(&b->off_gh, rows * b->dva);
+    take(&b->off_pp, rows * b->dva);
+    take(&b->off_st, b->BH * b->n_st * rec);
+    take(&b->off_rt, b->BH * b->n_st * rec);
+    take(&b->off_ac, causal ? b->BH * b->n_st * C * C : 0);
+    take(&b->off_mt, causal ? b->BH * b->n_st * C * C : 0);
+    take(&b->off_dvt, causal ? rows * b->d_v : 0);
+    take(&b->off_p12, rows * 2 * b->d_r);
+    take(&b->off_xa, rows * b->dxa);
+    take(&b->off_gp, 2 * b->BH * b->n_sg * b->K * b->dxa);
+    b->total = off;
+    return GMA_SUCCESS;
+}
+
 // Workspace bytes advertised for (problem, op): the register-staged plan or the token-split plan,
 // whichever is larger (which one runs is decided per call from pointer alignment).  0 if invalid.
 size_t advertised_workspace(const gma_problem_t* problem, int op) {
+    if (op == GMA_OP_BACKWARD_BIDIR || op == GMA_OP_BACKWARD_CAUSAL) {
+        BwdPlan b;
+        return make_bwd_plan(problem, op == GMA_OP_BACKWARD_CAUSAL, &b) == GMA_SUCCESS ? b.total : 0;
+    }
     Plan pl;
     if (make_plan(problem, op, &pl) != GMA_SUCCESS) return 0;
     size_t total = pl.total;
@@ -632,6 +728,156 @@ gma_status_t forward_bidir_kv(const gma_problem_t* p, int64_t n_kv, const void* 
     return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, (int)(BH * plq.P), s); });
 }
 
+// Backward (see gma_backward.hip for the formulas): all intermediates fp32 in the workspace.
+gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const void* kx, const void* v,
+                      const float* mu, const float* rv, const float* pr, const void* dout, void* dqx, void* dkx,
+                      void* dv, float* dmu, float* drv, float* dpr, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    BwdPlan b;
+    gma_status_t st = make_bwd_plan(p, causal, &b);
+    if (st != GMA_SUCCESS) return st;
+    const void* ptrs[] = {qx, kx, v, mu, rv, pr, dout, dqx, dkx, dv, dmu, drv, dpr};
+    for (int i = 0; i < 13; ++i)
+        if (!ptrs[i]) return fail(GMA_ERROR_INVALID_VALUE, "pointer argument %d is NULL", i);
+    if (ws_bytes < b.total)
+        return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                    ws_bytes, b.total);
+    if (!ws) return fail(GMA_ERROR_INVALID_VALUE, "workspace is NULL");
+    if (misaligned(ws, 16)) return fail(GMA_ERROR_INVALID_VALUE, "workspace must be 16-byte aligned");
+    const size_t es = b.f32 ? 4 : 2;
+    for (const void* ptr : {qx, kx, v, dout, (const void*)dqx, (const void*)dkx, (const void*)dv})
+        if (misaligned(ptr, es)) return fail(GMA_ERROR_INVALID_VALUE, "tensor pointers must be %zu-byte aligned", es);
+    for (const void* ptr : {(const void*)mu, (const void*)rv, (const void*)pr, (const void*)dmu, (const void*)drv,
+                            (const void*)dpr})
+        if (misaligned(ptr, 4)) return fail(GMA_ERROR_INVALID_VALUE, "parameter pointers must be 4-byte aligned");
+    const size_t nx = (size_t)(b.BH * b.N) * b.d_r * es, nv = (size_t)(b.BH * b.N) * b.d_v * es;
+    const size_t np = (size_t)(b.H * b.K) * b.d_r * 4, nk = (size_t)(b.H * b.K) * 4;
+    const void* ins[] = {qx, kx, v, dout, mu, rv, pr, ws};
+    const size_t insz[] = {nx, nx, nv, nv, np, np, nk, b.total};
+    const void* outs[] = {dqx, dkx, dv, dmu, drv, dpr};
+    const size_t osz[] = {nx, nx, nv, np, np, nk};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 8; ++j)
+            if (overlaps(outs[i], osz[i], ins[j], insz[j]))
+                return fail(GMA_ERROR_INVALID_VALUE, "gradients must not overlap the inputs or the workspace");
+        for (int j = 0; j < i; ++j)
+            if (overlaps(outs[i], osz[i], outs[j], osz[j]))
+                return fail(GMA_ERROR_INVALID_VALUE, "gradients must not overlap each other");
+    }
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* w = reinterpret_cast<char*>(ws);
+    auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+    float *mw = F(b.off_mw), *cp = F(b.off_cp), *gq = F(b.off_gq), *gk = F(b.off_gk), *dgq = F(b.off_dgq),
+          *dgk = F(b.off_dgk), *va = F(b.off_va), *gh = F(b.off_gh), *pp = F(b.off_pp), *stt = F(b.off_st),
+          *rt = F(b.off_rt), *ac = F(b.off_ac), *mt = F(b.off_mt), *dvt = F(b.off_dvt), *p12 = F(b.off_p12),
+          *xa = F(b.off_xa), *gp = F(b.off_gp);
+    const int64_t BH = b.BH, N = b.N, rows = BH * N, rec = (int64_t)b.K * b.dva;
+    const int K = b.K, d_r = b.d_r, d_v = b.d_v, dva = b.dva, dxa = b.dxa, H = (int)b.H;
+    const int C = b.st_step;
+    const bool f32 = b.f32;
+
+    // operand views: token rows of width wd per state entry (tok) or per parameter segment (seg); the
+    // states of every entry (all_st) or the one each entry reads (cur_st: its own prefix / suffix when
+    // causal, the total in entry 0 when bidirectional); per-chunk C x C blocks (sq)
+    struct View { const float* p; int64_t s0, s1; int ld; int64_t mod; };
+    auto tok = [&](const float* ptr, int wd) { return View{ptr, N * wd, (int64_t)C * wd, wd, 0}; };
+    auto seg = [&](const float* ptr, int wd) { return View{ptr, N * wd, (int64_t)kBwdSeg * wd, wd, 0}; };
+    auto all_st = [&](const float* ptr) { return View{ptr, b.n_st * rec, rec, dva, 0}; };
+    auto cur_st = [&](const float* ptr) { return View{ptr, b.n_st * rec, causal ? rec : 0, dva, 0}; };
+    auto sq = [&](const float* ptr) { return View{ptr, b.n_st * C * C, (int64_t)C * C, C, 0}; };
+    auto gemm = [&](View A, bool ta, View Bv, bool tb, View Cv, void* out, bool out_bf16, int M, int Nn, int Kd,
+                    int tokf, int tril, const float* cin, bool per_seg) -> gma_status_t {
+        BwdGemm g;
+        g.A = A.p;
+        g.sA0 = A.s0;
+        g.sA1 = A.s1;
+        g.lda = A.ld;
+        g.B = Bv.p;
+        g.sB0 = Bv.s0;
+        g.sB1 = Bv.s1;
+        g.ldb = Bv.ld;
+        g.modB = Bv.mod;
+        g.C = out;
+        g.sC0 = Cv.s0;
+        g.sC1 = Cv.s1;
+        g.ldc = Cv.ld;
+        g.Cin = cin;
+        g.beta = cin ? 1.f : 0.f;
+        g.M = M;
+        g.N = Nn;
+        g.Kd = Kd;
+        g.n_outer = BH;
+        g.n_inner = (int)(per_seg ? b.n_sg : b.n_st);
+        g.ntok = N;
+        g.tok_step = per_seg ? kBwdSeg : C;
+        g.tok_flags = tokf;
+        g.tril = tril;
+        return timed_launch(K_BWD_GEMM, s, [&] { launch_bwd_gemm(g, ta, tb, out_bf16, s); });
+    };
+#define GMA_TRY(x)                        \
+    do {                                  \
+        st = (x);                         \
+        if (st != GMA_SUCCESS) return st; \
+    } while (0)
+    constexpr int TM = 1, TN = 2, TK = 4;   // token axes of a product
+
+    // mixture constants, responsibilities of both sides, [V | 1]
+    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_prep(mu, rv, pr, mw, cp, H, K, d_r, s); }));
+    GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] { launch_bwd_gamma(qx, f32, mu, mw, cp, gq, BH, N, H, K, d_r, s); }));
+    GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] { launch_bwd_gamma(kx, f32, mu, mw, cp, gk, BH, N, H, K, d_r, s); }));
+    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_vaug(v, f32, va, rows, d_v, dva, s); }));
+    // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
+    GMA_TRY(gemm(tok(gk, K), true, tok(va, dva), false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false));
+    GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, causal ? 0 : 2, s); }));
+    // read phase: [num | Gamma_Q . Z] = Gamma_Q state (+ tril(Gamma_Q Gamma_K^T) [V | 1]), then g, h
+    GMA_TRY(gemm(tok(gq, K), false, cur_st(stt), false, tok(pp, dva), pp, false, C, dva, K, TM, 0, nullptr, false));
+    if (causal) {
+        GMA_TRY(gemm(tok(gq, K), false, tok(gk, K), true, sq(ac), ac, false, C, C, K, TM | TN, 1, nullptr, false));
+        GMA_TRY(gemm(sq(ac), false, tok(va, dva), false, tok(pp, dva), pp, false, C, dva, C, TM | TK, 0, pp, false));
+    }
+    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_gh(pp, dout, f32, gh, rows, d_v, dva, b.eps, s); }));
+    // Gamma_Q^T [g | h] per entry -> the sums over the later chunks / the total
+    GMA_TRY(gemm(tok(gq, K), true, tok(gh, dva), false, all_st(rt), rt, false, K, dva, C, TK, 0, nullptr, false));
+    GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(rt, BH, b.n_st, rec, causal ? 1 : 2, s); }));
+    // dGamma_Q = [g | h] state^T (+ tril([g | h] [V | 1]^T) Gamma_K)
+    GMA_TRY(gemm(tok(gh, dva), false, cur_st(stt), true, tok(dgq, K), dgq, false, C, K, dva, TM, 0, nullptr, false));
+    if (causal) {
+        GMA_TRY(gemm(tok(gh, dva), false, tok(va, dva), true, sq(mt), mt, false, C, C, dva, TM | TN, 1, nullptr, false));
+        GMA_TRY(gemm(sq(mt), false, tok(gk, K), false, tok(dgq, K), dgq, false, C, K, C, TM | TK, 0, dgq, false));
+    }
+    // dGamma_K = [V | 1] R^T (+ the same intra-chunk block transposed, times Gamma_Q)
+    GMA_TRY(gemm(tok(va, dva), false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false));
+    if (causal)
+        GMA_TRY(gemm(sq(mt), true, tok(gq, K), false, tok(dgk, K), dgk, false, C, K, C, TM | TK, 0, dgk, false));
+    // dV = Gamma_K R (+ tril(Gamma_Q Gamma_K^T)^T g), in the storage dtype
+    if (causal)
+        GMA_TRY(gemm(sq(ac), true, tok(gh, dva), false, tok(dvt, d_v), dvt, false, C, d_v, C, TM | TK, 0, nullptr,
+                     false));
+    GMA_TRY(gemm(tok(gk, K), false, cur_st(rt), false, tok(nullptr, d_v), dv, !f32, C, d_v, K, TM, 0,
+                 causal ? dvt : nullptr, false));
+    // posterior gradients, then per side the routing-input gradient and the parameter partials
+    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_dl(gq, dgq, rows, K, s); }));
+    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_dl(gk, dgk, rows, K, s); }));
+    for (int side = 0; side < 2; ++side) {
+        const void* x = side ? kx : qx;
+        const float* dl = side ? dgk : dgq;
+        void* dx = side ? dkx : dqx;
+        GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_xaug(x, f32, xa, rows, d_r, dxa, s); }));
+        const View mwv{mw, (int64_t)K * 2 * d_r, 0, 2 * d_r, H};
+        GMA_TRY(gemm(seg(dl, K), false, mwv, false, seg(p12, 2 * d_r), p12, false, kBwdSeg, 2 * d_r, K, TM, 0, nullptr,
+                     true));
+        GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_dx(x, p12, dx, f32, rows, d_r, s); }));
+        float* gps = gp + (size_t)side * BH * b.n_sg * K * dxa;
+        const View gpv{gps, b.n_sg * K * dxa, (int64_t)K * dxa, dxa, 0};
+        GMA_TRY(gemm(seg(dl, K), true, seg(xa, dxa), false, gpv, gps, false, K, dxa, kBwdSeg, TK, 0, nullptr, true));
+    }
+#undef GMA_TRY
+    return timed_launch(K_BWD_PARAM, s, [&] {
+        launch_bwd_param(gp, mu, rv, pr, dmu, drv, dpr, b.B, H, K, d_r, dxa, b.n_sg, s);
+    });
+}
+
 }  // namespace
 }  // namespace gma
 
@@ -815,6 +1061,22 @@ gma_status_t gma_forward_causal_state(const gma_problem_t* p, const void* qx, co
                                       void* stream) {
     return forward(p, GMA_OP_FORWARD_CAUSAL_STATE, qx, kx, v, mu, raw_var, prior_logits, state_in, state_out, o, ws,
                    ws_bytes, stream);
+}
+
+gma_status_t gma_backward_bidir(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,
+                                const float* raw_var, const float* prior_logits, const void* dout, void* dqx, void* dkx,
+                                void* dv, float* dmu, float* draw_var, float* dprior_logits, void* ws, size_t ws_bytes,
+                                void* stream) {
+    return backward(p, false, qx, kx, v, mu, raw_var, prior_logits, dout, dqx, dkx, dv, dmu, draw_var, dprior_logits,
+                    ws, ws_bytes, stream);
+}
+
+gma_status_t gma_backward_causal(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,
+                                 const float* raw_var, const float* prior_logits, const void* dout, void* dqx,
+                                 void* dkx, void* dv, float* dmu, float* draw_var, float* dprior_logits, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    return backward(p, true, qx, kx, v, mu, raw_var, prior_logits, dout, dqx, dkx, dv, dmu, draw_var, dprior_logits,
+                    ws, ws_bytes, stream);
 }
 
 const char* gma_status_string(gma_status_t s) {

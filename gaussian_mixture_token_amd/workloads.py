@@ -73,7 +73,7 @@ def workload(i: int, **overrides) -> Workload:
     return w.with_(**overrides) if overrides else w
 
 
-_TENSOR_IDS = {"mu": 1, "raw_var": 2, "prior_logits": 3, "qx": 4, "kx": 5, "v": 6}
+_TENSOR_IDS = {"mu": 1, "raw_var": 2, "prior_logits": 3, "qx": 4, "kx": 5, "v": 6, "dout": 7}
 
 
 def _generator(seed: int, tensor: str, b: int, h: int) -> torch.Generator:
@@ -128,4 +128,14 @@ def make_inputs(w: Workload, heads: Optional[Iterable[int]] = None) -> Dict[str,
             for k in ("qx", "kx", "v"):
                 out[k][b, j].copy_(hi[k])
     out.update(make_params(w, hs))
+    return out
+
+
+def make_dout(w: Workload, heads: Optional[Iterable[int]] = None) -> torch.Tensor:
+    """Upstream gradient dL/dO [B, H', N, d_v] for the backward pass: i.i.d. N(0, 1) in the storage dtype."""
+    hs = list(range(w.heads)) if heads is None else list(heads)
+    out = torch.empty(w.batch, len(hs), w.seq_len, w.d_value, dtype=w.torch_dtype)
+    for b in range(w.batch):
+        for j, h in enumerate(hs):
+            out[b, j].copy_(torch.randn(w.seq_len, w.d_value, generator=_generator(w.seed, "dout", b, h)))
     return out

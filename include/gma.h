@@ -1,6 +1,6 @@
 /*
- * gma.h -- C ABI of libgma.so, the MI355X (gfx950) forward pass of Gaussian Mixture
- * Attention (GMA).
+ * gma.h -- C ABI of libgma.so, the MI355X (gfx950) forward and backward passes of
+ * Gaussian Mixture Attention (GMA).
  *
  * The operation (page "Attention par Mélange Gaussien (GMA)", gist.science paper
  * 2606.18283, section "Méthodologie", sub-section "Mécanisme Central"):
@@ -65,7 +65,9 @@ typedef enum {
     GMA_OP_FORWARD_BIDIR = 1,
     GMA_OP_FORWARD_CAUSAL = 2,
     GMA_OP_FORWARD_CAUSAL_STATE = 3,
-    GMA_OP_RESPONSIBILITY_STATS = 4
+    GMA_OP_RESPONSIBILITY_STATS = 4,
+    GMA_OP_BACKWARD_BIDIR = 5,
+    GMA_OP_BACKWARD_CAUSAL = 6
 } gma_op_t;
 
 /* Problem sizes.  eps >= 0 and finite; it is added to each row's denominator Gamma_Q Z. */
@@ -164,6 +166,34 @@ gma_status_t gma_decode_step(const gma_problem_t* problem, const void* qx, const
                              void* o, void* stream);
 
 /* Static description of a status code. */
+/* Backward of the bidirectional (gma_backward_bidir) or causal (gma_backward_causal) forward above:
+ * the gradients of a scalar loss L with respect to every input, given dout = dL/dO [B, H, N, d_v].
+ * The pages train the layer end to end (item 3: softplus variances and softmax priors are the
+ * learned reparameterisation), so these are the chain rule through items 1-3:
+ *   read    g_i = dO_i / den_i, h_i = -(dO_i . O_i) / den_i, dGamma_Q[i] = Vt_i g_i + Z_i h_i
+ *   write   dGamma_K[j] = R_j v_j + r_j and dv_j = R_j^T gamma_K[j], with R_j, r_j the sums of
+ *           Gamma_Q[i] (x) g_i and Gamma_Q[i] h_i over the queries i that see key j
+ *   item 1  dl = gamma (dgamma - gamma . dgamma) per row; dx_d = sum_k dl_k (mu_kd - x_d) / s_kd
+ *   item 3  dmu, dsigma2 and dlog pi summed over the rows of both Q_X and K_X of every batch, then
+ *           draw_var = dsigma2 * sigmoid(raw_var), dprior_logits = G - pi sum_k G_k (G = dlog pi).
+ * Outputs (written, not accumulated): dqx, dkx [B, H, N, d_r] and dv [B, H, N, d_v] in the storage
+ * dtype; dmu, draw_var [H, K, d_r] and dprior_logits [H, K] fp32.  The forward is recomputed from the
+ * inputs (O is not an argument).  Every sum and product runs in fp32 on the fp32 matrix cores, also
+ * for bf16 storage (inputs are upcast exactly; outputs are rounded once).  Workspace:
+ * gma_workspace_size(problem, GMA_OP_BACKWARD_BIDIR or GMA_OP_BACKWARD_CAUSAL) bytes, about
+ * B * H * N * (6 K + 3 (d_v + 1) + 4 d_r) * 4 bytes plus per-chunk states.  No gradient may overlap an
+ * input, another gradient or the workspace. */
+gma_status_t gma_backward_bidir(const gma_problem_t* problem, const void* qx, const void* kx,
+                                const void* v, const float* mu, const float* raw_var,
+                                const float* prior_logits, const void* dout, void* dqx, void* dkx,
+                                void* dv, float* dmu, float* draw_var, float* dprior_logits,
+                                void* workspace, size_t workspace_bytes, void* stream);
+gma_status_t gma_backward_causal(const gma_problem_t* problem, const void* qx, const void* kx,
+                                 const void* v, const float* mu, const float* raw_var,
+                                 const float* prior_logits, const void* dout, void* dqx, void* dkx,
+                                 void* dv, float* dmu, float* draw_var, float* dprior_logits,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 const char* gma_status_string(gma_status_t status);
 
 /* Message of the last failing call on this thread ("" if none). */

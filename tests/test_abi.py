@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gma_responsibilities", "gma_forward_bidir", "gma_forward_causal", "gma_workspace_size",
-              "gma_status_string"):
+              "gma_backward_bidir", "gma_backward_causal", "gma_status_string"):
         assert n in names
 
 
@@ -226,3 +226,44 @@ def test_responsibility_stats_validation(lib):
     assert f(ctypes.byref(prob), x, FAKE, FAKE, FAKE, u, hc, e, ws, need - 1, None) == 3
     assert f(ctypes.byref(prob), x, FAKE, FAKE, FAKE, u, u, e, ws, need, None) == 1       # outputs overlap
     assert f(ctypes.byref(_prob(n_comp=300)), x, FAKE, FAKE, FAKE, u, hc, e, ws, need, None) == 2
+
+
+def _bwd(lib, fn, prob, ws_bytes=1 << 44, **override):
+    big = 1 << 36   # spacing that keeps the fake tensors of the 65536-token problem disjoint
+    args = dict(qx=1, kx=2, v=3, mu=4, rv=5, pl=6, do=7, dqx=8, dkx=9, dv=10, dmu=11, drv=12, dpl=13, ws=14)
+    vals = {k: ctypes.c_void_p(i * big) for k, i in args.items()}
+    for k, v in override.items():
+        vals[k] = v
+    order = ("qx", "kx", "v", "mu", "rv", "pl", "do", "dqx", "dkx", "dv", "dmu", "drv", "dpl", "ws")
+    a = [vals[k] for k in order]
+    return getattr(lib, fn)(ctypes.byref(prob), *a[:13], a[13], ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["gma_backward_bidir", "gma_backward_causal"])
+def test_backward_validation(lib, fn):
+    op = 6 if fn.endswith("causal") else 5
+    prob = _prob(seq_len=4096)
+    need = lib.gma_workspace_size(ctypes.byref(prob), op)
+    assert need > 0
+    for field, value, status in (("batch", 0, 1), ("eps", -1.0, 1), ("n_comp", 257, 2), ("dtype", 5, 1)):
+        assert _bwd(lib, fn, _prob(seq_len=4096, **{field: value})) == status
+        assert lib.gma_last_error()
+    for name in ("qx", "kx", "v", "mu", "rv", "pl", "do", "dqx", "dkx", "dv", "dmu", "drv", "dpl"):
+        assert _bwd(lib, fn, prob, **{name: None}) == 1, name
+    assert _bwd(lib, fn, prob, ws_bytes=need - 1) == 3
+    assert _bwd(lib, fn, prob, ws_bytes=need, ws=None) == 1
+    assert _bwd(lib, fn, prob, ws=ctypes.c_void_p((14 << 36) + 8)) == 1       # workspace not 16-byte aligned
+    assert _bwd(lib, fn, prob, dqx=ctypes.c_void_p((8 << 36) + 1)) == 1       # odd address for bf16
+    assert _bwd(lib, fn, prob, dmu=ctypes.c_void_p((11 << 36) + 2)) == 1      # fp32 parameter gradient misaligned
+    assert _bwd(lib, fn, prob, dv=ctypes.c_void_p(3 << 36)) == 1              # dv aliases v
+    assert _bwd(lib, fn, prob, dkx=ctypes.c_void_p(8 << 36)) == 1             # dkx aliases dqx
+    assert _bwd(lib, fn, prob, dpl=ctypes.c_void_p(14 << 36)) == 1            # gradient inside the workspace
+
+
+def test_backward_workspace_is_linear_in_the_sequence(lib):
+    # fp32 intermediates per token and per chunk state; nothing quadratic in N
+    for op in (5, 6):
+        a = _ws(lib, op, seq_len=1 << 14)
+        b = _ws(lib, op, seq_len=1 << 16)
+        assert a > 0 and 3.9 * a < b < 4.1 * a, (op, a, b)
+    assert _ws(lib, 5, seq_len=4096) < _ws(lib, 6, seq_len=4096)   # the causal chunk blocks

@@ -1,0 +1,156 @@
+"""GPU parity of the backward pass (gma_backward_bidir / gma_backward_causal) against the fp64 oracle.
+
+Tolerance per gradient tensor, the forward's contract carried over: max |g_gpu - g_ref| / max |g_ref|
+<= 1e-4 for fp32 storage and <= 1e-2 for bf16 storage.  The backward computes in fp32 throughout
+(inputs upcast exactly, fp32 matrix cores), so for bf16 the error is dominated by the one rounding
+of dqx, dkx and dv to bf16 (unit roundoff 2^-8).
+
+Inputs: the seeded workload generators (gaussian_mixture_token_amd.workloads) plus a seeded dL/dO.
+With d_r >= 64 and N(0, 1) routing inputs the posteriors are nearly one-hot, so the routing
+gradients are small; the "soft" cases scale Q_X and K_X by 1/4 (exact in bf16) so that every
+term of the softmax and log-density gradients is exercised.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.conftest import gpu_available
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+DEV = "cuda:0"
+NAMES = ("dqx", "dkx", "dv", "dmu", "draw_var", "dprior_logits")
+
+
+@pytest.fixture(scope="module")
+def gma():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import gaussian_mixture_token_amd as g
+    from gaussian_mixture_token_amd import _lib
+    _lib.load()
+    oracle.build(force=False)
+    return g
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def inputs(g, w, soft, heads=None):
+    inp = g.make_inputs(w, heads)
+    if soft:
+        inp["qx"] = inp["qx"] * 0.25
+        inp["kx"] = inp["kx"] * 0.25
+    return inp, g.make_dout(w, heads)
+
+
+def run_gpu(g, w, inp, dout, causal, **kw):
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    out = g.backward(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], dout.to(DEV), eps=w.eps,
+                     causal=causal, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(w, inp, dout, causal, got, only=NAMES):
+    ref = oracle.backward(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"], inp["prior_logits"], dout,
+                          eps=w.eps, causal=causal)
+    for name in only:
+        a = got[name].detach().float().cpu().numpy().astype(np.float64)
+        r = ref[name]
+        assert np.isfinite(a).all(), name
+        scale = np.abs(r).max()
+        err = float(np.abs(a - r).max() / scale) if scale > 0 else float(np.abs(a).max())
+        say("  %-14s rel-to-max %.3e (max |ref| %.3e)" % (name, err, scale))
+        assert err <= TOL[w.dtype], name
+
+
+@pytest.mark.parametrize("soft", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cfg,N", [(0, 256), (1, 700), (2, 1100), (3, 700), (4, 300)])
+def test_backward_matches_oracle(gma, cfg, N, causal, soft):
+    w = gma.workload(cfg)
+    w = w.with_(batch=min(w.batch, 2), heads=min(w.heads, 2), seq_len=N)
+    say("backward cfg%d causal=%s soft=%s %s" % (cfg, causal, soft, w))
+    inp, dout = inputs(gma, w, soft)
+    check(w, inp, dout, causal, run_gpu(gma, w, inp, dout, causal))
+
+
+@pytest.mark.parametrize("base", [0, 3])
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 1023, 1024, 1025])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_tails_and_tiny_lengths(gma, base, N, causal):
+    # eps = 0.05 here: with a row that sees a single key (N = 1, or row 0 of a causal pass) and
+    # eps -> 0, O = v a / (a + eps) and the routing gradient of that row is an O(eps) remainder of
+    # two nearly equal terms, which fp32 resolves only to about u / eps of its own size
+    w = gma.workload(base)
+    w = w.with_(batch=1, heads=min(w.heads, 2), seq_len=N, eps=0.05)
+    say("backward tails base=%d N=%d causal=%s" % (base, N, causal))
+    inp, dout = inputs(gma, w, True)
+    check(w, inp, dout, causal, run_gpu(gma, w, inp, dout, causal))
+
+
+@pytest.mark.parametrize("shape", [(5, 7, 6), (40, 1, 20), (3, 256, 2), (256, 16, 255), (130, 65, 129)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_odd_shapes(gma, shape, dtype, causal):
+    d_r, K, d_v = shape
+    w = gma.workload(0).with_(dtype=dtype, batch=2, heads=2, seq_len=150, d_route=d_r, n_comp=K, d_value=d_v)
+    say("backward shape=%s %s causal=%s" % (shape, dtype, causal))
+    inp, dout = inputs(gma, w, True)
+    check(w, inp, dout, causal, run_gpu(gma, w, inp, dout, causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_single_token_small_eps(gma, causal):
+    # the degenerate case above at eps = 1e-6: dv = (gamma_Q . gamma_K) dO / (gamma_Q . gamma_K + eps) is
+    # well conditioned and held to the usual bound; the routing and mixture gradients are O(eps)
+    # remainders, held to an absolute bound of fp32 rounding on the terms that cancel
+    w = gma.workload(0).with_(seq_len=1, heads=2)
+    inp, dout = inputs(gma, w, True)
+    got = run_gpu(gma, w, inp, dout, causal)
+    check(w, inp, dout, causal, got, only=("dv",))
+    ref = oracle.backward(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"], inp["prior_logits"], dout,
+                          eps=w.eps, causal=causal)
+    terms = float(dout.abs().max()) * float(inp["v"].abs().max()) * 64.0   # |dO| |v| times the log-density slope
+    for name in ("dqx", "dkx", "dmu", "draw_var", "dprior_logits"):
+        err = float(np.abs(got[name].cpu().numpy().astype(np.float64) - ref[name]).max())
+        say("  %-14s abs err %.3e (bound %.3e)" % (name, err, 1e-5 * terms))
+        assert err <= 1e-5 * terms, name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_bitwise_deterministic(gma, causal):
+    w = gma.workload(3).with_(heads=2, seq_len=1500)
+    inp, dout = inputs(gma, w, True)
+    a = run_gpu(gma, w, inp, dout, causal)
+    b = run_gpu(gma, w, inp, dout, causal)
+    for name in NAMES:
+        assert torch.equal(a[name], b[name]), name
+
+
+def test_backward_causal_ignores_later_gradients(gma):
+    # dL/dO zero from row m on: no key or value at a row >= m reaches the loss (only later queries
+    # see it), so dkx and dv vanish there exactly, and so does dqx
+    w = gma.workload(3).with_(heads=2, seq_len=900)
+    inp, dout = inputs(gma, w, True)
+    m = 333
+    dout[:, :, m:] = 0
+    got = run_gpu(gma, w, inp, dout, True)
+    for name in ("dqx", "dkx", "dv"):
+        assert got[name][:, :, m:].abs().max().item() == 0.0, name
+
+
+def test_backward_cfg3_full_size_sampled_head(gma):
+    # the full 16-head, 65536-token causal bf16 problem on the GPU; the oracle on head 0 (heads are
+    # independent and B = 1, so every gradient of head 0, parameters included, comes from it alone)
+    w = gma.workload(3)
+    say("backward cfg3 full size %s" % (w,))
+    inp, dout = inputs(gma, w, False)
+    got = run_gpu(gma, w, inp, dout, True)
+    sub = {k: (v[:, :1] if k in ("qx", "kx", "v") else v[:1]) for k, v in inp.items()}
+    got0 = {k: (v[:, :1] if k in ("dqx", "dkx", "dv") else v[:1]) for k, v in got.items()}
+    check(w.with_(heads=1), sub, dout[:, :1], True, got0)
