@@ -5,7 +5,11 @@ the chunked causal output pass) over one batch of synthetic inputs already resid
 Default workload: causal, bf16 storage / fp32 accumulation, B=1, H=16, N=65536, d_r=128,
 K=128, d_v=128.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+With --backward a step is one call of the backward instead (forward recompute and every
+gradient, from a seeded dL/dO); its line carries the whole step against the fp32 matrix-core
+roof, since every product of the backward runs in fp32.
+
+    python bench.py [--steps K] [--warmup W] [--workload I] [--backward] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -20,6 +24,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix peaks
 METRIC = "GMA fwd tokens/sec (causal, N=64K, K=128) + % of HBM/MFMA roofline"
+METRIC_BWD = "GMA backward tokens/sec (causal, N=64K, K=128) + % of fp32 matrix-core roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -43,6 +48,19 @@ def algorithmic_flops_per_token_head(w) -> int:
     return 8 * w.n_comp * w.d_route + 4 * w.n_comp * w.d_value
 
 
+def backward_bytes_per_token_head(w) -> int:
+    # read Q_X, K_X, V, dL/dO; write dQ_X, dK_X, dV
+    es = 2 if w.dtype == "bf16" else 4
+    return es * (4 * w.d_route + 3 * w.d_value)
+
+
+def backward_flops_per_token_head(w) -> int:
+    # the forward's contractions again, then: dGamma_Q = Vt g + Z h and the sums R = Gamma_Q^T g
+    # (2 K d_v each), dGamma_K = R v and dV = R^T gamma_K (2 K d_v each), and per side
+    # dl [mu/s | 1/s] for dX and dl^T [x | x^2] for the parameters (4 K d_r each)
+    return algorithmic_flops_per_token_head(w) + 8 * w.n_comp * w.d_value + 16 * w.n_comp * w.d_route
+
+
 def load_traffic(workload_name: str, kernel: str, src_hash: str):
     """HBM bytes per launch (reads + writes) of `kernel` from the committed rocprofv3 counter runs
     (FETCH_SIZE and WRITE_SIZE scaled by a copy-kernel calibration), or None if they were taken on a
@@ -56,6 +74,23 @@ def load_traffic(workload_name: str, kernel: str, src_hash: str):
     if not ent or ent.get("source_hash") != src_hash:
         return None
     return ent.get("bytes_per_launch")
+
+
+def cpu_baseline_backward(w, heads, dout):
+    import oracle
+    from gaussian_mixture_token_amd import make_inputs
+    inp = make_inputs(w, heads=heads)
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.backward(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"], inp["prior_logits"], dout,
+                    eps=w.eps, causal=w.causal)
+    dt = time.perf_counter() - t0
+    token_heads = w.batch * len(heads) * w.seq_len
+    return {"value": token_heads / dt / w.heads, "unit": "tokens/s", "cores": min(threads, w.batch * len(heads)),
+            "kind": "oracle",
+            "sample": "%d of %d heads, full N=%d, %s fp64 oracle backward (threads over (batch, head)), %.1f s wall" %
+                      (len(heads), w.heads, w.seq_len, "causal" if w.causal else "bidirectional", dt)}
 
 
 def cpu_baseline(w, heads):
@@ -83,6 +118,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--backward", action="store_true", help="time the backward pass instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) and exit; "
                          "its FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
@@ -123,6 +159,19 @@ def main():
         gma.forward(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps,
                     causal=w.causal, out=out, workspace=ws)
 
+    if args.backward:
+        del out, ws
+        dout = gma.make_dout(w).to(dev)
+        grads = {"dqx": torch.empty_like(t["qx"]), "dkx": torch.empty_like(t["kx"]), "dv": torch.empty_like(t["v"]),
+                 "dmu": torch.empty_like(t["mu"]), "draw_var": torch.empty_like(t["raw_var"]),
+                 "dprior_logits": torch.empty_like(t["prior_logits"])}
+        bop = _lib.GMA_OP_BACKWARD_CAUSAL if w.causal else _lib.GMA_OP_BACKWARD_BIDIR
+        ws = torch.empty(gma.workspace_size(prob, bop), dtype=torch.uint8, device=dev)
+
+        def step():   # noqa: F811
+            gma.backward(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], dout, eps=w.eps,
+                         causal=w.causal, workspace=ws, grads=grads)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -158,9 +207,12 @@ def main():
         _lib.check(lib.gma_timing_read(k, tot, n))
         if n.value:
             kernels[lib.gma_kernel_name(k).decode()] = {"avg_us": 1e3 * tot.value / n.value, "launches": n.value}
+    T = w.batch * w.heads * w.seq_len
+    if args.backward:
+        bwd_line(args, w, value, ms_per_step, kernels, T, dout)
+        return
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     avg_s = kernels[dominant]["avg_us"] * 1e-6
-    T = w.batch * w.heads * w.seq_len
     alg_bytes = algorithmic_bytes_per_token_head(w) * T
     alg_flops = algorithmic_flops_per_token_head(w) * T
     hbm_frac = alg_bytes / avg_s / 1e9 / HBM_PEAK_GBS
@@ -208,6 +260,36 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
         "source_hash": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bwd_line(args, w, value, ms_per_step, kernels, T, dout):
+    """The backward's JSON line: the whole step against the fp32 matrix-core peak (every product of the
+    backward is an fp32 matrix-core product) and, for reference, against HBM."""
+    step_s = ms_per_step * 1e-3
+    flops = backward_flops_per_token_head(w) * T
+    nbytes = backward_bytes_per_token_head(w) * T
+    peak = MFMA_PEAK_TFLOPS["f32"]
+    roof = {"bound": "mfma", "achieved": flops / step_s / 1e12, "peak": peak, "unit": "TFLOP/s",
+            "frac": flops / step_s / 1e12 / peak, "traffic": None, "kernel": "backward step (all kernels)",
+            "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": nbytes,
+            "hbm_frac": nbytes / step_s / 1e9 / HBM_PEAK_GBS}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle backward)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_backward(w, [0], dout[:, :1].cpu())
+    line = {
+        "metric": METRIC_BWD, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 arithmetic, %s storage" % w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs and dL/dO, N(0,1) means, U(-1,1) raw variances, "
+                "N(0,0.5^2) prior logits)",
+        "config": {"workload": w.name, "pass": "backward", "mode": "causal" if w.causal else "bidirectional",
+                   "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "d_route": w.d_route,
+                   "n_comp": w.n_comp, "d_value": w.d_value, "eps": w.eps, "global_batch": w.batch,
+                   "parallelism": "single GPU"},
+        "roofline": roof, "kernels": kernels, "cpu_baseline": cpu, "source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
 
