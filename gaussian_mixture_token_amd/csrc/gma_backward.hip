@@ -52,12 +52,19 @@ int64_t grid_for(int64_t n, int64_t per_block) {
 }
 
 // ---------------------------------------------------------------------------------- products
-constexpr int GM = 64, GN = 64, GK = 16, GLD = 80;   // tile, inner step, LDS row pitch (floats)
+constexpr int GM = 64, GN = 64, GK = 32, GLD = 80;   // tile, inner step, LDS row pitch (floats)
 
 // Workgroup of four wavefronts; wave w computes the 32 x 32 quarter (w / 2, w % 2) of the 64 x 64
-// tile as 2 x 2 accumulator tiles.  The operand tiles are staged in LDS inner-index-major
-// (s_a[k][m], s_b[k][n]) with a pitch of 80 floats, so that the 16-lane groups of a fragment read
-// (4 inner rows x 16 consecutive columns) fall in disjoint banks.
+// tile as 2 x 2 accumulator tiles (v_mfma_f32_16x16x4_f32).  Operand tiles are staged in LDS
+// inner-index-major (s_a[k][m], s_b[k][n]) with a pitch of 80 floats: the 16-lane groups of a
+// fragment read (4 inner rows x 16 consecutive columns) fall in disjoint banks.  The next inner
+// step's operands are fetched into registers while the current one is multiplied.
+//
+// Global fetch of an operand whose inner index is contiguous (A not transposed, B transposed):
+// thread t takes row t % 64 and inner elements 8 (t / 64) .. + 7 of the step, so that each wave's
+// LDS writes cover 64 consecutive columns of one inner row.  Of an operand whose outer index is
+// contiguous: thread t takes inner row t / 8 and columns 8 (t % 8) .. + 7.  Eight consecutive
+// elements inside the matrix are fetched as two 16-byte loads where the view allows it (vec*).
 template <bool TA, bool TB, bool OUT_BF16>
 __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     __shared__ float s_a[GK][GLD];
@@ -82,54 +89,90 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
     const int r = lane & 15, q = lane >> 4;
+
+    // fetch of 8 elements: contiguous in the inner index (row `row` of the view, inner k .. k+7) or
+    // in the outer one (inner row k, columns c .. c+7)
+    auto fetch_inner = [](const float* X, int ld, bool vec, int row, bool row_ok, int k, int kd, float (&v)[8]) {
+        const float* p = X + (int64_t)row * ld + k;
+        if (vec && row_ok && k + 8 <= kd) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(p), hi = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { v[j] = lo[j]; v[4 + j] = hi[j]; }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (row_ok && k + j < kd) ? p[j] : 0.f;
+        }
+    };
+    auto fetch_outer = [](const float* X, int ld, bool vec, int k, bool k_ok, int c, int cn, float (&v)[8]) {
+        const float* p = X + (int64_t)k * ld + c;
+        if (vec && k_ok && c + 8 <= cn) {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(p), hi = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { v[j] = lo[j]; v[4 + j] = hi[j]; }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (k_ok && c + j < cn) ? p[j] : 0.f;
+        }
+    };
+    float ra[8], rb[8];
+    const int ri = tid & 63, ki = (tid >> 6) * 8;     // contiguous-inner mapping
+    const int ko = tid >> 3, co = (tid & 7) * 8;      // contiguous-outer mapping
+    auto fetch = [&](int k0) {
+        if constexpr (!TA) fetch_inner(A, g.lda, g.vecA, m0 + ri, m0 + ri < M, k0 + ki, Kd, ra);
+        else fetch_outer(A, g.lda, g.vecA, k0 + ko, k0 + ko < Kd, m0 + co, M, ra);
+        if constexpr (TB) fetch_inner(B, g.ldb, g.vecB, n0 + ri, n0 + ri < N, k0 + ki, Kd, rb);
+        else fetch_outer(B, g.ldb, g.vecB, k0 + ko, k0 + ko < Kd, n0 + co, N, rb);
+    };
+    auto stage = [&]() {
+        if constexpr (!TA) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s_a[ki + j][ri] = ra[j];
+        } else {
+            *reinterpret_cast<f32x4*>(&s_a[ko][co]) = f32x4{ra[0], ra[1], ra[2], ra[3]};
+            *reinterpret_cast<f32x4*>(&s_a[ko][co + 4]) = f32x4{ra[4], ra[5], ra[6], ra[7]};
+        }
+        if constexpr (TB) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s_b[ki + j][ri] = rb[j];
+        } else {
+            *reinterpret_cast<f32x4*>(&s_b[ko][co]) = f32x4{rb[0], rb[1], rb[2], rb[3]};
+            *reinterpret_cast<f32x4*>(&s_b[ko][co + 4]) = f32x4{rb[4], rb[5], rb[6], rb[7]};
+        }
+    };
+
     f32x4 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // accumulator tiles wholly past a ragged edge are skipped (wave-uniform)
+    const bool mok1 = m0 + wm + 16 < M, nok1 = n0 + wn + 16 < N;
+    const bool wave_ok = m0 + wm < M && n0 + wn < N;
 
+    if (Kd > 0) {
+        fetch(0);
+        stage();
+        __syncthreads();
+    }
     for (int k0 = 0; k0 < Kd; k0 += GK) {
-        if constexpr (!TA) {   // A[m][k]: four consecutive k per thread
-            const int m = tid >> 2, kk = (tid & 3) * 4;
-            const bool mv = m0 + m < M;
+        const bool more = k0 + GK < Kd;
+        if (more) fetch(k0 + GK);
+        if (wave_ok) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k = k0 + kk + j;
-                s_a[kk + j][m] = (mv && k < Kd) ? A[(int64_t)(m0 + m) * g.lda + k] : 0.f;
-            }
-        } else {               // A[k][m]: four consecutive m per thread
-            const int kk = tid >> 4, m = (tid & 15) * 4;
-            const bool kv = k0 + kk < Kd;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                s_a[kk][m + j] = (kv && m0 + m + j < M) ? A[(int64_t)(k0 + kk) * g.lda + m0 + m + j] : 0.f;
-        }
-        if constexpr (!TB) {   // B[k][n]
-            const int kk = tid >> 4, n = (tid & 15) * 4;
-            const bool kv = k0 + kk < Kd;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                s_b[kk][n + j] = (kv && n0 + n + j < N) ? B[(int64_t)(k0 + kk) * g.ldb + n0 + n + j] : 0.f;
-        } else {               // B[n][k]
-            const int n = tid >> 2, kk = (tid & 3) * 4;
-            const bool nv = n0 + n < N;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k = k0 + kk + j;
-                s_b[kk + j][n] = (nv && k < Kd) ? B[(int64_t)(n0 + n) * g.ldb + k] : 0.f;
+            for (int ks = 0; ks < GK; ks += 4) {
+                const float a0 = s_a[ks + q][wm + r], a1 = s_a[ks + q][wm + 16 + r];
+                const float b0 = s_b[ks + q][wn + r], b1 = s_b[ks + q][wn + 16 + r];
+                acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
+                if (nok1) acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
+                if (mok1) acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
+                if (mok1 && nok1) acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
             }
         }
         __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < GK; ks += 4) {
-            const float a0 = s_a[ks + q][wm + r], a1 = s_a[ks + q][wm + 16 + r];
-            const float b0 = s_b[ks + q][wn + r], b1 = s_b[ks + q][wn + 16 + r];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b1, acc[1][1], 0, 0, 0);
+        if (more) {
+            stage();
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     const int64_t coff = outer * g.sC0 + (int64_t)inner * g.sC1;
@@ -152,21 +195,33 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
 
 // ---------------------------------------------------------------------------------- mixture
 // One workgroup per head; thread e handles elements e, e + 256, ... of [K, d_r].
-__global__ void __launch_bounds__(256) bwd_prep_kernel(const float* mu, const float* raw_var, const float* prior,
-                                                       float* mw, float* cp, int K, int d_r) {
+// The operands of the matrix-core log-densities (expanded form
+//   l_k = cq_k + sum_d (-s_kd^-1 / 2) x_d^2 + sum_d (mu_kd / s_kd) x_d,
+//   cq_k = log pi_k - 1/2 sum_d (log s_kd + mu_kd^2 / s_kd), fp64):
+// bf [H][d_r / 16 steps][2 parts (x^2, x)][KT][64 lanes][4]: lane (r, q) of component tile kt holds the
+// coefficients of component 16 kt + r for dims 16 step + 4 q .. + 3 (zero past K or d_r), the order
+// of the A fragments of the rows; cq [H][16 KT] with -inf past K.
+__global__ void __launch_bounds__(256) bwd_frag_kernel(const float* mu, const float* raw_var, const float* prior,
+                                                       float* bf, double* cq, int K, int d_r, int KT) {
     const int h = blockIdx.x, tid = threadIdx.x;
-    const float* m_h = mu + (int64_t)h * K * d_r;
-    const float* r_h = raw_var + (int64_t)h * K * d_r;
-    float* mw_h = mw + (int64_t)h * K * 2 * d_r;
-    for (int e = tid; e < K * d_r; e += 256) {
-        const int k = e / d_r, d = e % d_r;
-        const float rv = r_h[e];
-        const float s = fmaxf(rv, 0.f) + log1pf(expf(-fabsf(rv)));   // softplus
-        const float wv = 1.f / s;
-        mw_h[(int64_t)k * 2 * d_r + d] = m_h[e] * wv;
-        mw_h[(int64_t)k * 2 * d_r + d_r + d] = wv;
+    const int steps = (d_r + 15) / 16, KP = 16 * KT;
+    const int64_t per_head = (int64_t)steps * 2 * KT * 256;
+    for (int64_t e = tid; e < per_head; e += 256) {
+        const int j = (int)(e & 3), lane = (int)((e >> 2) & 63);
+        int64_t t = e >> 8;
+        const int kt = (int)(t % KT);
+        t /= KT;
+        const int part = (int)(t & 1), st = (int)(t >> 1);
+        const int k = 16 * kt + (lane & 15), d = 16 * st + 4 * (lane >> 4) + j;
+        float val = 0.f;
+        if (k < K && d < d_r) {
+            const int64_t pe = ((int64_t)h * K + k) * d_r + d;
+            const float rv = raw_var[pe];
+            const float sv = fmaxf(rv, 0.f) + log1pf(expf(-fabsf(rv)));
+            val = part == 0 ? -0.5f / sv : mu[pe] / sv;
+        }
+        bf[(int64_t)h * per_head + e] = val;
     }
-    // log pi_k (log-softmax of the prior logits) and the log-determinant terms, fp64 sums
     __shared__ double s_lse;
     if (tid < 64) {
         double mx = -INFINITY;
@@ -180,100 +235,111 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const float* mu, const fl
         if (tid == 0) s_lse = mx + log(sm);
     }
     __syncthreads();
-    for (int k = tid; k < K; k += 256) {
-        double ld = 0.0;
-        for (int d = 0; d < d_r; ++d) {
-            const double rv = r_h[(int64_t)k * d_r + d];
-            ld += log(fmax(rv, 0.0) + log1p(exp(-fabs(rv))));
+    for (int k = tid; k < KP; k += 256) {
+        double c = -INFINITY;
+        if (k < K) {
+            double acc = 0.0;
+            for (int d = 0; d < d_r; ++d) {
+                const int64_t pe = ((int64_t)h * K + k) * d_r + d;
+                const double rv = raw_var[pe], m = mu[pe];
+                const double sv = fmax(rv, 0.0) + log1p(exp(-fabs(rv)));
+                acc += log(sv) + m * m / sv;
+            }
+            c = (double)prior[(int64_t)h * K + k] - s_lse - 0.5 * acc;
         }
-        cp[(int64_t)h * K + k] = (float)((double)prior[(int64_t)h * K + k] - s_lse - 0.5 * ld);
+        cq[(int64_t)h * KP + k] = c;
     }
 }
 
-// Responsibilities in the direct form l_k = cp_k - 1/2 sum_d (x_d - mu_kd)^2 / s_kd.  Workgroup:
-// 64 rows of one (batch, head); thread (tr, tk) = (tid / 16, tid % 16) accumulates rows 4 tr + i and
-// components tk + 16 j (j < KJ); the softmax over components reduces over the 16 lanes of a row
-// group.  x, mu and 1/s are staged through LDS 16 dimensions at a time.  Each term is formed in fp32
-// and the sum over d_r runs in fp64: the logits reach a few hundred at d_r = 256, and an fp32 running
-// sum would put an error of about 1e-4 into gamma (fp64 adds cost no more than fp32 ones here).
-template <int KJ, bool F32>
-__global__ void __launch_bounds__(256) bwd_gamma_kernel(const void* x, const float* mu, const float* mw,
-                                                        const float* cp, float* gamma, int64_t N, int H, int K,
-                                                        int d_r) {
-    constexpr int KC = 16 * KJ;
-    __shared__ float s_x[64][17];
-    __shared__ float s_m[KC][17];
-    __shared__ float s_w[KC][17];
+// One workgroup per head; thread e handles elements e, e + 256, ... of [K, d_r].
+__global__ void __launch_bounds__(256) bwd_prep_kernel(const float* mu, const float* raw_var, float* mw, int K,
+                                                       int d_r) {
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const float* m_h = mu + (int64_t)h * K * d_r;
+    const float* r_h = raw_var + (int64_t)h * K * d_r;
+    float* mw_h = mw + (int64_t)h * K * 2 * d_r;
+    for (int e = tid; e < K * d_r; e += 256) {
+        const int k = e / d_r, d = e % d_r;
+        const float rv = r_h[e];
+        const float s = fmaxf(rv, 0.f) + log1pf(expf(-fabsf(rv)));   // softplus
+        const float wv = 1.f / s;
+        mw_h[(int64_t)k * 2 * d_r + d] = m_h[e] * wv;
+        mw_h[(int64_t)k * 2 * d_r + d_r + d] = wv;
+    }
+}
+
+// Responsibilities on the fp32 matrix cores, expanded form (see bwd_frag_kernel).  Workgroup: 64
+// rows of one (batch, head), wave w rows 16 w .. 16 w + 15 against all 16 KT components.  Per step of
+// 16 dims, lane (r, q) holds x and x^2 of row 16 w + r, dims 4 q .. 4 q + 3 (the permuted contraction
+// order of the fragments in bf), and each component tile takes four v_mfma_f32_16x16x4_f32 per part.
+// The fp32 accumulators of a step are added into fp64 ones after the step, so that no fp32 sum runs
+// over more than 32 products (the logits reach a few hundred); constants in fp64.  Softmax over the
+// components of each row: in registers over the tiles, butterflies over the 16 lanes of a column.
+template <int KT, bool F32>
+__global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, const float* bf, const double* cq,
+                                                             float* gamma, int64_t N, int H, int K, int d_r) {
     const int64_t tiles = (N + 63) / 64;
     const int64_t bh = (int64_t)blockIdx.x / tiles;
     const int h = (int)(bh % H);
-    const int64_t row0 = ((int64_t)blockIdx.x % tiles) * 64;
-    const int tid = threadIdx.x, tk = tid & 15, tr = tid >> 4;
-    double acc[4][KJ];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t row = ((int64_t)blockIdx.x % tiles) * 64 + 16 * w + r;   // A-fragment row of this lane
+    const bool row_ok = row < N;
+    const int steps = (d_r + 15) / 16;
+    const f32x4* bfh = reinterpret_cast<const f32x4*>(bf) + (int64_t)h * steps * 2 * KT * 64;
+    double acc[KT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int j = 0; j < KJ; ++j) acc[i][j] = 0.0;
-    const float* m_h = mu + (int64_t)h * K * d_r;
-    const float* w_h = mw + (int64_t)h * K * 2 * d_r + d_r;
-    for (int d0 = 0; d0 < d_r; d0 += 16) {
-        for (int e = tid; e < 64 * 16; e += 256) {
-            const int rr = e >> 4, dd = e & 15;
-            const int64_t row = row0 + rr;
-            s_x[rr][dd] = (row < N && d0 + dd < d_r) ? ld_elem<F32>(x, (bh * N + row) * d_r + d0 + dd) : 0.f;
+        for (int i = 0; i < 4; ++i) acc[kt][i] = 0.0;
+    for (int st = 0; st < steps; ++st) {
+        f32x4 xa = {0.f, 0.f, 0.f, 0.f};
+        const int d0 = 16 * st + 4 * q;
+        if (row_ok) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (d0 + j < d_r) xa[j] = ld_elem<F32>(x, (bh * N + row) * d_r + d0 + j);
         }
-        for (int e = tid; e < KC * 16; e += 256) {
-            const int k = e >> 4, dd = e & 15;
-            const bool in = k < K && d0 + dd < d_r;
-            s_m[k][dd] = in ? m_h[(int64_t)k * d_r + d0 + dd] : 0.f;
-            s_w[k][dd] = in ? w_h[(int64_t)k * 2 * d_r + d0 + dd] : 0.f;
+        const f32x4 x2 = xa * xa;
+        const f32x4* bs = bfh + (int64_t)st * 2 * KT * 64 + lane;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            mma(c, x2, bs[kt * 64]);
+            mma(c, xa, bs[(KT + kt) * 64]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[kt][i] += (double)c[i];
         }
-        __syncthreads();
-#pragma unroll 4
-        for (int dd = 0; dd < 16; ++dd) {
-            float xv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = s_x[4 * tr + i][dd];
-#pragma unroll
-            for (int j = 0; j < KJ; ++j) {
-                const float mv = s_m[tk + 16 * j][dd], wv = s_w[tk + 16 * j][dd];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float df = xv[i] - mv;
-                    acc[i][j] += (double)(wv * df * df);
-                }
-            }
-        }
-        __syncthreads();
     }
+    const double* cqh = cq + (int64_t)h * 16 * KT;
+    const int64_t row0 = ((int64_t)blockIdx.x % tiles) * 64 + 16 * w + 4 * q;   // accumulator rows 4 q + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        double ld[KJ];
         double mx = -INFINITY;
+        double l[KT];
 #pragma unroll
-        for (int j = 0; j < KJ; ++j) {
-            const int k = tk + 16 * j;
-            ld[j] = (k < K) ? (double)cp[(int64_t)h * K + k] - 0.5 * acc[i][j] : -INFINITY;
-            mx = fmax(mx, ld[j]);
+        for (int kt = 0; kt < KT; ++kt) {
+            l[kt] = cqh[16 * kt + r] + acc[kt][i];
+            mx = fmax(mx, l[kt]);
         }
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
-        float l[KJ];
+        float e[KT];
         float sm = 0.f;
 #pragma unroll
-        for (int j = 0; j < KJ; ++j) {
-            l[j] = expf((float)(ld[j] - mx));
-            sm += l[j];
+        for (int kt = 0; kt < KT; ++kt) {
+            e[kt] = expf((float)(l[kt] - mx));
+            sm += e[kt];
         }
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
         const float inv = 1.f / sm;
-        const int64_t row = row0 + 4 * tr + i;
-        if (row < N) {
+        const int64_t rr = row0 + i;
+        if (rr < N) {
 #pragma unroll
-            for (int j = 0; j < KJ; ++j) {
-                const int k = tk + 16 * j;
-                if (k < K) gamma[(bh * N + row) * K + k] = l[j] * inv;
+            for (int kt = 0; kt < KT; ++kt) {
+                const int k = 16 * kt + r;
+                if (k < K) gamma[(bh * N + rr) * K + k] = e[kt] * inv;
             }
         }
     }
@@ -443,39 +509,55 @@ void gemm_dispatch(const BwdGemm& g, bool out_bf16, int64_t grid, hipStream_t s)
     else bwd_gemm_kernel<TA, TB, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
 }
 
-template <int KJ>
-void gamma_dispatch(const void* x, bool f32, const float* mu, const float* mw, const float* cp, float* gamma,
-                    int64_t BH, int64_t N, int H, int K, int d_r, hipStream_t s) {
+template <int KT>
+void gamma_mfma_dispatch(const void* x, bool f32, const float* bf, const double* cq, float* gamma, int64_t BH,
+                         int64_t N, int H, int K, int d_r, hipStream_t s) {
     const dim3 grid((unsigned)((N + 63) / 64 * BH));
-    if (f32) bwd_gamma_kernel<KJ, true><<<grid, dim3(256), 0, s>>>(x, mu, mw, cp, gamma, N, H, K, d_r);
-    else bwd_gamma_kernel<KJ, false><<<grid, dim3(256), 0, s>>>(x, mu, mw, cp, gamma, N, H, K, d_r);
+    if (f32) bwd_gamma_mfma_kernel<KT, true><<<grid, dim3(256), 0, s>>>(x, bf, cq, gamma, N, H, K, d_r);
+    else bwd_gamma_mfma_kernel<KT, false><<<grid, dim3(256), 0, s>>>(x, bf, cq, gamma, N, H, K, d_r);
 }
 
 }  // namespace
 
-void launch_bwd_gemm(const BwdGemm& g, bool ta, bool tb, bool out_bf16, hipStream_t s) {
-    const int64_t tiles = (int64_t)((g.M + GM - 1) / GM) * ((g.N + GN - 1) / GN);
-    const int64_t grid = tiles * g.n_inner * g.n_outer;
+void launch_bwd_gemm(const BwdGemm& g0, bool ta, bool tb, bool out_bf16, hipStream_t s) {
+    const int64_t tiles = (int64_t)((g0.M + GM - 1) / GM) * ((g0.N + GN - 1) / GN);
+    const int64_t grid = tiles * g0.n_inner * g0.n_outer;
     if (grid <= 0) return;
+    BwdGemm g = g0;
+    auto vec_ok = [](const float* p, int ld, int64_t s0, int64_t s1, int64_t mod) {
+        return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0 && s0 % 4 == 0 && s1 % 4 == 0 && mod >= 0;
+    };
+    g.vecA = vec_ok(g.A, g.lda, g.sA0, g.sA1, 0);
+    g.vecB = vec_ok(g.B, g.ldb, g.sB0, g.sB1, g.modB);
     if (!ta && !tb) gemm_dispatch<false, false>(g, out_bf16, grid, s);
     else if (!ta && tb) gemm_dispatch<false, true>(g, out_bf16, grid, s);
     else if (ta && !tb) gemm_dispatch<true, false>(g, out_bf16, grid, s);
     else gemm_dispatch<true, true>(g, out_bf16, grid, s);
 }
 
-void launch_bwd_prep(const float* mu, const float* raw_var, const float* prior, float* mw, float* cp, int H, int K,
-                     int d_r, hipStream_t s) {
-    bwd_prep_kernel<<<dim3(H), dim3(256), 0, s>>>(mu, raw_var, prior, mw, cp, K, d_r);
+void launch_bwd_prep(const float* mu, const float* raw_var, float* mw, int H, int K, int d_r, hipStream_t s) {
+    bwd_prep_kernel<<<dim3(H), dim3(256), 0, s>>>(mu, raw_var, mw, K, d_r);
 }
 
-void launch_bwd_gamma(const void* x, bool f32, const float* mu, const float* mw, const float* cp, float* gamma,
-                      int64_t BH, int64_t N, int H, int K, int d_r, hipStream_t s) {
-    const int kj = (K + 15) / 16;
-    if (kj <= 1) gamma_dispatch<1>(x, f32, mu, mw, cp, gamma, BH, N, H, K, d_r, s);
-    else if (kj <= 2) gamma_dispatch<2>(x, f32, mu, mw, cp, gamma, BH, N, H, K, d_r, s);
-    else if (kj <= 4) gamma_dispatch<4>(x, f32, mu, mw, cp, gamma, BH, N, H, K, d_r, s);
-    else if (kj <= 8) gamma_dispatch<8>(x, f32, mu, mw, cp, gamma, BH, N, H, K, d_r, s);
-    else gamma_dispatch<16>(x, f32, mu, mw, cp, gamma, BH, N, H, K, d_r, s);
+int bwd_gamma_tiles(int K) {
+    const int kt = (K + 15) / 16;
+    return kt <= 1 ? 1 : kt <= 2 ? 2 : kt <= 4 ? 4 : kt <= 8 ? 8 : 16;
+}
+
+void launch_bwd_frag(const float* mu, const float* raw_var, const float* prior, float* bf, double* cq, int H, int K,
+                     int d_r, hipStream_t s) {
+    bwd_frag_kernel<<<dim3(H), dim3(256), 0, s>>>(mu, raw_var, prior, bf, cq, K, d_r, bwd_gamma_tiles(K));
+}
+
+void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const double* cq, float* gamma, int64_t BH,
+                           int64_t N, int H, int K, int d_r, hipStream_t s) {
+    switch (bwd_gamma_tiles(K)) {
+        case 1: gamma_mfma_dispatch<1>(x, f32, bf, cq, gamma, BH, N, H, K, d_r, s); break;
+        case 2: gamma_mfma_dispatch<2>(x, f32, bf, cq, gamma, BH, N, H, K, d_r, s); break;
+        case 4: gamma_mfma_dispatch<4>(x, f32, bf, cq, gamma, BH, N, H, K, d_r, s); break;
+        case 8: gamma_mfma_dispatch<8>(x, f32, bf, cq, gamma, BH, N, H, K, d_r, s); break;
+        default: gamma_mfma_dispatch<16>(x, f32, bf, cq, gamma, BH, N, H, K, d_r, s); break;
+    }
 }
 
 void launch_bwd_vaug(const void* v, bool f32, float* vaug, int64_t rows, int d_v, int dva, hipStream_t s) {

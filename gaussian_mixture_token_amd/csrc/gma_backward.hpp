@@ -32,18 +32,25 @@ struct BwdGemm {
     int tok_flags = 0;
     float alpha = 1.f, beta = 0.f;
     int tril = 0;
+    // set by launch_bwd_gemm: 16-byte loads are allowed (base 16-byte aligned, leading dimension and
+    // batch strides multiples of 4 elements)
+    bool vecA = false, vecB = false;
 };
 void launch_bwd_gemm(const BwdGemm& g, bool ta, bool tb, bool out_bf16, hipStream_t s);
 
-// Mixture constants for the gradient: mw [H, K, 2 d_r] (row k: mu_kd / s_kd for d < d_r, then
-// 1 / s_kd), cp [H, K] = log pi_k - 1/2 sum_d log s_kd (s = softplus(raw_var)).
-void launch_bwd_prep(const float* mu, const float* raw_var, const float* prior, float* mw, float* cp, int H, int K,
-                     int d_r, hipStream_t s);
+// Mixture constants for the routing-input gradient: mw [H, K, 2 d_r] (row k: mu_kd / s_kd for d < d_r,
+// then 1 / s_kd; s = softplus(raw_var)).
+void launch_bwd_prep(const float* mu, const float* raw_var, float* mw, int H, int K, int d_r, hipStream_t s);
 
-// Responsibilities of rows x [BH, N, d_r] (bf16 or fp32) in fp32, from the direct form of the
-// log-density: gamma [BH, N, K].
-void launch_bwd_gamma(const void* x, bool f32, const float* mu, const float* mw, const float* cp, float* gamma,
-                      int64_t BH, int64_t N, int H, int K, int d_r, hipStream_t s);
+// Responsibilities of rows x [BH, N, d_r] (bf16 or fp32) in fp32 -> gamma [BH, N, K], on the matrix
+// cores from the expanded log-density: component tiles of 16 (KT tiles, a power of two covering K),
+// the fragment-ordered coefficients bf [H][ceil(d_r / 16)][2][KT][64][4] fp32 and constants cq
+// [H][16 KT] fp64, written by launch_bwd_frag.
+int bwd_gamma_tiles(int K);
+void launch_bwd_frag(const float* mu, const float* raw_var, const float* prior, float* bf, double* cq, int H, int K,
+                     int d_r, hipStream_t s);
+void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const double* cq, float* gamma, int64_t BH,
+                           int64_t N, int H, int K, int d_r, hipStream_t s);
 
 // [V | 1 | 0...] rows of width dva (fp32) from v [rows, d_v].
 void launch_bwd_vaug(const void* v, bool f32, float* vaug, int64_t rows, int d_v, int dva, hipStream_t s);

@@ -196,7 +196,8 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
 }
 
 // Backward workspace: fp32 intermediates of the gradient, each region 256-byte aligned.
-//   mw [H, K, 2 d_r], cp [H, K]               mixture constants (mu / s | 1 / s; log pi - 1/2 sum log s)
+//   bf, cq                                    matrix-core log-density operands (launch_bwd_frag)
+//   mw [H, K, 2 d_r]                          mixture constants mu / s | 1 / s
 //   gq, gk, dgq, dgk [BH, N, K]               responsibilities and their gradients (then dl)
 //   va, gh, pp [BH, N, dva]                   [V | 1], [g | h], [num | Gamma_Q . Z]  (dva = d_v + 1 rounded
 //                                             up to a multiple of 4, zero padded)
@@ -216,7 +217,7 @@ struct BwdPlan {
     float eps = 0.f;
     int st_step = 0;            // tokens per state entry
     int64_t n_st = 0, n_sg = 0;  // state entries and parameter segments per (batch, head)
-    size_t off_mw = 0, off_cp = 0, off_gq = 0, off_gk = 0, off_dgq = 0, off_dgk = 0, off_va = 0, off_gh = 0,
+    size_t off_bf = 0, off_cq = 0, off_mw = 0, off_gq = 0, off_gk = 0, off_dgq = 0, off_dgk = 0, off_va = 0, off_gh = 0,
            off_pp = 0, off_st = 0, off_rt = 0, off_ac = 0, off_mt = 0, off_dvt = 0, off_p12 = 0, off_xa = 0,
            off_gp = 0, total = 0;
 };
@@ -252,8 +253,10 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
         *o = off;
         off = align_up(off + (size_t)floats * sizeof(float), 256);
     };
+    const int KT = bwd_gamma_tiles(b->K);
+    take(&b->off_bf, b->H * ((b->d_r + 15) / 16) * 2 * KT * 256);
+    take(&b->off_cq, b->H * 16 * KT * 2);   // fp64
     take(&b->off_mw, b->H * b->K * 2 * b->d_r);
-    take(&b->off_cp, b->H * b->K);
     take(&b->off_gq, rows * b->K);
     take(&b->off_gk, rows * b->K);
     take(&b->off_dgq, rows * b->K);
@@ -768,7 +771,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* w = reinterpret_cast<char*>(ws);
     auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
-    float *mw = F(b.off_mw), *cp = F(b.off_cp), *gq = F(b.off_gq), *gk = F(b.off_gk), *dgq = F(b.off_dgq),
+    float *mw = F(b.off_mw), *gq = F(b.off_gq), *gk = F(b.off_gk), *dgq = F(b.off_dgq),
           *dgk = F(b.off_dgk), *va = F(b.off_va), *gh = F(b.off_gh), *pp = F(b.off_pp), *stt = F(b.off_st),
           *rt = F(b.off_rt), *ac = F(b.off_ac), *mt = F(b.off_mt), *dvt = F(b.off_dvt), *p12 = F(b.off_p12),
           *xa = F(b.off_xa), *gp = F(b.off_gp);
@@ -823,9 +826,17 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     constexpr int TM = 1, TN = 2, TK = 4;   // token axes of a product
 
     // mixture constants, responsibilities of both sides, [V | 1]
-    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_prep(mu, rv, pr, mw, cp, H, K, d_r, s); }));
-    GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] { launch_bwd_gamma(qx, f32, mu, mw, cp, gq, BH, N, H, K, d_r, s); }));
-    GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] { launch_bwd_gamma(kx, f32, mu, mw, cp, gk, BH, N, H, K, d_r, s); }));
+    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_prep(mu, rv, mw, H, K, d_r, s); }));
+    const double* cq = reinterpret_cast<const double*>(w + b.off_cq);
+    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] {
+        launch_bwd_frag(mu, rv, pr, F(b.off_bf), reinterpret_cast<double*>(w + b.off_cq), H, K, d_r, s);
+    }));
+    GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] {
+        launch_bwd_gamma_mfma(qx, f32, F(b.off_bf), cq, gq, BH, N, H, K, d_r, s);
+    }));
+    GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] {
+        launch_bwd_gamma_mfma(kx, f32, F(b.off_bf), cq, gk, BH, N, H, K, d_r, s);
+    }));
     GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_vaug(v, f32, va, rows, d_v, dva, s); }));
     // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
     GMA_TRY(gemm(tok(gk, K), true, tok(va, dva), false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false));
