@@ -47,10 +47,6 @@ __device__ __forceinline__ float wave_sum_f(float x) {
     return x;
 }
 
-int64_t grid_for(int64_t n, int64_t per_block) {
-    return std::max<int64_t>(1, std::min<int64_t>((n + per_block - 1) / per_block, int64_t(1) << 20));
-}
-
 // ---------------------------------------------------------------------------------- products
 constexpr int GM = 64, GN = 64, GK = 32, GLD = 80;   // tile, inner step, LDS row pitch (floats)
 
@@ -346,29 +342,33 @@ __global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, cons
 }
 
 // ---------------------------------------------------------------------------------- rows
+// Row kernels: workgroup = kRowsPerBlock rows, threads over the columns (no per-element division).
+constexpr int kRowsPerBlock = 8;
+
 template <bool F32>
 __global__ void __launch_bounds__(256) bwd_vaug_kernel(const void* v, float* vaug, int64_t rows, int d_v, int dva) {
-    const int64_t total = rows * dva;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-        const int64_t rr = e / dva;
-        const int c = (int)(e % dva);
-        vaug[e] = (c < d_v) ? ld_elem<F32>(v, rr * d_v + c) : (c == d_v ? 1.f : 0.f);
+    const int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock;
+    for (int i = 0; i < kRowsPerBlock && r0 + i < rows; ++i) {
+        const int64_t rr = r0 + i;
+        for (int c = threadIdx.x; c < dva; c += 256)
+            vaug[rr * dva + c] = (c < d_v) ? ld_elem<F32>(v, rr * d_v + c) : (c == d_v ? 1.f : 0.f);
     }
 }
 
 template <bool F32>
 __global__ void __launch_bounds__(256) bwd_xaug_kernel(const void* x, float* xaug, int64_t rows, int d_r, int dxa) {
-    const int64_t total = rows * dxa;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-        const int64_t rr = e / dxa;
-        const int c = (int)(e % dxa);
-        float val;
-        if (c < d_r) val = ld_elem<F32>(x, rr * d_r + c);
-        else if (c < 2 * d_r) {
-            const float t = ld_elem<F32>(x, rr * d_r + c - d_r);
-            val = t * t;
-        } else val = (c == 2 * d_r) ? 1.f : 0.f;
-        xaug[e] = val;
+    const int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock;
+    for (int i = 0; i < kRowsPerBlock && r0 + i < rows; ++i) {
+        const int64_t rr = r0 + i;
+        for (int c = threadIdx.x; c < dxa; c += 256) {
+            float val;
+            if (c < d_r) val = ld_elem<F32>(x, rr * d_r + c);
+            else if (c < 2 * d_r) {
+                const float t = ld_elem<F32>(x, rr * d_r + c - d_r);
+                val = t * t;
+            } else val = (c == 2 * d_r) ? 1.f : 0.f;
+            xaug[rr * dxa + c] = val;
+        }
     }
 }
 
@@ -407,12 +407,12 @@ __global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* 
 
 template <bool F32>
 __global__ void __launch_bounds__(256) bwd_dx_kernel(const void* x, const float* p12, void* dx, int64_t rows, int d_r) {
-    const int64_t total = rows * d_r;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-        const int64_t rr = e / d_r;
-        const int d = (int)(e % d_r);
+    const int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock;
+    for (int i = 0; i < kRowsPerBlock && r0 + i < rows; ++i) {
+        const int64_t rr = r0 + i;
         const float* pr = p12 + rr * 2 * d_r;
-        st_elem<F32>(dx, e, pr[d] - ld_elem<F32>(x, e) * pr[d_r + d]);
+        for (int d = threadIdx.x; d < d_r; d += 256)
+            st_elem<F32>(dx, rr * d_r + d, pr[d] - ld_elem<F32>(x, rr * d_r + d) * pr[d_r + d]);
     }
 }
 
@@ -561,13 +561,13 @@ void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const doubl
 }
 
 void launch_bwd_vaug(const void* v, bool f32, float* vaug, int64_t rows, int d_v, int dva, hipStream_t s) {
-    const dim3 grid((unsigned)grid_for(rows * dva, 256));
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     if (f32) bwd_vaug_kernel<true><<<grid, dim3(256), 0, s>>>(v, vaug, rows, d_v, dva);
     else bwd_vaug_kernel<false><<<grid, dim3(256), 0, s>>>(v, vaug, rows, d_v, dva);
 }
 
 void launch_bwd_xaug(const void* x, bool f32, float* xaug, int64_t rows, int d_r, int dxa, hipStream_t s) {
-    const dim3 grid((unsigned)grid_for(rows * dxa, 256));
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     if (f32) bwd_xaug_kernel<true><<<grid, dim3(256), 0, s>>>(x, xaug, rows, d_r, dxa);
     else bwd_xaug_kernel<false><<<grid, dim3(256), 0, s>>>(x, xaug, rows, d_r, dxa);
 }
@@ -584,7 +584,7 @@ void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream
 }
 
 void launch_bwd_dx(const void* x, const float* p12, void* dx, bool f32, int64_t rows, int d_r, hipStream_t s) {
-    const dim3 grid((unsigned)grid_for(rows * d_r, 256));
+    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     if (f32) bwd_dx_kernel<true><<<grid, dim3(256), 0, s>>>(x, p12, dx, rows, d_r);
     else bwd_dx_kernel<false><<<grid, dim3(256), 0, s>>>(x, p12, dx, rows, d_r);
 }
