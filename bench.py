@@ -28,10 +28,18 @@ METRIC_BWD = "GMA backward tokens/sec (causal, N=64K, K=128) + % of fp32 matrix-
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
+# sources of the forward path's kernels and their launches (the backward and decode kernels live in
+# files of their own, which the forward's code does not include)
+_OTHER_PATHS = ("gma_backward", "gma_decode")
+
+
+def kernel_source_hash(backward: bool = False) -> str:
+    """Hash of the sources that the timed path's kernels are built and launched from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gaussian_mixture_token_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not backward and name.startswith(_OTHER_PATHS):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -289,7 +297,7 @@ def bwd_line(args, w, value, ms_per_step, kernels, T, dout):
                    "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "d_route": w.d_route,
                    "n_comp": w.n_comp, "d_value": w.d_value, "eps": w.eps, "global_batch": w.batch,
                    "parallelism": "single GPU"},
-        "roofline": roof, "kernels": kernels, "cpu_baseline": cpu, "source_hash": kernel_source_hash(),
+        "roofline": roof, "kernels": kernels, "cpu_baseline": cpu, "source_hash": kernel_source_hash(backward=True),
     }
     print(json.dumps(line), flush=True)
 
