@@ -264,78 +264,125 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const float* mu, const fl
     }
 }
 
-// Responsibilities on the fp32 matrix cores, expanded form (see bwd_frag_kernel).  Workgroup: 64
-// rows of one (batch, head), wave w rows 16 w .. 16 w + 15 against all 16 KT components.  Per step of
-// 16 dims, lane (r, q) holds x and x^2 of row 16 w + r, dims 4 q .. 4 q + 3 (the permuted contraction
-// order of the fragments in bf), and each component tile takes four v_mfma_f32_16x16x4_f32 per part.
-// The fp32 accumulators of a step are added into fp64 ones after the step, so that no fp32 sum runs
-// over more than 32 products (the logits reach a few hundred); constants in fp64.  Softmax over the
-// components of each row: in registers over the tiles, butterflies over the 16 lanes of a column.
-template <int KT, bool F32>
+// Responsibilities on the fp32 matrix cores, expanded form (see bwd_frag_kernel).  Workgroup: 64 G
+// rows of one (batch, head); wave w takes the 16-row groups w, w + 4, ... (G of them) against all 16 KT
+// components.  Per step of 16 dims the step's coefficient fragments (2 KT KiB) are staged once in LDS
+// for the workgroup (double-buffered, the next step's fetched into registers meanwhile); lane (r, q)
+// holds x and x^2 of row r of a group, dims 4 q .. 4 q + 3 (the permuted contraction order of the
+// fragments), and each component tile takes four v_mfma_f32_16x16x4_f32 per part.  The fp32
+// accumulators of a step are added into fp64 ones after the step, so that no fp32 sum runs over more
+// than 32 products (the logits reach a few hundred); constants in fp64.  Softmax over the components
+// of each row: in registers over the tiles, butterflies over the 16 lanes of a column.
+template <int KT, int G, bool F32>
 __global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, const float* bf, const double* cq,
-                                                             float* gamma, int64_t N, int H, int K, int d_r) {
-    const int64_t tiles = (N + 63) / 64;
+                                                             float* gamma, int64_t N, int H, int K, int d_r,
+                                                             int vecx) {
+    constexpr int NF = 2 * KT * 64;                  // f32x4 fragments per step
+    constexpr int NE = (NF + 255) / 256;             // ... staged per thread
+    __shared__ f32x4 s_bf[2][NF];
+    const int64_t tiles = (N + 64 * G - 1) / (64 * G);
     const int64_t bh = (int64_t)blockIdx.x / tiles;
     const int h = (int)(bh % H);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, q = lane >> 4;
-    const int64_t row = ((int64_t)blockIdx.x % tiles) * 64 + 16 * w + r;   // A-fragment row of this lane
-    const bool row_ok = row < N;
+    const int64_t base = ((int64_t)blockIdx.x % tiles) * 64 * G;
     const int steps = (d_r + 15) / 16;
-    const f32x4* bfh = reinterpret_cast<const f32x4*>(bf) + (int64_t)h * steps * 2 * KT * 64;
-    double acc[KT][4];
+    const f32x4* bfh = reinterpret_cast<const f32x4*>(bf) + (int64_t)h * steps * NF;
+    double acc[G][KT][4];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[kt][i] = 0.0;
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[g][kt][i] = 0.0;
+    f32x4 pre[NE];
+    auto fetch_b = [&](int st) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            if (tid + 256 * e < NF) pre[e] = bfh[(int64_t)st * NF + tid + 256 * e];
+    };
+    auto stage_b = [&](int buf) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            if (tid + 256 * e < NF) s_bf[buf][tid + 256 * e] = pre[e];
+    };
+    fetch_b(0);
+    stage_b(0);
+    __syncthreads();
     for (int st = 0; st < steps; ++st) {
-        f32x4 xa = {0.f, 0.f, 0.f, 0.f};
+        const int buf = st & 1;
+        if (st + 1 < steps) fetch_b(st + 1);
         const int d0 = 16 * st + 4 * q;
-        if (row_ok) {
+        f32x4 xa[G], x2[G];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (d0 + j < d_r) xa[j] = ld_elem<F32>(x, (bh * N + row) * d_r + d0 + j);
+        for (int g = 0; g < G; ++g) {
+            const int64_t row = base + 16 * (w + 4 * g) + r;
+            xa[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (row < N) {
+                const int64_t off = (bh * N + row) * d_r + d0;
+                if (vecx && d0 + 4 <= d_r) {
+                    if constexpr (F32) {
+                        xa[g] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(x) + off);
+                    } else {
+                        const u32x2 u = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(x) + off);
+                        xa[g] = f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                                      __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (d0 + j < d_r) xa[g][j] = ld_elem<F32>(x, off + j);
+                }
+            }
+            x2[g] = xa[g] * xa[g];
         }
-        const f32x4 x2 = xa * xa;
-        const f32x4* bs = bfh + (int64_t)st * 2 * KT * 64 + lane;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-            mma(c, x2, bs[kt * 64]);
-            mma(c, xa, bs[(KT + kt) * 64]);
+            const f32x4 bsq = s_bf[buf][kt * 64 + lane], blin = s_bf[buf][(KT + kt) * 64 + lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[kt][i] += (double)c[i];
+            for (int g = 0; g < G; ++g) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+                mma(c, x2[g], bsq);
+                mma(c, xa[g], blin);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[g][kt][i] += (double)c[i];
+            }
         }
+        if (st + 1 < steps) stage_b(buf ^ 1);
+        __syncthreads();
     }
     const double* cqh = cq + (int64_t)h * 16 * KT;
-    const int64_t row0 = ((int64_t)blockIdx.x % tiles) * 64 + 16 * w + 4 * q;   // accumulator rows 4 q + i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        double mx = -INFINITY;
-        double l[KT];
+    for (int g = 0; g < G; ++g) {
+        const int64_t row0 = base + 16 * (w + 4 * g) + 4 * q;   // accumulator rows 4 q + i of the group
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            l[kt] = cqh[16 * kt + r] + acc[kt][i];
-            mx = fmax(mx, l[kt]);
-        }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
-        float e[KT];
-        float sm = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            e[kt] = expf((float)(l[kt] - mx));
-            sm += e[kt];
-        }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
-        const float inv = 1.f / sm;
-        const int64_t rr = row0 + i;
-        if (rr < N) {
+        for (int i = 0; i < 4; ++i) {
+            double mx = -INFINITY;
+            double l[KT];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                const int k = 16 * kt + r;
-                if (k < K) gamma[(bh * N + rr) * K + k] = e[kt] * inv;
+                l[kt] = cqh[16 * kt + r] + acc[g][kt][i];
+                mx = fmax(mx, l[kt]);
+            }
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+            float e[KT];
+            float sm = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                e[kt] = expf((float)(l[kt] - mx));
+                sm += e[kt];
+            }
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
+            const float inv = 1.f / sm;
+            const int64_t rr = row0 + i;
+            if (rr < N) {
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    const int k = 16 * kt + r;
+                    if (k < K) gamma[(bh * N + rr) * K + k] = e[kt] * inv;
+                }
             }
         }
     }
@@ -512,9 +559,11 @@ void gemm_dispatch(const BwdGemm& g, bool out_bf16, int64_t grid, hipStream_t s)
 template <int KT>
 void gamma_mfma_dispatch(const void* x, bool f32, const float* bf, const double* cq, float* gamma, int64_t BH,
                          int64_t N, int H, int K, int d_r, hipStream_t s) {
-    const dim3 grid((unsigned)((N + 63) / 64 * BH));
-    if (f32) bwd_gamma_mfma_kernel<KT, true><<<grid, dim3(256), 0, s>>>(x, bf, cq, gamma, N, H, K, d_r);
-    else bwd_gamma_mfma_kernel<KT, false><<<grid, dim3(256), 0, s>>>(x, bf, cq, gamma, N, H, K, d_r);
+    constexpr int G = KT <= 8 ? 2 : 1;   // row groups per wave (fp64 accumulators: 8 G KT registers)
+    const dim3 grid((unsigned)((N + 64 * G - 1) / (64 * G) * BH));
+    const int vecx = (reinterpret_cast<uintptr_t>(x) % 16 == 0 && d_r % 4 == 0) ? 1 : 0;
+    if (f32) bwd_gamma_mfma_kernel<KT, G, true><<<grid, dim3(256), 0, s>>>(x, bf, cq, gamma, N, H, K, d_r, vecx);
+    else bwd_gamma_mfma_kernel<KT, G, false><<<grid, dim3(256), 0, s>>>(x, bf, cq, gamma, N, H, K, d_r, vecx);
 }
 
 }  // namespace
