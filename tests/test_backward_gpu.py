@@ -70,7 +70,7 @@ def check(w, inp, dout, causal, got, only=NAMES):
 
 @pytest.mark.parametrize("soft", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("cfg,N", [(0, 256), (1, 700), (2, 1100), (3, 700), (4, 300)])
+@pytest.mark.parametrize("cfg,N", [(0, 256), (1, 700), (2, 1100), (3, 2100), (4, 3001)])
 def test_backward_matches_oracle(gma, cfg, N, causal, soft):
     w = gma.workload(cfg)
     w = w.with_(batch=min(w.batch, 2), heads=min(w.heads, 2), seq_len=N)
@@ -154,3 +154,13 @@ def test_backward_cfg3_full_size_sampled_head(gma):
     sub = {k: (v[:, :1] if k in ("qx", "kx", "v") else v[:1]) for k, v in inp.items()}
     got0 = {k: (v[:, :1] if k in ("dqx", "dkx", "dv") else v[:1]) for k, v in got.items()}
     check(w.with_(heads=1), sub, dout[:, :1], True, got0)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_backward_full_size_every_head(gma, cfg):
+    # the fp32 causal (B4 H8 N4096 K64) and bf16 bidirectional (B32 H8 N4096 K32) workloads at full size,
+    # every (batch, head) against the oracle
+    w = gma.workload(cfg)
+    say("backward full size %s" % (w,))
+    inp, dout = inputs(gma, w, False)
+    check(w, inp, dout, w.causal, run_gpu(gma, w, inp, dout, w.causal))
