@@ -464,29 +464,34 @@ __global__ void __launch_bounds__(256) bwd_dx_kernel(const void* x, const float*
 }
 
 // ---------------------------------------------------------------------------------- scans
-// thread = one state element of one (batch, head); sequential over the n chunk entries
+// thread = one state element of one (batch, head); sequential over the n chunk entries, in groups of
+// 16 independent loads (then the group's running sums), so that loads are in flight back to back
 __global__ void __launch_bounds__(256) bwd_scan_kernel(float* st, int64_t n, int64_t rec, int mode) {
     const int64_t per = (rec + 255) / 256;   // workgroups per (batch, head)
     const int64_t e = ((int64_t)blockIdx.x % per) * 256 + threadIdx.x;
     if (e >= rec) return;
     float* base = st + ((int64_t)blockIdx.x / per) * n * rec + e;
     float run = 0.f;
-    if (mode == 0) {
-        for (int64_t c = 0; c < n; ++c) {
-            const float x = base[c * rec];
-            base[c * rec] = run;
-            run += x;
+    for (int64_t c0 = 0; c0 < n; c0 += 16) {
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t c = mode == 1 ? n - 1 - (c0 + j) : c0 + j;   // suffix: entries from the end
+            x[j] = (c0 + j < n) ? base[c * rec] : 0.f;
         }
-    } else if (mode == 1) {
-        for (int64_t c = n - 1; c >= 0; --c) {
-            const float x = base[c * rec];
-            base[c * rec] = run;
-            run += x;
+        if (mode == 2) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) run += x[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t c = mode == 1 ? n - 1 - (c0 + j) : c0 + j;
+                if (c0 + j < n) base[c * rec] = run;
+                run += x[j];
+            }
         }
-    } else {
-        for (int64_t c = 0; c < n; ++c) run += base[c * rec];
-        base[0] = run;
     }
+    if (mode == 2) base[0] = run;
 }
 
 // ---------------------------------------------------------------------------------- parameters
