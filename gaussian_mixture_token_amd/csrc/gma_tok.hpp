@@ -51,6 +51,9 @@ tok_kernel(const MainArgs a) {
     constexpr bool NEED_K = AGG || (MODE == MODE_OUT_CAUSAL);   // K_X staged, Gamma_K computed
     constexpr bool NEED_V = AGG || CAUSAL;
     constexpr bool OUT = NEED_Q;
+    // The aggregate passes (a plain sum over the segment's chunks) walk their chunks last to first,
+    // so that the chunks they touch last are the ones the causal output pass reads first.
+    constexpr bool REV = AGG;
     static_assert(MODE != MODE_RESP, "responsibilities use main_kernel");
     static_assert(DRC >= 64 && DRC % 64 == 0 && NSEG <= 2, "X rows are staged in one or two 128-byte segments");
     static_assert(KC % 32 == 0 && VC % 16 == 0, "tile shapes");
@@ -315,7 +318,7 @@ tok_kernel(const MainArgs a) {
         write_z();
     }
 
-    if (ch0 < ch1) issue(ch0, 0);
+    if (ch0 < ch1) issue(REV ? ch1 - 1 : ch0, 0);
     lds_barrier();   // s_c (and the bidirectional state) visible
 
     // Passes with one logits side (the aggregate passes: K; the stored-tile causal pass: Q) read the
@@ -477,8 +480,9 @@ tok_kernel(const MainArgs a) {
         lane_v = opaque_v(lane);
         [[maybe_unused]] const int lane = lane_v, lr = lane & 15, lg = lane >> 4;
         const uint32_t n0 = (uint32_t)(ch * C);
-        const bool first = ch == ch0;
-        const bool has_next = ch + 1 < ch1;
+        const bool first = REV ? ch == ch1 - 1 : ch == ch0;
+        const bool has_next = REV ? ch > ch0 : ch + 1 < ch1;
+        const int64_t nxt = REV ? ch - 1 : ch + 1;
         const lds_char* xw = LX + BUF * XBUF + w * XWAVE;
         const lds_char* vb = LV + (NEED_V ? BUF * VBUF : 0);
         const uint32_t tok = n0 + 16 * w + lr;
@@ -495,7 +499,7 @@ tok_kernel(const MainArgs a) {
             if constexpr (NEED_V) lds_barrier();   // B0
         }
         if constexpr (!CAUSAL && !AGG) {
-            if (has_next) issue(ch + 1, BUF ^ 1);
+            if (has_next) issue(nxt, BUF ^ 1);
         }
 
         if constexpr (MODE == MODE_OUT_BIDIR) {
@@ -573,7 +577,7 @@ tok_kernel(const MainArgs a) {
                         }
                     }
                     const int d0 = ks * NPARTS / NKS2, d1 = (ks + 1) * NPARTS / NKS2;
-                    if (p < d1 - d0 && has_next) issue_part(ch + 1, BUF ^ 1, d0 + p);
+                    if (p < d1 - d0 && has_next) issue_part(nxt, BUF ^ 1, d0 + p);
                 };
                 if constexpr (AGG) {
                     // Aggregate passes: tile order.  Component tile ct's chain of 2 NKS2 MFMAs accumulates
@@ -596,7 +600,7 @@ tok_kernel(const MainArgs a) {
                                 const int sl = (ct - 1) * NKS2 + ks;
 #pragma unroll
                                 for (int t = 0; t < EPS; ++t)
-                                    if (sl * EPS + t < NPARTS && has_next) issue_part(ch + 1, BUF ^ 1, sl * EPS + t);
+                                    if (sl * EPS + t < NPARTS && has_next) issue_part(nxt, BUF ^ 1, sl * EPS + t);
                             }
                             fence();
                         }
@@ -665,7 +669,7 @@ tok_kernel(const MainArgs a) {
                     }
                     // DMA parts: step ks issues the parts ks * NPARTS / NKS2 .. (ks + 1) * NPARTS / NKS2 - 1
                     const int d0 = ks * NPARTS / NKS2, d1 = (ks + 1) * NPARTS / NKS2;
-                    if (p < d1 - d0 && has_next) issue_part(ch + 1, BUF ^ 1, d0 + p);
+                    if (p < d1 - d0 && has_next) issue_part(nxt, BUF ^ 1, d0 + p);
                 };
                 // most pieces in one step: K and Q words, state fragments, Z, DMA parts
                 constexpr int NPA = 4 + 4 + (NPUB + NKS2 - 1) / NKS2 + 1 + (NPARTS + NKS2 - 1) / NKS2;
@@ -933,9 +937,16 @@ tok_kernel(const MainArgs a) {
         }
     };
 
-    for (int64_t ch = ch0; ch < ch1; ch += 2) {
-        body(std::integral_constant<int, 0>{}, ch);
-        if (ch + 1 < ch1) body(std::integral_constant<int, 1>{}, ch + 1);
+    if constexpr (REV) {
+        for (int64_t ch = ch1 - 1; ch >= ch0; ch -= 2) {
+            body(std::integral_constant<int, 0>{}, ch);
+            if (ch - 1 >= ch0) body(std::integral_constant<int, 1>{}, ch - 1);
+        }
+    } else {
+        for (int64_t ch = ch0; ch < ch1; ch += 2) {
+            body(std::integral_constant<int, 0>{}, ch);
+            if (ch + 1 < ch1) body(std::integral_constant<int, 1>{}, ch + 1);
+        }
     }
 
     if constexpr (AGG) {
