@@ -82,6 +82,12 @@ tok_kernel(const MainArgs a) {
     constexpr int NGS = GSTORE ? GKWAVE / 1024 : 0;   // Gamma_K tile stores per wave and chunk
     // vector-memory stores per wave and chunk, issued after the DMA of the next chunk
     constexpr int NST = OUT ? NVT : NGS;
+    // bidirectional read pass with d_v = VC: the wave's output rows go out as whole rows (16 bytes per
+    // lane) from an LDS staging area, NSTF stores per chunk instead of NVT
+    constexpr bool OROWS = MODE == MODE_OUT_BIDIR;
+    constexpr int OROW = VC * 2 + 16;               // staging row pitch (bytes), 16 bytes of padding
+    constexpr int NSTF = 16 * VC * 2 / 1024;        // 1 KiB row stores per wave and chunk
+    static_assert(!OROWS || (16 * VC * 2) % 1024 == 0, "output row stores");
     static_assert(NVB % W == 0 && (NVD == 0 || NVD == 2 || NVD == 4), "V blocks must split across waves");
     static_assert(GKWAVE % 1024 == 0, "Gamma_K tile blocks");
     static_assert(NXD + NVD + NGD + NST < 64, "vmcnt range");
@@ -97,6 +103,7 @@ tok_kernel(const MainArgs a) {
     __shared__ __attribute__((aligned(16))) char s_st[OUT ? NVT * NKQ * 1024 : 16];   // state^T fragments
     __shared__ __attribute__((aligned(16))) char s_zx[OUT ? NKQ * 1024 : 16];         // [Z_hi; Z_lo; 1; 0] fragments
     __shared__ __attribute__((aligned(16))) float s_c[KC];
+    __shared__ __attribute__((aligned(16))) char s_o[OROWS ? W * 16 * OROW : 16];
     // Z of the state before the current chunk: in registers of the owning wave, except in the pass
     // that computes both the K and the Q side (its registers are full), which keeps Z in LDS
     constexpr bool ZREG = MODE != MODE_OUT_CAUSAL;
@@ -108,6 +115,7 @@ tok_kernel(const MainArgs a) {
     lds_char* const LZX = (lds_char*)s_zx;
     lds_char* const LZ = (lds_char*)s_z;
     lds_char* const LC = (lds_char*)s_c;
+    lds_char* const LO = (lds_char*)s_o;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -495,6 +503,7 @@ tok_kernel(const MainArgs a) {
             block_barrier();   // B0
         } else {
             if (first) wait_vmcnt<NVD + NGD>();
+            else if (OROWS && d_v == VC) wait_vmcnt<NVD + NGD + NSTF>();
             else wait_vmcnt<NVD + NGD + NST>();
             if constexpr (NEED_V) lds_barrier();   // B0
         }
@@ -524,9 +533,27 @@ tok_kernel(const MainArgs a) {
                 mma(dx, lds_ld<bf16x8>(LZX + kq * 1024 + lane * 16), pq[kq]);
             }
             const float inv = fast_rcp(dx[0] + dx[1] + a.eps * dx[2]);
-            const uint32_t base = row_base(tok);
+            if (d_v == VC) {
+                // rows through LDS: lane (r, g) puts d_v 16 vt + 4g .. +3 of row r, then lane l takes
+                // 16 bytes (chunk l % (VC / 8)) of row i (64 / (VC / 8)) + l / (VC / 8) per store
+                lds_char* ow = LO + w * 16 * OROW;
 #pragma unroll
-            for (int vt = 0; vt < NVT; ++vt) store_tile(oacc[vt], inv, base, vt);
+                for (int vt = 0; vt < NVT; ++vt)
+                    lds_st<u32x2>(ow + lr * OROW + (16 * vt + 4 * lg) * 2, __builtin_bit_cast(u32x2, pack4(oacc[vt] * inv)));
+                asm volatile("" ::: "memory");
+                constexpr int CPR2 = VC / 8;        // 16-byte chunks per row
+                constexpr int RPS = 64 / CPR2;      // rows per store
+#pragma unroll
+                for (int i = 0; i < NSTF; ++i) {
+                    const int row = i * RPS + lane / CPR2, chunk = lane % CPR2;
+                    const u32x4 v = lds_ld<u32x4>(ow + row * OROW + chunk * 16);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rs_o, ((n0 + 16 * w + row) * d_v) * 2 + chunk * 16, 0, 0);
+                }
+            } else {
+                const uint32_t base = row_base(tok);
+#pragma unroll
+                for (int vt = 0; vt < NVT; ++vt) store_tile(oacc[vt], inv, base, vt);
+            }
             return;
         } else {
             // ---- P1
