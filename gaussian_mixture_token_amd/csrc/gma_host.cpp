@@ -38,6 +38,9 @@ gma_status_t fail(gma_status_t st, const char* fmt, ...) {
 // (not a device query) keeps the decomposition, and therefore every result bit, independent of
 // the device and of the HIP runtime state.
 constexpr int64_t kComputeUnits = 256;
+// bidirectional passes with at most this many segments per (batch, head) skip the scan kernel: the
+// read pass adds the segment records itself (in segment order, the scan's order)
+constexpr int kBidirReadSum = 4;
 
 int next_pow2(int x) {
     int p = 1;
@@ -634,14 +637,18 @@ gma_status_t forward(const gma_problem_t* p, int op, const void* qx, const void*
         st = timed_launch(K_AGG, s, [&] { f_agg(ag, agrid, s); });
         if (st != GMA_SUCCESS) return st;
     }
-    if (pl.P > 1 || rec_in || rec_out) {
+    const bool read_sum = !causal && pl.P <= kBidirReadSum;
+    if ((pl.P > 1 || rec_in || rec_out) && !read_sum) {
         st = timed_launch(K_SCAN, s, [&] {
             hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), BH), dim3(256), 0, s, a.seg, pl.P, rec,
                                causal ? 1 : 0, n_agg, (const float*)rec_in, rec_out);
         });
         if (st != GMA_SUCCESS) return st;
     }
-    if (!causal) return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, grid, s); });
+    if (!causal) {
+        a.bidir_segs = read_sum ? pl.P : 1;
+        return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, grid, s); });
+    }
     a.has_carry = pl.P > 1 || rec_in;
     st = timed_launch(K_OUT_CAUSAL, s, [&] { f_causal(a, grid, s); });
     if (st != GMA_SUCCESS || !rec_out) return st;
@@ -711,7 +718,8 @@ gma_status_t forward_bidir_kv(const gma_problem_t* p, int64_t n_kv, const void* 
     st = timed_launch(K_AGG, s, [&] { f_agg(ag, (int)(BH * plk.P), s); });
     if (st != GMA_SUCCESS) return st;
     const int64_t rec = (int64_t)plk.cls->kc * plk.cls->vc + plk.cls->kc;
-    if (plk.P > 1) {
+    const bool read_sum = plk.P <= kBidirReadSum;
+    if (plk.P > 1 && !read_sum) {
         st = timed_launch(K_SCAN, s, [&] {
             hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), (unsigned)BH), dim3(256), 0, s, ag.seg,
                                plk.P, rec, 0, plk.P, (const float*)nullptr, (float*)nullptr);
@@ -723,6 +731,7 @@ gma_status_t forward_bidir_kv(const gma_problem_t* p, int64_t n_kv, const void* 
     a.N = plq.N;
     a.Pg = plq.P;
     a.seg_chunks = plq.seg_chunks;
+    a.bidir_segs = read_sum ? plk.P : 1;
     a.qx = qx;
     a.o = o;
     a.vec_x = vec_ok(qx, plq.d_r, plq.f32);

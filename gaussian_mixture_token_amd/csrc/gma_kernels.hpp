@@ -90,6 +90,8 @@ struct MainArgs {
     int seg_chunks;        // chunks of C tokens per segment
     int vec_x, vec_v, vec_o;  // 16-byte (x, v) / 4-element (o) vector access allowed (register staging)
     int has_carry;         // causal: load the carried state (P > 1)
+    int bidir_segs;        // bidirectional read pass: segment records to sum in order (0 or 1: record 0
+                           // already holds the total)
     float eps;
 };
 
@@ -490,6 +492,18 @@ main_kernel(const MainArgs a) {
                                   : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         for (int k = tid; k < KC; k += NTHR) s_z[k] = load ? src[(int64_t)KC * VC + k] : 0.f;
+        if constexpr (MODE == MODE_OUT_BIDIR) {
+            // total over the segment records, added in segment order (the order of the scan kernel)
+            for (int t = 1; t < a.bidir_segs; ++t) {
+                const float* r = src + (int64_t)t * rec;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int vt = 0; vt < VT_W; ++vt)
+                        st[ct][vt] += *reinterpret_cast<const f32x4*>(r + ((int64_t)(ct * NVT + w * VT_W + vt) * 64 + lane) * 4);
+                for (int k = tid; k < KC; k += NTHR) s_z[k] += r[(int64_t)KC * VC + k];
+            }
+        }
     }
     lds_barrier();   // s_c and s_z visible to every wave
 

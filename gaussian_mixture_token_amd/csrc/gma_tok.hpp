@@ -276,6 +276,27 @@ tok_kernel(const MainArgs a) {
         } else {
             for (int k = tid; k < KC; k += 256) s_z[k] = load ? src[(int64_t)KC * VC + k] : 0.f;
         }
+        if constexpr (MODE == MODE_OUT_BIDIR) {
+            // total over the segment records, added in segment order (the order of the scan kernel)
+            for (int t = 1; t < a.bidir_segs; ++t) {
+                const float* r = src + (int64_t)t * rec;
+#pragma unroll
+                for (int kqi = 0; kqi < KQW; ++kqi)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int ct = 2 * (kq0 + kqi) + hh;
+#pragma unroll
+                        for (int vti = 0; vti < VTW; ++vti)
+                            st[kqi][hh][vti] += *reinterpret_cast<const f32x4*>(r + ((int64_t)(ct * NVT + vt0 + vti) * 64 + lane) * 4);
+                        if constexpr (ZREG) {
+                            if (zown) zst[kqi][hh] += *reinterpret_cast<const f32x4*>(r + (int64_t)KC * VC + ct * 16 + lg * 4);
+                        }
+                    }
+                if constexpr (!ZREG) {
+                    for (int k = tid; k < KC; k += 256) s_z[k] += r[(int64_t)KC * VC + k];
+                }
+            }
+        }
     }
     // bf16 state^T fragments: (vt, kq) is the A operand of O^T(vt) += state^T(vt, kq) . Gamma_Q^T(kq);
     // lane (r, g) holds d_v column 16 vt + r, components 32 kq + 4g + i and 32 kq + 16 + 4g + i
