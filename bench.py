@@ -56,6 +56,20 @@ def algorithmic_flops_per_token_head(w) -> int:
     return 8 * w.n_comp * w.d_route + 4 * w.n_comp * w.d_value
 
 
+def kernel_work_per_token_head(w, kernel: str):
+    """Algorithmic (bytes, flops) per token-head of one forward kernel, for its roofline.
+
+    causal_output: the path's figures (it reads Q_X, V and the stored Gamma_K tiles, the size of K_X
+    when K = d_r, and writes O; its flops are counted as the whole path's).  segment_aggregate reads
+    K_X and V (K-side logits, write); bidir_output reads Q_X and writes O (Q-side logits, read)."""
+    es = 2 if w.dtype == "bf16" else 4
+    if kernel == "segment_aggregate":
+        return es * (w.d_route + w.d_value), 4 * w.n_comp * w.d_route + 2 * w.n_comp * w.d_value
+    if kernel == "bidir_output":
+        return es * (w.d_route + w.d_value), 4 * w.n_comp * w.d_route + 2 * w.n_comp * w.d_value
+    return algorithmic_bytes_per_token_head(w), algorithmic_flops_per_token_head(w)
+
+
 def backward_bytes_per_token_head(w) -> int:
     # read Q_X, K_X, V, dL/dO; write dQ_X, dK_X, dV
     es = 2 if w.dtype == "bf16" else 4
@@ -221,8 +235,9 @@ def main():
         return
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     avg_s = kernels[dominant]["avg_us"] * 1e-6
-    alg_bytes = algorithmic_bytes_per_token_head(w) * T
-    alg_flops = algorithmic_flops_per_token_head(w) * T
+    kb, kf = kernel_work_per_token_head(w, dominant)
+    alg_bytes = kb * T
+    alg_flops = kf * T
     hbm_frac = alg_bytes / avg_s / 1e9 / HBM_PEAK_GBS
     mfma_frac = alg_flops / avg_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]
     src_hash = kernel_source_hash()
@@ -236,10 +251,13 @@ def main():
     roof.update({"kernel": dominant, "kernel_avg_us": kernels[dominant]["avg_us"],
                  "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": alg_flops,
                  "hbm_frac": hbm_frac, "mfma_frac": mfma_frac})
-    # whole-step fractions (all kernels of the step against the same algorithmic work)
+    # whole-step fractions (all kernels of the step against the path's algorithmic work)
     step_s = ms_per_step * 1e-3
-    step_roof = {"hbm_frac": alg_bytes / step_s / 1e9 / HBM_PEAK_GBS,
-                 "mfma_frac": alg_flops / step_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]}
+    path_bytes = algorithmic_bytes_per_token_head(w) * T
+    path_flops = algorithmic_flops_per_token_head(w) * T
+    step_roof = {"hbm_frac": path_bytes / step_s / 1e9 / HBM_PEAK_GBS,
+                 "mfma_frac": path_flops / step_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+                 "algorithmic_bytes_per_step": path_bytes, "algorithmic_flops_per_step": path_flops}
 
     cpu = None
     if not args.no_cpu_baseline:
