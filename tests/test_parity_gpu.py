@@ -107,6 +107,19 @@ def test_forward_cfg2_full_size_sampled_slices(gma, causal):
         assert err <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("batch", [32, 22, 16, 13])
+def test_bidirectional_segment_totals(gma, batch):
+    # K = 32 workload shape at 8 heads and N = 600 (10 chunks of 64): 512 workgroups over B*H heads give
+    # 2, 3, 4 and 5 segments per head.  Up to four, the read pass adds the segment records itself;
+    # with five, the scan kernel forms the total first.  Both must give the oracle's result.
+    w = gma.workload(2, batch=batch, seq_len=600)
+    say("bidirectional segment totals %s" % (w,))
+    inp = gma.make_inputs(w)
+    err = rel_err(gpu_forward(gma, w, inp, False), ref_forward(w, inp, False))
+    say("  rel err %.3e" % err)
+    assert err <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("cfg,N", [(3, 5000), (4, 3001)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_bf16_reduced_length_all_heads(gma, cfg, N, causal):
