@@ -9,7 +9,10 @@ With --backward a step is one call of the backward instead (forward recompute an
 gradient, from a seeded dL/dO); its line carries the whole step against the fp32 matrix-core
 roof, since every product of the backward runs in fp32.
 
-    python bench.py [--steps K] [--warmup W] [--workload I] [--backward] [--no-cpu-baseline]
+With --decode it times one-token causal decode steps at the workload's shape instead (mixture
+from the raw parameters every step, and prepared once), and prints their latency.
+
+    python bench.py [--steps K] [--warmup W] [--workload I] [--backward | --decode] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -141,6 +144,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=4)
     ap.add_argument("--backward", action="store_true", help="time the backward pass instead of the forward")
+    ap.add_argument("--decode", action="store_true",
+                    help="time one-token causal decode steps (raw and prepared mixture) at the workload's B, H, "
+                         "d_r, K, d_v instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) and exit; "
                          "its FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
@@ -169,6 +175,9 @@ def main():
     lib = _lib.load()
     w = gma.workload(args.workload)
     print("bench: workload %s" % w.name, file=sys.stderr, flush=True)
+    if args.decode:
+        decode_line(args, w, gma, dev)
+        return
     inp = gma.make_inputs(w)
     t = {k: v.to(dev) for k, v in inp.items()}
     del inp
@@ -317,6 +326,42 @@ def bwd_line(args, w, value, ms_per_step, kernels, T, dout):
                    "parallelism": "single GPU"},
         "roofline": roof, "kernels": kernels, "cpu_baseline": cpu, "source_hash": kernel_source_hash(backward=True),
     }
+    print(json.dumps(line), flush=True)
+
+
+def decode_line(args, w, gma, dev):
+    """Per-step time of gma_decode_step (mixture from the raw parameters every step) and of
+    gma_decode_step_prepared (mixture prepared once) on one token per (batch, head), state in place."""
+    import torch
+    w1 = w.with_(seq_len=max(args.steps, 1))
+    inp = gma.make_inputs(w1)
+    t = {k: v.to(dev) for k, v in inp.items()}
+    st = torch.zeros(w.batch, w.heads, w.n_comp, w.d_value + 1, dtype=torch.float32, device=dev)
+    out = torch.empty(w.batch, w.heads, 1, w.d_value, dtype=w.torch_dtype, device=dev)
+    rows = {k: [t[k][:, :, i:i + 1].contiguous() for i in range(w1.seq_len)] for k in ("qx", "kx", "v")}
+    res = {}
+    for mode in ("raw", "prepared"):
+        prep = gma.decode_prepare(t["raw_var"], t["prior_logits"]) if mode == "prepared" else None
+        for i in range(min(args.warmup, w1.seq_len)):
+            gma.decode_step(rows["qx"][i], rows["kx"][i], rows["v"][i], t["mu"], t["raw_var"], t["prior_logits"], st,
+                            eps=w.eps, out=out, prepared=prep)
+        st.zero_()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(w1.seq_len):
+            gma.decode_step(rows["qx"][i], rows["kx"][i], rows["v"][i], t["mu"], t["raw_var"], t["prior_logits"], st,
+                            eps=w.eps, out=out, prepared=prep)
+        e1.record()
+        torch.cuda.synchronize()
+        res[mode] = e0.elapsed_time(e1) * 1e3 / w1.seq_len
+        st.zero_()
+    line = {"metric": "GMA causal decode step latency (one token per (batch, head), state in place)",
+            "value": res["prepared"], "unit": "us/step", "n_gpus": 1, "steps": w1.seq_len, "warmup": args.warmup,
+            "higher_is_better": False, "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": w.name, "pass": "decode", "batch": w.batch, "heads": w.heads,
+                       "d_route": w.d_route, "n_comp": w.n_comp, "d_value": w.d_value},
+            "us_per_step": res}
     print(json.dumps(line), flush=True)
 
 

@@ -47,6 +47,10 @@ _SIGS = [
     ("gma_responsibility_stats", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                 ctypes.c_size_t, _VP]),
     ("gma_decode_step", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    ("gma_decode_params_size", ctypes.c_size_t, [ctypes.POINTER(Problem)]),
+    ("gma_decode_prepare", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    ("gma_decode_step_prepared", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP,
+                                                _VP, _VP, _VP]),
     ("gma_forward_causal_state", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                 ctypes.c_size_t, _VP]),
     ("gma_backward_bidir", ctypes.c_int, [ctypes.POINTER(Problem)] + [_VP] * 14 + [ctypes.c_size_t, _VP]),

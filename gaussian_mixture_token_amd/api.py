@@ -165,10 +165,36 @@ def forward(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, causal: boo
     return f(qx, kx, v, mu, raw_var, prior_logits, eps=eps, out=out, workspace=workspace)
 
 
-def decode_step(qx, kx, v, mu, raw_var, prior_logits, state, eps: float = 1e-6, out=None, state_out=None):
+def decode_prepare(raw_var, prior_logits, prepared=None):
+    """The decode step's mixture quantities (1 / softplus(raw_var) and the per-component constants) for
+    raw_var [H, K, d_r] and prior_logits [H, K], as a uint8 device tensor of gma_decode_params_size bytes
+    (written into `prepared` if given).  Pass it to decode_step(..., prepared=...) while the parameters
+    stay unchanged."""
+    H, K, d_r = raw_var.shape
+    if raw_var.dtype != torch.float32 or prior_logits.dtype != torch.float32 or tuple(prior_logits.shape) != (H, K):
+        raise ValueError("raw_var [H, K, d_r] and prior_logits [H, K] must be float32")
+    raw_var, prior_logits = raw_var.contiguous(), prior_logits.contiguous()
+    dev = _check_gpu(raw_var, prior_logits)
+    prob = problem(1, H, 1, d_r, K, 1, torch.float32)
+    lib = _lib.load()
+    nbytes = int(lib.gma_decode_params_size(ctypes.byref(prob)))
+    if nbytes == 0:
+        raise ValueError("unsupported mixture shape H=%d K=%d d_r=%d" % (H, K, d_r))
+    if prepared is None:
+        prepared = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check_gpu(prepared)
+    _lib.check(lib.gma_decode_prepare(ctypes.byref(prob), _ptr(raw_var), _ptr(prior_logits), _ptr(prepared),
+                                      prepared.numel() * prepared.element_size(), _stream(dev)))
+    return prepared
+
+
+def decode_step(qx, kx, v, mu, raw_var, prior_logits, state, eps: float = 1e-6, out=None, state_out=None,
+                prepared=None):
     """One causal decode step: qx, kx [B, H, 1, d_r] (or [B, H, d_r]), v [B, H, 1, d_v]; state float32
     [B, H, K, d_v + 1] (row k: Vt[k, :] then Z[k]) is the memory after all earlier tokens and is
-    updated in place unless state_out is given.  Returns the output row o [B, H, 1, d_v]."""
+    updated in place unless state_out is given.  Returns the output row o [B, H, 1, d_v].  With
+    `prepared` (decode_prepare of the same raw_var and prior_logits) the step reads the prepared
+    mixture instead of deriving it from raw_var and prior_logits."""
     if qx.dim() == 3:
         qx, kx, v = qx.unsqueeze(2), kx.unsqueeze(2), v.unsqueeze(2)
     qx, kx, v = qx.contiguous(), kx.contiguous(), v.contiguous()   # one-token slices of a longer sequence
@@ -191,6 +217,12 @@ def decode_step(qx, kx, v, mu, raw_var, prior_logits, state, eps: float = 1e-6, 
         out = torch.empty(B, H, 1, d_v, dtype=qx.dtype, device=dev)
     _check_gpu(out)
     dst = state if state_out is None else state_out
+    if prepared is not None:
+        _check_gpu(prepared)
+        _lib.check(_lib.load().gma_decode_step_prepared(
+            ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu), _ptr(prepared),
+            prepared.numel() * prepared.element_size(), _ptr(state), _ptr(dst), _ptr(out), _stream(dev)))
+        return out
     _lib.check(_lib.load().gma_decode_step(ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu), _ptr(raw_var),
                                            _ptr(prior_logits), _ptr(state), _ptr(dst), _ptr(out), _stream(dev)))
     return out

@@ -8,7 +8,9 @@
 //
 // A step touches K (d_r + d_v + 1) numbers per head: plain vector code, no matrix cores, 16 waves per
 // (batch, head).  Per-dimension terms (softplus, log, reciprocal) in fp32; the log-density sums
-// over d_r and the prior log-sum-exp in fp64; the state in fp32.
+// over d_r and the prior log-sum-exp in fp64; the state in fp32.  With a prepared mixture
+// (decode_prepare_kernel, once per parameter update) the step reads 1 / sigma^2 and the
+// per-component constants instead of deriving them from the raw parameters every token.
 #include "gma_decode.hpp"
 #include "gma_device.hpp"
 
@@ -50,7 +52,42 @@ __device__ __forceinline__ double wave_max(double x) {
 
 }  // namespace
 
-template <bool F32>
+// Per-component quantities of the decode step that depend on the mixture only, by one workgroup per
+// head: 1 / sigma^2 (softplus in fp32, as in the step) and c_k = log pi_k - 1/2 sum_d log sigma^2_kd
+// (the fp32 logs summed in fp64 by lanes over dims and fixed-order butterflies, the prior
+// log-sum-exp in fp64).  With them a step's log-density is c_k - 1/2 sum_d (x_d - mu_kd)^2 / sigma^2_kd.
+__global__ void __launch_bounds__(kThreads) decode_prepare_kernel(const DecodePrepArgs a) {
+    const int h = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int K = a.K, dr = a.d_r;
+    __shared__ double s_lse;
+    if (w == 0) {
+        double m = -INFINITY;
+        for (int k = lane; k < K; k += 64) m = fmax(m, (double)a.prior[(int64_t)h * K + k]);
+        m = wave_max(m);
+        double e = 0.0;
+        for (int k = lane; k < K; k += 64) e += exp((double)a.prior[(int64_t)h * K + k] - m);
+        e = wave_sum(e);
+        if (lane == 0) s_lse = m + log(e);
+    }
+    __syncthreads();
+    const double lse = s_lse;
+    for (int k = w; k < K; k += kWaves) {
+        double sl = 0.0;
+        for (int d = lane; d < dr; d += 64) {
+            const int64_t i = ((int64_t)h * K + k) * dr + d;
+            const float r = a.raw_var[i];
+            const float var = fmaxf(r, 0.f) + log1pf(expf(-fabsf(r)));   // softplus
+            a.inv_var[i] = 1.f / var;
+            sl += (double)logf(var);
+        }
+        sl = wave_sum(sl);
+        if (lane == 0) a.cconst[(int64_t)h * K + k] = ((double)a.prior[(int64_t)h * K + k] - lse) - 0.5 * sl;
+    }
+}
+
+// PREP: the mixture comes as mu plus the prepared 1 / sigma^2 and c_k (decode_prepare_kernel).
+template <bool F32, bool PREP>
 __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
     const int64_t bh = blockIdx.x;
     const int h = (int)(bh % a.H);
@@ -70,7 +107,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
     for (int j = tid; j < dv; j += kThreads) s_v[j] = load_elem<F32>(a.v, bh * dv + j);
 
     // log pi = prior - log-sum-exp(prior), by wave 0 (fixed-order butterflies)
-    if (w == 0) {
+    if (!PREP && w == 0) {
         double m = -INFINITY;
         for (int k = lane; k < K; k += 64) m = fmax(m, (double)a.prior[(int64_t)h * K + k]);
         m = wave_max(m);
@@ -80,7 +117,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
         if (lane == 0) s_red[0] = m + log(e);
     }
     __syncthreads();
-    const double lse = s_red[0];
+    const double lse = PREP ? 0.0 : s_red[0];
 
     // log-densities of the query and the key: l_k(x) = log pi_k - 1/2 sum_d [log var + (x - mu)^2 / var]
     // (the d_r/2 log 2 pi term is common to all components and cancels).  Wave w takes components
@@ -100,17 +137,22 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
             for (int u = 0; u < G; ++u) {
                 const int k = k0 + kWaves * u;
                 const int64_t i = ((int64_t)h * K + (k < K ? k : 0)) * dr + d;
-                r[u] = a.raw_var[i];
+                r[u] = PREP ? a.inv_var[i] : a.raw_var[i];
                 m[u] = a.mu[i];
             }
 #pragma unroll
             for (int u = 0; u < G; ++u) {
-                const float var = fmaxf(r[u], 0.f) + log1pf(expf(-fabsf(r[u])));   // softplus
-                const float inv = 1.f / var;
-                const float lv = logf(var);
                 const float dq = (float)xq - m[u], dk = (float)xk - m[u];
-                sq[u] += (double)(lv + dq * dq * inv);
-                sk[u] += (double)(lv + dk * dk * inv);
+                if constexpr (PREP) {
+                    sq[u] += (double)(dq * dq * r[u]);
+                    sk[u] += (double)(dk * dk * r[u]);
+                } else {
+                    const float var = fmaxf(r[u], 0.f) + log1pf(expf(-fabsf(r[u])));   // softplus
+                    const float inv = 1.f / var;
+                    const float lv = logf(var);
+                    sq[u] += (double)(lv + dq * dq * inv);
+                    sk[u] += (double)(lv + dk * dk * inv);
+                }
             }
         }
 #pragma unroll
@@ -118,7 +160,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
             const int k = k0 + kWaves * u;
             const double tq = wave_sum(sq[u]), tk = wave_sum(sk[u]);
             if (lane == 0 && k < K) {
-                const double lp = (double)a.prior[(int64_t)h * K + k] - lse;
+                const double lp = PREP ? a.cconst[(int64_t)h * K + k] : (double)a.prior[(int64_t)h * K + k] - lse;
                 s_lq[k] = lp - 0.5 * tq;
                 s_lk[k] = lp - 0.5 * tk;
             }
@@ -216,8 +258,18 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
 }
 
 void launch_decode(const DecodeArgs& a, int64_t bh, bool f32, hipStream_t s) {
-    if (f32) hipLaunchKernelGGL((decode_kernel<true>), dim3((unsigned)bh), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((decode_kernel<false>), dim3((unsigned)bh), dim3(kThreads), 0, s, a);
+    const dim3 g((unsigned)bh), b(kThreads);
+    if (a.inv_var) {
+        if (f32) hipLaunchKernelGGL((decode_kernel<true, true>), g, b, 0, s, a);
+        else hipLaunchKernelGGL((decode_kernel<false, true>), g, b, 0, s, a);
+    } else {
+        if (f32) hipLaunchKernelGGL((decode_kernel<true, false>), g, b, 0, s, a);
+        else hipLaunchKernelGGL((decode_kernel<false, false>), g, b, 0, s, a);
+    }
+}
+
+void launch_decode_prepare(const DecodePrepArgs& a, int heads, hipStream_t s) {
+    hipLaunchKernelGGL(decode_prepare_kernel, dim3((unsigned)heads), dim3(kThreads), 0, s, a);
 }
 
 }  // namespace gma

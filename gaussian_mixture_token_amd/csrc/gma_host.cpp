@@ -50,12 +50,12 @@ int next_pow2(int x) {
 
 enum KernelId {
     K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_STATS,
-    K_BWD_GAMMA, K_BWD_GEMM, K_BWD_ROWS, K_BWD_SCAN, K_BWD_PARAM, K_COUNT
+    K_BWD_GAMMA, K_BWD_GEMM, K_BWD_ROWS, K_BWD_SCAN, K_BWD_PARAM, K_DECODE_PREP, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan", "causal_output", "bidir_output",
                                      "responsibilities", "state_convert", "decode_step", "responsibility_stats",
                                      "backward_responsibilities", "backward_products", "backward_rows",
-                                     "backward_scan", "backward_parameters"};
+                                     "backward_scan", "backward_parameters", "decode_prepare"};
 
 struct Plan {
     const ShapeClass* cls = nullptr;
@@ -898,6 +898,91 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     });
 }
 
+// Prepared decode mixture: 1 / sigma^2 [H, K, d_r] fp32, then c [H, K] fp64 at a 256-byte boundary.
+struct DecodePrepLayout {
+    size_t off_c, total;
+};
+DecodePrepLayout decode_prep_layout(const gma_problem_t* p) {
+    DecodePrepLayout l;
+    l.off_c = align_up((size_t)p->heads * p->n_comp * p->d_route * sizeof(float), 256);
+    l.total = align_up(l.off_c + (size_t)p->heads * p->n_comp * sizeof(double), 256);
+    return l;
+}
+
+// Shared by the decode entry points: validation (host only, before any HIP call) and the launch.
+// With `prepared` the mixture is mu plus the gma_decode_prepare output; raw_var and prior_logits
+// are then unused (NULL).
+gma_status_t decode(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,
+                    const float* raw_var, const float* prior_logits, const void* prepared, size_t prepared_bytes,
+                    const float* state_in, float* state_out, void* o, void* stream) {
+    g_last_error.clear();
+    if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
+    if (p->batch < 1 || p->heads < 1) return fail(GMA_ERROR_INVALID_VALUE, "batch and heads must be >= 1");
+    if (p->seq_len != 1)
+        return fail(GMA_ERROR_INVALID_VALUE, "a decode step takes one token per (batch, head): seq_len must be 1");
+    if (p->d_route < 1 || p->n_comp < 1 || p->d_value < 1)
+        return fail(GMA_ERROR_INVALID_VALUE, "d_route, n_comp and d_value must be >= 1");
+    if (p->d_route > 256 || p->n_comp > 256 || p->d_value > 256)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "d_route, n_comp and d_value must be <= 256");
+    if (p->dtype != GMA_DTYPE_F32 && p->dtype != GMA_DTYPE_BF16)
+        return fail(GMA_ERROR_INVALID_VALUE, "dtype must be GMA_DTYPE_F32 or GMA_DTYPE_BF16 (got %d)", p->dtype);
+    if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(GMA_ERROR_INVALID_VALUE, "eps must be finite and >= 0");
+    if (p->batch > (int64_t(1) << 40) / p->heads || p->batch * p->heads > INT32_MAX / 2)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "batch * heads too large");
+    const void* ptrs[] = {qx, kx, v, mu, prepared ? prepared : (const void*)raw_var,
+                          prepared ? prepared : (const void*)prior_logits, o};
+    for (int i = 0; i < 7; ++i)
+        if (!ptrs[i]) return fail(GMA_ERROR_INVALID_VALUE, "pointer argument %d is NULL", i);
+    const bool f32 = p->dtype == GMA_DTYPE_F32;
+    const size_t es = f32 ? 4 : 2;
+    for (const void* ptr : {qx, kx, v, (const void*)o})
+        if (misaligned(ptr, es)) return fail(GMA_ERROR_INVALID_VALUE, "tensor pointers must be %zu-byte aligned", es);
+    for (const void* ptr : {(const void*)mu, (const void*)raw_var, (const void*)prior_logits, (const void*)state_in,
+                            (const void*)state_out})
+        if (misaligned(ptr, 4)) return fail(GMA_ERROR_INVALID_VALUE, "parameter and state pointers must be 4-byte aligned");
+    const DecodePrepLayout lay = decode_prep_layout(p);
+    if (prepared) {
+        if (misaligned(prepared, 256)) return fail(GMA_ERROR_INVALID_VALUE, "prepared must be 256-byte aligned");
+        if (prepared_bytes < lay.total)
+            return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "prepared holds %zu bytes, %zu needed", prepared_bytes, lay.total);
+    }
+    const int64_t BH = p->batch * p->heads;
+    const size_t nx = (size_t)BH * p->d_route * es, nv = (size_t)BH * p->d_value * es;
+    const size_t ns = (size_t)BH * p->n_comp * (p->d_value + 1) * sizeof(float);
+    if (overlaps(o, nv, qx, nx) || overlaps(o, nv, kx, nx) || overlaps(o, nv, v, nv))
+        return fail(GMA_ERROR_INVALID_VALUE, "o must not overlap qx, kx or v");
+    for (const void* sp : {(const void*)state_in, (const void*)state_out})
+        if (sp && (overlaps(sp, ns, qx, nx) || overlaps(sp, ns, kx, nx) || overlaps(sp, ns, v, nv) ||
+                   overlaps(sp, ns, o, nv) || (prepared && overlaps(sp, ns, prepared, lay.total))))
+            return fail(GMA_ERROR_INVALID_VALUE, "states must not overlap qx, kx, v, o or prepared");
+    if (prepared && overlaps(o, nv, prepared, lay.total))
+        return fail(GMA_ERROR_INVALID_VALUE, "o must not overlap prepared");
+    if (state_in && state_out && state_in != state_out && overlaps(state_in, ns, state_out, ns))
+        return fail(GMA_ERROR_INVALID_VALUE, "state_in and state_out must be the same buffer or disjoint");
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.qx = qx;
+    a.kx = kx;
+    a.v = v;
+    a.o = o;
+    a.mu = mu;
+    a.raw_var = prepared ? nullptr : raw_var;
+    a.prior = prepared ? nullptr : prior_logits;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.H = (int)p->heads;
+    a.K = p->n_comp;
+    a.d_r = p->d_route;
+    a.d_v = p->d_value;
+    a.eps = p->eps;
+    if (prepared) {
+        a.inv_var = reinterpret_cast<const float*>(prepared);
+        a.cconst = reinterpret_cast<const double*>(reinterpret_cast<const char*>(prepared) + lay.off_c);
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return timed_launch(K_DECODE, s, [&] { launch_decode(a, BH, f32, s); });
+}
+
 }  // namespace
 }  // namespace gma
 
@@ -1021,58 +1106,50 @@ gma_status_t gma_forward_bidir_kv(const gma_problem_t* p, int64_t seq_len_kv, co
 gma_status_t gma_decode_step(const gma_problem_t* p, const void* qx, const void* kx, const void* v, const float* mu,
                              const float* raw_var, const float* prior_logits, const float* state_in, float* state_out,
                              void* o, void* stream) {
+    return decode(p, qx, kx, v, mu, raw_var, prior_logits, nullptr, 0, state_in, state_out, o, stream);
+}
+
+size_t gma_decode_params_size(const gma_problem_t* p) {
+    if (!p || p->heads < 1 || p->n_comp < 1 || p->d_route < 1 || p->n_comp > 256 || p->d_route > 256) return 0;
+    return decode_prep_layout(p).total;
+}
+
+gma_status_t gma_decode_prepare(const gma_problem_t* p, const float* raw_var, const float* prior_logits,
+                                void* prepared, size_t prepared_bytes, void* stream) {
     g_last_error.clear();
     if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
-    if (p->batch < 1 || p->heads < 1) return fail(GMA_ERROR_INVALID_VALUE, "batch and heads must be >= 1");
-    if (p->seq_len != 1)
-        return fail(GMA_ERROR_INVALID_VALUE, "a decode step takes one token per (batch, head): seq_len must be 1");
-    if (p->d_route < 1 || p->n_comp < 1 || p->d_value < 1)
-        return fail(GMA_ERROR_INVALID_VALUE, "d_route, n_comp and d_value must be >= 1");
-    if (p->d_route > 256 || p->n_comp > 256 || p->d_value > 256)
-        return fail(GMA_ERROR_NOT_SUPPORTED, "d_route, n_comp and d_value must be <= 256");
-    if (p->dtype != GMA_DTYPE_F32 && p->dtype != GMA_DTYPE_BF16)
-        return fail(GMA_ERROR_INVALID_VALUE, "dtype must be GMA_DTYPE_F32 or GMA_DTYPE_BF16 (got %d)", p->dtype);
-    if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(GMA_ERROR_INVALID_VALUE, "eps must be finite and >= 0");
-    if (p->batch > (int64_t(1) << 40) / p->heads || p->batch * p->heads > INT32_MAX / 2)
-        return fail(GMA_ERROR_NOT_SUPPORTED, "batch * heads too large");
-    const void* ptrs[] = {qx, kx, v, mu, raw_var, prior_logits, o};
-    for (int i = 0; i < 7; ++i)
-        if (!ptrs[i]) return fail(GMA_ERROR_INVALID_VALUE, "pointer argument %d is NULL", i);
-    const bool f32 = p->dtype == GMA_DTYPE_F32;
-    const size_t es = f32 ? 4 : 2;
-    for (const void* ptr : {qx, kx, v, (const void*)o})
-        if (misaligned(ptr, es)) return fail(GMA_ERROR_INVALID_VALUE, "tensor pointers must be %zu-byte aligned", es);
-    for (const void* ptr : {(const void*)mu, (const void*)raw_var, (const void*)prior_logits, (const void*)state_in,
-                            (const void*)state_out})
-        if (misaligned(ptr, 4)) return fail(GMA_ERROR_INVALID_VALUE, "parameter and state pointers must be 4-byte aligned");
-    const int64_t BH = p->batch * p->heads;
-    const size_t nx = (size_t)BH * p->d_route * es, nv = (size_t)BH * p->d_value * es;
-    const size_t ns = (size_t)BH * p->n_comp * (p->d_value + 1) * sizeof(float);
-    if (overlaps(o, nv, qx, nx) || overlaps(o, nv, kx, nx) || overlaps(o, nv, v, nv))
-        return fail(GMA_ERROR_INVALID_VALUE, "o must not overlap qx, kx or v");
-    for (const void* sp : {(const void*)state_in, (const void*)state_out})
-        if (sp && (overlaps(sp, ns, qx, nx) || overlaps(sp, ns, kx, nx) || overlaps(sp, ns, v, nv) ||
-                   overlaps(sp, ns, o, nv)))
-            return fail(GMA_ERROR_INVALID_VALUE, "states must not overlap qx, kx, v or o");
-    if (state_in && state_out && state_in != state_out && overlaps(state_in, ns, state_out, ns))
-        return fail(GMA_ERROR_INVALID_VALUE, "state_in and state_out must be the same buffer or disjoint");
-    DecodeArgs a;
-    a.qx = qx;
-    a.kx = kx;
-    a.v = v;
-    a.o = o;
-    a.mu = mu;
+    if (p->heads < 1 || p->n_comp < 1 || p->d_route < 1)
+        return fail(GMA_ERROR_INVALID_VALUE, "heads, n_comp and d_route must be >= 1");
+    if (p->n_comp > 256 || p->d_route > 256) return fail(GMA_ERROR_NOT_SUPPORTED, "n_comp and d_route must be <= 256");
+    if (p->heads > INT32_MAX / 2) return fail(GMA_ERROR_NOT_SUPPORTED, "heads too large");
+    if (!raw_var || !prior_logits || !prepared)
+        return fail(GMA_ERROR_INVALID_VALUE, "raw_var, prior_logits and prepared must not be NULL");
+    for (const void* ptr : {(const void*)raw_var, (const void*)prior_logits})
+        if (misaligned(ptr, 4)) return fail(GMA_ERROR_INVALID_VALUE, "parameter pointers must be 4-byte aligned");
+    if (misaligned(prepared, 256)) return fail(GMA_ERROR_INVALID_VALUE, "prepared must be 256-byte aligned");
+    const DecodePrepLayout lay = decode_prep_layout(p);
+    if (prepared_bytes < lay.total)
+        return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "prepared holds %zu bytes, %zu needed", prepared_bytes, lay.total);
+    const size_t np = (size_t)p->heads * p->n_comp * p->d_route * sizeof(float);
+    if (overlaps(prepared, lay.total, raw_var, np))
+        return fail(GMA_ERROR_INVALID_VALUE, "prepared must not overlap the parameters");
+    if (overlaps(prepared, lay.total, prior_logits, (size_t)p->heads * p->n_comp * sizeof(float)))
+        return fail(GMA_ERROR_INVALID_VALUE, "prepared must not overlap the parameters");
+    DecodePrepArgs a;
     a.raw_var = raw_var;
     a.prior = prior_logits;
-    a.state_in = state_in;
-    a.state_out = state_out;
-    a.H = (int)p->heads;
+    a.inv_var = reinterpret_cast<float*>(prepared);
+    a.cconst = reinterpret_cast<double*>(reinterpret_cast<char*>(prepared) + lay.off_c);
     a.K = p->n_comp;
     a.d_r = p->d_route;
-    a.d_v = p->d_value;
-    a.eps = p->eps;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    return timed_launch(K_DECODE, s, [&] { launch_decode(a, BH, f32, s); });
+    return timed_launch(K_DECODE_PREP, s, [&] { launch_decode_prepare(a, (int)p->heads, s); });
+}
+
+gma_status_t gma_decode_step_prepared(const gma_problem_t* p, const void* qx, const void* kx, const void* v,
+                                      const float* mu, const void* prepared, size_t prepared_bytes,
+                                      const float* state_in, float* state_out, void* o, void* stream) {
+    return decode(p, qx, kx, v, mu, nullptr, nullptr, prepared, prepared_bytes, state_in, state_out, o, stream);
 }
 
 gma_status_t gma_forward_causal_state(const gma_problem_t* p, const void* qx, const void* kx, const void* v,

@@ -165,6 +165,33 @@ gma_status_t gma_decode_step(const gma_problem_t* problem, const void* qx, const
                              const float* prior_logits, const float* state_in, float* state_out,
                              void* o, void* stream);
 
+/* Decode with a prepared mixture (item 3, streaming).  gma_decode_step derives the variances and
+ * the prior from the raw parameters (softplus, log, log-sum-exp over K·d_r numbers) on every token;
+ * a decoder whose parameters are fixed between updates prepares them once instead:
+ *   gma_decode_params_size  bytes of the prepared form for problem->heads, n_comp, d_route
+ *                           (0 for an invalid problem): 1 / softplus(raw_var) [H, K, d_r] fp32, then,
+ *                           at the next 256-byte boundary, c_k = log pi_k - 1/2 sum_d log sigma^2_kd
+ *                           [H, K] fp64 (log pi = log-softmax of prior_logits).
+ *   gma_decode_prepare      writes that form into `prepared` (caller-owned device memory, 256-byte
+ *                           aligned, prepared_bytes >= gma_decode_params_size, disjoint from the
+ *                           parameters), asynchronously on `stream`.  Only heads, n_comp and
+ *                           d_route of the problem are read.
+ *   gma_decode_step_prepared  as gma_decode_step, with the mixture given by mu and `prepared`
+ *                           (raw_var and prior_logits are not read).  The log-density of a row x is
+ *                           c_k - 1/2 sum_d (x_d - mu_kd)^2 / sigma^2_kd: the same quantity as
+ *                           gma_decode_step's, summed in a different order (results agree to
+ *                           rounding).  `prepared` must be the output of gma_decode_prepare for the
+ *                           current parameters and must not overlap o or the states.
+ * Errors as gma_decode_step; GMA_ERROR_WORKSPACE_TOO_SMALL when prepared_bytes is too small. */
+size_t gma_decode_params_size(const gma_problem_t* problem);
+gma_status_t gma_decode_prepare(const gma_problem_t* problem, const float* raw_var,
+                                const float* prior_logits, void* prepared, size_t prepared_bytes,
+                                void* stream);
+gma_status_t gma_decode_step_prepared(const gma_problem_t* problem, const void* qx, const void* kx,
+                                      const void* v, const float* mu, const void* prepared,
+                                      size_t prepared_bytes, const float* state_in, float* state_out,
+                                      void* o, void* stream);
+
 /* Static description of a status code. */
 /* Backward of the bidirectional (gma_backward_bidir) or causal (gma_backward_causal) forward above:
  * the gradients of a scalar loss L with respect to every input, given dout = dL/dO [B, H, N, d_v].

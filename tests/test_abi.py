@@ -215,6 +215,36 @@ def test_decode_step_validation(lib):
     assert f(ctypes.byref(one), *ptrs, ctypes.c_void_p(0x80000000000 + 64), None, o, None) == 1   # state over o
 
 
+def test_decode_prepared_size_and_validation(lib):
+    one = _prob(seq_len=1)
+    # 1 / sigma^2 [H, K, d_r] fp32, then c [H, K] fp64 at a 256-byte boundary
+    lay = 16 * 128 * 128 * 4
+    assert lib.gma_decode_params_size(ctypes.byref(one)) == lay + 16 * 128 * 8
+    assert lib.gma_decode_params_size(ctypes.byref(_prob(heads=3, n_comp=5, d_route=7))) == 512 + 256
+    assert lib.gma_decode_params_size(None) == 0
+    assert lib.gma_decode_params_size(ctypes.byref(_prob(n_comp=257))) == 0
+    need = lib.gma_decode_params_size(ctypes.byref(one))
+    prep = ctypes.c_void_p(0x300000000000)
+    f = lib.gma_decode_prepare
+    assert f(None, FAKE, FAKE, prep, need, None) == 1
+    assert f(ctypes.byref(one), None, FAKE, prep, need, None) == 1
+    assert f(ctypes.byref(one), FAKE, FAKE, None, need, None) == 1
+    assert f(ctypes.byref(one), FAKE, FAKE, ctypes.c_void_p(0x300000000000 + 16), need, None) == 1   # not 256-aligned
+    assert f(ctypes.byref(one), FAKE, FAKE, prep, need - 1, None) == 3                                # too small
+    assert f(ctypes.byref(_prob(seq_len=1, n_comp=257)), FAKE, FAKE, prep, need, None) == 2
+    assert f(ctypes.byref(one), ctypes.c_void_p(0x300000000000 + 4096), FAKE, prep, need, None) == 1  # overlap
+    g = lib.gma_decode_step_prepared
+    ptrs = [FAKE, ctypes.c_void_p(0x20000000), ctypes.c_void_p(0x40000000), FAKE]
+    s, o = ctypes.c_void_p(0x200000000000), ctypes.c_void_p(0x80000000000)
+    assert g(None, *ptrs, prep, need, s, s, o, None) == 1
+    assert g(ctypes.byref(_prob(seq_len=2)), *ptrs, prep, need, s, s, o, None) == 1
+    assert g(ctypes.byref(one), *ptrs, None, need, s, s, o, None) == 1                # prepared NULL
+    assert g(ctypes.byref(one), *ptrs, prep, need - 8, s, s, o, None) == 3            # prepared too small
+    assert g(ctypes.byref(one), *ptrs, ctypes.c_void_p(0x300000000000 + 8), need, s, s, o, None) == 1
+    assert g(ctypes.byref(one), *ptrs, prep, need, ctypes.c_void_p(0x300000000000 + 64), None, o, None) == 1  # state over prepared
+    assert g(ctypes.byref(one), *ptrs, prep, need, s, s, ctypes.c_void_p(0x300000000000), None) == 1  # o over prepared
+
+
 def test_responsibility_stats_validation(lib):
     f = lib.gma_responsibility_stats
     prob = _prob(d_value=1)

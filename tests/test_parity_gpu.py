@@ -321,10 +321,12 @@ def test_causal_state_without_state_equals_plain_causal(gma):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("prepared", [False, True])
 @pytest.mark.parametrize("cfg,shape", [(3, None), (1, None), (4, None), (2, (37, 29, 45)), (0, (5, 3, 7))])
-def test_decode_steps_match_the_oracle(gma, cfg, shape):
+def test_decode_steps_match_the_oracle(gma, cfg, shape, prepared):
     # one-token steps from a zero state, updated in place, against the oracle's one pass over the
-    # same tokens (outputs and final state); any d_r, K, d_v <= 256
+    # same tokens (outputs and final state); any d_r, K, d_v <= 256.  prepared: the mixture is
+    # prepared once (gma_decode_prepare) and every step reads it
     T = 30
     kw = dict(batch=2, heads=2, seq_len=T)
     if shape:
@@ -336,13 +338,33 @@ def test_decode_steps_match_the_oracle(gma, cfg, shape):
                                                inp["prior_logits"], eps=w.eps)
     t = {k: v.to(DEV) for k, v in inp.items()}
     st = torch.zeros(2, 2, w.n_comp, w.d_value + 1, dtype=torch.float32, device=DEV)
+    prep = gma.decode_prepare(t["raw_var"], t["prior_logits"]) if prepared else None
     outs = [gma.decode_step(t["qx"][:, :, i:i + 1], t["kx"][:, :, i:i + 1], t["v"][:, :, i:i + 1], t["mu"],
-                            t["raw_var"], t["prior_logits"], st, eps=w.eps) for i in range(T)]
+                            t["raw_var"], t["prior_logits"], st, eps=w.eps, prepared=prep) for i in range(T)]
     torch.cuda.synchronize()
     err_o, err_s = _rel(torch.cat(outs, dim=2), o_ref), _rel(st, s_ref)
     say("  O err %.2e, state err %.2e" % (err_o, err_s))
     assert err_o <= TOL[w.dtype], err_o
     assert err_s <= TOL[w.dtype], err_s
+
+
+def test_decode_prepared_equals_raw_step_to_rounding(gma):
+    # the same 20 steps with the raw and with the prepared mixture: the log-densities differ only in
+    # summation order, so outputs and states agree far inside the tolerance
+    w = gma.workload(1, batch=2, heads=3, seq_len=20)
+    inp = gma.make_inputs(w)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    prep = gma.decode_prepare(t["raw_var"], t["prior_logits"])
+    sa = torch.zeros(2, 3, w.n_comp, w.d_value + 1, dtype=torch.float32, device=DEV)
+    sb = torch.zeros_like(sa)
+    for i in range(20):
+        args = (t["qx"][:, :, i:i + 1], t["kx"][:, :, i:i + 1], t["v"][:, :, i:i + 1], t["mu"], t["raw_var"],
+                t["prior_logits"])
+        oa = gma.decode_step(*args, sa, eps=w.eps)
+        ob = gma.decode_step(*args, sb, eps=w.eps, prepared=prep)
+        torch.cuda.synchronize()
+        assert _rel(ob, oa.double().cpu().numpy()) <= 1e-5, i
+    assert _rel(sb, sa.double().cpu().numpy()) <= 1e-5
 
 
 def test_decode_after_a_bulk_prefix(gma):
