@@ -76,12 +76,24 @@ struct Plan {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // vc < 0: any d_v class (the responsibilities kernel does not touch V).
+// The compiled class that covers the padded sizes (kc <= class K, vc <= class d_v, drc <= class d_r;
+// vc < 0: any d_v) with the least padded work per token, K (2 d_r + d_v); the first such class on a
+// tie.  Padding components get c = -inf (zero responsibilities), padding dims and columns zero
+// coefficients, so a larger class computes the same result.
 const ShapeClass* find_class(bool f32, int kc, int vc, int drc) {
     int n = 0;
     const ShapeClass* tab = f32 ? classes_f32(&n) : classes_bf16(&n);
-    for (int i = 0; i < n; ++i)
-        if (tab[i].kc == kc && (vc < 0 || tab[i].vc == vc) && tab[i].drc == drc) return &tab[i];
-    return nullptr;
+    const ShapeClass* best = nullptr;
+    int64_t best_cost = 0;
+    for (int i = 0; i < n; ++i) {
+        if (tab[i].kc < kc || (vc >= 0 && tab[i].vc < vc) || tab[i].drc < drc) continue;
+        const int64_t cost = (int64_t)tab[i].kc * (2 * tab[i].drc + (vc >= 0 ? tab[i].vc : 0));
+        if (!best || cost < best_cost) {
+            best = &tab[i];
+            best_cost = cost;
+        }
+    }
+    return best;
 }
 
 // Validates sizes (pure host) and fills the plan for the register-staged kernels or, with tok, for

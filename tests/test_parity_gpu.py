@@ -185,6 +185,22 @@ def test_bf16_padded_shapes(gma, shape, causal):
     assert err <= TOL[w.dtype], err
 
 
+@pytest.mark.parametrize("cfg,shape", [
+    (3, (64, 64, 64)), (3, (32, 16, 16)), (3, (1, 1, 1)), (3, (8, 100, 24)), (3, (16, 256, 16)), (3, (128, 64, 32)),
+    (1, (32, 32, 32)), (1, (3, 40, 5)),
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_shapes_served_by_a_larger_class(gma, cfg, shape, causal):
+    # (d_r, K, d_v) whose padded sizes match no compiled class exactly run on the cheapest class that
+    # covers them (padding components have zero responsibility, padding dims zero coefficients)
+    w = gma.workload(cfg, batch=1, heads=2, seq_len=300, d_route=shape[0], n_comp=shape[1], d_value=shape[2])
+    say("larger class %s causal=%s %s" % (shape, causal, w))
+    inp = gma.make_inputs(w)
+    err = rel_err(gpu_forward(gma, w, inp, causal), ref_forward(w, inp, causal))
+    say("  rel err %.3e" % err)
+    assert err <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("cfg,N", [(3, 5000), (4, 3001), (2, 2000)])
 def test_causal_without_room_for_stored_tiles(gma, cfg, N):
     # less than the advertised workspace: no stored Gamma_K tiles, the causal output pass recomputes
