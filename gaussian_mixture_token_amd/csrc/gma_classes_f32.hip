@@ -7,6 +7,7 @@ namespace gma {
 static const ShapeClass kClassesF32[] = {
     GMA_SHAPE_CLASS_F32(16, 16, 16, 1, 64),
     GMA_SHAPE_CLASS_F32(64, 64, 64, 4, 64),
+    GMA_SHAPE_CLASS_F32(128, 128, 128, 4, 32),
 };
 
 const ShapeClass* classes_f32(int* count) {

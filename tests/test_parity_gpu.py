@@ -60,10 +60,12 @@ def rel_err(o, ref):
 # ------------------------------------------------------------------------------------ responsibilities
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_responsibilities_match_oracle(gma, cfg):
+@pytest.mark.parametrize("cfg,shape", [(0, None), (1, None), (2, None), (3, None), (4, None), (1, (128, 128, 128))])
+def test_responsibilities_match_oracle(gma, cfg, shape):
     w = gma.workload(cfg)
     w = w.with_(batch=1, heads=min(w.heads, 2), seq_len=min(w.seq_len, 1000))
+    if shape:
+        w = w.with_(d_route=shape[0], n_comp=shape[1], d_value=shape[2])
     say("responsibilities cfg%d %s" % (cfg, w))
     inp = gma.make_inputs(w)
     t = {k: v.to(DEV) for k, v in inp.items()}
@@ -187,7 +189,7 @@ def test_bf16_padded_shapes(gma, shape, causal):
 
 @pytest.mark.parametrize("cfg,shape", [
     (3, (64, 64, 64)), (3, (32, 16, 16)), (3, (1, 1, 1)), (3, (8, 100, 24)), (3, (16, 256, 16)), (3, (128, 64, 32)),
-    (1, (32, 32, 32)), (1, (3, 40, 5)),
+    (1, (32, 32, 32)), (1, (3, 40, 5)), (1, (128, 128, 128)), (1, (100, 70, 90)), (1, (65, 128, 16)),
 ])
 @pytest.mark.parametrize("causal", [False, True])
 def test_shapes_served_by_a_larger_class(gma, cfg, shape, causal):
