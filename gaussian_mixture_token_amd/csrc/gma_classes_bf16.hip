@@ -10,6 +10,7 @@ static const ShapeClass kClassesBf16[] = {
     GMA_SHAPE_CLASS_BF16(32, 64, 64, 2, 32, 2, 2),
     GMA_SHAPE_CLASS_BF16(128, 128, 128, 4, 32, 2, 1),
     GMA_SHAPE_CLASS_BF16(256, 64, 64, 4, 32, 1, 1),
+    GMA_SHAPE_CLASS_BF16_NOTOK(256, 128, 128, 4, 32, 1),
 };
 
 const ShapeClass* classes_bf16(int* count) {

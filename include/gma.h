@@ -35,11 +35,11 @@
  *              GMA_ERROR_LAUNCH reports a failed kernel launch.  gma_last_error() gives a
  *              human-readable message for the last failing call on the calling thread.
  *   Limits     1 <= d_r, K, d_v <= 256; B, H, N >= 1.  Shapes are padded internally to a compiled
- *              tile class (K, d_v, d_r): bf16 (32, 64, 64), (128, 128, 128), (256, 64, 64); fp32
- *              (16, 16, 16), (64, 64, 64), (128, 128, 128).  The cheapest class that covers the
- *              shape runs it (padding components get zero responsibility, padding dims zero
- *              coefficients); a shape that no class covers (bf16: d_r or d_v > 64 with K > 128;
- *              fp32: any size > 128) returns GMA_ERROR_NOT_SUPPORTED.  gma_decode_step and the backward have no classes.
+ *              tile class (K, d_v, d_r): bf16 (32, 64, 64), (128, 128, 128), (256, 64, 64),
+ *              (256, 128, 128); fp32 (16, 16, 16), (64, 64, 64), (128, 128, 128).  The cheapest class
+ *              that covers the shape runs it (padding components get zero responsibility, padding
+ *              dims zero coefficients); a shape that no class covers (d_r or d_v > 128) returns
+ *              GMA_ERROR_NOT_SUPPORTED.  gma_decode_step and the backward have no classes.
  *   Results    deterministic: repeated calls give bitwise identical outputs (no atomics; every
  *              reduction runs in a fixed order independent of the device).
  */

@@ -60,7 +60,8 @@ def rel_err(o, ref):
 # ------------------------------------------------------------------------------------ responsibilities
 
 
-@pytest.mark.parametrize("cfg,shape", [(0, None), (1, None), (2, None), (3, None), (4, None), (1, (128, 128, 128))])
+@pytest.mark.parametrize("cfg,shape", [(0, None), (1, None), (2, None), (3, None), (4, None), (1, (128, 128, 128)),
+                                       (3, (128, 256, 128))])
 def test_responsibilities_match_oracle(gma, cfg, shape):
     w = gma.workload(cfg)
     w = w.with_(batch=1, heads=min(w.heads, 2), seq_len=min(w.seq_len, 1000))
@@ -189,6 +190,7 @@ def test_bf16_padded_shapes(gma, shape, causal):
 
 @pytest.mark.parametrize("cfg,shape", [
     (3, (64, 64, 64)), (3, (32, 16, 16)), (3, (1, 1, 1)), (3, (8, 100, 24)), (3, (16, 256, 16)), (3, (128, 64, 32)),
+    (3, (128, 256, 128)), (3, (100, 200, 60)), (3, (96, 180, 128)),
     (1, (32, 32, 32)), (1, (3, 40, 5)), (1, (128, 128, 128)), (1, (100, 70, 90)), (1, (65, 128, 16)),
 ])
 @pytest.mark.parametrize("causal", [False, True])
