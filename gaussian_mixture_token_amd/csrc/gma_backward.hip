@@ -61,7 +61,9 @@ constexpr int GM = 64, GN = 64, GK = 32, GLD = 80;   // tile, inner step, LDS ro
 // LDS writes cover 64 consecutive columns of one inner row.  Of an operand whose outer index is
 // contiguous: thread t takes inner row t / 8 and columns 8 (t % 8) .. + 7.  Eight consecutive
 // elements inside the matrix are fetched as two 16-byte loads where the view allows it (vec*).
-template <bool TA, bool TB, bool OUT_BF16>
+// BX: B is generated from the routing rows (BwdGemm::Bx), [x | x^2 | 1 | 0 ...] per row, instead of being
+// read from a materialised matrix.
+template <bool TA, bool TB, bool OUT_BF16, bool BX = false>
 __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     __shared__ float s_a[GK][GLD];
     __shared__ float s_b[GK][GLD];
@@ -81,7 +83,8 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     if (m0 >= M || n0 >= N) return;   // whole workgroup: the tile lies past a ragged end
 
     const float* A = g.A + outer * g.sA0 + (int64_t)inner * g.sA1;
-    const float* B = g.B + (g.modB > 0 ? outer % g.modB : outer) * g.sB0 + (int64_t)inner * g.sB1;
+    const float* B = BX ? nullptr : g.B + (g.modB > 0 ? outer % g.modB : outer) * g.sB0 + (int64_t)inner * g.sB1;
+    const int64_t bx0 = BX ? outer * g.sB0 + (int64_t)inner * g.sB1 : 0;   // element offset of the rows of x
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
     const int r = lane & 15, q = lane >> 4;
@@ -113,10 +116,55 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     float ra[8], rb[8];
     const int ri = tid & 63, ki = (tid >> 6) * 8;     // contiguous-inner mapping
     const int ko = tid >> 3, co = (tid & 7) * 8;      // contiguous-outer mapping
+    // columns c .. c+7 of row k of [x | x^2 | 1 | 0 ...] (BX): a whole vector of x or of x^2 where the
+    // eight columns fall inside one part and x allows 16-byte loads, element by element otherwise
+    auto fetch_xaug = [&](int k, bool k_ok, int c, int cn, float (&v)[8]) {
+        const int dr = g.bx_dr;
+        const int64_t row = bx0 + (int64_t)k * dr;
+        auto ld = [&](int d) -> float {
+            if (g.bx_f32) return reinterpret_cast<const float*>(g.Bx)[row + d];
+            return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(g.Bx)[row + d] << 16);
+        };
+        const int part = (c + 8 <= dr) ? 0 : (c >= dr && c + 8 <= 2 * dr) ? 1 : 2;
+        if (k_ok && part < 2 && c + 8 <= cn && g.vecB) {
+            const int d0 = part ? c - dr : c;
+            float x[8];
+            if (g.bx_f32) {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(g.Bx) + row + d0);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(g.Bx) + row + d0 + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { x[j] = lo[j]; x[4 + j] = hi[j]; }
+            } else {
+                const u32x4 h = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(g.Bx) + row + d0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[2 * j] = __uint_as_float(h[j] << 16);
+                    x[2 * j + 1] = __uint_as_float(h[j] & 0xffff0000u);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = part ? x[j] * x[j] : x[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int col = c + j;
+                float val = 0.f;
+                if (k_ok && col < cn) {
+                    if (col < dr) val = ld(col);
+                    else if (col < 2 * dr) {
+                        const float t = ld(col - dr);
+                        val = t * t;
+                    } else if (col == 2 * dr) val = 1.f;
+                }
+                v[j] = val;
+            }
+        }
+    };
     auto fetch = [&](int k0) {
         if constexpr (!TA) fetch_inner(A, g.lda, g.vecA, m0 + ri, m0 + ri < M, k0 + ki, Kd, ra);
         else fetch_outer(A, g.lda, g.vecA, k0 + ko, k0 + ko < Kd, m0 + co, M, ra);
-        if constexpr (TB) fetch_inner(B, g.ldb, g.vecB, n0 + ri, n0 + ri < N, k0 + ki, Kd, rb);
+        if constexpr (BX) fetch_xaug(k0 + ko, k0 + ko < Kd, n0 + co, N, rb);
+        else if constexpr (TB) fetch_inner(B, g.ldb, g.vecB, n0 + ri, n0 + ri < N, k0 + ki, Kd, rb);
         else fetch_outer(B, g.ldb, g.vecB, k0 + ko, k0 + ko < Kd, n0 + co, N, rb);
     };
     auto stage = [&]() {
@@ -402,23 +450,6 @@ __global__ void __launch_bounds__(256) bwd_vaug_kernel(const void* v, float* vau
     }
 }
 
-template <bool F32>
-__global__ void __launch_bounds__(256) bwd_xaug_kernel(const void* x, float* xaug, int64_t rows, int d_r, int dxa) {
-    const int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock;
-    for (int i = 0; i < kRowsPerBlock && r0 + i < rows; ++i) {
-        const int64_t rr = r0 + i;
-        for (int c = threadIdx.x; c < dxa; c += 256) {
-            float val;
-            if (c < d_r) val = ld_elem<F32>(x, rr * d_r + c);
-            else if (c < 2 * d_r) {
-                const float t = ld_elem<F32>(x, rr * d_r + c - d_r);
-                val = t * t;
-            } else val = (c == 2 * d_r) ? 1.f : 0.f;
-            xaug[rr * dxa + c] = val;
-        }
-    }
-}
-
 // one wavefront per row; lane l holds columns l, l + 64, ...
 template <bool F32>
 __global__ void __launch_bounds__(256) bwd_gh_kernel(const float* p, const void* dout, float* gh, int64_t rows, int d_v,
@@ -582,6 +613,13 @@ void launch_bwd_gemm(const BwdGemm& g0, bool ta, bool tb, bool out_bf16, hipStre
         return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0 && s0 % 4 == 0 && s1 % 4 == 0 && mod >= 0;
     };
     g.vecA = vec_ok(g.A, g.lda, g.sA0, g.sA1, 0);
+    if (g.Bx) {
+        // 16-byte loads of eight x elements: fp32 needs 4-element, bf16 8-element aligned rows
+        const int q = g.bx_f32 ? 4 : 8;
+        g.vecB = reinterpret_cast<uintptr_t>(g.Bx) % 16 == 0 && g.bx_dr % 8 == 0 && g.sB0 % q == 0 && g.sB1 % q == 0;
+        bwd_gemm_kernel<true, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
+        return;
+    }
     g.vecB = vec_ok(g.B, g.ldb, g.sB0, g.sB1, g.modB);
     if (!ta && !tb) gemm_dispatch<false, false>(g, out_bf16, grid, s);
     else if (!ta && tb) gemm_dispatch<false, true>(g, out_bf16, grid, s);
@@ -618,12 +656,6 @@ void launch_bwd_vaug(const void* v, bool f32, float* vaug, int64_t rows, int d_v
     const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     if (f32) bwd_vaug_kernel<true><<<grid, dim3(256), 0, s>>>(v, vaug, rows, d_v, dva);
     else bwd_vaug_kernel<false><<<grid, dim3(256), 0, s>>>(v, vaug, rows, d_v, dva);
-}
-
-void launch_bwd_xaug(const void* x, bool f32, float* xaug, int64_t rows, int d_r, int dxa, hipStream_t s) {
-    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-    if (f32) bwd_xaug_kernel<true><<<grid, dim3(256), 0, s>>>(x, xaug, rows, d_r, dxa);
-    else bwd_xaug_kernel<false><<<grid, dim3(256), 0, s>>>(x, xaug, rows, d_r, dxa);
 }
 
 void launch_bwd_gh(const float* p, const void* dout, bool f32, float* gh, int64_t rows, int d_v, int dva, float eps,

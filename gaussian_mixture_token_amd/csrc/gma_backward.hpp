@@ -35,6 +35,11 @@ struct BwdGemm {
     // set by launch_bwd_gemm: 16-byte loads are allowed (base 16-byte aligned, leading dimension and
     // batch strides multiples of 4 elements)
     bool vecA = false, vecB = false;
+    // B generated from routing rows instead of read (B not transposed, A transposed, fp32 output): row k
+    // of B is [x_k | x_k^2 | 1 | 0 ...] over N columns, x_k the d_r elements at Bx + row offset
+    // (sB0, sB1, ldb = bx_dr in elements of x; fp32 or bf16 storage)
+    const void* Bx = nullptr;
+    int bx_f32 = 0, bx_dr = 0;
 };
 void launch_bwd_gemm(const BwdGemm& g, bool ta, bool tb, bool out_bf16, hipStream_t s);
 
@@ -55,7 +60,6 @@ void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const doubl
 // [V | 1 | 0...] rows of width dva (fp32) from v [rows, d_v].
 void launch_bwd_vaug(const void* v, bool f32, float* vaug, int64_t rows, int d_v, int dva, hipStream_t s);
 // [x | x^2 | 1 | 0...] rows of width dxa (fp32) from x [rows, d_r].
-void launch_bwd_xaug(const void* x, bool f32, float* xaug, int64_t rows, int d_r, int dxa, hipStream_t s);
 // Read-phase gradient per row: p [rows, dva] holds (num | Gamma_Q . Z, the denominator without
 // eps); gh [rows, dva] <- (g = dO / den | h = -(dO . O) / den | 0...).
 void launch_bwd_gh(const float* p, const void* dout, bool f32, float* gh, int64_t rows, int d_v, int dva, float eps,
