@@ -63,7 +63,8 @@ constexpr int GM = 64, GN = 64, GK = 32, GLD = 80;   // tile, inner step, LDS ro
 // elements inside the matrix are fetched as two 16-byte loads where the view allows it (vec*).
 // BX: B is generated from the routing rows (BwdGemm::Bx), [x | x^2 | 1 | 0 ...] per row, instead of being
 // read from a materialised matrix.
-template <bool TA, bool TB, bool OUT_BF16, bool BX = false>
+// DX: the routing-input gradient epilogue (BwdGemm::dx_x).
+template <bool TA, bool TB, bool OUT_BF16, bool BX = false, bool DX = false>
 __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     __shared__ float s_a[GK][GLD];
     __shared__ float s_b[GK][GLD];
@@ -220,6 +221,28 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     }
 
     const int64_t coff = outer * g.sC0 + (int64_t)inner * g.sC1;
+    if constexpr (DX) {
+        // lanes r and r ^ 1 hold columns 2d and 2d + 1 of the same row: the even lane forms dx of dim d
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float val = acc[mt][nt][i];
+                    const float oth = __shfl_xor(val, 1, 64);
+                    const int m = m0 + wm + mt * 16 + 4 * q + i, n = n0 + wn + nt * 16 + r;
+                    if (m >= M || n >= N || (r & 1)) continue;
+                    const int64_t o = coff + (int64_t)m * g.ldc + (n >> 1);
+                    float xv;
+                    if constexpr (OUT_BF16) xv = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(g.dx_x)[o] << 16);
+                    else xv = reinterpret_cast<const float*>(g.dx_x)[o];
+                    const float dxv = val - xv * oth;
+                    if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = bf16_bits(dxv);
+                    else reinterpret_cast<float*>(g.C)[o] = dxv;
+                }
+        return;
+    }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -307,8 +330,8 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const float* mu, const fl
         const float rv = r_h[e];
         const float s = fmaxf(rv, 0.f) + log1pf(expf(-fabsf(rv)));   // softplus
         const float wv = 1.f / s;
-        mw_h[(int64_t)k * 2 * d_r + d] = m_h[e] * wv;
-        mw_h[(int64_t)k * 2 * d_r + d_r + d] = wv;
+        mw_h[(int64_t)k * 2 * d_r + 2 * d] = m_h[e] * wv;
+        mw_h[(int64_t)k * 2 * d_r + 2 * d + 1] = wv;
     }
 }
 
@@ -483,17 +506,6 @@ __global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* 
     for (int k = lane; k < K; k += 64) dr[k] = gr[k] * (dr[k] - dot);
 }
 
-template <bool F32>
-__global__ void __launch_bounds__(256) bwd_dx_kernel(const void* x, const float* p12, void* dx, int64_t rows, int d_r) {
-    const int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock;
-    for (int i = 0; i < kRowsPerBlock && r0 + i < rows; ++i) {
-        const int64_t rr = r0 + i;
-        const float* pr = p12 + rr * 2 * d_r;
-        for (int d = threadIdx.x; d < d_r; d += 256)
-            st_elem<F32>(dx, rr * d_r + d, pr[d] - ld_elem<F32>(x, rr * d_r + d) * pr[d_r + d]);
-    }
-}
-
 // ---------------------------------------------------------------------------------- scans
 // thread = one state element of one (batch, head); sequential over the n chunk entries, in groups of
 // 16 independent loads (then the group's running sums), so that loads are in flight back to back
@@ -613,6 +625,12 @@ void launch_bwd_gemm(const BwdGemm& g0, bool ta, bool tb, bool out_bf16, hipStre
         return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0 && s0 % 4 == 0 && s1 % 4 == 0 && mod >= 0;
     };
     g.vecA = vec_ok(g.A, g.lda, g.sA0, g.sA1, 0);
+    if (g.dx_x) {
+        g.vecB = vec_ok(g.B, g.ldb, g.sB0, g.sB1, g.modB);
+        if (out_bf16) bwd_gemm_kernel<false, false, true, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
+        else bwd_gemm_kernel<false, false, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
+        return;
+    }
     if (g.Bx) {
         // 16-byte loads of eight x elements: fp32 needs 4-element, bf16 8-element aligned rows
         const int q = g.bx_f32 ? 4 : 8;
@@ -667,12 +685,6 @@ void launch_bwd_gh(const float* p, const void* dout, bool f32, float* gh, int64_
 
 void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream_t s) {
     bwd_dl_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(gamma, dg, rows, K);
-}
-
-void launch_bwd_dx(const void* x, const float* p12, void* dx, bool f32, int64_t rows, int d_r, hipStream_t s) {
-    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-    if (f32) bwd_dx_kernel<true><<<grid, dim3(256), 0, s>>>(x, p12, dx, rows, d_r);
-    else bwd_dx_kernel<false><<<grid, dim3(256), 0, s>>>(x, p12, dx, rows, d_r);
 }
 
 void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mode, hipStream_t s) {

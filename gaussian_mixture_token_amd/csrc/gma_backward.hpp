@@ -40,11 +40,15 @@ struct BwdGemm {
     // (sB0, sB1, ldb = bx_dr in elements of x; fp32 or bf16 storage)
     const void* Bx = nullptr;
     int bx_f32 = 0, bx_dr = 0;
+    // routing-input gradient in the epilogue (A, B not transposed): the product's columns come in pairs
+    // (2d, 2d + 1) = (dl . mu / s, dl . 1 / s) of dim d, and the output is dx[m][d] = C[m][2d] -
+    // dx_x[m][d] C[m][2d + 1] in the storage dtype (OUT_BF16), at the C strides (ldc = d_r)
+    const void* dx_x = nullptr;
 };
 void launch_bwd_gemm(const BwdGemm& g, bool ta, bool tb, bool out_bf16, hipStream_t s);
 
-// Mixture constants for the routing-input gradient: mw [H, K, 2 d_r] (row k: mu_kd / s_kd for d < d_r,
-// then 1 / s_kd; s = softplus(raw_var)).
+// Mixture constants for the routing-input gradient: mw [H, K, 2 d_r] (row k: mu_kd / s_kd and 1 / s_kd
+// interleaved, at columns 2d and 2d + 1; s = softplus(raw_var)).
 void launch_bwd_prep(const float* mu, const float* raw_var, float* mw, int H, int K, int d_r, hipStream_t s);
 
 // Responsibilities of rows x [BH, N, d_r] (bf16 or fp32) in fp32 -> gamma [BH, N, K], on the matrix
@@ -66,8 +70,6 @@ void launch_bwd_gh(const float* p, const void* dout, bool f32, float* gh, int64_
                    hipStream_t s);
 // Softmax gradient in place: dl = gamma (dgamma - gamma . dgamma) per row of K.
 void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream_t s);
-// Routing-input gradient: dx = p12[:, :d_r] - x * p12[:, d_r:] (dx in the storage dtype).
-void launch_bwd_dx(const void* x, const float* p12, void* dx, bool f32, int64_t rows, int d_r, hipStream_t s);
 // Chunk-state scans over [n_outer][n][rec]: mode 0 exclusive prefix in place, 1 exclusive suffix in
 // place, 2 the total into entry 0.
 void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mode, hipStream_t s);

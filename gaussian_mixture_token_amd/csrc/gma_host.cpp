@@ -212,7 +212,7 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
 
 // Backward workspace: fp32 intermediates of the gradient, each region 256-byte aligned.
 //   bf, cq                                    matrix-core log-density operands (launch_bwd_frag)
-//   mw [H, K, 2 d_r]                          mixture constants mu / s | 1 / s
+//   mw [H, K, 2 d_r]                          mixture constants mu / s and 1 / s, interleaved by dim
 //   gq, gk, dgq, dgk [BH, N, K]               responsibilities and their gradients (then dl)
 //   va, gh, pp [BH, N, dva]                   [V | 1], [g | h], [num | Gamma_Q . Z]  (dva = d_v + 1 rounded
 //                                             up to a multiple of 4, zero padded)
@@ -220,7 +220,6 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
 //                                             Gamma_K^T [V | 1] -> prefix, Gamma_Q^T [g | h] -> suffix
 //   ac, mt [BH, n_st, C, C] (causal)          tril(Gamma_Q Gamma_K^T), tril([g | h] [V | 1]^T) per chunk
 //   dvt [BH, N, d_v] (causal)                 intra-chunk part of dV
-//   p12 [BH, N, 2 d_r]                        dl [mu / s | 1 / s]
 //   gp [2, BH, n_sg, K, dxa]                  per-segment dl^T [x | x^2 | 1] of both sides (dxa = 2 d_r + 1
 //                                             rounded up to a multiple of 4; the product generates the
 //                                             augmented rows from x)
@@ -235,7 +234,7 @@ struct BwdPlan {
     int st_step = 0;            // tokens per state entry
     int64_t n_st = 0, n_sg = 0;  // state entries and parameter segments per (batch, head)
     size_t off_bf = 0, off_cq = 0, off_mw = 0, off_gq = 0, off_gk = 0, off_dgq = 0, off_dgk = 0, off_va = 0, off_gh = 0,
-           off_pp = 0, off_st = 0, off_rt = 0, off_ac = 0, off_mt = 0, off_dvt = 0, off_p12 = 0, off_gp = 0,
+           off_pp = 0, off_st = 0, off_rt = 0, off_ac = 0, off_mt = 0, off_dvt = 0, off_gp = 0,
            total = 0;
 };
 
@@ -286,7 +285,6 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
     take(&b->off_ac, causal ? b->BH * b->n_st * C * C : 0);
     take(&b->off_mt, causal ? b->BH * b->n_st * C * C : 0);
     take(&b->off_dvt, causal ? rows * b->d_v : 0);
-    take(&b->off_p12, rows * 2 * b->d_r);
     take(&b->off_gp, 2 * b->BH * b->n_sg * b->K * b->dxa);
     b->total = off;
     return GMA_SUCCESS;
@@ -795,7 +793,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
     float *mw = F(b.off_mw), *gq = F(b.off_gq), *gk = F(b.off_gk), *dgq = F(b.off_dgq),
           *dgk = F(b.off_dgk), *va = F(b.off_va), *gh = F(b.off_gh), *pp = F(b.off_pp), *stt = F(b.off_st),
-          *rt = F(b.off_rt), *ac = F(b.off_ac), *mt = F(b.off_mt), *dvt = F(b.off_dvt), *p12 = F(b.off_p12),
+          *rt = F(b.off_rt), *ac = F(b.off_ac), *mt = F(b.off_mt), *dvt = F(b.off_dvt),
           *gp = F(b.off_gp);
     const int64_t BH = b.BH, N = b.N, rows = BH * N, rec = (int64_t)b.K * b.dva;
     const int K = b.K, d_r = b.d_r, d_v = b.d_v, dva = b.dva, dxa = b.dxa, H = (int)b.H;
@@ -812,8 +810,10 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     auto cur_st = [&](const float* ptr) { return View{ptr, b.n_st * rec, causal ? rec : 0, dva, 0}; };
     auto sq = [&](const float* ptr) { return View{ptr, b.n_st * C * C, (int64_t)C * C, C, 0}; };
     auto gemm = [&](View A, bool ta, View Bv, bool tb, View Cv, void* out, bool out_bf16, int M, int Nn, int Kd,
-                    int tokf, int tril, const float* cin, bool per_seg, const void* bx = nullptr) -> gma_status_t {
+                    int tokf, int tril, const float* cin, bool per_seg, const void* bx = nullptr,
+                    const void* dx_x = nullptr) -> gma_status_t {
         BwdGemm g;
+        g.dx_x = dx_x;   // routing-input gradient epilogue: out = dx, from the pairs (dl . mu / s, dl . 1 / s)
         g.Bx = bx;   // B = [x | x^2 | 1] rows generated from the routing input bx (strides of Bv in its elements)
         g.bx_f32 = f32 ? 1 : 0;
         g.bx_dr = d_r;
@@ -900,9 +900,9 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         const float* dl = side ? dgk : dgq;
         void* dx = side ? dkx : dqx;
         const View mwv{mw, (int64_t)K * 2 * d_r, 0, 2 * d_r, H};
-        GMA_TRY(gemm(seg(dl, K), false, mwv, false, seg(p12, 2 * d_r), p12, false, kBwdSeg, 2 * d_r, K, TM, 0, nullptr,
-                     true));
-        GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_dx(x, p12, dx, f32, rows, d_r, s); }));
+        // dx = dl . mu / s - x (dl . 1 / s), formed in the product's epilogue from the interleaved columns
+        GMA_TRY(gemm(seg(dl, K), false, mwv, false, View{nullptr, N * d_r, (int64_t)kBwdSeg * d_r, d_r, 0}, dx, !f32,
+                     kBwdSeg, 2 * d_r, K, TM, 0, nullptr, true, nullptr, x));
         float* gps = gp + (size_t)side * BH * b.n_sg * K * dxa;
         const View gpv{gps, b.n_sg * K * dxa, (int64_t)K * dxa, dxa, 0};
         // dl^T [x | x^2 | 1] per segment, the augmented rows generated from x inside the product
