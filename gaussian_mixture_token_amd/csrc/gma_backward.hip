@@ -63,8 +63,9 @@ constexpr int GM = 64, GN = 64, GK = 32, GLD = 80;   // tile, inner step, LDS ro
 // elements inside the matrix are fetched as two 16-byte loads where the view allows it (vec*).
 // BX: B is generated from the routing rows (BwdGemm::Bx), [x | x^2 | 1 | 0 ...] per row, instead of being
 // read from a materialised matrix.
-// DX: the routing-input gradient epilogue (BwdGemm::dx_x).
-template <bool TA, bool TB, bool OUT_BF16, bool BX = false, bool DX = false>
+// DX: the routing-input gradient epilogue (BwdGemm::dx_x).  AV / BV: operand A / B is [V | 1] generated
+// from the value rows (BwdGemm::Vg).
+template <bool TA, bool TB, bool OUT_BF16, bool BX = false, bool DX = false, bool AV = false, bool BV = false>
 __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     __shared__ float s_a[GK][GLD];
     __shared__ float s_b[GK][GLD];
@@ -84,7 +85,10 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     if (m0 >= M || n0 >= N) return;   // whole workgroup: the tile lies past a ragged end
 
     const float* A = g.A + outer * g.sA0 + (int64_t)inner * g.sA1;
-    const float* B = BX ? nullptr : g.B + (g.modB > 0 ? outer % g.modB : outer) * g.sB0 + (int64_t)inner * g.sB1;
+    const float* B = (BX || BV) ? nullptr : g.B + (g.modB > 0 ? outer % g.modB : outer) * g.sB0 + (int64_t)inner * g.sB1;
+    // element offsets of the value rows of a generated [V | 1] operand
+    const int64_t av0 = AV ? outer * g.sA0 + (int64_t)inner * g.sA1 : 0;
+    const int64_t bv0 = BV ? outer * g.sB0 + (int64_t)inner * g.sB1 : 0;
     const int64_t bx0 = BX ? outer * g.sB0 + (int64_t)inner * g.sB1 : 0;   // element offset of the rows of x
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
@@ -161,10 +165,51 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
             }
         }
     };
+    // columns c .. c+7 of the row of [V | 1 | 0 ...] whose values start at element `row` of Vg (columns
+    // >= cn read as zero): one vector of v where the eight columns lie inside v and the layout allows it
+    auto fetch_vaug = [&](int64_t row, bool ok, int c, int cn, bool vec, float (&v)[8]) {
+        const int dv = g.v_dv;
+        if (ok && vec && c + 8 <= dv && c + 8 <= cn) {
+            if (g.v_f32) {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(g.Vg) + row + c);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(g.Vg) + row + c + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { v[j] = lo[j]; v[4 + j] = hi[j]; }
+            } else {
+                const u32x4 h = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(g.Vg) + row + c);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[2 * j] = __uint_as_float(h[j] << 16);
+                    v[2 * j + 1] = __uint_as_float(h[j] & 0xffff0000u);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int col = c + j;
+                float val = 0.f;
+                if (ok && col < cn) {
+                    if (col < dv) {
+                        if (g.v_f32) val = reinterpret_cast<const float*>(g.Vg)[row + col];
+                        else val = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(g.Vg)[row + col] << 16);
+                    } else if (col == dv) {
+                        val = 1.f;
+                    }
+                }
+                v[j] = val;
+            }
+        }
+    };
     auto fetch = [&](int k0) {
-        if constexpr (!TA) fetch_inner(A, g.lda, g.vecA, m0 + ri, m0 + ri < M, k0 + ki, Kd, ra);
+        if constexpr (AV) {
+            static_assert(!TA, "generated A is read row by row");
+            fetch_vaug(av0 + (int64_t)(m0 + ri) * g.v_dv, m0 + ri < M, k0 + ki, Kd, g.vecA, ra);
+        } else if constexpr (!TA) fetch_inner(A, g.lda, g.vecA, m0 + ri, m0 + ri < M, k0 + ki, Kd, ra);
         else fetch_outer(A, g.lda, g.vecA, k0 + ko, k0 + ko < Kd, m0 + co, M, ra);
-        if constexpr (BX) fetch_xaug(k0 + ko, k0 + ko < Kd, n0 + co, N, rb);
+        if constexpr (BV) {
+            if constexpr (TB) fetch_vaug(bv0 + (int64_t)(n0 + ri) * g.v_dv, n0 + ri < N, k0 + ki, Kd, g.vecB, rb);
+            else fetch_vaug(bv0 + (int64_t)(k0 + ko) * g.v_dv, k0 + ko < Kd, n0 + co, N, g.vecB, rb);
+        } else if constexpr (BX) fetch_xaug(k0 + ko, k0 + ko < Kd, n0 + co, N, rb);
         else if constexpr (TB) fetch_inner(B, g.ldb, g.vecB, n0 + ri, n0 + ri < N, k0 + ki, Kd, rb);
         else fetch_outer(B, g.ldb, g.vecB, k0 + ko, k0 + ko < Kd, n0 + co, N, rb);
     };
@@ -460,19 +505,6 @@ __global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, cons
 }
 
 // ---------------------------------------------------------------------------------- rows
-// Row kernels: workgroup = kRowsPerBlock rows, threads over the columns (no per-element division).
-constexpr int kRowsPerBlock = 8;
-
-template <bool F32>
-__global__ void __launch_bounds__(256) bwd_vaug_kernel(const void* v, float* vaug, int64_t rows, int d_v, int dva) {
-    const int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock;
-    for (int i = 0; i < kRowsPerBlock && r0 + i < rows; ++i) {
-        const int64_t rr = r0 + i;
-        for (int c = threadIdx.x; c < dva; c += 256)
-            vaug[rr * dva + c] = (c < d_v) ? ld_elem<F32>(v, rr * d_v + c) : (c == d_v ? 1.f : 0.f);
-    }
-}
-
 // one wavefront per row; lane l holds columns l, l + 64, ...
 template <bool F32>
 __global__ void __launch_bounds__(256) bwd_gh_kernel(const float* p, const void* dout, float* gh, int64_t rows, int d_v,
@@ -625,6 +657,22 @@ void launch_bwd_gemm(const BwdGemm& g0, bool ta, bool tb, bool out_bf16, hipStre
         return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0 && s0 % 4 == 0 && s1 % 4 == 0 && mod >= 0;
     };
     g.vecA = vec_ok(g.A, g.lda, g.sA0, g.sA1, 0);
+    if (g.Vg) {
+        // 16-byte loads of eight values: fp32 needs 4-element, bf16 8-element aligned rows
+        const int q = g.v_f32 ? 4 : 8;
+        const bool vec = reinterpret_cast<uintptr_t>(g.Vg) % 16 == 0 && g.v_dv % 8 == 0;
+        if (g.v_which == 1) {
+            g.vecA = vec && g.sA0 % q == 0 && g.sA1 % q == 0;
+            g.vecB = vec_ok(g.B, g.ldb, g.sB0, g.sB1, g.modB);
+            bwd_gemm_kernel<false, true, false, false, false, true, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
+        } else {
+            g.vecB = vec && g.sB0 % q == 0 && g.sB1 % q == 0;
+            if (ta && !tb) bwd_gemm_kernel<true, false, false, false, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
+            else if (!ta && !tb) bwd_gemm_kernel<false, false, false, false, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
+            else bwd_gemm_kernel<false, true, false, false, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
+        }
+        return;
+    }
     if (g.dx_x) {
         g.vecB = vec_ok(g.B, g.ldb, g.sB0, g.sB1, g.modB);
         if (out_bf16) bwd_gemm_kernel<false, false, true, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
@@ -668,12 +716,6 @@ void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const doubl
         case 8: gamma_mfma_dispatch<8>(x, f32, bf, cq, gamma, BH, N, H, K, d_r, s); break;
         default: gamma_mfma_dispatch<16>(x, f32, bf, cq, gamma, BH, N, H, K, d_r, s); break;
     }
-}
-
-void launch_bwd_vaug(const void* v, bool f32, float* vaug, int64_t rows, int d_v, int dva, hipStream_t s) {
-    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-    if (f32) bwd_vaug_kernel<true><<<grid, dim3(256), 0, s>>>(v, vaug, rows, d_v, dva);
-    else bwd_vaug_kernel<false><<<grid, dim3(256), 0, s>>>(v, vaug, rows, d_v, dva);
 }
 
 void launch_bwd_gh(const float* p, const void* dout, bool f32, float* gh, int64_t rows, int d_v, int dva, float eps,

@@ -44,6 +44,11 @@ struct BwdGemm {
     // (2d, 2d + 1) = (dl . mu / s, dl . 1 / s) of dim d, and the output is dx[m][d] = C[m][2d] -
     // dx_x[m][d] C[m][2d + 1] in the storage dtype (OUT_BF16), at the C strides (ldc = d_r)
     const void* dx_x = nullptr;
+    // [V | 1] generated from the value rows instead of read: operand A (v_which = 1, A not transposed) or B
+    // (v_which = 2); row t is [v_t | 1 | 0 ...] over the operand's columns, v_t the d_v elements at Vg + row
+    // offset (the operand's strides and leading dimension in elements of V; fp32 or bf16 storage)
+    const void* Vg = nullptr;
+    int v_which = 0, v_f32 = 0, v_dv = 0;
 };
 void launch_bwd_gemm(const BwdGemm& g, bool ta, bool tb, bool out_bf16, hipStream_t s);
 
@@ -61,9 +66,6 @@ void launch_bwd_frag(const float* mu, const float* raw_var, const float* prior, 
 void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const double* cq, float* gamma, int64_t BH,
                            int64_t N, int H, int K, int d_r, hipStream_t s);
 
-// [V | 1 | 0...] rows of width dva (fp32) from v [rows, d_v].
-void launch_bwd_vaug(const void* v, bool f32, float* vaug, int64_t rows, int d_v, int dva, hipStream_t s);
-// [x | x^2 | 1 | 0...] rows of width dxa (fp32) from x [rows, d_r].
 // Read-phase gradient per row: p [rows, dva] holds (num | Gamma_Q . Z, the denominator without
 // eps); gh [rows, dva] <- (g = dO / den | h = -(dO . O) / den | 0...).
 void launch_bwd_gh(const float* p, const void* dout, bool f32, float* gh, int64_t rows, int d_v, int dva, float eps,

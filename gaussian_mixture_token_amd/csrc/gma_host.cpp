@@ -214,7 +214,7 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
 //   bf, cq                                    matrix-core log-density operands (launch_bwd_frag)
 //   mw [H, K, 2 d_r]                          mixture constants mu / s and 1 / s, interleaved by dim
 //   gq, gk, dgq, dgk [BH, N, K]               responsibilities and their gradients (then dl)
-//   va, gh, pp [BH, N, dva]                   [V | 1], [g | h], [num | Gamma_Q . Z]  (dva = d_v + 1 rounded
+//   gh, pp [BH, N, dva]                       [g | h], [num | Gamma_Q . Z]  (dva = d_v + 1 rounded
 //                                             up to a multiple of 4, zero padded)
 //   st, rt [BH, n_st, K, dva]                 states per chunk (causal) or segment (bidirectional):
 //                                             Gamma_K^T [V | 1] -> prefix, Gamma_Q^T [g | h] -> suffix
@@ -233,7 +233,7 @@ struct BwdPlan {
     float eps = 0.f;
     int st_step = 0;            // tokens per state entry
     int64_t n_st = 0, n_sg = 0;  // state entries and parameter segments per (batch, head)
-    size_t off_bf = 0, off_cq = 0, off_mw = 0, off_gq = 0, off_gk = 0, off_dgq = 0, off_dgk = 0, off_va = 0, off_gh = 0,
+    size_t off_bf = 0, off_cq = 0, off_mw = 0, off_gq = 0, off_gk = 0, off_dgq = 0, off_dgk = 0, off_gh = 0,
            off_pp = 0, off_st = 0, off_rt = 0, off_ac = 0, off_mt = 0, off_dvt = 0, off_gp = 0,
            total = 0;
 };
@@ -277,7 +277,6 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
     take(&b->off_gk, rows * b->K);
     take(&b->off_dgq, rows * b->K);
     take(&b->off_dgk, rows * b->K);
-    take(&b->off_va, rows * b->dva);
     take(&b->off_gh, rows * b->dva);
     take(&b->off_pp, rows * b->dva);
     take(&b->off_st, b->BH * b->n_st * rec);
@@ -792,7 +791,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     char* w = reinterpret_cast<char*>(ws);
     auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
     float *mw = F(b.off_mw), *gq = F(b.off_gq), *gk = F(b.off_gk), *dgq = F(b.off_dgq),
-          *dgk = F(b.off_dgk), *va = F(b.off_va), *gh = F(b.off_gh), *pp = F(b.off_pp), *stt = F(b.off_st),
+          *dgk = F(b.off_dgk), *gh = F(b.off_gh), *pp = F(b.off_pp), *stt = F(b.off_st),
           *rt = F(b.off_rt), *ac = F(b.off_ac), *mt = F(b.off_mt), *dvt = F(b.off_dvt),
           *gp = F(b.off_gp);
     const int64_t BH = b.BH, N = b.N, rows = BH * N, rec = (int64_t)b.K * b.dva;
@@ -811,8 +810,14 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     auto sq = [&](const float* ptr) { return View{ptr, b.n_st * C * C, (int64_t)C * C, C, 0}; };
     auto gemm = [&](View A, bool ta, View Bv, bool tb, View Cv, void* out, bool out_bf16, int M, int Nn, int Kd,
                     int tokf, int tril, const float* cin, bool per_seg, const void* bx = nullptr,
-                    const void* dx_x = nullptr) -> gma_status_t {
+                    const void* dx_x = nullptr, int v_which = 0) -> gma_status_t {
         BwdGemm g;
+        // [V | 1] operand generated from the value rows (1: A, 2: B), with the strides of its view in
+        // elements of V
+        g.Vg = v_which ? v : nullptr;
+        g.v_which = v_which;
+        g.v_f32 = f32 ? 1 : 0;
+        g.v_dv = d_v;
         g.dx_x = dx_x;   // routing-input gradient epilogue: out = dx, from the pairs (dl . mu / s, dl . 1 / s)
         g.Bx = bx;   // B = [x | x^2 | 1] rows generated from the routing input bx (strides of Bv in its elements)
         g.bx_f32 = f32 ? 1 : 0;
@@ -862,15 +867,18 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] {
         launch_bwd_gamma_mfma(kx, f32, F(b.off_bf), cq, gk, BH, N, H, K, d_r, s);
     }));
-    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_vaug(v, f32, va, rows, d_v, dva, s); }));
+    // [V | 1] is generated from V inside the products that read it (views in elements of V)
+    const View vv{nullptr, N * d_v, (int64_t)C * d_v, d_v, 0};
     // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
-    GMA_TRY(gemm(tok(gk, K), true, tok(va, dva), false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false));
+    GMA_TRY(gemm(tok(gk, K), true, vv, false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false, nullptr, nullptr,
+                 2));
     GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, causal ? 0 : 2, s); }));
     // read phase: [num | Gamma_Q . Z] = Gamma_Q state (+ tril(Gamma_Q Gamma_K^T) [V | 1]), then g, h
     GMA_TRY(gemm(tok(gq, K), false, cur_st(stt), false, tok(pp, dva), pp, false, C, dva, K, TM, 0, nullptr, false));
     if (causal) {
         GMA_TRY(gemm(tok(gq, K), false, tok(gk, K), true, sq(ac), ac, false, C, C, K, TM | TN, 1, nullptr, false));
-        GMA_TRY(gemm(sq(ac), false, tok(va, dva), false, tok(pp, dva), pp, false, C, dva, C, TM | TK, 0, pp, false));
+        GMA_TRY(gemm(sq(ac), false, vv, false, tok(pp, dva), pp, false, C, dva, C, TM | TK, 0, pp, false, nullptr,
+                     nullptr, 2));
     }
     GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_gh(pp, dout, f32, gh, rows, d_v, dva, b.eps, s); }));
     // Gamma_Q^T [g | h] per entry -> the sums over the later chunks / the total
@@ -879,11 +887,13 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     // dGamma_Q = [g | h] state^T (+ tril([g | h] [V | 1]^T) Gamma_K)
     GMA_TRY(gemm(tok(gh, dva), false, cur_st(stt), true, tok(dgq, K), dgq, false, C, K, dva, TM, 0, nullptr, false));
     if (causal) {
-        GMA_TRY(gemm(tok(gh, dva), false, tok(va, dva), true, sq(mt), mt, false, C, C, dva, TM | TN, 1, nullptr, false));
+        GMA_TRY(gemm(tok(gh, dva), false, vv, true, sq(mt), mt, false, C, C, dva, TM | TN, 1, nullptr, false, nullptr,
+                     nullptr, 2));
         GMA_TRY(gemm(sq(mt), false, tok(gk, K), false, tok(dgq, K), dgq, false, C, K, C, TM | TK, 0, dgq, false));
     }
     // dGamma_K = [V | 1] R^T (+ the same intra-chunk block transposed, times Gamma_Q)
-    GMA_TRY(gemm(tok(va, dva), false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false));
+    GMA_TRY(gemm(vv, false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false, nullptr,
+                 nullptr, 1));
     if (causal)
         GMA_TRY(gemm(sq(mt), true, tok(gq, K), false, tok(dgk, K), dgk, false, C, K, C, TM | TK, 0, dgk, false));
     // dV = Gamma_K R (+ tril(Gamma_Q Gamma_K^T)^T g), in the storage dtype
