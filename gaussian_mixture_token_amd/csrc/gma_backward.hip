@@ -23,6 +23,7 @@
 #include "gma_device.hpp"
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 
 namespace gma {
@@ -61,11 +62,9 @@ constexpr int GM = 64, GN = 64, GK = 32, GLD = 80;   // tile, inner step, LDS ro
 // LDS writes cover 64 consecutive columns of one inner row.  Of an operand whose outer index is
 // contiguous: thread t takes inner row t / 8 and columns 8 (t % 8) .. + 7.  Eight consecutive
 // elements inside the matrix are fetched as two 16-byte loads where the view allows it (vec*).
-// BX: B is generated from the routing rows (BwdGemm::Bx), [x | x^2 | 1 | 0 ...] per row, instead of being
-// read from a materialised matrix.
-// DX: the routing-input gradient epilogue (BwdGemm::dx_x).  AV / BV: operand A / B is [V | 1] generated
-// from the value rows (BwdGemm::Vg).
-template <bool TA, bool TB, bool OUT_BF16, bool BX = false, bool DX = false, bool AV = false, bool BV = false>
+// GA / GB: operand A / B is generated (BwdGemm::ga / gb, GEN_*) instead of read.  DX: the routing-input
+// gradient epilogue (BwdGemm::dx_x).
+template <bool TA, bool TB, bool OUT_BF16, int GA = GEN_NONE, int GB = GEN_NONE, bool DX = false>
 __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     __shared__ float s_a[GK][GLD];
     __shared__ float s_b[GK][GLD];
@@ -84,12 +83,11 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     const int m0 = tm * GM, n0 = tn * GN;
     if (m0 >= M || n0 >= N) return;   // whole workgroup: the tile lies past a ragged end
 
-    const float* A = g.A + outer * g.sA0 + (int64_t)inner * g.sA1;
-    const float* B = (BX || BV) ? nullptr : g.B + (g.modB > 0 ? outer % g.modB : outer) * g.sB0 + (int64_t)inner * g.sB1;
-    // element offsets of the value rows of a generated [V | 1] operand
-    const int64_t av0 = AV ? outer * g.sA0 + (int64_t)inner * g.sA1 : 0;
-    const int64_t bv0 = BV ? outer * g.sB0 + (int64_t)inner * g.sB1 : 0;
-    const int64_t bx0 = BX ? outer * g.sB0 + (int64_t)inner * g.sB1 : 0;   // element offset of the rows of x
+    const float* A = GA ? nullptr : g.A + outer * g.sA0 + (int64_t)inner * g.sA1;
+    const float* B = GB ? nullptr : g.B + (g.modB > 0 ? outer % g.modB : outer) * g.sB0 + (int64_t)inner * g.sB1;
+    // first row of a generated operand's view
+    const int64_t ga0 = GA ? outer * g.sA0 + (int64_t)inner * g.sA1 : 0;
+    const int64_t gb0 = GB ? outer * g.sB0 + (int64_t)inner * g.sB1 : 0;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
     const int r = lane & 15, q = lane >> 4;
@@ -121,26 +119,35 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     float ra[8], rb[8];
     const int ri = tid & 63, ki = (tid >> 6) * 8;     // contiguous-inner mapping
     const int ko = tid >> 3, co = (tid & 7) * 8;      // contiguous-outer mapping
-    // columns c .. c+7 of row k of [x | x^2 | 1 | 0 ...] (BX): a whole vector of x or of x^2 where the
-    // eight columns fall inside one part and x allows 16-byte loads, element by element otherwise
-    auto fetch_xaug = [&](int k, bool k_ok, int c, int cn, float (&v)[8]) {
-        const int dr = g.bx_dr;
-        const int64_t row = bx0 + (int64_t)k * dr;
-        auto ld = [&](int d) -> float {
-            if (g.bx_f32) return reinterpret_cast<const float*>(g.Bx)[row + d];
-            return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(g.Bx)[row + d] << 16);
+    // columns c .. c+7 (columns >= cn read as zero) of row `row` of a generated operand: one 16-byte
+    // load of eight storage elements where the columns lie inside one part of the row and the layout
+    // allows it, element by element otherwise
+    auto gen = [&](auto kind_tag, const BwdGen& s, int64_t row, bool ok, int c, int cn, bool vec, float (&v)[8]) {
+        constexpr int kind = decltype(kind_tag)::value;
+        const int d = s.d;
+        const int64_t e0 = row * d;
+        auto ld1 = [&](int col) -> float {
+            if (s.f32) return reinterpret_cast<const float*>(s.src)[e0 + col];
+            return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(s.src)[e0 + col] << 16);
         };
-        const int part = (c + 8 <= dr) ? 0 : (c >= dr && c + 8 <= 2 * dr) ? 1 : 2;
-        if (k_ok && part < 2 && c + 8 <= cn && g.vecB) {
-            const int d0 = part ? c - dr : c;
+        float scale = 1.f, tail = 1.f;   // GEN_GH: 1 / den and h of the row
+        if constexpr (kind == GEN_GH) {
+            if (ok) {
+                scale = s.rs[2 * row];
+                tail = s.rs[2 * row + 1];
+            }
+        }
+        const bool sq = kind == GEN_XAUG && c >= d;   // the x^2 part
+        const int d0 = sq ? c - d : c;
+        if (ok && vec && c + 8 <= cn && d0 + 8 <= d && (!sq || c + 8 <= 2 * d)) {
             float x[8];
-            if (g.bx_f32) {
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(g.Bx) + row + d0);
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(g.Bx) + row + d0 + 4);
+            if (s.f32) {
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(s.src) + e0 + d0);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(s.src) + e0 + d0 + 4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) { x[j] = lo[j]; x[4 + j] = hi[j]; }
             } else {
-                const u32x4 h = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(g.Bx) + row + d0);
+                const u32x4 h = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(s.src) + e0 + d0);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     x[2 * j] = __uint_as_float(h[j] << 16);
@@ -148,52 +155,24 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
                 }
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = part ? x[j] * x[j] : x[j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int col = c + j;
-                float val = 0.f;
-                if (k_ok && col < cn) {
-                    if (col < dr) val = ld(col);
-                    else if (col < 2 * dr) {
-                        const float t = ld(col - dr);
-                        val = t * t;
-                    } else if (col == 2 * dr) val = 1.f;
-                }
-                v[j] = val;
-            }
-        }
-    };
-    // columns c .. c+7 of the row of [V | 1 | 0 ...] whose values start at element `row` of Vg (columns
-    // >= cn read as zero): one vector of v where the eight columns lie inside v and the layout allows it
-    auto fetch_vaug = [&](int64_t row, bool ok, int c, int cn, bool vec, float (&v)[8]) {
-        const int dv = g.v_dv;
-        if (ok && vec && c + 8 <= dv && c + 8 <= cn) {
-            if (g.v_f32) {
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(g.Vg) + row + c);
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(g.Vg) + row + c + 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { v[j] = lo[j]; v[4 + j] = hi[j]; }
-            } else {
-                const u32x4 h = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(g.Vg) + row + c);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v[2 * j] = __uint_as_float(h[j] << 16);
-                    v[2 * j + 1] = __uint_as_float(h[j] & 0xffff0000u);
-                }
-            }
+            for (int j = 0; j < 8; ++j) v[j] = sq ? x[j] * x[j] : x[j] * scale;
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int col = c + j;
                 float val = 0.f;
                 if (ok && col < cn) {
-                    if (col < dv) {
-                        if (g.v_f32) val = reinterpret_cast<const float*>(g.Vg)[row + col];
-                        else val = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(g.Vg)[row + col] << 16);
-                    } else if (col == dv) {
-                        val = 1.f;
+                    if (col < d) {
+                        val = ld1(col) * scale;
+                    } else if (kind == GEN_XAUG) {
+                        if (col < 2 * d) {
+                            const float t = ld1(col - d);
+                            val = t * t;
+                        } else if (col == 2 * d) {
+                            val = 1.f;
+                        }
+                    } else if (col == d) {
+                        val = tail;
                     }
                 }
                 v[j] = val;
@@ -201,16 +180,15 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
         }
     };
     auto fetch = [&](int k0) {
-        if constexpr (AV) {
-            static_assert(!TA, "generated A is read row by row");
-            fetch_vaug(av0 + (int64_t)(m0 + ri) * g.v_dv, m0 + ri < M, k0 + ki, Kd, g.vecA, ra);
+        if constexpr (GA != GEN_NONE) {
+            static_assert(!TA, "a generated A is read row by row");
+            gen(std::integral_constant<int, GA>{}, g.ga, ga0 + m0 + ri, m0 + ri < M, k0 + ki, Kd, g.vecA, ra);
         } else if constexpr (!TA) fetch_inner(A, g.lda, g.vecA, m0 + ri, m0 + ri < M, k0 + ki, Kd, ra);
         else fetch_outer(A, g.lda, g.vecA, k0 + ko, k0 + ko < Kd, m0 + co, M, ra);
-        if constexpr (BV) {
-            if constexpr (TB) fetch_vaug(bv0 + (int64_t)(n0 + ri) * g.v_dv, n0 + ri < N, k0 + ki, Kd, g.vecB, rb);
-            else fetch_vaug(bv0 + (int64_t)(k0 + ko) * g.v_dv, k0 + ko < Kd, n0 + co, N, g.vecB, rb);
-        } else if constexpr (BX) fetch_xaug(k0 + ko, k0 + ko < Kd, n0 + co, N, rb);
-        else if constexpr (TB) fetch_inner(B, g.ldb, g.vecB, n0 + ri, n0 + ri < N, k0 + ki, Kd, rb);
+        if constexpr (GB != GEN_NONE) {
+            if constexpr (TB) gen(std::integral_constant<int, GB>{}, g.gb, gb0 + n0 + ri, n0 + ri < N, k0 + ki, Kd, g.vecB, rb);
+            else gen(std::integral_constant<int, GB>{}, g.gb, gb0 + k0 + ko, k0 + ko < Kd, n0 + co, N, g.vecB, rb);
+        } else if constexpr (TB) fetch_inner(B, g.ldb, g.vecB, n0 + ri, n0 + ri < N, k0 + ki, Kd, rb);
         else fetch_outer(B, g.ldb, g.vecB, k0 + ko, k0 + ko < Kd, n0 + co, N, rb);
     };
     auto stage = [&]() {
@@ -507,7 +485,7 @@ __global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, cons
 // ---------------------------------------------------------------------------------- rows
 // one wavefront per row; lane l holds columns l, l + 64, ...
 template <bool F32>
-__global__ void __launch_bounds__(256) bwd_gh_kernel(const float* p, const void* dout, float* gh, int64_t rows, int d_v,
+__global__ void __launch_bounds__(256) bwd_gh_kernel(const float* p, const void* dout, float* rs, int64_t rows, int d_v,
                                                      int dva, float eps) {
     const int lane = threadIdx.x & 63;
     const int64_t rr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -518,11 +496,9 @@ __global__ void __launch_bounds__(256) bwd_gh_kernel(const float* p, const void*
     float dot = 0.f;
     for (int c = lane; c < d_v; c += 64) dot += ld_elem<F32>(dout, rr * d_v + c) * (pr[c] * inv);
     dot = wave_sum_f(dot);
-    for (int c = lane; c < dva; c += 64) {
-        float val = 0.f;
-        if (c < d_v) val = ld_elem<F32>(dout, rr * d_v + c) * inv;
-        else if (c == d_v) val = -dot * inv;
-        gh[rr * dva + c] = val;
+    if (lane == 0) {
+        rs[2 * rr] = inv;
+        rs[2 * rr + 1] = -dot * inv;
     }
 }
 
@@ -648,49 +624,44 @@ void gamma_mfma_dispatch(const void* x, bool f32, const float* bf, const double*
 
 }  // namespace
 
-void launch_bwd_gemm(const BwdGemm& g0, bool ta, bool tb, bool out_bf16, hipStream_t s) {
+bool launch_bwd_gemm(const BwdGemm& g0, bool ta, bool tb, bool out_bf16, hipStream_t s) {
     const int64_t tiles = (int64_t)((g0.M + GM - 1) / GM) * ((g0.N + GN - 1) / GN);
     const int64_t grid = tiles * g0.n_inner * g0.n_outer;
-    if (grid <= 0) return;
+    if (grid <= 0) return true;
     BwdGemm g = g0;
     auto vec_ok = [](const float* p, int ld, int64_t s0, int64_t s1, int64_t mod) {
         return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0 && s0 % 4 == 0 && s1 % 4 == 0 && mod >= 0;
     };
-    g.vecA = vec_ok(g.A, g.lda, g.sA0, g.sA1, 0);
-    if (g.Vg) {
-        // 16-byte loads of eight values: fp32 needs 4-element, bf16 8-element aligned rows
-        const int q = g.v_f32 ? 4 : 8;
-        const bool vec = reinterpret_cast<uintptr_t>(g.Vg) % 16 == 0 && g.v_dv % 8 == 0;
-        if (g.v_which == 1) {
-            g.vecA = vec && g.sA0 % q == 0 && g.sA1 % q == 0;
-            g.vecB = vec_ok(g.B, g.ldb, g.sB0, g.sB1, g.modB);
-            bwd_gemm_kernel<false, true, false, false, false, true, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
-        } else {
-            g.vecB = vec && g.sB0 % q == 0 && g.sB1 % q == 0;
-            if (ta && !tb) bwd_gemm_kernel<true, false, false, false, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
-            else if (!ta && !tb) bwd_gemm_kernel<false, false, false, false, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
-            else bwd_gemm_kernel<false, true, false, false, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
-        }
-        return;
-    }
+    // a generated operand's rows start at multiples of d elements: 16-byte loads need d % 8 == 0 (bf16: 8
+    // elements, fp32: two loads of 4) and an aligned base
+    auto gen_vec = [](const BwdGen& q) { return reinterpret_cast<uintptr_t>(q.src) % 16 == 0 && q.d % 8 == 0; };
+    g.vecA = g.ga.kind ? gen_vec(g.ga) : vec_ok(g.A, g.lda, g.sA0, g.sA1, 0);
+    g.vecB = g.gb.kind ? gen_vec(g.gb) : vec_ok(g.B, g.ldb, g.sB0, g.sB1, g.modB);
+    const dim3 gr((unsigned)grid), bl(256);
+    const int ga = g.ga.kind, gb = g.gb.kind;
     if (g.dx_x) {
-        g.vecB = vec_ok(g.B, g.ldb, g.sB0, g.sB1, g.modB);
-        if (out_bf16) bwd_gemm_kernel<false, false, true, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
-        else bwd_gemm_kernel<false, false, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
-        return;
+        if (ta || tb || ga || gb) return false;
+        if (out_bf16) bwd_gemm_kernel<false, false, true, GEN_NONE, GEN_NONE, true><<<gr, bl, 0, s>>>(g);
+        else bwd_gemm_kernel<false, false, false, GEN_NONE, GEN_NONE, true><<<gr, bl, 0, s>>>(g);
+        return true;
     }
-    if (g.Bx) {
-        // 16-byte loads of eight x elements: fp32 needs 4-element, bf16 8-element aligned rows
-        const int q = g.bx_f32 ? 4 : 8;
-        g.vecB = reinterpret_cast<uintptr_t>(g.Bx) % 16 == 0 && g.bx_dr % 8 == 0 && g.sB0 % q == 0 && g.sB1 % q == 0;
-        bwd_gemm_kernel<true, false, false, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(g);
-        return;
+    if (ga || gb) {
+        if (out_bf16) return false;
+        if (ta && !tb && !ga && gb == GEN_XAUG) bwd_gemm_kernel<true, false, false, GEN_NONE, GEN_XAUG><<<gr, bl, 0, s>>>(g);
+        else if (ta && !tb && !ga && gb == GEN_VAUG) bwd_gemm_kernel<true, false, false, GEN_NONE, GEN_VAUG><<<gr, bl, 0, s>>>(g);
+        else if (ta && !tb && !ga && gb == GEN_GH) bwd_gemm_kernel<true, false, false, GEN_NONE, GEN_GH><<<gr, bl, 0, s>>>(g);
+        else if (!ta && !tb && !ga && gb == GEN_VAUG) bwd_gemm_kernel<false, false, false, GEN_NONE, GEN_VAUG><<<gr, bl, 0, s>>>(g);
+        else if (!ta && tb && ga == GEN_GH && gb == GEN_VAUG) bwd_gemm_kernel<false, true, false, GEN_GH, GEN_VAUG><<<gr, bl, 0, s>>>(g);
+        else if (!ta && tb && ga == GEN_GH && !gb) bwd_gemm_kernel<false, true, false, GEN_GH, GEN_NONE><<<gr, bl, 0, s>>>(g);
+        else if (!ta && tb && ga == GEN_VAUG && !gb) bwd_gemm_kernel<false, true, false, GEN_VAUG, GEN_NONE><<<gr, bl, 0, s>>>(g);
+        else return false;
+        return true;
     }
-    g.vecB = vec_ok(g.B, g.ldb, g.sB0, g.sB1, g.modB);
     if (!ta && !tb) gemm_dispatch<false, false>(g, out_bf16, grid, s);
     else if (!ta && tb) gemm_dispatch<false, true>(g, out_bf16, grid, s);
     else if (ta && !tb) gemm_dispatch<true, false>(g, out_bf16, grid, s);
     else gemm_dispatch<true, true>(g, out_bf16, grid, s);
+    return true;
 }
 
 void launch_bwd_prep(const float* mu, const float* raw_var, float* mw, int H, int K, int d_r, hipStream_t s) {
@@ -718,11 +689,11 @@ void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const doubl
     }
 }
 
-void launch_bwd_gh(const float* p, const void* dout, bool f32, float* gh, int64_t rows, int d_v, int dva, float eps,
+void launch_bwd_gh(const float* p, const void* dout, bool f32, float* rs, int64_t rows, int d_v, int dva, float eps,
                    hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4));
-    if (f32) bwd_gh_kernel<true><<<grid, dim3(256), 0, s>>>(p, dout, gh, rows, d_v, dva, eps);
-    else bwd_gh_kernel<false><<<grid, dim3(256), 0, s>>>(p, dout, gh, rows, d_v, dva, eps);
+    if (f32) bwd_gh_kernel<true><<<grid, dim3(256), 0, s>>>(p, dout, rs, rows, d_v, dva, eps);
+    else bwd_gh_kernel<false><<<grid, dim3(256), 0, s>>>(p, dout, rs, rows, d_v, dva, eps);
 }
 
 void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream_t s) {

@@ -16,6 +16,15 @@ namespace gma {
 // ragged last chunk), and operand entries past it are read as zero and never stored.
 // tril: entry (i, j) of the product is kept only for j <= i (chunk-local token indices).
 // Cin (fp32, may be null) uses C's strides.  C is fp32, or bf16 with out_bf16.
+enum { GEN_NONE = 0, GEN_XAUG = 1, GEN_VAUG = 2, GEN_GH = 3 };
+// GEN_XAUG: [x | x^2 | 1 | 0 ...]; GEN_VAUG: [v | 1 | 0 ...]; GEN_GH: [v rs0 | rs1 | 0 ...] (the read-phase
+// gradient [g | h]: rs0 = 1 / den, rs1 = h of the row)
+struct BwdGen {
+    const void* src = nullptr;
+    const float* rs = nullptr;
+    int kind = GEN_NONE, f32 = 0, d = 0;
+};
+
 struct BwdGemm {
     const float* A = nullptr;
     const float* B = nullptr;
@@ -35,22 +44,17 @@ struct BwdGemm {
     // set by launch_bwd_gemm: 16-byte loads are allowed (base 16-byte aligned, leading dimension and
     // batch strides multiples of 4 elements)
     bool vecA = false, vecB = false;
-    // B generated from routing rows instead of read (B not transposed, A transposed, fp32 output): row k
-    // of B is [x_k | x_k^2 | 1 | 0 ...] over N columns, x_k the d_r elements at Bx + row offset
-    // (sB0, sB1, ldb = bx_dr in elements of x; fp32 or bf16 storage)
-    const void* Bx = nullptr;
-    int bx_f32 = 0, bx_dr = 0;
     // routing-input gradient in the epilogue (A, B not transposed): the product's columns come in pairs
     // (2d, 2d + 1) = (dl . mu / s, dl . 1 / s) of dim d, and the output is dx[m][d] = C[m][2d] -
     // dx_x[m][d] C[m][2d + 1] in the storage dtype (OUT_BF16), at the C strides (ldc = d_r)
     const void* dx_x = nullptr;
-    // [V | 1] generated from the value rows instead of read: operand A (v_which = 1, A not transposed) or B
-    // (v_which = 2); row t is [v_t | 1 | 0 ...] over the operand's columns, v_t the d_v elements at Vg + row
-    // offset (the operand's strides and leading dimension in elements of V; fp32 or bf16 storage)
-    const void* Vg = nullptr;
-    int v_which = 0, v_f32 = 0, v_dv = 0;
+    // operands generated from storage rows instead of read from a materialised fp32 matrix (kind != 0);
+    // the operand's batch strides (sA0, sA1 or sB0, sB1) then count rows, and row t of the view is built
+    // from the d elements at src + t d (fp32 or bf16) and, for GEN_GH, the pair rs[2 t], rs[2 t + 1]
+    BwdGen ga, gb;
 };
-void launch_bwd_gemm(const BwdGemm& g, bool ta, bool tb, bool out_bf16, hipStream_t s);
+// false: no compiled kernel for this combination of transposes, generated operands and epilogue
+bool launch_bwd_gemm(const BwdGemm& g, bool ta, bool tb, bool out_bf16, hipStream_t s);
 
 // Mixture constants for the routing-input gradient: mw [H, K, 2 d_r] (row k: mu_kd / s_kd and 1 / s_kd
 // interleaved, at columns 2d and 2d + 1; s = softplus(raw_var)).
@@ -67,8 +71,8 @@ void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const doubl
                            int64_t N, int H, int K, int d_r, hipStream_t s);
 
 // Read-phase gradient per row: p [rows, dva] holds (num | Gamma_Q . Z, the denominator without
-// eps); gh [rows, dva] <- (g = dO / den | h = -(dO . O) / den | 0...).
-void launch_bwd_gh(const float* p, const void* dout, bool f32, float* gh, int64_t rows, int d_v, int dva, float eps,
+// eps); rs [rows, 2] <- (1 / den, h = -(dO . O) / den), so that [g | h] = [dO rs0 | rs1] (GEN_GH).
+void launch_bwd_gh(const float* p, const void* dout, bool f32, float* rs, int64_t rows, int d_v, int dva, float eps,
                    hipStream_t s);
 // Softmax gradient in place: dl = gamma (dgamma - gamma . dgamma) per row of K.
 void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream_t s);

@@ -214,8 +214,9 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
 //   bf, cq                                    matrix-core log-density operands (launch_bwd_frag)
 //   mw [H, K, 2 d_r]                          mixture constants mu / s and 1 / s, interleaved by dim
 //   gq, gk, dgq, dgk [BH, N, K]               responsibilities and their gradients (then dl)
-//   gh, pp [BH, N, dva]                       [g | h], [num | Gamma_Q . Z]  (dva = d_v + 1 rounded
-//                                             up to a multiple of 4, zero padded)
+//   pp [BH, N, dva]                           [num | Gamma_Q . Z]  (dva = d_v + 1 rounded up to a multiple
+//                                             of 4, zero padded)
+//   rs [BH, N, 2]                             1 / den and h per row ([g | h] = [dO rs0 | rs1])
 //   st, rt [BH, n_st, K, dva]                 states per chunk (causal) or segment (bidirectional):
 //                                             Gamma_K^T [V | 1] -> prefix, Gamma_Q^T [g | h] -> suffix
 //   ac, mt [BH, n_st, C, C] (causal)          tril(Gamma_Q Gamma_K^T), tril([g | h] [V | 1]^T) per chunk
@@ -277,7 +278,7 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
     take(&b->off_gk, rows * b->K);
     take(&b->off_dgq, rows * b->K);
     take(&b->off_dgk, rows * b->K);
-    take(&b->off_gh, rows * b->dva);
+    take(&b->off_gh, rows * 2);
     take(&b->off_pp, rows * b->dva);
     take(&b->off_st, b->BH * b->n_st * rec);
     take(&b->off_rt, b->BH * b->n_st * rec);
@@ -791,7 +792,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     char* w = reinterpret_cast<char*>(ws);
     auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
     float *mw = F(b.off_mw), *gq = F(b.off_gq), *gk = F(b.off_gk), *dgq = F(b.off_dgq),
-          *dgk = F(b.off_dgk), *gh = F(b.off_gh), *pp = F(b.off_pp), *stt = F(b.off_st),
+          *dgk = F(b.off_dgk), *rs = F(b.off_gh), *pp = F(b.off_pp), *stt = F(b.off_st),
           *rt = F(b.off_rt), *ac = F(b.off_ac), *mt = F(b.off_mt), *dvt = F(b.off_dvt),
           *gp = F(b.off_gp);
     const int64_t BH = b.BH, N = b.N, rows = BH * N, rec = (int64_t)b.K * b.dva;
@@ -809,19 +810,12 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     auto cur_st = [&](const float* ptr) { return View{ptr, b.n_st * rec, causal ? rec : 0, dva, 0}; };
     auto sq = [&](const float* ptr) { return View{ptr, b.n_st * C * C, (int64_t)C * C, C, 0}; };
     auto gemm = [&](View A, bool ta, View Bv, bool tb, View Cv, void* out, bool out_bf16, int M, int Nn, int Kd,
-                    int tokf, int tril, const float* cin, bool per_seg, const void* bx = nullptr,
-                    const void* dx_x = nullptr, int v_which = 0) -> gma_status_t {
+                    int tokf, int tril, const float* cin, bool per_seg, BwdGen ga = BwdGen{}, BwdGen gb = BwdGen{},
+                    const void* dx_x = nullptr) -> gma_status_t {
         BwdGemm g;
-        // [V | 1] operand generated from the value rows (1: A, 2: B), with the strides of its view in
-        // elements of V
-        g.Vg = v_which ? v : nullptr;
-        g.v_which = v_which;
-        g.v_f32 = f32 ? 1 : 0;
-        g.v_dv = d_v;
+        g.ga = ga;       // generated operands (their views count rows)
+        g.gb = gb;
         g.dx_x = dx_x;   // routing-input gradient epilogue: out = dx, from the pairs (dl . mu / s, dl . 1 / s)
-        g.Bx = bx;   // B = [x | x^2 | 1] rows generated from the routing input bx (strides of Bv in its elements)
-        g.bx_f32 = f32 ? 1 : 0;
-        g.bx_dr = d_r;
         g.A = A.p;
         g.sA0 = A.s0;
         g.sA1 = A.s1;
@@ -846,7 +840,10 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         g.tok_step = per_seg ? kBwdSeg : C;
         g.tok_flags = tokf;
         g.tril = tril;
-        return timed_launch(K_BWD_GEMM, s, [&] { launch_bwd_gemm(g, ta, tb, out_bf16, s); });
+        bool ok = true;
+        const gma_status_t ls = timed_launch(K_BWD_GEMM, s, [&] { ok = launch_bwd_gemm(g, ta, tb, out_bf16, s); });
+        if (!ok) return fail(GMA_ERROR_LAUNCH, "no backward product kernel for this operand combination");
+        return ls;
     };
 #define GMA_TRY(x)                        \
     do {                                  \
@@ -867,39 +864,39 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] {
         launch_bwd_gamma_mfma(kx, f32, F(b.off_bf), cq, gk, BH, N, H, K, d_r, s);
     }));
-    // [V | 1] is generated from V inside the products that read it (views in elements of V)
-    const View vv{nullptr, N * d_v, (int64_t)C * d_v, d_v, 0};
+    // operands generated inside the products (views in rows): [V | 1] from V, [g | h] from dO and the row
+    // pair rs = (1 / den, h), [x | x^2 | 1] from the routing input
+    const View rows_tok{nullptr, N, C, 1, 0}, rows_seg{nullptr, N, kBwdSeg, 1, 0};
+    const View vv = rows_tok, ghv = rows_tok;
+    const BwdGen gen_v{v, nullptr, GEN_VAUG, f32 ? 1 : 0, d_v};
+    const BwdGen gen_gh{dout, rs, GEN_GH, f32 ? 1 : 0, d_v};
     // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
-    GMA_TRY(gemm(tok(gk, K), true, vv, false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false, nullptr, nullptr,
-                 2));
+    GMA_TRY(gemm(tok(gk, K), true, vv, false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{}, gen_v));
     GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, causal ? 0 : 2, s); }));
     // read phase: [num | Gamma_Q . Z] = Gamma_Q state (+ tril(Gamma_Q Gamma_K^T) [V | 1]), then g, h
     GMA_TRY(gemm(tok(gq, K), false, cur_st(stt), false, tok(pp, dva), pp, false, C, dva, K, TM, 0, nullptr, false));
     if (causal) {
         GMA_TRY(gemm(tok(gq, K), false, tok(gk, K), true, sq(ac), ac, false, C, C, K, TM | TN, 1, nullptr, false));
-        GMA_TRY(gemm(sq(ac), false, vv, false, tok(pp, dva), pp, false, C, dva, C, TM | TK, 0, pp, false, nullptr,
-                     nullptr, 2));
+        GMA_TRY(gemm(sq(ac), false, vv, false, tok(pp, dva), pp, false, C, dva, C, TM | TK, 0, pp, false, BwdGen{}, gen_v));
     }
-    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_gh(pp, dout, f32, gh, rows, d_v, dva, b.eps, s); }));
+    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_gh(pp, dout, f32, rs, rows, d_v, dva, b.eps, s); }));
     // Gamma_Q^T [g | h] per entry -> the sums over the later chunks / the total
-    GMA_TRY(gemm(tok(gq, K), true, tok(gh, dva), false, all_st(rt), rt, false, K, dva, C, TK, 0, nullptr, false));
+    GMA_TRY(gemm(tok(gq, K), true, ghv, false, all_st(rt), rt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{}, gen_gh));
     GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(rt, BH, b.n_st, rec, causal ? 1 : 2, s); }));
     // dGamma_Q = [g | h] state^T (+ tril([g | h] [V | 1]^T) Gamma_K)
-    GMA_TRY(gemm(tok(gh, dva), false, cur_st(stt), true, tok(dgq, K), dgq, false, C, K, dva, TM, 0, nullptr, false));
+    GMA_TRY(gemm(ghv, false, cur_st(stt), true, tok(dgq, K), dgq, false, C, K, dva, TM, 0, nullptr, false, gen_gh));
     if (causal) {
-        GMA_TRY(gemm(tok(gh, dva), false, vv, true, sq(mt), mt, false, C, C, dva, TM | TN, 1, nullptr, false, nullptr,
-                     nullptr, 2));
+        GMA_TRY(gemm(ghv, false, vv, true, sq(mt), mt, false, C, C, dva, TM | TN, 1, nullptr, false, gen_gh, gen_v));
         GMA_TRY(gemm(sq(mt), false, tok(gk, K), false, tok(dgq, K), dgq, false, C, K, C, TM | TK, 0, dgq, false));
     }
     // dGamma_K = [V | 1] R^T (+ the same intra-chunk block transposed, times Gamma_Q)
-    GMA_TRY(gemm(vv, false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false, nullptr,
-                 nullptr, 1));
+    GMA_TRY(gemm(vv, false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false, gen_v));
     if (causal)
         GMA_TRY(gemm(sq(mt), true, tok(gq, K), false, tok(dgk, K), dgk, false, C, K, C, TM | TK, 0, dgk, false));
     // dV = Gamma_K R (+ tril(Gamma_Q Gamma_K^T)^T g), in the storage dtype
     if (causal)
-        GMA_TRY(gemm(sq(ac), true, tok(gh, dva), false, tok(dvt, d_v), dvt, false, C, d_v, C, TM | TK, 0, nullptr,
-                     false));
+        GMA_TRY(gemm(sq(ac), true, ghv, false, tok(dvt, d_v), dvt, false, C, d_v, C, TM | TK, 0, nullptr, false,
+                     BwdGen{}, gen_gh));
     GMA_TRY(gemm(tok(gk, K), false, cur_st(rt), false, tok(nullptr, d_v), dv, !f32, C, d_v, K, TM, 0,
                  causal ? dvt : nullptr, false));
     // posterior gradients, then per side the routing-input gradient and the parameter partials
@@ -912,12 +909,12 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         const View mwv{mw, (int64_t)K * 2 * d_r, 0, 2 * d_r, H};
         // dx = dl . mu / s - x (dl . 1 / s), formed in the product's epilogue from the interleaved columns
         GMA_TRY(gemm(seg(dl, K), false, mwv, false, View{nullptr, N * d_r, (int64_t)kBwdSeg * d_r, d_r, 0}, dx, !f32,
-                     kBwdSeg, 2 * d_r, K, TM, 0, nullptr, true, nullptr, x));
+                     kBwdSeg, 2 * d_r, K, TM, 0, nullptr, true, BwdGen{}, BwdGen{}, x));
         float* gps = gp + (size_t)side * BH * b.n_sg * K * dxa;
         const View gpv{gps, b.n_sg * K * dxa, (int64_t)K * dxa, dxa, 0};
         // dl^T [x | x^2 | 1] per segment, the augmented rows generated from x inside the product
-        GMA_TRY(gemm(seg(dl, K), true, View{nullptr, N * d_r, (int64_t)kBwdSeg * d_r, d_r, 0}, false, gpv, gps, false,
-                     K, dxa, kBwdSeg, TK, 0, nullptr, true, x));
+        GMA_TRY(gemm(seg(dl, K), true, rows_seg, false, gpv, gps, false, K, dxa, kBwdSeg, TK, 0, nullptr, true,
+                     BwdGen{}, BwdGen{x, nullptr, GEN_XAUG, f32 ? 1 : 0, d_r}));
     }
 #undef GMA_TRY
     return timed_launch(K_BWD_PARAM, s, [&] {
