@@ -224,6 +224,30 @@ def main():
     value = tokens / (ms_per_step / 1e3)
     print("bench: %.3f ms/step (wall %.3f s)" % (ms_per_step, wall), file=sys.stderr, flush=True)
 
+    # timed region 3: isolated single steps, each bracketed by its own events and followed by a
+    # synchronize. "cold": a 512 MiB fill before each step evicts the last-level cache; "warm": the
+    # same step run once untimed before each timed one. Median and 10th / 90th percentiles of each.
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+    iso = {"cold": [], "warm": []}
+    for _ in range(max(args.steps, 10)):
+        for kind in ("cold", "warm"):
+            if kind == "cold":
+                flush.fill_(1.0)
+            else:
+                step()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            step()
+            a1.record()
+            torch.cuda.synchronize()
+            iso[kind].append(a0.elapsed_time(a1))
+    del flush
+    step_isolated = {"flush_bytes_before_cold_steps": 1 << 29, "steps": max(args.steps, 10)}
+    for kind, ts in iso.items():
+        ts.sort()
+        for name, f in (("median_ms", 0.5), ("p10_ms", 0.1), ("p90_ms", 0.9)):
+            step_isolated["%s_%s" % (kind, name)] = ts[min(len(ts) - 1, int(f * (len(ts) - 1) + 0.5))]
+
     # timed region 2: the same steps with per-kernel HIP events on the launch stream
     lib.gma_timing_enable(1)
     for k in range(lib.gma_kernel_count()):
@@ -240,7 +264,7 @@ def main():
             kernels[lib.gma_kernel_name(k).decode()] = {"avg_us": 1e3 * tot.value / n.value, "launches": n.value}
     T = w.batch * w.heads * w.seq_len
     if args.backward:
-        bwd_line(args, w, value, ms_per_step, kernels, T, dout)
+        bwd_line(args, w, value, ms_per_step, kernels, T, dout, step_isolated)
         return
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     avg_s = kernels[dominant]["avg_us"] * 1e-6
@@ -292,6 +316,7 @@ def main():
                    "d_value": w.d_value, "eps": w.eps, "global_batch": w.batch, "parallelism": "single GPU"},
         "roofline": roof,
         "step_roofline": step_roof,
+        "step_isolated": step_isolated,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "source_hash": src_hash,
@@ -299,7 +324,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def bwd_line(args, w, value, ms_per_step, kernels, T, dout):
+def bwd_line(args, w, value, ms_per_step, kernels, T, dout, step_isolated):
     """The backward's JSON line: the whole step against the fp32 matrix-core peak (every product of the
     backward is an fp32 matrix-core product) and, for reference, against HBM."""
     step_s = ms_per_step * 1e-3
@@ -324,7 +349,8 @@ def bwd_line(args, w, value, ms_per_step, kernels, T, dout):
                    "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "d_route": w.d_route,
                    "n_comp": w.n_comp, "d_value": w.d_value, "eps": w.eps, "global_batch": w.batch,
                    "parallelism": "single GPU"},
-        "roofline": roof, "kernels": kernels, "cpu_baseline": cpu, "source_hash": kernel_source_hash(backward=True),
+        "roofline": roof, "step_isolated": step_isolated, "kernels": kernels, "cpu_baseline": cpu,
+        "source_hash": kernel_source_hash(backward=True),
     }
     print(json.dumps(line), flush=True)
 
