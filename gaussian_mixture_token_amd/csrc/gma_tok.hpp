@@ -82,6 +82,11 @@ tok_kernel(const MainArgs a) {
     constexpr int NGS = GSTORE ? GKWAVE / 1024 : 0;   // Gamma_K tile stores per wave and chunk
     // vector-memory stores per wave and chunk, issued after the DMA of the next chunk
     constexpr int NST = OUT ? NVT : NGS;
+    // d_v tiles per output stage of the causal passes.  With an even count and no d_v padding the
+    // tiles go out in pairs, 16 bytes per lane: NSTP stores per wave and chunk instead of NST.
+    constexpr int VPS = (NKQ >= 8) ? 1 : ((8 / NKQ < NVT) ? 8 / NKQ : NVT);
+    constexpr bool PAIRS = CAUSAL && VPS % 2 == 0;
+    constexpr int NSTP = PAIRS ? NST / 2 : NST;
     // bidirectional read pass with d_v = VC: the wave's output rows go out as whole rows (16 bytes per
     // lane) from an LDS staging area, NSTF stores per chunk instead of NVT
     constexpr bool OROWS = MODE == MODE_OUT_BIDIR;
@@ -133,6 +138,7 @@ tok_kernel(const MainArgs a) {
     const int vt0 = (NKQ >= W) ? 0 : (w % WPK) * VTW;
     const bool zown = (NKQ >= W) || (w % WPK == 0);   // this wave keeps Z of its components
     const uint32_t d_r = (uint32_t)a.d_r, d_v = (uint32_t)a.d_v;
+    const bool pair_st = PAIRS && d_v == VC;
 
     const uint16_t* qx = reinterpret_cast<const uint16_t*>(a.qx) + (int64_t)bh * N * a.d_r;
     const uint16_t* kx = reinterpret_cast<const uint16_t*>(a.kx) + (int64_t)bh * N * a.d_r;
@@ -495,6 +501,22 @@ tok_kernel(const MainArgs a) {
         }
     };
     auto row_base = [&](uint32_t tok) -> uint32_t { return (tok * d_v + (lane_v >> 4) * 4) * 2; };
+    // Two d_v tiles 2p, 2p + 1 stored as 16 bytes per lane: one lane-row exchange (rows of 16 lanes
+    // g = 1, 3 of tile 2p trade places with rows g = 0, 2 of tile 2p + 1) leaves lane (r, g) with d_v
+    // columns 32p + pcol(g) .. +7 of token 16 w + r, pcol = 0, 16, 8, 24 for g = 0 .. 3: 64 contiguous
+    // bytes of each token row per store instruction instead of two 32-byte pieces.
+    auto pair_base = [&](uint32_t tok) -> uint32_t {
+        const int g = lane_v >> 4;
+        return (tok * d_v + 16 * (g & 1) + 8 * (g >> 1)) * 2;
+    };
+    auto store_pair = [&](const f32x4& o0, const f32x4& o1, float inv, uint32_t base, int p) {
+        const u32x2 x = __builtin_bit_cast(u32x2, pack4(o0 * inv));
+        const u32x2 y = __builtin_bit_cast(u32x2, pack4(o1 * inv));
+        const auto s0 = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+        const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs_o, base, p * 64, 0);
+    };
 
     // causal mask of the intra-chunk tiles: key 16 J + 4g + i is kept for query 16 w + r when
     // 16 J + i <= 16 w + r - 4g; as a factor 0 / 1 from a clamped difference (no per-element compare)
@@ -525,6 +547,7 @@ tok_kernel(const MainArgs a) {
         } else {
             if (first) wait_vmcnt<NVD + NGD>();
             else if (OROWS && d_v == VC) wait_vmcnt<NVD + NGD + NSTF>();
+            else if (pair_st) wait_vmcnt<NVD + NGD + NSTP>();
             else wait_vmcnt<NVD + NGD + NST>();
             if constexpr (NEED_V) lds_barrier();   // B0
         }
@@ -790,8 +813,13 @@ tok_kernel(const MainArgs a) {
                 if (has_next) wait_vmcnt<NXD + NVD + NGD>();
                 else wait_vmcnt<0>();
             } else {
-                if (has_next) wait_vmcnt<NST + NXD + NVD + NGD>();
-                else wait_vmcnt<NST>();
+                if (pair_st) {
+                    if (has_next) wait_vmcnt<NSTP + NXD + NVD + NGD>();
+                    else wait_vmcnt<NSTP>();
+                } else {
+                    if (has_next) wait_vmcnt<NST + NXD + NVD + NGD>();
+                    else wait_vmcnt<NST>();
+                }
             }
             lds_barrier();   // B1
             const lds_char* gkb = LGK + (GLOAD ? BUF * GKBUF : 0);
@@ -817,7 +845,7 @@ tok_kernel(const MainArgs a) {
             // Software pipeline over stages: each stage first issues the LDS reads of the next stage,
             // then the matrix work of the current one (fences keep the order), so that LDS latency
             // is covered by MFMAs.
-            constexpr int VP = (NKQ >= 8) ? 1 : ((8 / NKQ < NVT) ? 8 / NKQ : NVT);   // d_v tiles per stage
+            constexpr int VP = VPS;   // d_v tiles per stage
             static_assert(NVT % VP == 0, "d_v tile stages");
             bf16x8 vfr[2][VP][2];
             bf16x8 sst[2][VP][CAUSAL ? NKQ : 1];
@@ -889,7 +917,18 @@ tok_kernel(const MainArgs a) {
             } else {
                 if constexpr (ALL_VT) load_vstage(0, 0);
             }
-            const uint32_t obase = row_base(tok);
+            const uint32_t obase = pair_st ? pair_base(tok) : row_base(tok);
+            auto store_stage = [&](const f32x4 (&ot)[VP], int vs) {
+                if constexpr (PAIRS) {
+                    if (pair_st) {
+#pragma unroll
+                        for (int j = 0; j < VP; j += 2) store_pair(ot[j], ot[j + 1], inv, obase, (vs * VP + j) / 2);
+                        return;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < VP; ++j) store_tile(ot[j], inv, obase, vs * VP + j);
+            };
             fence();
 
             // stages of VP d_v tiles: inter (state before the chunk) and intra output of own queries,
@@ -925,19 +964,13 @@ tok_kernel(const MainArgs a) {
                                         mma(st[kqi][hh][vs * VP + j], gkc[kqi][hh][tk], vfr[cb][j][tk]);
                     }
                     if constexpr (CAUSAL) {
-                        if (vs > 0) {
-#pragma unroll
-                            for (int j = 0; j < VP; ++j) store_tile(oprev[j], inv, obase, (vs - 1) * VP + j);
-                        }
+                        if (vs > 0) store_stage(oprev, vs - 1);
 #pragma unroll
                         for (int j = 0; j < VP; ++j) oprev[j] = o[j];
                     }
                     fence();
                 }
-                if constexpr (CAUSAL) {
-#pragma unroll
-                    for (int j = 0; j < VP; ++j) store_tile(oprev[j], inv, obase, (NVT / VP - 1) * VP + j);
-                }
+                if constexpr (CAUSAL) store_stage(oprev, NVT / VP - 1);
             }
             if constexpr (!ALL_VT) {
                 // the owned d_v tiles are a slice: fetch their V fragments again
@@ -979,7 +1012,8 @@ tok_kernel(const MainArgs a) {
                 // chunk's stores were issued.  Done after the last chunk too (the reads then see
                 // stale LDS and are never used): an unconditional update keeps the carried
                 // registers dead through the chunk.
-                wait_vmcnt<NVD + NGD + NST>();
+                if (pair_st) wait_vmcnt<NVD + NGD + NSTP>();
+                else wait_vmcnt<NVD + NGD + NST>();
                 prefetch_x(LX + (BUF ^ 1) * XBUF + w * XWAVE);
             }
         }
