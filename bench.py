@@ -152,7 +152,7 @@ def main():
                          "its FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+        print("bench.py: measures one GPU only; the library has no multi-GPU path "
               "(each (batch, head) or sequence shard would run the same single-GPU path).", file=sys.stderr)
         sys.exit(2)
 
