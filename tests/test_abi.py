@@ -4,7 +4,6 @@ Validation is pure host code that returns before any HIP call, so every error pa
 exercised here without a GPU.
 """
 import ctypes
-import math
 import os
 import re
 
