@@ -502,6 +502,9 @@ __global__ void __launch_bounds__(256) bwd_gh_kernel(const float* p, const void*
     }
 }
 
+// dl = gamma * (dg - <gamma, dg>) per row, one wave per row.  Rows of up to 256 entries stay in
+// registers between the dot product and the update (element k on lane k % 64, slot k / 64); longer
+// rows are read twice.  Either way each row's dot product is summed in the same order.
 __global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* dg, int64_t rows, int K) {
     const int lane = threadIdx.x & 63;
     const int64_t rr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -509,26 +512,49 @@ __global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* 
     const float* gr = gamma + rr * K;
     float* dr = dg + rr * K;
     float dot = 0.f;
+    if (K <= 256) {
+        float g[4], d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = lane + 64 * j;
+            g[j] = k < K ? gr[k] : 0.f;
+            d[j] = k < K ? dr[k] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (lane + 64 * j < K) dot += g[j] * d[j];
+        dot = wave_sum_f(dot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = lane + 64 * j;
+            if (k < K) dr[k] = g[j] * (d[j] - dot);
+        }
+        return;
+    }
     for (int k = lane; k < K; k += 64) dot += gr[k] * dr[k];
     dot = wave_sum_f(dot);
     for (int k = lane; k < K; k += 64) dr[k] = gr[k] * (dr[k] - dot);
 }
 
 // ---------------------------------------------------------------------------------- scans
-// thread = one state element of one (batch, head); sequential over the n chunk entries, in groups of
-// 16 independent loads (then the group's running sums), so that loads are in flight back to back
-__global__ void __launch_bounds__(256) bwd_scan_kernel(float* st, int64_t n, int64_t rec, int mode) {
-    const int64_t per = (rec + 255) / 256;   // workgroups per (batch, head)
-    const int64_t e = ((int64_t)blockIdx.x % per) * 256 + threadIdx.x;
-    if (e >= rec) return;
-    float* base = st + ((int64_t)blockIdx.x / per) * n * rec + e;
-    float run = 0.f;
+// In place over the n chunk entries of each (batch, head), entry stride rec floats: mode 0 exclusive
+// prefix, mode 1 exclusive suffix, mode 2 total (into entry 0).  A thread owns four consecutive state
+// elements (one 16-byte access per entry; rec is a multiple of four) and walks the entries
+// sequentially, in groups of 16 independent loads followed by the group's running sums, so that
+// loads are in flight back to back.  Each element is summed in entry order.
+__global__ void __launch_bounds__(64) bwd_scan_kernel(float* st, int64_t n, int64_t rec, int mode) {
+    const int64_t rec4 = rec / 4;
+    const int64_t per = (rec4 + 63) / 64;   // workgroups per (batch, head)
+    const int64_t e = ((int64_t)blockIdx.x % per) * 64 + threadIdx.x;
+    if (e >= rec4) return;
+    f32x4* base = reinterpret_cast<f32x4*>(st + ((int64_t)blockIdx.x / per) * n * rec) + e;
+    f32x4 run = {0.f, 0.f, 0.f, 0.f};
     for (int64_t c0 = 0; c0 < n; c0 += 16) {
-        float x[16];
+        f32x4 x[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int64_t c = mode == 1 ? n - 1 - (c0 + j) : c0 + j;   // suffix: entries from the end
-            x[j] = (c0 + j < n) ? base[c * rec] : 0.f;
+            x[j] = (c0 + j < n) ? base[c * rec4] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
         if (mode == 2) {
 #pragma unroll
@@ -537,7 +563,7 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(float* st, int64_t n, int
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int64_t c = mode == 1 ? n - 1 - (c0 + j) : c0 + j;
-                if (c0 + j < n) base[c * rec] = run;
+                if (c0 + j < n) base[c * rec4] = run;
                 run += x[j];
             }
         }
@@ -701,7 +727,7 @@ void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream
 }
 
 void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mode, hipStream_t s) {
-    bwd_scan_kernel<<<dim3((unsigned)((rec + 255) / 256 * n_outer)), dim3(256), 0, s>>>(st, n, rec, mode);
+    bwd_scan_kernel<<<dim3((unsigned)((rec / 4 + 63) / 64 * n_outer)), dim3(64), 0, s>>>(st, n, rec, mode);
 }
 
 void launch_bwd_param(const float* gp, const float* mu, const float* raw_var, const float* prior, float* dmu,

@@ -77,7 +77,8 @@ void launch_bwd_gh(const float* p, const void* dout, bool f32, float* rs, int64_
 // Softmax gradient in place: dl = gamma (dgamma - gamma . dgamma) per row of K.
 void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream_t s);
 // Chunk-state scans over [n_outer][n][rec]: mode 0 exclusive prefix in place, 1 exclusive suffix in
-// place, 2 the total into entry 0.
+// place, 2 the total into entry 0.  rec is a multiple of 4 (K times d_v + 1 rounded up to 4) and st
+// 16-byte aligned.
 void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mode, hipStream_t s);
 // Mixture-parameter gradients from the partial sums gp [parts][K][dxa] (parts = 2 sides x B x
 // n_seg per head; columns x | x^2 | 1 of dl^T [x | x^2 | 1]).
