@@ -483,57 +483,104 @@ __global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, cons
 }
 
 // ---------------------------------------------------------------------------------- rows
-// one wavefront per row; lane l holds columns l, l + 64, ...
+// One wavefront per group of kRowsPerWave consecutive rows (a million single-row waves per launch
+// would be bound by wave launch, not by memory): each row's loads are issued for the whole group
+// first, then its sums; within a row lane l holds columns l, l + 64, ... and the per-row order of
+// every sum is that of a one-row-per-wave kernel.
+constexpr int kRowsPerWave = 4;
+
 template <bool F32>
 __global__ void __launch_bounds__(256) bwd_gh_kernel(const float* p, const void* dout, float* rs, int64_t rows, int d_v,
                                                      int dva, float eps) {
     const int lane = threadIdx.x & 63;
-    const int64_t rr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (rr >= rows) return;
-    const float* pr = p + rr * dva;
-    const float den = pr[d_v] + eps;
-    const float inv = 1.f / den;
-    float dot = 0.f;
-    for (int c = lane; c < d_v; c += 64) dot += ld_elem<F32>(dout, rr * d_v + c) * (pr[c] * inv);
-    dot = wave_sum_f(dot);
-    if (lane == 0) {
-        rs[2 * rr] = inv;
-        rs[2 * rr + 1] = -dot * inv;
-    }
-}
-
-// dl = gamma * (dg - <gamma, dg>) per row, one wave per row.  Rows of up to 256 entries stay in
-// registers between the dot product and the update (element k on lane k % 64, slot k / 64); longer
-// rows are read twice.  Either way each row's dot product is summed in the same order.
-__global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* dg, int64_t rows, int K) {
-    const int lane = threadIdx.x & 63;
-    const int64_t rr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (rr >= rows) return;
-    const float* gr = gamma + rr * K;
-    float* dr = dg + rr * K;
-    float dot = 0.f;
-    if (K <= 256) {
-        float g[4], d[4];
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
+    if (r0 >= rows) return;
+    if (d_v <= 128) {
+        float den[kRowsPerWave], pv[kRowsPerWave][2], dv[kRowsPerWave][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = lane + 64 * j;
-            g[j] = k < K ? gr[k] : 0.f;
-            d[j] = k < K ? dr[k] : 0.f;
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            const int64_t rr = r0 + i < rows ? r0 + i : rows - 1;   // clamped: results of rows past the end are dropped
+            const float* pr = p + rr * dva;
+            den[i] = pr[d_v];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = lane + 64 * j;
+                pv[i][j] = c < d_v ? pr[c] : 0.f;
+                dv[i][j] = c < d_v ? ld_elem<F32>(dout, rr * d_v + c) : 0.f;
+            }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (lane + 64 * j < K) dot += g[j] * d[j];
-        dot = wave_sum_f(dot);
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            const float inv = 1.f / (den[i] + eps);
+            float dot = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = lane + 64 * j;
-            if (k < K) dr[k] = g[j] * (d[j] - dot);
+            for (int j = 0; j < 2; ++j)
+                if (lane + 64 * j < d_v) dot += dv[i][j] * (pv[i][j] * inv);
+            dot = wave_sum_f(dot);
+            if (lane == 0 && r0 + i < rows) {
+                rs[2 * (r0 + i)] = inv;
+                rs[2 * (r0 + i) + 1] = -dot * inv;
+            }
         }
         return;
     }
-    for (int k = lane; k < K; k += 64) dot += gr[k] * dr[k];
-    dot = wave_sum_f(dot);
-    for (int k = lane; k < K; k += 64) dr[k] = gr[k] * (dr[k] - dot);
+    for (int i = 0; i < kRowsPerWave && r0 + i < rows; ++i) {
+        const int64_t rr = r0 + i;
+        const float* pr = p + rr * dva;
+        const float inv = 1.f / (pr[d_v] + eps);
+        float dot = 0.f;
+        for (int c = lane; c < d_v; c += 64) dot += ld_elem<F32>(dout, rr * d_v + c) * (pr[c] * inv);
+        dot = wave_sum_f(dot);
+        if (lane == 0) {
+            rs[2 * rr] = inv;
+            rs[2 * rr + 1] = -dot * inv;
+        }
+    }
+}
+
+// dl = gamma * (dg - <gamma, dg>) per row.  Rows of up to 256 entries stay in registers between the
+// dot product and the update (element k on lane k % 64, slot k / 64); longer rows are read twice.
+__global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* dg, int64_t rows, int K) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
+    if (r0 >= rows) return;
+    if (K <= 256) {
+        float g[kRowsPerWave][4], d[kRowsPerWave][4];
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            const int64_t rr = r0 + i < rows ? r0 + i : rows - 1;   // clamped: rows past the end are not written
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = lane + 64 * j;
+                g[i][j] = k < K ? gamma[rr * K + k] : 0.f;
+                d[i][j] = k < K ? dg[rr * K + k] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            float dot = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (lane + 64 * j < K) dot += g[i][j] * d[i][j];
+            dot = wave_sum_f(dot);
+            if (r0 + i < rows) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int k = lane + 64 * j;
+                    if (k < K) dg[(r0 + i) * K + k] = g[i][j] * (d[i][j] - dot);
+                }
+            }
+        }
+        return;
+    }
+    for (int i = 0; i < kRowsPerWave && r0 + i < rows; ++i) {
+        const float* gr = gamma + (r0 + i) * K;
+        float* dr = dg + (r0 + i) * K;
+        float dot = 0.f;
+        for (int k = lane; k < K; k += 64) dot += gr[k] * dr[k];
+        dot = wave_sum_f(dot);
+        for (int k = lane; k < K; k += 64) dr[k] = gr[k] * (dr[k] - dot);
+    }
 }
 
 // ---------------------------------------------------------------------------------- scans
@@ -575,6 +622,8 @@ __global__ void __launch_bounds__(64) bwd_scan_kernel(float* st, int64_t n, int6
 // gp [2][B * H][n_seg][K][dxa]; element (k, d) of head blockIdx.y sums its partials in a fixed order:
 //   G1 = sum dl x_d, G2 = sum dl x_d^2, G0 = sum dl
 //   dmu = (G1 - mu G0) / s, ds = ((G2 - 2 mu G1 + mu^2 G0) / s^2 - G0 / s) / 2, draw_var = ds sigmoid(rho)
+constexpr int kParamBatch = 8;   // partial loads in flight per thread in the parameter reductions
+
 __global__ void __launch_bounds__(256) bwd_param_kernel(const float* gp, const float* mu, const float* raw_var,
                                                         float* dmu, float* draw_var, int64_t B, int H, int K, int d_r,
                                                         int dxa, int64_t n_seg) {
@@ -584,16 +633,28 @@ __global__ void __launch_bounds__(256) bwd_param_kernel(const float* gp, const f
     if (e >= K * d_r) return;
     const int k = e / d_r, d = e % d_r;
     const int64_t part = (int64_t)K * dxa;
+    // partial t = (side * B + b) * n_seg + sg, summed in that order; loads batched kParamBatch at a time
+    const int64_t nt = 2 * B * n_seg;
     float g0 = 0.f, g1 = 0.f, g2 = 0.f;
-    for (int side = 0; side < 2; ++side)
-        for (int64_t b = 0; b < B; ++b) {
-            const float* p = gp + ((side * B + b) * H + h) * n_seg * part + (int64_t)k * dxa;
-            for (int64_t sg = 0; sg < n_seg; ++sg) {
-                g1 += p[sg * part + d];
-                g2 += p[sg * part + d_r + d];
-                g0 += p[sg * part + 2 * d_r];
-            }
+    for (int64_t t0 = 0; t0 < nt; t0 += kParamBatch) {
+        float a0[kParamBatch], a1[kParamBatch], a2[kParamBatch];
+#pragma unroll
+        for (int j = 0; j < kParamBatch; ++j) {
+            const int64_t t = t0 + j < nt ? t0 + j : nt - 1;
+            const int64_t q = t / n_seg;
+            const float* p = gp + ((q * H + h) * n_seg + (t - q * n_seg)) * part + (int64_t)k * dxa;
+            a1[j] = p[d];
+            a2[j] = p[d_r + d];
+            a0[j] = p[2 * d_r];
         }
+#pragma unroll
+        for (int j = 0; j < kParamBatch; ++j)
+            if (t0 + j < nt) {
+                g1 += a1[j];
+                g2 += a2[j];
+                g0 += a0[j];
+            }
+    }
     const int64_t pe = (int64_t)h * K * d_r + e;
     const float m = mu[pe], rv = raw_var[pe];
     const float s = fmaxf(rv, 0.f) + log1pf(expf(-fabsf(rv)));
@@ -611,12 +672,20 @@ __global__ void __launch_bounds__(256) bwd_prior_kernel(const float* gp, const f
     __shared__ float s_p[256];
     const int64_t part = (int64_t)K * dxa;
     if (tid < K) {
+        const int64_t nt = 2 * B * n_seg;
         float g0 = 0.f;
-        for (int side = 0; side < 2; ++side)
-            for (int64_t b = 0; b < B; ++b) {
-                const float* p = gp + ((side * B + b) * H + h) * n_seg * part + (int64_t)tid * dxa + 2 * d_r;
-                for (int64_t sg = 0; sg < n_seg; ++sg) g0 += p[sg * part];
+        for (int64_t t0 = 0; t0 < nt; t0 += kParamBatch) {
+            float a0[kParamBatch];
+#pragma unroll
+            for (int j = 0; j < kParamBatch; ++j) {
+                const int64_t t = t0 + j < nt ? t0 + j : nt - 1;
+                const int64_t q = t / n_seg;
+                a0[j] = gp[((q * H + h) * n_seg + (t - q * n_seg)) * part + (int64_t)tid * dxa + 2 * d_r];
             }
+#pragma unroll
+            for (int j = 0; j < kParamBatch; ++j)
+                if (t0 + j < nt) g0 += a0[j];
+        }
         s_g[tid] = g0;
         s_p[tid] = prior[(int64_t)h * K + tid];
     }
@@ -717,13 +786,14 @@ void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const doubl
 
 void launch_bwd_gh(const float* p, const void* dout, bool f32, float* rs, int64_t rows, int d_v, int dva, float eps,
                    hipStream_t s) {
-    const dim3 grid((unsigned)((rows + 3) / 4));
+    const dim3 grid((unsigned)((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave)));
     if (f32) bwd_gh_kernel<true><<<grid, dim3(256), 0, s>>>(p, dout, rs, rows, d_v, dva, eps);
     else bwd_gh_kernel<false><<<grid, dim3(256), 0, s>>>(p, dout, rs, rows, d_v, dva, eps);
 }
 
 void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream_t s) {
-    bwd_dl_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(gamma, dg, rows, K);
+    bwd_dl_kernel<<<dim3((unsigned)((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave))), dim3(256), 0, s>>>(gamma, dg,
+                                                                                                       rows, K);
 }
 
 void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mode, hipStream_t s) {
