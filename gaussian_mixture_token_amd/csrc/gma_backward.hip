@@ -284,24 +284,26 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
 }
 
 // ---------------------------------------------------------------------------------- mixture
-// One workgroup per head; thread e handles elements e, e + 256, ... of [K, d_r].
 // The operands of the matrix-core log-densities (expanded form
 //   l_k = cq_k + sum_d (-s_kd^-1 / 2) x_d^2 + sum_d (mu_kd / s_kd) x_d,
 //   cq_k = log pi_k - 1/2 sum_d (log s_kd + mu_kd^2 / s_kd), fp64):
 // bf [H][d_r / 16 steps][2 parts (x^2, x)][KT][64 lanes][4]: lane (r, q) of component tile kt holds the
 // coefficients of component 16 kt + r for dims 16 step + 4 q .. + 3 (zero past K or d_r), the order
 // of the A fragments of the rows; cq [H][16 KT] with -inf past K.
+// One workgroup per (head, component tile): workgroup h * KT + kt writes the coefficients of tile kt
+// and the constants cq of its 16 components.  The terms log s_kd + mu_kd^2 / s_kd of cq are computed in
+// parallel, 128 dims at a time, into LDS; one thread per component adds them in dim order.
 __global__ void __launch_bounds__(256) bwd_frag_kernel(const float* mu, const float* raw_var, const float* prior,
                                                        float* bf, double* cq, int K, int d_r, int KT) {
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const int h = blockIdx.x / KT, kt = blockIdx.x % KT, tid = threadIdx.x;
     const int steps = (d_r + 15) / 16, KP = 16 * KT;
     const int64_t per_head = (int64_t)steps * 2 * KT * 256;
-    for (int64_t e = tid; e < per_head; e += 256) {
-        const int j = (int)(e & 3), lane = (int)((e >> 2) & 63);
-        int64_t t = e >> 8;
-        const int kt = (int)(t % KT);
-        t /= KT;
-        const int part = (int)(t & 1), st = (int)(t >> 1);
+    // element e of the head's operands: e >> 8 = (2 st + part) KT + kt, e & 255 = 4 lane + j
+    for (int i = tid; i < 2 * steps * 256; i += 256) {
+        const int sp = i >> 8;
+        const int64_t e = ((int64_t)sp * KT + kt) * 256 + (i & 255);
+        const int j = i & 3, lane = (i >> 2) & 63;
+        const int part = sp & 1, st = sp >> 1;
         const int k = 16 * kt + (lane & 15), d = 16 * st + 4 * (lane >> 4) + j;
         float val = 0.f;
         if (k < K && d < d_r) {
@@ -313,6 +315,7 @@ __global__ void __launch_bounds__(256) bwd_frag_kernel(const float* mu, const fl
         bf[(int64_t)h * per_head + e] = val;
     }
     __shared__ double s_lse;
+    __shared__ double s_term[16 * 128];
     if (tid < 64) {
         double mx = -INFINITY;
         for (int k = tid; k < K; k += 64) mx = fmax(mx, (double)prior[(int64_t)h * K + k]);
@@ -324,19 +327,29 @@ __global__ void __launch_bounds__(256) bwd_frag_kernel(const float* mu, const fl
         for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
         if (tid == 0) s_lse = mx + log(sm);
     }
-    __syncthreads();
-    for (int k = tid; k < KP; k += 256) {
-        double c = -INFINITY;
-        if (k < K) {
-            double acc = 0.0;
-            for (int d = 0; d < d_r; ++d) {
-                const int64_t pe = ((int64_t)h * K + k) * d_r + d;
+    double acc = 0.0;
+    for (int d0 = 0; d0 < d_r; d0 += 128) {
+        const int nd = d_r - d0 < 128 ? d_r - d0 : 128;
+        for (int i = tid; i < 16 * 128; i += 256) {
+            const int r = i >> 7, dd = i & 127, k = 16 * kt + r;
+            double term = 0.0;
+            if (k < K && dd < nd) {
+                const int64_t pe = ((int64_t)h * K + k) * d_r + d0 + dd;
                 const double rv = raw_var[pe], m = mu[pe];
                 const double sv = fmax(rv, 0.0) + log1p(exp(-fabs(rv)));
-                acc += log(sv) + m * m / sv;
+                term = log(sv) + m * m / sv;
             }
-            c = (double)prior[(int64_t)h * K + k] - s_lse - 0.5 * acc;
+            s_term[i] = term;
         }
+        __syncthreads();
+        if (tid < 16)
+            for (int dd = 0; dd < nd; ++dd) acc += s_term[tid * 128 + dd];
+        __syncthreads();
+    }
+    if (tid < 16) {
+        const int k = 16 * kt + tid;
+        double c = -INFINITY;
+        if (k < K) c = (double)prior[(int64_t)h * K + k] - s_lse - 0.5 * acc;
         cq[(int64_t)h * KP + k] = c;
     }
 }
@@ -770,7 +783,9 @@ int bwd_gamma_tiles(int K) {
 
 void launch_bwd_frag(const float* mu, const float* raw_var, const float* prior, float* bf, double* cq, int H, int K,
                      int d_r, hipStream_t s) {
-    bwd_frag_kernel<<<dim3(H), dim3(256), 0, s>>>(mu, raw_var, prior, bf, cq, K, d_r, bwd_gamma_tiles(K));
+    // H * KT <= 16 H fits the 32-bit grid (the backward plan bounds B * H * 16 by INT32_MAX)
+    const int KT = bwd_gamma_tiles(K);
+    bwd_frag_kernel<<<dim3((unsigned)(H * KT)), dim3(256), 0, s>>>(mu, raw_var, prior, bf, cq, K, d_r, KT);
 }
 
 void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const double* cq, float* gamma, int64_t BH,
