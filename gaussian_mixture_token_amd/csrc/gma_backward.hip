@@ -354,21 +354,23 @@ __global__ void __launch_bounds__(256) bwd_frag_kernel(const float* mu, const fl
     }
 }
 
-// One workgroup per head; thread e handles elements e, e + 256, ... of [K, d_r].
+// Element e = k d_r + d of [K, d_r] of head h: workgroup blockIdx.x = h * per + e / 256 with per
+// workgroups per head, one thread per element.
 __global__ void __launch_bounds__(256) bwd_prep_kernel(const float* mu, const float* raw_var, float* mw, int K,
                                                        int d_r) {
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const int per = (K * d_r + 255) / 256;
+    const int h = blockIdx.x / per;
+    const int e = (blockIdx.x % per) * 256 + threadIdx.x;
+    if (e >= K * d_r) return;
     const float* m_h = mu + (int64_t)h * K * d_r;
     const float* r_h = raw_var + (int64_t)h * K * d_r;
     float* mw_h = mw + (int64_t)h * K * 2 * d_r;
-    for (int e = tid; e < K * d_r; e += 256) {
-        const int k = e / d_r, d = e % d_r;
-        const float rv = r_h[e];
-        const float s = fmaxf(rv, 0.f) + log1pf(expf(-fabsf(rv)));   // softplus
-        const float wv = 1.f / s;
-        mw_h[(int64_t)k * 2 * d_r + 2 * d] = m_h[e] * wv;
-        mw_h[(int64_t)k * 2 * d_r + 2 * d + 1] = wv;
-    }
+    const int k = e / d_r, d = e % d_r;
+    const float rv = r_h[e];
+    const float s = fmaxf(rv, 0.f) + log1pf(expf(-fabsf(rv)));   // softplus
+    const float wv = 1.f / s;
+    mw_h[(int64_t)k * 2 * d_r + 2 * d] = m_h[e] * wv;
+    mw_h[(int64_t)k * 2 * d_r + 2 * d + 1] = wv;
 }
 
 // Responsibilities on the fp32 matrix cores, expanded form (see bwd_frag_kernel).  Workgroup: 64 G
@@ -773,7 +775,8 @@ bool launch_bwd_gemm(const BwdGemm& g0, bool ta, bool tb, bool out_bf16, hipStre
 }
 
 void launch_bwd_prep(const float* mu, const float* raw_var, float* mw, int H, int K, int d_r, hipStream_t s) {
-    bwd_prep_kernel<<<dim3(H), dim3(256), 0, s>>>(mu, raw_var, mw, K, d_r);
+    // the backward plan bounds H * ceil(K d_r / 256) by INT32_MAX (this grid and the parameter kernel's)
+    bwd_prep_kernel<<<dim3((unsigned)((K * d_r + 255) / 256 * H)), dim3(256), 0, s>>>(mu, raw_var, mw, K, d_r);
 }
 
 int bwd_gamma_tiles(int K) {

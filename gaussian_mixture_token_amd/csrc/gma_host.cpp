@@ -262,7 +262,8 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
     // one product's grid: tiles x batches must fit a 32-bit launch
     const int64_t widest = std::max<int64_t>(std::max<int64_t>(b->K, b->dva), std::max<int64_t>(2 * b->d_r, b->dxa));
     if (b->BH * std::max(b->n_st, b->n_sg) * ((kBwdSeg + 63) / 64) * ((widest + 63) / 64) > INT32_MAX ||
-        rows / 4 + 1 > INT32_MAX || b->BH * ((rec + 255) / 256) > INT32_MAX)
+        rows / 4 + 1 > INT32_MAX || b->BH * ((rec + 255) / 256) > INT32_MAX ||
+        b->H * (((int64_t)b->K * b->d_r + 255) / 256) > INT32_MAX)
         return fail(GMA_ERROR_NOT_SUPPORTED, "problem too large for the backward grids");
     const int64_t C = b->st_step;
     size_t off = 0;
