@@ -498,8 +498,8 @@ __global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, cons
 }
 
 // ---------------------------------------------------------------------------------- rows
-// One wavefront per group of kRowsPerWave consecutive rows (a million single-row waves per launch
-// would be bound by wave launch, not by memory): each row's loads are issued for the whole group
+// One wavefront per group of consecutive rows (a million single-row waves of the short [g | h] rows
+// per launch are bound by wave launch, not by memory): each row's loads are issued for the whole group
 // first, then its sums; within a row lane l holds columns l, l + 64, ... and the per-row order of
 // every sum is that of a one-row-per-wave kernel.
 constexpr int kRowsPerWave = 4;
@@ -555,14 +555,17 @@ __global__ void __launch_bounds__(256) bwd_gh_kernel(const float* p, const void*
 
 // dl = gamma * (dg - <gamma, dg>) per row.  Rows of up to 256 entries stay in registers between the
 // dot product and the update (element k on lane k % 64, slot k / 64); longer rows are read twice.
+// Rows per wave R: 4 for short rows (K <= 64); rows of K > 64 already stream near the HBM rate at one
+// row per wave and measured slower with four (271 -> 293 us at B1 H16 N65536 K128).
+template <int R>
 __global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* dg, int64_t rows, int K) {
     const int lane = threadIdx.x & 63;
-    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
     if (r0 >= rows) return;
     if (K <= 256) {
-        float g[kRowsPerWave][4], d[kRowsPerWave][4];
+        float g[R][4], d[R][4];
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) {
+        for (int i = 0; i < R; ++i) {
             const int64_t rr = r0 + i < rows ? r0 + i : rows - 1;   // clamped: rows past the end are not written
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -572,7 +575,7 @@ __global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* 
             }
         }
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave; ++i) {
+        for (int i = 0; i < R; ++i) {
             float dot = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -588,7 +591,7 @@ __global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* 
         }
         return;
     }
-    for (int i = 0; i < kRowsPerWave && r0 + i < rows; ++i) {
+    for (int i = 0; i < R && r0 + i < rows; ++i) {
         const float* gr = gamma + (r0 + i) * K;
         float* dr = dg + (r0 + i) * K;
         float dot = 0.f;
@@ -810,8 +813,10 @@ void launch_bwd_gh(const float* p, const void* dout, bool f32, float* rs, int64_
 }
 
 void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream_t s) {
-    bwd_dl_kernel<<<dim3((unsigned)((rows + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave))), dim3(256), 0, s>>>(gamma, dg,
-                                                                                                       rows, K);
+    if (K <= 64)
+        bwd_dl_kernel<4><<<dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s>>>(gamma, dg, rows, K);
+    else
+        bwd_dl_kernel<1><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(gamma, dg, rows, K);
 }
 
 void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mode, hipStream_t s) {
