@@ -640,7 +640,7 @@ __global__ void __launch_bounds__(64) bwd_scan_kernel(float* st, int64_t n, int6
 // gp [2][B * H][n_seg][K][dxa]; element (k, d) of head blockIdx.y sums its partials in a fixed order:
 //   G1 = sum dl x_d, G2 = sum dl x_d^2, G0 = sum dl
 //   dmu = (G1 - mu G0) / s, ds = ((G2 - 2 mu G1 + mu^2 G0) / s^2 - G0 / s) / 2, draw_var = ds sigmoid(rho)
-constexpr int kParamBatch = 8;   // partial loads in flight per thread in the parameter reductions
+constexpr int kParamBatch = 16;  // partial loads in flight per thread in the parameter reductions
 
 __global__ void __launch_bounds__(256) bwd_param_kernel(const float* gp, const float* mu, const float* raw_var,
                                                         float* dmu, float* draw_var, int64_t B, int H, int K, int d_r,
