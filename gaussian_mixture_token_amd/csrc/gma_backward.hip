@@ -728,7 +728,9 @@ void gemm_dispatch(const BwdGemm& g, bool out_bf16, int64_t grid, hipStream_t s)
 template <int KT>
 void gamma_mfma_dispatch(const void* x, bool f32, const float* bf, const double* cq, float* gamma, int64_t BH,
                          int64_t N, int H, int K, int d_r, hipStream_t s) {
-    constexpr int G = KT <= 8 ? 2 : 1;   // row groups per wave (fp64 accumulators: 8 G KT registers)
+    // row groups per wave (fp64 accumulators: 8 G KT registers); at KT = 8 one group measured faster than
+    // two (816 -> 806 us at B1 H16 N65536 K128: twice the workgroups, half the accumulators)
+    constexpr int G = KT <= 4 ? 2 : 1;
     const dim3 grid((unsigned)((N + 64 * G - 1) / (64 * G) * BH));
     const int vecx = (reinterpret_cast<uintptr_t>(x) % 16 == 0 && d_r % 4 == 0) ? 1 : 0;
     if (f32) bwd_gamma_mfma_kernel<KT, G, true><<<grid, dim3(256), 0, s>>>(x, bf, cq, gamma, N, H, K, d_r, vecx);
