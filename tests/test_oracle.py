@@ -445,8 +445,38 @@ def test_stats_invariants(oracle_mod):
     usage, hard, ent, gap = oracle_mod.responsibility_stats(x, mu, rv, pl)
     np.testing.assert_allclose(usage.sum(axis=-1), N, rtol=1e-12)      # rows of Gamma sum to one
     assert (hard.sum(axis=-1) == N).all()
-    assert (ent >= 0).all() and (ent <= math.log(K) + 1e-12).all()
+    assert (ent >= 0).all() and (ent <= 1 + 1e-12).all()               # normalised by ln K
     assert (gap >= 0).all() and (gap <= 1).all()
+    # uniform usage has the largest entropy: identical components with equal priors give p_k = 1/K
+    mu1 = np.repeat(mu[:, :1], K, axis=1)
+    rv1 = np.repeat(rv[:, :1], K, axis=1)
+    _, _, e1, g1 = oracle_mod.responsibility_stats(x, mu1, rv1, np.zeros((H, K)))
+    np.testing.assert_allclose(e1, 1.0, rtol=1e-12)
+    np.testing.assert_allclose(g1, 0.0, atol=1e-15)
+
+
+def test_stats_gap_closed_forms(oracle_mod):
+    # d_r = 1, K = 2, equal variances and priors: gamma_1 = sigmoid((mu1 - mu2)(x - (mu1 + mu2)/2)/s2)
+    # (GMA page, item 1: the posterior of a two-component mixture), so the gap between the two
+    # responsibilities is |2 gamma_1 - 1| = |tanh((mu1 - mu2)(x - (mu1 + mu2)/2)/(2 s2))|
+    mu1, mu2, s2 = 0.7, -1.3, 0.8
+    rho = math.log(math.expm1(s2))                                       # softplus(rho) = s2
+    x = np.linspace(-4.0, 4.0, 97)
+    _, _, _, gap = oracle_mod.responsibility_stats(x.reshape(1, 1, -1, 1), np.array([[[mu1], [mu2]]]),
+                                                   np.full((1, 2, 1), rho), np.zeros((1, 2)))
+    want = np.abs(np.tanh((mu1 - mu2) * (x - (mu1 + mu2) / 2) / (2 * s2)))
+    np.testing.assert_allclose(gap[0, 0], want, rtol=1e-12, atol=1e-14)
+    # three components on a line (unit variances, equal priors), listed out of order (means 3, 0, 1):
+    # at x the weights are proportional to exp(-(x - m)^2 / 2).  The gap is the largest minus the
+    # second largest responsibility -- not the largest minus the smallest, and not a difference of
+    # components in index order.
+    means = [3.0, 0.0, 1.0]
+    xs = np.array([0.6, 0.45, 2.2, -1.0])
+    _, _, _, gap = oracle_mod.responsibility_stats(xs.reshape(1, 1, -1, 1), np.array([[[m] for m in means]]),
+                                                   np.full((1, 3, 1), math.log(math.e - 1.0)), np.zeros((1, 3)))
+    for i, xv in enumerate(xs):
+        wts = sorted(math.exp(-(xv - m) ** 2 / 2) for m in means)
+        assert gap[0, 0, i] == pytest.approx((wts[2] - wts[1]) / sum(wts), rel=1e-12, abs=1e-15)
 
 
 def test_stats_single_component_and_separated_clusters(oracle_mod):
@@ -454,7 +484,7 @@ def test_stats_single_component_and_separated_clusters(oracle_mod):
     rng = np.random.default_rng(42)
     mu, rv, pl = rand_params(rng, 1, 1, 3)
     u, hd, e, _ = oracle_mod.responsibility_stats(rng.normal(0, 1, (1, 1, 50, 3)), mu, rv, pl)
-    assert u[0, 0, 0] == pytest.approx(50.0) and hd[0, 0, 0] == 50 and e[0, 0] == pytest.approx(0.0, abs=1e-12)
+    assert u[0, 0, 0] == pytest.approx(50.0) and hd[0, 0, 0] == 50 and e[0, 0] == 0.0
     # three far-apart unit-variance clusters with equal priors, 10 / 20 / 30 points drawn at each mean:
     # hard counts are the cluster sizes, usage is the same to within e^-(distance), entropy follows
     dr = 2
@@ -467,7 +497,7 @@ def test_stats_single_component_and_separated_clusters(oracle_mod):
     assert list(hd[0, 0]) == [10, 20, 30]
     np.testing.assert_allclose(u[0, 0], [10, 20, 30], atol=1e-9)
     p = np.array([10, 20, 30]) / 60
-    assert e[0, 0] == pytest.approx(float(-(p * np.log(p)).sum()), rel=1e-9)
+    assert e[0, 0] == pytest.approx(float(-(p * np.log(p)).sum()) / math.log(3), rel=1e-9)
 
 
 # ----------------------------------------------------------------------------- backward
