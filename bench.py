@@ -60,17 +60,19 @@ def algorithmic_flops_per_token_head(w) -> int:
 
 
 def kernel_work_per_token_head(w, kernel: str):
-    """Algorithmic (bytes, flops) per token-head of one forward kernel, for its roofline.
+    """Algorithmic (bytes, flops) per token-head of one forward kernel: the bytes the path charges it and
+    the flops of the method it performs.
 
-    causal_output: the path's figures (it reads Q_X, V and the stored Gamma_K tiles, the size of K_X
-    when K = d_r, and writes O; its flops are counted as the whole path's).  segment_aggregate reads
-    K_X and V (K-side logits, write); bidir_output reads Q_X and writes O (Q-side logits, read)."""
+    causal_output: the path's bytes (it reads Q_X, V and the stored Gamma_K tiles, the size of K_X when
+    K = d_r, and writes O); flops of the Q-side logits (4 K d_r), the read (2 K d_v) and the running
+    state update (2 K d_v) -- the K-side logits run in the aggregate pass.  segment_aggregate reads K_X
+    and V (K-side logits, write); bidir_output reads Q_X and writes O (Q-side logits, read)."""
     es = 2 if w.dtype == "bf16" else 4
     if kernel == "segment_aggregate":
         return es * (w.d_route + w.d_value), 4 * w.n_comp * w.d_route + 2 * w.n_comp * w.d_value
     if kernel == "bidir_output":
         return es * (w.d_route + w.d_value), 4 * w.n_comp * w.d_route + 2 * w.n_comp * w.d_value
-    return algorithmic_bytes_per_token_head(w), algorithmic_flops_per_token_head(w)
+    return algorithmic_bytes_per_token_head(w), 4 * w.n_comp * w.d_route + 4 * w.n_comp * w.d_value
 
 
 def backward_bytes_per_token_head(w) -> int:
@@ -101,6 +103,29 @@ def load_traffic(workload_name: str, kernel: str, src_hash: str):
     return ent.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def step_traffic(w, kernels, src_hash: str):
+    """Measured HBM bytes of one whole step: each kernel's counter bytes per launch times its launches
+    per step, or None unless every kernel of the step has counters for the current source."""
+    total = 0.0
+    for name, k in kernels.items():
+        b = load_traffic(w.name, name, src_hash)
+        if b is None:
+            return None
+        total += b * k["launches_per_step"]
+    return total
+
+
 def cpu_baseline_backward(w, heads, dout):
     import oracle
     from gaussian_mixture_token_amd import make_inputs
@@ -113,7 +138,7 @@ def cpu_baseline_backward(w, heads, dout):
     dt = time.perf_counter() - t0
     token_heads = w.batch * len(heads) * w.seq_len
     return {"value": token_heads / dt / w.heads, "unit": "tokens/s", "cores": min(threads, w.batch * len(heads)),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d of %d heads, full N=%d, %s fp64 oracle backward (threads over (batch, head)), %.1f s wall" %
                       (len(heads), w.heads, w.seq_len, "causal" if w.causal else "bidirectional", dt)}
 
@@ -131,7 +156,7 @@ def cpu_baseline(w, heads):
     dt = time.perf_counter() - t0
     token_heads = w.batch * len(heads) * w.seq_len
     return {"value": token_heads / dt / w.heads, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d heads, full N=%d, %s fp64 oracle, %.1f s wall" %
+            "cpu_model": cpu_model(), "sample": "%d of %d heads, full N=%d, %s fp64 oracle, %.1f s wall" %
                       (len(heads), w.heads, w.seq_len, "causal" if w.causal else "bidirectional", dt)}
 
 
@@ -147,6 +172,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time one-token causal decode steps (raw and prepared mixture) at the workload's B, H, "
                          "d_r, K, d_v instead of the forward")
+    ap.add_argument("--rounds", type=int, default=None,
+                    help="launch the causal pass in this many rounds over the sequence (GMA_CAUSAL_ROUNDS; "
+                         "a measured-slower schedule kept for comparison)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) and exit; "
                          "its FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
@@ -156,6 +184,8 @@ def main():
               "(each (batch, head) or sequence shard would run the same single-GPU path).", file=sys.stderr)
         sys.exit(2)
 
+    if args.rounds is not None:
+        os.environ["GMA_CAUSAL_ROUNDS"] = str(args.rounds)
     import torch
     import gaussian_mixture_token_amd as gma
     from gaussian_mixture_token_amd import _lib
@@ -261,36 +291,44 @@ def main():
         tot, n = ctypes_double(), ctypes_int64()
         _lib.check(lib.gma_timing_read(k, tot, n))
         if n.value:
-            kernels[lib.gma_kernel_name(k).decode()] = {"avg_us": 1e3 * tot.value / n.value, "launches": n.value}
+            kernels[lib.gma_kernel_name(k).decode()] = {"avg_us": 1e3 * tot.value / n.value, "launches": n.value,
+                                                        "launches_per_step": n.value / args.steps}
     T = w.batch * w.heads * w.seq_len
     if args.backward:
         bwd_line(args, w, value, ms_per_step, kernels, T, dout, step_isolated)
         return
-    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    avg_s = kernels[dominant]["avg_us"] * 1e-6
-    kb, kf = kernel_work_per_token_head(w, dominant)
-    alg_bytes = kb * T
-    alg_flops = kf * T
-    hbm_frac = alg_bytes / avg_s / 1e9 / HBM_PEAK_GBS
-    mfma_frac = alg_flops / avg_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]
     src_hash = kernel_source_hash()
-    traffic = load_traffic(w.name, dominant, src_hash)
-    if hbm_frac >= mfma_frac:
-        roof = {"bound": "hbm", "achieved": alg_bytes / avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": hbm_frac, "traffic": traffic}
-    else:
-        roof = {"bound": "mfma", "achieved": alg_flops / avg_s / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype],
-                "unit": "TFLOP/s", "frac": mfma_frac, "traffic": traffic}
-    roof.update({"kernel": dominant, "kernel_avg_us": kernels[dominant]["avg_us"],
-                 "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": alg_flops,
-                 "hbm_frac": hbm_frac, "mfma_frac": mfma_frac})
-    # whole-step fractions (all kernels of the step against the path's algorithmic work)
+    # The roofline of the step: the path's algorithmic bytes and flops (read Q_X, K_X, V once, write O
+    # once; logits of both sides, write and read) over the sustained time of back-to-back whole steps
+    # (timed region 1, events on the launch stream).  `traffic`: the HBM bytes the step's kernels move,
+    # from the committed counter runs of the same source.
     step_s = ms_per_step * 1e-3
     path_bytes = algorithmic_bytes_per_token_head(w) * T
     path_flops = algorithmic_flops_per_token_head(w) * T
-    step_roof = {"hbm_frac": path_bytes / step_s / 1e9 / HBM_PEAK_GBS,
-                 "mfma_frac": path_flops / step_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
-                 "algorithmic_bytes_per_step": path_bytes, "algorithmic_flops_per_step": path_flops}
+    hbm_frac = path_bytes / step_s / 1e9 / HBM_PEAK_GBS
+    mfma_frac = path_flops / step_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]
+    traffic = step_traffic(w, kernels, src_hash)
+    if hbm_frac >= mfma_frac:
+        roof = {"bound": "hbm", "achieved": path_bytes / step_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": hbm_frac, "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": path_flops / step_s / 1e12, "peak": MFMA_PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": mfma_frac, "traffic": traffic}
+    roof.update({"kernel": "whole step (%s, back to back)" % ", ".join(kernels), "time_us": ms_per_step * 1e3,
+                 "algorithmic_bytes_per_step": path_bytes, "algorithmic_flops_per_step": path_flops,
+                 "hbm_frac": hbm_frac, "mfma_frac": mfma_frac,
+                 "traffic_over_algorithmic": None if traffic is None else traffic / path_bytes})
+    # The longest kernel alone, timed in region 2 (a HIP event pair around every launch): lighter duty
+    # than back-to-back steps (the event packets leave gaps between kernels), so its fractions are an
+    # upper bound on what the kernel sustains inside the step.
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    avg_s = kernels[dominant]["avg_us"] * 1e-6
+    kb, kf = kernel_work_per_token_head(w, dominant)
+    dom = {"kernel": dominant, "avg_us": kernels[dominant]["avg_us"], "timing": "HIP event pair per launch",
+           "algorithmic_bytes_per_launch": kb * T, "algorithmic_flops_per_launch": kf * T,
+           "hbm_frac": kb * T / avg_s / 1e9 / HBM_PEAK_GBS,
+           "mfma_frac": kf * T / avg_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
+           "traffic": load_traffic(w.name, dominant, src_hash)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -315,7 +353,7 @@ def main():
                    "heads": w.heads, "seq_len": w.seq_len, "d_route": w.d_route, "n_comp": w.n_comp,
                    "d_value": w.d_value, "eps": w.eps, "global_batch": w.batch, "parallelism": "single GPU"},
         "roofline": roof,
-        "step_roofline": step_roof,
+        "dominant_kernel": dom,
         "step_isolated": step_isolated,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -60,10 +60,27 @@ def _params(mu, raw_var, prior_logits, H, K, d_r):
             raise ValueError("%s must have shape %s, got %s" % (name, shape, tuple(t.shape)))
 
 
+def _on(t: torch.Tensor, dev: torch.device, name: str) -> None:
+    """t is a contiguous GPU tensor on device dev (the library is handed raw device pointers)."""
+    if not t.is_cuda or t.device != dev:
+        raise ValueError("%s must be on the inputs' device %s (got %s)" % (name, dev, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_out(out: torch.Tensor, shape, dtype: torch.dtype, dev: torch.device, name: str = "out") -> None:
+    """A caller-supplied output: the library writes prod(shape) elements of dtype through its pointer."""
+    _on(out, dev, name)
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype:
+        raise ValueError("%s must be a %s tensor of shape %s (got %s %s)" % (name, dtype, tuple(shape), out.dtype,
+                                                                            tuple(out.shape)))
+
+
 def _workspace(nbytes: int, device: torch.device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
     # a caller's workspace is passed through with its size: the library validates it (the causal
     # pass accepts less than the advertised size and then recomputes Gamma_K)
     if workspace is not None:
+        _on(workspace, device, "workspace")
         return workspace
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
@@ -78,7 +95,7 @@ def responsibilities(x: torch.Tensor, mu: torch.Tensor, raw_var: torch.Tensor, p
     prob = problem(B, H, N, d_r, K, 1, x.dtype)
     if out is None:
         out = torch.empty(B, H, N, K, dtype=torch.float32, device=dev)
-    _check_gpu(out)
+    _check_out(out, (B, H, N, K), torch.float32, dev)
     ws = _workspace(workspace_size(prob, _lib.GMA_OP_RESPONSIBILITIES), dev, workspace)
     _lib.check(_lib.load().gma_responsibilities(ctypes.byref(prob), _ptr(x), _ptr(mu), _ptr(raw_var), _ptr(prior_logits),
                                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
@@ -98,7 +115,7 @@ def _forward(fn_name: str, op: int, qx, kx, v, mu, raw_var, prior_logits, eps, o
     prob = problem(B, H, N, d_r, K, d_v, qx.dtype, eps)
     if out is None:
         out = torch.empty(B, H, N, d_v, dtype=qx.dtype, device=dev)
-    _check_gpu(out)
+    _check_out(out, (B, H, N, d_v), qx.dtype, dev)
     ws = _workspace(workspace_size(prob, op), dev, workspace)
     fn = getattr(_lib.load(), fn_name)
     extra = []
@@ -107,7 +124,7 @@ def _forward(fn_name: str, op: int, qx, kx, v, mu, raw_var, prior_logits, eps, o
             if t is not None:
                 if t.dtype != torch.float32 or tuple(t.shape) != (B, H, K, d_v + 1) or not t.is_contiguous():
                     raise ValueError("%s must be a contiguous float32 [B, H, K, d_v + 1] tensor" % name)
-                _check_gpu(t)
+                _on(t, dev, name)
         extra = [_ptr(t) if t is not None else None for t in states]
     _lib.check(fn(ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu), _ptr(raw_var), _ptr(prior_logits),
                   *extra, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev)))
@@ -137,7 +154,7 @@ def _forward_kv(qx, kx, v, mu, raw_var, prior_logits, eps, out, workspace):
     prob = problem(B, H, Nq, d_r, K, d_v, qx.dtype, eps)
     if out is None:
         out = torch.empty(B, H, Nq, d_v, dtype=qx.dtype, device=dev)
-    _check_gpu(out)
+    _check_out(out, (B, H, Nq, d_v), qx.dtype, dev)
     ws = _workspace(workspace_size(problem(B, H, Nk, d_r, K, d_v, qx.dtype, eps), _lib.GMA_OP_FORWARD_BIDIR), dev,
                     workspace)
     _lib.check(_lib.load().gma_forward_bidir_kv(ctypes.byref(prob), Nk, _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu),
@@ -182,7 +199,7 @@ def decode_prepare(raw_var, prior_logits, prepared=None):
         raise ValueError("unsupported mixture shape H=%d K=%d d_r=%d" % (H, K, d_r))
     if prepared is None:
         prepared = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    _check_gpu(prepared)
+    _on(prepared, dev, "prepared")
     _lib.check(lib.gma_decode_prepare(ctypes.byref(prob), _ptr(raw_var), _ptr(prior_logits), _ptr(prepared),
                                       prepared.numel() * prepared.element_size(), _stream(dev)))
     return prepared
@@ -211,14 +228,14 @@ def decode_step(qx, kx, v, mu, raw_var, prior_logits, state, eps: float = 1e-6, 
         if t is not None:
             if t.dtype != torch.float32 or tuple(t.shape) != (B, H, K, d_v + 1) or not t.is_contiguous():
                 raise ValueError("%s must be a contiguous float32 [B, H, K, d_v + 1] tensor" % name)
-            _check_gpu(t)
+            _on(t, dev, name)
     prob = problem(B, H, 1, d_r, K, d_v, qx.dtype, eps)
     if out is None:
         out = torch.empty(B, H, 1, d_v, dtype=qx.dtype, device=dev)
-    _check_gpu(out)
+    _check_out(out, (B, H, 1, d_v), qx.dtype, dev)
     dst = state if state_out is None else state_out
     if prepared is not None:
-        _check_gpu(prepared)
+        _on(prepared, dev, "prepared")
         _lib.check(_lib.load().gma_decode_step_prepared(
             ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu), _ptr(prepared),
             prepared.numel() * prepared.element_size(), _ptr(state), _ptr(dst), _ptr(out), _stream(dev)))
@@ -231,7 +248,8 @@ def decode_step(qx, kx, v, mu, raw_var, prior_logits, state, eps: float = 1e-6, 
 def responsibility_stats(x, mu, raw_var, prior_logits, workspace=None):
     """Diagnostics of the responsibilities of x [B, H, N, d_r]: usage [B, H, K] fp32 (sum of Gamma over
     the rows), hard counts [B, H, K] int32 view of uint32 (rows whose largest gamma is at k, ties to
-    the lowest k) and usage entropy [B, H] fp32 (of usage / N, natural log)."""
+    the lowest k) and usage entropy [B, H] fp32 (of usage / N, divided by ln K: a fraction of its largest
+    value)."""
     B, H, N, d_r = x.shape
     K = mu.shape[1]
     _params(mu, raw_var, prior_logits, H, K, d_r)
@@ -271,7 +289,7 @@ def backward(qx, kx, v, mu, raw_var, prior_logits, dout, eps: float = 1e-6, caus
         t = grads[name]
         if t.dtype != ref.dtype or t.shape != ref.shape:
             raise ValueError("%s must match its input's dtype and shape" % name)
-        _check_gpu(t)
+        _on(t, dev, name)
     op = _lib.GMA_OP_BACKWARD_CAUSAL if causal else _lib.GMA_OP_BACKWARD_BIDIR
     ws = _workspace(workspace_size(prob, op), dev, workspace)
     fn = _lib.load().gma_backward_causal if causal else _lib.load().gma_backward_bidir

@@ -68,7 +68,10 @@ struct Plan {
     int seg_chunks = 1;
     bool dma = false;
     bool gtiles = false;   // causal token-split pair through stored Gamma_K tiles
-    size_t off_ab = 0, off_c = 0, off_seg = 0, off_gk = 0, off_state = 0, total = 0;
+    int rounds = 1;        // causal token-split pair: launches of (aggregate, scan, output) over the sequence
+    int P_round = 1;       // segments per (batch, head) in one round (P = rounds * P_round)
+    int64_t gk_ring = 0;   // Gamma_K tile slots per (batch, head) (one round's chunks; 0: n_chunks)
+    size_t off_ab = 0, off_c = 0, off_seg = 0, off_gk = 0, off_total = 0, off_state = 0, total = 0;
     int stat_segs = 0;                     // responsibility diagnostics: row segments per (batch, head)
     size_t off_gamma = 0, off_part = 0;
 };
@@ -163,9 +166,26 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
         int64_t P = (target + BH - 1) / BH;
         if (P > plan->n_chunks) P = plan->n_chunks;
         if (P < 1) P = 1;
-        const int64_t sc = (plan->n_chunks + P - 1) / P;
+        // Causal token-split pair: the sequence may be taken in R rounds of P segments per (batch, head),
+        // each round's aggregate, scan and output launched in turn, so that the output pass re-reads
+        // the K_X, V and Gamma_K tiles of its round while they may still be in the last-level cache.
+        // Measured slower at every R > 1 on MI355X (the passes are bound by their own instruction
+        // streams, not by HBM traffic, and each round adds a launch triple), so R = 1 unless
+        // GMA_CAUSAL_ROUNDS asks for more (a measurement switch; results then differ only in the
+        // summation order of the carried state).
+        const bool causal_op = op == GMA_OP_FORWARD_CAUSAL || op == GMA_OP_FORWARD_CAUSAL_STATE;
+        int64_t R = 1;
+        if (tok && causal_op) {
+            const char* env = getenv("GMA_CAUSAL_ROUNDS");
+            if (env) R = std::max<int64_t>(1, std::min<int64_t>(atoi(env), 64));
+            R = std::min<int64_t>(R, std::max<int64_t>(1, plan->n_chunks / P));
+        }
+        const int64_t sc = (plan->n_chunks + P * R - 1) / (P * R);
         plan->seg_chunks = (int)sc;
         plan->P = (int)((plan->n_chunks + sc - 1) / sc);
+        plan->P_round = (int)std::min<int64_t>(P, plan->P);
+        plan->rounds = (plan->P + plan->P_round - 1) / plan->P_round;
+        plan->gk_ring = plan->rounds > 1 ? (int64_t)plan->P_round * sc : 0;
     }
     if (BH * plan->P > INT32_MAX)
         return fail(GMA_ERROR_NOT_SUPPORTED, "grid too large");
@@ -191,14 +211,19 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     const bool stateful = op == GMA_OP_FORWARD_CAUSAL_STATE;
     size_t seg_bytes = 0;
     const bool need_seg = (op == GMA_OP_FORWARD_BIDIR) || (causal && (plan->P > 1 || plan->gtiles || stateful));
-    if (need_seg) seg_bytes = (size_t)BH * plan->P * rec_bytes;
-    const size_t gk_bytes = plan->gtiles ? (size_t)BH * plan->n_chunks * tile_bytes : 0;
+    // with rounds, the segment records and the Gamma_K tiles of one round are reused by the next, and
+    // the running total of the finished rounds is kept beside them
+    if (need_seg) seg_bytes = (size_t)BH * (plan->rounds > 1 ? plan->P_round : plan->P) * rec_bytes;
+    const int64_t gk_slots = plan->rounds > 1 ? plan->gk_ring : plan->n_chunks;
+    const size_t gk_bytes = plan->gtiles ? (size_t)BH * gk_slots * tile_bytes : 0;
+    const size_t total_bytes = plan->rounds > 1 ? (size_t)BH * rec_bytes : 0;
     const size_t state_bytes = stateful ? 2 * (size_t)BH * rec_bytes : 0;
     plan->off_ab = 0;
     plan->off_c = align_up(ab_bytes, 256);
     plan->off_seg = align_up(plan->off_c + c_bytes, 256);
     plan->off_gk = align_up(plan->off_seg + seg_bytes, 256);
-    plan->off_state = align_up(plan->off_gk + gk_bytes, 256);
+    plan->off_total = align_up(plan->off_gk + gk_bytes, 256);
+    plan->off_state = align_up(plan->off_total + total_bytes, 256);
     plan->total = align_up(plan->off_state + state_bytes, 256);
     if (op == GMA_OP_RESPONSIBILITY_STATS) {
         // Gamma of every row, then per-segment partial usages and counts
@@ -365,21 +390,24 @@ gma_status_t timed_launch(int kid, hipStream_t s, F&& launch) {
 //         NULL); n_agg = aggregates present (P, or P - 1 when the last one was not computed);
 //         total[bh] <- init[bh] + sum of all P aggregates (only when n_agg = P and total != NULL)
 // bidir : seg[bh][0] <- sum_{t < P} seg[bh][t]
-__global__ void __launch_bounds__(256) scan_kernel(float* seg, int P, int64_t rec, int causal, int n_agg,
-                                                   const float* init, float* total) {
+// The P records of (batch, head) y start at record y * stride + s0 (stride = P, s0 = 0 for one pass
+// over the sequence; a round of the causal pair scans its own P records with init = the total of the
+// previous rounds).  init and total are [B*H, rec] and may be the same buffer (read before written).
+__global__ void __launch_bounds__(256) scan_kernel(float* seg, int P, int stride, int s0, int64_t rec, int causal,
+                                                   int n_agg, const float* init, float* total) {
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= rec) return;
-    float* base = seg + (int64_t)blockIdx.y * P * rec + e;
+    float* base = seg + ((int64_t)blockIdx.y * stride + s0) * rec + e;
     const int n = causal ? n_agg : P;
     float run = (causal && init) ? init[(int64_t)blockIdx.y * rec + e] : 0.f;
     // groups of 16 independent loads, then the sequential sum over the group
-    for (int s0 = 0; s0 < P; s0 += 16) {
+    for (int g0 = 0; g0 < P; g0 += 16) {
         float x[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) x[j] = (s0 + j < n) ? base[(int64_t)(s0 + j) * rec] : 0.f;
+        for (int j = 0; j < 16; ++j) x[j] = (g0 + j < n) ? base[(int64_t)(g0 + j) * rec] : 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            if (causal && s0 + j < P) base[(int64_t)(s0 + j) * rec] = run;
+            if (causal && g0 + j < P) base[(int64_t)(g0 + j) * rec] = run;
             run += x[j];
         }
     }
@@ -469,7 +497,8 @@ __global__ void __launch_bounds__(256) stats_partial_kernel(const float* gamma, 
     }
 }
 
-// Second level: usage and counts summed over the segments in order; usage entropy of usage / N.
+// Second level: usage and counts summed over the segments in order; usage entropy of usage / N,
+// normalised by ln K.
 __global__ void __launch_bounds__(256) stats_final_kernel(const float* pu, const uint32_t* pc, float* usage,
                                                           uint32_t* hard, float* entropy, int64_t N, int K, int S) {
     const int64_t bh = blockIdx.x;
@@ -492,7 +521,8 @@ __global__ void __launch_bounds__(256) stats_final_kernel(const float* pu, const
     for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o, 64);
     if (lane == 0) s_e[w] = e;
     __syncthreads();
-    if (tid == 0) entropy[bh] = ((s_e[0] + s_e[1]) + s_e[2]) + s_e[3];
+    // normalised by its largest value ln K (0 for K = 1)
+    if (tid == 0) entropy[bh] = K > 1 ? (((s_e[0] + s_e[1]) + s_e[2]) + s_e[3]) / logf((float)K) : 0.f;
 }
 
 gma_status_t launch_prep(const Plan& pl, const float* mu, const float* rv, const float* pr, char* ws, hipStream_t s) {
@@ -639,30 +669,58 @@ gma_status_t forward(const gma_problem_t* p, int op, const void* qx, const void*
         });
         if (st != GMA_SUCCESS) return st;
     }
-    // causal: the last segment's aggregate is needed only for the final state, but with stored tiles
-    // its Gamma_K tiles are
-    const int n_agg = (!causal || gt || rec_out) ? (int)pl.P : (int)pl.P - 1;
-    if (n_agg > 0) {
-        MainArgs ag = a;
-        ag.Pg = n_agg;
-        const int agrid = (int)(pl.B * pl.H * ag.Pg);
-        st = timed_launch(K_AGG, s, [&] { f_agg(ag, agrid, s); });
-        if (st != GMA_SUCCESS) return st;
-    }
-    const bool read_sum = !causal && pl.P <= kBidirReadSum;
-    if ((pl.P > 1 || rec_in || rec_out) && !read_sum) {
-        st = timed_launch(K_SCAN, s, [&] {
-            hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), BH), dim3(256), 0, s, a.seg, pl.P, rec,
-                               causal ? 1 : 0, n_agg, (const float*)rec_in, rec_out);
-        });
-        if (st != GMA_SUCCESS) return st;
-    }
     if (!causal) {
+        const int n_agg = (int)pl.P;
+        MainArgs ag = a;
+        st = timed_launch(K_AGG, s, [&] { f_agg(ag, (int)(pl.B * pl.H * n_agg), s); });
+        if (st != GMA_SUCCESS) return st;
+        const bool read_sum = pl.P <= kBidirReadSum;
+        if (pl.P > 1 && !read_sum) {
+            st = timed_launch(K_SCAN, s, [&] {
+                hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), BH), dim3(256), 0, s, a.seg, pl.P,
+                                   pl.P, 0, rec, 0, n_agg, (const float*)nullptr, (float*)nullptr);
+            });
+            if (st != GMA_SUCCESS) return st;
+        }
         a.bidir_segs = read_sum ? pl.P : 1;
         return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, grid, s); });
     }
-    a.has_carry = pl.P > 1 || rec_in;
-    st = timed_launch(K_OUT_CAUSAL, s, [&] { f_causal(a, grid, s); });
+    // Causal: rounds r = 0 .. rounds - 1, each over P_round consecutive segments of every (batch, head)
+    // (one round when the plan has none): aggregate pass, exclusive prefix of the round's aggregates
+    // from the total of the earlier rounds (the initial state, or zero, in round 0), output pass.  A
+    // round's records and Gamma_K tiles are reused by the next round.
+    float* run_total = pl.rounds > 1 ? reinterpret_cast<float*>(w + pl.off_total) : nullptr;
+    a.P = pl.rounds > 1 ? pl.P_round : pl.P;
+    a.gk_ring = pl.gk_ring;
+    for (int r = 0; r < pl.rounds; ++r) {
+        const int s0 = r * pl.P_round;
+        const int np = std::min(pl.P_round, pl.P - s0);
+        const bool last = r + 1 == pl.rounds;
+        // the last segment's aggregate is needed only for the final state, but with stored tiles its
+        // Gamma_K tiles are
+        const int n_agg = (!last || gt || rec_out) ? np : np - 1;
+        MainArgs ar = a;
+        ar.seg0 = s0;
+        if (n_agg > 0) {
+            MainArgs ag = ar;
+            ag.Pg = n_agg;
+            st = timed_launch(K_AGG, s, [&] { f_agg(ag, (int)(pl.B * pl.H * n_agg), s); });
+            if (st != GMA_SUCCESS) return st;
+        }
+        const float* init = r == 0 ? (const float*)rec_in : run_total;
+        float* tot = last ? rec_out : run_total;
+        if (np > 1 || init || tot) {
+            st = timed_launch(K_SCAN, s, [&] {
+                hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), BH), dim3(256), 0, s, a.seg, np,
+                                   a.P, 0, rec, 1, n_agg, init, tot);
+            });
+            if (st != GMA_SUCCESS) return st;
+        }
+        ar.Pg = np;
+        ar.has_carry = np > 1 || init;
+        st = timed_launch(K_OUT_CAUSAL, s, [&] { f_causal(ar, (int)(pl.B * pl.H * np), s); });
+        if (st != GMA_SUCCESS) return st;
+    }
     if (st != GMA_SUCCESS || !rec_out) return st;
     const int64_t nstate = (int64_t)pl.K * (pl.d_v + 1);
     return timed_launch(K_STATE, s, [&] {
@@ -734,7 +792,7 @@ gma_status_t forward_bidir_kv(const gma_problem_t* p, int64_t n_kv, const void* 
     if (plk.P > 1 && !read_sum) {
         st = timed_launch(K_SCAN, s, [&] {
             hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), (unsigned)BH), dim3(256), 0, s, ag.seg,
-                               plk.P, rec, 0, plk.P, (const float*)nullptr, (float*)nullptr);
+                               plk.P, plk.P, 0, rec, 0, plk.P, (const float*)nullptr, (float*)nullptr);
         });
         if (st != GMA_SUCCESS) return st;
     }

@@ -84,10 +84,13 @@ struct MainArgs {
     void* gk;              // [BH, n_chunks, 64 * KC] bf16 Gamma_K chunk tiles (MODE_AGG_G / MODE_OUT_CAUSAL_G)
     int64_t N;
     int H;
-    int P;                 // segments per head (record stride)
+    int P;                 // record stride per head (segments per head, or per round)
     int Pg;                // segments per head launched by this grid (P, or P - 1 for causal aggregates)
     int d_r, d_v, K;
     int seg_chunks;        // chunks of C tokens per segment
+    int seg0;              // first segment index of this launch (rounds of the causal token-split pair)
+    int64_t gk_ring;       // Gamma_K tiles kept per (batch, head): chunk ch lives in slot ch mod gk_ring
+                           // (0: one slot per chunk).  A launch's segments lie in one ring window.
     int vec_x, vec_v, vec_o;  // 16-byte (x, v) / 4-element (o) vector access allowed (register staging)
     int has_carry;         // causal: load the carried state (P > 1)
     int bidir_segs;        // bidirectional read pass: segment records to sum in order (0 or 1: record 0
@@ -538,12 +541,25 @@ main_kernel(const MainArgs a) {
         }
 
         // ---- logits^T tiles for own components: acc[kt][tt] (rows: comps 4g+i of tile ct, col: token 16tt+r)
+        // fp32 storage: the matrix cores sum each step of 16 dims (a x^2 + b x, 32 products) in fp32,
+        // and the steps are added in fp64 onto c.  The expanded form's terms are large and cancel (the
+        // logits of a row are around -100 in log2 units while their differences are a few units), so a
+        // single fp32 running sum over 2 d_r products would put about 1e-4 of error into the
+        // differences at d_r = 128, and ln 2 / 4 of that into Gamma.
         auto logits = [&](int which, f32x4 (&acc)[KT_W][NT]) {
+            [[maybe_unused]] double acc64[F32 ? KT_W : 1][F32 ? NT : 1][4];
 #pragma unroll
             for (int kt = 0; kt < KT_W; ++kt) {
                 const f32x4 cinit = *reinterpret_cast<const f32x4*>(&s_c[(w * KT_W + kt) * 16 + lg * 4]);
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) acc[kt][tt] = cinit;
+                for (int tt = 0; tt < NT; ++tt) {
+                    if constexpr (F32) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc64[kt][tt][i] = (double)cinit[i];
+                    } else {
+                        acc[kt][tt] = cinit;
+                    }
+                }
             }
 #pragma unroll
             for (int ks = 0; ks < NKS2; ++ks) {
@@ -559,10 +575,26 @@ main_kernel(const MainArgs a) {
                     const xfrag_t x2 = xf * xf;
 #pragma unroll
                     for (int kt = 0; kt < KT_W; ++kt) {
-                        mma(acc[kt][tt], abf[kt][ks], x2);
-                        mma(acc[kt][tt], abf[kt][ks + NKS2], xf);
+                        if constexpr (F32) {
+                            f32x4 part = {0.f, 0.f, 0.f, 0.f};
+                            mma(part, abf[kt][ks], x2);
+                            mma(part, abf[kt][ks + NKS2], xf);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc64[kt][tt][i] += (double)part[i];
+                        } else {
+                            mma(acc[kt][tt], abf[kt][ks], x2);
+                            mma(acc[kt][tt], abf[kt][ks + NKS2], xf);
+                        }
                     }
                 }
+            }
+            if constexpr (F32) {
+#pragma unroll
+                for (int kt = 0; kt < KT_W; ++kt)
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[kt][tt][i] = (float)acc64[kt][tt][i];
             }
         };
         f32x4 lq[NEED_Q ? KT_W : 1][NT];

@@ -128,7 +128,7 @@ tok_kernel(const MainArgs a) {
     [[maybe_unused]] const int lr = lane & 15;
     [[maybe_unused]] const int lg = lane >> 4;
     const int bh = blockIdx.x / a.Pg;
-    const int sidx = blockIdx.x % a.Pg;
+    const int sidx = a.seg0 + (int)(blockIdx.x % a.Pg);
     const int h = bh % a.H;
     const int64_t N = a.N;
     const int64_t n_chunks = (N + C - 1) / C;
@@ -152,12 +152,15 @@ tok_kernel(const MainArgs a) {
     if constexpr (NEED_K) rs_k = uniform_rsrc(make_rsrc_words(kx, (uint32_t)(N * a.d_r * 2)));
     if constexpr (NEED_V) rs_v = uniform_rsrc(make_rsrc_words(vv, (uint32_t)(N * a.d_v * 2)));
     if constexpr (OUT) rs_o = make_rsrc(oo, (uint32_t)(N * a.d_v * 2));
-    // Gamma_K tiles of this (batch, head): n_chunks images of GKBUF bytes
-    char* gkt = reinterpret_cast<char*>(a.gk) + (int64_t)bh * n_chunks * GKBUF;
+    // Gamma_K tiles of this (batch, head): a ring of `ring` images of GKBUF bytes; chunk ch of this
+    // segment sits in slot ch - gwin (the segment lies inside one ring window)
+    const int64_t ring = a.gk_ring ? a.gk_ring : n_chunks;
+    const int64_t gwin = (ch0 / ring) * ring;
+    char* gkt = reinterpret_cast<char*>(a.gk) + (int64_t)bh * ring * GKBUF;
     i32x4 rs_g;
     __amdgpu_buffer_rsrc_t rs_gs;
-    if constexpr (GLOAD) rs_g = uniform_rsrc(make_rsrc_words(gkt, (uint32_t)(n_chunks * GKBUF)));
-    if constexpr (GSTORE) rs_gs = make_rsrc(gkt, (uint32_t)(n_chunks * GKBUF));
+    if constexpr (GLOAD) rs_g = uniform_rsrc(make_rsrc_words(gkt, (uint32_t)(ring * GKBUF)));
+    if constexpr (GSTORE) rs_gs = make_rsrc(gkt, (uint32_t)(ring * GKBUF));
 
     // Lane id as seen inside the chunk loop: reassigned (opaque to the optimiser) at the start of every
     // chunk, so that lane-dependent offsets are recomputed there rather than held in registers
@@ -213,7 +216,7 @@ tok_kernel(const MainArgs a) {
             }
         } else {
             if constexpr (GLOAD) {
-                const uint32_t g0 = (uint32_t)(ch * GKBUF) + w * GKWAVE + lane * 16;
+                const uint32_t g0 = (uint32_t)((ch - gwin) * GKBUF) + w * GKWAVE + lane * 16;
                 const uint32_t m0 = lg_base + buf * GKBUF + w * GKWAVE;
 #pragma unroll
                 for (int j = 0; j < NGD; j += 4) {
@@ -254,7 +257,9 @@ tok_kernel(const MainArgs a) {
     f32x4 st[HAS_STATE ? KQW : 1][2][HAS_STATE ? VTW : 1];
     f32x4 zst[(HAS_STATE && ZREG) ? KQW : 1][2];
     const int64_t rec = (int64_t)KC * VC + KC;
-    float* segrec = a.seg + ((int64_t)bh * a.P + sidx) * rec;
+    // record of this segment: index sidx - seg0 among the launch's segments (a round reuses the
+    // records of the previous one; a.P is the record stride per (batch, head))
+    float* segrec = a.seg + ((int64_t)bh * a.P + (sidx - a.seg0)) * rec;
     if constexpr (HAS_STATE) {
         const bool load = (MODE == MODE_OUT_BIDIR) || (CAUSAL && a.has_carry);
         const float* src = (MODE == MODE_OUT_BIDIR) ? a.seg + (int64_t)bh * a.P * rec : segrec;
@@ -828,7 +833,7 @@ tok_kernel(const MainArgs a) {
 #pragma unroll
                 for (int j = 0; j < NGS; ++j) {
                     const int off = w * GKWAVE + j * 1024 + lane * 16;
-                    __builtin_amdgcn_raw_buffer_store_b128(lds_ld<u32x4>(LGK + off), rs_gs, (uint32_t)(ch * GKBUF) + off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(lds_ld<u32x4>(LGK + off), rs_gs, (uint32_t)((ch - gwin) * GKBUF) + off, 0, 0);
                 }
             }
 

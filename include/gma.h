@@ -42,6 +42,9 @@
  *              GMA_ERROR_NOT_SUPPORTED.  gma_decode_step and the backward have no classes.
  *   Results    deterministic: repeated calls give bitwise identical outputs (no atomics; every
  *              reduction runs in a fixed order independent of the device).
+ *   Environment GMA_CAUSAL_ROUNDS=R (measurement only; default 1): the bf16 causal pass launches its
+ *              aggregate, scan and output kernels in R rounds over the sequence instead of once.
+ *              Results differ from R = 1 only in the summation order of the carried state.
  */
 #ifndef GMA_H_
 #define GMA_H_
@@ -105,7 +108,11 @@ gma_status_t gma_responsibilities(const gma_problem_t* problem, const void* x, c
  *   hard_counts [B, H, K] uint32 number of rows whose largest gamma is at component k (ties go to the
  *                                lowest k; decided on the library's fp32 Gamma, so rows whose two
  *                                largest responsibilities are within its rounding may go either way);
- *   usage_entropy [B, H] fp32    -sum_k p_k ln p_k with p = usage / N (0 ln 0 = 0).
+ *   usage_entropy [B, H] fp32    -sum_k p_k ln p_k / ln K with p = usage / N (0 ln 0 = 0; 0 when
+ *                                K = 1): the usage entropy as a fraction of its largest value, the
+ *                                normalisation under which the page's interpretability figures (usage
+ *                                entropy 0.933 with 104 of 128 components in use, section "Résultats
+ *                                et Performance") are consistent.  Components in use: hard_counts > 0.
  * Gamma of every row is formed in the workspace: gma_workspace_size(problem,
  * GMA_OP_RESPONSIBILITY_STATS) bytes (about B * H * N * K * 4).  d_value is ignored. */
 gma_status_t gma_responsibility_stats(const gma_problem_t* problem, const void* x, const float* mu,
@@ -195,7 +202,6 @@ gma_status_t gma_decode_step_prepared(const gma_problem_t* problem, const void* 
                                       size_t prepared_bytes, const float* state_in, float* state_out,
                                       void* o, void* stream);
 
-/* Static description of a status code. */
 /* Backward of the bidirectional (gma_backward_bidir) or causal (gma_backward_causal) forward above:
  * the gradients of a scalar loss L with respect to every input, given dout = dL/dO [B, H, N, d_v].
  * The pages train the layer end to end (item 3: softplus variances and softmax priors are the
@@ -224,6 +230,7 @@ gma_status_t gma_backward_causal(const gma_problem_t* problem, const void* qx, c
                                  void* dv, float* dmu, float* draw_var, float* dprior_logits,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Static description of a status code. */
 const char* gma_status_string(gma_status_t status);
 
 /* Message of the last failing call on this thread ("" if none). */

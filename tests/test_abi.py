@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gma.h")
@@ -296,3 +297,13 @@ def test_backward_workspace_is_linear_in_the_sequence(lib):
         b = _ws(lib, op, seq_len=1 << 16)
         assert a > 0 and 3.9 * a < b < 4.1 * a, (op, a, b)
     assert _ws(lib, 5, seq_len=4096) < _ws(lib, 6, seq_len=4096)   # the causal chunk blocks
+
+
+def test_binding_rejects_outputs_that_do_not_fit():
+    # the checks that guard raw-pointer writes; a host tensor is never a valid output or workspace
+    from gaussian_mixture_token_amd import api
+    dev = torch.device("cuda", 0)
+    with pytest.raises(ValueError):
+        api._check_out(torch.zeros(2, 3), (2, 3), torch.float32, dev)
+    with pytest.raises(ValueError):
+        api._on(torch.zeros(4, dtype=torch.uint8), dev, "workspace")

@@ -2,7 +2,10 @@
 
 Tolerance (from the method's precision contract): max |O_gpu - O_ref| / max |O_ref| <= 1e-4
 for fp32 storage and <= 1e-2 for bf16 storage with fp32 accumulation.  Responsibilities:
-max |Gamma_gpu - Gamma_ref| <= 1e-4 (fp32) / 1e-2 (bf16), an absolute bound on probabilities.
+max |Gamma_gpu - Gamma_ref| <= 1e-5 (fp32) / 1e-2 (bf16), an absolute bound on probabilities.  The
+fp32 bound follows from the arithmetic: the logits are summed in fp64 over steps of 16 dims, each
+step's 32 products in fp32 (a few ulp of a partial sum of order 10), and an error dl in a logit
+difference moves Gamma by at most ln 2 / 4 * dl.
 
 Inputs come from gaussian_mixture_token_amd.workloads (seeded; shapes of the five workloads).
 Full-size workloads that the oracle cannot finish in seconds are compared on sampled heads:
@@ -18,6 +21,7 @@ from tests.conftest import gpu_available
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 1e-2}
+TOL_GAMMA = {"f32": 1e-5, "bf16": 1e-2}
 
 
 @pytest.fixture(scope="module")
@@ -78,7 +82,7 @@ def test_responsibilities_match_oracle(gma, cfg, shape):
     np.testing.assert_allclose(got.sum(-1), 1.0, atol=1e-5)
     err = np.abs(got - ref).max()
     say("  max |dGamma| = %.3e" % err)
-    assert err <= TOL[w.dtype]
+    assert err <= TOL_GAMMA[w.dtype]
 
 
 # ------------------------------------------------------------------------------------ forward parity
@@ -223,8 +227,10 @@ def test_causal_without_room_for_stored_tiles(gma, cfg, N):
 
 @pytest.mark.parametrize("cfg,B,H,N", [(3, 1, 3, 7000), (4, 1, 2, 5000), (2, 2, 2, 3000), (1, 2, 2, 2000), (0, 1, 1, 256)])
 def test_responsibility_stats_match_the_oracle(gma, cfg, B, H, N):
-    # usage and entropy within the Gamma tolerance; hard counts exactly, except that rows whose two
-    # largest responsibilities (oracle) are closer than twice that tolerance may go either way
+    # usage within twice the Gamma tolerance times sqrt(N) (the row errors do not share one sign), and
+    # summing to N over the components to fp32 rounding (a dropped or repeated row moves it by 1);
+    # entropy within twice the Gamma tolerance; hard counts exactly, except that rows whose two largest
+    # responsibilities (oracle) are closer than twice that tolerance may go either way
     w = gma.workload(cfg, batch=B, heads=H, seq_len=N)
     say("stats cfg %d B%d H%d N%d" % (cfg, B, H, N))
     inp = gma.make_inputs(w)
@@ -232,9 +238,10 @@ def test_responsibility_stats_match_the_oracle(gma, cfg, B, H, N):
     t = {k: v.to(DEV) for k, v in inp.items()}
     u, hc, e = gma.responsibility_stats(t["qx"], t["mu"], t["raw_var"], t["prior_logits"])
     torch.cuda.synchronize()
-    tol = 1e-4 if w.dtype == "f32" else 1e-2
+    tol = TOL_GAMMA[w.dtype]
     u, hc, e = u.cpu().numpy().astype(np.float64), hc.cpu().numpy().astype(np.int64), e.cpu().numpy()
-    assert np.abs(u - u_ref).max() <= tol * N
+    assert np.abs(u - u_ref).max() <= 2 * tol * np.sqrt(N)
+    np.testing.assert_allclose(u.sum(axis=-1), N, rtol=1e-5)
     assert (hc.sum(axis=-1) == N).all()
     np.testing.assert_allclose(e, e_ref, atol=2 * tol)
     ambiguous = (gap < 2 * tol).sum(axis=-1)                   # [B, H]
@@ -274,8 +281,11 @@ def _rel(a, b):
     return float(np.abs(a - b).max() / np.abs(b).max())
 
 
-@pytest.mark.parametrize("cfg,N,m", [(3, 3000, 1100), (4, 2500, 700), (2, 2000, 64), (1, 1500, 333)])
-@pytest.mark.parametrize("reduced_ws", [False, True])
+# reduced_ws: a workspace without room for the stored Gamma_K tiles, so the causal pass recomputes
+# Gamma_K from K_X (the tiles exist for bf16 storage only, so the fp32 workload has one case)
+@pytest.mark.parametrize("cfg,N,m,reduced_ws", [(3, 3000, 1100, False), (4, 2500, 700, False), (2, 2000, 64, False),
+                                                (1, 1500, 333, False), (3, 3000, 1100, True), (4, 2500, 700, True),
+                                                (2, 2000, 64, True)])
 def test_causal_state_continues_a_sequence(gma, cfg, N, m, reduced_ws):
     # the oracle runs tokens [0, m) and hands its state over; the GPU runs [m, N) from it and must
     # give the oracle's one-pass outputs of those rows and its final state
@@ -292,8 +302,6 @@ def test_causal_state_continues_a_sequence(gma, cfg, N, m, reduced_ws):
     s_out = torch.empty_like(s_in)
     kw = {}
     if reduced_ws:
-        if w.dtype != "bf16":
-            pytest.skip("the recompute path exists for bf16 storage only")
         prob = gma.problem(1, 2, N - m, w.d_route, w.n_comp, w.d_value, w.torch_dtype, w.eps)
         kw["workspace"] = torch.empty(gma.workspace_size(prob, 3) - 1, dtype=torch.uint8, device=DEV)
     o = gma.forward_causal(tail["qx"], tail["kx"], tail["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps,
