@@ -16,6 +16,7 @@ GMA_OP_FORWARD_CAUSAL_STATE = 3
 GMA_OP_RESPONSIBILITY_STATS = 4
 GMA_OP_BACKWARD_BIDIR = 5
 GMA_OP_BACKWARD_CAUSAL = 6
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GMA_NOALLOC_SCRATCH_BYTES in gma.h
 STATUS = {0: "GMA_SUCCESS", 1: "GMA_ERROR_INVALID_VALUE", 2: "GMA_ERROR_NOT_SUPPORTED",
           3: "GMA_ERROR_WORKSPACE_TOO_SMALL", 4: "GMA_ERROR_LAUNCH"}
 
@@ -42,6 +43,7 @@ _SIGS = [
     ("gma_responsibilities", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     ("gma_forward_bidir", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
     ("gma_forward_causal", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]),
+    ("gma_forward_causal_noalloc", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     ("gma_forward_bidir_kv", ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                             _VP, ctypes.c_size_t, _VP]),
     ("gma_responsibility_stats", ctypes.c_int, [ctypes.POINTER(Problem), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,

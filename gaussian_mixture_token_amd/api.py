@@ -13,7 +13,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["problem", "workspace_size", "responsibilities", "forward_bidir", "forward_causal",
+__all__ = ["problem", "workspace_size", "responsibilities", "forward_bidir", "forward_causal", "forward_causal_noalloc",
            "forward", "backward", "decode_step", "responsibility_stats", "GmaError"]
 
 GmaError = _lib.GmaError
@@ -175,6 +175,27 @@ def forward_causal(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=
                         out, workspace)
     return _forward("gma_forward_causal_state", _lib.GMA_OP_FORWARD_CAUSAL_STATE, qx, kx, v, mu, raw_var,
                     prior_logits, eps, out, workspace, states=(state_in, state_out))
+
+
+def forward_causal_noalloc(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, out=None):
+    """Causal O through gma_forward_causal_noalloc: the library's fixed scratch array is the workspace,
+    so the call allocates nothing (``out`` must then be supplied by a caller that cannot allocate)."""
+    B, H, N, d_r = qx.shape
+    d_v = v.shape[-1]
+    K = mu.shape[1]
+    if tuple(kx.shape) != (B, H, N, d_r) or tuple(v.shape[:3]) != (B, H, N):
+        raise ValueError("qx, kx must be [B, H, N, d_r] and v [B, H, N, d_v]")
+    if not (qx.dtype == kx.dtype == v.dtype):
+        raise TypeError("qx, kx and v must share one dtype")
+    _params(mu, raw_var, prior_logits, H, K, d_r)
+    dev = _check_gpu(qx, kx, v, mu, raw_var, prior_logits)
+    prob = problem(B, H, N, d_r, K, d_v, qx.dtype, eps)
+    if out is None:
+        out = torch.empty(B, H, N, d_v, dtype=qx.dtype, device=dev)
+    _check_out(out, (B, H, N, d_v), qx.dtype, dev)
+    _lib.check(_lib.load().gma_forward_causal_noalloc(ctypes.byref(prob), _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu),
+                                                      _ptr(raw_var), _ptr(prior_logits), _ptr(out), _stream(dev)))
+    return out
 
 
 def forward(qx, kx, v, mu, raw_var, prior_logits, eps: float = 1e-6, causal: bool = False, out=None, workspace=None):

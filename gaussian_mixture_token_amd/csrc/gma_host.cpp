@@ -1069,6 +1069,65 @@ gma_status_t decode(const gma_problem_t* p, const void* qx, const void* kx, cons
 }  // namespace
 }  // namespace gma
 
+// Workspace of gma_forward_causal_noalloc: a fixed device array, so that the call allocates nothing.
+// In host code `scratch` names a host-side stand-in, not device memory: its device address is taken
+// once per device with hipGetSymbolAddress (that device current) and only that address is used.
+static __device__ __align__(256) char scratch[GMA_NOALLOC_SCRATCH_BYTES];
+
+namespace gma {
+namespace {
+
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on the first call per device.
+gma_status_t scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GMA_ERROR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GMA_ERROR_NOT_SUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(GMA_ERROR_LAUNCH, "hipGetSymbolAddress of the scratch array failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GMA_SUCCESS;
+}
+
+// gma_forward_causal with the device's scratch array as its workspace: the workspace the causal pass
+// needs when the Gamma_K tiles are not stored (the larger of the two stagings, since pointer alignment
+// decides which runs) must fit the array; the pass stores the tiles only where they fit as well.
+gma_status_t forward_causal_noalloc(const gma_problem_t* p, const void* qx, const void* kx, const void* v,
+                                    const float* mu, const float* rv, const float* pr, void* o, void* stream) {
+    g_last_error.clear();
+    Plan pl, pt;
+    gma_status_t st = make_plan(p, GMA_OP_FORWARD_CAUSAL, &pl);
+    if (st != GMA_SUCCESS) return st;
+    for (const void* ptr : {qx, kx, v, (const void*)mu, (const void*)rv, (const void*)pr, (const void*)o})
+        if (!ptr) return fail(GMA_ERROR_INVALID_VALUE, "pointer arguments must not be NULL");
+    size_t need = pl.total;
+    if (pl.cls->tok_out_causal && make_plan(p, GMA_OP_FORWARD_CAUSAL, &pt, true, false) == GMA_SUCCESS)
+        need = std::max(need, pt.total);
+    if (need > (size_t)GMA_NOALLOC_SCRATCH_BYTES)
+        return fail(GMA_ERROR_WORKSPACE_TOO_SMALL,
+                    "the problem needs %zu bytes of workspace; the no-allocation entry point has %zu", need,
+                    (size_t)GMA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != GMA_SUCCESS) return st;
+    return forward(p, GMA_OP_FORWARD_CAUSAL, qx, kx, v, mu, rv, pr, nullptr, nullptr, o, ws,
+                   (size_t)GMA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+}  // namespace
+}  // namespace gma
+
 using namespace gma;
 
 extern "C" {
@@ -1178,6 +1237,12 @@ gma_status_t gma_forward_causal(const gma_problem_t* p, const void* qx, const vo
                                 void* stream) {
     return forward(p, GMA_OP_FORWARD_CAUSAL, qx, kx, v, mu, raw_var, prior_logits, nullptr, nullptr, o, ws, ws_bytes,
                    stream);
+}
+
+gma_status_t gma_forward_causal_noalloc(const gma_problem_t* p, const void* qx, const void* kx, const void* v,
+                                        const float* mu, const float* raw_var, const float* prior_logits, void* o,
+                                        void* stream) {
+    return forward_causal_noalloc(p, qx, kx, v, mu, raw_var, prior_logits, o, stream);
 }
 
 gma_status_t gma_forward_bidir_kv(const gma_problem_t* p, int64_t seq_len_kv, const void* qx, const void* kx,

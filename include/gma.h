@@ -135,6 +135,27 @@ gma_status_t gma_forward_causal(const gma_problem_t* problem, const void* qx, co
                                 const float* prior_logits, void* o, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Causal forward that allocates nothing, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): gma_forward_causal with
+ * no workspace argument.  Its workspace is a fixed array of GMA_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held from the library's first use on that GPU until the process ends; its
+ * address on the current device is looked up on the first call there.  Results are those of
+ * gma_forward_causal given a workspace of GMA_NOALLOC_SCRATCH_BYTES bytes (the stored Gamma_K tiles
+ * are used only where they fit; otherwise Gamma_K is recomputed from K_X).
+ *   Limit   the workspace the causal pass needs without the stored tiles must fit the array: about
+ *           B H P (K_pad (d_v_pad + 1)) 4 + H K_pad (4 d_r_pad + 4) bytes with B H P >= 256, e.g.
+ *           17 MiB for K = d_r = d_v = 128.  Larger problems return GMA_ERROR_WORKSPACE_TOO_SMALL
+ *           (before any HIP call).
+ *   Races   every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ *           (on different streams, or from different threads without ordering) race and give wrong
+ *           results.  Calls ordered on one stream are safe.  The stream's device must be current.
+ *   No call of this entry point allocates or frees memory (hipMalloc, hipFree or any allocating
+ *   library routine).  Other arguments and errors as gma_forward_causal. */
+#define GMA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gma_status_t gma_forward_causal_noalloc(const gma_problem_t* problem, const void* qx, const void* kx,
+                                        const void* v, const float* mu, const float* raw_var,
+                                        const float* prior_logits, void* o, void* stream);
+
 /* Bidirectional forward with separate query and key/value sequences (cross-attention; the pages
  * name N_q != N_k as future work, and the write / read equations of item 2 apply unchanged):
  * qx [B, H, N_q, d_r] and o [B, H, N_q, d_v] with N_q = problem->seq_len; kx [B, H, N_kv, d_r] and
