@@ -155,8 +155,8 @@ def _forward_kv(qx, kx, v, mu, raw_var, prior_logits, eps, out, workspace):
     if out is None:
         out = torch.empty(B, H, Nq, d_v, dtype=qx.dtype, device=dev)
     _check_out(out, (B, H, Nq, d_v), qx.dtype, dev)
-    ws = _workspace(workspace_size(problem(B, H, Nk, d_r, K, d_v, qx.dtype, eps), _lib.GMA_OP_FORWARD_BIDIR), dev,
-                    workspace)
+    ws = _workspace(workspace_size(problem(B, H, max(Nq, Nk), d_r, K, d_v, qx.dtype, eps), _lib.GMA_OP_FORWARD_BIDIR),
+                    dev, workspace)
     _lib.check(_lib.load().gma_forward_bidir_kv(ctypes.byref(prob), Nk, _ptr(qx), _ptr(kx), _ptr(v), _ptr(mu),
                                                 _ptr(raw_var), _ptr(prior_logits), _ptr(out), _ptr(ws),
                                                 ws.numel() * ws.element_size(), _stream(dev)))

@@ -50,12 +50,15 @@ int next_pow2(int x) {
 
 enum KernelId {
     K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_STATS,
-    K_BWD_GAMMA, K_BWD_GEMM, K_BWD_ROWS, K_BWD_SCAN, K_BWD_PARAM, K_DECODE_PREP, K_COUNT
+    K_BWD_GAMMA, K_BWD_GEMM, K_BWD_ROWS, K_BWD_SCAN, K_BWD_PARAM, K_DECODE_PREP,
+    K_GEN_PREP, K_GEN_GAMMA, K_GEN_GEMM, K_GEN_SCAN, K_GEN_OUT, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan", "causal_output", "bidir_output",
                                      "responsibilities", "state_convert", "decode_step", "responsibility_stats",
                                      "backward_responsibilities", "backward_products", "backward_rows",
-                                     "backward_scan", "backward_parameters", "decode_prepare"};
+                                     "backward_scan", "backward_parameters", "decode_prepare",
+                                     "generic_prep", "generic_responsibilities", "generic_products",
+                                     "generic_scan", "generic_output"};
 
 struct Plan {
     const ShapeClass* cls = nullptr;
@@ -74,6 +77,14 @@ struct Plan {
     size_t off_ab = 0, off_c = 0, off_seg = 0, off_gk = 0, off_total = 0, off_state = 0, total = 0;
     int stat_segs = 0;                     // responsibility diagnostics: row segments per (batch, head)
     size_t off_gamma = 0, off_part = 0;
+    // Generic path (no compiled class covers the shape): fp32 responsibilities and products over
+    // materialised Gamma_Q, Gamma_K.  Rows of tokens in entries of gen_step (a causal chunk or a
+    // bidirectional segment); records [K, gen_dva] = [Vt | Z | 0 ..] per entry.
+    bool generic = false;
+    int gen_step = 0, gen_dva = 0;
+    int64_t gen_nst = 0, gen_rows = 0;
+    size_t off_gbf = 0, off_gcq = 0, off_gq = 0, off_ggk = 0, off_gpp = 0, off_gst = 0, off_gac = 0, off_grin = 0,
+           off_grout = 0;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -125,6 +136,58 @@ gma_status_t validate_problem(const gma_problem_t* p) {
     return GMA_SUCCESS;
 }
 
+constexpr int kBwdChunk = 64;    // causal chunk (tokens) of the backward and of the generic forward
+constexpr int kBwdSeg = 1024;    // bidirectional state segments and parameter-partial segments (tokens)
+
+// Generic plan for the shapes that no compiled class covers (d_r or d_v in (128, 256]): Gamma_Q and
+// Gamma_K in fp32 from the matrix-core responsibilities kernel of the backward (expanded
+// log-density, fp32 steps of 16 dims added in fp64), then the write and read phases as batched fp32
+// matrix-core products.  Workspace (256-byte aligned regions): coefficient fragments and constants;
+// for the forward Gamma_Q, Gamma_K [BH, N, K], [num | den] [BH, N, dva], the entry records
+// [BH, n_entries, K, dva], (causal) the intra-chunk blocks tril(Gamma_Q Gamma_K^T) [BH, n_chunks, 64, 64]
+// and (carried state) the initial and final records [BH, K, dva].
+gma_status_t make_generic_plan(const gma_problem_t* p, int op, Plan* plan) {
+    const bool causal = op == GMA_OP_FORWARD_CAUSAL || op == GMA_OP_FORWARD_CAUSAL_STATE;
+    const bool resp = op == GMA_OP_RESPONSIBILITIES || op == GMA_OP_RESPONSIBILITY_STATS;
+    const int64_t BH = plan->B * plan->H, N = plan->N;
+    const int K = plan->K;
+    plan->generic = true;
+    plan->gen_step = causal ? kBwdChunk : kBwdSeg;
+    plan->gen_nst = (N + plan->gen_step - 1) / plan->gen_step;
+    plan->gen_dva = (plan->d_v + 1 + 3) / 4 * 4;
+    plan->gen_rows = BH * N;
+    const int64_t rec = (int64_t)K * plan->gen_dva;
+    const int64_t widest = std::max<int64_t>(std::max<int64_t>(K, plan->gen_dva), plan->gen_step);
+    if (BH * plan->gen_nst * ((kBwdSeg + 63) / 64) * ((widest + 63) / 64) > INT32_MAX ||
+        plan->gen_rows / 4 + 1 > INT32_MAX || BH * ((rec + 255) / 256) > INT32_MAX)
+        return fail(GMA_ERROR_NOT_SUPPORTED, "problem too large for the generic path's grids");
+    size_t off = 0;
+    auto take = [&](size_t* o, int64_t floats) {
+        *o = off;
+        off = align_up(off + (size_t)floats * sizeof(float), 256);
+    };
+    const int KT = bwd_gamma_tiles(K);
+    take(&plan->off_gbf, plan->H * ((plan->d_r + 15) / 16) * 2 * KT * 256);
+    take(&plan->off_gcq, plan->H * 16 * KT * 2);   // fp64
+    if (!resp) {
+        take(&plan->off_gq, plan->gen_rows * K);
+        take(&plan->off_ggk, plan->gen_rows * K);
+        take(&plan->off_gpp, plan->gen_rows * plan->gen_dva);
+        take(&plan->off_gst, BH * plan->gen_nst * rec);
+        take(&plan->off_gac, causal ? BH * plan->gen_nst * kBwdChunk * kBwdChunk : 0);
+        take(&plan->off_grin, op == GMA_OP_FORWARD_CAUSAL_STATE ? BH * rec : 0);
+        take(&plan->off_grout, op == GMA_OP_FORWARD_CAUSAL_STATE ? BH * rec : 0);
+    }
+    plan->total = off;
+    if (op == GMA_OP_RESPONSIBILITY_STATS) {
+        plan->stat_segs = (int)std::max<int64_t>(1, std::min<int64_t>((1024 + BH - 1) / BH, (N + 63) / 64));
+        plan->off_gamma = plan->total;
+        plan->off_part = align_up(plan->off_gamma + (size_t)BH * N * K * sizeof(float), 256);
+        plan->total = align_up(plan->off_part + (size_t)BH * plan->stat_segs * K * 8, 256);
+    }
+    return GMA_SUCCESS;
+}
+
 gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = false, bool tiles = true) {
     if (!p) return fail(GMA_ERROR_INVALID_VALUE, "problem is NULL");
     if (op < GMA_OP_RESPONSIBILITIES || op > GMA_OP_RESPONSIBILITY_STATS)
@@ -148,9 +211,10 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     const int drc = std::max(plan->f32 ? 16 : 32, next_pow2(p->d_route));
     const bool resp = op == GMA_OP_RESPONSIBILITIES || op == GMA_OP_RESPONSIBILITY_STATS;
     plan->cls = find_class(plan->f32, kc, resp ? -1 : vc, drc);
-    if (!plan->cls)
-        return fail(GMA_ERROR_NOT_SUPPORTED, "no compiled kernel class for dtype=%s K=%d d_v=%d d_r=%d (padded %d/%d/%d)",
-                    plan->f32 ? "f32" : "bf16", p->n_comp, p->d_value, p->d_route, kc, vc, drc);
+    if (!plan->cls) {
+        if (tok) return fail(GMA_ERROR_NOT_SUPPORTED, "no token-split kernels for this shape");
+        return make_generic_plan(p, op, plan);
+    }
     if (tok && !plan->cls->tok_out_causal)
         return fail(GMA_ERROR_NOT_SUPPORTED, "no token-split kernels for this class");
     plan->dma = tok;
@@ -249,9 +313,6 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
 //   gp [2, BH, n_sg, K, dxa]                  per-segment dl^T [x | x^2 | 1] of both sides (dxa = 2 d_r + 1
 //                                             rounded up to a multiple of 4; the product generates the
 //                                             augmented rows from x)
-constexpr int kBwdChunk = 64;    // causal chunk (tokens)
-constexpr int kBwdSeg = 1024;    // bidirectional state segments and parameter-partial segments (tokens)
-
 struct BwdPlan {
     int64_t B = 0, H = 0, N = 0, BH = 0;
     int d_r = 0, K = 0, d_v = 0, dva = 0, dxa = 0;
@@ -327,7 +388,7 @@ size_t advertised_workspace(const gma_problem_t* problem, int op) {
     if (make_plan(problem, op, &pl) != GMA_SUCCESS) return 0;
     size_t total = pl.total;
     Plan pt;
-    if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_RESPONSIBILITY_STATS && pl.cls->tok_out_causal &&
+    if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_RESPONSIBILITY_STATS && !pl.generic && pl.cls->tok_out_causal &&
         make_plan(problem, op, &pt, true) == GMA_SUCCESS)
         total = std::max(total, pt.total);
     return total;
@@ -580,6 +641,138 @@ gma_status_t check_common(const gma_problem_t* p, const void* const* ptrs, int n
     return GMA_SUCCESS;
 }
 
+// ---------------------------------------------------------------------------------- generic path
+// Carried state [B*H, K, d_v + 1] <-> generic record [B*H, K, dva] (row k: Vt[k, :], Z[k], zeros).
+__global__ void __launch_bounds__(256) state_to_genrec(const float* state, float* recs, int K, int dv, int dva) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)K * dva) return;
+    const int k = (int)(e / dva), j = (int)(e % dva);
+    recs[(int64_t)blockIdx.y * K * dva + e] = j <= dv ? state[((int64_t)blockIdx.y * K + k) * (dv + 1) + j] : 0.f;
+}
+
+__global__ void __launch_bounds__(256) genrec_to_state(const float* recs, float* state, int K, int dv, int dva) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)K * (dv + 1)) return;
+    const int k = (int)(e / (dv + 1)), j = (int)(e % (dv + 1));
+    state[(int64_t)blockIdx.y * K * (dv + 1) + e] = recs[((int64_t)blockIdx.y * K + k) * dva + j];
+}
+
+// O = num / (den + eps) per row from p [rows, dva] = [num | den | 0 ..], in the storage dtype.
+__global__ void __launch_bounds__(256) generic_out_kernel(const float* p, void* o, int64_t rows, int dv, int dva,
+                                                          float eps, int f32) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= rows * dv) return;
+    const int64_t r = e / dv;
+    const int j = (int)(e % dv);
+    const float val = p[r * dva + j] / (p[r * dva + dv] + eps);
+    if (f32) reinterpret_cast<float*>(o)[e] = val;
+    else reinterpret_cast<uint16_t*>(o)[e] = bf16_bits(val);
+}
+
+// Responsibilities of x [BH, N, d_r] in fp32 on the generic path -> gamma [BH, N, K].
+gma_status_t generic_gamma(const Plan& pl, const void* x, const float* mu, const float* rv, const float* pr,
+                           float* gamma, int64_t N, char* w, hipStream_t s, bool prep) {
+    float* bf = reinterpret_cast<float*>(w + pl.off_gbf);
+    double* cq = reinterpret_cast<double*>(w + pl.off_gcq);
+    if (prep) {
+        const gma_status_t st = timed_launch(K_GEN_PREP, s, [&] {
+            launch_bwd_frag(mu, rv, pr, bf, cq, (int)pl.H, pl.K, pl.d_r, s);
+        });
+        if (st != GMA_SUCCESS) return st;
+    }
+    return timed_launch(K_GEN_GAMMA, s, [&] {
+        launch_bwd_gamma_mfma(x, pl.f32, bf, cq, gamma, pl.B * pl.H, N, (int)pl.H, pl.K, pl.d_r, s);
+    });
+}
+
+// Forward on the generic path (the plan from make_generic_plan; n_q query rows, n_kv key / value rows,
+// equal when causal).  Write phase: records Gamma_K^T [V | 1] per entry (a 64-token chunk when causal, a
+// 1024-token segment otherwise), then the fixed-order scan of the forward (exclusive prefix from the
+// initial state when causal, the total into entry 0 otherwise).  Read phase: [num | den] = Gamma_Q
+// times the record each entry reads, plus (causal) tril(Gamma_Q Gamma_K^T) [V | 1] within the chunk;
+// O = num / (den + eps).
+gma_status_t forward_generic(const Plan& pl, bool causal, int64_t n_q, int64_t n_kv, const void* qx, const void* kx,
+                             const void* v, const float* mu, const float* rv, const float* pr, const float* state_in,
+                             float* state_out, void* o, char* w, hipStream_t s) {
+    const int64_t BH = pl.B * pl.H;
+    const int K = pl.K, d_v = pl.d_v, dva = pl.gen_dva, step = pl.gen_step;
+    const int64_t rec = (int64_t)K * dva;
+    const int64_t nst_k = (n_kv + step - 1) / step, nst_q = (n_q + step - 1) / step;
+    auto F = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+    float *gq = F(pl.off_gq), *gk = F(pl.off_ggk), *pp = F(pl.off_gpp), *st = F(pl.off_gst), *ac = F(pl.off_gac);
+    float* rin = state_in ? F(pl.off_grin) : nullptr;
+    float* rout = state_out ? F(pl.off_grout) : nullptr;
+    gma_status_t r = generic_gamma(pl, qx, mu, rv, pr, gq, n_q, w, s, true);
+    if (r != GMA_SUCCESS) return r;
+    r = generic_gamma(pl, kx, mu, rv, pr, gk, n_kv, w, s, false);
+    if (r != GMA_SUCCESS) return r;
+    struct View { const float* p; int64_t s0, s1; int ld; };
+    auto gemm = [&](View A, bool ta, View B, bool tb, View C, float* out, int M, int Nn, int Kd, int tokf, int tril,
+                    const float* cin, int64_t ntok, int64_t n_inner, BwdGen gb) -> gma_status_t {
+        BwdGemm g;
+        g.gb = gb;
+        g.A = A.p; g.sA0 = A.s0; g.sA1 = A.s1; g.lda = A.ld;
+        g.B = B.p; g.sB0 = B.s0; g.sB1 = B.s1; g.ldb = B.ld;
+        g.C = out; g.sC0 = C.s0; g.sC1 = C.s1; g.ldc = C.ld;
+        g.Cin = cin;
+        g.beta = cin ? 1.f : 0.f;
+        g.M = M; g.N = Nn; g.Kd = Kd;
+        g.n_outer = BH;
+        g.n_inner = (int)n_inner;
+        g.ntok = ntok;
+        g.tok_step = step;
+        g.tok_flags = tokf;
+        g.tril = tril;
+        bool ok = true;
+        const gma_status_t ls = timed_launch(K_GEN_GEMM, s, [&] { ok = launch_bwd_gemm(g, ta, tb, false, s); });
+        if (!ok) return fail(GMA_ERROR_LAUNCH, "no product kernel for this operand combination");
+        return ls;
+    };
+    constexpr int TM = 1, TN = 2, TK = 4;   // token axes of a product
+    const BwdGen gen_v{v, nullptr, GEN_VAUG, pl.f32 ? 1 : 0, d_v};
+    const View v_rows{nullptr, n_kv, step, 1};   // [V | 1] generated from V (views count rows)
+    // write phase
+    r = gemm(View{gk, n_kv * K, (int64_t)step * K, K}, true, v_rows, false, View{st, nst_k * rec, rec, dva}, st, K, dva,
+             step, TK, 0, nullptr, n_kv, nst_k, gen_v);
+    if (r != GMA_SUCCESS) return r;
+    if (rin) {
+        r = timed_launch(K_STATE, s, [&] {
+            hipLaunchKernelGGL(state_to_genrec, dim3((unsigned)((rec + 255) / 256), (unsigned)BH), dim3(256), 0, s,
+                               state_in, rin, K, d_v, dva);
+        });
+        if (r != GMA_SUCCESS) return r;
+    }
+    r = timed_launch(K_GEN_SCAN, s, [&] {
+        hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), (unsigned)BH), dim3(256), 0, s, st,
+                           (int)nst_k, (int)nst_k, 0, rec, causal ? 1 : 0, (int)nst_k, (const float*)rin, rout);
+    });
+    if (r != GMA_SUCCESS) return r;
+    // read phase
+    r = gemm(View{gq, n_q * K, (int64_t)step * K, K}, false, View{st, nst_k * rec, causal ? rec : 0, dva}, false,
+             View{pp, n_q * dva, (int64_t)step * dva, dva}, pp, step, dva, K, TM, 0, nullptr, n_q, nst_q, BwdGen{});
+    if (r != GMA_SUCCESS) return r;
+    if (causal) {
+        const int64_t C = step;
+        r = gemm(View{gq, n_q * K, C * K, K}, false, View{gk, n_kv * K, C * K, K}, true,
+                 View{ac, nst_q * C * C, C * C, (int)C}, ac, (int)C, (int)C, K, TM | TN, 1, nullptr, n_q, nst_q, BwdGen{});
+        if (r != GMA_SUCCESS) return r;
+        r = gemm(View{ac, nst_q * C * C, C * C, (int)C}, false, v_rows, false, View{pp, n_q * dva, C * dva, dva}, pp,
+                 (int)C, dva, (int)C, TM | TK, 0, pp, n_q, nst_q, gen_v);
+        if (r != GMA_SUCCESS) return r;
+    }
+    const int64_t n_out = BH * n_q * d_v;
+    r = timed_launch(K_GEN_OUT, s, [&] {
+        hipLaunchKernelGGL(generic_out_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, (const float*)pp, o,
+                           BH * n_q, d_v, dva, pl.eps, pl.f32 ? 1 : 0);
+    });
+    if (r != GMA_SUCCESS || !rout) return r;
+    const int64_t nstate = (int64_t)K * (d_v + 1);
+    return timed_launch(K_STATE, s, [&] {
+        hipLaunchKernelGGL(genrec_to_state, dim3((unsigned)((nstate + 255) / 256), (unsigned)BH), dim3(256), 0, s,
+                           (const float*)rout, state_out, K, d_v, dva);
+    });
+}
+
 // op: GMA_OP_FORWARD_BIDIR, GMA_OP_FORWARD_CAUSAL or GMA_OP_FORWARD_CAUSAL_STATE (state_in /
 // state_out used only by the last; either may be NULL)
 gma_status_t forward(const gma_problem_t* p, int op, const void* qx, const void* kx, const void* v,
@@ -616,6 +809,19 @@ gma_status_t forward(const gma_problem_t* p, int op, const void* qx, const void*
             return fail(GMA_ERROR_INVALID_VALUE, "state_in and state_out must be the same buffer or disjoint");
     }
 
+    if (pl.generic) {
+        if (ws_bytes < pl.total)
+            return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                        ws_bytes, pl.total);
+        if (overlaps(ws, pl.total, qx, nx) || overlaps(ws, pl.total, kx, nx) || overlaps(ws, pl.total, v, nv) ||
+            overlaps(ws, pl.total, o, nv) ||
+            (stateful && (overlaps(ws, pl.total, state_in, state_in ? ns : 0) ||
+                          overlaps(ws, pl.total, state_out, state_out ? ns : 0))))
+            return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
+        return forward_generic(pl, causal, pl.N, pl.N, qx, kx, v, mu, rv, pr, stateful ? state_in : nullptr,
+                               stateful ? state_out : nullptr, o, reinterpret_cast<char*>(ws),
+                               reinterpret_cast<hipStream_t>(stream));
+    }
     // Token-split LDS-DMA kernels: bf16, rows in whole 16-byte chunks, 16-byte aligned bases, byte
     // offsets within one (batch, head) slice (one chunk past the end included) below 2^31.
     const bool dma = !pl.f32 && pl.cls->tok_out_causal && pl.d_r % 8 == 0 && pl.d_v % 8 == 0 &&
@@ -758,6 +964,22 @@ gma_status_t forward_bidir_kv(const gma_problem_t* p, int64_t n_kv, const void* 
     const size_t nv = (size_t)(BH * n_kv) * plq.d_v * es, no = (size_t)(BH * plq.N) * plq.d_v * es;
     if (overlaps(o, no, qx, nq) || overlaps(o, no, kx, nk) || overlaps(o, no, v, nv))
         return fail(GMA_ERROR_INVALID_VALUE, "o must not overlap qx, kx or v");
+    if (plk.generic) {
+        // one plan for both sides: its row buffers hold max(N_q, N_kv) rows per (batch, head)
+        Plan pg;
+        gma_problem_t pm = *p;
+        pm.seq_len = std::max(plq.N, n_kv);
+        st = make_plan(&pm, GMA_OP_FORWARD_BIDIR, &pg);
+        if (st != GMA_SUCCESS) return st;
+        if (ws_bytes < pg.total)
+            return fail(GMA_ERROR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                        ws_bytes, pg.total);
+        if (overlaps(ws, pg.total, qx, nq) || overlaps(ws, pg.total, kx, nk) || overlaps(ws, pg.total, v, nv) ||
+            overlaps(ws, pg.total, o, no))
+            return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
+        return forward_generic(pg, false, plq.N, n_kv, qx, kx, v, mu, rv, pr, nullptr, nullptr, o,
+                               reinterpret_cast<char*>(ws), reinterpret_cast<hipStream_t>(stream));
+    }
     const bool dma = !plq.f32 && plq.cls->tok_out_causal && plq.d_r % 8 == 0 && plq.d_v % 8 == 0 &&
                      !misaligned(qx, 16) && !misaligned(kx, 16) && !misaligned(v, 16) && !misaligned(o, 16) &&
                      (std::max(plq.N, n_kv) + kTokChunk) * std::max(plq.d_r, plq.d_v) * 2 < (int64_t(1) << 31);
@@ -1112,7 +1334,7 @@ gma_status_t forward_causal_noalloc(const gma_problem_t* p, const void* qx, cons
     for (const void* ptr : {qx, kx, v, (const void*)mu, (const void*)rv, (const void*)pr, (const void*)o})
         if (!ptr) return fail(GMA_ERROR_INVALID_VALUE, "pointer arguments must not be NULL");
     size_t need = pl.total;
-    if (pl.cls->tok_out_causal && make_plan(p, GMA_OP_FORWARD_CAUSAL, &pt, true, false) == GMA_SUCCESS)
+    if (!pl.generic && pl.cls->tok_out_causal && make_plan(p, GMA_OP_FORWARD_CAUSAL, &pt, true, false) == GMA_SUCCESS)
         need = std::max(need, pt.total);
     if (need > (size_t)GMA_NOALLOC_SCRATCH_BYTES)
         return fail(GMA_ERROR_WORKSPACE_TOO_SMALL,
@@ -1158,6 +1380,7 @@ gma_status_t gma_responsibilities(const gma_problem_t* p, const void* x, const f
         return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap the tensors");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* w = reinterpret_cast<char*>(ws);
+    if (pl.generic) return generic_gamma(pl, x, mu, raw_var, prior_logits, gamma, pl.N, w, s, true);
     st = launch_prep(pl, mu, raw_var, prior_logits, w, s);
     if (st != GMA_SUCCESS) return st;
     MainArgs a = base_args(pl, w);
@@ -1198,25 +1421,31 @@ gma_status_t gma_responsibility_stats(const gma_problem_t* p, const void* x, con
     if (ws && overlaps(ws, pl.total, x, nx)) return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap x");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* w = reinterpret_cast<char*>(ws);
-    st = launch_prep(pl, mu, raw_var, prior_logits, w, s);
-    if (st != GMA_SUCCESS) return st;
     // Gamma of every row into the workspace (the responsibilities kernels), then the reductions
-    MainArgs a = base_args(pl, w);
-    a.qx = x;
-    a.gamma = reinterpret_cast<float*>(w + pl.off_gamma);
-    a.vec_x = vec_ok(x, pl.d_r, pl.f32);
-    const bool dma = !pl.f32 && pl.cls->dma_resp && pl.d_r % 8 == 0 && !misaligned(x, 16) &&
-                     (pl.N + pl.cls->c) * pl.d_r * 2 < (int64_t(1) << 31);
-    const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
-    st = timed_launch(K_RESP, s, [&] { f_resp(a, (int)(BH * pl.P), s); });
-    if (st != GMA_SUCCESS) return st;
+    float* gam = reinterpret_cast<float*>(w + pl.off_gamma);
+    if (pl.generic) {
+        st = generic_gamma(pl, x, mu, raw_var, prior_logits, gam, pl.N, w, s, true);
+        if (st != GMA_SUCCESS) return st;
+    } else {
+        st = launch_prep(pl, mu, raw_var, prior_logits, w, s);
+        if (st != GMA_SUCCESS) return st;
+        MainArgs a = base_args(pl, w);
+        a.qx = x;
+        a.gamma = gam;
+        a.vec_x = vec_ok(x, pl.d_r, pl.f32);
+        const bool dma = !pl.f32 && pl.cls->dma_resp && pl.d_r % 8 == 0 && !misaligned(x, 16) &&
+                         (pl.N + pl.cls->c) * pl.d_r * 2 < (int64_t(1) << 31);
+        const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
+        st = timed_launch(K_RESP, s, [&] { f_resp(a, (int)(BH * pl.P), s); });
+        if (st != GMA_SUCCESS) return st;
+    }
     float* pu = reinterpret_cast<float*>(w + pl.off_part);
     uint32_t* pc = reinterpret_cast<uint32_t*>(pu + (size_t)BH * pl.stat_segs * pl.K);
     const int S = pl.stat_segs;
     const int64_t rps = (pl.N + S - 1) / S;
     st = timed_launch(K_STATS, s, [&] {
         hipLaunchKernelGGL(stats_partial_kernel, dim3((unsigned)S, (unsigned)BH), dim3(256), 0, s,
-                           (const float*)a.gamma, pu, pc, pl.N, pl.K, S, rps);
+                           (const float*)gam, pu, pc, pl.N, pl.K, S, rps);
     });
     if (st != GMA_SUCCESS) return st;
     return timed_launch(K_STATS, s, [&] {

@@ -38,8 +38,12 @@
  *              tile class (K, d_v, d_r): bf16 (32, 64, 64), (128, 128, 128), (256, 64, 64),
  *              (256, 128, 128); fp32 (16, 16, 16), (64, 64, 64), (128, 128, 128).  The cheapest class
  *              that covers the shape runs it (padding components get zero responsibility, padding
- *              dims zero coefficients); a shape that no class covers (d_r or d_v > 128) returns
- *              GMA_ERROR_NOT_SUPPORTED.  gma_decode_step and the backward have no classes.
+ *              dims zero coefficients).  A shape that no class covers (d_r or d_v in (128, 256])
+ *              runs on the generic path: Gamma_Q and Gamma_K materialised in fp32 in the workspace
+ *              (logits on the fp32 matrix cores, each 16-dim step added in fp64), and the write and
+ *              read phases as fp32 matrix-core products (causal: 64-token chunks); slower, with a
+ *              workspace of about B H N (2 K + d_v + 1) 4 bytes (+ B H N 64 4 when causal).
+ *              gma_decode_step and the backward have no classes.
  *   Results    deterministic: repeated calls give bitwise identical outputs (no atomics; every
  *              reduction runs in a fixed order independent of the device).
  *   Environment GMA_CAUSAL_ROUNDS=R (measurement only; default 1): the bf16 causal pass launches its
@@ -160,7 +164,8 @@ gma_status_t gma_forward_causal_noalloc(const gma_problem_t* problem, const void
  * name N_q != N_k as future work, and the write / read equations of item 2 apply unchanged):
  * qx [B, H, N_q, d_r] and o [B, H, N_q, d_v] with N_q = problem->seq_len; kx [B, H, N_kv, d_r] and
  * v [B, H, N_kv, d_v] with N_kv = seq_len_kv >= 1.  Workspace: gma_workspace_size() of the same
- * problem with seq_len = seq_len_kv and op GMA_OP_FORWARD_BIDIR.  Otherwise as gma_forward_bidir. */
+ * problem with seq_len = max(N_q, N_kv) and op GMA_OP_FORWARD_BIDIR (the compiled classes need only
+ * that of seq_len = N_kv; the generic path holds rows of both sides).  Otherwise as gma_forward_bidir. */
 gma_status_t gma_forward_bidir_kv(const gma_problem_t* problem, int64_t seq_len_kv, const void* qx,
                                   const void* kx, const void* v, const float* mu, const float* raw_var,
                                   const float* prior_logits, void* o, void* workspace,

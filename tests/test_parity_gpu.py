@@ -209,6 +209,73 @@ def test_shapes_served_by_a_larger_class(gma, cfg, shape, causal):
     assert err <= TOL[w.dtype]
 
 
+# --------------------------------------------------------------- wide dims (the generic path)
+# (d_r, K, d_v) with d_r or d_v in (128, 256] match no compiled class and run on the generic path:
+# Gamma_Q, Gamma_K materialised in fp32, write and read phases as fp32 matrix-core products.
+
+
+@pytest.mark.parametrize("cfg,shape,N", [
+    (3, (256, 128, 256), 700), (3, (200, 64, 160), 1100), (3, (129, 256, 129), 300), (3, (256, 256, 8), 200),
+    (3, (8, 16, 256), 400), (1, (256, 128, 256), 700), (1, (200, 64, 160), 1100), (1, (130, 7, 250), 129),
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_dims_generic_path(gma, cfg, shape, N, causal):
+    w = gma.workload(cfg, batch=2, heads=2, seq_len=N, d_route=shape[0], n_comp=shape[1], d_value=shape[2])
+    say("generic path %s causal=%s %s" % (shape, causal, w))
+    inp = gma.make_inputs(w)
+    err = rel_err(gpu_forward(gma, w, inp, causal), ref_forward(w, inp, causal))
+    say("  rel err %.3e" % err)
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 1023, 1024, 1025])
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_dims_ragged_lengths(gma, N, causal):
+    w = gma.workload(3, batch=1, heads=2, seq_len=N, d_route=200, n_comp=64, d_value=160)
+    inp = gma.make_inputs(w)
+    err = rel_err(gpu_forward(gma, w, inp, causal), ref_forward(w, inp, causal))
+    assert err <= TOL[w.dtype], err
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_wide_dims_responsibilities_state_and_cross(gma, cfg):
+    w = gma.workload(cfg, batch=1, heads=2, seq_len=1500, d_route=256, n_comp=128, d_value=256)
+    say("generic path extras cfg %d" % cfg)
+    inp = gma.make_inputs(w)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    # responsibilities
+    g = gma.responsibilities(t["qx"], t["mu"], t["raw_var"], t["prior_logits"])
+    torch.cuda.synchronize()
+    ref = oracle.responsibilities(inp["qx"], inp["mu"], inp["raw_var"], inp["prior_logits"])
+    gerr = float(np.abs(g.cpu().numpy().astype(np.float64) - ref).max())
+    say("  max |dGamma| %.3e" % gerr)
+    assert gerr <= TOL_GAMMA[w.dtype]
+    # carried state: the oracle's state after 500 tokens, the GPU continues
+    m = 500
+    o_ref, s_ref = oracle.forward_causal_state(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"],
+                                               inp["prior_logits"], eps=w.eps)
+    _, s_m = oracle.forward_causal_state(inp["qx"][:, :, :m], inp["kx"][:, :, :m], inp["v"][:, :, :m], inp["mu"],
+                                         inp["raw_var"], inp["prior_logits"], eps=w.eps)
+    tail = {k: t[k][:, :, m:].contiguous() for k in ("qx", "kx", "v")}
+    s_io = torch.from_numpy(s_m).float().to(DEV)
+    o = gma.forward_causal(tail["qx"], tail["kx"], tail["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps,
+                           state_in=s_io, state_out=s_io)
+    torch.cuda.synchronize()
+    err_o, err_s = _rel(o, o_ref[:, :, m:]), _rel(s_io, s_ref)
+    say("  state: O err %.2e, state err %.2e" % (err_o, err_s))
+    assert err_o <= TOL[w.dtype] and err_s <= TOL[w.dtype], (err_o, err_s)
+    # cross-attention, both orders of the lengths
+    for nq, nk in ((300, 1500), (1500, 300)):
+        ref = oracle.forward_bidir_kv(inp["qx"][:, :, :nq], inp["kx"][:, :, :nk], inp["v"][:, :, :nk], inp["mu"],
+                                      inp["raw_var"], inp["prior_logits"], eps=w.eps)
+        o = gma.forward_bidir(t["qx"][:, :, :nq].contiguous(), t["kx"][:, :, :nk].contiguous(),
+                              t["v"][:, :, :nk].contiguous(), t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps)
+        torch.cuda.synchronize()
+        err = rel_err(o, ref)
+        say("  cross N_q %d N_kv %d: rel err %.3e" % (nq, nk, err))
+        assert err <= TOL[w.dtype], err
+
+
 @pytest.mark.parametrize("cfg,N", [(3, 5000), (4, 3001), (2, 2000)])
 def test_causal_without_room_for_stored_tiles(gma, cfg, N):
     # less than the advertised workspace: no stored Gamma_K tiles, the causal output pass recomputes
@@ -225,14 +292,18 @@ def test_causal_without_room_for_stored_tiles(gma, cfg, N):
 # ------------------------------------------------------------------------------ diagnostics
 
 
-@pytest.mark.parametrize("cfg,B,H,N", [(3, 1, 3, 7000), (4, 1, 2, 5000), (2, 2, 2, 3000), (1, 2, 2, 2000), (0, 1, 1, 256)])
-def test_responsibility_stats_match_the_oracle(gma, cfg, B, H, N):
+@pytest.mark.parametrize("cfg,B,H,N,d_r", [(3, 1, 3, 7000, None), (4, 1, 2, 5000, None), (2, 2, 2, 3000, None),
+                                           (1, 2, 2, 2000, None), (0, 1, 1, 256, None), (3, 1, 2, 3000, 256),
+                                           (1, 1, 2, 1000, 200)])
+def test_responsibility_stats_match_the_oracle(gma, cfg, B, H, N, d_r):
     # usage within twice the Gamma tolerance times sqrt(N) (the row errors do not share one sign), and
     # summing to N over the components to fp32 rounding (a dropped or repeated row moves it by 1);
     # entropy within twice the Gamma tolerance; hard counts exactly, except that rows whose two largest
     # responsibilities (oracle) are closer than twice that tolerance may go either way
     w = gma.workload(cfg, batch=B, heads=H, seq_len=N)
-    say("stats cfg %d B%d H%d N%d" % (cfg, B, H, N))
+    if d_r:
+        w = w.with_(d_route=d_r)
+    say("stats cfg %d B%d H%d N%d d_r %d" % (cfg, B, H, N, w.d_route))
     inp = gma.make_inputs(w)
     u_ref, h_ref, e_ref, gap = oracle.responsibility_stats(inp["qx"], inp["mu"], inp["raw_var"], inp["prior_logits"])
     t = {k: v.to(DEV) for k, v in inp.items()}
