@@ -15,6 +15,7 @@
 #include "gma.h"
 #include "gma_backward.hpp"
 #include "gma_decode.hpp"
+#include "gma_fixup.hpp"
 #include "gma_registry.hpp"
 
 namespace gma {
@@ -51,14 +52,14 @@ int next_pow2(int x) {
 enum KernelId {
     K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_STATS,
     K_BWD_GAMMA, K_BWD_GEMM, K_BWD_ROWS, K_BWD_SCAN, K_BWD_PARAM, K_DECODE_PREP,
-    K_GEN_PREP, K_GEN_GAMMA, K_GEN_GEMM, K_GEN_SCAN, K_GEN_OUT, K_COUNT
+    K_GEN_PREP, K_GEN_GAMMA, K_GEN_GEMM, K_GEN_SCAN, K_GEN_OUT, K_FIXUP, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan", "causal_output", "bidir_output",
                                      "responsibilities", "state_convert", "decode_step", "responsibility_stats",
                                      "backward_responsibilities", "backward_products", "backward_rows",
                                      "backward_scan", "backward_parameters", "decode_prepare",
                                      "generic_prep", "generic_responsibilities", "generic_products",
-                                     "generic_scan", "generic_output"};
+                                     "generic_scan", "generic_output", "out_of_range_fixup"};
 
 struct Plan {
     const ShapeClass* cls = nullptr;
@@ -75,6 +76,9 @@ struct Plan {
     int P_round = 1;       // segments per (batch, head) in one round (P = rounds * P_round)
     int64_t gk_ring = 0;   // Gamma_K tile slots per (batch, head) (one round's chunks; 0: n_chunks)
     size_t off_ab = 0, off_c = 0, off_seg = 0, off_gk = 0, off_total = 0, off_state = 0, total = 0;
+    // bf16 classes: the out-of-range flags [BH] and the exact recomputation's mixture scratch
+    size_t off_flags = 0, off_fix = 0;
+    bool flags = false;
     int stat_segs = 0;                     // responsibility diagnostics: row segments per (batch, head)
     size_t off_gamma = 0, off_part = 0;
     // Generic path (no compiled class covers the shape): fp32 responsibilities and products over
@@ -289,6 +293,12 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     plan->off_total = align_up(plan->off_gk + gk_bytes, 256);
     plan->off_state = align_up(plan->off_total + total_bytes, 256);
     plan->total = align_up(plan->off_state + state_bytes, 256);
+    plan->flags = !plan->f32;
+    if (plan->flags) {
+        plan->off_flags = plan->total;
+        plan->off_fix = align_up(plan->off_flags + (size_t)BH * sizeof(int), 256);
+        plan->total = align_up(plan->off_fix + fixup_scratch_bytes((int)plan->H, plan->K, plan->d_r), 256);
+    }
     if (op == GMA_OP_RESPONSIBILITY_STATS) {
         // Gamma of every row, then per-segment partial usages and counts
         plan->stat_segs = (int)std::max<int64_t>(1, std::min<int64_t>((1024 + BH - 1) / BH, (plan->N + 63) / 64));
@@ -596,6 +606,8 @@ gma_status_t launch_prep(const Plan& pl, const float* mu, const float* rv, const
     pa.H = (int)pl.H;
     pa.K = pl.K;
     pa.d_r = pl.d_r;
+    pa.flags = pl.flags ? reinterpret_cast<int*>(ws + pl.off_flags) : nullptr;
+    pa.n_flags = pl.B * pl.H;
     return timed_launch(K_PREP, s, [&] { pl.cls->prep(pa, (int)pl.H, s); });
 }
 
@@ -615,7 +627,36 @@ MainArgs base_args(const Plan& pl, char* ws) {
     a.K = pl.K;
     a.seg_chunks = pl.seg_chunks;
     a.eps = pl.eps;
+    a.flags = pl.flags ? reinterpret_cast<int*>(ws + pl.off_flags) : nullptr;
     return a;
+}
+
+// Exact recomputation of the (batch, head) slices a bf16 call flagged (rows whose logits left the
+// fp16 operand range); every other slice returns at once.
+FixArgs fix_args(const Plan& pl, char* ws) {
+    FixArgs f;
+    std::memset(&f, 0, sizeof(f));
+    f.flags = reinterpret_cast<const int*>(ws + pl.off_flags);
+    f.scratch = reinterpret_cast<float*>(ws + pl.off_fix);
+    f.N = pl.N;
+    f.N_kv = pl.N;
+    f.H = (int)pl.H;
+    f.K = pl.K;
+    f.d_r = pl.d_r;
+    f.d_v = pl.d_v;
+    f.eps = pl.eps;
+    return f;
+}
+
+gma_status_t launch_fixup(const Plan& pl, FixArgs f, bool forward, bool causal, hipStream_t s) {
+    bool ok = true;
+    const gma_status_t st = timed_launch(K_FIXUP, s, [&] {
+        ok = forward ? launch_fixup_forward(f, pl.cls->kc, pl.cls->vc, pl.B * pl.H, causal, s)
+                     : launch_fixup_resp(f, pl.cls->kc, pl.B * pl.H, s);
+    });
+    if (!ok) return fail(GMA_ERROR_LAUNCH, "no out-of-range recomputation kernel for class K=%d d_v=%d", pl.cls->kc,
+                         pl.cls->vc);
+    return st;
 }
 
 int vec_ok(const void* ptr, int d, bool f32) {
@@ -889,7 +930,17 @@ gma_status_t forward(const gma_problem_t* p, int op, const void* qx, const void*
             if (st != GMA_SUCCESS) return st;
         }
         a.bidir_segs = read_sum ? pl.P : 1;
-        return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, grid, s); });
+        st = timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, grid, s); });
+        if (st != GMA_SUCCESS || !pl.flags) return st;
+        FixArgs f = fix_args(pl, w);
+        f.qx = qx;
+        f.kx = kx;
+        f.v = v;
+        f.o = o;
+        f.mu = mu;
+        f.raw_var = rv;
+        f.prior = pr;
+        return launch_fixup(pl, f, true, false, s);
     }
     // Causal: rounds r = 0 .. rounds - 1, each over P_round consecutive segments of every (batch, head)
     // (one round when the plan has none): aggregate pass, exclusive prefix of the round's aggregates
@@ -927,12 +978,28 @@ gma_status_t forward(const gma_problem_t* p, int op, const void* qx, const void*
         st = timed_launch(K_OUT_CAUSAL, s, [&] { f_causal(ar, (int)(pl.B * pl.H * np), s); });
         if (st != GMA_SUCCESS) return st;
     }
-    if (st != GMA_SUCCESS || !rec_out) return st;
-    const int64_t nstate = (int64_t)pl.K * (pl.d_v + 1);
-    return timed_launch(K_STATE, s, [&] {
-        hipLaunchKernelGGL(record_to_state, dim3((unsigned)((nstate + 255) / 256), BH), dim3(256), 0, s,
-                           (const float*)rec_out, state_out, pl.K, pl.d_v, pl.cls->kc, pl.cls->vc, rec);
-    });
+    if (rec_out) {
+        const int64_t nstate = (int64_t)pl.K * (pl.d_v + 1);
+        st = timed_launch(K_STATE, s, [&] {
+            hipLaunchKernelGGL(record_to_state, dim3((unsigned)((nstate + 255) / 256), BH), dim3(256), 0, s,
+                               (const float*)rec_out, state_out, pl.K, pl.d_v, pl.cls->kc, pl.cls->vc, rec);
+        });
+        if (st != GMA_SUCCESS) return st;
+    }
+    if (!pl.flags) return GMA_SUCCESS;
+    // flagged slices are recomputed from the inputs (and the initial state's record, which no kernel
+    // above has written), after the final state was written, so they overwrite O and the state
+    FixArgs f = fix_args(pl, w);
+    f.qx = qx;
+    f.kx = kx;
+    f.v = v;
+    f.o = o;
+    f.mu = mu;
+    f.raw_var = rv;
+    f.prior = pr;
+    f.rec_in = rec_in;
+    f.state_out = rec_out ? state_out : nullptr;
+    return launch_fixup(pl, f, true, true, s);
 }
 
 // Bidirectional forward with N_q query rows (problem->seq_len) and N_kv key/value rows: the
@@ -1029,7 +1096,19 @@ gma_status_t forward_bidir_kv(const gma_problem_t* p, int64_t n_kv, const void* 
     a.vec_x = vec_ok(qx, plq.d_r, plq.f32);
     a.vec_o = vec_o_ok(o, plq.d_v, plq.f32);
     const main_launch_t f_bidir = dma ? plq.cls->tok_out_bidir : plq.cls->out_bidir;
-    return timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, (int)(BH * plq.P), s); });
+    st = timed_launch(K_OUT_BIDIR, s, [&] { f_bidir(a, (int)(BH * plq.P), s); });
+    if (st != GMA_SUCCESS || !plk.flags) return st;
+    FixArgs f = fix_args(plk, w);
+    f.N = plq.N;
+    f.N_kv = n_kv;
+    f.qx = qx;
+    f.kx = kx;
+    f.v = v;
+    f.o = o;
+    f.mu = mu;
+    f.raw_var = rv;
+    f.prior = pr;
+    return launch_fixup(plk, f, true, false, s);
 }
 
 // Backward (see gma_backward.hip for the formulas): all intermediates fp32 in the workspace.
@@ -1391,7 +1470,15 @@ gma_status_t gma_responsibilities(const gma_problem_t* p, const void* x, const f
                      (pl.N + pl.cls->c) * pl.d_r * 2 < (int64_t(1) << 31);
     const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
     const int grid = (int)(pl.B * pl.H * pl.P);
-    return timed_launch(K_RESP, s, [&] { f_resp(a, grid, s); });
+    st = timed_launch(K_RESP, s, [&] { f_resp(a, grid, s); });
+    if (st != GMA_SUCCESS || !pl.flags) return st;
+    FixArgs f = fix_args(pl, w);
+    f.qx = x;
+    f.gamma = gamma;
+    f.mu = mu;
+    f.raw_var = raw_var;
+    f.prior = prior_logits;
+    return launch_fixup(pl, f, false, false, s);
 }
 
 gma_status_t gma_responsibility_stats(const gma_problem_t* p, const void* x, const float* mu, const float* raw_var,
@@ -1438,6 +1525,16 @@ gma_status_t gma_responsibility_stats(const gma_problem_t* p, const void* x, con
         const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
         st = timed_launch(K_RESP, s, [&] { f_resp(a, (int)(BH * pl.P), s); });
         if (st != GMA_SUCCESS) return st;
+        if (pl.flags) {
+            FixArgs f = fix_args(pl, w);
+            f.qx = x;
+            f.gamma = gam;
+            f.mu = mu;
+            f.raw_var = raw_var;
+            f.prior = prior_logits;
+            st = launch_fixup(pl, f, false, false, s);
+            if (st != GMA_SUCCESS) return st;
+        }
     }
     float* pu = reinterpret_cast<float*>(w + pl.off_part);
     uint32_t* pc = reinterpret_cast<uint32_t*>(pu + (size_t)BH * pl.stat_segs * pl.K);

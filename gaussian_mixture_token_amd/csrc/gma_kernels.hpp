@@ -92,6 +92,8 @@ struct MainArgs {
     int64_t gk_ring;       // Gamma_K tiles kept per (batch, head): chunk ch lives in slot ch mod gk_ring
                            // (0: one slot per chunk).  A launch's segments lie in one ring window.
     int vec_x, vec_v, vec_o;  // 16-byte (x, v) / 4-element (o) vector access allowed (register staging)
+    int* flags;            // [BH] or null (bf16): set to 1 for a (batch, head) with a row whose logits are
+                           // not finite (a routing input or coefficient past the fp16 operand range)
     int has_carry;         // causal: load the carried state (P > 1)
     int bidir_segs;        // bidirectional read pass: segment records to sum in order (0 or 1: record 0
                            // already holds the total)
@@ -104,6 +106,8 @@ struct PrepArgs {
     const float* prior;     // [H, K]
     void* ab;               // out
     float* cvec;            // out [H, KC]
+    int* flags;             // out [n_flags] zeroed (null: none), for the out-of-range flags of the call
+    int64_t n_flags;
     int H, K, d_r;
 };
 
@@ -129,6 +133,12 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(const PrepArgs p) {
     const double LOG2E = 1.4426950408889634073599246810019;
     __shared__ double s_t[16][DRC];
     __shared__ double s_lse;
+    // clear the call's out-of-range flags (the kernels that follow set them)
+    if (p.flags) {
+        const int64_t nthr = (int64_t)gridDim.x * gridDim.y * kPrepThreads;
+        for (int64_t i = ((int64_t)blockIdx.x * gridDim.y + blockIdx.y) * kPrepThreads + tid; i < p.n_flags; i += nthr)
+            p.flags[i] = 0;
+    }
 
     // log-sum-exp of the prior logits of this head, by wave 0 (butterfly reductions, fixed order)
     if (tid < 64) {
@@ -517,6 +527,10 @@ main_kernel(const MainArgs a) {
     // byte offset of (row, column) in the bf16 Gamma_K tile
     auto gk_off = [&](int row, int col) -> int { return row * GKR + col * 2; };
 
+    // set on a lane that met a live row whose logits are not finite (bf16: a routing input or a
+    // coefficient past the fp16 operand range); the (batch, head) is flagged after the chunk loop
+    [[maybe_unused]] bool nonfin = false;
+
     // ---- one chunk; BUF selects the DMA staging buffer (compile-time, so the two buffers are
     // distinct LDS objects)
     auto body = [&](auto buf_tag, int64_t ch) {
@@ -648,6 +662,8 @@ main_kernel(const MainArgs a) {
                 const float sg = (lg < W) ? s_ms[which][lg < W ? lg : 0][tok][1] : 0.f;
                 const float M = group4_max(mg);
                 const float S = group4_sum(mg == -INFINITY ? 0.f : sg * fast_exp2(mg - M));
+                // a row maximum of -inf or NaN, or a NaN row sum (the maximum skips NaN logits)
+                if constexpr (!F32) nonfin |= (tok < rows_valid) && !(M > -INFINITY && S < INFINITY);
                 const bool live = mloc[tt] != -INFINITY && tok < rows_valid;
                 const float f = live ? fast_exp2(mloc[tt] - M) * fast_rcp(S) : 0.f;
 #pragma unroll
@@ -941,6 +957,9 @@ main_kernel(const MainArgs a) {
     for (int64_t ch = ch0; ch < ch1; ch += 2) {
         body(std::integral_constant<int, 0>{}, ch);
         if (ch + 1 < ch1) body(std::integral_constant<int, 1>{}, ch + 1);
+    }
+    if constexpr (!F32) {
+        if (nonfin && a.flags) a.flags[bh] = 1;
     }
 
     if constexpr (MODE == MODE_AGG) {

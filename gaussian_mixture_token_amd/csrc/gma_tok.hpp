@@ -466,6 +466,11 @@ tok_kernel(const MainArgs a) {
             }
         }
     };
+    // set on a lane that met a row whose logits are not finite (a routing input or a coefficient past
+    // the fp16 operand range): a row maximum of -inf or NaN, or (output passes) a denominator that is
+    // NaN or inf, which a NaN logit of the row or of any key it reads makes it (the maximum skips NaN).
+    // The (batch, head) is flagged after the chunk loop.  Rows past N have zero inputs and finite logits.
+    bool nonfin = false;
     // 2^(l - max_k l) in place (base-2 logits)
     auto exp_rows = [&](f32x4 (&acc)[NCT]) {
         float m = acc[0][0];
@@ -474,6 +479,7 @@ tok_kernel(const MainArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) m = fmaxf(m, acc[ct][i]);
         m = group4_max(m);
+        nonfin |= !(m > -INFINITY);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -581,7 +587,9 @@ tok_kernel(const MainArgs a) {
                     mma(oacc[vt], lds_ld<bf16x8>(LST + (vt * NKQ + kq) * 1024 + lane * 16), pq[kq]);
                 mma(dx, lds_ld<bf16x8>(LZX + kq * 1024 + lane * 16), pq[kq]);
             }
-            const float inv = fast_rcp(dx[0] + dx[1] + a.eps * dx[2]);
+            const float den = dx[0] + dx[1] + a.eps * dx[2];
+            nonfin |= !(den < INFINITY);   // NaN or inf: a logit of this row or a key's was not finite
+            const float inv = fast_rcp(den);
             if (d_v == VC) {
                 // rows through LDS: lane (r, g) puts d_v 16 vt + 4g .. +3 of row r, then lane l takes
                 // 16 bytes (chunk l % (VC / 8)) of row i (64 / (VC / 8)) + l / (VC / 8) per store
@@ -778,7 +786,11 @@ tok_kernel(const MainArgs a) {
                         return;
                     }
                     p -= NMAXP;
-                    if (p == 0) { mk = group4_max(mk); return; }
+                    if (p == 0) {
+                        mk = group4_max(mk);
+                        nonfin |= !(mk > -INFINITY);
+                        return;
+                    }
                     p -= 1;
                     if (p < NCT) {
 #pragma unroll
@@ -918,7 +930,9 @@ tok_kernel(const MainArgs a) {
                     sfr[t] = pack_pair(sacc[2 * t], sacc[2 * t + 1]);
                     mma(dacc, ones, sfr[t]);
                 }
-                inv = fast_rcp(dx[0] + dx[1] + a.eps * dx[2] + dacc[0]);
+                const float den = dx[0] + dx[1] + a.eps * dx[2] + dacc[0];
+                nonfin |= !(den < INFINITY);   // NaN or inf: a logit of this row or an earlier key's was not finite
+                inv = fast_rcp(den);
             } else {
                 if constexpr (ALL_VT) load_vstage(0, 0);
             }
@@ -1035,6 +1049,7 @@ tok_kernel(const MainArgs a) {
             if (ch + 1 < ch1) body(std::integral_constant<int, 1>{}, ch + 1);
         }
     }
+    if (nonfin && a.flags) a.flags[bh] = 1;
 
     if constexpr (AGG) {
 #pragma unroll

@@ -22,8 +22,12 @@
  *   Dtypes     GMA_DTYPE_F32: x, qx, kx, v and o are fp32; all arithmetic is fp32.
  *              GMA_DTYPE_BF16: x, qx, kx, v and o are bf16; logits use fp16 matrix-core
  *              operands, responsibilities / values / states use bf16 operands, every sum and
- *              the softmax accumulate in fp32.  Domain of the bf16 path: |x| < 256 (x^2 must
- *              fit fp16) and |mu| / sigma^2 < 40000.
+ *              the softmax accumulate in fp32.  A (batch, head) with a row whose fp16 logits
+ *              are not finite (|x| >= 256, so x^2 leaves fp16; sigma^2 < 1.1e-5 or |mu| / sigma^2
+ *              > 45000, so a coefficient does) is detected by the kernels and recomputed exactly
+ *              afterwards in the same call (log-density in its direct form in fp64, state in
+ *              fp32): correct for every finite bf16 input, but one workgroup per such slice walks
+ *              its tokens in order (milliseconds per 10^4 tokens).  fp32 storage: |x| < 1e19.
  *   Memory     every tensor pointer is a device pointer owned by the caller; the workspace is a
  *              caller-owned device buffer of at least gma_workspace_size() bytes, 16-byte
  *              aligned, whose contents need not be initialised and are clobbered.  The library

@@ -276,6 +276,110 @@ def test_wide_dims_responsibilities_state_and_cross(gma, cfg):
         assert err <= TOL[w.dtype], err
 
 
+# ------------------------------------------------- bf16 rows past the fp16 operand range
+# The bf16 path forms its logits on fp16 matrix-core operands: x^2 leaves the fp16 range at |x| >= 256,
+# and a coefficient -1/(2 sigma^2) at sigma^2 < 1.1e-5.  Such a (batch, head) is flagged by the kernels
+# and recomputed exactly (log-density in fp64); the other slices are untouched.
+
+
+def _plant_out_of_range(inp, head=1):
+    """A few routing rows of one head at |x| in [256, 4096] (values exact in bf16)."""
+    q, k = inp["qx"].clone(), inp["kx"].clone()
+    N = q.shape[2]
+    q[0, head, min(5, N - 1), 3] = 300.0
+    q[0, head, N // 2, :4] = -2048.0
+    k[0, head, min(17, N - 1), 0] = 4096.0
+    k[0, head, N - 1, 1:3] = 256.0
+    out = dict(inp)
+    out["qx"], out["kx"] = q, k
+    return out
+
+
+@pytest.mark.parametrize("cfg,K", [(3, None), (2, None), (4, None), (3, 256)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_out_of_range_rows_forward(gma, cfg, K, causal):
+    w = gma.workload(cfg, batch=1, heads=3, seq_len=1000)
+    if K:
+        w = w.with_(n_comp=K)
+    say("out-of-range rows %s causal=%s" % (w, causal))
+    clean = gma.make_inputs(w)
+    inp = _plant_out_of_range(clean)
+    o = gpu_forward(gma, w, inp, causal)
+    assert torch.isfinite(o.float()).all()
+    err = rel_err(o, ref_forward(w, inp, causal))
+    say("  rel err %.3e" % err)
+    assert err <= TOL[w.dtype], err
+    # the slices without such rows take the usual path, bitwise
+    o_clean = gpu_forward(gma, w, clean, causal)
+    assert torch.equal(o[:, 0], o_clean[:, 0]) and torch.equal(o[:, 2], o_clean[:, 2])
+
+
+def test_out_of_range_tiny_variance(gma):
+    # a component with sigma^2 = softplus(-12) ~ 6e-6: its fp16 coefficient -1/(2 sigma^2) overflows
+    w = gma.workload(3, batch=1, heads=2, seq_len=700)
+    inp = gma.make_inputs(w)
+    rv = inp["raw_var"].clone()
+    rv[1, 3, :] = -12.0
+    inp["raw_var"] = rv
+    for causal in (False, True):
+        err = rel_err(gpu_forward(gma, w, inp, causal), ref_forward(w, inp, causal))
+        say("tiny variance causal=%s rel err %.3e" % (causal, err))
+        assert err <= TOL[w.dtype], err
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    g = gma.responsibilities(t["qx"], t["mu"], t["raw_var"], t["prior_logits"])
+    torch.cuda.synchronize()
+    ref = oracle.responsibilities(inp["qx"], inp["mu"], inp["raw_var"], inp["prior_logits"])
+    assert float(np.abs(g.cpu().numpy().astype(np.float64) - ref).max()) <= TOL_GAMMA[w.dtype]
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_out_of_range_responsibilities_and_stats(gma, cfg):
+    w = gma.workload(cfg, batch=1, heads=3, seq_len=900)
+    inp = _plant_out_of_range(gma.make_inputs(w))
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    g = gma.responsibilities(t["qx"], t["mu"], t["raw_var"], t["prior_logits"])
+    u, hc, e = gma.responsibility_stats(t["qx"], t["mu"], t["raw_var"], t["prior_logits"])
+    torch.cuda.synchronize()
+    ref = oracle.responsibilities(inp["qx"], inp["mu"], inp["raw_var"], inp["prior_logits"])
+    gerr = float(np.abs(g.cpu().numpy().astype(np.float64) - ref).max())
+    say("out-of-range responsibilities cfg %d: max |dGamma| %.3e" % (cfg, gerr))
+    assert gerr <= TOL_GAMMA[w.dtype]
+    u_ref, h_ref, e_ref, gap = oracle.responsibility_stats(inp["qx"], inp["mu"], inp["raw_var"], inp["prior_logits"])
+    u = u.cpu().numpy().astype(np.float64)
+    assert np.abs(u - u_ref).max() <= 2 * TOL_GAMMA[w.dtype] * np.sqrt(w.seq_len)
+    np.testing.assert_allclose(e.cpu().numpy(), e_ref, atol=2 * TOL_GAMMA[w.dtype])
+    diff = np.abs(hc.cpu().numpy().astype(np.int64) - h_ref).sum(axis=-1)
+    assert (diff <= 2 * (gap < 2 * TOL_GAMMA[w.dtype]).sum(axis=-1)).all()
+
+
+def test_out_of_range_carried_state_and_cross_attention(gma):
+    w = gma.workload(3, batch=1, heads=3, seq_len=1200)
+    inp = _plant_out_of_range(gma.make_inputs(w))
+    m = 400
+    o_ref, s_ref = oracle.forward_causal_state(inp["qx"], inp["kx"], inp["v"], inp["mu"], inp["raw_var"],
+                                               inp["prior_logits"], eps=w.eps)
+    _, s_m = oracle.forward_causal_state(inp["qx"][:, :, :m], inp["kx"][:, :, :m], inp["v"][:, :, :m], inp["mu"],
+                                         inp["raw_var"], inp["prior_logits"], eps=w.eps)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    tail = {k: t[k][:, :, m:].contiguous() for k in ("qx", "kx", "v")}
+    s_io = torch.from_numpy(s_m).float().to(DEV)   # updated in place
+    o = gma.forward_causal(tail["qx"], tail["kx"], tail["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps,
+                           state_in=s_io, state_out=s_io)
+    torch.cuda.synchronize()
+    err_o, err_s = _rel(o, o_ref[:, :, m:]), _rel(s_io, s_ref)
+    say("out-of-range carried state: O err %.2e, state err %.2e" % (err_o, err_s))
+    assert err_o <= TOL[w.dtype] and err_s <= TOL[w.dtype], (err_o, err_s)
+    for nq, nk in ((300, 1200), (1200, 300)):
+        ref = oracle.forward_bidir_kv(inp["qx"][:, :, -nq:], inp["kx"][:, :, :nk], inp["v"][:, :, :nk], inp["mu"],
+                                      inp["raw_var"], inp["prior_logits"], eps=w.eps)
+        o = gma.forward_bidir(t["qx"][:, :, -nq:].contiguous(), t["kx"][:, :, :nk].contiguous(),
+                              t["v"][:, :, :nk].contiguous(), t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps)
+        torch.cuda.synchronize()
+        err = rel_err(o, ref)
+        say("out-of-range cross N_q %d N_kv %d: rel err %.3e" % (nq, nk, err))
+        assert err <= TOL[w.dtype], err
+
+
 @pytest.mark.parametrize("cfg,N", [(3, 5000), (4, 3001), (2, 2000)])
 def test_causal_without_room_for_stored_tiles(gma, cfg, N):
     # less than the advertised workspace: no stored Gamma_K tiles, the causal output pass recomputes
