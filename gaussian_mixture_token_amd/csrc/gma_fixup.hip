@@ -80,11 +80,11 @@ __device__ void fix_setup(const FixArgs& a, int h, float* mt, float* it, double 
     __syncthreads();
 }
 
-// Responsibilities of one row x (bf16, d_r elements) by one wave: lane l holds components l, l + 64,
-// ...; the result goes to out[k] (fp32, LDS or global).
+// Responsibilities of one row x (bf16, d_r elements) by one wave: lane l gets components l, l + 64, ...
+// in g[] (0 past K).
 template <int KC>
-__device__ void fix_row(const FixArgs& a, const void* x, int64_t row, const float* mt, const float* it,
-                        const double (&s_c)[KC], float* out) {
+__device__ void fix_row_vals(const FixArgs& a, const void* x, int64_t row, const float* mt, const float* it,
+                             const double (&s_c)[KC], double (&g)[(KC + 63) / 64]) {
     constexpr int NK = (KC + 63) / 64;
     const int lane = threadIdx.x & 63;
     const int K = a.K, dr = a.d_r;
@@ -118,9 +118,21 @@ __device__ void fix_row(const FixArgs& a, const void* x, int64_t row, const floa
     }
     s = fix_wave_sum(s);
 #pragma unroll
+    for (int u = 0; u < NK; ++u) g[u] = l[u] / s;
+}
+
+// The same, stored to out[k] (fp32, LDS or global).
+template <int KC>
+__device__ void fix_row(const FixArgs& a, const void* x, int64_t row, const float* mt, const float* it,
+                        const double (&s_c)[KC], float* out) {
+    constexpr int NK = (KC + 63) / 64;
+    const int lane = threadIdx.x & 63;
+    double g[NK];
+    fix_row_vals<KC>(a, x, row, mt, it, s_c, g);
+#pragma unroll
     for (int u = 0; u < NK; ++u) {
         const int k = lane + 64 * u;
-        if (k < K) out[k] = (float)(l[u] / s);
+        if (k < a.K) out[k] = (float)g[u];
     }
 }
 
@@ -138,6 +150,67 @@ __global__ void __launch_bounds__(kFixThreads) fixup_resp_kernel(const FixArgs a
     const int w = threadIdx.x >> 6;
     for (int64_t r = w; r < a.N; r += kFixWaves)
         fix_row<KC>(a, a.qx, bh * a.N + r, mt, it, s_c, a.gamma + (bh * a.N + r) * a.K);
+}
+
+// Diagnostics of a flagged (batch, head): usage and hard counts over all its rows, into segment 0 of the
+// partials (the other segments zeroed, so the fixed-order combine gives the totals).  Usage per lane in
+// fp64, the waves' sums added in wave order; counts in LDS (integer, order-free).
+template <int KC>
+__global__ void __launch_bounds__(kFixThreads) fixup_stats_kernel(const FixArgs a) {
+    constexpr int NK = (KC + 63) / 64;
+    const int64_t bh = blockIdx.x;
+    if (!a.flags[bh]) return;
+    const int h = (int)(bh % a.H);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int K = a.K;
+    __shared__ double s_c[KC];
+    __shared__ double s_red[4];
+    __shared__ double s_use[kFixWaves][KC];
+    __shared__ uint32_t s_cnt[KC];
+    float* mt = a.scratch + (int64_t)h * 2 * K * a.d_r;
+    float* it = mt + (int64_t)K * a.d_r;
+    for (int k = tid; k < KC; k += kFixThreads) s_cnt[k] = 0u;
+    fix_setup<KC>(a, h, mt, it, s_c, s_red);
+    double use[NK];
+#pragma unroll
+    for (int u = 0; u < NK; ++u) use[u] = 0.0;
+    for (int64_t r = w; r < a.N; r += kFixWaves) {
+        double g[NK];
+        fix_row_vals<KC>(a, a.qx, bh * a.N + r, mt, it, s_c, g);
+        double best = -1.0;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int u = 0; u < NK; ++u) {
+            use[u] += g[u];
+            if (lane + 64 * u < K && g[u] > best) {
+                best = g[u];
+                bi = lane + 64 * u;
+            }
+        }
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double ob = __shfl_xor(best, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (ob > best || (ob == best && oi < bi)) {
+                best = ob;
+                bi = oi;
+            }
+        }
+        if (lane == 0 && bi < K) atomicAdd(&s_cnt[bi], 1u);
+    }
+#pragma unroll
+    for (int u = 0; u < NK; ++u)
+        if (lane + 64 * u < KC) s_use[w][lane + 64 * u] = use[u];
+    __syncthreads();
+    for (int k = tid; k < K; k += kFixThreads) {
+        double u = 0.0;
+        for (int v = 0; v < kFixWaves; ++v) u += s_use[v][k];
+        for (int q = 0; q < a.stat_segs; ++q) {
+            const int64_t i = (bh * a.stat_segs + q) * K + k;
+            a.stat_usage[i] = q == 0 ? (float)u : 0.f;
+            a.stat_count[i] = q == 0 ? s_cnt[k] : 0u;
+        }
+    }
 }
 
 // Forward of a flagged (batch, head): T tokens per chunk (the LDS holds the state [KC][VC] fp32 and the
@@ -250,6 +323,14 @@ bool launch_fixup_forward(const FixArgs& a, int kc, int vc, int64_t BH, bool cau
     else if (kc == 128 && vc == 128) launch_fixup_forward_t<128, 128, 48>(a, BH, causal, s);
     else if (kc == 256 && vc == 64) launch_fixup_forward_t<256, 64, 32>(a, BH, causal, s);
     else if (kc == 256 && vc == 128) launch_fixup_forward_t<256, 128, 8>(a, BH, causal, s);
+    else return false;
+    return true;
+}
+
+bool launch_fixup_stats(const FixArgs& a, int kc, int64_t BH, hipStream_t s) {
+    if (kc == 32) hipLaunchKernelGGL((fixup_stats_kernel<32>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
+    else if (kc == 128) hipLaunchKernelGGL((fixup_stats_kernel<128>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
+    else if (kc == 256) hipLaunchKernelGGL((fixup_stats_kernel<256>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
     else return false;
     return true;
 }

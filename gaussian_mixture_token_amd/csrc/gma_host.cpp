@@ -184,6 +184,7 @@ gma_status_t make_generic_plan(const gma_problem_t* p, int op, Plan* plan) {
     }
     plan->total = off;
     if (op == GMA_OP_RESPONSIBILITY_STATS) {
+        // Gamma of every row, then per-segment partial usages and counts
         plan->stat_segs = (int)std::max<int64_t>(1, std::min<int64_t>((1024 + BH - 1) / BH, (N + 63) / 64));
         plan->off_gamma = plan->total;
         plan->off_part = align_up(plan->off_gamma + (size_t)BH * N * K * sizeof(float), 256);
@@ -226,7 +227,7 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     const int wg_per_cu = tok ? plan->cls->tok_wg_per_cu : plan->cls->wg_per_cu;
     const int64_t BH = plan->B * plan->H;
     plan->n_chunks = (plan->N + C - 1) / C;
-    if (resp) {
+    if (op == GMA_OP_RESPONSIBILITIES) {
         plan->P = (int)std::min<int64_t>(plan->n_chunks, INT32_MAX / 4);
         plan->seg_chunks = (int)((plan->n_chunks + plan->P - 1) / plan->P);
     } else {
@@ -300,10 +301,10 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
         plan->total = align_up(plan->off_fix + fixup_scratch_bytes((int)plan->H, plan->K, plan->d_r), 256);
     }
     if (op == GMA_OP_RESPONSIBILITY_STATS) {
-        // Gamma of every row, then per-segment partial usages and counts
-        plan->stat_segs = (int)std::max<int64_t>(1, std::min<int64_t>((1024 + BH - 1) / BH, (plan->N + 63) / 64));
-        plan->off_gamma = plan->total;
-        plan->off_part = align_up(plan->off_gamma + (size_t)BH * plan->N * plan->K * sizeof(float), 256);
+        // per-segment partial usages and counts, formed by the responsibilities kernel itself (Gamma is
+        // never stored): [BH, P, K] of each, independent of N
+        plan->stat_segs = plan->P;
+        plan->off_part = plan->total;
         plan->total = align_up(plan->off_part + (size_t)BH * plan->stat_segs * plan->K * 8, 256);
     }
     return GMA_SUCCESS;
@@ -652,7 +653,8 @@ gma_status_t launch_fixup(const Plan& pl, FixArgs f, bool forward, bool causal, 
     bool ok = true;
     const gma_status_t st = timed_launch(K_FIXUP, s, [&] {
         ok = forward ? launch_fixup_forward(f, pl.cls->kc, pl.cls->vc, pl.B * pl.H, causal, s)
-                     : launch_fixup_resp(f, pl.cls->kc, pl.B * pl.H, s);
+             : f.stat_usage ? launch_fixup_stats(f, pl.cls->kc, pl.B * pl.H, s)
+                            : launch_fixup_resp(f, pl.cls->kc, pl.B * pl.H, s);
     });
     if (!ok) return fail(GMA_ERROR_LAUNCH, "no out-of-range recomputation kernel for class K=%d d_v=%d", pl.cls->kc,
                          pl.cls->vc);
@@ -1508,43 +1510,47 @@ gma_status_t gma_responsibility_stats(const gma_problem_t* p, const void* x, con
     if (ws && overlaps(ws, pl.total, x, nx)) return fail(GMA_ERROR_INVALID_VALUE, "workspace must not overlap x");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* w = reinterpret_cast<char*>(ws);
-    // Gamma of every row into the workspace (the responsibilities kernels), then the reductions
-    float* gam = reinterpret_cast<float*>(w + pl.off_gamma);
+    float* pu = reinterpret_cast<float*>(w + pl.off_part);
+    uint32_t* pc = reinterpret_cast<uint32_t*>(pu + (size_t)BH * pl.stat_segs * pl.K);
+    const int S = pl.stat_segs;
     if (pl.generic) {
+        // generic path: Gamma of every row into the workspace, then the per-segment reductions
+        float* gam = reinterpret_cast<float*>(w + pl.off_gamma);
         st = generic_gamma(pl, x, mu, raw_var, prior_logits, gam, pl.N, w, s, true);
         if (st != GMA_SUCCESS) return st;
+        const int64_t rps = (pl.N + S - 1) / S;
+        st = timed_launch(K_STATS, s, [&] {
+            hipLaunchKernelGGL(stats_partial_kernel, dim3((unsigned)S, (unsigned)BH), dim3(256), 0, s,
+                               (const float*)gam, pu, pc, pl.N, pl.K, S, rps);
+        });
+        if (st != GMA_SUCCESS) return st;
     } else {
+        // the responsibilities kernel forms the per-segment usage and counts itself (Gamma is not stored)
         st = launch_prep(pl, mu, raw_var, prior_logits, w, s);
         if (st != GMA_SUCCESS) return st;
         MainArgs a = base_args(pl, w);
         a.qx = x;
-        a.gamma = gam;
+        a.stat_usage = pu;
+        a.stat_count = pc;
         a.vec_x = vec_ok(x, pl.d_r, pl.f32);
         const bool dma = !pl.f32 && pl.cls->dma_resp && pl.d_r % 8 == 0 && !misaligned(x, 16) &&
                          (pl.N + pl.cls->c) * pl.d_r * 2 < (int64_t(1) << 31);
         const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
-        st = timed_launch(K_RESP, s, [&] { f_resp(a, (int)(BH * pl.P), s); });
+        st = timed_launch(K_STATS, s, [&] { f_resp(a, (int)(BH * pl.P), s); });
         if (st != GMA_SUCCESS) return st;
         if (pl.flags) {
             FixArgs f = fix_args(pl, w);
             f.qx = x;
-            f.gamma = gam;
             f.mu = mu;
             f.raw_var = raw_var;
             f.prior = prior_logits;
+            f.stat_usage = pu;
+            f.stat_count = pc;
+            f.stat_segs = S;
             st = launch_fixup(pl, f, false, false, s);
             if (st != GMA_SUCCESS) return st;
         }
     }
-    float* pu = reinterpret_cast<float*>(w + pl.off_part);
-    uint32_t* pc = reinterpret_cast<uint32_t*>(pu + (size_t)BH * pl.stat_segs * pl.K);
-    const int S = pl.stat_segs;
-    const int64_t rps = (pl.N + S - 1) / S;
-    st = timed_launch(K_STATS, s, [&] {
-        hipLaunchKernelGGL(stats_partial_kernel, dim3((unsigned)S, (unsigned)BH), dim3(256), 0, s,
-                           (const float*)gam, pu, pc, pl.N, pl.K, S, rps);
-    });
-    if (st != GMA_SUCCESS) return st;
     return timed_launch(K_STATS, s, [&] {
         hipLaunchKernelGGL(stats_final_kernel, dim3((unsigned)BH), dim3(256), 0, s, (const float*)pu,
                            (const uint32_t*)pc, usage, hard_counts, usage_entropy, pl.N, pl.K, S);

@@ -92,6 +92,8 @@ struct MainArgs {
     int64_t gk_ring;       // Gamma_K tiles kept per (batch, head): chunk ch lives in slot ch mod gk_ring
                            // (0: one slot per chunk).  A launch's segments lie in one ring window.
     int vec_x, vec_v, vec_o;  // 16-byte (x, v) / 4-element (o) vector access allowed (register staging)
+    float* stat_usage;     // MODE_RESP diagnostics (null: write Gamma): [BH, Pg, K] per-segment usage sums
+    uint32_t* stat_count;  //   and hard-assignment counts; Gamma is not written
     int* flags;            // [BH] or null (bf16): set to 1 for a (batch, head) with a row whose logits are
                            // not finite (a routing input or coefficient past the fp16 operand range)
     int has_carry;         // causal: load the carried state (P > 1)
@@ -386,6 +388,12 @@ main_kernel(const MainArgs a) {
     __shared__ float s_den[W][C];
     __shared__ __attribute__((aligned(16))) float s_c[KC];   // per-component logit constants c_k
     __shared__ __attribute__((aligned(16))) float s_z[KC];   // running Z (each wave owns its components)
+    // diagnostics (MODE_RESP with stat_usage): each wave's largest gamma per row and its component, and
+    // the segment's hard-assignment counts
+    constexpr bool RESP = MODE == MODE_RESP;
+    __shared__ float s_amv[RESP ? W : 1][RESP ? C : 1];
+    __shared__ int s_ami[RESP ? W : 1][RESP ? C : 1];
+    __shared__ uint32_t s_cnt[RESP ? KC : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -485,7 +493,12 @@ main_kernel(const MainArgs a) {
             for (int ks = 0; ks < NKS; ++ks) abf[kt][ks] = abg[((int64_t)ct * NKS + ks) * 64 + lane];
         }
         for (int k = tid; k < KC; k += NTHR) s_c[k] = a.cvec[(int64_t)h * KC + k];
+        if constexpr (RESP) {
+            for (int k = tid; k < KC; k += NTHR) s_cnt[k] = 0u;
+        }
     }
+    // diagnostics: this lane's usage sums of its components (over its rows of every chunk)
+    [[maybe_unused]] float use[RESP ? KT_W : 1][4] = {};
 
     // ---- running state: [Vt | Z] columns owned by this wave (all components), Z of own components
     constexpr int ST_T = HAS_STATE ? NCT : 1;
@@ -674,6 +687,60 @@ main_kernel(const MainArgs a) {
         if constexpr (NEED_K) finish_softmax(lk, mk, 1);
 
         if constexpr (MODE == MODE_RESP) {
+            if (a.stat_usage) {
+                // diagnostics instead of Gamma rows: usage sums of own components (rows past the end and
+                // pad components have gamma 0), and each row's largest gamma over own components, then
+                // over the lane groups (ties to the lowest component)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    const int tok = tt * 16 + lr;
+                    float best = -1.f;
+                    int bi = 0x7fffffff;
+#pragma unroll
+                    for (int kt = 0; kt < KT_W; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int c = (w * KT_W + kt) * 16 + lg * 4 + i;
+                            const float g = lq[kt][tt][i];
+                            use[kt][i] += g;
+                            if (c < a.K && g > best) {
+                                best = g;
+                                bi = c;
+                            }
+                        }
+#pragma unroll
+                    for (int o = 16; o < 64; o <<= 1) {
+                        const float ob = __shfl_xor(best, o, 64);
+                        const int oi = __shfl_xor(bi, o, 64);
+                        if (ob > best || (ob == best && oi < bi)) {
+                            best = ob;
+                            bi = oi;
+                        }
+                    }
+                    if (lg == 0) {
+                        s_amv[w][tok] = best;
+                        s_ami[w][tok] = bi;
+                    }
+                }
+                lds_barrier();
+                // the row's component over the waves (in wave order: the lowest component on ties); a row
+                // whose gammas are not finite (flagged, recomputed afterwards) counts nowhere
+                for (int tok = tid; tok < rows_valid; tok += NTHR) {
+                    float best = s_amv[0][tok];
+                    int bi = s_ami[0][tok];
+                    for (int v = 1; v < W; ++v) {
+                        const float ob = s_amv[v][tok];
+                        const int oi = s_ami[v][tok];
+                        if (ob > best || (ob == best && oi < bi)) {
+                            best = ob;
+                            bi = oi;
+                        }
+                    }
+                    if (bi < a.K) atomicAdd(&s_cnt[bi], 1u);
+                }
+                if constexpr (!DMA) lds_barrier();  // staging buffers are rewritten by the next chunk
+                return;
+            }
             // Gamma rows out: lane holds comps 16ct + 4g .. +3 of token 16tt + r
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
@@ -960,6 +1027,34 @@ main_kernel(const MainArgs a) {
     }
     if constexpr (!F32) {
         if (nonfin && a.flags) a.flags[bh] = 1;
+    }
+
+    if constexpr (RESP) {
+        if (a.stat_usage) {
+            // the segment's partials: usage summed over the 16 rows of each lane group (fixed butterfly
+            // order), counts from LDS
+#pragma unroll
+            for (int kt = 0; kt < KT_W; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float u = use[kt][i];
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) u += __shfl_xor(u, o, 64);
+                    use[kt][i] = u;
+                }
+            lds_barrier();
+            const int64_t base = ((int64_t)bh * a.Pg + sidx) * a.K;
+            if (lr == 0) {
+#pragma unroll
+                for (int kt = 0; kt < KT_W; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = (w * KT_W + kt) * 16 + lg * 4 + i;
+                        if (c < a.K) a.stat_usage[base + c] = use[kt][i];
+                    }
+            }
+            for (int c = tid; c < a.K; c += NTHR) a.stat_count[base + c] = s_cnt[c];
+        }
     }
 
     if constexpr (MODE == MODE_AGG) {

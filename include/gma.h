@@ -121,8 +121,11 @@ gma_status_t gma_responsibilities(const gma_problem_t* problem, const void* x, c
  *                                normalisation under which the page's interpretability figures (usage
  *                                entropy 0.933 with 104 of 128 components in use, section "Résultats
  *                                et Performance") are consistent.  Components in use: hard_counts > 0.
- * Gamma of every row is formed in the workspace: gma_workspace_size(problem,
- * GMA_OP_RESPONSIBILITY_STATS) bytes (about B * H * N * K * 4).  d_value is ignored. */
+ * The responsibilities kernel reduces its rows as it forms them: per-segment usage sums and counts
+ * (a few segments per (batch, head)) are combined in a fixed order, and Gamma is never stored.
+ * Workspace: gma_workspace_size(problem, GMA_OP_RESPONSIBILITY_STATS) bytes, independent of N for the
+ * compiled classes (the generic path, d_r > 128, forms Gamma, about B * H * N * K * 4 bytes).
+ * d_value is ignored. */
 gma_status_t gma_responsibility_stats(const gma_problem_t* problem, const void* x, const float* mu,
                                       const float* raw_var, const float* prior_logits, float* usage,
                                       uint32_t* hard_counts, float* usage_entropy, void* workspace,
