@@ -175,6 +175,9 @@ def main():
     ap.add_argument("--rounds", type=int, default=None,
                     help="launch the causal pass in this many rounds over the sequence (GMA_CAUSAL_ROUNDS; "
                          "a measured-slower schedule kept for comparison)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="causal bf16: pass a workspace without room for the stored Gamma_K tiles, so the output "
+                         "pass recomputes Gamma_K from K_X (the other schedule of the same path, for comparison)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) and exit; "
                          "its FETCH_SIZE / WRITE_SIZE counters calibrate the traffic figures")
@@ -214,7 +217,10 @@ def main():
     out = torch.empty(w.batch, w.heads, w.seq_len, w.d_value, dtype=w.torch_dtype, device=dev)
     prob = gma.problem(w.batch, w.heads, w.seq_len, w.d_route, w.n_comp, w.d_value, w.torch_dtype, w.eps)
     op = _lib.GMA_OP_FORWARD_CAUSAL if w.causal else _lib.GMA_OP_FORWARD_BIDIR
-    ws = torch.empty(gma.workspace_size(prob, op), dtype=torch.uint8, device=dev)
+    ws_bytes = gma.workspace_size(prob, op)
+    if args.recompute:
+        ws_bytes -= 1   # one byte short of the tiles' room: the library takes the recompute schedule
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step():
         gma.forward(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], eps=w.eps,
@@ -351,7 +357,9 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs, N(0,1) means, U(-1,1) raw variances, N(0,0.5^2) prior logits)",
         "config": {"workload": w.name, "mode": "causal" if w.causal else "bidirectional", "batch": w.batch,
                    "heads": w.heads, "seq_len": w.seq_len, "d_route": w.d_route, "n_comp": w.n_comp,
-                   "d_value": w.d_value, "eps": w.eps, "global_batch": w.batch, "parallelism": "single GPU"},
+                   "d_value": w.d_value, "eps": w.eps, "global_batch": w.batch, "parallelism": "single GPU",
+                   "schedule": ("recompute Gamma_K" if args.recompute else "default")
+                               + ("" if args.rounds is None else ", %d rounds" % args.rounds)},
         "roofline": roof,
         "dominant_kernel": dom,
         "step_isolated": step_isolated,
