@@ -51,6 +51,17 @@ __device__ __forceinline__ float wave_sum_f(float x) {
 // ---------------------------------------------------------------------------------- products
 constexpr int GM = 64, GN = 64, GK = 32, GLD = 80;   // tile, inner step, LDS row pitch (floats)
 
+// Eight fp32 values as bf16 hi (nearest even) and lo = the rounded remainder: hi + lo carries about 16
+// significant bits of each value.
+__device__ __forceinline__ void split_bf16x8(const float (&v)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const __bf16 h = (__bf16)v[j];
+        hi[j] = h;
+        lo[j] = (__bf16)(v[j] - (float)h);
+    }
+}
+
 // Workgroup of four wavefronts; wave w computes the 32 x 32 quarter (w / 2, w % 2) of the 64 x 64
 // tile as 2 x 2 accumulator tiles (v_mfma_f32_16x16x4_f32).  Operand tiles are staged in LDS
 // inner-index-major (s_a[k][m], s_b[k][n]) with a pitch of 80 floats: the 16-lane groups of a
@@ -225,7 +236,32 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
     for (int k0 = 0; k0 < Kd; k0 += GK) {
         const bool more = k0 + GK < Kd;
         if (more) fetch(k0 + GK);
-        if (wave_ok) {
+        if (wave_ok && g.split) {
+            // one 32-deep step on the bf16 matrix cores: lane group q takes inner indices q, q + 4, ..,
+            // q + 28 of both operands (the matrix core pairs element j of A's and B's fragments, so any
+            // common order sums the same products; this one reads four disjoint bank groups at pitch 80)
+            bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                float va[8], vb[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    va[j] = s_a[q + 4 * j][wm + 16 * t + r];
+                    vb[j] = s_b[q + 4 * j][wn + 16 * t + r];
+                }
+                split_bf16x8(va, ah[t], al[t]);
+                split_bf16x8(vb, bh[t], bl[t]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    if ((mt && !mok1) || (nt && !nok1)) continue;
+                    mma(acc[mt][nt], al[mt], bh[nt]);
+                    mma(acc[mt][nt], ah[mt], bl[nt]);
+                    mma(acc[mt][nt], ah[mt], bh[nt]);
+                }
+        } else if (wave_ok) {
 #pragma unroll
             for (int ks = 0; ks < GK; ks += 4) {
                 const float a0 = s_a[ks + q][wm + r], a1 = s_a[ks + q][wm + 16 + r];

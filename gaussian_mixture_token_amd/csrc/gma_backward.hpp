@@ -41,6 +41,10 @@ struct BwdGemm {
     int tok_flags = 0;
     float alpha = 1.f, beta = 0.f;
     int tril = 0;
+    // bf16 matrix cores: each fp32 operand value split into bf16 hi + lo and the product formed as
+    // hi hi + hi lo + lo hi (three v_mfma_f32_16x16x32_bf16 per 32-deep step, about 16 significant bits,
+    // fp32 accumulation) instead of eight v_mfma_f32_16x16x4_f32
+    int split = 0;
     // set by launch_bwd_gemm: 16-byte loads are allowed (base 16-byte aligned, leading dimension and
     // batch strides multiples of 4 elements)
     bool vecA = false, vecB = false;

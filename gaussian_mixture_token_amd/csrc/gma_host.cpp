@@ -766,6 +766,7 @@ gma_status_t forward_generic(const Plan& pl, bool causal, int64_t n_q, int64_t n
         g.tok_step = step;
         g.tok_flags = tokf;
         g.tril = tril;
+        g.split = pl.f32 ? 0 : 1;   // bf16 storage: split-bf16 products on the bf16 matrix cores
         bool ok = true;
         const gma_status_t ls = timed_launch(K_GEN_GEMM, s, [&] { ok = launch_bwd_gemm(g, ta, tb, false, s); });
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no product kernel for this operand combination");
@@ -1202,6 +1203,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         g.tok_step = per_seg ? kBwdSeg : C;
         g.tok_flags = tokf;
         g.tril = tril;
+        g.split = f32 ? 0 : 1;   // bf16 storage: split-bf16 products on the bf16 matrix cores
         bool ok = true;
         const gma_status_t ls = timed_launch(K_BWD_GEMM, s, [&] { ok = launch_bwd_gemm(g, ta, tb, out_bf16, s); });
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no backward product kernel for this operand combination");
