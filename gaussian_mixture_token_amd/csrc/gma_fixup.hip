@@ -10,8 +10,8 @@
 // are not finite.  Those kernels flag the (batch, head) of such a row; the kernels here run after them
 // and recompute every flagged (batch, head) from the inputs with the log-density in its direct form,
 // log pi_k - 1/2 sum_d [log sigma^2_kd + (x_d - mu_kd)^2 / sigma^2_kd], summed in fp64 (so any finite
-// bf16 input is in range), the posterior in fp64, and the state in fp32.  Heads that are not flagged
-// return at once.  One workgroup of 1024 threads per (batch, head):
+// bf16 input is in range), the posterior in fp64, and the state in fp32.  Slices that are not flagged
+// are skipped.  A few workgroups of 1024 threads, each walking (batch, head) slices:
 //   set-up   mu and 1 / sigma^2 of the head, transposed to [d][k] in the workspace (lanes read
 //            consecutive components), and c_k = log pi_k - 1/2 sum_d log sigma^2_kd in LDS (fp64);
 //   rows     one wave per row: lanes over components, a sequential loop over dims, the softmax by
@@ -139,17 +139,19 @@ __device__ void fix_row(const FixArgs& a, const void* x, int64_t row, const floa
 // Responsibilities of every row of a flagged (batch, head) into gamma [BH, N, K].
 template <int KC>
 __global__ void __launch_bounds__(kFixThreads) fixup_resp_kernel(const FixArgs a) {
-    const int64_t bh = blockIdx.x;
-    if (!a.flags[bh]) return;
-    const int h = (int)(bh % a.H);
     __shared__ double s_c[KC];
     __shared__ double s_red[4];
-    float* mt = a.scratch + (int64_t)h * 2 * a.K * a.d_r;
-    float* it = mt + (int64_t)a.K * a.d_r;
-    fix_setup<KC>(a, h, mt, it, s_c, s_red);
-    const int w = threadIdx.x >> 6;
-    for (int64_t r = w; r < a.N; r += kFixWaves)
-        fix_row<KC>(a, a.qx, bh * a.N + r, mt, it, s_c, a.gamma + (bh * a.N + r) * a.K);
+    for (int64_t bh = blockIdx.x; bh < a.BH; bh += gridDim.x) {
+        if (!a.flags[bh]) continue;
+        const int h = (int)(bh % a.H);
+        float* mt = a.scratch + (int64_t)h * 2 * a.K * a.d_r;
+        float* it = mt + (int64_t)a.K * a.d_r;
+        fix_setup<KC>(a, h, mt, it, s_c, s_red);
+        const int w = threadIdx.x >> 6;
+        for (int64_t r = w; r < a.N; r += kFixWaves)
+            fix_row<KC>(a, a.qx, bh * a.N + r, mt, it, s_c, a.gamma + (bh * a.N + r) * a.K);
+        __syncthreads();
+    }
 }
 
 // Diagnostics of a flagged (batch, head): usage and hard counts over all its rows, into segment 0 of the
@@ -158,15 +160,15 @@ __global__ void __launch_bounds__(kFixThreads) fixup_resp_kernel(const FixArgs a
 template <int KC>
 __global__ void __launch_bounds__(kFixThreads) fixup_stats_kernel(const FixArgs a) {
     constexpr int NK = (KC + 63) / 64;
-    const int64_t bh = blockIdx.x;
-    if (!a.flags[bh]) return;
-    const int h = (int)(bh % a.H);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int K = a.K;
     __shared__ double s_c[KC];
     __shared__ double s_red[4];
     __shared__ double s_use[kFixWaves][KC];
     __shared__ uint32_t s_cnt[KC];
+    for (int64_t bh = blockIdx.x; bh < a.BH; bh += gridDim.x) {
+    if (!a.flags[bh]) continue;
+    const int h = (int)(bh % a.H);
     float* mt = a.scratch + (int64_t)h * 2 * K * a.d_r;
     float* it = mt + (int64_t)K * a.d_r;
     for (int k = tid; k < KC; k += kFixThreads) s_cnt[k] = 0u;
@@ -211,15 +213,14 @@ __global__ void __launch_bounds__(kFixThreads) fixup_stats_kernel(const FixArgs 
             a.stat_count[i] = q == 0 ? s_cnt[k] : 0u;
         }
     }
+    __syncthreads();
+    }
 }
 
 // Forward of a flagged (batch, head): T tokens per chunk (the LDS holds the state [KC][VC] fp32 and the
 // chunk's Gamma rows of both sides).
 template <int KC, int VC, int T, bool CAUSAL>
 __global__ void __launch_bounds__(kFixThreads) fixup_forward_kernel(const FixArgs a) {
-    const int64_t bh = blockIdx.x;
-    if (!a.flags[bh]) return;
-    const int h = (int)(bh % a.H);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int K = a.K, dv = a.d_v;
     constexpr int PARTS = kFixThreads / VC;   // partial sums per output column
@@ -229,6 +230,9 @@ __global__ void __launch_bounds__(kFixThreads) fixup_forward_kernel(const FixArg
     __shared__ float s_gk[T][KC], s_gq[T][KC];
     __shared__ float s_part[PARTS][VC];
     __shared__ double s_red[4];
+    for (int64_t bh = blockIdx.x; bh < a.BH; bh += gridDim.x) {
+    if (!a.flags[bh]) continue;
+    const int h = (int)(bh % a.H);
     float* mt = a.scratch + (int64_t)h * 2 * K * a.d_r;
     float* it = mt + (int64_t)K * a.d_r;
     fix_setup<KC>(a, h, mt, it, s_c, s_red);
@@ -306,12 +310,19 @@ __global__ void __launch_bounds__(kFixThreads) fixup_forward_kernel(const FixArg
             a.state_out[bh * K * (dv + 1) + e] = (j < dv) ? s_st[k * VC + j] : s_z[k];
         }
     }
+    __syncthreads();
+    }
 }
+
+// Workgroups of the launch (each walks the slices bh = blockIdx.x, + gridDim.x, ...): few enough that a
+// call with no flagged slice pays little for the launch.
+constexpr int64_t kFixGrid = 32;
+unsigned fix_grid(int64_t BH) { return (unsigned)(BH < kFixGrid ? BH : kFixGrid); }
 
 template <int KC, int VC, int T>
 void launch_fixup_forward_t(const FixArgs& a, int64_t BH, bool causal, hipStream_t s) {
-    if (causal) hipLaunchKernelGGL((fixup_forward_kernel<KC, VC, T, true>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
-    else hipLaunchKernelGGL((fixup_forward_kernel<KC, VC, T, false>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
+    if (causal) hipLaunchKernelGGL((fixup_forward_kernel<KC, VC, T, true>), dim3(fix_grid(BH)), dim3(kFixThreads), 0, s, a);
+    else hipLaunchKernelGGL((fixup_forward_kernel<KC, VC, T, false>), dim3(fix_grid(BH)), dim3(kFixThreads), 0, s, a);
 }
 
 }  // namespace
@@ -328,17 +339,17 @@ bool launch_fixup_forward(const FixArgs& a, int kc, int vc, int64_t BH, bool cau
 }
 
 bool launch_fixup_stats(const FixArgs& a, int kc, int64_t BH, hipStream_t s) {
-    if (kc == 32) hipLaunchKernelGGL((fixup_stats_kernel<32>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
-    else if (kc == 128) hipLaunchKernelGGL((fixup_stats_kernel<128>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
-    else if (kc == 256) hipLaunchKernelGGL((fixup_stats_kernel<256>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
+    if (kc == 32) hipLaunchKernelGGL((fixup_stats_kernel<32>), dim3(fix_grid(BH)), dim3(kFixThreads), 0, s, a);
+    else if (kc == 128) hipLaunchKernelGGL((fixup_stats_kernel<128>), dim3(fix_grid(BH)), dim3(kFixThreads), 0, s, a);
+    else if (kc == 256) hipLaunchKernelGGL((fixup_stats_kernel<256>), dim3(fix_grid(BH)), dim3(kFixThreads), 0, s, a);
     else return false;
     return true;
 }
 
 bool launch_fixup_resp(const FixArgs& a, int kc, int64_t BH, hipStream_t s) {
-    if (kc == 32) hipLaunchKernelGGL((fixup_resp_kernel<32>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
-    else if (kc == 128) hipLaunchKernelGGL((fixup_resp_kernel<128>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
-    else if (kc == 256) hipLaunchKernelGGL((fixup_resp_kernel<256>), dim3((unsigned)BH), dim3(kFixThreads), 0, s, a);
+    if (kc == 32) hipLaunchKernelGGL((fixup_resp_kernel<32>), dim3(fix_grid(BH)), dim3(kFixThreads), 0, s, a);
+    else if (kc == 128) hipLaunchKernelGGL((fixup_resp_kernel<128>), dim3(fix_grid(BH)), dim3(kFixThreads), 0, s, a);
+    else if (kc == 256) hipLaunchKernelGGL((fixup_resp_kernel<256>), dim3(fix_grid(BH)), dim3(kFixThreads), 0, s, a);
     else return false;
     return true;
 }

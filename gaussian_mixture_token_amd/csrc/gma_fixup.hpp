@@ -23,6 +23,7 @@ struct FixArgs {
     float* stat_usage;      // diagnostics: per-segment partials [BH, stat_segs, K] (usage, then counts);
     uint32_t* stat_count;   //   a flagged slice gets its totals in segment 0 and zeros elsewhere
     int stat_segs;
+    int64_t BH;             // (batch, head) slices
     int64_t N;              // rows of qx / o (and of kx / v when causal)
     int64_t N_kv;           // rows of kx / v
     int H, K, d_r, d_v;

@@ -639,6 +639,7 @@ FixArgs fix_args(const Plan& pl, char* ws) {
     std::memset(&f, 0, sizeof(f));
     f.flags = reinterpret_cast<const int*>(ws + pl.off_flags);
     f.scratch = reinterpret_cast<float*>(ws + pl.off_fix);
+    f.BH = pl.B * pl.H;
     f.N = pl.N;
     f.N_kv = pl.N;
     f.H = (int)pl.H;

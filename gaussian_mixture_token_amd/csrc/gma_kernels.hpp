@@ -121,7 +121,7 @@ struct PrepArgs {
 // with A = [a | b] (k < DRC: a_{comp,k}; k >= DRC: b_{comp,k-DRC}).  Pad components get
 // a = b = 0 and c = -inf (their posterior is exactly 0); pad dimensions get a = b = 0.
 // Softplus and log in fp32 (about one ulp); a, b, the per-dimension terms of c and their sum in
-// fp64; every reduction runs in a fixed order.
+// fp64 (runs of consecutive dims, then a butterfly); every reduction runs in a fixed order.
 constexpr int kPrepThreads = 512;
 template <bool F32, int KC, int DRC>
 __global__ void __launch_bounds__(kPrepThreads) prep_kernel(const PrepArgs p) {
@@ -192,14 +192,25 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(const PrepArgs p) {
         }
     }
     __syncthreads();
-    if (tid < 16) {
-        const int comp = ct * 16 + tid;
+    // c of the tile's 16 components: L threads per component each add a run of DRC / L consecutive
+    // dims in order, then a fixed butterfly over the L (the terms past d_r are zero)
+    constexpr int L = DRC < 32 ? DRC : 32;
+    constexpr int PER = DRC / L;
+    static_assert(16 * L <= kPrepThreads && 64 % L == 0, "prep: threads per component");
+    const int cl = tid / L, sub = tid % L;
+    double part = 0.0;
+    if (tid < 16 * L) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) part += s_t[cl][sub * PER + j];
+    }
+#pragma unroll
+    for (int o = L / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (tid < 16 * L && sub == 0) {
+        const int comp = ct * 16 + cl;
         float c = -INFINITY;
         if (comp < p.K) {
-            double sum = 0.0;
-            for (int d = 0; d < p.d_r; ++d) sum += s_t[tid][d];
             const double logpi = (double)p.prior[(int64_t)h * p.K + comp] - s_lse;
-            c = (float)(LOG2E * (logpi - 0.5 * sum));
+            c = (float)(LOG2E * (logpi - 0.5 * part));
         }
         p.cvec[(int64_t)h * KC + comp] = c;
     }
