@@ -100,18 +100,17 @@ def test_forward_full_size_fp32(gma, cfg, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_cfg2_full_size_sampled_slices(gma, causal):
-    # B=32, H=8, N=4096: the GPU runs everything; the oracle checks 3 (batch, head) slices.
+def test_forward_cfg2_full_size_every_slice(gma, causal):
+    # B=32, H=8, N=4096: every (batch, head) slice against the oracle, and each slice's own error
     w = gma.workload(2)
     say("forward cfg2 causal=%s %s" % (causal, w))
     inp = gma.make_inputs(w)
-    o = gpu_forward(gma, w, inp, causal).float().cpu()
-    for b, h in ((0, 0), (17, 3), (31, 7)):
-        sl = {k: inp[k][b:b + 1, h:h + 1] for k in ("qx", "kx", "v")}
-        sl.update({k: inp[k][h:h + 1] for k in ("mu", "raw_var", "prior_logits")})
-        err = rel_err(o[b:b + 1, h:h + 1], ref_forward(w, sl, causal))
-        say("  slice b=%d h=%d rel err %.3e" % (b, h, err))
-        assert err <= TOL[w.dtype]
+    o = gpu_forward(gma, w, inp, causal).float().cpu().numpy().astype(np.float64)
+    ref = ref_forward(w, inp, causal)
+    err = rel_err(o, ref)
+    per = np.abs(o - ref).max(axis=(2, 3)) / np.abs(ref).max(axis=(2, 3))   # [B, H]
+    say("  rel err %.3e (worst slice %.3e)" % (err, per.max()))
+    assert err <= TOL[w.dtype] and per.max() <= TOL[w.dtype]
 
 
 @pytest.mark.parametrize("batch", [32, 22, 16, 13])
@@ -139,31 +138,33 @@ def test_forward_bf16_reduced_length_all_heads(gma, cfg, N, causal):
     assert err <= TOL[w.dtype]
 
 
-def test_forward_cfg3_full_size_sampled_heads(gma):
+def test_forward_cfg3_full_size_every_head(gma):
+    # the benchmark workload as the bench runs it (16 heads, 65,536 tokens), every head against the oracle
     w = gma.workload(3)
     say("forward cfg3 full size %s" % (w,))
     inp = gma.make_inputs(w)
+    o = gpu_forward(gma, w, inp).float().cpu().numpy().astype(np.float64)
+    ref = ref_forward(w, inp)
+    for h in range(w.heads):
+        err = rel_err(o[:, h:h + 1], ref[:, h:h + 1])
+        say("  head %d rel err %.3e" % (h, err))
+        assert err <= TOL[w.dtype]
+
+
+def test_forward_cfg4_full_size_two_heads(gma):
+    # 8 heads of 1,048,576 tokens on the GPU; the oracle checks a first and a last head
+    w = gma.workload(4)
+    say("forward cfg4 full size %s" % (w,))
+    inp = gma.make_inputs(w)
     o = gpu_forward(gma, w, inp).float().cpu()
-    heads = [0, 11]
+    del inp
+    heads = [0, 5]
     sub = gma.make_inputs(w, heads=heads)
     ref = ref_forward(w, sub)
     for j, h in enumerate(heads):
         err = rel_err(o[:, h:h + 1], ref[:, j:j + 1])
         say("  head %d rel err %.3e" % (h, err))
         assert err <= TOL[w.dtype]
-
-
-def test_forward_cfg4_full_size_one_head(gma):
-    w = gma.workload(4)
-    say("forward cfg4 full size %s" % (w,))
-    inp = gma.make_inputs(w)
-    o = gpu_forward(gma, w, inp).float().cpu()
-    del inp
-    sub = gma.make_inputs(w, heads=[5])
-    ref = ref_forward(w, sub)
-    err = rel_err(o[:, 5:6], ref)
-    say("  head 5 rel err %.3e" % err)
-    assert err <= TOL[w.dtype]
 
 
 # ------------------------------------------------------------------------------------ edge cases
