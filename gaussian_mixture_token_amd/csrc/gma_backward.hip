@@ -637,6 +637,273 @@ __global__ void __launch_bounds__(256) bwd_dl_kernel(const float* gamma, float* 
     }
 }
 
+// ---------------------------------------------------------------------------------- fused rows
+// One side's posterior gradient, routing-input gradient and parameter partials in one pass (bf16
+// storage, K = d_r = 128), instead of the dl row kernel and the two products that read dl:
+//   dl = gamma (dgamma - gamma . dgamma)      per row, fp32
+//   dx = dl [mu / s] - x (dl [1 / s])         v_mfma_f32_16x16x32_bf16
+//   P += dl^T [x | x^2 | 1]                   the same matrix cores, summed over the segment
+// Workgroup: four wavefronts over one (batch, head) and a segment of `seg` tokens (a multiple of 64),
+// in chunks of 64 tokens.  gamma and dgamma rows arrive by LDS DMA; wave w forms dl of rows 16 w ..
+// 16 w + 15 and leaves it in LDS as two bf16 images, hi and lo = the rounded remainder (about 16
+// significant bits); x arrives by LDS DMA as an image as well.  Wave w then owns dims 32 w .. 32 w + 31
+// of both products: the dx columns mu / s and 1 / s of those dims (their B fragments, split into hi
+// and lo once, stay in registers), and the P columns x and x^2 of those dims for every component
+// (accumulated in registers over the segment; the ones column for components 32 w .. 32 w + 31).
+// Where both operands are fp32 values the product is hi hi + hi lo + lo hi; against the exact bf16 x
+// and the ones column it is hi + lo.  dl never reaches HBM.
+namespace {
+
+// Byte offset of 16-byte chunk c of row `row` in a 64 x 256-byte LDS image: chunks are XOR-swizzled by
+// the row's low four bits (written r2 r1 r0 r3), so that both read patterns are conflict-free: 16 rows
+// of one chunk (row fragments) and 8 consecutive rows of one chunk pair (transposed fragments).
+__device__ __forceinline__ int img_chunk(int row, int c) {
+    const int f = ((row & 7) << 1) | ((row >> 3) & 1);
+    return row * 256 + ((c ^ f) << 4);
+}
+
+}  // namespace
+
+constexpr int kFusedChunk = 64;
+
+template <int KC, int DRC>
+__global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma, const float* dgamma, const void* x,
+                                                             const float* mw, void* dx, float* gp, int64_t N, int H,
+                                                             int seg, int64_t n_seg, int dxa) {
+    static_assert(KC == 128 && DRC == 128, "one 256-byte image row per token");
+    constexpr int C = kFusedChunk;
+    constexpr int ROWB = KC * 4;           // bytes per fp32 row of gamma
+    constexpr int STG = C * ROWB;          // one staged array of the chunk
+    constexpr int IMG = C * 256;           // one bf16 image of the chunk
+    constexpr int NCT = KC / 16;           // component tiles
+    constexpr int NST = 4 * 2 * 4;         // dx stores per wave and chunk
+    __shared__ __attribute__((aligned(16))) char s_stage[2 * STG];   // gamma, dgamma rows of the chunk
+    __shared__ __attribute__((aligned(16))) char s_dl[2 * IMG];      // dl hi, dl lo
+    __shared__ __attribute__((aligned(16))) char s_x[2 * IMG];       // x rows, two chunks
+    lds_char* const LS = (lds_char*)s_stage;
+    lds_char* const LDH = (lds_char*)s_dl;
+    lds_char* const LDL = LDH + IMG;
+    lds_char* const LX = (lds_char*)s_x;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / n_seg;
+    const int64_t sg = blockIdx.x % n_seg;
+    const int h = (int)(bh % H);
+    const int64_t t0 = sg * seg;
+    const int64_t t1 = t0 + seg < N ? t0 + seg : N;
+    const int nch = (int)((t1 - t0 + C - 1) / C);
+
+    // buffer descriptors over this (batch, head): rows past N read as zero, their stores are dropped
+    const i32x4 rs_g = uniform_rsrc(make_rsrc_words(gamma + bh * N * KC, (uint32_t)(N * ROWB)));
+    const i32x4 rs_d = uniform_rsrc(make_rsrc_words(dgamma + bh * N * KC, (uint32_t)(N * ROWB)));
+    const i32x4 rs_x =
+        uniform_rsrc(make_rsrc_words(reinterpret_cast<const uint16_t*>(x) + bh * N * DRC, (uint32_t)(N * DRC * 2)));
+    const __amdgpu_buffer_rsrc_t rs_o =
+        make_rsrc(reinterpret_cast<uint16_t*>(dx) + bh * N * DRC, (uint32_t)(N * DRC * 2));
+    const uint32_t ls_base = lds_addr(LS), lx_base = lds_addr(LX);
+
+    // DMA of the chunk at token n0: wave w's 16 rows of gamma and of dgamma (blocks of two rows: lane l
+    // takes row l / 32, floats 4 (l % 32) .. + 3) and 16 rows of x (blocks of four rows: lane l takes
+    // row l / 16 and the global chunk that the image keeps at chunk l % 16)
+    auto issue = [&](int64_t n0, int xbuf) {
+        const uint32_t v0 = (uint32_t)(((n0 + 16 * w + (lane >> 5)) * KC + 4 * (lane & 31)) * 4);
+        const uint32_t m0 = ls_base + (uint32_t)(16 * w * ROWB);
+#pragma unroll
+        for (int b = 0; b < 8; b += 4) {
+            dma16x4(rs_g, m0 + b * 1024, m0 + (b + 1) * 1024, m0 + (b + 2) * 1024, m0 + (b + 3) * 1024, v0 + b * 1024,
+                    v0 + (b + 1) * 1024, v0 + (b + 2) * 1024, v0 + (b + 3) * 1024);
+            dma16x4(rs_d, m0 + STG + b * 1024, m0 + STG + (b + 1) * 1024, m0 + STG + (b + 2) * 1024,
+                    m0 + STG + (b + 3) * 1024, v0 + b * 1024, v0 + (b + 1) * 1024, v0 + (b + 2) * 1024,
+                    v0 + (b + 3) * 1024);
+        }
+        uint32_t xv[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int row = 16 * w + 4 * bb + (lane >> 4);
+            const int gc = (lane & 15) ^ (((row & 7) << 1) | ((row >> 3) & 1));
+            xv[bb] = (uint32_t)((n0 + row) * DRC * 2 + gc * 16);
+        }
+        const uint32_t mx = lx_base + (uint32_t)(xbuf * IMG + 16 * w * 256);
+        dma16x4(rs_x, mx, mx + 1024, mx + 2048, mx + 3072, xv[0], xv[1], xv[2], xv[3]);
+    };
+
+    // transposed fragment: lane (r, g) gets column 16 ct + r of the image for tokens 32 tk + 4 g + i and
+    // 32 tk + 16 + 4 g + i (i = 0..3), the contraction order of both operands of P
+    auto tr_frag = [&](const lds_char* img, int ct, int tk) -> bf16x8 {
+        const int q = lane & 3, i4 = (lane >> 2) & 3;
+        u32x2 part[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int row = (2 * tk + hf) * 16 + g * 4 + i4;
+            const int slot = 4 * ct + q;
+            part[hf] = ds_read_tr16_at(img + img_chunk(row, slot >> 1) + ((slot & 1) << 3));
+        }
+        return __builtin_bit_cast(bf16x8, u32x4{part[0][0], part[0][1], part[1][0], part[1][1]});
+    };
+
+    // B fragments of dx: column tile j (0, 1: mu / s of dims 32 w + 16 j + r; 2, 3: 1 / s of dims
+    // 32 w + 16 (j - 2) + r), inner step ks: components 32 ks + 8 g .. + 7 (mw interleaves mu / s and 1 / s)
+    bf16x8 wh[4][4], wl[4][4];
+    {
+        const float* mwh = mw + (int64_t)h * KC * 2 * DRC;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int d = 32 * w + 16 * (j & 1) + r;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = mwh[(int64_t)(32 * ks + 8 * g + e) * 2 * DRC + 2 * d + (j >> 1)];
+                split_bf16x8(v, wh[j][ks], wl[j][ks]);
+            }
+    }
+    // P of the segment: px / p2 [ct][jj] = components 16 ct + 4 g + i, columns x / x^2 of dim
+    // 16 (2 w + jj) + r; po[hh] = components 16 (2 w + hh) + 4 g + i, the ones column (column r = 0)
+    f32x4 px[NCT][2], p2[NCT][2], po[2];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            px[ct][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            p2[ct][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    po[0] = po[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 ones0;
+    {
+        const __bf16 o = (__bf16)(r == 0 ? 1.f : 0.f);
+        ones0 = bf16x8{o, o, o, o, o, o, o, o};
+    }
+
+    if (nch > 0) issue(t0, 0);
+    for (int c = 0; c < nch; ++c) {
+        const int64_t n0 = t0 + (int64_t)c * C;
+        const int xbuf = c & 1;
+        // B0: this chunk's rows landed (after them only the previous chunk's dx stores were issued);
+        // every wave is done with the previous chunk's images
+        if (c == 0) wait_vmcnt<0>();
+        else wait_vmcnt<NST>();
+        block_barrier();
+        {
+            // dl of rows 16 w + 2 j + l / 32: lane l holds components 4 (l % 32) .. + 3
+            const lds_char* gs = LS + 16 * w * ROWB;
+            const int rl = lane >> 5, cl = lane & 31;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int rr = 2 * j + rl;
+                const f32x4 gv = lds_ld<f32x4>(gs + rr * ROWB + cl * 16);
+                const f32x4 dv = lds_ld<f32x4>(gs + STG + rr * ROWB + cl * 16);
+                float dot = gv[0] * dv[0] + gv[1] * dv[1] + gv[2] * dv[2] + gv[3] * dv[3];
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) dot += __shfl_xor(dot, o, 64);
+                bf16x4 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = gv[e] * (dv[e] - dot);
+                    hi[e] = (__bf16)v;
+                    lo[e] = (__bf16)(v - (float)hi[e]);
+                }
+                const int off = img_chunk(16 * w + rr, cl >> 1) + ((cl & 1) << 3);
+                lds_st<bf16x4>(LDH + off, hi);
+                lds_st<bf16x4>(LDL + off, lo);
+            }
+        }
+        lds_barrier();   // B1: the dl images are complete and the staged rows consumed
+        if (c + 1 < nch) issue(n0 + C, xbuf ^ 1);
+        const lds_char* xi = LX + xbuf * IMG;
+        {
+            // P += dl^T [x | x^2 | 1]
+            bf16x8 xf[2][2], xh[2][2], xl[2][2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int tk = 0; tk < 2; ++tk) {
+                    xf[jj][tk] = tr_frag(xi, 2 * w + jj, tk);
+                    float sq[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sq[e] = (float)xf[jj][tk][e] * (float)xf[jj][tk][e];
+                    split_bf16x8(sq, xh[jj][tk], xl[jj][tk]);
+                }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int tk = 0; tk < 2; ++tk) {
+                    const bf16x8 ah = tr_frag(LDH, ct, tk), al = tr_frag(LDL, ct, tk);
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        mma(px[ct][jj], al, xf[jj][tk]);
+                        mma(px[ct][jj], ah, xf[jj][tk]);
+                        mma(p2[ct][jj], al, xh[jj][tk]);
+                        mma(p2[ct][jj], ah, xl[jj][tk]);
+                        mma(p2[ct][jj], ah, xh[jj][tk]);
+                    }
+                    if ((ct >> 1) == w) {
+                        mma(po[ct & 1], al, ones0);
+                        mma(po[ct & 1], ah, ones0);
+                    }
+                }
+        }
+        {
+            // dx of dims 32 w .. + 31: acc[tt][j] rows = tokens 16 tt + 4 g + i, column tile j as in wh
+            f32x4 acc[4][4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                bf16x8 ah[4], al[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int off = img_chunk(16 * tt + r, 4 * ks + g);
+                    ah[tt] = lds_ld<bf16x8>(LDH + off);
+                    al[tt] = lds_ld<bf16x8>(LDL + off);
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        mma(acc[tt][j], al[tt], wh[j][ks]);
+                        mma(acc[tt][j], ah[tt], wl[j][ks]);
+                        mma(acc[tt][j], ah[tt], wh[j][ks]);
+                    }
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * tt + 4 * g + i, d = 32 * w + 16 * jj + r;
+                        const uint32_t xb = lds_ld<uint16_t>(xi + img_chunk(t, d >> 3) + (d & 7) * 2);
+                        const float val = acc[tt][jj][i] - __uint_as_float(xb << 16) * acc[tt][jj + 2][i];
+                        __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(val), rs_o,
+                                                              (uint32_t)(((n0 + t) * DRC + d) * 2), 0, 0);
+                    }
+        }
+    }
+
+    // the segment's partial: gp [bh][sg][K][dxa], columns x | x^2 | 1 (dxa >= 2 d_r + 1)
+    float* gpo = gp + (bh * n_seg + sg) * (int64_t)KC * dxa;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = 16 * ct + 4 * g + i, d = 16 * (2 * w + jj) + r;
+                gpo[k * dxa + d] = px[ct][jj][i];
+                gpo[k * dxa + DRC + d] = p2[ct][jj][i];
+            }
+    if (r == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gpo[(16 * (2 * w + hh) + 4 * g + i) * dxa + 2 * DRC] = po[hh][i];
+    }
+}
+
 // ---------------------------------------------------------------------------------- scans
 // In place over the n chunk entries of each (batch, head), entry stride rec floats: mode 0 exclusive
 // prefix, mode 1 exclusive suffix, mode 2 total (into entry 0).  A thread owns four consecutive state
@@ -855,6 +1122,23 @@ void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream
         bwd_dl_kernel<4><<<dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s>>>(gamma, dg, rows, K);
     else
         bwd_dl_kernel<1><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s>>>(gamma, dg, rows, K);
+}
+
+bool bwd_fused_rows_supported(int K, int d_r, bool f32) { return !f32 && K == 128 && d_r == 128; }
+
+int bwd_fused_rows_seg(int64_t BH, int64_t N, int min_seg) {
+    int seg = 4096;
+    while (seg / 2 >= min_seg && BH * ((N + seg - 1) / seg) < 256) seg /= 2;
+    return seg < min_seg ? min_seg : seg;
+}
+
+bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* x, const float* mw, void* dx, float* gp,
+                           int64_t BH, int64_t N, int H, int K, int d_r, int dxa, int seg, hipStream_t s) {
+    if (!bwd_fused_rows_supported(K, d_r, false) || seg % kFusedChunk != 0 || dxa < 2 * d_r + 1) return false;
+    const int64_t n_seg = (N + seg - 1) / seg;
+    bwd_fused_rows_kernel<128, 128><<<dim3((unsigned)(BH * n_seg)), dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N,
+                                                                                      H, seg, n_seg, dxa);
+    return true;
 }
 
 void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mode, hipStream_t s) {

@@ -80,6 +80,19 @@ void launch_bwd_gh(const float* p, const void* dout, bool f32, float* rs, int64_
                    hipStream_t s);
 // Softmax gradient in place: dl = gamma (dgamma - gamma . dgamma) per row of K.
 void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream_t s);
+// Posterior gradient, routing-input gradient and parameter partials of one side in one kernel
+// (bf16 storage, K = d_r = 128; bwd_fused_rows_supported): from gamma and dgamma [BH, N, K] fp32, the
+// routing input x [BH, N, d_r] bf16 and mw (launch_bwd_prep) it writes dx [BH, N, d_r] bf16 and the
+// partials gp [BH][n_seg][K][dxa] (columns x | x^2 | 1 of dl^T [x | x^2 | 1], rows dxa >= 2 d_r + 1
+// floats apart) over segments of
+// `seg` tokens (n_seg = ceil(N / seg)).  dl itself is not written.  Bases 16-byte aligned,
+// (N + 64) K 4 < 2^31.  false: no fused kernel for this shape.
+// bwd_fused_rows_seg: the segment length, a power of two in [min_seg, 4096] (min_seg a power of two
+// >= 64, at most 4096), long enough to keep n_seg within the partials buffer sized for min_seg.
+bool bwd_fused_rows_supported(int K, int d_r, bool f32);
+int bwd_fused_rows_seg(int64_t BH, int64_t N, int min_seg);
+bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* x, const float* mw, void* dx, float* gp,
+                           int64_t BH, int64_t N, int H, int K, int d_r, int dxa, int seg, hipStream_t s);
 // Chunk-state scans over [n_outer][n][rec]: mode 0 exclusive prefix in place, 1 exclusive suffix in
 // place, 2 the total into entry 0.  rec is a multiple of 4 (K times d_v + 1 rounded up to 4) and st
 // 16-byte aligned.

@@ -52,14 +52,15 @@ int next_pow2(int x) {
 enum KernelId {
     K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_STATS,
     K_BWD_GAMMA, K_BWD_GEMM, K_BWD_ROWS, K_BWD_SCAN, K_BWD_PARAM, K_DECODE_PREP,
-    K_GEN_PREP, K_GEN_GAMMA, K_GEN_GEMM, K_GEN_SCAN, K_GEN_OUT, K_FIXUP, K_COUNT
+    K_GEN_PREP, K_GEN_GAMMA, K_GEN_GEMM, K_GEN_SCAN, K_GEN_OUT, K_FIXUP, K_BWD_FUSED, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan", "causal_output", "bidir_output",
                                      "responsibilities", "state_convert", "decode_step", "responsibility_stats",
                                      "backward_responsibilities", "backward_products", "backward_rows",
                                      "backward_scan", "backward_parameters", "decode_prepare",
                                      "generic_prep", "generic_responsibilities", "generic_products",
-                                     "generic_scan", "generic_output", "out_of_range_fixup"};
+                                     "generic_scan", "generic_output", "out_of_range_fixup",
+                                     "backward_route_gradients"};
 
 struct Plan {
     const ShapeClass* cls = nullptr;
@@ -1264,7 +1265,28 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
                      BwdGen{}, gen_gh));
     GMA_TRY(gemm(tok(gk, K), false, cur_st(rt), false, tok(nullptr, d_v), dv, !f32, C, d_v, K, TM, 0,
                  causal ? dvt : nullptr, false));
-    // posterior gradients, then per side the routing-input gradient and the parameter partials
+    // posterior gradients, then per side the routing-input gradient and the parameter partials: one
+    // fused kernel per side where there is one for the shape (dl then stays on chip)
+    // The partials buffer holds n_sg segments of kBwdSeg tokens per side: the fused segments are no
+    // shorter, so their count fits.
+    const int fseg = bwd_fused_rows_seg(BH, N, kBwdSeg);
+    const int64_t fn = (N + fseg - 1) / fseg;
+    const bool fused = bwd_fused_rows_supported(K, d_r, f32) && !misaligned(qx, 16) && !misaligned(kx, 16) &&
+                       !misaligned(dqx, 16) && !misaligned(dkx, 16) && (N + 64) * K * 4 < (int64_t(1) << 31) &&
+                       fn <= b.n_sg;
+    if (fused) {
+        for (int side = 0; side < 2; ++side) {
+            bool ok = true;
+            GMA_TRY(timed_launch(K_BWD_FUSED, s, [&] {
+                ok = launch_bwd_fused_rows(side ? gk : gq, side ? dgk : dgq, side ? kx : qx, mw, side ? dkx : dqx,
+                                           gp + (size_t)side * BH * fn * K * dxa, BH, N, H, K, d_r, dxa, fseg, s);
+            }));
+            if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused backward row kernel for this shape");
+        }
+        return timed_launch(K_BWD_PARAM, s, [&] {
+            launch_bwd_param(gp, mu, rv, pr, dmu, drv, dpr, b.B, H, K, d_r, dxa, fn, s);
+        });
+    }
     GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_dl(gq, dgq, rows, K, s); }));
     GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_dl(gk, dgk, rows, K, s); }));
     for (int side = 0; side < 2; ++side) {
