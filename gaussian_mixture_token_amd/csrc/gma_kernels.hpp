@@ -115,7 +115,8 @@ struct PrepArgs {
 
 // ---------------------------------------------------------------------------------------------
 // prep: softplus variances, log-softmax priors, expanded-quadratic coefficients.
-// Grid (H, KC/16): one workgroup per 16 components of a head.  [a | b] is written in the exact
+// Grid (H, KC / kPrepComps<DRC>): one workgroup per kPrepComps components of a head, one thread per
+// (component, dim) where the padded dims allow it.  [a | b] is written in the exact
 // per-lane fragment order the main kernel loads:
 //   ab[h][ct][ks][lane][j] = A[comp = 16 ct + lane % 16][k = ks*KS + (lane/16)*(KS/4) + j]
 // with A = [a | b] (k < DRC: a_{comp,k}; k >= DRC: b_{comp,k-DRC}).  Pad components get
@@ -123,17 +124,21 @@ struct PrepArgs {
 // Softplus and log in fp32 (about one ulp); a, b, the per-dimension terms of c and their sum in
 // fp64 (runs of consecutive dims, then a butterfly); every reduction runs in a fixed order.
 constexpr int kPrepThreads = 512;
+template <int DRC>
+constexpr int kPrepComps = (kPrepThreads / DRC >= 16) ? 16 : (kPrepThreads / DRC >= 1 ? kPrepThreads / DRC : 1);
 template <bool F32, int KC, int DRC>
 __global__ void __launch_bounds__(kPrepThreads) prep_kernel(const PrepArgs p) {
     using T = Tr<F32>;
     constexpr int KS = T::KS;
     constexpr int NKS = 2 * DRC / KS;
     constexpr int EPL = KS / 4;  // elements per lane per fragment
+    constexpr int CPB = kPrepComps<DRC>;
+    static_assert(KC % CPB == 0 && 16 % CPB == 0, "prep: components per workgroup");
     const int h = blockIdx.x;
-    const int ct = blockIdx.y;
+    const int comp0 = blockIdx.y * CPB;
     const int tid = threadIdx.x;
     const double LOG2E = 1.4426950408889634073599246810019;
-    __shared__ double s_t[16][DRC];
+    __shared__ double s_t[CPB][DRC];
     __shared__ double s_lse;
     // clear the call's out-of-range flags (the kernels that follow set them)
     if (p.flags) {
@@ -155,11 +160,12 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(const PrepArgs p) {
         if (tid == 0) s_lse = m + log(acc);
     }
 
-    // a, b and the per-dimension terms of c for the 16 components of this tile
-    for (int e = tid; e < 16 * DRC; e += kPrepThreads) {
+    // a, b and the per-dimension terms of c for the CPB components of this workgroup
+    for (int e = tid; e < CPB * DRC; e += kPrepThreads) {
         const int cl = e / DRC;
         const int d = e % DRC;
-        const int comp = ct * 16 + cl;
+        const int comp = comp0 + cl;
+        const int ct = comp / 16;
         // softplus and log in fp32 (about one ulp each); the per-dimension terms of c are summed in
         // fp64 below
         double a = 0.0, b = 0.0, t = 0.0;
@@ -192,21 +198,21 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(const PrepArgs p) {
         }
     }
     __syncthreads();
-    // c of the tile's 16 components: L threads per component each add a run of DRC / L consecutive
+    // c of the workgroup's components: L threads per component each add a run of DRC / L consecutive
     // dims in order, then a fixed butterfly over the L (the terms past d_r are zero)
     constexpr int L = DRC < 32 ? DRC : 32;
     constexpr int PER = DRC / L;
-    static_assert(16 * L <= kPrepThreads && 64 % L == 0, "prep: threads per component");
+    static_assert(CPB * L <= kPrepThreads && 64 % L == 0, "prep: threads per component");
     const int cl = tid / L, sub = tid % L;
     double part = 0.0;
-    if (tid < 16 * L) {
+    if (tid < CPB * L) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) part += s_t[cl][sub * PER + j];
     }
 #pragma unroll
     for (int o = L / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-    if (tid < 16 * L && sub == 0) {
-        const int comp = ct * 16 + cl;
+    if (tid < CPB * L && sub == 0) {
+        const int comp = comp0 + cl;
         float c = -INFINITY;
         if (comp < p.K) {
             const double logpi = (double)p.prior[(int64_t)h * p.K + comp] - s_lse;

@@ -34,7 +34,7 @@ const ShapeClass* classes_bf16(int* count);
 
 template <bool F32, int KC, int DRC>
 void launch_prep(const PrepArgs& p, int heads, hipStream_t s) {
-    hipLaunchKernelGGL((prep_kernel<F32, KC, DRC>), dim3(heads, KC / 16), dim3(kPrepThreads), 0, s, p);
+    hipLaunchKernelGGL((prep_kernel<F32, KC, DRC>), dim3(heads, KC / kPrepComps<DRC>), dim3(kPrepThreads), 0, s, p);
 }
 
 // WPE: wavefronts per SIMD the register allocation must allow (2 lets two workgroups share a CU).
