@@ -329,13 +329,42 @@ __global__ void __launch_bounds__(256) bwd_gemm_kernel(const BwdGemm g) {
 // One workgroup per (head, component tile): workgroup h * KT + kt writes the coefficients of tile kt
 // and the constants cq of its 16 components.  The terms log s_kd + mu_kd^2 / s_kd of cq are computed in
 // parallel, 128 dims at a time, into LDS; one thread per component adds them in dim order.
+// split (d_r a multiple of 32): the operands for bwd_gamma_split_kernel instead, in the same bytes:
+// bf16 [H][d_r / 32 steps][KT][4 parts: a hi, a lo, b hi, b lo][64 lanes][8], lane (r, g) of tile kt
+// holding component 16 kt + r, dims 32 step + 8 g .. + 7 (a = -1 / (2 s), b = mu / s, hi the nearest
+// bf16, lo the bf16 of the remainder).
 __global__ void __launch_bounds__(256) bwd_frag_kernel(const float* mu, const float* raw_var, const float* prior,
-                                                       float* bf, double* cq, int K, int d_r, int KT) {
+                                                       float* bf, double* cq, int K, int d_r, int KT, int split) {
     const int h = blockIdx.x / KT, kt = blockIdx.x % KT, tid = threadIdx.x;
     const int steps = (d_r + 15) / 16, KP = 16 * KT;
     const int64_t per_head = (int64_t)steps * 2 * KT * 256;
+    if (split) {
+        uint16_t* fb = reinterpret_cast<uint16_t*>(bf + (int64_t)h * per_head);
+        const int S = d_r / 32;
+        for (int i = tid; i < S * 512; i += 256) {
+            const int st = i >> 9, lane = (i >> 3) & 63, e = i & 7;
+            const int k = 16 * kt + (lane & 15), d = 32 * st + 8 * (lane >> 4) + e;
+            float a = 0.f, b = 0.f;
+            if (k < K) {
+                const int64_t pe = ((int64_t)h * K + k) * d_r + d;
+                const float rv = raw_var[pe];
+                const float sv = fmaxf(rv, 0.f) + log1pf(expf(-fabsf(rv)));
+                a = -0.5f / sv;
+                b = mu[pe] / sv;
+            }
+            const float parts[2] = {a, b};
+#pragma unroll
+            for (int pb = 0; pb < 2; ++pb) {
+                const uint16_t hb = bf16_bits(parts[pb]);
+                const uint16_t lb = bf16_bits(parts[pb] - __uint_as_float((uint32_t)hb << 16));
+                const int64_t base = ((int64_t)(st * KT + kt) * 4 + 2 * pb) * 512 + lane * 8 + e;
+                fb[base] = hb;
+                fb[base + 512] = lb;
+            }
+        }
+    }
     // element e of the head's operands: e >> 8 = (2 st + part) KT + kt, e & 255 = 4 lane + j
-    for (int i = tid; i < 2 * steps * 256; i += 256) {
+    for (int i = tid; i < (split ? 0 : 2 * steps * 256); i += 256) {
         const int sp = i >> 8;
         const int64_t e = ((int64_t)sp * KT + kt) * 256 + (i & 255);
         const int j = i & 3, lane = (i >> 2) & 63;
@@ -527,6 +556,106 @@ __global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, cons
                 for (int kt = 0; kt < KT; ++kt) {
                     const int k = 16 * kt + r;
                     if (k < K) gamma[(bh * N + rr) * K + k] = e[kt] * inv;
+                }
+            }
+        }
+    }
+}
+
+// Responsibilities for bf16 storage on the bf16 matrix cores (d_r a multiple of 32): the expanded form
+// with x exact in bf16 and x^2, a, b split into bf16 hi + lo (the lo lo products dropped), fp32
+// accumulation: x b_lo + x b_hi + x^2_lo a_hi + x^2_hi a_lo + x^2_hi a_hi per 32 dims and component
+// tile, five v_mfma_f32_16x16x32_bf16.  The head's operand fragments (bwd_frag_kernel, split) stay in
+// LDS for the workgroup, which walks `rows` consecutive rows of one (batch, head) in blocks of 64, wave w
+// rows 16 w .. 16 w + 15 of a block (lane (r, g): row r, dims 8 g .. 8 g + 7 of a step); the next
+// block's x is loaded during the current block.  Softmax as in bwd_gamma_mfma_kernel, in fp32.
+template <int KT, int SMAX>
+__global__ void __launch_bounds__(256) bwd_gamma_split_kernel(const uint16_t* x, const bf16x8* fr, const double* cq,
+                                                              float* gamma, int64_t N, int H, int K, int d_r,
+                                                              int rows) {
+    __shared__ bf16x8 s_f[SMAX * KT * 4 * 64];
+    const int S = d_r / 32;
+    const int64_t blocks = (N + rows - 1) / rows;
+    const int64_t bh = (int64_t)blockIdx.x / blocks;
+    const int h = (int)(bh % H);
+    const int64_t r0 = ((int64_t)blockIdx.x % blocks) * rows;
+    const int64_t r1 = r0 + rows < N ? r0 + rows : N;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const bf16x8* fh = fr + (int64_t)h * S * KT * 4 * 64;
+    for (int i = tid; i < S * KT * 4 * 64; i += 256) s_f[i] = fh[i];
+    float cr[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) cr[kt] = (float)cq[(int64_t)h * 16 * KT + 16 * kt + r];
+    __syncthreads();
+    const uint16_t* xh = x + bh * N * d_r;
+    float* gh = gamma + bh * N * K;
+    auto load = [&](int64_t rb, u32x4 (&xr)[SMAX]) {
+        const int64_t row = rb + r;
+#pragma unroll
+        for (int st = 0; st < SMAX; ++st)
+            xr[st] = (st < S && row < r1) ? *reinterpret_cast<const u32x4*>(xh + row * d_r + 32 * st + 8 * g)
+                                          : u32x4{0u, 0u, 0u, 0u};
+    };
+    u32x4 xn[SMAX];
+    load(r0 + 16 * w, xn);
+    for (int64_t rb = r0 + 16 * w; rb < r1; rb += 64) {
+        u32x4 xr[SMAX];
+#pragma unroll
+        for (int st = 0; st < SMAX; ++st) xr[st] = xn[st];
+        if (rb + 64 < r1) load(rb + 64, xn);
+        f32x4 acc[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < SMAX; ++st) {
+            if (st >= S) break;
+            const bf16x8 xa = __builtin_bit_cast(bf16x8, xr[st]);
+            float sq[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = (float)xa[e];
+                sq[e] = v * v;
+            }
+            bf16x8 qh, ql;
+            split_bf16x8(sq, qh, ql);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                const bf16x8* fb = s_f + (st * KT + kt) * 4 * 64 + lane;
+                mma(acc[kt], xa, fb[192]);
+                mma(acc[kt], xa, fb[128]);
+                mma(acc[kt], ql, fb[0]);
+                mma(acc[kt], qh, fb[64]);
+                mma(acc[kt], qh, fb[0]);
+            }
+        }
+        // rows rb + 4 g + i: softmax over the components (tiles in registers, 16 lanes per tile)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float l[KT];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                l[kt] = cr[kt] + acc[kt][i];
+                mx = fmaxf(mx, l[kt]);
+            }
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            float sm = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                l[kt] = expf(l[kt] - mx);
+                sm += l[kt];
+            }
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
+            const float inv = 1.f / sm;
+            const int64_t row = rb + 4 * g + i;
+            if (row < r1) {
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    const int k = 16 * kt + r;
+                    if (k < K) gh[row * K + k] = l[kt] * inv;
                 }
             }
         }
@@ -1093,10 +1222,31 @@ int bwd_gamma_tiles(int K) {
 }
 
 void launch_bwd_frag(const float* mu, const float* raw_var, const float* prior, float* bf, double* cq, int H, int K,
-                     int d_r, hipStream_t s) {
+                     int d_r, bool split, hipStream_t s) {
     // H * KT <= 16 H fits the 32-bit grid (the backward plan bounds B * H * 16 by INT32_MAX)
     const int KT = bwd_gamma_tiles(K);
-    bwd_frag_kernel<<<dim3((unsigned)(H * KT)), dim3(256), 0, s>>>(mu, raw_var, prior, bf, cq, K, d_r, KT);
+    bwd_frag_kernel<<<dim3((unsigned)(H * KT)), dim3(256), 0, s>>>(mu, raw_var, prior, bf, cq, K, d_r, KT,
+                                                                   split ? 1 : 0);
+}
+
+bool bwd_gamma_split_supported(int K, int d_r, bool f32) {
+    return !f32 && d_r % 32 == 0 && bwd_gamma_tiles(K) * (d_r / 32) <= 32;
+}
+
+void launch_bwd_gamma_split(const void* x, const float* bf, const double* cq, float* gamma, int64_t BH, int64_t N,
+                            int H, int K, int d_r, hipStream_t s) {
+    const int KT = bwd_gamma_tiles(K);
+    const int rows = 1024;
+    const dim3 grid((unsigned)((N + rows - 1) / rows * BH)), block(256);
+    const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
+    const bf16x8* fr = reinterpret_cast<const bf16x8*>(bf);
+    switch (KT) {
+        case 1: bwd_gamma_split_kernel<1, 8><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        case 2: bwd_gamma_split_kernel<2, 8><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        case 4: bwd_gamma_split_kernel<4, 8><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        case 8: bwd_gamma_split_kernel<8, 4><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        default: bwd_gamma_split_kernel<16, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+    }
 }
 
 void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const double* cq, float* gamma, int64_t BH,

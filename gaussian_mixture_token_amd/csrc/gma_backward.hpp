@@ -70,9 +70,15 @@ void launch_bwd_prep(const float* mu, const float* raw_var, float* mw, int H, in
 // [H][16 KT] fp64, written by launch_bwd_frag.
 int bwd_gamma_tiles(int K);
 void launch_bwd_frag(const float* mu, const float* raw_var, const float* prior, float* bf, double* cq, int H, int K,
-                     int d_r, hipStream_t s);
+                     int d_r, bool split, hipStream_t s);
 void launch_bwd_gamma_mfma(const void* x, bool f32, const float* bf, const double* cq, float* gamma, int64_t BH,
                            int64_t N, int H, int K, int d_r, hipStream_t s);
+// The same for bf16 rows on the bf16 matrix cores with split operands (bwd_gamma_split_supported:
+// bf16, d_r a multiple of 32, the head's fragments within 128 KiB), from the fragments that
+// launch_bwd_frag writes with split = true (same bytes as the fp32 ones).  x 16-byte aligned.
+bool bwd_gamma_split_supported(int K, int d_r, bool f32);
+void launch_bwd_gamma_split(const void* x, const float* bf, const double* cq, float* gamma, int64_t BH, int64_t N,
+                            int H, int K, int d_r, hipStream_t s);
 
 // Read-phase gradient per row: p [rows, dva] holds (num | Gamma_Q . Z, the denominator without
 // eps); rs [rows, 2] <- (1 / den, h = -(dO . O) / den), so that [g | h] = [dO rs0 | rs1] (GEN_GH).

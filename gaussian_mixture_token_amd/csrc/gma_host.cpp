@@ -721,7 +721,7 @@ gma_status_t generic_gamma(const Plan& pl, const void* x, const float* mu, const
     double* cq = reinterpret_cast<double*>(w + pl.off_gcq);
     if (prep) {
         const gma_status_t st = timed_launch(K_GEN_PREP, s, [&] {
-            launch_bwd_frag(mu, rv, pr, bf, cq, (int)pl.H, pl.K, pl.d_r, s);
+            launch_bwd_frag(mu, rv, pr, bf, cq, (int)pl.H, pl.K, pl.d_r, false, s);
         });
         if (st != GMA_SUCCESS) return st;
     }
@@ -1221,15 +1221,20 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     // mixture constants, responsibilities of both sides, [V | 1]
     GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_prep(mu, rv, mw, H, K, d_r, s); }));
     const double* cq = reinterpret_cast<const double*>(w + b.off_cq);
+    // bf16 rows: split-bf16 products on the bf16 matrix cores (the operand fragments then take the split
+    // layout in the same bytes); fp32 rows: the fp32 matrix cores with fp64 partial sums
+    const bool gsplit = bwd_gamma_split_supported(K, d_r, f32) && !misaligned(qx, 16) && !misaligned(kx, 16);
     GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] {
-        launch_bwd_frag(mu, rv, pr, F(b.off_bf), reinterpret_cast<double*>(w + b.off_cq), H, K, d_r, s);
+        launch_bwd_frag(mu, rv, pr, F(b.off_bf), reinterpret_cast<double*>(w + b.off_cq), H, K, d_r, gsplit, s);
     }));
-    GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] {
-        launch_bwd_gamma_mfma(qx, f32, F(b.off_bf), cq, gq, BH, N, H, K, d_r, s);
-    }));
-    GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] {
-        launch_bwd_gamma_mfma(kx, f32, F(b.off_bf), cq, gk, BH, N, H, K, d_r, s);
-    }));
+    for (int side = 0; side < 2; ++side) {
+        const void* x = side ? kx : qx;
+        float* gam = side ? gk : gq;
+        GMA_TRY(timed_launch(K_BWD_GAMMA, s, [&] {
+            if (gsplit) launch_bwd_gamma_split(x, F(b.off_bf), cq, gam, BH, N, H, K, d_r, s);
+            else launch_bwd_gamma_mfma(x, f32, F(b.off_bf), cq, gam, BH, N, H, K, d_r, s);
+        }));
+    }
     // operands generated inside the products (views in rows): [V | 1] from V, [g | h] from dO and the row
     // pair rs = (1 / den, h), [x | x^2 | 1] from the routing input
     const View rows_tok{nullptr, N, C, 1, 0}, rows_seg{nullptr, N, kBwdSeg, 1, 0};
