@@ -52,7 +52,7 @@ int next_pow2(int x) {
 enum KernelId {
     K_PREP = 0, K_AGG, K_SCAN, K_OUT_CAUSAL, K_OUT_BIDIR, K_RESP, K_STATE, K_DECODE, K_STATS,
     K_BWD_GAMMA, K_BWD_GEMM, K_BWD_ROWS, K_BWD_SCAN, K_BWD_PARAM, K_DECODE_PREP,
-    K_GEN_PREP, K_GEN_GAMMA, K_GEN_GEMM, K_GEN_SCAN, K_GEN_OUT, K_FIXUP, K_BWD_FUSED, K_COUNT
+    K_GEN_PREP, K_GEN_GAMMA, K_GEN_GEMM, K_GEN_SCAN, K_GEN_OUT, K_FIXUP, K_BWD_FUSED, K_BWD_CHUNK, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan", "causal_output", "bidir_output",
                                      "responsibilities", "state_convert", "decode_step", "responsibility_stats",
@@ -60,7 +60,7 @@ const char* kKernelNames[K_COUNT] = {"prep", "segment_aggregate", "segment_scan"
                                      "backward_scan", "backward_parameters", "decode_prepare",
                                      "generic_prep", "generic_responsibilities", "generic_products",
                                      "generic_scan", "generic_output", "out_of_range_fixup",
-                                     "backward_route_gradients"};
+                                     "backward_route_gradients", "backward_query_chunks"};
 
 struct Plan {
     const ShapeClass* cls = nullptr;
@@ -1244,21 +1244,34 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
     GMA_TRY(gemm(tok(gk, K), true, vv, false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{}, gen_v));
     GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, causal ? 0 : 2, s); }));
-    // read phase: [num | Gamma_Q . Z] = Gamma_Q state (+ tril(Gamma_Q Gamma_K^T) [V | 1]), then g, h
-    GMA_TRY(gemm(tok(gq, K), false, cur_st(stt), false, tok(pp, dva), pp, false, C, dva, K, TM, 0, nullptr, false));
-    if (causal) {
-        GMA_TRY(gemm(tok(gq, K), false, tok(gk, K), true, sq(ac), ac, false, C, C, K, TM | TN, 1, nullptr, false));
-        GMA_TRY(gemm(sq(ac), false, vv, false, tok(pp, dva), pp, false, C, dva, C, TM | TK, 0, pp, false, BwdGen{}, gen_v));
+    // Causal bf16 at K = d_v = 128: one fused kernel per chunk does the read phase, the chunk terms of the
+    // suffix sums and dGamma_Q (and writes the intra-chunk blocks ac, mt for the key side)
+    const bool qfused = causal && bwd_chunk_q_supported(K, d_v, f32) && !misaligned(v, 16) && !misaligned(dout, 16);
+    if (qfused) {
+        bool ok = true;
+        GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
+            ok = launch_bwd_chunk_q(gq, gk, v, dout, stt, rs, rt, ac, mt, dgq, BH, N, b.n_st, K, d_v, dva, b.eps, s);
+        }));
+        if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused query-side chunk kernel for this shape");
+        GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(rt, BH, b.n_st, rec, 1, s); }));
     }
-    GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_gh(pp, dout, f32, rs, rows, d_v, dva, b.eps, s); }));
-    // Gamma_Q^T [g | h] per entry -> the sums over the later chunks / the total
-    GMA_TRY(gemm(tok(gq, K), true, ghv, false, all_st(rt), rt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{}, gen_gh));
-    GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(rt, BH, b.n_st, rec, causal ? 1 : 2, s); }));
-    // dGamma_Q = [g | h] state^T (+ tril([g | h] [V | 1]^T) Gamma_K)
-    GMA_TRY(gemm(ghv, false, cur_st(stt), true, tok(dgq, K), dgq, false, C, K, dva, TM, 0, nullptr, false, gen_gh));
-    if (causal) {
-        GMA_TRY(gemm(ghv, false, vv, true, sq(mt), mt, false, C, C, dva, TM | TN, 1, nullptr, false, gen_gh, gen_v));
-        GMA_TRY(gemm(sq(mt), false, tok(gk, K), false, tok(dgq, K), dgq, false, C, K, C, TM | TK, 0, dgq, false));
+    if (!qfused) {
+        // read phase: [num | Gamma_Q . Z] = Gamma_Q state (+ tril(Gamma_Q Gamma_K^T) [V | 1]), then g, h
+        GMA_TRY(gemm(tok(gq, K), false, cur_st(stt), false, tok(pp, dva), pp, false, C, dva, K, TM, 0, nullptr, false));
+        if (causal) {
+            GMA_TRY(gemm(tok(gq, K), false, tok(gk, K), true, sq(ac), ac, false, C, C, K, TM | TN, 1, nullptr, false));
+            GMA_TRY(gemm(sq(ac), false, vv, false, tok(pp, dva), pp, false, C, dva, C, TM | TK, 0, pp, false, BwdGen{}, gen_v));
+        }
+        GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_gh(pp, dout, f32, rs, rows, d_v, dva, b.eps, s); }));
+        // Gamma_Q^T [g | h] per entry -> the sums over the later chunks / the total
+        GMA_TRY(gemm(tok(gq, K), true, ghv, false, all_st(rt), rt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{}, gen_gh));
+        GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(rt, BH, b.n_st, rec, causal ? 1 : 2, s); }));
+        // dGamma_Q = [g | h] state^T (+ tril([g | h] [V | 1]^T) Gamma_K)
+        GMA_TRY(gemm(ghv, false, cur_st(stt), true, tok(dgq, K), dgq, false, C, K, dva, TM, 0, nullptr, false, gen_gh));
+        if (causal) {
+            GMA_TRY(gemm(ghv, false, vv, true, sq(mt), mt, false, C, C, dva, TM | TN, 1, nullptr, false, gen_gh, gen_v));
+            GMA_TRY(gemm(sq(mt), false, tok(gk, K), false, tok(dgq, K), dgq, false, C, K, C, TM | TK, 0, dgq, false));
+        }
     }
     // dGamma_K = [V | 1] R^T (+ the same intra-chunk block transposed, times Gamma_Q)
     GMA_TRY(gemm(vv, false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false, gen_v));
