@@ -1067,27 +1067,29 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
 }
 
 // ---------------------------------------------------------------------------------- fused chunk, query side
-// The query-side chunk work of the causal backward in one kernel (bf16 storage, K = d_v = 128), one
-// workgroup of four wavefronts per (batch, head, chunk of 64 tokens).  From the recomputed posteriors,
-// V, dO and the state before the chunk S = [Vt | Z] (the exclusive prefix over chunks of
-// Gamma_K^T [V | 1]):
+// The query-side chunk work of the causal backward in one kernel (bf16 storage, K = d_v = 128).  From the
+// recomputed posteriors, V, dO and the state before the chunk S = [Vt | Z] (the exclusive prefix over
+// chunks of Gamma_K^T [V | 1]), per chunk of 64 tokens:
 //   ac  = tril(Gamma_Q Gamma_K^T)
 //   num = Gamma_Q Vt + ac V,   den = Gamma_Q . Z + ac 1 + eps
 //   g   = dO / den,  h = -(dO . num / den) / den                -> rs = (1 / den, h)
 //   rt  = Gamma_Q^T [g | h]                                      (the chunk's term of the suffix sums)
 //   mt  = tril([g | h] [V | 1]^T)
 //   dGamma_Q = [g | h] S^T + mt Gamma_K
-// ac and mt also go to HBM for the key-side products.  Gamma_Q, Gamma_K, g, ac and mt live in LDS as
-// bf16 hi + lo images, V (and dO, for one step) as exact bf16 images; the state comes from HBM straight
-// into split B fragments in registers (wave w: d_v columns 32 w .. + 31 for num, components 32 w .. + 31
-// for dGamma_Q).  Wave w owns q tile w of ac and mt, d_v columns 32 w .. + 31 of num, components
-// 32 w .. + 31 of rt and dGamma_Q.  Products: hi hi + hi lo + lo hi between two fp32 operands, hi + lo
-// against V, fp32 accumulation.
+// ac and mt also go to HBM for the key-side products.  A workgroup of four wavefronts walks `per`
+// consecutive chunks of one (batch, head); the next chunk's operands are loaded into registers while
+// the current one is processed.  Gamma_Q, Gamma_K, g, ac and mt live in LDS as bf16 hi + lo images, V
+// (and dO, for one step) as exact bf16 images; the state goes from HBM straight into split fragments
+// (wave w: d_v columns 32 w .. + 31 for num, components 32 w .. + 31 for dGamma_Q).  Wave w owns q
+// tile w of ac and mt, d_v columns 32 w .. + 31 of num and components 32 w .. + 31 of rt and
+// dGamma_Q.  ac, mt, rt and dGamma_Q are formed transposed (their accumulator rows run along the
+// stored rows), so that each lane stores 16 contiguous bytes.  Products: hi hi + hi lo + lo hi between
+// two fp32 operands, hi + lo against V, fp32 accumulation.
 template <int KC, int VC>
 __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const float* gk, const void* v,
                                                           const void* dout, const float* stt, float* rs, float* rt,
                                                           float* ac_out, float* mt_out, float* dgq, int64_t N,
-                                                          int64_t n_st, int dva, float eps) {
+                                                          int64_t n_st, int per, int dva, float eps) {
     static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
     constexpr int C = 64;
     constexpr int IMG = C * 256;
@@ -1110,345 +1112,384 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int64_t bh = blockIdx.x / n_st, c = blockIdx.x % n_st;
-    const int64_t n0 = c * C;
-    const int nv = (int)(N - n0 < C ? N - n0 : C);   // rows of the chunk inside the sequence
+    const int64_t groups = (n_st + per - 1) / per;
+    const int64_t bh = blockIdx.x / groups;
+    const int64_t c0 = (blockIdx.x % groups) * per;
+    const int64_t c1 = c0 + per < n_st ? c0 + per : n_st;
     const int64_t rec = (int64_t)KC * dva;
-    const float* S = stt + (bh * n_st + c) * rec;
-    const float* gqh = gq + (bh * N + n0) * KC;
-    const float* gkh = gk + (bh * N + n0) * KC;
-    const uint16_t* vh = reinterpret_cast<const uint16_t*>(v) + (bh * N + n0) * VC;
-    const uint16_t* dh = reinterpret_cast<const uint16_t*>(dout) + (bh * N + n0) * VC;
-    float* blk_ac = ac_out + (bh * n_st + c) * C * C;
-    float* blk_mt = mt_out + (bh * n_st + c) * C * C;
 
-    // ---- operands: Gamma_Q, Gamma_K rows 16 w + 2 j + l / 32 (lane l: components 4 (l % 32) .. + 3)
-    {
+    // ---- the token operands of one chunk, loaded a chunk ahead: Gamma_Q, Gamma_K rows 16 w + 2 j + l / 32
+    // (components 4 (l % 32) .. + 3); V, dO rows 16 w + 4 bb + l / 16 (chunk l % 16)
+    f32x4 pq[8], pk[8];
+    u32x4 pv[4], pd[4];
+    auto fetch = [&](int64_t c) {
+        const int64_t n0 = c * C;
+        const int nv = (int)(N - n0 < C ? N - n0 : C);
+        const float* gqh = gq + (bh * N + n0) * KC;
+        const float* gkh = gk + (bh * N + n0) * KC;
+        const uint16_t* vh = reinterpret_cast<const uint16_t*>(v) + (bh * N + n0) * VC;
+        const uint16_t* dh = reinterpret_cast<const uint16_t*>(dout) + (bh * N + n0) * VC;
         const int rl = lane >> 5, cl = lane & 31;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int row = 16 * w + 2 * j + rl;
-            f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-            if (row < nv) {
-                a = *reinterpret_cast<const f32x4*>(gqh + (int64_t)row * KC + 4 * cl);
-                b = *reinterpret_cast<const f32x4*>(gkh + (int64_t)row * KC + 4 * cl);
-            }
-            const int off = img_slot(row, cl);
-            bf16x4 hi, lo;
-            split4(a, hi, lo);
-            lds_st<bf16x4>(LQH + off, hi);
-            lds_st<bf16x4>(LQL + off, lo);
-            split4(b, hi, lo);
-            lds_st<bf16x4>(LKH + off, hi);
-            lds_st<bf16x4>(LKL + off, lo);
+            pq[j] = row < nv ? *reinterpret_cast<const f32x4*>(gqh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
+            pk[j] = row < nv ? *reinterpret_cast<const f32x4*>(gkh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    }
-    // V rows 16 w + 4 bb + l / 16, chunk l % 16 into the image; dO the same into registers
-    u32x4 dor[4];
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-        const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
-        u32x4 vv = {0u, 0u, 0u, 0u}, dd = {0u, 0u, 0u, 0u};
-        if (row < nv) {
-            vv = *reinterpret_cast<const u32x4*>(vh + (int64_t)row * VC + 8 * ch);
-            dd = *reinterpret_cast<const u32x4*>(dh + (int64_t)row * VC + 8 * ch);
+        for (int bb = 0; bb < 4; ++bb) {
+            const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
+            pv[bb] = row < nv ? *reinterpret_cast<const u32x4*>(vh + (int64_t)row * VC + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+            pd[bb] = row < nv ? *reinterpret_cast<const u32x4*>(dh + (int64_t)row * VC + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
         }
-        lds_st<u32x4>(LV + img_chunk(row, ch), vv);
-        dor[bb] = dd;
-    }
-    if (tid < KC) s_z[tid] = S[(int64_t)tid * dva + VC];
-    // state fragments: for num, B[k = component 32 ks + 8 g + e][n = d_v 32 w + 16 t + r]; for dGamma_Q,
-    // B[k = d_v 32 ks + 8 g + e][n = component 32 w + 16 t + r]
-    bf16x8 snh[2][4], snl[2][4], sdh[2][4], sdl[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            float a[8], b[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = S[(int64_t)(32 * ks + 8 * g + e) * dva + 32 * w + 16 * t + r];
-            split_bf16x8(a, snh[t][ks], snl[t][ks]);
-            const float* p = S + (int64_t)(32 * w + 16 * t + r) * dva + 32 * ks + 8 * g;
-            const f32x4 p0 = *reinterpret_cast<const f32x4*>(p), p1 = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                b[e] = p0[e];
-                b[4 + e] = p1[e];
-            }
-            split_bf16x8(b, sdh[t][ks], sdl[t][ks]);
-        }
-    lds_barrier();
+    };
 
-    // ---- ac = tril(Gamma_Q Gamma_K^T), q tile w: image, HBM, row sums
-    {
-        f32x4 acc[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 ah = img_row(LQH, 16 * w + r, ks, g), al = img_row(LQL, 16 * w + r, ks, g);
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                if (kt > w) continue;
-                const bf16x8 bh_ = img_row(LKH, 16 * kt + r, ks, g), bl = img_row(LKL, 16 * kt + r, ks, g);
-                mma(acc[kt], al, bh_);
-                mma(acc[kt], ah, bl);
-                mma(acc[kt], ah, bh_);
-            }
-        }
-        float rsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int q = 16 * w + 4 * g + i, key = 16 * kt + r;
-                const float val = (kt <= w && key <= q) ? acc[kt][i] : 0.f;
-                rsum[i] += val;
-                const __bf16 hb = (__bf16)val;
-                lds_st<__bf16>(LMH + img_elem(q, key), hb);
-                lds_st<__bf16>(LML + img_elem(q, key), (__bf16)(val - (float)hb));
-                blk_ac[q * C + key] = val;
-            }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x = rsum[i];
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
-            if (r == 0) s_den[16 * w + 4 * g + i] = x;
-        }
-    }
-    lds_barrier();
+    fetch(c0);
+    for (int64_t c = c0; c < c1; ++c) {
+        const int64_t n0 = c * C;
+        const int nv = (int)(N - n0 < C ? N - n0 : C);   // rows of the chunk inside the sequence
+        float* blk_ac = ac_out + (bh * n_st + c) * C * C;
+        float* blk_mt = mt_out + (bh * n_st + c) * C * C;
+        if (c > c0) lds_barrier();   // every wave is done with the previous chunk's images
 
-    // ---- num (d_v columns 32 w .. + 31), den of q tile w
-    f32x4 num[4][2];
+        // ---- stage this chunk's operands
+        {
+            const int rl = lane >> 5, cl = lane & 31;
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) num[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-            const bf16x8 ah = img_row(LQH, 16 * qt + r, ks, g), al = img_row(LQL, 16 * qt + r, ks, g);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                mma(num[qt][t], al, snh[t][ks]);
-                mma(num[qt][t], ah, snl[t][ks]);
-                mma(num[qt][t], ah, snh[t][ks]);
+            for (int j = 0; j < 8; ++j) {
+                const int off = img_slot(16 * w + 2 * j + rl, cl);
+                bf16x4 hi, lo;
+                split4(pq[j], hi, lo);
+                lds_st<bf16x4>(LQH + off, hi);
+                lds_st<bf16x4>(LQL + off, lo);
+                split4(pk[j], hi, lo);
+                lds_st<bf16x4>(LKH + off, hi);
+                lds_st<bf16x4>(LKL + off, lo);
             }
         }
+        u32x4 dor[4];
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-        bf16x8 vb[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) vb[t] = img_tr(LV, 2 * w + t, ks2, lane);
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-            if (ks2 == 1 && qt < 2) continue;   // keys 32 .. 63 lie above those rows: ac = 0
-            const bf16x8 ah = img_row_perm(LMH, 16 * qt + r, ks2, g), al = img_row_perm(LML, 16 * qt + r, ks2, g);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                mma(num[qt][t], al, vb[t]);
-                mma(num[qt][t], ah, vb[t]);
-            }
+        for (int bb = 0; bb < 4; ++bb) {
+            lds_st<u32x4>(LV + img_chunk(16 * w + 4 * bb + (lane >> 4), lane & 15), pv[bb]);
+            dor[bb] = pd[bb];
         }
-    }
-    {
-        f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 ah = img_row(LQH, 16 * w + r, ks, g), al = img_row(LQL, 16 * w + r, ks, g);
-            float zv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) zv[e] = r == 0 ? s_z[32 * ks + 8 * g + e] : 0.f;
-            bf16x8 zh, zl;
-            split_bf16x8(zv, zh, zl);
-            mma(dacc, al, zh);
-            mma(dacc, ah, zl);
-            mma(dacc, ah, zh);
-        }
-        if (r == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s_den[16 * w + 4 * g + i] += dacc[i] + eps;
-        }
-    }
-    lds_barrier();   // den complete; ac no longer read
-
-    // ---- g, h: dO into the spare image, 1 / den, the wave's part of dO . num per row
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) lds_st<u32x4>(LMH + img_chunk(16 * w + 4 * bb + (lane >> 4), lane & 15), dor[bb]);
-    if (tid < C) s_inv[tid] = tid < nv ? 1.f / s_den[tid] : 0.f;   // rows past N: g = h = 0 (even with eps = 0)
-    lds_barrier();
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = 16 * qt + 4 * g + i;
-            const float inv = s_inv[q];
-            float d = 0.f;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int col = 32 * w + 16 * t + r;
-                const float dov = (float)lds_ld<__bf16>(LMH + img_elem(q, col));
-                d += num[qt][t][i] * inv * dov;
-            }
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) d += __shfl_xor(d, o, 64);
-            if (r == 0) s_part[w][q] = d;
-        }
-    lds_barrier();
-    if (tid < C) {
-        const float inv = s_inv[tid];
-        const float hv = -(s_part[0][tid] + s_part[1][tid] + s_part[2][tid] + s_part[3][tid]) * inv;
-        s_h[tid] = hv;
-        if (tid < nv) {
-            rs[(bh * N + n0 + tid) * 2] = inv;
-            rs[(bh * N + n0 + tid) * 2 + 1] = hv;
-        }
-    }
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-        const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
-        const float inv = s_inv[row];
-        const bf16x8 dv8 = __builtin_bit_cast(bf16x8, dor[bb]);
-        float gv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) gv[e] = (float)dv8[e] * inv;
-        bf16x8 hi, lo;
-        split_bf16x8(gv, hi, lo);
-        lds_st<bf16x8>(LGH + img_chunk(row, ch), hi);
-        lds_st<bf16x8>(LGL + img_chunk(row, ch), lo);
-    }
-    lds_barrier();   // g, h visible; dO no longer read
-
-    // ---- rt = Gamma_Q^T [g | h], components 32 w .. + 31 (tile 8: the h column)
-    {
-        float* rth = rt + (bh * n_st + c) * rec;
-        f32x4 racc[2][9];
+        // the state before this chunk, loaded now and split where it is used: for num (rows 32 ks + 8 g + e,
+        // column 32 w + 16 t + r), for dGamma_Q (row 32 w + 16 t + r, columns 32 ks + 8 g .. + 7), Z
+        const float* S = stt + (bh * n_st + c) * rec;
+        float psn[2][4][8];
+        f32x4 psd[2][4][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int vt = 0; vt < 9; ++vt) racc[t][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int tk = 0; tk < 2; ++tk) {
-            bf16x8 ah[2], al[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                ah[t] = img_tr(LQH, 2 * w + t, tk, lane);
-                al[t] = img_tr(LQL, 2 * w + t, tk, lane);
+                for (int e = 0; e < 8; ++e) psn[t][ks][e] = S[(int64_t)(32 * ks + 8 * g + e) * dva + 32 * w + 16 * t + r];
+                const float* p = S + (int64_t)(32 * w + 16 * t + r) * dva + 32 * ks + 8 * g;
+                psd[t][ks][0] = *reinterpret_cast<const f32x4*>(p);
+                psd[t][ks][1] = *reinterpret_cast<const f32x4*>(p + 4);
             }
+        const float pz = tid < KC ? S[(int64_t)tid * dva + VC] : 0.f;
+        if (c + 1 < c1) fetch(c + 1);
+        lds_barrier();
+
+        // ---- ac^T = Gamma_K Gamma_Q^T, q tile w: acc[kt] rows = keys 16 kt + 4 g + i, column = q 16 w + r
+        {
+            const int q = 16 * w + r;
+            f32x4 acc[4];
 #pragma unroll
-            for (int vt = 0; vt < 8; ++vt) {
-                const bf16x8 bh_ = img_tr(LGH, vt, tk, lane), bl = img_tr(LGL, vt, tk, lane);
+            for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    mma(racc[t][vt], al[t], bh_);
-                    mma(racc[t][vt], ah[t], bl);
-                    mma(racc[t][vt], ah[t], bh_);
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 bh_ = img_row(LQH, q, ks, g), bl = img_row(LQL, q, ks, g);
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    if (kt > w) continue;
+                    const bf16x8 ah = img_row(LKH, 16 * kt + r, ks, g), al = img_row(LKL, 16 * kt + r, ks, g);
+                    mma(acc[kt], al, bh_);
+                    mma(acc[kt], ah, bl);
+                    mma(acc[kt], ah, bh_);
                 }
             }
-            float hv[8];
+            float rsum = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) hv[e] = r == 0 ? s_h[32 * tk + 16 * (e >> 2) + 4 * g + (e & 3)] : 0.f;
-            bf16x8 hh, hl;
-            split_bf16x8(hv, hh, hl);
+            for (int kt = 0; kt < 4; ++kt) {
+                f32x4 val;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                mma(racc[t][8], al[t], hh);
-                mma(racc[t][8], ah[t], hl);
-                mma(racc[t][8], ah[t], hh);
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * kt + 4 * g + i;
+                    val[i] = (kt <= w && key <= q) ? acc[kt][i] : 0.f;
+                    rsum += val[i];
+                }
+                bf16x4 hi, lo;
+                split4(val, hi, lo);
+                lds_st<bf16x4>(LMH + img_slot(q, 4 * kt + g), hi);
+                lds_st<bf16x4>(LML + img_slot(q, 4 * kt + g), lo);
+                *reinterpret_cast<f32x4*>(blk_ac + q * C + 16 * kt + 4 * g) = val;
             }
+            rsum += __shfl_xor(rsum, 16, 64);
+            rsum += __shfl_xor(rsum, 32, 64);
+            if (g == 0) s_den[q] = rsum;
         }
+        if (tid < KC) s_z[tid] = pz;
+        lds_barrier();
+        bf16x8 snh[2][4], snl[2][4];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int comp = 32 * w + 16 * t + 4 * g + i;
-#pragma unroll
-                for (int vt = 0; vt < 8; ++vt) rth[(int64_t)comp * dva + 16 * vt + r] = racc[t][vt][i];
-                if (r < dva - VC) rth[(int64_t)comp * dva + VC + r] = racc[t][8][i];
-            }
-    }
+            for (int ks = 0; ks < 4; ++ks) split_bf16x8(psn[t][ks], snh[t][ks], snl[t][ks]);
 
-    // ---- mt = tril([g | h] [V | 1]^T), q tile w: image, HBM
-    {
-        f32x4 macc[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) macc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 ah = img_row(LGH, 16 * w + r, ks, g), al = img_row(LGL, 16 * w + r, ks, g);
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                if (kt > w) continue;
-                const bf16x8 vb = img_row(LV, 16 * kt + r, ks, g);
-                mma(macc[kt], al, vb);
-                mma(macc[kt], ah, vb);
-            }
-        }
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int q = 16 * w + 4 * g + i, key = 16 * kt + r;
-                const float val = (kt <= w && key <= q && key < nv) ? macc[kt][i] + s_h[q] : 0.f;
-                const __bf16 hb = (__bf16)val;
-                lds_st<__bf16>(LMH + img_elem(q, key), hb);
-                lds_st<__bf16>(LML + img_elem(q, key), (__bf16)(val - (float)hb));
-                blk_mt[q * C + key] = val;
-            }
-    }
-    lds_barrier();
-
-    // ---- dGamma_Q = [g | h] S^T + mt Gamma_K, components 32 w .. + 31
-    {
-        f32x4 dacc[4][2];
+        // ---- num (d_v columns 32 w .. + 31: rows q 16 qt + 4 g + i), den of q tile w
+        f32x4 num[4][2];
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) dacc[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < 2; ++t) num[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) {
-                const bf16x8 ah = img_row(LGH, 16 * qt + r, ks, g), al = img_row(LGL, 16 * qt + r, ks, g);
+                const bf16x8 ah = img_row(LQH, 16 * qt + r, ks, g), al = img_row(LQL, 16 * qt + r, ks, g);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    mma(dacc[qt][t], al, sdh[t][ks]);
-                    mma(dacc[qt][t], ah, sdl[t][ks]);
-                    mma(dacc[qt][t], ah, sdh[t][ks]);
+                    mma(num[qt][t], al, snh[t][ks]);
+                    mma(num[qt][t], ah, snl[t][ks]);
+                    mma(num[qt][t], ah, snh[t][ks]);
                 }
             }
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
-            bf16x8 bkh[2], bkl[2];
+            bf16x8 vb[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                bkh[t] = img_tr(LKH, 2 * w + t, ks2, lane);
-                bkl[t] = img_tr(LKL, 2 * w + t, ks2, lane);
-            }
+            for (int t = 0; t < 2; ++t) vb[t] = img_tr(LV, 2 * w + t, ks2, lane);
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) {
-                if (ks2 == 1 && qt < 2) continue;   // mt = 0 above the diagonal
+                if (ks2 == 1 && qt < 2) continue;   // keys 32 .. 63 lie above those rows: ac = 0
                 const bf16x8 ah = img_row_perm(LMH, 16 * qt + r, ks2, g), al = img_row_perm(LML, 16 * qt + r, ks2, g);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    mma(dacc[qt][t], al, bkh[t]);
-                    mma(dacc[qt][t], ah, bkl[t]);
-                    mma(dacc[qt][t], ah, bkh[t]);
+                    mma(num[qt][t], al, vb[t]);
+                    mma(num[qt][t], ah, vb[t]);
                 }
             }
         }
-        float* dqh = dgq + (bh * N + n0) * KC;
+        {
+            f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 ah = img_row(LQH, 16 * w + r, ks, g), al = img_row(LQL, 16 * w + r, ks, g);
+                float zv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) zv[e] = r == 0 ? s_z[32 * ks + 8 * g + e] : 0.f;
+                bf16x8 zh, zl;
+                split_bf16x8(zv, zh, zl);
+                mma(dacc, al, zh);
+                mma(dacc, ah, zl);
+                mma(dacc, ah, zh);
+            }
+            if (r == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_den[16 * w + 4 * g + i] += dacc[i] + eps;
+            }
+        }
+        lds_barrier();   // den complete; ac no longer read
+
+        // ---- g, h: dO into the spare image, 1 / den, the wave's part of dO . num per row
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) lds_st<u32x4>(LMH + img_chunk(16 * w + 4 * bb + (lane >> 4), lane & 15), dor[bb]);
+        if (tid < C) s_inv[tid] = tid < nv ? 1.f / s_den[tid] : 0.f;   // rows past N: g = h = 0 (even with eps = 0)
+        lds_barrier();
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int i = 0; i < 4; ++i) {
+                const int q = 16 * qt + 4 * g + i;
+                const float inv = s_inv[q];
+                float d = 0.f;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const float dov = (float)lds_ld<__bf16>(LMH + img_elem(q, 32 * w + 16 * t + r));
+                    d += num[qt][t][i] * inv * dov;
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) d += __shfl_xor(d, o, 64);
+                if (r == 0) s_part[w][q] = d;
+            }
+        lds_barrier();
+        if (tid < C) {
+            const float inv = s_inv[tid];
+            const float hv = -(s_part[0][tid] + s_part[1][tid] + s_part[2][tid] + s_part[3][tid]) * inv;
+            s_h[tid] = hv;
+            if (tid < nv) {
+                rs[(bh * N + n0 + tid) * 2] = inv;
+                rs[(bh * N + n0 + tid) * 2 + 1] = hv;
+            }
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
+            const float inv = s_inv[row];
+            const bf16x8 dv8 = __builtin_bit_cast(bf16x8, dor[bb]);
+            float gv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gv[e] = (float)dv8[e] * inv;
+            bf16x8 hi, lo;
+            split_bf16x8(gv, hi, lo);
+            lds_st<bf16x8>(LGH + img_chunk(row, ch), hi);
+            lds_st<bf16x8>(LGL + img_chunk(row, ch), lo);
+        }
+        lds_barrier();   // g, h visible; dO no longer read
+
+        // ---- rt^T = [g | h]^T Gamma_Q: racc[vt][t] rows = d_v 16 vt + 4 g + i (vt 8: the h row 128 and
+        // the zero padding), column = component 32 w + 16 t + r
+        {
+            float* rth = rt + (bh * n_st + c) * rec;
+            f32x4 racc[9][2];
+#pragma unroll
+            for (int vt = 0; vt < 9; ++vt)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) racc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int tk = 0; tk < 2; ++tk) {
+                bf16x8 bqh[2], bql[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    bqh[t] = img_tr(LQH, 2 * w + t, tk, lane);
+                    bql[t] = img_tr(LQL, 2 * w + t, tk, lane);
+                }
+#pragma unroll
+                for (int vt = 0; vt < 8; ++vt) {
+                    const bf16x8 ah = img_tr(LGH, vt, tk, lane), al = img_tr(LGL, vt, tk, lane);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        mma(racc[vt][t], al, bqh[t]);
+                        mma(racc[vt][t], ah, bql[t]);
+                        mma(racc[vt][t], ah, bqh[t]);
+                    }
+                }
+                float hv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) hv[e] = r == 0 ? s_h[32 * tk + 16 * (e >> 2) + 4 * g + (e & 3)] : 0.f;
+                bf16x8 hh, hl;
+                split_bf16x8(hv, hh, hl);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    mma(racc[8][t], hl, bqh[t]);
+                    mma(racc[8][t], hh, bql[t]);
+                    mma(racc[8][t], hh, bqh[t]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                float* row = rth + (int64_t)(32 * w + 16 * t + r) * dva;
+#pragma unroll
+                for (int vt = 0; vt < 8; ++vt) *reinterpret_cast<f32x4*>(row + 16 * vt + 4 * g) = racc[vt][t];
+                if (g == 0) *reinterpret_cast<f32x4*>(row + VC) = racc[8][t];
+            }
+        }
+
+        // ---- mt^T = [V | 1] [g | h]^T, q tile w: macc[kt] rows = keys 16 kt + 4 g + i, column = q 16 w + r
+        {
+            const int q = 16 * w + r;
+            const float hq = s_h[q];
+            f32x4 macc[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) macc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 bh_ = img_row(LGH, q, ks, g), bl = img_row(LGL, q, ks, g);
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    if (kt > w) continue;
+                    const bf16x8 av = img_row(LV, 16 * kt + r, ks, g);
+                    mma(macc[kt], av, bl);
+                    mma(macc[kt], av, bh_);
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                f32x4 val;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int q = 16 * qt + 4 * g + i, comp = 32 * w + 16 * t + r;
-                    if (q < nv) dqh[(int64_t)q * KC + comp] = dacc[qt][t][i] + s_h[q] * s_z[comp];
+                    const int key = 16 * kt + 4 * g + i;
+                    val[i] = (kt <= w && key <= q && key < nv) ? macc[kt][i] + hq : 0.f;
                 }
+                bf16x4 hi, lo;
+                split4(val, hi, lo);
+                lds_st<bf16x4>(LMH + img_slot(q, 4 * kt + g), hi);
+                lds_st<bf16x4>(LML + img_slot(q, 4 * kt + g), lo);
+                *reinterpret_cast<f32x4*>(blk_mt + q * C + 16 * kt + 4 * g) = val;
+            }
+        }
+        lds_barrier();
+
+        // ---- dGamma_Q^T = S [g | h]^T + Gamma_K^T mt^T: dacc[t][qt] rows = components 32 w + 16 t + 4 g + i,
+        // column = q 16 qt + r
+        {
+            bf16x8 sdh[2][4], sdl[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    float b[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        b[e] = psd[t][ks][0][e];
+                        b[4 + e] = psd[t][ks][1][e];
+                    }
+                    split_bf16x8(b, sdh[t][ks], sdl[t][ks]);
+                }
+            f32x4 dacc[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int qt = 0; qt < 4; ++qt) dacc[t][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int qt = 0; qt < 4; ++qt) {
+                    const bf16x8 bh_ = img_row(LGH, 16 * qt + r, ks, g), bl = img_row(LGL, 16 * qt + r, ks, g);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        mma(dacc[t][qt], sdl[t][ks], bh_);
+                        mma(dacc[t][qt], sdh[t][ks], bl);
+                        mma(dacc[t][qt], sdh[t][ks], bh_);
+                    }
+                }
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
+                bf16x8 akh[2], akl[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    akh[t] = img_tr(LKH, 2 * w + t, ks2, lane);
+                    akl[t] = img_tr(LKL, 2 * w + t, ks2, lane);
+                }
+#pragma unroll
+                for (int qt = 0; qt < 4; ++qt) {
+                    if (ks2 == 1 && qt < 2) continue;   // mt = 0 above the diagonal
+                    const bf16x8 bh_ = img_row_perm(LMH, 16 * qt + r, ks2, g), bl = img_row_perm(LML, 16 * qt + r, ks2, g);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        mma(dacc[t][qt], akl[t], bh_);
+                        mma(dacc[t][qt], akh[t], bl);
+                        mma(dacc[t][qt], akh[t], bh_);
+                    }
+                }
+            }
+            float* dqh = dgq + (bh * N + n0) * KC;
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt) {
+                const int q = 16 * qt + r;
+                const float hq = s_h[q];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int comp0 = 32 * w + 16 * t + 4 * g;
+                    f32x4 val;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) val[i] = dacc[t][qt][i] + hq * s_z[comp0 + i];
+                    if (q < nv) *reinterpret_cast<f32x4*>(dqh + (int64_t)q * KC + comp0) = val;
+                }
+            }
+        }
     }
 }
 
@@ -1698,9 +1739,13 @@ bool bwd_chunk_q_supported(int K, int d_v, bool f32) { return !f32 && K == 128 &
 bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const void* dout, const float* stt, float* rs,
                         float* rt, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st, int K,
                         int d_v, int dva, float eps, hipStream_t s) {
-    if (!bwd_chunk_q_supported(K, d_v, false) || dva < d_v + 1 || dva % 4 != 0) return false;
-    bwd_chunk_q_kernel<128, 128><<<dim3((unsigned)(BH * n_st)), dim3(256), 0, s>>>(gq, gk, v, dout, stt, rs, rt, ac, mt,
-                                                                                  dgq, N, n_st, dva, eps);
+    if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4) return false;
+    // chunks per workgroup: enough workgroups for every compute unit several times over
+    int per = 4;
+    while (per > 1 && BH * ((n_st + per - 1) / per) < 1024) per /= 2;
+    const int64_t groups = (n_st + per - 1) / per;
+    bwd_chunk_q_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gq, gk, v, dout, stt, rs, rt, ac,
+                                                                                    mt, dgq, N, n_st, per, dva, eps);
     return true;
 }
 
