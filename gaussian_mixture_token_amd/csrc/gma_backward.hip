@@ -1148,8 +1148,8 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
     for (int64_t c = c0; c < c1; ++c) {
         const int64_t n0 = c * C;
         const int nv = (int)(N - n0 < C ? N - n0 : C);   // rows of the chunk inside the sequence
-        float* blk_ac = ac_out + (bh * n_st + c) * C * C;
-        float* blk_mt = mt_out + (bh * n_st + c) * C * C;
+        float* blk_ac = ac_out ? ac_out + (bh * n_st + c) * C * C : nullptr;   // null: the blocks are not stored
+        float* blk_mt = mt_out ? mt_out + (bh * n_st + c) * C * C : nullptr;
         if (c > c0) lds_barrier();   // every wave is done with the previous chunk's images
 
         // ---- stage this chunk's operands
@@ -1224,7 +1224,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 split4(val, hi, lo);
                 lds_st<bf16x4>(LMH + img_slot(q, 4 * kt + g), hi);
                 lds_st<bf16x4>(LML + img_slot(q, 4 * kt + g), lo);
-                *reinterpret_cast<f32x4*>(blk_ac + q * C + 16 * kt + 4 * g) = val;
+                if (ac_out) *reinterpret_cast<f32x4*>(blk_ac + q * C + 16 * kt + 4 * g) = val;
             }
             rsum += __shfl_xor(rsum, 16, 64);
             rsum += __shfl_xor(rsum, 32, 64);
@@ -1417,7 +1417,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 split4(val, hi, lo);
                 lds_st<bf16x4>(LMH + img_slot(q, 4 * kt + g), hi);
                 lds_st<bf16x4>(LML + img_slot(q, 4 * kt + g), lo);
-                *reinterpret_cast<f32x4*>(blk_mt + q * C + 16 * kt + 4 * g) = val;
+                if (mt_out) *reinterpret_cast<f32x4*>(blk_mt + q * C + 16 * kt + 4 * g) = val;
             }
         }
         lds_barrier();
@@ -1487,6 +1487,332 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
 #pragma unroll
                     for (int i = 0; i < 4; ++i) val[i] = dacc[t][qt][i] + hq * s_z[comp0 + i];
                     if (q < nv) *reinterpret_cast<f32x4*>(dqh + (int64_t)q * KC + comp0) = val;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------- fused chunk, key side
+// The key-side chunk work of the causal backward in one kernel (bf16 storage, K = d_v = 128).  From the
+// recomputed posteriors, V, dO, the per-row pairs rs = (1 / den, h) and the state after the chunk
+// R = [Rv | r] (the exclusive suffix over chunks of Gamma_Q^T [g | h]), per chunk of 64 tokens:
+//   ac = tril(Gamma_Q Gamma_K^T),  mt = tril([g | h] [V | 1]^T)      (recomputed, never stored)
+//   dV       = Gamma_K Rv + ac^T g
+//   dGamma_K = [V | 1] R^T + mt^T Gamma_Q
+// Layout and work split follow the query-side kernel: a workgroup walks `per` consecutive chunks of one
+// (batch, head) with the next chunk's token operands loaded ahead; Gamma_Q, Gamma_K, g and the 64 x 64
+// blocks in LDS as bf16 hi + lo images, V exact; R from HBM into split fragments (wave w: d_v columns
+// 32 w .. + 31 for dV, components 32 w .. + 31 for dGamma_K); both outputs formed transposed so that
+// each lane stores contiguous bytes.
+template <int KC, int VC>
+__global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const float* gk, const void* v,
+                                                          const void* dout, const float* rs, const float* rt,
+                                                          float* dgk, void* dv, int64_t N, int64_t n_st, int per,
+                                                          int dva) {
+    static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
+    constexpr int C = 64;
+    constexpr int IMG = C * 256;
+    __shared__ __attribute__((aligned(16))) char s_q[2 * IMG];   // Gamma_Q hi, lo
+    __shared__ __attribute__((aligned(16))) char s_k[2 * IMG];   // Gamma_K hi, lo
+    __shared__ __attribute__((aligned(16))) char s_v[IMG];       // V
+    __shared__ __attribute__((aligned(16))) char s_g[2 * IMG];   // g hi, lo
+    __shared__ __attribute__((aligned(16))) char s_m[2 * IMG];   // ac hi, lo; then mt hi, lo
+    __shared__ float s_h[C];
+    lds_char* const LQH = (lds_char*)s_q;
+    lds_char* const LQL = LQH + IMG;
+    lds_char* const LKH = (lds_char*)s_k;
+    lds_char* const LKL = LKH + IMG;
+    lds_char* const LV = (lds_char*)s_v;
+    lds_char* const LGH = (lds_char*)s_g;
+    lds_char* const LGL = LGH + IMG;
+    lds_char* const LMH = (lds_char*)s_m;
+    lds_char* const LML = LMH + IMG;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t groups = (n_st + per - 1) / per;
+    const int64_t bh = blockIdx.x / groups;
+    const int64_t c0 = (blockIdx.x % groups) * per;
+    const int64_t c1 = c0 + per < n_st ? c0 + per : n_st;
+    const int64_t rec = (int64_t)KC * dva;
+
+    // token operands of one chunk, loaded a chunk ahead (rows as in the query-side kernel); rs of the
+    // V / dO rows
+    f32x4 pq[8], pk[8];
+    u32x4 pv[4], pd[4];
+    float pr0[4], pr1[4];
+    auto fetch = [&](int64_t c) {
+        const int64_t n0 = c * C;
+        const int nv = (int)(N - n0 < C ? N - n0 : C);
+        const float* gqh = gq + (bh * N + n0) * KC;
+        const float* gkh = gk + (bh * N + n0) * KC;
+        const uint16_t* vh = reinterpret_cast<const uint16_t*>(v) + (bh * N + n0) * VC;
+        const uint16_t* dh = reinterpret_cast<const uint16_t*>(dout) + (bh * N + n0) * VC;
+        const int rl = lane >> 5, cl = lane & 31;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = 16 * w + 2 * j + rl;
+            pq[j] = row < nv ? *reinterpret_cast<const f32x4*>(gqh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
+            pk[j] = row < nv ? *reinterpret_cast<const f32x4*>(gkh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
+            const bool ok = row < nv;
+            pv[bb] = ok ? *reinterpret_cast<const u32x4*>(vh + (int64_t)row * VC + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+            pd[bb] = ok ? *reinterpret_cast<const u32x4*>(dh + (int64_t)row * VC + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+            pr0[bb] = ok ? rs[(bh * N + n0 + row) * 2] : 0.f;
+            pr1[bb] = ok ? rs[(bh * N + n0 + row) * 2 + 1] : 0.f;
+        }
+    };
+
+    fetch(c0);
+    for (int64_t c = c0; c < c1; ++c) {
+        const int64_t n0 = c * C;
+        const int nv = (int)(N - n0 < C ? N - n0 : C);
+        if (c > c0) lds_barrier();   // every wave is done with the previous chunk's images
+
+        // ---- stage: Gamma_Q, Gamma_K, V, g = dO / den, h
+        {
+            const int rl = lane >> 5, cl = lane & 31;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int off = img_slot(16 * w + 2 * j + rl, cl);
+                bf16x4 hi, lo;
+                split4(pq[j], hi, lo);
+                lds_st<bf16x4>(LQH + off, hi);
+                lds_st<bf16x4>(LQL + off, lo);
+                split4(pk[j], hi, lo);
+                lds_st<bf16x4>(LKH + off, hi);
+                lds_st<bf16x4>(LKL + off, lo);
+            }
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
+            lds_st<u32x4>(LV + img_chunk(row, ch), pv[bb]);
+            const bf16x8 dv8 = __builtin_bit_cast(bf16x8, pd[bb]);
+            float gv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gv[e] = (float)dv8[e] * pr0[bb];
+            bf16x8 hi, lo;
+            split_bf16x8(gv, hi, lo);
+            lds_st<bf16x8>(LGH + img_chunk(row, ch), hi);
+            lds_st<bf16x8>(LGL + img_chunk(row, ch), lo);
+            if (ch == 0) s_h[row] = pr1[bb];
+        }
+        // the state after this chunk, loaded now and split where it is used: for dV (rows 32 ks + 8 g + e,
+        // column 32 w + 16 t + r), for dGamma_K (row 32 w + 16 t + r, columns 32 ks + 8 g .. + 7, and the r
+        // column of rows 32 w + 16 t + 4 g + i)
+        const float* R = rt + (bh * n_st + c) * rec;
+        float prn[2][4][8];
+        f32x4 prd[2][4][2];
+        float prr[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) prn[t][ks][e] = R[(int64_t)(32 * ks + 8 * g + e) * dva + 32 * w + 16 * t + r];
+                const float* p = R + (int64_t)(32 * w + 16 * t + r) * dva + 32 * ks + 8 * g;
+                prd[t][ks][0] = *reinterpret_cast<const f32x4*>(p);
+                prd[t][ks][1] = *reinterpret_cast<const f32x4*>(p + 4);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) prr[t][i] = R[(int64_t)(32 * w + 16 * t + 4 * g + i) * dva + VC];
+        }
+        if (c + 1 < c1) fetch(c + 1);
+        lds_barrier();
+
+        // ---- ac^T = Gamma_K Gamma_Q^T, q tile w, into the block image (rows q)
+        {
+            const int q = 16 * w + r;
+            f32x4 acc[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 bh_ = img_row(LQH, q, ks, g), bl = img_row(LQL, q, ks, g);
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    if (kt > w) continue;
+                    const bf16x8 ah = img_row(LKH, 16 * kt + r, ks, g), al = img_row(LKL, 16 * kt + r, ks, g);
+                    mma(acc[kt], al, bh_);
+                    mma(acc[kt], ah, bl);
+                    mma(acc[kt], ah, bh_);
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                f32x4 val;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * kt + 4 * g + i;
+                    val[i] = (kt <= w && key <= q) ? acc[kt][i] : 0.f;
+                }
+                bf16x4 hi, lo;
+                split4(val, hi, lo);
+                lds_st<bf16x4>(LMH + img_slot(q, 4 * kt + g), hi);
+                lds_st<bf16x4>(LML + img_slot(q, 4 * kt + g), lo);
+            }
+        }
+        lds_barrier();
+
+        // ---- dV^T = Rv^T Gamma_K^T + g^T ac: vacc[t][kt] rows = d_v 32 w + 16 t + 4 g + i, column = key 16 kt + r
+        {
+            bf16x8 anh[2][4], anl[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) split_bf16x8(prn[t][ks], anh[t][ks], anl[t][ks]);
+            f32x4 vacc[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) vacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const bf16x8 bh_ = img_row(LKH, 16 * kt + r, ks, g), bl = img_row(LKL, 16 * kt + r, ks, g);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        mma(vacc[t][kt], anl[t][ks], bh_);
+                        mma(vacc[t][kt], anh[t][ks], bl);
+                        mma(vacc[t][kt], anh[t][ks], bh_);
+                    }
+                }
+#pragma unroll
+            for (int tk = 0; tk < 2; ++tk) {
+                bf16x8 agh[2], agl[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    agh[t] = img_tr(LGH, 2 * w + t, tk, lane);
+                    agl[t] = img_tr(LGL, 2 * w + t, tk, lane);
+                }
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    if (tk == 0 && kt >= 2) continue;   // queries 0 .. 31 see no key of these tiles
+                    const bf16x8 bh_ = img_tr(LMH, kt, tk, lane), bl = img_tr(LML, kt, tk, lane);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        mma(vacc[t][kt], agl[t], bh_);
+                        mma(vacc[t][kt], agh[t], bl);
+                        mma(vacc[t][kt], agh[t], bh_);
+                    }
+                }
+            }
+            uint16_t* dvh = reinterpret_cast<uint16_t*>(dv) + (bh * N + n0) * VC;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const int key = 16 * kt + r;
+                if (key >= nv) continue;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    *reinterpret_cast<bf16x4*>(dvh + (int64_t)key * VC + 32 * w + 16 * t + 4 * g) = pack4(vacc[t][kt]);
+            }
+        }
+        lds_barrier();   // ac no longer read
+
+        // ---- mt^T = [V | 1] [g | h]^T, q tile w, into the block image (rows q)
+        {
+            const int q = 16 * w + r;
+            const float hq = s_h[q];
+            f32x4 macc[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) macc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 bh_ = img_row(LGH, q, ks, g), bl = img_row(LGL, q, ks, g);
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    if (kt > w) continue;
+                    const bf16x8 av = img_row(LV, 16 * kt + r, ks, g);
+                    mma(macc[kt], av, bl);
+                    mma(macc[kt], av, bh_);
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                f32x4 val;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * kt + 4 * g + i;
+                    val[i] = (kt <= w && key <= q && key < nv) ? macc[kt][i] + hq : 0.f;
+                }
+                bf16x4 hi, lo;
+                split4(val, hi, lo);
+                lds_st<bf16x4>(LMH + img_slot(q, 4 * kt + g), hi);
+                lds_st<bf16x4>(LML + img_slot(q, 4 * kt + g), lo);
+            }
+        }
+        lds_barrier();
+
+        // ---- dGamma_K^T = R [V | 1]^T + Gamma_Q^T mt: kacc[t][kt] rows = components 32 w + 16 t + 4 g + i,
+        // column = key 16 kt + r
+        {
+            bf16x8 adh[2][4], adl[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    float b[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        b[e] = prd[t][ks][0][e];
+                        b[4 + e] = prd[t][ks][1][e];
+                    }
+                    split_bf16x8(b, adh[t][ks], adl[t][ks]);
+                }
+            f32x4 kacc[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) kacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const bf16x8 bv = img_row(LV, 16 * kt + r, ks, g);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        mma(kacc[t][kt], adl[t][ks], bv);
+                        mma(kacc[t][kt], adh[t][ks], bv);
+                    }
+                }
+#pragma unroll
+            for (int tk = 0; tk < 2; ++tk) {
+                bf16x8 aqh[2], aql[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    aqh[t] = img_tr(LQH, 2 * w + t, tk, lane);
+                    aql[t] = img_tr(LQL, 2 * w + t, tk, lane);
+                }
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    if (tk == 0 && kt >= 2) continue;   // queries 0 .. 31 see no key of these tiles
+                    const bf16x8 bh_ = img_tr(LMH, kt, tk, lane), bl = img_tr(LML, kt, tk, lane);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        mma(kacc[t][kt], aql[t], bh_);
+                        mma(kacc[t][kt], aqh[t], bl);
+                        mma(kacc[t][kt], aqh[t], bh_);
+                    }
+                }
+            }
+            float* dkh = dgk + (bh * N + n0) * KC;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const int key = 16 * kt + r;
+                if (key >= nv) continue;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x4 val;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) val[i] = kacc[t][kt][i] + prr[t][i];
+                    *reinterpret_cast<f32x4*>(dkh + (int64_t)key * KC + 32 * w + 16 * t + 4 * g) = val;
                 }
             }
         }
@@ -1755,6 +2081,18 @@ int bwd_fused_rows_seg(int64_t BH, int64_t N, int min_seg) {
     int seg = 4096;
     while (seg / 2 >= min_seg && BH * ((N + seg - 1) / seg) < 256) seg /= 2;
     return seg < min_seg ? min_seg : seg;
+}
+
+bool launch_bwd_chunk_k(const float* gq, const float* gk, const void* v, const void* dout, const float* rs,
+                        const float* rt, float* dgk, void* dv, int64_t BH, int64_t N, int64_t n_st, int K, int d_v,
+                        int dva, hipStream_t s) {
+    if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4) return false;
+    int per = 4;
+    while (per > 1 && BH * ((n_st + per - 1) / per) < 1024) per /= 2;
+    const int64_t groups = (n_st + per - 1) / per;
+    bwd_chunk_k_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gq, gk, v, dout, rs, rt, dgk, dv, N,
+                                                                                    n_st, per, dva);
+    return true;
 }
 
 bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* x, const float* mw, void* dx, float* gp,

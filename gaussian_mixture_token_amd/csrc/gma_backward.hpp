@@ -89,14 +89,20 @@ void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream
 // The query-side chunk work of the causal backward in one kernel (bf16 storage, K = d_v = 128;
 // bwd_chunk_q_supported), one workgroup per (batch, head, chunk of 64 tokens): from gq, gk [BH, N, K],
 // v, dout [BH, N, d_v] bf16 and the exclusive prefix states stt [BH, n_st, K, dva] it writes rs
-// [BH N, 2] = (1 / den, h), rt [BH, n_st, K, dva] = Gamma_Q^T [g | h] per chunk (zero padded),
-// ac = tril(Gamma_Q Gamma_K^T) and mt = tril([g | h] [V | 1]^T) [BH, n_st, 64, 64], and dgq =
-// [g | h] S^T + mt Gamma_K [BH, N, K].  Rows of v and dout 16-byte aligned.  false: no kernel for
-// this shape.
+// [BH N, 2] = (1 / den, h), rt [BH, n_st, K, dva] = Gamma_Q^T [g | h] per chunk (zero padded), dgq =
+// [g | h] S^T + mt Gamma_K [BH, N, K] and, where ac and mt are not null, ac = tril(Gamma_Q Gamma_K^T)
+// and mt = tril([g | h] [V | 1]^T) [BH, n_st, 64, 64].  dva = d_v + 4; rows of v and dout 16-byte
+// aligned.  false: no kernel for this shape.
 bool bwd_chunk_q_supported(int K, int d_v, bool f32);
 bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const void* dout, const float* stt, float* rs,
                         float* rt, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st, int K,
                         int d_v, int dva, float eps, hipStream_t s);
+// Its key-side counterpart (the same shapes): from gq, gk, v, dout, rs and the exclusive suffix states
+// rt [BH, n_st, K, dva] it writes dgk = [V | 1] R^T + mt^T Gamma_Q [BH, N, K] and dv = Gamma_K Rv +
+// ac^T g [BH, N, d_v] bf16, recomputing ac and mt.
+bool launch_bwd_chunk_k(const float* gq, const float* gk, const void* v, const void* dout, const float* rs,
+                        const float* rt, float* dgk, void* dv, int64_t BH, int64_t N, int64_t n_st, int K, int d_v,
+                        int dva, hipStream_t s);
 
 // Posterior gradient, routing-input gradient and parameter partials of one side in one kernel
 // (bf16 storage, K = d_r = 128; bwd_fused_rows_supported): from gamma and dgamma [BH, N, K] fp32, the

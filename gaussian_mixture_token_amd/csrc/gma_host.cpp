@@ -1246,11 +1246,13 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, causal ? 0 : 2, s); }));
     // Causal bf16 at K = d_v = 128: one fused kernel per chunk does the read phase, the chunk terms of the
     // suffix sums and dGamma_Q (and writes the intra-chunk blocks ac, mt for the key side)
-    const bool qfused = causal && bwd_chunk_q_supported(K, d_v, f32) && !misaligned(v, 16) && !misaligned(dout, 16);
+    const bool qfused = causal && bwd_chunk_q_supported(K, d_v, f32) && !misaligned(v, 16) && !misaligned(dout, 16) &&
+                        !misaligned(dv, 16) && dva == d_v + 4;
     if (qfused) {
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            ok = launch_bwd_chunk_q(gq, gk, v, dout, stt, rs, rt, ac, mt, dgq, BH, N, b.n_st, K, d_v, dva, b.eps, s);
+            ok = launch_bwd_chunk_q(gq, gk, v, dout, stt, rs, rt, nullptr, nullptr, dgq, BH, N, b.n_st, K, d_v, dva,
+                                    b.eps, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused query-side chunk kernel for this shape");
         GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(rt, BH, b.n_st, rec, 1, s); }));
@@ -1273,16 +1275,25 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
             GMA_TRY(gemm(sq(mt), false, tok(gk, K), false, tok(dgq, K), dgq, false, C, K, C, TM | TK, 0, dgq, false));
         }
     }
-    // dGamma_K = [V | 1] R^T (+ the same intra-chunk block transposed, times Gamma_Q)
-    GMA_TRY(gemm(vv, false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false, gen_v));
-    if (causal)
-        GMA_TRY(gemm(sq(mt), true, tok(gq, K), false, tok(dgk, K), dgk, false, C, K, C, TM | TK, 0, dgk, false));
-    // dV = Gamma_K R (+ tril(Gamma_Q Gamma_K^T)^T g), in the storage dtype
-    if (causal)
-        GMA_TRY(gemm(sq(ac), true, ghv, false, tok(dvt, d_v), dvt, false, C, d_v, C, TM | TK, 0, nullptr, false,
-                     BwdGen{}, gen_gh));
-    GMA_TRY(gemm(tok(gk, K), false, cur_st(rt), false, tok(nullptr, d_v), dv, !f32, C, d_v, K, TM, 0,
-                 causal ? dvt : nullptr, false));
+    if (qfused) {
+        // the key-side counterpart: dGamma_K and dV per chunk (ac and mt recomputed)
+        bool ok = true;
+        GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
+            ok = launch_bwd_chunk_k(gq, gk, v, dout, rs, rt, dgk, dv, BH, N, b.n_st, K, d_v, dva, s);
+        }));
+        if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused key-side chunk kernel for this shape");
+    } else {
+        // dGamma_K = [V | 1] R^T (+ the same intra-chunk block transposed, times Gamma_Q)
+        GMA_TRY(gemm(vv, false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false, gen_v));
+        if (causal)
+            GMA_TRY(gemm(sq(mt), true, tok(gq, K), false, tok(dgk, K), dgk, false, C, K, C, TM | TK, 0, dgk, false));
+        // dV = Gamma_K R (+ tril(Gamma_Q Gamma_K^T)^T g), in the storage dtype
+        if (causal)
+            GMA_TRY(gemm(sq(ac), true, ghv, false, tok(dvt, d_v), dvt, false, C, d_v, C, TM | TK, 0, nullptr, false,
+                         BwdGen{}, gen_gh));
+        GMA_TRY(gemm(tok(gk, K), false, cur_st(rt), false, tok(nullptr, d_v), dv, !f32, C, d_v, K, TM, 0,
+                     causal ? dvt : nullptr, false));
+    }
     // posterior gradients, then per side the routing-input gradient and the parameter partials: one
     // fused kernel per side where there is one for the shape (dl then stays on chip)
     // The partials buffer holds n_sg segments of kBwdSeg tokens per side: the fused segments are no
