@@ -568,7 +568,9 @@ __global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, cons
 // tile, five v_mfma_f32_16x16x32_bf16.  The head's operand fragments (bwd_frag_kernel, split) stay in
 // LDS for the workgroup, which walks `rows` consecutive rows of one (batch, head) in blocks of 64, wave w
 // rows 16 w .. 16 w + 15 of a block (lane (r, g): row r, dims 8 g .. 8 g + 7 of a step); the next
-// block's x is loaded during the current block.  Softmax as in bwd_gamma_mfma_kernel, in fp32.
+// block's x is loaded during the current block.  The product is formed transposed (coefficient fragments
+// as A, the rows as B), so that each lane ends with four consecutive components of one row: the softmax
+// runs in fp32 in the lane and across the four lane groups, and rows are stored 16 bytes per lane.
 template <int KT, int SMAX>
 __global__ void __launch_bounds__(256) bwd_gamma_split_kernel(const uint16_t* x, const bf16x8* fr, const double* cq,
                                                               float* gamma, int64_t N, int H, int K, int d_r,
@@ -584,9 +586,12 @@ __global__ void __launch_bounds__(256) bwd_gamma_split_kernel(const uint16_t* x,
     const int r = lane & 15, g = lane >> 4;
     const bf16x8* fh = fr + (int64_t)h * S * KT * 4 * 64;
     for (int i = tid; i < S * KT * 4 * 64; i += 256) s_f[i] = fh[i];
-    float cr[KT];
+    // constants of the components this lane's accumulator rows hold: 16 kt + 4 g + i
+    float cr[KT][4];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) cr[kt] = (float)cq[(int64_t)h * 16 * KT + 16 * kt + r];
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cr[kt][i] = (float)cq[(int64_t)h * 16 * KT + 16 * kt + 4 * g + i];
     __syncthreads();
     const uint16_t* xh = x + bh * N * d_r;
     float* gh = gamma + bh * N * K;
@@ -619,43 +624,53 @@ __global__ void __launch_bounds__(256) bwd_gamma_split_kernel(const uint16_t* x,
             }
             bf16x8 qh, ql;
             split_bf16x8(sq, qh, ql);
+            // transposed product (coefficients as A, rows as B): acc[kt] rows = components 16 kt + 4 g + i,
+            // column = row rb + r
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
                 const bf16x8* fb = s_f + (st * KT + kt) * 4 * 64 + lane;
-                mma(acc[kt], xa, fb[192]);
-                mma(acc[kt], xa, fb[128]);
-                mma(acc[kt], ql, fb[0]);
-                mma(acc[kt], qh, fb[64]);
-                mma(acc[kt], qh, fb[0]);
+                mma(acc[kt], fb[192], xa);
+                mma(acc[kt], fb[128], xa);
+                mma(acc[kt], fb[0], ql);
+                mma(acc[kt], fb[64], qh);
+                mma(acc[kt], fb[0], qh);
             }
         }
-        // rows rb + 4 g + i: softmax over the components (tiles in registers, 16 lanes per tile)
+        // row rb + r: softmax over its components (in the lane's registers, then across the four lane
+        // groups), stored as 16-byte runs of four components
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float l[KT];
-            float mx = -INFINITY;
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[kt][i] += cr[kt][i];
+                mx = fmaxf(mx, acc[kt][i]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float sm = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[kt][i] = expf(acc[kt][i] - mx);
+                sm += acc[kt][i];
+            }
+        sm += __shfl_xor(sm, 16, 64);
+        sm += __shfl_xor(sm, 32, 64);
+        const float inv = 1.f / sm;
+        const int64_t row = rb + r;
+        if (row < r1) {
+            float* grow = gh + row * K;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
-                l[kt] = cr[kt] + acc[kt][i];
-                mx = fmaxf(mx, l[kt]);
-            }
+                const int k0 = 16 * kt + 4 * g;
+                if (k0 + 4 <= K && K % 4 == 0) {
+                    *reinterpret_cast<f32x4*>(grow + k0) = acc[kt] * inv;
+                } else {
 #pragma unroll
-            for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-            float sm = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                l[kt] = expf(l[kt] - mx);
-                sm += l[kt];
-            }
-#pragma unroll
-            for (int o = 8; o > 0; o >>= 1) sm += __shfl_xor(sm, o, 64);
-            const float inv = 1.f / sm;
-            const int64_t row = rb + 4 * g + i;
-            if (row < r1) {
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    const int k = 16 * kt + r;
-                    if (k < K) gh[row * K + k] = l[kt] * inv;
+                    for (int i = 0; i < 4; ++i)
+                        if (k0 + i < K) grow[k0 + i] = acc[kt][i] * inv;
                 }
             }
         }
@@ -838,7 +853,7 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
     constexpr int STG = C * ROWB;          // one staged array of the chunk
     constexpr int IMG = C * 256;           // one bf16 image of the chunk
     constexpr int NCT = KC / 16;           // component tiles
-    constexpr int NST = 4 * 2 * 4;         // dx stores per wave and chunk
+    constexpr int NST = 4 * 2;             // dx stores per wave and chunk
     __shared__ __attribute__((aligned(16))) char s_stage[2 * STG];   // gamma, dgamma rows of the chunk
     __shared__ __attribute__((aligned(16))) char s_dl[2 * IMG];      // dl hi, dl lo
     __shared__ __attribute__((aligned(16))) char s_x[2 * IMG];       // x rows, two chunks
@@ -1007,7 +1022,8 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
                 }
         }
         {
-            // dx of dims 32 w .. + 31: acc[tt][j] rows = tokens 16 tt + 4 g + i, column tile j as in wh
+            // dx of dims 32 w .. + 31, formed transposed (the B fragments of mu / s, 1 / s as A, dl as B):
+            // acc[tt][j] rows = the dims of tile j (32 w + 16 (j % 2) + 4 g + i), column = token 16 tt + r
             f32x4 acc[4][4];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
@@ -1026,23 +1042,24 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        mma(acc[tt][j], al[tt], wh[j][ks]);
-                        mma(acc[tt][j], ah[tt], wl[j][ks]);
-                        mma(acc[tt][j], ah[tt], wh[j][ks]);
+                        mma(acc[tt][j], wh[j][ks], al[tt]);
+                        mma(acc[tt][j], wl[j][ks], ah[tt]);
+                        mma(acc[tt][j], wh[j][ks], ah[tt]);
                     }
             }
+            // lane (r, g): token 16 tt + r, dims d0 .. d0 + 3, 8 bytes per store
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int t = 16 * tt + r, d0 = 32 * w + 16 * jj + 4 * g;
+                    const bf16x4 xv = __builtin_bit_cast(bf16x4, lds_ld<u32x2>(xi + img_slot(t, d0 >> 2)));
+                    f32x4 val;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = 16 * tt + 4 * g + i, d = 32 * w + 16 * jj + r;
-                        const uint32_t xb = lds_ld<uint16_t>(xi + img_chunk(t, d >> 3) + (d & 7) * 2);
-                        const float val = acc[tt][jj][i] - __uint_as_float(xb << 16) * acc[tt][jj + 2][i];
-                        __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(val), rs_o,
-                                                              (uint32_t)(((n0 + t) * DRC + d) * 2), 0, 0);
-                    }
+                    for (int i = 0; i < 4; ++i) val[i] = acc[tt][jj][i] - (float)xv[i] * acc[tt][jj + 2][i];
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack4(val)), rs_o,
+                                                          (uint32_t)(((n0 + t) * DRC + d0) * 2), 0, 0);
+                }
         }
     }
 
