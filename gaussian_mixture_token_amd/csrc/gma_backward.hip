@@ -648,12 +648,14 @@ __global__ void __launch_bounds__(256) bwd_gamma_split_kernel(const uint16_t* x,
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // e^(l - max) as 2^((l - max) log2 e) on the hardware exp2 (about one ulp)
+        constexpr float kLog2e = 1.4426950408889634f;
         float sm = 0.f;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc[kt][i] = expf(acc[kt][i] - mx);
+                acc[kt][i] = __builtin_amdgcn_exp2f((acc[kt][i] - mx) * kLog2e);
                 sm += acc[kt][i];
             }
         sm += __shfl_xor(sm, 16, 64);
@@ -1080,6 +1082,118 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int i = 0; i < 4; ++i) gpo[(16 * (2 * w + hh) + 4 * g + i) * dxa + 2 * DRC] = po[hh][i];
+    }
+}
+
+// ---------------------------------------------------------------------------------- chunk states
+// The chunk terms of the causal prefix states, Gamma_K^T [V | 1] per chunk of 64 tokens (bf16 storage,
+// K = d_v = 128), written as [K][dva] records (columns d_v .. dva - 1: Z, then zeros).  A workgroup
+// walks `per` consecutive chunks of one (batch, head), the next chunk's rows loaded ahead; Gamma_K goes
+// to LDS as a bf16 hi + lo image, V as an exact one.  The product is formed transposed, V^T Gamma_K
+// (A = V^T, B = Gamma_K, both transposed fragments), so each lane stores four consecutive d_v columns
+// of one component; the Z row comes from a ones fragment.  Wave w takes d_v tiles 2 w, 2 w + 1 for all
+// components, and the Z row of component tiles 2 w, 2 w + 1.
+template <int KC, int VC>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) bwd_chunk_state_kernel(const float* gk, const void* v, float* stt, int64_t N,
+                                                              int64_t n_st, int per, int dva) {
+    static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
+    constexpr int C = 64;
+    constexpr int IMG = C * 256;
+    __shared__ __attribute__((aligned(16))) char s_k[2 * IMG];   // Gamma_K hi, lo
+    __shared__ __attribute__((aligned(16))) char s_v[IMG];       // V
+    lds_char* const LKH = (lds_char*)s_k;
+    lds_char* const LKL = LKH + IMG;
+    lds_char* const LV = (lds_char*)s_v;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t groups = (n_st + per - 1) / per;
+    const int64_t bh = blockIdx.x / groups;
+    const int64_t c0 = (blockIdx.x % groups) * per;
+    const int64_t c1 = c0 + per < n_st ? c0 + per : n_st;
+    const int64_t rec = (int64_t)KC * dva;
+
+    f32x4 pk[8];
+    u32x4 pv[4];
+    auto fetch = [&](int64_t c) {
+        const int64_t n0 = c * C;
+        const int nv = (int)(N - n0 < C ? N - n0 : C);
+        const float* gkh = gk + (bh * N + n0) * KC;
+        const uint16_t* vh = reinterpret_cast<const uint16_t*>(v) + (bh * N + n0) * VC;
+        const int rl = lane >> 5, cl = lane & 31;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = 16 * w + 2 * j + rl;
+            pk[j] = row < nv ? *reinterpret_cast<const f32x4*>(gkh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int row = 16 * w + 4 * bb + (lane >> 4);
+            pv[bb] = row < nv ? *reinterpret_cast<const u32x4*>(vh + (int64_t)row * VC + 8 * (lane & 15)) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    bf16x8 ones0;   // A fragment of the Z row: row 0 ones, the other rows zero
+    {
+        const __bf16 o = (__bf16)(r == 0 ? 1.f : 0.f);
+        ones0 = bf16x8{o, o, o, o, o, o, o, o};
+    }
+
+    fetch(c0);
+    for (int64_t c = c0; c < c1; ++c) {
+        if (c > c0) lds_barrier();
+        {
+            const int rl = lane >> 5, cl = lane & 31;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int off = img_slot(16 * w + 2 * j + rl, cl);
+                bf16x4 hi, lo;
+                split4(pk[j], hi, lo);
+                lds_st<bf16x4>(LKH + off, hi);
+                lds_st<bf16x4>(LKL + off, lo);
+            }
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) lds_st<u32x4>(LV + img_chunk(16 * w + 4 * bb + (lane >> 4), lane & 15), pv[bb]);
+        }
+        if (c + 1 < c1) fetch(c + 1);
+        lds_barrier();
+        // acc[t][ct] rows = d_v 32 w + 16 t + 4 g + i, column = component 16 ct + r
+        f32x4 acc[2][8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[0][ct] = acc[1][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tk = 0; tk < 2; ++tk) {
+            bf16x8 av[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) av[t] = img_tr(LV, 2 * w + t, tk, lane);
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                const bf16x8 bh_ = img_tr(LKH, ct, tk, lane), bl = img_tr(LKL, ct, tk, lane);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    mma(acc[t][ct], av[t], bl);
+                    mma(acc[t][ct], av[t], bh_);
+                }
+            }
+        }
+        float* rec_c = stt + (bh * n_st + c) * rec;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            float* row = rec_c + (int64_t)(16 * ct + r) * dva;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) *reinterpret_cast<f32x4*>(row + 32 * w + 16 * t + 4 * g) = acc[t][ct];
+        }
+        // Z (row 0 of the ones fragment's product) and the zero padding: component tiles 2 w, 2 w + 1
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int ct = 2 * w + hh;
+            f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int tk = 0; tk < 2; ++tk) {
+                mma(zacc, ones0, img_tr(LKL, ct, tk, lane));
+                mma(zacc, ones0, img_tr(LKH, ct, tk, lane));
+            }
+            if (g == 0) *reinterpret_cast<f32x4*>(rec_c + (int64_t)(16 * ct + r) * dva + VC) = zacc;
+        }
     }
 }
 
@@ -2098,6 +2212,16 @@ int bwd_fused_rows_seg(int64_t BH, int64_t N, int min_seg) {
     int seg = 4096;
     while (seg / 2 >= min_seg && BH * ((N + seg - 1) / seg) < 256) seg /= 2;
     return seg < min_seg ? min_seg : seg;
+}
+
+bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, int64_t BH, int64_t N, int64_t n_st, int K,
+                            int d_v, int dva, hipStream_t s) {
+    if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4) return false;
+    int per = 4;
+    while (per > 1 && BH * ((n_st + per - 1) / per) < 1024) per /= 2;
+    const int64_t groups = (n_st + per - 1) / per;
+    bwd_chunk_state_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gk, v, stt, N, n_st, per, dva);
+    return true;
 }
 
 bool launch_bwd_chunk_k(const float* gq, const float* gk, const void* v, const void* dout, const float* rs,

@@ -97,6 +97,10 @@ bool bwd_chunk_q_supported(int K, int d_v, bool f32);
 bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const void* dout, const float* stt, float* rs,
                         float* rt, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st, int K,
                         int d_v, int dva, float eps, hipStream_t s);
+// The chunk terms Gamma_K^T [V | 1] of the prefix states (the same shapes): stt [BH, n_st, K, dva], columns
+// d_v .. dva - 1 = Z, 0, 0, 0 (before the prefix scan).
+bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, int64_t BH, int64_t N, int64_t n_st, int K,
+                            int d_v, int dva, hipStream_t s);
 // Its key-side counterpart (the same shapes): from gq, gk, v, dout, rs and the exclusive suffix states
 // rt [BH, n_st, K, dva] it writes dgk = [V | 1] R^T + mt^T Gamma_Q [BH, N, K] and dv = Gamma_K Rv +
 // ac^T g [BH, N, d_v] bf16, recomputing ac and mt.

@@ -1241,13 +1241,22 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     const View vv = rows_tok, ghv = rows_tok;
     const BwdGen gen_v{v, nullptr, GEN_VAUG, f32 ? 1 : 0, d_v};
     const BwdGen gen_gh{dout, rs, GEN_GH, f32 ? 1 : 0, d_v};
-    // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
-    GMA_TRY(gemm(tok(gk, K), true, vv, false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{}, gen_v));
-    GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, causal ? 0 : 2, s); }));
-    // Causal bf16 at K = d_v = 128: one fused kernel per chunk does the read phase, the chunk terms of the
-    // suffix sums and dGamma_Q (and writes the intra-chunk blocks ac, mt for the key side)
+    // Causal bf16 at K = d_v = 128: fused chunk kernels for the state terms, the query side (read phase,
+    // chunk terms of the suffix sums, dGamma_Q) and the key side (dGamma_K, dV)
     const bool qfused = causal && bwd_chunk_q_supported(K, d_v, f32) && !misaligned(v, 16) && !misaligned(dout, 16) &&
                         !misaligned(dv, 16) && dva == d_v + 4;
+    // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
+    if (qfused) {
+        bool ok = true;
+        GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
+            ok = launch_bwd_chunk_state(gk, v, stt, BH, N, b.n_st, K, d_v, dva, s);
+        }));
+        if (!ok) return fail(GMA_ERROR_LAUNCH, "no chunk-state kernel for this shape");
+    } else {
+        GMA_TRY(gemm(tok(gk, K), true, vv, false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{},
+                     gen_v));
+    }
+    GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, causal ? 0 : 2, s); }));
     if (qfused) {
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
