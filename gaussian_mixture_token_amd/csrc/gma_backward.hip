@@ -25,6 +25,7 @@
 #include <algorithm>
 #include <type_traits>
 #include <cmath>
+#include <cstdlib>
 
 namespace gma {
 
@@ -566,12 +567,13 @@ __global__ void __launch_bounds__(256) bwd_gamma_mfma_kernel(const void* x, cons
 // with x exact in bf16 and x^2, a, b split into bf16 hi + lo (the lo lo products dropped), fp32
 // accumulation: x b_lo + x b_hi + x^2_lo a_hi + x^2_hi a_lo + x^2_hi a_hi per 32 dims and component
 // tile, five v_mfma_f32_16x16x32_bf16.  The head's operand fragments (bwd_frag_kernel, split) stay in
-// LDS for the workgroup, which walks `rows` consecutive rows of one (batch, head) in blocks of 64, wave w
-// rows 16 w .. 16 w + 15 of a block (lane (r, g): row r, dims 8 g .. 8 g + 7 of a step); the next
-// block's x is loaded during the current block.  The product is formed transposed (coefficient fragments
+// LDS for the workgroup, which walks `rows` consecutive rows of one (batch, head) (a multiple of 64 G) in
+// blocks of 64 G, wave w the G 16-row groups w, w + 4, .. of a block (lane (r, g): row r of a group, dims
+// 8 g .. 8 g + 7 of a step), so that every fragment read from LDS serves G groups; the next block's x
+// is loaded during the current block.  The product is formed transposed (coefficient fragments
 // as A, the rows as B), so that each lane ends with four consecutive components of one row: the softmax
 // runs in fp32 in the lane and across the four lane groups, and rows are stored 16 bytes per lane.
-template <int KT, int SMAX>
+template <int KT, int SMAX, int G>
 __global__ void __launch_bounds__(256) bwd_gamma_split_kernel(const uint16_t* x, const bf16x8* fr, const double* cq,
                                                               float* gamma, int64_t N, int H, int K, int d_r,
                                                               int rows) {
@@ -595,84 +597,103 @@ __global__ void __launch_bounds__(256) bwd_gamma_split_kernel(const uint16_t* x,
     __syncthreads();
     const uint16_t* xh = x + bh * N * d_r;
     float* gh = gamma + bh * N * K;
-    auto load = [&](int64_t rb, u32x4 (&xr)[SMAX]) {
-        const int64_t row = rb + r;
+    // wave w takes the G 16-row groups w, w + 4, .. of each block of 64 G rows (lane (r, g): row r of a
+    // group, dims 8 g .. 8 g + 7 of a step): every fragment read from LDS serves G groups
+    auto load = [&](int64_t rb, u32x4 (&xr)[G][SMAX]) {
 #pragma unroll
-        for (int st = 0; st < SMAX; ++st)
-            xr[st] = (st < S && row < r1) ? *reinterpret_cast<const u32x4*>(xh + row * d_r + 32 * st + 8 * g)
-                                          : u32x4{0u, 0u, 0u, 0u};
+        for (int gg = 0; gg < G; ++gg) {
+            const int64_t row = rb + 64 * gg + r;
+#pragma unroll
+            for (int st = 0; st < SMAX; ++st)
+                xr[gg][st] = (st < S && row < r1) ? *reinterpret_cast<const u32x4*>(xh + row * d_r + 32 * st + 8 * g)
+                                                  : u32x4{0u, 0u, 0u, 0u};
+        }
     };
-    u32x4 xn[SMAX];
+    u32x4 xn[G][SMAX];
     load(r0 + 16 * w, xn);
-    for (int64_t rb = r0 + 16 * w; rb < r1; rb += 64) {
-        u32x4 xr[SMAX];
+    for (int64_t rb = r0 + 16 * w; rb < r1; rb += 64 * G) {
+        u32x4 xr[G][SMAX];
 #pragma unroll
-        for (int st = 0; st < SMAX; ++st) xr[st] = xn[st];
-        if (rb + 64 < r1) load(rb + 64, xn);
-        f32x4 acc[KT];
+        for (int gg = 0; gg < G; ++gg)
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int st = 0; st < SMAX; ++st) xr[gg][st] = xn[gg][st];
+        if (rb + 64 * G < r1) load(rb + 64 * G, xn);
+        f32x4 acc[G][KT];
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) acc[gg][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < SMAX; ++st) {
             if (st >= S) break;
-            const bf16x8 xa = __builtin_bit_cast(bf16x8, xr[st]);
-            float sq[8];
+            bf16x8 xa[G], qh[G], ql[G];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = (float)xa[e];
-                sq[e] = v * v;
+            for (int gg = 0; gg < G; ++gg) {
+                xa[gg] = __builtin_bit_cast(bf16x8, xr[gg][st]);
+                float sq[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float v = (float)xa[gg][e];
+                    sq[e] = v * v;
+                }
+                split_bf16x8(sq, qh[gg], ql[gg]);
             }
-            bf16x8 qh, ql;
-            split_bf16x8(sq, qh, ql);
-            // transposed product (coefficients as A, rows as B): acc[kt] rows = components 16 kt + 4 g + i,
-            // column = row rb + r
+            // transposed product (coefficients as A, the rows as B): acc[gg][kt] rows = components
+            // 16 kt + 4 g + i, column = row rb + 64 gg + r
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
                 const bf16x8* fb = s_f + (st * KT + kt) * 4 * 64 + lane;
-                mma(acc[kt], fb[192], xa);
-                mma(acc[kt], fb[128], xa);
-                mma(acc[kt], fb[0], ql);
-                mma(acc[kt], fb[64], qh);
-                mma(acc[kt], fb[0], qh);
+                const bf16x8 ahi = fb[0], alo = fb[64], bhi = fb[128], blo = fb[192];
+#pragma unroll
+                for (int gg = 0; gg < G; ++gg) {
+                    mma(acc[gg][kt], blo, xa[gg]);
+                    mma(acc[gg][kt], bhi, xa[gg]);
+                    mma(acc[gg][kt], ahi, ql[gg]);
+                    mma(acc[gg][kt], alo, qh[gg]);
+                    mma(acc[gg][kt], ahi, qh[gg]);
+                }
             }
         }
-        // row rb + r: softmax over its components (in the lane's registers, then across the four lane
+        // row rb + 64 gg + r: softmax over its components (in the lane's registers, then across the four lane
         // groups), stored as 16-byte runs of four components
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[kt][i] += cr[kt][i];
-                mx = fmaxf(mx, acc[kt][i]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // e^(l - max) as 2^((l - max) log2 e) on the hardware exp2 (about one ulp)
         constexpr float kLog2e = 1.4426950408889634f;
-        float sm = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+        for (int gg = 0; gg < G; ++gg) {
+            float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[kt][i] = __builtin_amdgcn_exp2f((acc[kt][i] - mx) * kLog2e);
-                sm += acc[kt][i];
-            }
-        sm += __shfl_xor(sm, 16, 64);
-        sm += __shfl_xor(sm, 32, 64);
-        const float inv = 1.f / sm;
-        const int64_t row = rb + r;
-        if (row < r1) {
-            float* grow = gh + row * K;
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                const int k0 = 16 * kt + 4 * g;
-                if (k0 + 4 <= K && K % 4 == 0) {
-                    *reinterpret_cast<f32x4*>(grow + k0) = acc[kt] * inv;
-                } else {
+                for (int i = 0; i < 4; ++i) {
+                    acc[gg][kt][i] += cr[kt][i];
+                    mx = fmaxf(mx, acc[gg][kt][i]);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            // e^(l - max) as 2^((l - max) log2 e) on the hardware exp2 (about one ulp)
+            float sm = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (k0 + i < K) grow[k0 + i] = acc[kt][i] * inv;
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[gg][kt][i] = __builtin_amdgcn_exp2f((acc[gg][kt][i] - mx) * kLog2e);
+                    sm += acc[gg][kt][i];
+                }
+            sm += __shfl_xor(sm, 16, 64);
+            sm += __shfl_xor(sm, 32, 64);
+            const float inv = 1.f / sm;
+            const int64_t row = rb + 64 * gg + r;
+            if (row < r1) {
+                float* grow = gh + row * K;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    const int k0 = 16 * kt + 4 * g;
+                    if (k0 + 4 <= K && K % 4 == 0) {
+                        *reinterpret_cast<f32x4*>(grow + k0) = acc[gg][kt] * inv;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (k0 + i < K) grow[k0 + i] = acc[gg][kt][i] * inv;
+                    }
                 }
             }
         }
@@ -1198,6 +1219,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) b
 }
 
 // ---------------------------------------------------------------------------------- fused chunk, query side
+// Ownership in the fused chunk kernels, for W = 4 or 8 wavefronts: TW = 8 / W of the eight 16-wide
+// tiles of d_v or of the components per wave (tiles TW w .. TW w + TW - 1); for the 64 x 64 blocks,
+// QW = W / 4 waves per q tile: wave w takes q tile w / QW and the key tiles kt = w % QW (mod QW);
+// staging rows 64 / W per wave.
+template <int W>
+struct ChunkSplit {
+    static_assert(W == 4 || W == 8, "four or eight wavefronts");
+    static constexpr int TW = 8 / W;
+    static constexpr int QW = W / 4;
+    static constexpr int RPW = 64 / W;
+};
+
 // The query-side chunk work of the causal backward in one kernel (bf16 storage, K = d_v = 128).  From the
 // recomputed posteriors, V, dO and the state before the chunk S = [Vt | Z] (the exclusive prefix over
 // chunks of Gamma_K^T [V | 1]), per chunk of 64 tokens:
@@ -1207,21 +1240,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) b
 //   rt  = Gamma_Q^T [g | h]                                      (the chunk's term of the suffix sums)
 //   mt  = tril([g | h] [V | 1]^T)
 //   dGamma_Q = [g | h] S^T + mt Gamma_K
-// ac and mt also go to HBM for the key-side products.  A workgroup of four wavefronts walks `per`
-// consecutive chunks of one (batch, head); the next chunk's operands are loaded into registers while
-// the current one is processed.  Gamma_Q, Gamma_K, g, ac and mt live in LDS as bf16 hi + lo images, V
-// (and dO, for one step) as exact bf16 images; the state goes from HBM straight into split fragments
-// (wave w: d_v columns 32 w .. + 31 for num, components 32 w .. + 31 for dGamma_Q).  Wave w owns q
-// tile w of ac and mt, d_v columns 32 w .. + 31 of num and components 32 w .. + 31 of rt and
-// dGamma_Q.  ac, mt, rt and dGamma_Q are formed transposed (their accumulator rows run along the
-// stored rows), so that each lane stores 16 contiguous bytes.  Products: hi hi + hi lo + lo hi between
-// two fp32 operands, hi + lo against V, fp32 accumulation.
-template <int KC, int VC>
-__global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const float* gk, const void* v,
-                                                          const void* dout, const float* stt, float* rs, float* rt,
-                                                          float* ac_out, float* mt_out, float* dgq, int64_t N,
-                                                          int64_t n_st, int per, int dva, float eps) {
+// ac and mt go to HBM only where asked for.  A workgroup of W wavefronts walks `per` consecutive chunks
+// of one (batch, head); the next chunk's token operands are loaded into registers while the current one
+// is processed.  Gamma_Q, Gamma_K, g and the 64 x 64 blocks live in LDS as bf16 hi + lo images, V (and
+// dO, for one step) as exact bf16 images; the state goes from HBM straight into split fragments (the
+// wave's d_v tiles for num, its component tiles for dGamma_Q).  ac, mt, rt and dGamma_Q are formed
+// transposed (their accumulator rows run along the stored rows), so that each lane stores 16
+// contiguous bytes.  Products: hi hi + hi lo + lo hi between two fp32 operands, hi + lo against V,
+// fp32 accumulation.
+template <int KC, int VC, int W>
+__global__ void __launch_bounds__(W * 64) bwd_chunk_q_kernel(const float* gq, const float* gk, const void* v,
+                                                             const void* dout, const float* stt, float* rs, float* rt,
+                                                             float* ac_out, float* mt_out, float* dgq, int64_t N,
+                                                             int64_t n_st, int per, int dva, float eps) {
     static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
+    using CS = ChunkSplit<W>;
+    constexpr int TW = CS::TW, QW = CS::QW, RPW = CS::RPW;
     constexpr int C = 64;
     constexpr int IMG = C * 256;
     __shared__ __attribute__((aligned(16))) char s_q[2 * IMG];   // Gamma_Q hi, lo
@@ -1229,7 +1263,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
     __shared__ __attribute__((aligned(16))) char s_v[IMG];       // V
     __shared__ __attribute__((aligned(16))) char s_g[2 * IMG];   // g hi, lo
     __shared__ __attribute__((aligned(16))) char s_m[2 * IMG];   // ac hi, lo; then dO; then mt hi, lo
-    __shared__ float s_z[KC], s_den[C], s_inv[C], s_h[C], s_part[4][C];
+    __shared__ float s_z[KC], s_den[C], s_inv[C], s_h[C], s_part[W][C], s_dpart[QW][C];
     lds_char* const LQH = (lds_char*)s_q;
     lds_char* const LQL = LQH + IMG;
     lds_char* const LKH = (lds_char*)s_k;
@@ -1243,16 +1277,17 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
+    const int qw = w / QW, kp = w % QW;   // the wave's q tile and key-tile phase in the 64 x 64 blocks
     const int64_t groups = (n_st + per - 1) / per;
     const int64_t bh = blockIdx.x / groups;
     const int64_t c0 = (blockIdx.x % groups) * per;
     const int64_t c1 = c0 + per < n_st ? c0 + per : n_st;
     const int64_t rec = (int64_t)KC * dva;
 
-    // ---- the token operands of one chunk, loaded a chunk ahead: Gamma_Q, Gamma_K rows 16 w + 2 j + l / 32
-    // (components 4 (l % 32) .. + 3); V, dO rows 16 w + 4 bb + l / 16 (chunk l % 16)
-    f32x4 pq[8], pk[8];
-    u32x4 pv[4], pd[4];
+    // ---- the token operands of one chunk, loaded a chunk ahead: Gamma_Q, Gamma_K rows RPW w + 2 j + l / 32
+    // (components 4 (l % 32) .. + 3); V, dO rows RPW w + 4 bb + l / 16 (chunk l % 16)
+    f32x4 pq[RPW / 2], pk[RPW / 2];
+    u32x4 pv[RPW / 4], pd[RPW / 4];
     auto fetch = [&](int64_t c) {
         const int64_t n0 = c * C;
         const int nv = (int)(N - n0 < C ? N - n0 : C);
@@ -1262,14 +1297,14 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
         const uint16_t* dh = reinterpret_cast<const uint16_t*>(dout) + (bh * N + n0) * VC;
         const int rl = lane >> 5, cl = lane & 31;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = 16 * w + 2 * j + rl;
+        for (int j = 0; j < RPW / 2; ++j) {
+            const int row = RPW * w + 2 * j + rl;
             pq[j] = row < nv ? *reinterpret_cast<const f32x4*>(gqh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
             pk[j] = row < nv ? *reinterpret_cast<const f32x4*>(gkh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
+        for (int bb = 0; bb < RPW / 4; ++bb) {
+            const int row = RPW * w + 4 * bb + (lane >> 4), ch = lane & 15;
             pv[bb] = row < nv ? *reinterpret_cast<const u32x4*>(vh + (int64_t)row * VC + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
             pd[bb] = row < nv ? *reinterpret_cast<const u32x4*>(dh + (int64_t)row * VC + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
         }
@@ -1287,8 +1322,8 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
         {
             const int rl = lane >> 5, cl = lane & 31;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int off = img_slot(16 * w + 2 * j + rl, cl);
+            for (int j = 0; j < RPW / 2; ++j) {
+                const int off = img_slot(RPW * w + 2 * j + rl, cl);
                 bf16x4 hi, lo;
                 split4(pq[j], hi, lo);
                 lds_st<bf16x4>(LQH + off, hi);
@@ -1298,34 +1333,31 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 lds_st<bf16x4>(LKL + off, lo);
             }
         }
-        u32x4 dor[4];
+        u32x4 dor[RPW / 4];
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            lds_st<u32x4>(LV + img_chunk(16 * w + 4 * bb + (lane >> 4), lane & 15), pv[bb]);
+        for (int bb = 0; bb < RPW / 4; ++bb) {
+            lds_st<u32x4>(LV + img_chunk(RPW * w + 4 * bb + (lane >> 4), lane & 15), pv[bb]);
             dor[bb] = pd[bb];
         }
-        // the state before this chunk, loaded now and split where it is used: for num (rows 32 ks + 8 g + e,
-        // column 32 w + 16 t + r), for dGamma_Q (row 32 w + 16 t + r, columns 32 ks + 8 g .. + 7), Z
+        // the state before this chunk, split where it is used: for num (rows 32 ks + 8 g + e, the wave's d_v
+        // columns 16 (TW w + t) + r) loaded now, for dGamma_Q (the wave's component rows 16 (TW w + t) + r,
+        // columns 32 ks + 8 g .. + 7) loaded after rt; Z
         const float* S = stt + (bh * n_st + c) * rec;
-        float psn[2][4][8];
-        f32x4 psd[2][4][2];
+        float psn[TW][4][8];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) psn[t][ks][e] = S[(int64_t)(32 * ks + 8 * g + e) * dva + 32 * w + 16 * t + r];
-                const float* p = S + (int64_t)(32 * w + 16 * t + r) * dva + 32 * ks + 8 * g;
-                psd[t][ks][0] = *reinterpret_cast<const f32x4*>(p);
-                psd[t][ks][1] = *reinterpret_cast<const f32x4*>(p + 4);
-            }
+                for (int e = 0; e < 8; ++e) psn[t][ks][e] = S[(int64_t)(32 * ks + 8 * g + e) * dva + 16 * (TW * w + t) + r];
         const float pz = tid < KC ? S[(int64_t)tid * dva + VC] : 0.f;
         if (c + 1 < c1) fetch(c + 1);
         lds_barrier();
 
-        // ---- ac^T = Gamma_K Gamma_Q^T, q tile w: acc[kt] rows = keys 16 kt + 4 g + i, column = q 16 w + r
+        // ---- ac^T = Gamma_K Gamma_Q^T, q tile qw, key tiles kp (mod QW): acc[kt] rows = keys 16 kt + 4 g + i,
+        // column = q 16 qw + r; image (rows q), row-sum parts
         {
-            const int q = 16 * w + r;
+            const int q = 16 * qw + r;
             f32x4 acc[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1334,7 +1366,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 const bf16x8 bh_ = img_row(LQH, q, ks, g), bl = img_row(LQL, q, ks, g);
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
-                    if (kt > w) continue;
+                    if (kt % QW != kp || kt > qw) continue;
                     const bf16x8 ah = img_row(LKH, 16 * kt + r, ks, g), al = img_row(LKL, 16 * kt + r, ks, g);
                     mma(acc[kt], al, bh_);
                     mma(acc[kt], ah, bl);
@@ -1344,44 +1376,45 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
             float rsum = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
+                if (kt % QW != kp) continue;
                 f32x4 val;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = 16 * kt + 4 * g + i;
-                    val[i] = (kt <= w && key <= q) ? acc[kt][i] : 0.f;
+                    val[i] = (kt <= qw && key <= q) ? acc[kt][i] : 0.f;
                     rsum += val[i];
                 }
                 bf16x4 hi, lo;
                 split4(val, hi, lo);
                 lds_st<bf16x4>(LMH + img_slot(q, 4 * kt + g), hi);
                 lds_st<bf16x4>(LML + img_slot(q, 4 * kt + g), lo);
-                if (ac_out) *reinterpret_cast<f32x4*>(blk_ac + q * C + 16 * kt + 4 * g) = val;
+                if (blk_ac) *reinterpret_cast<f32x4*>(blk_ac + q * C + 16 * kt + 4 * g) = val;
             }
             rsum += __shfl_xor(rsum, 16, 64);
             rsum += __shfl_xor(rsum, 32, 64);
-            if (g == 0) s_den[q] = rsum;
+            if (g == 0) s_dpart[kp][q] = rsum;
         }
         if (tid < KC) s_z[tid] = pz;
         lds_barrier();
-        bf16x8 snh[2][4], snl[2][4];
+        bf16x8 snh[TW][4], snl[TW][4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) split_bf16x8(psn[t][ks], snh[t][ks], snl[t][ks]);
 
-        // ---- num (d_v columns 32 w .. + 31: rows q 16 qt + 4 g + i), den of q tile w
-        f32x4 num[4][2];
+        // ---- num (the wave's d_v tiles: rows q 16 qt + 4 g + i), den of q tile qw (phase-0 waves)
+        f32x4 num[4][TW];
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) num[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < TW; ++t) num[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) {
                 const bf16x8 ah = img_row(LQH, 16 * qt + r, ks, g), al = img_row(LQL, 16 * qt + r, ks, g);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < TW; ++t) {
                     mma(num[qt][t], al, snh[t][ks]);
                     mma(num[qt][t], ah, snl[t][ks]);
                     mma(num[qt][t], ah, snh[t][ks]);
@@ -1389,25 +1422,25 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
             }
 #pragma unroll
         for (int ks2 = 0; ks2 < 2; ++ks2) {
-            bf16x8 vb[2];
+            bf16x8 vb[TW];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) vb[t] = img_tr(LV, 2 * w + t, ks2, lane);
+            for (int t = 0; t < TW; ++t) vb[t] = img_tr(LV, TW * w + t, ks2, lane);
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) {
                 if (ks2 == 1 && qt < 2) continue;   // keys 32 .. 63 lie above those rows: ac = 0
                 const bf16x8 ah = img_row_perm(LMH, 16 * qt + r, ks2, g), al = img_row_perm(LML, 16 * qt + r, ks2, g);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < TW; ++t) {
                     mma(num[qt][t], al, vb[t]);
                     mma(num[qt][t], ah, vb[t]);
                 }
             }
         }
-        {
+        if (kp == 0) {
             f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 ah = img_row(LQH, 16 * w + r, ks, g), al = img_row(LQL, 16 * w + r, ks, g);
+                const bf16x8 ah = img_row(LQH, 16 * qw + r, ks, g), al = img_row(LQL, 16 * qw + r, ks, g);
                 float zv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) zv[e] = r == 0 ? s_z[32 * ks + 8 * g + e] : 0.f;
@@ -1419,14 +1452,21 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
             }
             if (r == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s_den[16 * w + 4 * g + i] += dacc[i] + eps;
+                for (int i = 0; i < 4; ++i) {
+                    const int q = 16 * qw + 4 * g + i;
+                    float d = 0.f;
+#pragma unroll
+                    for (int p = 0; p < QW; ++p) d += s_dpart[p][q];
+                    s_den[q] = d + dacc[i] + eps;
+                }
             }
         }
         lds_barrier();   // den complete; ac no longer read
 
         // ---- g, h: dO into the spare image, 1 / den, the wave's part of dO . num per row
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) lds_st<u32x4>(LMH + img_chunk(16 * w + 4 * bb + (lane >> 4), lane & 15), dor[bb]);
+        for (int bb = 0; bb < RPW / 4; ++bb)
+            lds_st<u32x4>(LMH + img_chunk(RPW * w + 4 * bb + (lane >> 4), lane & 15), dor[bb]);
         if (tid < C) s_inv[tid] = tid < nv ? 1.f / s_den[tid] : 0.f;   // rows past N: g = h = 0 (even with eps = 0)
         lds_barrier();
 #pragma unroll
@@ -1437,8 +1477,8 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 const float inv = s_inv[q];
                 float d = 0.f;
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const float dov = (float)lds_ld<__bf16>(LMH + img_elem(q, 32 * w + 16 * t + r));
+                for (int t = 0; t < TW; ++t) {
+                    const float dov = (float)lds_ld<__bf16>(LMH + img_elem(q, 16 * (TW * w + t) + r));
                     d += num[qt][t][i] * inv * dov;
                 }
 #pragma unroll
@@ -1448,7 +1488,10 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
         lds_barrier();
         if (tid < C) {
             const float inv = s_inv[tid];
-            const float hv = -(s_part[0][tid] + s_part[1][tid] + s_part[2][tid] + s_part[3][tid]) * inv;
+            float d = 0.f;
+#pragma unroll
+            for (int p = 0; p < W; ++p) d += s_part[p][tid];
+            const float hv = -d * inv;
             s_h[tid] = hv;
             if (tid < nv) {
                 rs[(bh * N + n0 + tid) * 2] = inv;
@@ -1456,8 +1499,8 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
             }
         }
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
+        for (int bb = 0; bb < RPW / 4; ++bb) {
+            const int row = RPW * w + 4 * bb + (lane >> 4), ch = lane & 15;
             const float inv = s_inv[row];
             const bf16x8 dv8 = __builtin_bit_cast(bf16x8, dor[bb]);
             float gv[8];
@@ -1470,28 +1513,28 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
         }
         lds_barrier();   // g, h visible; dO no longer read
 
-        // ---- rt^T = [g | h]^T Gamma_Q: racc[vt][t] rows = d_v 16 vt + 4 g + i (vt 8: the h row 128 and
-        // the zero padding), column = component 32 w + 16 t + r
+        // ---- rt^T = [g | h]^T Gamma_Q: racc[vt][t] rows = d_v 16 vt + 4 g + i (vt 8: the h row 128 and the
+        // zero padding), column = component 16 (TW w + t) + r
         {
             float* rth = rt + (bh * n_st + c) * rec;
-            f32x4 racc[9][2];
+            f32x4 racc[9][TW];
 #pragma unroll
             for (int vt = 0; vt < 9; ++vt)
 #pragma unroll
-                for (int t = 0; t < 2; ++t) racc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < TW; ++t) racc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int tk = 0; tk < 2; ++tk) {
-                bf16x8 bqh[2], bql[2];
+                bf16x8 bqh[TW], bql[TW];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    bqh[t] = img_tr(LQH, 2 * w + t, tk, lane);
-                    bql[t] = img_tr(LQL, 2 * w + t, tk, lane);
+                for (int t = 0; t < TW; ++t) {
+                    bqh[t] = img_tr(LQH, TW * w + t, tk, lane);
+                    bql[t] = img_tr(LQL, TW * w + t, tk, lane);
                 }
 #pragma unroll
                 for (int vt = 0; vt < 8; ++vt) {
                     const bf16x8 ah = img_tr(LGH, vt, tk, lane), al = img_tr(LGL, vt, tk, lane);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < TW; ++t) {
                         mma(racc[vt][t], al, bqh[t]);
                         mma(racc[vt][t], ah, bql[t]);
                         mma(racc[vt][t], ah, bqh[t]);
@@ -1503,24 +1546,35 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 bf16x8 hh, hl;
                 split_bf16x8(hv, hh, hl);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < TW; ++t) {
                     mma(racc[8][t], hl, bqh[t]);
                     mma(racc[8][t], hh, bql[t]);
                     mma(racc[8][t], hh, bqh[t]);
                 }
             }
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                float* row = rth + (int64_t)(32 * w + 16 * t + r) * dva;
+            for (int t = 0; t < TW; ++t) {
+                float* row = rth + (int64_t)(16 * (TW * w + t) + r) * dva;
 #pragma unroll
                 for (int vt = 0; vt < 8; ++vt) *reinterpret_cast<f32x4*>(row + 16 * vt + 4 * g) = racc[vt][t];
                 if (g == 0) *reinterpret_cast<f32x4*>(row + VC) = racc[8][t];
             }
         }
 
-        // ---- mt^T = [V | 1] [g | h]^T, q tile w: macc[kt] rows = keys 16 kt + 4 g + i, column = q 16 w + r
+        f32x4 psd[TW][4][2];
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const float* p = S + (int64_t)(16 * (TW * w + t) + r) * dva + 32 * ks + 8 * g;
+                psd[t][ks][0] = *reinterpret_cast<const f32x4*>(p);
+                psd[t][ks][1] = *reinterpret_cast<const f32x4*>(p + 4);
+            }
+
+        // ---- mt^T = [V | 1] [g | h]^T, q tile qw, key tiles kp (mod QW): macc[kt] rows = keys 16 kt + 4 g + i,
+        // column = q 16 qw + r
         {
-            const int q = 16 * w + r;
+            const int q = 16 * qw + r;
             const float hq = s_h[q];
             f32x4 macc[4];
 #pragma unroll
@@ -1530,7 +1584,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 const bf16x8 bh_ = img_row(LGH, q, ks, g), bl = img_row(LGL, q, ks, g);
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
-                    if (kt > w) continue;
+                    if (kt % QW != kp || kt > qw) continue;
                     const bf16x8 av = img_row(LV, 16 * kt + r, ks, g);
                     mma(macc[kt], av, bl);
                     mma(macc[kt], av, bh_);
@@ -1538,27 +1592,28 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
             }
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
+                if (kt % QW != kp) continue;
                 f32x4 val;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = 16 * kt + 4 * g + i;
-                    val[i] = (kt <= w && key <= q && key < nv) ? macc[kt][i] + hq : 0.f;
+                    val[i] = (kt <= qw && key <= q && key < nv) ? macc[kt][i] + hq : 0.f;
                 }
                 bf16x4 hi, lo;
                 split4(val, hi, lo);
                 lds_st<bf16x4>(LMH + img_slot(q, 4 * kt + g), hi);
                 lds_st<bf16x4>(LML + img_slot(q, 4 * kt + g), lo);
-                if (mt_out) *reinterpret_cast<f32x4*>(blk_mt + q * C + 16 * kt + 4 * g) = val;
+                if (blk_mt) *reinterpret_cast<f32x4*>(blk_mt + q * C + 16 * kt + 4 * g) = val;
             }
         }
         lds_barrier();
 
-        // ---- dGamma_Q^T = S [g | h]^T + Gamma_K^T mt^T: dacc[t][qt] rows = components 32 w + 16 t + 4 g + i,
+        // ---- dGamma_Q^T = S [g | h]^T + Gamma_K^T mt^T: dacc[t][qt] rows = components 16 (TW w + t) + 4 g + i,
         // column = q 16 qt + r
         {
-            bf16x8 sdh[2][4], sdl[2][4];
+            bf16x8 sdh[TW][4], sdl[TW][4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     float b[8];
@@ -1569,9 +1624,9 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                     }
                     split_bf16x8(b, sdh[t][ks], sdl[t][ks]);
                 }
-            f32x4 dacc[2][4];
+            f32x4 dacc[TW][4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int qt = 0; qt < 4; ++qt) dacc[t][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1580,7 +1635,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 for (int qt = 0; qt < 4; ++qt) {
                     const bf16x8 bh_ = img_row(LGH, 16 * qt + r, ks, g), bl = img_row(LGL, 16 * qt + r, ks, g);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < TW; ++t) {
                         mma(dacc[t][qt], sdl[t][ks], bh_);
                         mma(dacc[t][qt], sdh[t][ks], bl);
                         mma(dacc[t][qt], sdh[t][ks], bh_);
@@ -1588,18 +1643,18 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 }
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2) {
-                bf16x8 akh[2], akl[2];
+                bf16x8 akh[TW], akl[TW];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    akh[t] = img_tr(LKH, 2 * w + t, ks2, lane);
-                    akl[t] = img_tr(LKL, 2 * w + t, ks2, lane);
+                for (int t = 0; t < TW; ++t) {
+                    akh[t] = img_tr(LKH, TW * w + t, ks2, lane);
+                    akl[t] = img_tr(LKL, TW * w + t, ks2, lane);
                 }
 #pragma unroll
                 for (int qt = 0; qt < 4; ++qt) {
                     if (ks2 == 1 && qt < 2) continue;   // mt = 0 above the diagonal
                     const bf16x8 bh_ = img_row_perm(LMH, 16 * qt + r, ks2, g), bl = img_row_perm(LML, 16 * qt + r, ks2, g);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < TW; ++t) {
                         mma(dacc[t][qt], akl[t], bh_);
                         mma(dacc[t][qt], akh[t], bl);
                         mma(dacc[t][qt], akh[t], bh_);
@@ -1612,8 +1667,8 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
                 const int q = 16 * qt + r;
                 const float hq = s_h[q];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int comp0 = 32 * w + 16 * t + 4 * g;
+                for (int t = 0; t < TW; ++t) {
+                    const int comp0 = 16 * (TW * w + t) + 4 * g;
                     f32x4 val;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) val[i] = dacc[t][qt][i] + hq * s_z[comp0 + i];
@@ -1631,17 +1686,16 @@ __global__ void __launch_bounds__(256) bwd_chunk_q_kernel(const float* gq, const
 //   ac = tril(Gamma_Q Gamma_K^T),  mt = tril([g | h] [V | 1]^T)      (recomputed, never stored)
 //   dV       = Gamma_K Rv + ac^T g
 //   dGamma_K = [V | 1] R^T + mt^T Gamma_Q
-// Layout and work split follow the query-side kernel: a workgroup walks `per` consecutive chunks of one
-// (batch, head) with the next chunk's token operands loaded ahead; Gamma_Q, Gamma_K, g and the 64 x 64
-// blocks in LDS as bf16 hi + lo images, V exact; R from HBM into split fragments (wave w: d_v columns
-// 32 w .. + 31 for dV, components 32 w .. + 31 for dGamma_K); both outputs formed transposed so that
-// each lane stores contiguous bytes.
-template <int KC, int VC>
-__global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const float* gk, const void* v,
-                                                          const void* dout, const float* rs, const float* rt,
-                                                          float* dgk, void* dv, int64_t N, int64_t n_st, int per,
-                                                          int dva) {
+// Layout, ownership and work split follow the query-side kernel: the wave's d_v tiles for dV, its
+// component tiles for dGamma_K; both outputs formed transposed so that each lane stores contiguous bytes.
+template <int KC, int VC, int W>
+__global__ void __launch_bounds__(W * 64) bwd_chunk_k_kernel(const float* gq, const float* gk, const void* v,
+                                                             const void* dout, const float* rs, const float* rt,
+                                                             float* dgk, void* dv, int64_t N, int64_t n_st, int per,
+                                                             int dva) {
     static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
+    using CS = ChunkSplit<W>;
+    constexpr int TW = CS::TW, QW = CS::QW, RPW = CS::RPW;
     constexpr int C = 64;
     constexpr int IMG = C * 256;
     __shared__ __attribute__((aligned(16))) char s_q[2 * IMG];   // Gamma_Q hi, lo
@@ -1663,6 +1717,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
+    const int qw = w / QW, kp = w % QW;
     const int64_t groups = (n_st + per - 1) / per;
     const int64_t bh = blockIdx.x / groups;
     const int64_t c0 = (blockIdx.x % groups) * per;
@@ -1671,9 +1726,9 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
 
     // token operands of one chunk, loaded a chunk ahead (rows as in the query-side kernel); rs of the
     // V / dO rows
-    f32x4 pq[8], pk[8];
-    u32x4 pv[4], pd[4];
-    float pr0[4], pr1[4];
+    f32x4 pq[RPW / 2], pk[RPW / 2];
+    u32x4 pv[RPW / 4], pd[RPW / 4];
+    float pr0[RPW / 4], pr1[RPW / 4];
     auto fetch = [&](int64_t c) {
         const int64_t n0 = c * C;
         const int nv = (int)(N - n0 < C ? N - n0 : C);
@@ -1683,14 +1738,14 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
         const uint16_t* dh = reinterpret_cast<const uint16_t*>(dout) + (bh * N + n0) * VC;
         const int rl = lane >> 5, cl = lane & 31;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = 16 * w + 2 * j + rl;
+        for (int j = 0; j < RPW / 2; ++j) {
+            const int row = RPW * w + 2 * j + rl;
             pq[j] = row < nv ? *reinterpret_cast<const f32x4*>(gqh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
             pk[j] = row < nv ? *reinterpret_cast<const f32x4*>(gkh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
+        for (int bb = 0; bb < RPW / 4; ++bb) {
+            const int row = RPW * w + 4 * bb + (lane >> 4), ch = lane & 15;
             const bool ok = row < nv;
             pv[bb] = ok ? *reinterpret_cast<const u32x4*>(vh + (int64_t)row * VC + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
             pd[bb] = ok ? *reinterpret_cast<const u32x4*>(dh + (int64_t)row * VC + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
@@ -1709,8 +1764,8 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
         {
             const int rl = lane >> 5, cl = lane & 31;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int off = img_slot(16 * w + 2 * j + rl, cl);
+            for (int j = 0; j < RPW / 2; ++j) {
+                const int off = img_slot(RPW * w + 2 * j + rl, cl);
                 bf16x4 hi, lo;
                 split4(pq[j], hi, lo);
                 lds_st<bf16x4>(LQH + off, hi);
@@ -1721,8 +1776,8 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
             }
         }
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
+        for (int bb = 0; bb < RPW / 4; ++bb) {
+            const int row = RPW * w + 4 * bb + (lane >> 4), ch = lane & 15;
             lds_st<u32x4>(LV + img_chunk(row, ch), pv[bb]);
             const bf16x8 dv8 = __builtin_bit_cast(bf16x8, pd[bb]);
             float gv[8];
@@ -1735,31 +1790,31 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
             if (ch == 0) s_h[row] = pr1[bb];
         }
         // the state after this chunk, loaded now and split where it is used: for dV (rows 32 ks + 8 g + e,
-        // column 32 w + 16 t + r), for dGamma_K (row 32 w + 16 t + r, columns 32 ks + 8 g .. + 7, and the r
-        // column of rows 32 w + 16 t + 4 g + i)
+        // the wave's d_v columns 16 (TW w + t) + r), for dGamma_K (the wave's component rows 16 (TW w + t) +
+        // r, columns 32 ks + 8 g .. + 7, and the r column of rows 16 (TW w + t) + 4 g + i)
         const float* R = rt + (bh * n_st + c) * rec;
-        float prn[2][4][8];
-        f32x4 prd[2][4][2];
-        float prr[2][4];
+        float prn[TW][4][8];
+        f32x4 prd[TW][4][2];
+        float prr[TW][4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < TW; ++t) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) prn[t][ks][e] = R[(int64_t)(32 * ks + 8 * g + e) * dva + 32 * w + 16 * t + r];
-                const float* p = R + (int64_t)(32 * w + 16 * t + r) * dva + 32 * ks + 8 * g;
+                for (int e = 0; e < 8; ++e) prn[t][ks][e] = R[(int64_t)(32 * ks + 8 * g + e) * dva + 16 * (TW * w + t) + r];
+                const float* p = R + (int64_t)(16 * (TW * w + t) + r) * dva + 32 * ks + 8 * g;
                 prd[t][ks][0] = *reinterpret_cast<const f32x4*>(p);
                 prd[t][ks][1] = *reinterpret_cast<const f32x4*>(p + 4);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) prr[t][i] = R[(int64_t)(32 * w + 16 * t + 4 * g + i) * dva + VC];
+            for (int i = 0; i < 4; ++i) prr[t][i] = R[(int64_t)(16 * (TW * w + t) + 4 * g + i) * dva + VC];
         }
         if (c + 1 < c1) fetch(c + 1);
         lds_barrier();
 
-        // ---- ac^T = Gamma_K Gamma_Q^T, q tile w, into the block image (rows q)
+        // ---- ac^T = Gamma_K Gamma_Q^T, q tile qw, key tiles kp (mod QW), into the block image (rows q)
         {
-            const int q = 16 * w + r;
+            const int q = 16 * qw + r;
             f32x4 acc[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1768,7 +1823,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
                 const bf16x8 bh_ = img_row(LQH, q, ks, g), bl = img_row(LQL, q, ks, g);
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
-                    if (kt > w) continue;
+                    if (kt % QW != kp || kt > qw) continue;
                     const bf16x8 ah = img_row(LKH, 16 * kt + r, ks, g), al = img_row(LKL, 16 * kt + r, ks, g);
                     mma(acc[kt], al, bh_);
                     mma(acc[kt], ah, bl);
@@ -1777,11 +1832,12 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
             }
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
+                if (kt % QW != kp) continue;
                 f32x4 val;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = 16 * kt + 4 * g + i;
-                    val[i] = (kt <= w && key <= q) ? acc[kt][i] : 0.f;
+                    val[i] = (kt <= qw && key <= q) ? acc[kt][i] : 0.f;
                 }
                 bf16x4 hi, lo;
                 split4(val, hi, lo);
@@ -1791,16 +1847,16 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
         }
         lds_barrier();
 
-        // ---- dV^T = Rv^T Gamma_K^T + g^T ac: vacc[t][kt] rows = d_v 32 w + 16 t + 4 g + i, column = key 16 kt + r
+        // ---- dV^T = Rv^T Gamma_K^T + g^T ac: vacc[t][kt] rows = d_v 16 (TW w + t) + 4 g + i, column = key 16 kt + r
         {
-            bf16x8 anh[2][4], anl[2][4];
+            bf16x8 anh[TW][4], anl[TW][4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) split_bf16x8(prn[t][ks], anh[t][ks], anl[t][ks]);
-            f32x4 vacc[2][4];
+            f32x4 vacc[TW][4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) vacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1809,7 +1865,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
                 for (int kt = 0; kt < 4; ++kt) {
                     const bf16x8 bh_ = img_row(LKH, 16 * kt + r, ks, g), bl = img_row(LKL, 16 * kt + r, ks, g);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < TW; ++t) {
                         mma(vacc[t][kt], anl[t][ks], bh_);
                         mma(vacc[t][kt], anh[t][ks], bl);
                         mma(vacc[t][kt], anh[t][ks], bh_);
@@ -1817,18 +1873,18 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
                 }
 #pragma unroll
             for (int tk = 0; tk < 2; ++tk) {
-                bf16x8 agh[2], agl[2];
+                bf16x8 agh[TW], agl[TW];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    agh[t] = img_tr(LGH, 2 * w + t, tk, lane);
-                    agl[t] = img_tr(LGL, 2 * w + t, tk, lane);
+                for (int t = 0; t < TW; ++t) {
+                    agh[t] = img_tr(LGH, TW * w + t, tk, lane);
+                    agl[t] = img_tr(LGL, TW * w + t, tk, lane);
                 }
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
                     if (tk == 0 && kt >= 2) continue;   // queries 0 .. 31 see no key of these tiles
                     const bf16x8 bh_ = img_tr(LMH, kt, tk, lane), bl = img_tr(LML, kt, tk, lane);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < TW; ++t) {
                         mma(vacc[t][kt], agl[t], bh_);
                         mma(vacc[t][kt], agh[t], bl);
                         mma(vacc[t][kt], agh[t], bh_);
@@ -1841,15 +1897,15 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
                 const int key = 16 * kt + r;
                 if (key >= nv) continue;
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    *reinterpret_cast<bf16x4*>(dvh + (int64_t)key * VC + 32 * w + 16 * t + 4 * g) = pack4(vacc[t][kt]);
+                for (int t = 0; t < TW; ++t)
+                    *reinterpret_cast<bf16x4*>(dvh + (int64_t)key * VC + 16 * (TW * w + t) + 4 * g) = pack4(vacc[t][kt]);
             }
         }
         lds_barrier();   // ac no longer read
 
-        // ---- mt^T = [V | 1] [g | h]^T, q tile w, into the block image (rows q)
+        // ---- mt^T = [V | 1] [g | h]^T, q tile qw, key tiles kp (mod QW), into the block image (rows q)
         {
-            const int q = 16 * w + r;
+            const int q = 16 * qw + r;
             const float hq = s_h[q];
             f32x4 macc[4];
 #pragma unroll
@@ -1859,7 +1915,7 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
                 const bf16x8 bh_ = img_row(LGH, q, ks, g), bl = img_row(LGL, q, ks, g);
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
-                    if (kt > w) continue;
+                    if (kt % QW != kp || kt > qw) continue;
                     const bf16x8 av = img_row(LV, 16 * kt + r, ks, g);
                     mma(macc[kt], av, bl);
                     mma(macc[kt], av, bh_);
@@ -1867,11 +1923,12 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
             }
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
+                if (kt % QW != kp) continue;
                 f32x4 val;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = 16 * kt + 4 * g + i;
-                    val[i] = (kt <= w && key <= q && key < nv) ? macc[kt][i] + hq : 0.f;
+                    val[i] = (kt <= qw && key <= q && key < nv) ? macc[kt][i] + hq : 0.f;
                 }
                 bf16x4 hi, lo;
                 split4(val, hi, lo);
@@ -1881,12 +1938,12 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
         }
         lds_barrier();
 
-        // ---- dGamma_K^T = R [V | 1]^T + Gamma_Q^T mt: kacc[t][kt] rows = components 32 w + 16 t + 4 g + i,
+        // ---- dGamma_K^T = R [V | 1]^T + Gamma_Q^T mt: kacc[t][kt] rows = components 16 (TW w + t) + 4 g + i,
         // column = key 16 kt + r
         {
-            bf16x8 adh[2][4], adl[2][4];
+            bf16x8 adh[TW][4], adl[TW][4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     float b[8];
@@ -1897,9 +1954,9 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
                     }
                     split_bf16x8(b, adh[t][ks], adl[t][ks]);
                 }
-            f32x4 kacc[2][4];
+            f32x4 kacc[TW][4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) kacc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1908,25 +1965,25 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
                 for (int kt = 0; kt < 4; ++kt) {
                     const bf16x8 bv = img_row(LV, 16 * kt + r, ks, g);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < TW; ++t) {
                         mma(kacc[t][kt], adl[t][ks], bv);
                         mma(kacc[t][kt], adh[t][ks], bv);
                     }
                 }
 #pragma unroll
             for (int tk = 0; tk < 2; ++tk) {
-                bf16x8 aqh[2], aql[2];
+                bf16x8 aqh[TW], aql[TW];
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    aqh[t] = img_tr(LQH, 2 * w + t, tk, lane);
-                    aql[t] = img_tr(LQL, 2 * w + t, tk, lane);
+                for (int t = 0; t < TW; ++t) {
+                    aqh[t] = img_tr(LQH, TW * w + t, tk, lane);
+                    aql[t] = img_tr(LQL, TW * w + t, tk, lane);
                 }
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
                     if (tk == 0 && kt >= 2) continue;   // queries 0 .. 31 see no key of these tiles
                     const bf16x8 bh_ = img_tr(LMH, kt, tk, lane), bl = img_tr(LML, kt, tk, lane);
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < TW; ++t) {
                         mma(kacc[t][kt], aql[t], bh_);
                         mma(kacc[t][kt], aqh[t], bl);
                         mma(kacc[t][kt], aqh[t], bh_);
@@ -1939,11 +1996,11 @@ __global__ void __launch_bounds__(256) bwd_chunk_k_kernel(const float* gq, const
                 const int key = 16 * kt + r;
                 if (key >= nv) continue;
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < TW; ++t) {
                     f32x4 val;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) val[i] = kacc[t][kt][i] + prr[t][i];
-                    *reinterpret_cast<f32x4*>(dkh + (int64_t)key * KC + 32 * w + 16 * t + 4 * g) = val;
+                    *reinterpret_cast<f32x4*>(dkh + (int64_t)key * KC + 16 * (TW * w + t) + 4 * g) = val;
                 }
             }
         }
@@ -2158,11 +2215,11 @@ void launch_bwd_gamma_split(const void* x, const float* bf, const double* cq, fl
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
     const bf16x8* fr = reinterpret_cast<const bf16x8*>(bf);
     switch (KT) {
-        case 1: bwd_gamma_split_kernel<1, 8><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
-        case 2: bwd_gamma_split_kernel<2, 8><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
-        case 4: bwd_gamma_split_kernel<4, 8><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
-        case 8: bwd_gamma_split_kernel<8, 4><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
-        default: bwd_gamma_split_kernel<16, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        case 1: bwd_gamma_split_kernel<1, 8, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        case 2: bwd_gamma_split_kernel<2, 8, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        case 4: bwd_gamma_split_kernel<4, 8, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        case 8: bwd_gamma_split_kernel<8, 4, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        default: bwd_gamma_split_kernel<16, 2, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
     }
 }
 
@@ -2201,8 +2258,11 @@ bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const v
     int per = 4;
     while (per > 1 && BH * ((n_st + per - 1) / per) < 1024) per /= 2;
     const int64_t groups = (n_st + per - 1) / per;
-    bwd_chunk_q_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gq, gk, v, dout, stt, rs, rt, ac,
-                                                                                    mt, dgq, N, n_st, per, dva, eps);
+    const dim3 grid((unsigned)(BH * groups));
+    // four wavefronts: eight (two per SIMD, half the tiles each) measured no faster (936 vs 944 us per
+    // launch at B1 H16 N65536) and spill
+    bwd_chunk_q_kernel<128, 128, 4><<<grid, dim3(256), 0, s>>>(gq, gk, v, dout, stt, rs, rt, ac, mt, dgq, N, n_st, per,
+                                                                dva, eps);
     return true;
 }
 
@@ -2231,8 +2291,8 @@ bool launch_bwd_chunk_k(const float* gq, const float* gk, const void* v, const v
     int per = 4;
     while (per > 1 && BH * ((n_st + per - 1) / per) < 1024) per /= 2;
     const int64_t groups = (n_st + per - 1) / per;
-    bwd_chunk_k_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gq, gk, v, dout, rs, rt, dgk, dv, N,
-                                                                                    n_st, per, dva);
+    const dim3 grid((unsigned)(BH * groups));
+    bwd_chunk_k_kernel<128, 128, 4><<<grid, dim3(256), 0, s>>>(gq, gk, v, dout, rs, rt, dgk, dv, N, n_st, per, dva);
     return true;
 }
 
