@@ -866,7 +866,8 @@ __device__ __forceinline__ void split4(const f32x4& v, bf16x4& hi, bf16x4& lo) {
 
 constexpr int kFusedChunk = 64;
 
-template <int KC, int DRC>
+// DL_IN: `dgamma` already holds dl (the fused chunk kernels formed it) and `gamma` is not read.
+template <int KC, int DRC, bool DL_IN>
 __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma, const float* dgamma, const void* x,
                                                              const float* mw, void* dx, float* gp, int64_t N, int H,
                                                              int seg, int64_t n_seg, int dxa) {
@@ -877,7 +878,7 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
     constexpr int IMG = C * 256;           // one bf16 image of the chunk
     constexpr int NCT = KC / 16;           // component tiles
     constexpr int NST = 4 * 2;             // dx stores per wave and chunk
-    __shared__ __attribute__((aligned(16))) char s_stage[2 * STG];   // gamma, dgamma rows of the chunk
+    __shared__ __attribute__((aligned(16))) char s_stage[(DL_IN ? 1 : 2) * STG];   // gamma, dgamma (or dl) rows
     __shared__ __attribute__((aligned(16))) char s_dl[2 * IMG];      // dl hi, dl lo
     __shared__ __attribute__((aligned(16))) char s_x[2 * IMG];       // x rows, two chunks
     lds_char* const LS = (lds_char*)s_stage;
@@ -896,7 +897,8 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
     const int nch = (int)((t1 - t0 + C - 1) / C);
 
     // buffer descriptors over this (batch, head): rows past N read as zero, their stores are dropped
-    const i32x4 rs_g = uniform_rsrc(make_rsrc_words(gamma + bh * N * KC, (uint32_t)(N * ROWB)));
+    // the first staged array: gamma, or dl with DL_IN; the second: dgamma
+    const i32x4 rs_g = uniform_rsrc(make_rsrc_words((DL_IN ? dgamma : gamma) + bh * N * KC, (uint32_t)(N * ROWB)));
     const i32x4 rs_d = uniform_rsrc(make_rsrc_words(dgamma + bh * N * KC, (uint32_t)(N * ROWB)));
     const i32x4 rs_x =
         uniform_rsrc(make_rsrc_words(reinterpret_cast<const uint16_t*>(x) + bh * N * DRC, (uint32_t)(N * DRC * 2)));
@@ -914,9 +916,10 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
         for (int b = 0; b < 8; b += 4) {
             dma16x4(rs_g, m0 + b * 1024, m0 + (b + 1) * 1024, m0 + (b + 2) * 1024, m0 + (b + 3) * 1024, v0 + b * 1024,
                     v0 + (b + 1) * 1024, v0 + (b + 2) * 1024, v0 + (b + 3) * 1024);
-            dma16x4(rs_d, m0 + STG + b * 1024, m0 + STG + (b + 1) * 1024, m0 + STG + (b + 2) * 1024,
-                    m0 + STG + (b + 3) * 1024, v0 + b * 1024, v0 + (b + 1) * 1024, v0 + (b + 2) * 1024,
-                    v0 + (b + 3) * 1024);
+            if constexpr (!DL_IN)
+                dma16x4(rs_d, m0 + STG + b * 1024, m0 + STG + (b + 1) * 1024, m0 + STG + (b + 2) * 1024,
+                        m0 + STG + (b + 3) * 1024, v0 + b * 1024, v0 + (b + 1) * 1024, v0 + (b + 2) * 1024,
+                        v0 + (b + 3) * 1024);
         }
         uint32_t xv[4];
 #pragma unroll
@@ -993,16 +996,21 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
             for (int j = 0; j < 8; ++j) {
                 const int rr = 2 * j + rl;
                 const f32x4 gv = lds_ld<f32x4>(gs + rr * ROWB + cl * 16);
-                const f32x4 dv = lds_ld<f32x4>(gs + STG + rr * ROWB + cl * 16);
-                float dot = gv[0] * dv[0] + gv[1] * dv[1] + gv[2] * dv[2] + gv[3] * dv[3];
+                f32x4 dl;
+                if constexpr (DL_IN) {
+                    dl = gv;
+                } else {
+                    const f32x4 dv = lds_ld<f32x4>(gs + STG + rr * ROWB + cl * 16);
+                    float dot = gv[0] * dv[0] + gv[1] * dv[1] + gv[2] * dv[2] + gv[3] * dv[3];
 #pragma unroll
-                for (int o = 1; o < 32; o <<= 1) dot += __shfl_xor(dot, o, 64);
+                    for (int o = 1; o < 32; o <<= 1) dot += __shfl_xor(dot, o, 64);
+                    dl = gv * (dv - dot);
+                }
                 bf16x4 hi, lo;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float v = gv[e] * (dv[e] - dot);
-                    hi[e] = (__bf16)v;
-                    lo[e] = (__bf16)(v - (float)hi[e]);
+                    hi[e] = (__bf16)dl[e];
+                    lo[e] = (__bf16)(dl[e] - (float)hi[e]);
                 }
                 const int off = img_chunk(16 * w + rr, cl >> 1) + ((cl & 1) << 3);
                 lds_st<bf16x4>(LDH + off, hi);
@@ -1231,6 +1239,56 @@ struct ChunkSplit {
     static constexpr int RPW = 64 / W;
 };
 
+// Epilogue of dGamma in the chunk kernels: acc[t][rt] rows = components 16 (TW w + t) + 4 g + i, column =
+// row 16 rt + r of the chunk (a query or a key).  Stores dGamma, or with emit_dl the posterior gradient
+// dl = gamma (dGamma - gamma . dGamma) of the row, gamma read back from the chunk's image (hi + lo, about
+// 16 significant bits); the row dot goes through part [W][64] in LDS (one barrier).  Rows past nv are
+// not stored.
+template <int TW, int W>
+__device__ __forceinline__ void finish_dgamma(f32x4 (&acc)[TW][4], const lds_char* gam_hi, const lds_char* gam_lo,
+                                              float (*part)[64], float* out, int nv, int w, int lane, int emit_dl) {
+    const int r = lane & 15, g = lane >> 4;
+    if (emit_dl) {
+        f32x4 gam[TW][4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            float d = 0.f;
+#pragma unroll
+            for (int t = 0; t < TW; ++t) {
+                const int off = img_slot(16 * rt + r, 4 * (TW * w + t) + g);
+                const bf16x4 hi = lds_ld<bf16x4>(gam_hi + off), lo = lds_ld<bf16x4>(gam_lo + off);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    gam[t][rt][i] = (float)hi[i] + (float)lo[i];
+                    d += gam[t][rt][i] * acc[t][rt][i];
+                }
+            }
+            d += __shfl_xor(d, 16, 64);
+            d += __shfl_xor(d, 32, 64);
+            if (g == 0) part[w][16 * rt + r] = d;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            float dot = 0.f;
+#pragma unroll
+            for (int p = 0; p < W; ++p) dot += part[p][16 * rt + r];
+#pragma unroll
+            for (int t = 0; t < TW; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[t][rt][i] = gam[t][rt][i] * (acc[t][rt][i] - dot);
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const int row = 16 * rt + r;
+        if (row >= nv) continue;
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+            *reinterpret_cast<f32x4*>(out + (int64_t)row * 128 + 16 * (TW * w + t) + 4 * g) = acc[t][rt];
+    }
+}
+
 // The query-side chunk work of the causal backward in one kernel (bf16 storage, K = d_v = 128).  From the
 // recomputed posteriors, V, dO and the state before the chunk S = [Vt | Z] (the exclusive prefix over
 // chunks of Gamma_K^T [V | 1]), per chunk of 64 tokens:
@@ -1252,7 +1310,7 @@ template <int KC, int VC, int W>
 __global__ void __launch_bounds__(W * 64) bwd_chunk_q_kernel(const float* gq, const float* gk, const void* v,
                                                              const void* dout, const float* stt, float* rs, float* rt,
                                                              float* ac_out, float* mt_out, float* dgq, int64_t N,
-                                                             int64_t n_st, int per, int dva, float eps) {
+                                                             int64_t n_st, int per, int dva, float eps, int emit_dl) {
     static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
     using CS = ChunkSplit<W>;
     constexpr int TW = CS::TW, QW = CS::QW, RPW = CS::RPW;
@@ -1661,20 +1719,17 @@ __global__ void __launch_bounds__(W * 64) bwd_chunk_q_kernel(const float* gq, co
                     }
                 }
             }
-            float* dqh = dgq + (bh * N + n0) * KC;
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) {
-                const int q = 16 * qt + r;
-                const float hq = s_h[q];
+                const float hq = s_h[16 * qt + r];
 #pragma unroll
                 for (int t = 0; t < TW; ++t) {
                     const int comp0 = 16 * (TW * w + t) + 4 * g;
-                    f32x4 val;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) val[i] = dacc[t][qt][i] + hq * s_z[comp0 + i];
-                    if (q < nv) *reinterpret_cast<f32x4*>(dqh + (int64_t)q * KC + comp0) = val;
+                    for (int i = 0; i < 4; ++i) dacc[t][qt][i] += hq * s_z[comp0 + i];
                 }
             }
+            finish_dgamma<TW, W>(dacc, LQH, LQL, s_part, dgq + (bh * N + n0) * KC, nv, w, lane, emit_dl);
         }
     }
 }
@@ -1692,7 +1747,7 @@ template <int KC, int VC, int W>
 __global__ void __launch_bounds__(W * 64) bwd_chunk_k_kernel(const float* gq, const float* gk, const void* v,
                                                              const void* dout, const float* rs, const float* rt,
                                                              float* dgk, void* dv, int64_t N, int64_t n_st, int per,
-                                                             int dva) {
+                                                             int dva, int emit_dl) {
     static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
     using CS = ChunkSplit<W>;
     constexpr int TW = CS::TW, QW = CS::QW, RPW = CS::RPW;
@@ -1703,7 +1758,7 @@ __global__ void __launch_bounds__(W * 64) bwd_chunk_k_kernel(const float* gq, co
     __shared__ __attribute__((aligned(16))) char s_v[IMG];       // V
     __shared__ __attribute__((aligned(16))) char s_g[2 * IMG];   // g hi, lo
     __shared__ __attribute__((aligned(16))) char s_m[2 * IMG];   // ac hi, lo; then mt hi, lo
-    __shared__ float s_h[C];
+    __shared__ float s_h[C], s_part[W][C];
     lds_char* const LQH = (lds_char*)s_q;
     lds_char* const LQL = LQH + IMG;
     lds_char* const LKH = (lds_char*)s_k;
@@ -1990,19 +2045,16 @@ __global__ void __launch_bounds__(W * 64) bwd_chunk_k_kernel(const float* gq, co
                     }
                 }
             }
-            float* dkh = dgk + (bh * N + n0) * KC;
+            // the r column of R: keys past N get none (their [V | 1] row is zero)
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
-                const int key = 16 * kt + r;
-                if (key >= nv) continue;
+                const bool valid = 16 * kt + r < nv;
 #pragma unroll
-                for (int t = 0; t < TW; ++t) {
-                    f32x4 val;
+                for (int t = 0; t < TW; ++t)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) val[i] = kacc[t][kt][i] + prr[t][i];
-                    *reinterpret_cast<f32x4*>(dkh + (int64_t)key * KC + 16 * (TW * w + t) + 4 * g) = val;
-                }
+                    for (int i = 0; i < 4; ++i) kacc[t][kt][i] += valid ? prr[t][i] : 0.f;
             }
+            finish_dgamma<TW, W>(kacc, LKH, LKL, s_part, dgk + (bh * N + n0) * KC, nv, w, lane, emit_dl);
         }
     }
 }
@@ -2252,7 +2304,7 @@ bool bwd_chunk_q_supported(int K, int d_v, bool f32) { return !f32 && K == 128 &
 
 bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const void* dout, const float* stt, float* rs,
                         float* rt, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st, int K,
-                        int d_v, int dva, float eps, hipStream_t s) {
+                        int d_v, int dva, float eps, bool emit_dl, hipStream_t s) {
     if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4) return false;
     // chunks per workgroup: enough workgroups for every compute unit several times over
     int per = 4;
@@ -2262,7 +2314,7 @@ bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const v
     // four wavefronts: eight (two per SIMD, half the tiles each) measured no faster (936 vs 944 us per
     // launch at B1 H16 N65536) and spill
     bwd_chunk_q_kernel<128, 128, 4><<<grid, dim3(256), 0, s>>>(gq, gk, v, dout, stt, rs, rt, ac, mt, dgq, N, n_st, per,
-                                                                dva, eps);
+                                                                dva, eps, emit_dl ? 1 : 0);
     return true;
 }
 
@@ -2286,22 +2338,28 @@ bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, int64_t 
 
 bool launch_bwd_chunk_k(const float* gq, const float* gk, const void* v, const void* dout, const float* rs,
                         const float* rt, float* dgk, void* dv, int64_t BH, int64_t N, int64_t n_st, int K, int d_v,
-                        int dva, hipStream_t s) {
+                        int dva, bool emit_dl, hipStream_t s) {
     if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4) return false;
     int per = 4;
     while (per > 1 && BH * ((n_st + per - 1) / per) < 1024) per /= 2;
     const int64_t groups = (n_st + per - 1) / per;
     const dim3 grid((unsigned)(BH * groups));
-    bwd_chunk_k_kernel<128, 128, 4><<<grid, dim3(256), 0, s>>>(gq, gk, v, dout, rs, rt, dgk, dv, N, n_st, per, dva);
+    bwd_chunk_k_kernel<128, 128, 4><<<grid, dim3(256), 0, s>>>(gq, gk, v, dout, rs, rt, dgk, dv, N, n_st, per, dva,
+                                                                emit_dl ? 1 : 0);
     return true;
 }
 
 bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* x, const float* mw, void* dx, float* gp,
-                           int64_t BH, int64_t N, int H, int K, int d_r, int dxa, int seg, hipStream_t s) {
+                           int64_t BH, int64_t N, int H, int K, int d_r, int dxa, int seg, bool dl_in, hipStream_t s) {
     if (!bwd_fused_rows_supported(K, d_r, false) || seg % kFusedChunk != 0 || dxa < 2 * d_r + 1) return false;
     const int64_t n_seg = (N + seg - 1) / seg;
-    bwd_fused_rows_kernel<128, 128><<<dim3((unsigned)(BH * n_seg)), dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N,
-                                                                                      H, seg, n_seg, dxa);
+    const dim3 grid((unsigned)(BH * n_seg));
+    if (dl_in)
+        bwd_fused_rows_kernel<128, 128, true><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, seg, n_seg,
+                                                                          dxa);
+    else
+        bwd_fused_rows_kernel<128, 128, false><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, seg, n_seg,
+                                                                           dxa);
     return true;
 }
 

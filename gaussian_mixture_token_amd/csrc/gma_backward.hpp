@@ -96,7 +96,7 @@ void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream
 bool bwd_chunk_q_supported(int K, int d_v, bool f32);
 bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const void* dout, const float* stt, float* rs,
                         float* rt, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st, int K,
-                        int d_v, int dva, float eps, hipStream_t s);
+                        int d_v, int dva, float eps, bool emit_dl, hipStream_t s);
 // The chunk terms Gamma_K^T [V | 1] of the prefix states (the same shapes): stt [BH, n_st, K, dva], columns
 // d_v .. dva - 1 = Z, 0, 0, 0 (before the prefix scan).
 bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, int64_t BH, int64_t N, int64_t n_st, int K,
@@ -106,7 +106,9 @@ bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, int64_t 
 // ac^T g [BH, N, d_v] bf16, recomputing ac and mt.
 bool launch_bwd_chunk_k(const float* gq, const float* gk, const void* v, const void* dout, const float* rs,
                         const float* rt, float* dgk, void* dv, int64_t BH, int64_t N, int64_t n_st, int K, int d_v,
-                        int dva, hipStream_t s);
+                        int dva, bool emit_dl, hipStream_t s);
+// emit_dl (both chunk kernels): write the posterior gradient dl = gamma (dGamma - gamma . dGamma) of each
+// row in place of dGamma (gamma as the chunk's split image holds it, about 16 significant bits).
 
 // Posterior gradient, routing-input gradient and parameter partials of one side in one kernel
 // (bf16 storage, K = d_r = 128; bwd_fused_rows_supported): from gamma and dgamma [BH, N, K] fp32, the
@@ -120,7 +122,8 @@ bool launch_bwd_chunk_k(const float* gq, const float* gk, const void* v, const v
 bool bwd_fused_rows_supported(int K, int d_r, bool f32);
 int bwd_fused_rows_seg(int64_t BH, int64_t N, int min_seg);
 bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* x, const float* mw, void* dx, float* gp,
-                           int64_t BH, int64_t N, int H, int K, int d_r, int dxa, int seg, hipStream_t s);
+                           int64_t BH, int64_t N, int H, int K, int d_r, int dxa, int seg, bool dl_in, hipStream_t s);
+// dl_in: dgamma already holds dl (from the chunk kernels with emit_dl) and gamma is not read.
 // Chunk-state scans over [n_outer][n][rec]: mode 0 exclusive prefix in place, 1 exclusive suffix in
 // place, 2 the total into entry 0.  rec is a multiple of 4 (K times d_v + 1 rounded up to 4) and st
 // 16-byte aligned.

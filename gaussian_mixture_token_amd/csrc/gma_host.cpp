@@ -1241,10 +1241,20 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     const View vv = rows_tok, ghv = rows_tok;
     const BwdGen gen_v{v, nullptr, GEN_VAUG, f32 ? 1 : 0, d_v};
     const BwdGen gen_gh{dout, rs, GEN_GH, f32 ? 1 : 0, d_v};
+    // Per side, the posterior gradient, the routing-input gradient and the parameter partials in one fused
+    // kernel where there is one for the shape.  The partials buffer holds n_sg segments of kBwdSeg tokens
+    // per side: the fused segments are no shorter, so their count fits.
+    const int fseg = bwd_fused_rows_seg(BH, N, kBwdSeg);
+    const int64_t fn = (N + fseg - 1) / fseg;
+    const bool fused = bwd_fused_rows_supported(K, d_r, f32) && !misaligned(qx, 16) && !misaligned(kx, 16) &&
+                       !misaligned(dqx, 16) && !misaligned(dkx, 16) && (N + 64) * K * 4 < (int64_t(1) << 31) &&
+                       fn <= b.n_sg;
     // Causal bf16 at K = d_v = 128: fused chunk kernels for the state terms, the query side (read phase,
-    // chunk terms of the suffix sums, dGamma_Q) and the key side (dGamma_K, dV)
+    // chunk terms of the suffix sums, dGamma_Q) and the key side (dGamma_K, dV).  With the fused row kernel
+    // after them they write dl in place of dGamma.
     const bool qfused = causal && bwd_chunk_q_supported(K, d_v, f32) && !misaligned(v, 16) && !misaligned(dout, 16) &&
                         !misaligned(dv, 16) && dva == d_v + 4;
+    const bool emit_dl = qfused && fused;
     // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
     if (qfused) {
         bool ok = true;
@@ -1261,7 +1271,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
             ok = launch_bwd_chunk_q(gq, gk, v, dout, stt, rs, rt, nullptr, nullptr, dgq, BH, N, b.n_st, K, d_v, dva,
-                                    b.eps, s);
+                                    b.eps, emit_dl, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused query-side chunk kernel for this shape");
         GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(rt, BH, b.n_st, rec, 1, s); }));
@@ -1288,7 +1298,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         // the key-side counterpart: dGamma_K and dV per chunk (ac and mt recomputed)
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            ok = launch_bwd_chunk_k(gq, gk, v, dout, rs, rt, dgk, dv, BH, N, b.n_st, K, d_v, dva, s);
+            ok = launch_bwd_chunk_k(gq, gk, v, dout, rs, rt, dgk, dv, BH, N, b.n_st, K, d_v, dva, emit_dl, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused key-side chunk kernel for this shape");
     } else {
@@ -1305,19 +1315,13 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     }
     // posterior gradients, then per side the routing-input gradient and the parameter partials: one
     // fused kernel per side where there is one for the shape (dl then stays on chip)
-    // The partials buffer holds n_sg segments of kBwdSeg tokens per side: the fused segments are no
-    // shorter, so their count fits.
-    const int fseg = bwd_fused_rows_seg(BH, N, kBwdSeg);
-    const int64_t fn = (N + fseg - 1) / fseg;
-    const bool fused = bwd_fused_rows_supported(K, d_r, f32) && !misaligned(qx, 16) && !misaligned(kx, 16) &&
-                       !misaligned(dqx, 16) && !misaligned(dkx, 16) && (N + 64) * K * 4 < (int64_t(1) << 31) &&
-                       fn <= b.n_sg;
     if (fused) {
         for (int side = 0; side < 2; ++side) {
             bool ok = true;
             GMA_TRY(timed_launch(K_BWD_FUSED, s, [&] {
                 ok = launch_bwd_fused_rows(side ? gk : gq, side ? dgk : dgq, side ? kx : qx, mw, side ? dkx : dqx,
-                                           gp + (size_t)side * BH * fn * K * dxa, BH, N, H, K, d_r, dxa, fseg, s);
+                                           gp + (size_t)side * BH * fn * K * dxa, BH, N, H, K, d_r, dxa, fseg, emit_dl,
+                                           s);
             }));
             if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused backward row kernel for this shape");
         }
