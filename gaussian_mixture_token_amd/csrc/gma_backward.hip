@@ -1115,16 +1115,20 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
 }
 
 // ---------------------------------------------------------------------------------- chunk states
-// The chunk terms of the causal prefix states, Gamma_K^T [V | 1] per chunk of 64 tokens (bf16 storage,
-// K = d_v = 128), written as [K][dva] records (columns d_v .. dva - 1: Z, then zeros).  A workgroup
-// walks `per` consecutive chunks of one (batch, head), the next chunk's rows loaded ahead; Gamma_K goes
-// to LDS as a bf16 hi + lo image, V as an exact one.  The product is formed transposed, V^T Gamma_K
-// (A = V^T, B = Gamma_K, both transposed fragments), so each lane stores four consecutive d_v columns
-// of one component; the Z row comes from a ones fragment.  Wave w takes d_v tiles 2 w, 2 w + 1 for all
+// The causal prefix states from the chunk terms Gamma_K^T [V | 1] (64 tokens per chunk, bf16 storage,
+// K = d_v = 128), as [K][dva] records (columns d_v .. dva - 1: Z, then zeros), in two passes over segments
+// of `per` consecutive chunks of one (batch, head): the first (totals) writes each segment's total into
+// seg [BH][ceil(n_st / per)]; an exclusive scan over seg gives the segments' prefixes; the second starts
+// a running sum at its segment's prefix and writes, for each chunk, the sum of the terms of all earlier
+// chunks into stt.  The running sum stays in registers; the next chunk's rows are loaded ahead.  Gamma_K
+// goes to LDS as a bf16 hi + lo image, V as an exact one.  The product is formed transposed, V^T Gamma_K
+// (A = V^T, B = Gamma_K, both transposed fragments), so each lane stores four consecutive d_v columns of
+// one component; the Z row comes from a ones fragment.  Wave w takes d_v tiles 2 w, 2 w + 1 for all
 // components, and the Z row of component tiles 2 w, 2 w + 1.
 template <int KC, int VC>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) bwd_chunk_state_kernel(const float* gk, const void* v, float* stt, int64_t N,
-                                                              int64_t n_st, int per, int dva) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_chunk_state_kernel(const float* gk, const void* v, float* stt, float* seg, int64_t N, int64_t n_st, int per,
+                       int dva, int totals) {
     static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
     constexpr int C = 64;
     constexpr int IMG = C * 256;
@@ -1167,9 +1171,41 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) b
         ones0 = bf16x8{o, o, o, o, o, o, o, o};
     }
 
+    // running sums: run[t][ct] in the accumulator layout below, zrun[hh] of the Z rows; the second pass
+    // starts at the segment's prefix
+    float* seg_rec = seg + (bh * ((n_st + per - 1) / per) + c0 / per) * rec;
+    f32x4 run[2][8], zrun[2];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) run[0][ct] = run[1][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    zrun[0] = zrun[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!totals) {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const float* row = seg_rec + (int64_t)(16 * ct + r) * dva;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) run[t][ct] = *reinterpret_cast<const f32x4*>(row + 32 * w + 16 * t + 4 * g);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            if (g == 0) zrun[hh] = *reinterpret_cast<const f32x4*>(seg_rec + (int64_t)(16 * (2 * w + hh) + r) * dva + VC);
+    }
+    auto store_rec = [&](float* rec_c) {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            float* row = rec_c + (int64_t)(16 * ct + r) * dva;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) *reinterpret_cast<f32x4*>(row + 32 * w + 16 * t + 4 * g) = run[t][ct];
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            if (g == 0) *reinterpret_cast<f32x4*>(rec_c + (int64_t)(16 * (2 * w + hh) + r) * dva + VC) = zrun[hh];
+    };
+
     fetch(c0);
     for (int64_t c = c0; c < c1; ++c) {
         if (c > c0) lds_barrier();
+        // this chunk's record: the terms of all earlier chunks
+        if (!totals) store_rec(stt + (bh * n_st + c) * rec);
         {
             const int rl = lane >> 5, cl = lane & 31;
 #pragma unroll
@@ -1185,10 +1221,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) b
         }
         if (c + 1 < c1) fetch(c + 1);
         lds_barrier();
-        // acc[t][ct] rows = d_v 32 w + 16 t + 4 g + i, column = component 16 ct + r
-        f32x4 acc[2][8];
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc[0][ct] = acc[1][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the chunk's term, added to the running sums: run[t][ct] rows = d_v 32 w + 16 t + 4 g + i, column =
+        // component 16 ct + r
 #pragma unroll
         for (int tk = 0; tk < 2; ++tk) {
             bf16x8 av[2];
@@ -1199,31 +1233,25 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) b
                 const bf16x8 bh_ = img_tr(LKH, ct, tk, lane), bl = img_tr(LKL, ct, tk, lane);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    mma(acc[t][ct], av[t], bl);
-                    mma(acc[t][ct], av[t], bh_);
+                    mma(run[t][ct], av[t], bl);
+                    mma(run[t][ct], av[t], bh_);
                 }
             }
         }
-        float* rec_c = stt + (bh * n_st + c) * rec;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            float* row = rec_c + (int64_t)(16 * ct + r) * dva;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) *reinterpret_cast<f32x4*>(row + 32 * w + 16 * t + 4 * g) = acc[t][ct];
-        }
-        // Z (row 0 of the ones fragment's product) and the zero padding: component tiles 2 w, 2 w + 1
+        // Z (row 0 of the ones fragment's product; rows 1 .. 3 stay zero, the padding): component tiles 2 w,
+        // 2 w + 1
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int ct = 2 * w + hh;
-            f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int tk = 0; tk < 2; ++tk) {
-                mma(zacc, ones0, img_tr(LKL, ct, tk, lane));
-                mma(zacc, ones0, img_tr(LKH, ct, tk, lane));
+                mma(zrun[hh], ones0, img_tr(LKL, ct, tk, lane));
+                mma(zrun[hh], ones0, img_tr(LKH, ct, tk, lane));
             }
-            if (g == 0) *reinterpret_cast<f32x4*>(rec_c + (int64_t)(16 * ct + r) * dva + VC) = zacc;
         }
     }
+    // the segment's total (first pass)
+    if (totals) store_rec(seg_rec);
 }
 
 // ---------------------------------------------------------------------------------- fused chunk, query side
@@ -2326,13 +2354,18 @@ int bwd_fused_rows_seg(int64_t BH, int64_t N, int min_seg) {
     return seg < min_seg ? min_seg : seg;
 }
 
-bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, int64_t BH, int64_t N, int64_t n_st, int K,
-                            int d_v, int dva, hipStream_t s) {
-    if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4) return false;
-    int per = 4;
-    while (per > 1 && BH * ((n_st + per - 1) / per) < 1024) per /= 2;
+int bwd_state_segment(int64_t BH, int64_t n_st) {
+    int per = 16;
+    while (per > 1 && BH * ((n_st + per - 1) / per) < 512) per /= 2;
+    return per;
+}
+
+bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, float* seg, int per, bool totals, int64_t BH,
+                            int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s) {
+    if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4 || per < 1) return false;
     const int64_t groups = (n_st + per - 1) / per;
-    bwd_chunk_state_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gk, v, stt, N, n_st, per, dva);
+    bwd_chunk_state_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gk, v, stt, seg, N, n_st, per,
+                                                                                        dva, totals ? 1 : 0);
     return true;
 }
 

@@ -97,10 +97,14 @@ bool bwd_chunk_q_supported(int K, int d_v, bool f32);
 bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const void* dout, const float* stt, float* rs,
                         float* rt, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st, int K,
                         int d_v, int dva, float eps, bool emit_dl, hipStream_t s);
-// The chunk terms Gamma_K^T [V | 1] of the prefix states (the same shapes): stt [BH, n_st, K, dva], columns
-// d_v .. dva - 1 = Z, 0, 0, 0 (before the prefix scan).
-bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, int64_t BH, int64_t N, int64_t n_st, int K,
-                            int d_v, int dva, hipStream_t s);
+// The prefix states of the chunk terms Gamma_K^T [V | 1] (the same shapes), in segments of `per` chunks
+// (bwd_state_segment), two passes: totals = true writes each segment's total into seg [BH, ceil(n_st /
+// per), K, dva]; after an exclusive scan of seg, totals = false writes each chunk's exclusive prefix
+// state into stt [BH, n_st, K, dva] (the segment's prefix plus the earlier chunks of the segment).
+// Columns d_v .. dva - 1 = Z, 0, 0, 0.
+int bwd_state_segment(int64_t BH, int64_t n_st);
+bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, float* seg, int per, bool totals, int64_t BH,
+                            int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s);
 // Its key-side counterpart (the same shapes): from gq, gk, v, dout, rs and the exclusive suffix states
 // rt [BH, n_st, K, dva] it writes dgk = [V | 1] R^T + mt^T Gamma_Q [BH, N, K] and dv = Gamma_K Rv +
 // ac^T g [BH, N, d_v] bf16, recomputing ac and mt.

@@ -333,8 +333,9 @@ struct BwdPlan {
     int st_step = 0;            // tokens per state entry
     int64_t n_st = 0, n_sg = 0;  // state entries and parameter segments per (batch, head)
     size_t off_bf = 0, off_cq = 0, off_mw = 0, off_gq = 0, off_gk = 0, off_dgq = 0, off_dgk = 0, off_gh = 0,
-           off_pp = 0, off_st = 0, off_rt = 0, off_ac = 0, off_mt = 0, off_dvt = 0, off_gp = 0,
+           off_pp = 0, off_st = 0, off_rt = 0, off_ac = 0, off_mt = 0, off_dvt = 0, off_gp = 0, off_sgs = 0,
            total = 0;
+    int sper = 1;   // causal: chunks per state segment (bwd_state_segment)
 };
 
 gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
@@ -385,6 +386,9 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
     take(&b->off_mt, causal ? b->BH * b->n_st * C * C : 0);
     take(&b->off_dvt, causal ? rows * b->d_v : 0);
     take(&b->off_gp, 2 * b->BH * b->n_sg * b->K * b->dxa);
+    // causal: the state segments' totals, then their exclusive prefixes
+    b->sper = causal ? bwd_state_segment(b->BH, b->n_st) : 1;
+    take(&b->off_sgs, causal ? b->BH * ((b->n_st + b->sper - 1) / b->sper) * rec : 0);
     b->total = off;
     return GMA_SUCCESS;
 }
@@ -1256,17 +1260,25 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
                         !misaligned(dv, 16) && dva == d_v + 4;
     const bool emit_dl = qfused && fused;
     // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
+    // (fused: the totals of state segments of b.sper chunks, their exclusive scan, then the prefixes of
+    // every chunk, from the segment's prefix on)
+    float* sgs = F(b.off_sgs);
+    const int64_t n_sgs = (b.n_st + b.sper - 1) / b.sper;
     if (qfused) {
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            ok = launch_bwd_chunk_state(gk, v, stt, BH, N, b.n_st, K, d_v, dva, s);
+            ok = launch_bwd_chunk_state(gk, v, stt, sgs, b.sper, true, BH, N, b.n_st, K, d_v, dva, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no chunk-state kernel for this shape");
+        GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(sgs, BH, n_sgs, rec, 0, s); }));
+        GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
+            launch_bwd_chunk_state(gk, v, stt, sgs, b.sper, false, BH, N, b.n_st, K, d_v, dva, s);
+        }));
     } else {
         GMA_TRY(gemm(tok(gk, K), true, vv, false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{},
                      gen_v));
+        GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, causal ? 0 : 2, s); }));
     }
-    GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, causal ? 0 : 2, s); }));
     if (qfused) {
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
