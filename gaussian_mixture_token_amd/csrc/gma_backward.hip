@@ -1254,6 +1254,164 @@ bwd_chunk_state_kernel(const float* gk, const void* v, float* stt, float* seg, i
     if (totals) store_rec(seg_rec);
 }
 
+// ---------------------------------------------------------------------------------- suffix states
+// The causal suffix states R_c = sum over the chunks after c of Gamma_Q^T [g | h] (64 tokens per chunk,
+// bf16 storage, K = d_v = 128), as [K][dva] records (columns d_v .. dva - 1: the h sums r, then zeros),
+// from the recomputed Gamma_Q, dO and the per-row pairs rs = (1 / den, h): g = dO / den.  Two passes
+// over segments of `per` consecutive chunks of one (batch, head), as for the prefix states: the first
+// (totals) writes each segment's total into seg; after an exclusive suffix scan of seg the second walks
+// its segment backwards from the segment's suffix and writes each chunk's R.  Gamma_Q and g go to LDS as
+// bf16 hi + lo images; the product is formed transposed, g^T Gamma_Q, so each lane stores four
+// consecutive d_v columns of one component; the r row comes from an h fragment (row 0 = h).  Wave w takes
+// d_v tiles 2 w, 2 w + 1 for all components and the r row of component tiles 2 w, 2 w + 1.
+template <int KC, int VC>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_suffix_state_kernel(const float* gq, const void* dout, const float* rs, float* rt, float* seg, int64_t N,
+                        int64_t n_st, int per, int dva, int totals) {
+    static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
+    constexpr int C = 64;
+    constexpr int IMG = C * 256;
+    __shared__ __attribute__((aligned(16))) char s_q[2 * IMG];   // Gamma_Q hi, lo
+    __shared__ __attribute__((aligned(16))) char s_g[2 * IMG];   // g hi, lo
+    __shared__ float s_h[C];
+    lds_char* const LQH = (lds_char*)s_q;
+    lds_char* const LQL = LQH + IMG;
+    lds_char* const LGH = (lds_char*)s_g;
+    lds_char* const LGL = LGH + IMG;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t groups = (n_st + per - 1) / per;
+    const int64_t bh = blockIdx.x / groups;
+    const int64_t c0 = (blockIdx.x % groups) * per;
+    const int64_t c1 = c0 + per < n_st ? c0 + per : n_st;
+    const int64_t rec = (int64_t)KC * dva;
+
+    f32x4 pq[8];
+    u32x4 pd[4];
+    float pr0[4], pr1[4];
+    auto fetch = [&](int64_t c) {
+        const int64_t n0 = c * C;
+        const int nv = (int)(N - n0 < C ? N - n0 : C);
+        const float* gqh = gq + (bh * N + n0) * KC;
+        const uint16_t* dh = reinterpret_cast<const uint16_t*>(dout) + (bh * N + n0) * VC;
+        const int rl = lane >> 5, cl = lane & 31;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = 16 * w + 2 * j + rl;
+            pq[j] = row < nv ? *reinterpret_cast<const f32x4*>(gqh + (int64_t)row * KC + 4 * cl) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int row = 16 * w + 4 * bb + (lane >> 4);
+            const bool ok = row < nv;
+            pd[bb] = ok ? *reinterpret_cast<const u32x4*>(dh + (int64_t)row * VC + 8 * (lane & 15)) : u32x4{0u, 0u, 0u, 0u};
+            pr0[bb] = ok ? rs[(bh * N + n0 + row) * 2] : 0.f;
+            pr1[bb] = ok ? rs[(bh * N + n0 + row) * 2 + 1] : 0.f;
+        }
+    };
+
+    // running sums: run[t][ct] rows = d_v 32 w + 16 t + 4 g + i, column = component 16 ct + r; hrun[hh] row 0
+    // = the r sums of component tile 2 w + hh.  The second pass starts at the segment's suffix.
+    float* seg_rec = seg + (bh * groups + c0 / per) * rec;
+    f32x4 run[2][8], hrun[2];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) run[0][ct] = run[1][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    hrun[0] = hrun[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!totals) {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const float* row = seg_rec + (int64_t)(16 * ct + r) * dva;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) run[t][ct] = *reinterpret_cast<const f32x4*>(row + 32 * w + 16 * t + 4 * g);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            if (g == 0) hrun[hh] = *reinterpret_cast<const f32x4*>(seg_rec + (int64_t)(16 * (2 * w + hh) + r) * dva + VC);
+    }
+    auto store_rec = [&](float* rec_c) {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            float* row = rec_c + (int64_t)(16 * ct + r) * dva;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) *reinterpret_cast<f32x4*>(row + 32 * w + 16 * t + 4 * g) = run[t][ct];
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            if (g == 0) *reinterpret_cast<f32x4*>(rec_c + (int64_t)(16 * (2 * w + hh) + r) * dva + VC) = hrun[hh];
+    };
+
+    // the second pass walks its segment backwards (a suffix), the first in any order
+    fetch(c1 - 1);
+    for (int64_t c = c1 - 1; c >= c0; --c) {
+        if (c < c1 - 1) lds_barrier();
+        if (!totals) store_rec(rt + (bh * n_st + c) * rec);   // the terms of all later chunks
+        {
+            const int rl = lane >> 5, cl = lane & 31;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int off = img_slot(16 * w + 2 * j + rl, cl);
+                bf16x4 hi, lo;
+                split4(pq[j], hi, lo);
+                lds_st<bf16x4>(LQH + off, hi);
+                lds_st<bf16x4>(LQL + off, lo);
+            }
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int row = 16 * w + 4 * bb + (lane >> 4), ch = lane & 15;
+                const bf16x8 dv8 = __builtin_bit_cast(bf16x8, pd[bb]);
+                float gv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) gv[e] = (float)dv8[e] * pr0[bb];
+                bf16x8 hi, lo;
+                split_bf16x8(gv, hi, lo);
+                lds_st<bf16x8>(LGH + img_chunk(row, ch), hi);
+                lds_st<bf16x8>(LGL + img_chunk(row, ch), lo);
+                if (ch == 0) s_h[row] = pr1[bb];
+            }
+        }
+        if (c > c0) fetch(c - 1);
+        lds_barrier();
+#pragma unroll
+        for (int tk = 0; tk < 2; ++tk) {
+            bf16x8 agh[2], agl[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                agh[t] = img_tr(LGH, 2 * w + t, tk, lane);
+                agl[t] = img_tr(LGL, 2 * w + t, tk, lane);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                const bf16x8 bh_ = img_tr(LQH, ct, tk, lane), bl = img_tr(LQL, ct, tk, lane);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    mma(run[t][ct], agl[t], bh_);
+                    mma(run[t][ct], agh[t], bl);
+                    mma(run[t][ct], agh[t], bh_);
+                }
+            }
+        }
+        // the r row: A fragment row 0 = h of the tokens (split), rows 1 .. 15 zero
+#pragma unroll
+        for (int tk = 0; tk < 2; ++tk) {
+            float hv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hv[e] = r == 0 ? s_h[32 * tk + 16 * (e >> 2) + 4 * g + (e & 3)] : 0.f;
+            bf16x8 hh_, hl;
+            split_bf16x8(hv, hh_, hl);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int ct = 2 * w + hh;
+                const bf16x8 bh_ = img_tr(LQH, ct, tk, lane), bl = img_tr(LQL, ct, tk, lane);
+                mma(hrun[hh], hl, bh_);
+                mma(hrun[hh], hh_, bl);
+                mma(hrun[hh], hh_, bh_);
+            }
+        }
+    }
+    if (totals) store_rec(seg_rec);   // the segment's total (first pass)
+}
+
 // ---------------------------------------------------------------------------------- fused chunk, query side
 // Ownership in the fused chunk kernels, for W = 4 or 8 wavefronts: TW = 8 / W of the eight 16-wide
 // tiles of d_v or of the components per wave (tiles TW w .. TW w + TW - 1); for the 64 x 64 blocks,
@@ -1600,8 +1758,9 @@ __global__ void __launch_bounds__(W * 64) bwd_chunk_q_kernel(const float* gq, co
         lds_barrier();   // g, h visible; dO no longer read
 
         // ---- rt^T = [g | h]^T Gamma_Q: racc[vt][t] rows = d_v 16 vt + 4 g + i (vt 8: the h row 128 and the
-        // zero padding), column = component 16 (TW w + t) + r
-        {
+        // zero padding), column = component 16 (TW w + t) + r (not where rt is null: the suffix-state
+        // kernel recomputes the terms)
+        if (rt) {
             float* rth = rt + (bh * n_st + c) * rec;
             f32x4 racc[9][TW];
 #pragma unroll
@@ -2290,7 +2449,9 @@ bool bwd_gamma_split_supported(int K, int d_r, bool f32) {
 void launch_bwd_gamma_split(const void* x, const float* bf, const double* cq, float* gamma, int64_t BH, int64_t N,
                             int H, int K, int d_r, hipStream_t s) {
     const int KT = bwd_gamma_tiles(K);
-    const int rows = 1024;
+    // two 16-row groups per wave: every fragment read from LDS serves both (four measured slower at KT = 8,
+    // 275 -> 289 us at B1 H16 N65536)
+    const int rows = 1024;   // a multiple of 64 G
     const dim3 grid((unsigned)((N + rows - 1) / rows * BH)), block(256);
     const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
     const bf16x8* fr = reinterpret_cast<const bf16x8*>(bf);
@@ -2366,6 +2527,15 @@ bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, float* s
     const int64_t groups = (n_st + per - 1) / per;
     bwd_chunk_state_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gk, v, stt, seg, N, n_st, per,
                                                                                         dva, totals ? 1 : 0);
+    return true;
+}
+
+bool launch_bwd_suffix_state(const float* gq, const void* dout, const float* rs, float* rt, float* seg, int per,
+                             bool totals, int64_t BH, int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s) {
+    if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4 || per < 1) return false;
+    const int64_t groups = (n_st + per - 1) / per;
+    bwd_suffix_state_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gq, dout, rs, rt, seg, N, n_st,
+                                                                                         per, dva, totals ? 1 : 0);
     return true;
 }
 

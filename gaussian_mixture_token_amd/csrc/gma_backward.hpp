@@ -89,7 +89,7 @@ void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream
 // The query-side chunk work of the causal backward in one kernel (bf16 storage, K = d_v = 128;
 // bwd_chunk_q_supported), one workgroup per (batch, head, chunk of 64 tokens): from gq, gk [BH, N, K],
 // v, dout [BH, N, d_v] bf16 and the exclusive prefix states stt [BH, n_st, K, dva] it writes rs
-// [BH N, 2] = (1 / den, h), rt [BH, n_st, K, dva] = Gamma_Q^T [g | h] per chunk (zero padded), dgq =
+// [BH N, 2] = (1 / den, h), rt (if not null) [BH, n_st, K, dva] = Gamma_Q^T [g | h] per chunk (zero padded), dgq =
 // [g | h] S^T + mt Gamma_K [BH, N, K] and, where ac and mt are not null, ac = tril(Gamma_Q Gamma_K^T)
 // and mt = tril([g | h] [V | 1]^T) [BH, n_st, 64, 64].  dva = d_v + 4; rows of v and dout 16-byte
 // aligned.  false: no kernel for this shape.
@@ -105,6 +105,12 @@ bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const v
 int bwd_state_segment(int64_t BH, int64_t n_st);
 bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, float* seg, int per, bool totals, int64_t BH,
                             int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s);
+// The suffix states R_c = sum over the later chunks of Gamma_Q^T [g | h] (the same shapes), from gq, dout and
+// rs, in two passes like launch_bwd_chunk_state: totals = true writes segment totals into seg; after an
+// exclusive suffix scan of seg, totals = false writes every chunk's R into rt [BH, n_st, K, dva] (columns
+// d_v .. dva - 1 = the h sums, 0, 0, 0).
+bool launch_bwd_suffix_state(const float* gq, const void* dout, const float* rs, float* rt, float* seg, int per,
+                             bool totals, int64_t BH, int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s);
 // Its key-side counterpart (the same shapes): from gq, gk, v, dout, rs and the exclusive suffix states
 // rt [BH, n_st, K, dva] it writes dgk = [V | 1] R^T + mt^T Gamma_Q [BH, N, K] and dv = Gamma_K Rv +
 // ac^T g [BH, N, d_v] bf16, recomputing ac and mt.
