@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix peaks
 METRIC = "GMA fwd tokens/sec (causal, N=64K, K=128) + % of HBM/MFMA roofline"
-METRIC_BWD = "GMA backward tokens/sec (causal, N=64K, K=128) + % of fp32 matrix-core roofline"
+METRIC_BWD = "GMA backward tokens/sec (causal, N=64K, K=128) + % of matrix-core roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -371,14 +371,20 @@ def main():
 
 
 def bwd_line(args, w, value, ms_per_step, kernels, T, dout, step_isolated):
-    """The backward's JSON line: the whole step against the fp32 matrix-core peak (every product of the
-    backward is an fp32 matrix-core product) and, for reference, against HBM."""
+    """The backward's JSON line: the whole step against the peak of the matrix cores its products run on
+    (bf16 storage: the bf16 matrix cores, each fp32 operand split into bf16 hi + lo, so about three
+    MFMAs per algorithmic product; fp32 storage: the fp32 matrix cores) and, for reference, against the
+    fp32 matrix-core peak and HBM."""
     step_s = ms_per_step * 1e-3
     flops = backward_flops_per_token_head(w) * T
     nbytes = backward_bytes_per_token_head(w) * T
-    peak = MFMA_PEAK_TFLOPS["f32"]
-    roof = {"bound": "mfma", "achieved": flops / step_s / 1e12, "peak": peak, "unit": "TFLOP/s",
-            "frac": flops / step_s / 1e12 / peak, "traffic": None, "kernel": "backward step (all kernels)",
+    units = "bf16" if w.dtype == "bf16" else "f32"
+    peak = MFMA_PEAK_TFLOPS[units]
+    achieved = flops / step_s / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+            "peak_units": units + (" (split operands)" if units == "bf16" else ""),
+            "fp32_frac": achieved / MFMA_PEAK_TFLOPS["f32"], "traffic": None,
+            "kernel": "backward step (all kernels)",
             "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": nbytes,
             "hbm_frac": nbytes / step_s / 1e9 / HBM_PEAK_GBS}
     cpu = None
@@ -388,7 +394,9 @@ def bwd_line(args, w, value, ms_per_step, kernels, T, dout, step_isolated):
     line = {
         "metric": METRIC_BWD, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32 arithmetic, %s storage" % w.dtype,
+        "vs_baseline": None,
+        "dtype": ("f32 accumulation, split-bf16 products, bf16 storage" if w.dtype == "bf16"
+                  else "f32 arithmetic, f32 storage"),
         "data": "synthetic (seeded N(0,1) inputs and dL/dO, N(0,1) means, U(-1,1) raw variances, "
                 "N(0,0.5^2) prior logits)",
         "config": {"workload": w.name, "pass": "backward", "mode": "causal" if w.causal else "bidirectional",

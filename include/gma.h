@@ -247,8 +247,10 @@ gma_status_t gma_decode_step_prepared(const gma_problem_t* problem, const void* 
  *           draw_var = dsigma2 * sigmoid(raw_var), dprior_logits = G - pi sum_k G_k (G = dlog pi).
  * Outputs (written, not accumulated): dqx, dkx [B, H, N, d_r] and dv [B, H, N, d_v] in the storage
  * dtype; dmu, draw_var [H, K, d_r] and dprior_logits [H, K] fp32.  The forward is recomputed from the
- * inputs (O is not an argument).  Every sum and product runs in fp32 on the fp32 matrix cores, also
- * for bf16 storage (inputs are upcast exactly; outputs are rounded once).  Workspace:
+ * inputs (O is not an argument).  Sums accumulate in fp32.  Products run on the fp32 matrix cores for
+ * fp32 storage; for bf16 storage on the bf16 matrix cores with every fp32 operand split into bf16
+ * hi + lo (about 16 significant bits; bf16 inputs are exact), and the outputs are rounded once.
+ * Workspace:
  * gma_workspace_size(problem, GMA_OP_BACKWARD_BIDIR or GMA_OP_BACKWARD_CAUSAL) bytes, about
  * B * H * N * (6 K + 3 (d_v + 1) + 4 d_r) * 4 bytes plus per-chunk states.  No gradient may overlap an
  * input, another gradient or the workspace. */

@@ -1,9 +1,9 @@
 """GPU parity of the backward pass (gma_backward_bidir / gma_backward_causal) against the fp64 oracle.
 
 Tolerance per gradient tensor, the forward's contract carried over: max |g_gpu - g_ref| / max |g_ref|
-<= 1e-4 for fp32 storage and <= 1e-2 for bf16 storage.  The backward computes in fp32 throughout
-(inputs upcast exactly, fp32 matrix cores), so for bf16 the error is dominated by the one rounding
-of dqx, dkx and dv to bf16 (unit roundoff 2^-8).
+<= 1e-4 for fp32 storage and <= 1e-2 for bf16 storage.  The backward accumulates in fp32; for bf16
+storage its products split every fp32 operand into bf16 hi + lo (about 16 significant bits), so the
+error is dominated by the one rounding of dqx, dkx and dv to bf16 (unit roundoff 2^-8).
 
 Inputs: the seeded workload generators (gaussian_mixture_token_amd.workloads) plus a seeded dL/dO.
 With d_r >= 64 and N(0, 1) routing inputs the posteriors are nearly one-hot, so the routing
