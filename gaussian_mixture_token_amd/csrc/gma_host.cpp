@@ -334,8 +334,14 @@ struct BwdPlan {
     int64_t n_st = 0, n_sg = 0;  // state entries and parameter segments per (batch, head)
     size_t off_bf = 0, off_cq = 0, off_mw = 0, off_gq = 0, off_gk = 0, off_dgq = 0, off_dgk = 0, off_gh = 0,
            off_pp = 0, off_st = 0, off_rt = 0, off_ac = 0, off_mt = 0, off_dvt = 0, off_gp = 0, off_sgs = 0,
-           total = 0;
+           off_vs = 0, off_ds = 0, off_dvs = 0, total = 0;
     int sper = 1;   // causal: chunks per state segment (bwd_state_segment)
+    // causal bf16 at K = d_v = 128: the fused chunk kernels, whose plan has no [num | den], no per-chunk
+    // 64 x 64 blocks and no fp32 dV; the suffix states share the bytes of the prefix states (the query side
+    // reads the last prefix before the first suffix is written), and there is room to stage V, dO and dV
+    // where the caller's rows are not 16-byte aligned (dO's staging shares the bytes of the parameter
+    // partials, which are written only after the last read of dO)
+    bool fq = false;
 };
 
 gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
@@ -371,6 +377,9 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
         off = align_up(off + (size_t)floats * sizeof(float), 256);
     };
     const int KT = bwd_gamma_tiles(b->K);
+    b->fq = causal && bwd_chunk_q_supported(b->K, b->d_v, b->f32) && b->dva == b->d_v + 4;
+    const int64_t gen = b->fq ? 0 : 1;   // arrays only the general path uses
+    const int64_t stage = (rows * b->d_v * 2 + 3) / 4;   // bf16 rows of V or dO, in floats
     take(&b->off_bf, b->H * ((b->d_r + 15) / 16) * 2 * KT * 256);
     take(&b->off_cq, b->H * 16 * KT * 2);   // fp64
     take(&b->off_mw, b->H * b->K * 2 * b->d_r);
@@ -379,13 +388,17 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
     take(&b->off_dgq, rows * b->K);
     take(&b->off_dgk, rows * b->K);
     take(&b->off_gh, rows * 2);
-    take(&b->off_pp, rows * b->dva);
+    take(&b->off_pp, gen * rows * b->dva);
     take(&b->off_st, b->BH * b->n_st * rec);
-    take(&b->off_rt, b->BH * b->n_st * rec);
-    take(&b->off_ac, causal ? b->BH * b->n_st * C * C : 0);
-    take(&b->off_mt, causal ? b->BH * b->n_st * C * C : 0);
-    take(&b->off_dvt, causal ? rows * b->d_v : 0);
-    take(&b->off_gp, 2 * b->BH * b->n_sg * b->K * b->dxa);
+    take(&b->off_rt, gen * b->BH * b->n_st * rec);
+    if (b->fq) b->off_rt = b->off_st;
+    take(&b->off_ac, causal ? gen * b->BH * b->n_st * C * C : 0);
+    take(&b->off_mt, causal ? gen * b->BH * b->n_st * C * C : 0);
+    take(&b->off_dvt, causal ? gen * rows * b->d_v : 0);
+    take(&b->off_vs, b->fq ? stage : 0);
+    take(&b->off_dvs, b->fq ? stage : 0);
+    take(&b->off_gp, std::max<int64_t>(2 * b->BH * b->n_sg * b->K * b->dxa, b->fq ? stage : 0));
+    b->off_ds = b->off_gp;
     // causal: the state segments' totals, then their exclusive prefixes
     b->sper = causal ? bwd_state_segment(b->BH, b->n_st) : 1;
     take(&b->off_sgs, causal ? b->BH * ((b->n_st + b->sper - 1) / b->sper) * rec : 0);
@@ -1256,9 +1269,27 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     // Causal bf16 at K = d_v = 128: fused chunk kernels for the state terms, the query side (read phase,
     // chunk terms of the suffix sums, dGamma_Q) and the key side (dGamma_K, dV).  With the fused row kernel
     // after them they write dl in place of dGamma.
-    const bool qfused = causal && bwd_chunk_q_supported(K, d_v, f32) && !misaligned(v, 16) && !misaligned(dout, 16) &&
-                        !misaligned(dv, 16) && dva == d_v + 4;
+    const bool qfused = b.fq;
     const bool emit_dl = qfused && fused;
+    // the chunk kernels read and write whole 16-byte pieces of bf16 rows: rows that are not 16-byte aligned
+    // go through aligned copies in the workspace
+    const void* vq = v;
+    const void* dq = dout;
+    void* dvq = dv;
+    const size_t row_bytes = (size_t)rows * d_v * 2;
+    if (qfused) {
+        if (misaligned(v, 16)) {
+            if (hipMemcpyAsync(w + b.off_vs, v, row_bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+                return fail(GMA_ERROR_LAUNCH, "staging copy of v failed");
+            vq = w + b.off_vs;
+        }
+        if (misaligned(dout, 16)) {
+            if (hipMemcpyAsync(w + b.off_ds, dout, row_bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+                return fail(GMA_ERROR_LAUNCH, "staging copy of dout failed");
+            dq = w + b.off_ds;
+        }
+        if (misaligned(dv, 16)) dvq = w + b.off_dvs;
+    }
     // write phase: Gamma_K^T [V | 1] per entry -> the state before each chunk / the total
     // (fused: the totals of state segments of b.sper chunks, their exclusive scan, then the prefixes of
     // every chunk, from the segment's prefix on)
@@ -1267,12 +1298,12 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     if (qfused) {
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            ok = launch_bwd_chunk_state(gk, v, stt, sgs, b.sper, true, BH, N, b.n_st, K, d_v, dva, s);
+            ok = launch_bwd_chunk_state(gk, vq, stt, sgs, b.sper, true, BH, N, b.n_st, K, d_v, dva, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no chunk-state kernel for this shape");
         GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(sgs, BH, n_sgs, rec, 0, s); }));
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            launch_bwd_chunk_state(gk, v, stt, sgs, b.sper, false, BH, N, b.n_st, K, d_v, dva, s);
+            launch_bwd_chunk_state(gk, vq, stt, sgs, b.sper, false, BH, N, b.n_st, K, d_v, dva, s);
         }));
     } else {
         GMA_TRY(gemm(tok(gk, K), true, vv, false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{},
@@ -1282,18 +1313,18 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     if (qfused) {
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            ok = launch_bwd_chunk_q(gq, gk, v, dout, stt, rs, nullptr, nullptr, nullptr, dgq, BH, N, b.n_st, K, d_v,
+            ok = launch_bwd_chunk_q(gq, gk, vq, dq, stt, rs, nullptr, nullptr, nullptr, dgq, BH, N, b.n_st, K, d_v,
                                     dva, b.eps, emit_dl, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused query-side chunk kernel for this shape");
         // the suffix states: segment totals of Gamma_Q^T [g | h], their exclusive suffix scan, then every
         // chunk's suffix from its segment's on (the segment array is free again)
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            launch_bwd_suffix_state(gq, dout, rs, rt, sgs, b.sper, true, BH, N, b.n_st, K, d_v, dva, s);
+            launch_bwd_suffix_state(gq, dq, rs, rt, sgs, b.sper, true, BH, N, b.n_st, K, d_v, dva, s);
         }));
         GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(sgs, BH, n_sgs, rec, 1, s); }));
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            launch_bwd_suffix_state(gq, dout, rs, rt, sgs, b.sper, false, BH, N, b.n_st, K, d_v, dva, s);
+            launch_bwd_suffix_state(gq, dq, rs, rt, sgs, b.sper, false, BH, N, b.n_st, K, d_v, dva, s);
         }));
     }
     if (!qfused) {
@@ -1318,9 +1349,11 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         // the key-side counterpart: dGamma_K and dV per chunk (ac and mt recomputed)
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            ok = launch_bwd_chunk_k(gq, gk, v, dout, rs, rt, dgk, dv, BH, N, b.n_st, K, d_v, dva, emit_dl, s);
+            ok = launch_bwd_chunk_k(gq, gk, vq, dq, rs, rt, dgk, dvq, BH, N, b.n_st, K, d_v, dva, emit_dl, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused key-side chunk kernel for this shape");
+        if (dvq != dv && hipMemcpyAsync(dv, dvq, row_bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return fail(GMA_ERROR_LAUNCH, "copy of the staged dv failed");
     } else {
         // dGamma_K = [V | 1] R^T (+ the same intra-chunk block transposed, times Gamma_Q)
         GMA_TRY(gemm(vv, false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false, gen_v));

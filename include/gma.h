@@ -252,8 +252,11 @@ gma_status_t gma_decode_step_prepared(const gma_problem_t* problem, const void* 
  * hi + lo (about 16 significant bits; bf16 inputs are exact), and the outputs are rounded once.
  * Workspace:
  * gma_workspace_size(problem, GMA_OP_BACKWARD_BIDIR or GMA_OP_BACKWARD_CAUSAL) bytes, about
- * B * H * N * (6 K + 3 (d_v + 1) + 4 d_r) * 4 bytes plus per-chunk states.  No gradient may overlap an
- * input, another gradient or the workspace. */
+ * B * H * N * (6 K + 3 (d_v + 1) + 4 d_r) * 4 bytes plus per-chunk states; causal bf16 at
+ * K = d_v = 128 (fused chunk kernels) about B * H * N * (4 K * 4 + 3 d_v * 2) bytes plus one array of
+ * per-chunk states, B * H * ceil(N / 64) * K * (d_v + 4) * 4 bytes (4.1 GB at B = 1, H = 16, N = 65536).
+ * There, v, dout or dv rows that are not 16-byte aligned are staged through aligned copies in the
+ * workspace.  No gradient may overlap an input, another gradient or the workspace. */
 gma_status_t gma_backward_bidir(const gma_problem_t* problem, const void* qx, const void* kx,
                                 const void* v, const float* mu, const float* raw_var,
                                 const float* prior_logits, const void* dout, void* dqx, void* dkx,

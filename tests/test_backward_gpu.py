@@ -180,3 +180,34 @@ def test_backward_peaked_posteriors(gma, dtype, causal):
     # components: a stress test of robustness, held to the bf16 bound on dv (the routing and mixture
     # gradients vanish except at such ties)
     check(w.with_(dtype="bf16"), inp, dout, causal, got, only=("dv",))
+
+
+def _shifted(t):
+    # the same values at an address 2 bytes past a 16-byte boundary (bf16 rows not 16-byte aligned)
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    out = buf[1:1 + t.numel()].view(t.shape)
+    out.copy_(t)
+    assert out.data_ptr() % 16 == 2
+    return out
+
+
+@pytest.mark.parametrize("which", ["v", "dout", "dv", "all"])
+def test_backward_fused_shape_with_misaligned_rows(gma, which):
+    # causal bf16 at K = d_v = 128 with v, dout or dv 2 bytes off a 16-byte boundary: staged through
+    # aligned copies in the workspace, same results as the aligned call
+    w = gma.workload(3).with_(heads=2, seq_len=700)
+    inp, dout = inputs(gma, w, True)
+    t = {k: x.to(DEV) for k, x in inp.items()}
+    d = dout.to(DEV)
+    ref = gma.backward(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], d, eps=w.eps, causal=True)
+    vv = _shifted(t["v"]) if which in ("v", "all") else t["v"]
+    dd = _shifted(d) if which in ("dout", "all") else d
+    grads = {k: torch.empty_like(x) for k, x in ref.items()}
+    if which in ("dv", "all"):
+        grads["dv"] = _shifted(torch.zeros_like(t["v"]))
+    got = gma.backward(t["qx"], t["kx"], vv, t["mu"], t["raw_var"], t["prior_logits"], dd, eps=w.eps, causal=True,
+                       grads=grads)
+    torch.cuda.synchronize()
+    for name in NAMES:
+        assert torch.equal(got[name], ref[name]), name
+    check(w, inp, dout, True, got)
