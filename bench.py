@@ -6,8 +6,11 @@ Default workload: causal, bf16 storage / fp32 accumulation, B=1, H=16, N=65536, 
 K=128, d_v=128.  Prints one JSON line.
 
 With --backward a step is one call of the backward instead (forward recompute and every
-gradient, from a seeded dL/dO); its line carries the whole step against the fp32 matrix-core
-roof, since every product of the backward runs in fp32.
+gradient, from a seeded dL/dO); its line carries the whole step against the peak of the matrix
+cores its products run on (bf16 with split operands for bf16 storage, fp32 for fp32 storage).
+
+The forward line also carries `copy_reference`: the rate a plain 1 GiB device copy sustains on the
+same GPU, beside the rate at which the step moves its measured HBM traffic.
 
 With --decode it times one-token causal decode steps at the workload's shape instead (mixture
 from the raw parameters every step, and prepared once), and prints their latency.
@@ -336,6 +339,12 @@ def main():
            "mfma_frac": kf * T / avg_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
            "traffic": load_traffic(w.name, dominant, src_hash)}
 
+    copy_gbs = copy_reference(dev)
+    copy_ref = {"kernel": "torch copy_ of 1 GiB fp32 into 1 GiB, 20 back to back", "gbs": copy_gbs,
+                "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
+                "step_traffic_gbs": None if traffic is None else traffic / step_s / 1e9,
+                "step_traffic_over_copy": None if traffic is None else traffic / step_s / 1e9 / copy_gbs}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -362,12 +371,33 @@ def main():
                                + ("" if args.rounds is None else ", %d rounds" % args.rounds)},
         "roofline": roof,
         "dominant_kernel": dom,
+        "copy_reference": copy_ref,
         "step_isolated": step_isolated,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "source_hash": src_hash,
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_reference(dev, steps: int = 20) -> float:
+    """GB/s of a plain device copy of 1 GiB into 1 GiB (torch's copy kernel), back to back on the current
+    stream after three untimed copies: the HBM rate an ordinary streaming kernel sustains on this GPU
+    next to the published peak, as context for the rate at which the step moves its own traffic."""
+    import torch
+    x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = steps * 2 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    return gbs
 
 
 def bwd_line(args, w, value, ms_per_step, kernels, T, dout, step_isolated):
