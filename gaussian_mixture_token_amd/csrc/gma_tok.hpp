@@ -235,18 +235,24 @@ tok_kernel(const MainArgs a) {
 #pragma unroll
         for (int part = 0; part < NPARTS; ++part) issue_part(ch, buf, part);
     };
+    // the first chunk's DMA goes out before the fragment and state loads below, so that its latency
+    // overlaps theirs (the waits further down then also cover those loads, which are issued after it)
+    if (ch0 < ch1) issue(REV ? ch1 - 1 : ch0, 0);
 
-    // ---- [a | b] operand fragments of every component (AGPRs), logit constants c (LDS)
+    // ---- [a | b] operand fragments of every component (AGPRs), logit constants c (LDS).  Every load is
+    // issued before the first is pinned, so that their latencies overlap (pinned one by one, each load
+    // waited for the previous: about 16 us per workgroup at 64 fragments)
     f16x8 abf[NCT][2 * NKS2];
     {
         const f16x8* abg = reinterpret_cast<const f16x8*>(a.ab) + (int64_t)h * NCT * 2 * NKS2 * 64;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int ks = 0; ks < 2 * NKS2; ++ks) {
-                abf[ct][ks] = abg[((int64_t)ct * 2 * NKS2 + ks) * 64 + lane];
-                pin_agpr(abf[ct][ks]);
-            }
+            for (int ks = 0; ks < 2 * NKS2; ++ks) abf[ct][ks] = abg[((int64_t)ct * 2 * NKS2 + ks) * 64 + lane];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int ks = 0; ks < 2 * NKS2; ++ks) pin_agpr(abf[ct][ks]);
         for (int k = tid; k < KC; k += 256) s_c[k] = a.cvec[(int64_t)h * KC + k];
     }
 
@@ -358,7 +364,6 @@ tok_kernel(const MainArgs a) {
         write_z();
     }
 
-    if (ch0 < ch1) issue(REV ? ch1 - 1 : ch0, 0);
     lds_barrier();   // s_c (and the bidirectional state) visible
 
     // Passes with one logits side (the aggregate passes: K; the stored-tile causal pass: Q) read the
