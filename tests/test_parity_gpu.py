@@ -151,6 +151,26 @@ def test_forward_cfg3_full_size_every_head(gma):
         assert err <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("rounds", [2, 3, 8])
+@pytest.mark.parametrize("cfg,N", [(3, 65536 + 777), (4, 65536 + 333)])
+def test_causal_rounds_match_the_oracle(gma, cfg, N, rounds, monkeypatch):
+    # the causal pair launched in rounds over the sequence (GMA_CAUSAL_ROUNDS, a measurement switch): the
+    # same result up to the summation order of the carried state, against the oracle, and bitwise
+    # reproducible.  Two heads give 128 segments per head, so N >= 8 * 128 * 64 tokens allows 8 rounds; the
+    # last round and the last segment are ragged
+    w = gma.workload(cfg).with_(batch=1, heads=2, seq_len=N)
+    say("forward rounds=%d %s" % (rounds, w))
+    inp = gma.make_inputs(w)
+    plain = gpu_forward(gma, w, inp)
+    monkeypatch.setenv("GMA_CAUSAL_ROUNDS", str(rounds))
+    o = gpu_forward(gma, w, inp)
+    o2 = gpu_forward(gma, w, inp)
+    assert torch.equal(o, o2)
+    err = rel_err(o, ref_forward(w, inp))
+    say("  rel err %.3e, max |rounds - plain| %.3e" % (err, (o.float() - plain.float()).abs().max().item()))
+    assert err <= TOL[w.dtype]
+
+
 def test_forward_cfg4_full_size_two_heads(gma):
     # 8 heads of 1,048,576 tokens on the GPU; the oracle checks a first and a last head
     w = gma.workload(4)
