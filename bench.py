@@ -13,9 +13,11 @@ The forward line also carries `copy_reference`: the rate a plain 1 GiB device co
 same GPU, beside the rate at which the step moves its measured HBM traffic.
 
 With --decode it times one-token causal decode steps at the workload's shape instead (mixture
-from the raw parameters every step, and prepared once), and prints their latency.
+from the raw parameters every step, and prepared once), and prints their latency.  With
+--responsibilities it times gma_responsibilities on the workload's K_X against the HBM roof of its
+own bytes (read the rows, write Gamma in fp32).
 
-    python bench.py [--steps K] [--warmup W] [--workload I] [--backward | --decode] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload I] [--backward | --decode | --responsibilities] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -175,6 +177,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time one-token causal decode steps (raw and prepared mixture) at the workload's B, H, "
                          "d_r, K, d_v instead of the forward")
+    ap.add_argument("--responsibilities", action="store_true",
+                    help="time gma_responsibilities (Gamma of every K_X row, fp32) at the workload's shape instead "
+                         "of the forward, against the HBM roof of its own bytes")
     ap.add_argument("--rounds", type=int, default=None,
                     help="launch the causal pass in this many rounds over the sequence (GMA_CAUSAL_ROUNDS; "
                          "a measured-slower schedule kept for comparison)")
@@ -213,6 +218,9 @@ def main():
     print("bench: workload %s" % w.name, file=sys.stderr, flush=True)
     if args.decode:
         decode_line(args, w, gma, dev)
+        return
+    if args.responsibilities:
+        resp_line(args, w, gma, dev, lib)
         return
     inp = gma.make_inputs(w)
     t = {k: v.to(dev) for k, v in inp.items()}
@@ -472,6 +480,68 @@ def decode_line(args, w, gma, dev):
             "config": {"workload": w.name, "pass": "decode", "batch": w.batch, "heads": w.heads,
                        "d_route": w.d_route, "n_comp": w.n_comp, "d_value": w.d_value},
             "us_per_step": res}
+    print(json.dumps(line), flush=True)
+
+
+def resp_line(args, w, gma, dev, lib):
+    """gma_responsibilities on the workload's K_X: back-to-back calls between events on the launch stream,
+    against HBM (it reads d_r and writes K fp32 per row), with the copy reference of the same run."""
+    import torch
+    from gaussian_mixture_token_amd import _lib
+    inp = gma.make_inputs(w)
+    x = inp["kx"].to(dev)
+    mu, rv, pl = inp["mu"].to(dev), inp["raw_var"].to(dev), inp["prior_logits"].to(dev)
+    del inp
+    out = torch.empty(w.batch, w.heads, w.seq_len, w.n_comp, dtype=torch.float32, device=dev)
+    prob = gma.problem(w.batch, w.heads, w.seq_len, w.d_route, w.n_comp, 1, w.torch_dtype, w.eps)
+    ws = torch.empty(max(gma.workspace_size(prob, _lib.GMA_OP_RESPONSIBILITIES), 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        gma.responsibilities(x, mu, rv, pl, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    lib.gma_timing_enable(1)
+    for k in range(lib.gma_kernel_count()):
+        lib.gma_timing_read(k, ctypes_double(), ctypes_int64())
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    lib.gma_timing_enable(0)
+    kernels = {}
+    for k in range(lib.gma_kernel_count()):
+        tot, n = ctypes_double(), ctypes_int64()
+        _lib.check(lib.gma_timing_read(k, tot, n))
+        if n.value:
+            kernels[lib.gma_kernel_name(k).decode()] = {"avg_us": 1e3 * tot.value / n.value, "launches": n.value,
+                                                        "launches_per_step": n.value / args.steps}
+    es = 2 if w.dtype == "bf16" else 4
+    T = w.batch * w.heads * w.seq_len
+    nbytes = (es * w.d_route + 4 * w.n_comp) * T
+    flops = 4 * w.n_comp * w.d_route * T
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    copy_gbs = copy_reference(dev)
+    line = {"metric": "GMA responsibilities rows/sec (Gamma of every row, fp32 out) + % of HBM roofline",
+            "value": T / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+            "data": "synthetic (the workload's K_X and mixture)",
+            "config": {"workload": w.name, "pass": "responsibilities", "batch": w.batch, "heads": w.heads,
+                       "seq_len": w.seq_len, "d_route": w.d_route, "n_comp": w.n_comp},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_step": nbytes,
+                         "algorithmic_flops_per_step": flops,
+                         "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype]},
+            "copy_reference": {"gbs": copy_gbs, "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
+                               "step_over_copy": gbs / copy_gbs},
+            "kernels": kernels, "source_hash": kernel_source_hash()}
     print(json.dumps(line), flush=True)
 
 

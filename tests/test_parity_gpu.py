@@ -85,6 +85,22 @@ def test_responsibilities_match_oracle(gma, cfg, shape):
     assert err <= TOL_GAMMA[w.dtype]
 
 
+@pytest.mark.parametrize("cfg,heads,N", [(3, 4, 65536 + 333), (4, 2, 65536 + 77)])
+def test_responsibilities_long_walks(gma, cfg, heads, N):
+    # long sequences, so that each workgroup walks several consecutive chunks (a few heads spread the
+    # sequence over all compute units) with a ragged last chunk; every row against the oracle
+    w = gma.workload(cfg).with_(batch=1, heads=heads, seq_len=N)
+    say("responsibilities long %s" % (w,))
+    inp = gma.make_inputs(w)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    got = gma.responsibilities(t["kx"], t["mu"], t["raw_var"], t["prior_logits"]).cpu().numpy().astype(np.float64)
+    ref = oracle.responsibilities(inp["kx"], inp["mu"], inp["raw_var"], inp["prior_logits"])
+    err = np.abs(got - ref).max()
+    say("  max |dGamma| = %.3e" % err)
+    assert err <= TOL_GAMMA[w.dtype]
+    np.testing.assert_allclose(got.sum(-1), 1.0, atol=1e-5)
+
+
 # ------------------------------------------------------------------------------------ forward parity
 
 
