@@ -441,6 +441,14 @@ main_kernel(const MainArgs a) {
         rs_v = make_rsrc_words(vv, (uint32_t)(N * a.d_v * 2));
         rs_o = make_rsrc(oo, (uint32_t)(N * a.d_v * 2));
     }
+    // responsibilities through buffer stores where the (batch, head)'s Gamma rows fit 31-bit offsets
+    // (bit 31 marks a dropped store); otherwise plain stores and a full wait per chunk
+    [[maybe_unused]] const bool resp_exact =
+        DMA && MODE == MODE_RESP && !a.stat_usage && (uint64_t)N * (uint64_t)a.K * 4u < 0x80000000ull;
+    [[maybe_unused]] const bool resp_k4 = (a.K & 3) == 0;
+    [[maybe_unused]] __amdgpu_buffer_rsrc_t rs_g;
+    if constexpr (DMA && MODE == MODE_RESP)
+        rs_g = make_rsrc(resp_exact ? a.gamma + (int64_t)bh * N * a.K : a.gamma, resp_exact ? (uint32_t)(N * a.K * 4) : 0u);
 
     // XOR swizzle of the 16-byte chunks of a staged X row: rows r and r + 8 of a 16-row fragment use
     // disjoint bank halves, so fragment reads are conflict-free
@@ -573,7 +581,11 @@ main_kernel(const MainArgs a) {
         // ---- inputs of this chunk in LDS
         if constexpr (DMA) {
             if (ch == ch0) wait_vmcnt<0>();
-            else wait_vmcnt<NSTORE>();
+            else if (RESP && resp_exact) {
+                // the previous chunk's Gamma stores were issued after this chunk's DMA: wait for the DMA only
+                if (resp_k4) wait_vmcnt<NT * KT_W>();
+                else wait_vmcnt<4 * NT * KT_W>();
+            } else wait_vmcnt<NSTORE>();
             convert_own_x(raw);
             lds_barrier();
             if (ch + 1 < ch1) issue_dma(ch + 1, raw_next);
@@ -758,7 +770,33 @@ main_kernel(const MainArgs a) {
                 if constexpr (!DMA) lds_barrier();  // staging buffers are rewritten by the next chunk
                 return;
             }
-            // Gamma rows out: lane holds comps 16ct + 4g .. +3 of token 16tt + r
+            // Gamma rows out: lane holds comps 16ct + 4g .. +3 of token 16tt + r.  DMA path: buffer stores, the
+            // same number on every lane and chunk (rows past N fall past the descriptor's range, pad
+            // components get bit 31 of the offset; both are dropped), so that the next chunk can wait for
+            // its own DMA alone
+            if constexpr (DMA) {
+                if (resp_exact) {
+#pragma unroll
+                    for (int tt = 0; tt < NT; ++tt) {
+                        const uint32_t rowb = (uint32_t)(n0 + tt * 16 + lr) * (uint32_t)a.K * 4u;
+#pragma unroll
+                        for (int kt = 0; kt < KT_W; ++kt) {
+                            const int c0 = (w * KT_W + kt) * 16 + lg * 4;
+                            if (resp_k4) {
+                                const uint32_t off = (rowb + (uint32_t)c0 * 4u) | (c0 + 4 <= a.K ? 0u : 0x80000000u);
+                                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lq[kt][tt]), rs_g, off, 0, 0);
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const uint32_t off = (rowb + (uint32_t)(c0 + i) * 4u) | (c0 + i < a.K ? 0u : 0x80000000u);
+                                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lq[kt][tt][i]), rs_g, off, 0, 0);
+                                }
+                            }
+                        }
+                    }
+                    return;
+                }
+            }
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt) {
                 const int tok = tt * 16 + lr;

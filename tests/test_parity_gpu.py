@@ -85,11 +85,15 @@ def test_responsibilities_match_oracle(gma, cfg, shape):
     assert err <= TOL_GAMMA[w.dtype]
 
 
-@pytest.mark.parametrize("cfg,heads,N", [(3, 4, 65536 + 333), (4, 2, 65536 + 77)])
-def test_responsibilities_long_walks(gma, cfg, heads, N):
+@pytest.mark.parametrize("cfg,heads,N,shape", [(3, 4, 65536 + 333, None), (4, 2, 65536 + 77, None),
+                                                (3, 2, 20000 + 5, (64, 7, 16)), (3, 2, 20000 + 5, (64, 100, 16))])
+def test_responsibilities_long_walks(gma, cfg, heads, N, shape):
     # long sequences, so that each workgroup walks several consecutive chunks (a few heads spread the
-    # sequence over all compute units) with a ragged last chunk; every row against the oracle
+    # sequence over all compute units) with a ragged last chunk, also with K not a multiple of 4 (single
+    # stores) and with padding components; every row against the oracle
     w = gma.workload(cfg).with_(batch=1, heads=heads, seq_len=N)
+    if shape:
+        w = w.with_(d_route=shape[0], n_comp=shape[1], d_value=shape[2])
     say("responsibilities long %s" % (w,))
     inp = gma.make_inputs(w)
     t = {k: v.to(DEV) for k, v in inp.items()}
