@@ -587,7 +587,19 @@ __global__ void __launch_bounds__(256) bwd_gamma_split_kernel(const uint16_t* x,
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const bf16x8* fh = fr + (int64_t)h * S * KT * 4 * 64;
-    for (int i = tid; i < S * KT * 4 * 64; i += 256) s_f[i] = fh[i];
+    {
+        // the head's fragments into LDS, every load of a thread issued before the first store (one load
+        // in flight at a time cost about 15 us per workgroup); S * KT of the SMAX * KT slots are used
+        constexpr int NMAX = SMAX * KT;
+        const int n = S * KT;
+        bf16x8 tmp[NMAX];
+#pragma unroll
+        for (int j = 0; j < NMAX; ++j)
+            if (j < n) tmp[j] = fh[tid + 256 * j];
+#pragma unroll
+        for (int j = 0; j < NMAX; ++j)
+            if (j < n) s_f[tid + 256 * j] = tmp[j];
+    }
     // constants of the components this lane's accumulator rows hold: 16 kt + 4 g + i
     float cr[KT][4];
 #pragma unroll
