@@ -10,7 +10,9 @@ gradient, from a seeded dL/dO); its line carries the whole step against the peak
 cores its products run on (bf16 with split operands for bf16 storage, fp32 for fp32 storage).
 
 The forward line also carries `copy_reference`: the rate a plain 1 GiB device copy sustains on the
-same GPU, beside the rate at which the step moves its measured HBM traffic.
+same GPU, beside the rate at which the step moves its measured HBM traffic; and `exp2_reference`: the
+measured rate of the hardware exponential and the time the step's 2 K exponentials per token-head
+take at it.
 
 With --decode it times one-token causal decode steps at the workload's shape instead (mixture
 from the raw parameters every step, and prepared once), and prints their latency.  With
@@ -36,9 +38,9 @@ METRIC_BWD = "GMA backward tokens/sec (causal, N=64K, K=128) + % of matrix-core 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-# sources of the forward path's kernels and their launches (the backward and decode kernels live in
-# files of their own, which the forward's code does not include)
-_OTHER_PATHS = ("gma_backward", "gma_decode")
+# sources of the forward path's kernels and their launches (the backward and decode kernels and the
+# exponential-rate probe live in files of their own, which the forward's code does not include)
+_OTHER_PATHS = ("gma_backward", "gma_decode", "gma_probe")
 
 
 def kernel_source_hash(backward: bool = False) -> str:
@@ -347,6 +349,7 @@ def main():
            "mfma_frac": kf * T / avg_s / 1e12 / MFMA_PEAK_TFLOPS[w.dtype],
            "traffic": load_traffic(w.name, dominant, src_hash)}
 
+    exp_ref = exp2_reference(lib, w, T, step_s)
     copy_gbs = copy_reference(dev)
     copy_ref = {"kernel": "torch copy_ of 1 GiB fp32 into 1 GiB, 20 back to back", "gbs": copy_gbs,
                 "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
@@ -380,6 +383,7 @@ def main():
         "roofline": roof,
         "dominant_kernel": dom,
         "copy_reference": copy_ref,
+        "exp2_reference": exp_ref,
         "step_isolated": step_isolated,
         "kernels": kernels,
         "cpu_baseline": cpu,
@@ -406,6 +410,23 @@ def copy_reference(dev, steps: int = 20) -> float:
     gbs = steps * 2 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del x, y
     return gbs
+
+
+EXP2_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9   # CUs x SIMDs x lanes at a quarter of the full rate x clock
+
+
+def exp2_reference(lib, w, T, step_s):
+    """The measured rate of the hardware exponential (gma_probe_exp2_rate) beside the unit-count estimate,
+    and the time the step's 2 K exponentials per token-head (the softmax of both posteriors) would take at
+    it: the vector-unit floor of the step, next to its HBM and matrix-core floors."""
+    import ctypes
+    from gaussian_mixture_token_amd import _lib
+    rate = ctypes.c_double()
+    _lib.check(lib.gma_probe_exp2_rate(ctypes.byref(rate), None))
+    exps = 2 * w.n_comp * T
+    return {"exp2_per_s": rate.value, "estimate_per_s": EXP2_PEAK_PER_S, "exps_per_step": exps,
+            "floor_us": exps / rate.value * 1e6 if rate.value > 0 else None,
+            "frac_of_step": exps / rate.value / step_s if rate.value > 0 else None}
 
 
 def bwd_line(args, w, value, ms_per_step, kernels, T, dout, step_isolated):

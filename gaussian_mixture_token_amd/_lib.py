@@ -63,6 +63,7 @@ _SIGS = [
     ("gma_timing_read", ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     ("gma_kernel_count", ctypes.c_int, []),
     ("gma_kernel_name", ctypes.c_char_p, [ctypes.c_int]),
+    ("gma_probe_exp2_rate", ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]),
 ]
 
 

@@ -284,6 +284,13 @@ gma_status_t gma_timing_read(int kernel_id, double* total_ms, int64_t* launches)
 int gma_kernel_count(void);
 const char* gma_kernel_name(int kernel_id);
 
+/* Measurement support: the measured rate of the hardware base-2 exponential on the current device,
+ * in exponentials per second, written to *per_second.  The softmax of item 1 takes 2 K of them per
+ * token-head.  Runs one untimed and one timed launch on `stream` (NULL: the null stream) and waits
+ * for them; allocates no device memory.  GMA_ERROR_INVALID_VALUE if per_second is NULL,
+ * GMA_ERROR_LAUNCH if a HIP call fails (*per_second is then 0). */
+gma_status_t gma_probe_exp2_rate(double* per_second, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
