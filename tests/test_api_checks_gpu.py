@@ -87,3 +87,16 @@ def test_decode_rejects_bad_out_and_state(gma):
     with pytest.raises(ValueError):
         gma.decode_step(*args, state[:, :, :-1].contiguous())
     assert (state == 0).all()
+
+
+@pytest.mark.gpu
+def test_exp2_rate_probe(gma):
+    # the measurement entry point: a positive rate of the order the unit counts give (about 1e13 per second
+    # on this class of GPU; bounded loosely so that a clock change cannot fail it), and NULL rejected
+    import ctypes
+    from gaussian_mixture_token_amd import _lib
+    lib = _lib.load()
+    rate = ctypes.c_double()
+    assert lib.gma_probe_exp2_rate(ctypes.byref(rate), None) == 0
+    assert 1e11 < rate.value < 1e15
+    assert lib.gma_probe_exp2_rate(None, None) == 1
