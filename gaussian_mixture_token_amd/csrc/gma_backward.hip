@@ -1566,6 +1566,14 @@ __global__ void __launch_bounds__(W * 64) bwd_chunk_q_kernel(const float* gq, co
         }
     };
 
+    // segment total of the suffix-state terms Gamma_Q^T [g | h] over this walk (rt non-null: the walk is one
+    // state segment): racc[vt][t] rows = d_v 16 vt + 4 g + i (vt 8: the h row and zero padding), column =
+    // component 16 (TW w + t) + r, summed over the walk's chunks in order
+    f32x4 racc[9][TW];
+#pragma unroll
+    for (int vt = 0; vt < 9; ++vt)
+#pragma unroll
+        for (int t = 0; t < TW; ++t) racc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     fetch(c0);
     for (int64_t c = c0; c < c1; ++c) {
         const int64_t n0 = c * C;
@@ -1769,16 +1777,9 @@ __global__ void __launch_bounds__(W * 64) bwd_chunk_q_kernel(const float* gq, co
         }
         lds_barrier();   // g, h visible; dO no longer read
 
-        // ---- rt^T = [g | h]^T Gamma_Q: racc[vt][t] rows = d_v 16 vt + 4 g + i (vt 8: the h row 128 and the
-        // zero padding), column = component 16 (TW w + t) + r (not where rt is null: the suffix-state
-        // kernel recomputes the terms)
+        // ---- the chunk's term [g | h]^T Gamma_Q of the suffix states, added to the walk's total (not where rt
+        // is null: the suffix-state kernel then forms the segment totals itself)
         if (rt) {
-            float* rth = rt + (bh * n_st + c) * rec;
-            f32x4 racc[9][TW];
-#pragma unroll
-            for (int vt = 0; vt < 9; ++vt)
-#pragma unroll
-                for (int t = 0; t < TW; ++t) racc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int tk = 0; tk < 2; ++tk) {
                 bf16x8 bqh[TW], bql[TW];
@@ -1808,13 +1809,6 @@ __global__ void __launch_bounds__(W * 64) bwd_chunk_q_kernel(const float* gq, co
                     mma(racc[8][t], hh, bql[t]);
                     mma(racc[8][t], hh, bqh[t]);
                 }
-            }
-#pragma unroll
-            for (int t = 0; t < TW; ++t) {
-                float* row = rth + (int64_t)(16 * (TW * w + t) + r) * dva;
-#pragma unroll
-                for (int vt = 0; vt < 8; ++vt) *reinterpret_cast<f32x4*>(row + 16 * vt + 4 * g) = racc[vt][t];
-                if (g == 0) *reinterpret_cast<f32x4*>(row + VC) = racc[8][t];
             }
         }
 
@@ -1929,6 +1923,16 @@ __global__ void __launch_bounds__(W * 64) bwd_chunk_q_kernel(const float* gq, co
                 }
             }
             finish_dgamma<TW, W>(dacc, LQH, LQL, s_part, dgq + (bh * N + n0) * KC, nv, w, lane, emit_dl);
+        }
+    }
+    if (rt) {
+        float* seg_rec = rt + (bh * groups + c0 / per) * rec;
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+            float* row = seg_rec + (int64_t)(16 * (TW * w + t) + r) * dva;
+#pragma unroll
+            for (int vt = 0; vt < 8; ++vt) *reinterpret_cast<f32x4*>(row + 16 * vt + 4 * g) = racc[vt][t];
+            if (g == 0) *reinterpret_cast<f32x4*>(row + VC) = racc[8][t];
         }
     }
 }
@@ -2504,14 +2508,15 @@ void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream
 bool bwd_chunk_q_supported(int K, int d_v, bool f32) { return !f32 && K == 128 && d_v == 128; }
 
 bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const void* dout, const float* stt, float* rs,
-                        float* rt, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st, int K,
-                        int d_v, int dva, float eps, bool emit_dl, hipStream_t s) {
-    if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4) return false;
+                        float* rt, int seg_per, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st,
+                        int K, int d_v, int dva, float eps, bool emit_dl, hipStream_t s) {
+    if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4 || (rt && seg_per < 1)) return false;
     // chunks per workgroup: enough workgroups for every compute unit several times over.  Longer walks
     // amortise the first chunk's unhidden loads: 16 chunks measured 1306 -> 1290 us per launch against 4
     // at B1 H16 N65536 (the key side 1078 -> 1057 us)
     int per = 16;
     while (per > 1 && BH * ((n_st + per - 1) / per) < 1024) per /= 2;
+    if (rt) per = seg_per;   // each walk is one state segment, whose total it forms
     const int64_t groups = (n_st + per - 1) / per;
     const dim3 grid((unsigned)(BH * groups));
     // four wavefronts: eight (two per SIMD, half the tiles each) measured no faster (936 vs 944 us per

@@ -89,14 +89,16 @@ void launch_bwd_dl(const float* gamma, float* dg, int64_t rows, int K, hipStream
 // The query-side chunk work of the causal backward in one kernel (bf16 storage, K = d_v = 128;
 // bwd_chunk_q_supported), one workgroup per (batch, head, chunk of 64 tokens): from gq, gk [BH, N, K],
 // v, dout [BH, N, d_v] bf16 and the exclusive prefix states stt [BH, n_st, K, dva] it writes rs
-// [BH N, 2] = (1 / den, h), rt (if not null) [BH, n_st, K, dva] = Gamma_Q^T [g | h] per chunk (zero padded), dgq =
-// [g | h] S^T + mt Gamma_K [BH, N, K] and, where ac and mt are not null, ac = tril(Gamma_Q Gamma_K^T)
-// and mt = tril([g | h] [V | 1]^T) [BH, n_st, 64, 64].  dva = d_v + 4; rows of v and dout 16-byte
-// aligned.  false: no kernel for this shape.
+// [BH N, 2] = (1 / den, h), rt (if not null) the segment totals of Gamma_Q^T [g | h] over segments of
+// seg_per chunks [BH, ceil(n_st / seg_per), K, dva] (zero padded; the layout launch_bwd_suffix_state's
+// first pass writes, so that pass can be left out), dgq = [g | h] S^T + mt Gamma_K [BH, N, K] and,
+// where ac and mt are not null, ac = tril(Gamma_Q Gamma_K^T) and mt = tril([g | h] [V | 1]^T)
+// [BH, n_st, 64, 64].  dva = d_v + 4; rows of v and dout 16-byte aligned.  false: no kernel for this
+// shape.
 bool bwd_chunk_q_supported(int K, int d_v, bool f32);
 bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const void* dout, const float* stt, float* rs,
-                        float* rt, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st, int K,
-                        int d_v, int dva, float eps, bool emit_dl, hipStream_t s);
+                        float* rt, int seg_per, float* ac, float* mt, float* dgq, int64_t BH, int64_t N, int64_t n_st,
+                        int K, int d_v, int dva, float eps, bool emit_dl, hipStream_t s);
 // The prefix states of the chunk terms Gamma_K^T [V | 1] (the same shapes), in segments of `per` chunks
 // (bwd_state_segment), two passes: totals = true writes each segment's total into seg [BH, ceil(n_st /
 // per), K, dva]; after an exclusive scan of seg, totals = false writes each chunk's exclusive prefix

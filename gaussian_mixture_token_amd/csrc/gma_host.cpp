@@ -1322,15 +1322,12 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     if (qfused) {
         bool ok = true;
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            ok = launch_bwd_chunk_q(gq, gk, vq, dq, stt, rs, nullptr, nullptr, nullptr, dgq, BH, N, b.n_st, K, d_v,
-                                    dva, b.eps, emit_dl, s);
+            ok = launch_bwd_chunk_q(gq, gk, vq, dq, stt, rs, sgs, b.sper, nullptr, nullptr, dgq, BH, N, b.n_st, K,
+                                    d_v, dva, b.eps, emit_dl, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused query-side chunk kernel for this shape");
-        // the suffix states: segment totals of Gamma_Q^T [g | h], their exclusive suffix scan, then every
-        // chunk's suffix from its segment's on (the segment array is free again)
-        GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            launch_bwd_suffix_state(gq, dq, rs, rt, sgs, b.sper, true, BH, N, b.n_st, K, d_v, dva, s);
-        }));
+        // the suffix states: the query side has left the segment totals of Gamma_Q^T [g | h] in the segment
+        // array (free again); their exclusive suffix scan, then every chunk's suffix from its segment's on
         GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(sgs, BH, n_sgs, rec, 1, s); }));
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
             launch_bwd_suffix_state(gq, dq, rs, rt, sgs, b.sper, false, BH, N, b.n_st, K, d_v, dva, s);
