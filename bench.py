@@ -10,7 +10,8 @@ gradient, from a seeded dL/dO); its line carries the whole step against the peak
 cores its products run on (bf16 with split operands for bf16 storage, fp32 for fp32 storage).
 
 The forward line also carries `copy_reference`: the rate a plain 1 GiB device copy sustains on the
-same GPU, beside the rate at which the step moves its measured HBM traffic; and `exp2_reference`: the
+same GPU (and, under `read_only`, the rate of a plain 1 GiB reduction, which only reads), beside the
+rate at which the step moves its measured HBM traffic; and `exp2_reference`: the
 measured rate of the hardware exponential and the time the step's 2 K exponentials per token-head
 take at it.
 
@@ -351,8 +352,11 @@ def main():
 
     exp_ref = exp2_reference(lib, w, T, step_s)
     copy_gbs = copy_reference(dev)
+    read_gbs = read_reference(dev)
     copy_ref = {"kernel": "torch copy_ of 1 GiB fp32 into 1 GiB, 20 back to back", "gbs": copy_gbs,
                 "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
+                "read_only": {"kernel": "torch amax over 1 GiB fp32, 20 back to back", "gbs": read_gbs,
+                              "frac_of_peak": read_gbs / HBM_PEAK_GBS},
                 "step_traffic_gbs": None if traffic is None else traffic / step_s / 1e9,
                 "step_traffic_over_copy": None if traffic is None else traffic / step_s / 1e9 / copy_gbs}
 
@@ -409,6 +413,25 @@ def copy_reference(dev, steps: int = 20) -> float:
     torch.cuda.synchronize()
     gbs = steps * 2 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del x, y
+    return gbs
+
+
+def read_reference(dev, steps: int = 20) -> float:
+    """GB/s of a plain device reduction over 1 GiB (torch's amax: reads only, writes one value), back to
+    back after three untimed runs: the rate a kernel that only reads sustains on this GPU, as context for
+    passes that read far more than they write."""
+    import torch
+    x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        x.amax()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        x.amax()
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = steps * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x
     return gbs
 
 
