@@ -51,7 +51,7 @@ def _check_resources(src: str, remarks: str) -> None:
         if m:
             cur = m.group(1)
             continue
-        m = re.search(r"remark: (VGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
+        m = re.search(r"remark:\s+(VGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
         if m and cur and int(m.group(2)) != 0:
             bad.append("%s: %s = %s" % (cur, m.group(1), m.group(2)))
     if bad:
