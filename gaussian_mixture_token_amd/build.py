@@ -40,10 +40,21 @@ def sources():
 RESOURCE_REMARK = "-Rpass-analysis=kernel-resource-usage"
 
 
+# Kernels known to spill vector registers to scratch memory, each with its reason.  Both are register-
+# staged output passes (plain loads, waits placed by the compiler, so scratch accesses are counted
+# correctly) of shapes outside the token-split classes: fp32 K = d_r = d_v = 128, and bf16 K = 256 with
+# d_r, d_v up to 128.  Their spills cost time, not correctness.
+SCRATCH_ALLOWED = {
+    "_ZN3gma11main_kernelILb1ELi128ELi128ELi128ELi4ELi32ELi3ELb0ELi1EEEvNS_8MainArgsE",
+    "_ZN3gma11main_kernelILb0ELi256ELi128ELi128ELi4ELi32ELi3ELb0ELi1EEEvNS_8MainArgsE",
+}
+
+
 def _check_resources(src: str, remarks: str) -> None:
-    """Every kernel must run without scratch memory: the DMA-staged kernels count their outstanding
-    vector-memory operations exactly (s_waitcnt vmcnt(N)), and scratch loads and stores would add
-    to that count.  (Scalar registers spilled into vector-register lanes use no memory.)"""
+    """Every kernel must run without scratch memory (SCRATCH_ALLOWED aside): the DMA-staged kernels
+    count their outstanding vector-memory operations exactly (s_waitcnt vmcnt(N)), and scratch loads
+    and stores would add to that count; elsewhere a spill is a slowdown that should not go unnoticed.
+    (Scalar registers spilled into vector-register lanes use no memory.)"""
     cur = None
     bad = []
     for line in remarks.splitlines():
@@ -51,8 +62,10 @@ def _check_resources(src: str, remarks: str) -> None:
         if m:
             cur = m.group(1)
             continue
-        m = re.search(r"remark:\s+(VGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
-        if m and cur and int(m.group(2)) != 0:
+        # "remark: <file>:<line>:<col>:     ScratchSize [bytes/lane]: N" (the location may also come
+        # before "remark:")
+        m = re.search(r"\s(VGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
+        if m and cur and int(m.group(2)) != 0 and cur not in SCRATCH_ALLOWED:
             bad.append("%s: %s = %s" % (cur, m.group(1), m.group(2)))
     if bad:
         raise RuntimeError("kernels in %s use scratch memory:\n  %s" % (src, "\n  ".join(bad)))

@@ -1269,17 +1269,17 @@ bwd_chunk_state_kernel(const float* gk, const void* v, float* stt, float* seg, i
 // ---------------------------------------------------------------------------------- suffix states
 // The causal suffix states R_c = sum over the chunks after c of Gamma_Q^T [g | h] (64 tokens per chunk,
 // bf16 storage, K = d_v = 128), as [K][dva] records (columns d_v .. dva - 1: the h sums r, then zeros),
-// from the recomputed Gamma_Q, dO and the per-row pairs rs = (1 / den, h): g = dO / den.  Two passes
-// over segments of `per` consecutive chunks of one (batch, head), as for the prefix states: the first
-// (totals) writes each segment's total into seg; after an exclusive suffix scan of seg the second walks
-// its segment backwards from the segment's suffix and writes each chunk's R.  Gamma_Q and g go to LDS as
+// from the recomputed Gamma_Q, dO and the per-row pairs rs = (1 / den, h): g = dO / den.  One pass over
+// segments of `per` consecutive chunks of one (batch, head): seg holds each segment's suffix (the query-side
+// chunk kernel writes the segment totals, an exclusive suffix scan turns them into suffixes), and each
+// workgroup walks its segment backwards from there and writes each chunk's R.  Gamma_Q and g go to LDS as
 // bf16 hi + lo images; the product is formed transposed, g^T Gamma_Q, so each lane stores four
 // consecutive d_v columns of one component; the r row comes from an h fragment (row 0 = h).  Wave w takes
 // d_v tiles 2 w, 2 w + 1 for all components and the r row of component tiles 2 w, 2 w + 1.
 template <int KC, int VC>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-bwd_suffix_state_kernel(const float* gq, const void* dout, const float* rs, float* rt, float* seg, int64_t N,
-                        int64_t n_st, int per, int dva, int totals) {
+bwd_suffix_state_kernel(const float* gq, const void* dout, const float* rs, float* rt, const float* seg,
+                        int64_t N, int64_t n_st, int per, int dva) {
     static_assert(KC == 128 && VC == 128, "one 256-byte image row per token");
     constexpr int C = 64;
     constexpr int IMG = C * 256;
@@ -1324,23 +1324,19 @@ bwd_suffix_state_kernel(const float* gq, const void* dout, const float* rs, floa
     };
 
     // running sums: run[t][ct] rows = d_v 32 w + 16 t + 4 g + i, column = component 16 ct + r; hrun[hh] row 0
-    // = the r sums of component tile 2 w + hh.  The second pass starts at the segment's suffix.
-    float* seg_rec = seg + (bh * groups + c0 / per) * rec;
+    // = the r sums of component tile 2 w + hh.  They start at the segment's suffix.
+    const float* seg_rec = seg + (bh * groups + c0 / per) * rec;
     f32x4 run[2][8], hrun[2];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) run[0][ct] = run[1][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    hrun[0] = hrun[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!totals) {
+    for (int ct = 0; ct < 8; ++ct) {
+        const float* row = seg_rec + (int64_t)(16 * ct + r) * dva;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const float* row = seg_rec + (int64_t)(16 * ct + r) * dva;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) run[t][ct] = *reinterpret_cast<const f32x4*>(row + 32 * w + 16 * t + 4 * g);
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            if (g == 0) hrun[hh] = *reinterpret_cast<const f32x4*>(seg_rec + (int64_t)(16 * (2 * w + hh) + r) * dva + VC);
+        for (int t = 0; t < 2; ++t) run[t][ct] = *reinterpret_cast<const f32x4*>(row + 32 * w + 16 * t + 4 * g);
     }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+        hrun[hh] = (g == 0) ? *reinterpret_cast<const f32x4*>(seg_rec + (int64_t)(16 * (2 * w + hh) + r) * dva + VC)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
     auto store_rec = [&](float* rec_c) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
@@ -1353,11 +1349,11 @@ bwd_suffix_state_kernel(const float* gq, const void* dout, const float* rs, floa
             if (g == 0) *reinterpret_cast<f32x4*>(rec_c + (int64_t)(16 * (2 * w + hh) + r) * dva + VC) = hrun[hh];
     };
 
-    // the second pass walks its segment backwards (a suffix), the first in any order
+    // the segment backwards (a suffix)
     fetch(c1 - 1);
     for (int64_t c = c1 - 1; c >= c0; --c) {
         if (c < c1 - 1) lds_barrier();
-        if (!totals) store_rec(rt + (bh * n_st + c) * rec);   // the terms of all later chunks
+        store_rec(rt + (bh * n_st + c) * rec);   // the terms of all later chunks
         {
             const int rl = lane >> 5, cl = lane & 31;
 #pragma unroll
@@ -1421,7 +1417,6 @@ bwd_suffix_state_kernel(const float* gq, const void* dout, const float* rs, floa
             }
         }
     }
-    if (totals) store_rec(seg_rec);   // the segment's total (first pass)
 }
 
 // ---------------------------------------------------------------------------------- fused chunk, query side
@@ -1777,8 +1772,8 @@ __global__ void __launch_bounds__(W * 64) bwd_chunk_q_kernel(const float* gq, co
         }
         lds_barrier();   // g, h visible; dO no longer read
 
-        // ---- the chunk's term [g | h]^T Gamma_Q of the suffix states, added to the walk's total (not where rt
-        // is null: the suffix-state kernel then forms the segment totals itself)
+        // ---- the chunk's term [g | h]^T Gamma_Q of the suffix states, added to the walk's total (where rt is
+        // given: the segment totals that the suffix-state kernel starts from)
         if (rt) {
 #pragma unroll
             for (int tk = 0; tk < 2; ++tk) {
@@ -2476,7 +2471,8 @@ void launch_bwd_gamma_split(const void* x, const float* bf, const double* cq, fl
         case 2: bwd_gamma_split_kernel<2, 8, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
         case 4: bwd_gamma_split_kernel<4, 8, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
         case 8: bwd_gamma_split_kernel<8, 4, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
-        default: bwd_gamma_split_kernel<16, 2, 2><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
+        // K = 256: one row group per wave (two leave too few registers for the 16 accumulator tiles each)
+        default: bwd_gamma_split_kernel<16, 2, 1><<<grid, block, 0, s>>>(xp, fr, cq, gamma, N, H, K, d_r, rows); break;
     }
 }
 
@@ -2549,12 +2545,12 @@ bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, float* s
     return true;
 }
 
-bool launch_bwd_suffix_state(const float* gq, const void* dout, const float* rs, float* rt, float* seg, int per,
-                             bool totals, int64_t BH, int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s) {
+bool launch_bwd_suffix_state(const float* gq, const void* dout, const float* rs, float* rt, const float* seg, int per,
+                             int64_t BH, int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s) {
     if (!bwd_chunk_q_supported(K, d_v, false) || dva != d_v + 4 || per < 1) return false;
     const int64_t groups = (n_st + per - 1) / per;
     bwd_suffix_state_kernel<128, 128><<<dim3((unsigned)(BH * groups)), dim3(256), 0, s>>>(gq, dout, rs, rt, seg, N, n_st,
-                                                                                         per, dva, totals ? 1 : 0);
+                                                                                         per, dva);
     return true;
 }
 

@@ -108,11 +108,11 @@ int bwd_state_segment(int64_t BH, int64_t n_st);
 bool launch_bwd_chunk_state(const float* gk, const void* v, float* stt, float* seg, int per, bool totals, int64_t BH,
                             int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s);
 // The suffix states R_c = sum over the later chunks of Gamma_Q^T [g | h] (the same shapes), from gq, dout and
-// rs, in two passes like launch_bwd_chunk_state: totals = true writes segment totals into seg; after an
-// exclusive suffix scan of seg, totals = false writes every chunk's R into rt [BH, n_st, K, dva] (columns
-// d_v .. dva - 1 = the h sums, 0, 0, 0).
-bool launch_bwd_suffix_state(const float* gq, const void* dout, const float* rs, float* rt, float* seg, int per,
-                             bool totals, int64_t BH, int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s);
+// rs: seg [BH, ceil(n_st / per), K, dva] holds each segment's exclusive suffix (the segment totals of
+// launch_bwd_chunk_q after an exclusive suffix scan); every chunk's R goes into rt [BH, n_st, K, dva]
+// (columns d_v .. dva - 1 = the h sums, 0, 0, 0).
+bool launch_bwd_suffix_state(const float* gq, const void* dout, const float* rs, float* rt, const float* seg, int per,
+                             int64_t BH, int64_t N, int64_t n_st, int K, int d_v, int dva, hipStream_t s);
 // Its key-side counterpart (the same shapes): from gq, gk, v, dout, rs and the exclusive suffix states
 // rt [BH, n_st, K, dva] it writes dgk = [V | 1] R^T + mt^T Gamma_Q [BH, N, K] and dv = Gamma_K Rv +
 // ac^T g [BH, N, d_v] bf16, recomputing ac and mt.

@@ -1330,7 +1330,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         // array (free again); their exclusive suffix scan, then every chunk's suffix from its segment's on
         GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(sgs, BH, n_sgs, rec, 1, s); }));
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            launch_bwd_suffix_state(gq, dq, rs, rt, sgs, b.sper, false, BH, N, b.n_st, K, d_v, dva, s);
+            launch_bwd_suffix_state(gq, dq, rs, rt, sgs, b.sper, BH, N, b.n_st, K, d_v, dva, s);
         }));
     }
     if (!qfused) {
