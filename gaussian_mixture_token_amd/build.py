@@ -71,14 +71,24 @@ def _check_resources(src: str, remarks: str) -> None:
         raise RuntimeError("kernels in %s use scratch memory:\n  %s" % (src, "\n  ".join(bad)))
 
 
+# Kernels that wait for their LDS-DMA prefetch with exact vmcnt counts: the token-split kernels, the
+# LDS-DMA staged main_kernel instantiations (template argument DMA = true, the eighth) and the fused
+# backward row kernel.
+EXACT_VMCNT_KERNELS = re.compile(
+    r"^(_ZN3gma10tok_kernel\S*|_ZN3gma11main_kernelILb[01](?:ELi-?\d+){6}ELb1\S*|"
+    r"_ZN3gma12_GLOBAL__N_121bwd_fused_rows_kernel\S*):", re.M)
+# sources whose assembly must hold such kernels (a check that finds none has a stale pattern)
+EXACT_VMCNT_SOURCES = ("gma_classes_bf16", "gma_backward")
+
+
 def _check_vmem_in_loops(asm_path: str) -> int:
-    """The token-split kernels wait for their LDS-DMA prefetch with exact vmcnt counts, which hold
-    only if the chunk loop issues no vector-memory operation other than the DMA loads (buffer_load
-    ... lds) and the output stores (buffer_store).  Checked on the assembly after the first barrier
-    (everything before it is the prologue): no scratch access, no other loads."""
+    """The exact vmcnt counts hold only if the chunk loop issues no vector-memory operation other
+    than the DMA loads (buffer_load ... lds) and the output stores.  Checked on the assembly after
+    the first barrier (everything before it is the prologue): no scratch access, no other loads.
+    Returns the number of kernels checked."""
     text = open(asm_path).read()
     n_checked = 0
-    for m in re.finditer(r"^(_ZN3gma10tok_kernel\S*):", text, re.M):
+    for m in EXACT_VMCNT_KERNELS.finditer(text):
         name = m.group(1)
         body = text[m.end(): text.index("s_endpgm", m.end())]
         loop = body[body.index("s_barrier"):] if "s_barrier" in body else ""
@@ -120,7 +130,9 @@ def _compile(src: str) -> str:
         base = os.path.splitext(os.path.basename(obj))[0]
         for name in os.listdir(BUILD_DIR):
             if name.startswith(base.replace(".hip", "")) and name.endswith("gfx950.s"):
-                _check_vmem_in_loops(os.path.join(BUILD_DIR, name))
+                n = _check_vmem_in_loops(os.path.join(BUILD_DIR, name))
+                if n == 0 and name.startswith(EXACT_VMCNT_SOURCES):
+                    raise RuntimeError("%s: no exact-vmcnt kernel found to check (stale pattern?)" % name)
     return obj
 
 

@@ -35,3 +35,40 @@ def test_scratch_or_spill_is_rejected(form, scratch, spill):
 def test_listed_kernel_is_allowed():
     name = sorted(build.SCRATCH_ALLOWED)[0]
     build._check_resources("k.hip", SAVE_TEMPS.replace("_Z3fooPf", name).format(scratch=28, spill=6))
+
+
+ASM = """\
+{name}:
+\tbuffer_load_dwordx4 v0, s[0:3], 0 offen lds
+\ts_barrier
+\tbuffer_load_dwordx4 v0, s[0:3], 0 offen lds
+\t{op}
+\tbuffer_store_dwordx4 v[0:3], v4, s[0:3], 0 offen
+\ts_endpgm
+"""
+TOK = "_ZN3gma10tok_kernelILi128ELi128ELi128ELi5ELi1EEEvNS_8MainArgsE"
+DMA_MAIN = "_ZN3gma11main_kernelILb0ELi128ELi64ELi128ELi4ELi32ELi0ELb1ELi2EEEvNS_8MainArgsE"
+PLAIN_MAIN = "_ZN3gma11main_kernelILb0ELi128ELi64ELi128ELi4ELi32ELi0ELb0ELi2EEEvNS_8MainArgsE"
+
+
+@pytest.mark.parametrize("name", [TOK, DMA_MAIN])
+def test_dma_loop_with_only_dma_loads_and_stores_passes(tmp_path, name):
+    f = tmp_path / "k.s"
+    f.write_text(ASM.format(name=name, op="s_nop 0"))
+    assert build._check_vmem_in_loops(str(f)) == 1
+
+
+@pytest.mark.parametrize("op", ["global_load_dword v1, v[2:3], off", "scratch_store_dword off, v1, s0",
+                                "buffer_load_dword v1, v2, s[0:3], 0 offen"])
+@pytest.mark.parametrize("name", [TOK, DMA_MAIN])
+def test_dma_loop_with_another_load_is_rejected(tmp_path, name, op):
+    f = tmp_path / "k.s"
+    f.write_text(ASM.format(name=name, op=op))
+    with pytest.raises(RuntimeError, match="unexpected vector-memory"):
+        build._check_vmem_in_loops(str(f))
+
+
+def test_register_staged_kernel_is_not_an_exact_count_kernel(tmp_path):
+    f = tmp_path / "k.s"
+    f.write_text(ASM.format(name=PLAIN_MAIN, op="global_load_dword v1, v[2:3], off"))
+    assert build._check_vmem_in_loops(str(f)) == 0
