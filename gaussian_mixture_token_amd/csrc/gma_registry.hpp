@@ -54,9 +54,10 @@ void launch_tok(const MainArgs& a, int grid, hipStream_t s) {
         &launch_main<F32, KC, VC, DRC, W, C, MODE_OUT_BIDIR, DMA, WPE>,                       \
         &launch_main<F32, KC, VC, DRC, W, C, MODE_OUT_CAUSAL, DMA, WPE>
 
-#define GMA_SHAPE_CLASS_F32(KC, VC, DRC, W, C)                                                \
+// WPC: workgroups per compute unit the segment split aims at (the aggregate pass's occupancy)
+#define GMA_SHAPE_CLASS_F32(KC, VC, DRC, W, C, WPC)                                           \
     ShapeClass {                                                                              \
-        1, KC, VC, DRC, W, C, 1, &launch_prep<true, KC, DRC>, GMA_MAIN_SET(true, KC, VC, DRC, W, C, false, 1), \
+        1, KC, VC, DRC, W, C, WPC, &launch_prep<true, KC, DRC>, GMA_MAIN_SET(true, KC, VC, DRC, W, C, false, 1), \
             nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr                           \
     }
 
