@@ -566,7 +566,11 @@ def test_causal_state_without_state_equals_plain_causal(gma):
 
 
 @pytest.mark.parametrize("prepared", [False, True])
-@pytest.mark.parametrize("cfg,shape", [(3, None), (1, None), (4, None), (2, (37, 29, 45)), (0, (5, 3, 7))])
+# the last three take the step kernel's further rounds of loads: more than one group of mixture parameters
+# per wave (K above 16 G components) and more than one batch of state elements per thread (d_v > 64 with
+# K > 128, d_v > 128 with K > 64), up to the largest shape
+@pytest.mark.parametrize("cfg,shape", [(3, None), (1, None), (4, None), (2, (37, 29, 45)), (0, (5, 3, 7)),
+                                       (2, (100, 150, 100)), (0, (200, 200, 200)), (3, (256, 256, 256))])
 def test_decode_steps_match_the_oracle(gma, cfg, shape, prepared):
     # one-token steps from a zero state, updated in place, against the oracle's one pass over the
     # same tokens (outputs and final state); any d_r, K, d_v <= 256.  prepared: the mixture is
@@ -592,10 +596,14 @@ def test_decode_steps_match_the_oracle(gma, cfg, shape, prepared):
     assert err_s <= TOL[w.dtype], err_s
 
 
-def test_decode_prepared_equals_raw_step_to_rounding(gma):
+@pytest.mark.parametrize("shape", [None, (200, 200, 200)])
+def test_decode_prepared_equals_raw_step_to_rounding(gma, shape):
     # the same 20 steps with the raw and with the prepared mixture: the log-densities differ only in
-    # summation order, so outputs and states agree far inside the tolerance
-    w = gma.workload(1, batch=2, heads=3, seq_len=20)
+    # summation order, so outputs and states agree far inside the tolerance (fp32 storage)
+    kw = dict(batch=2, heads=3, seq_len=20)
+    if shape:
+        kw.update(d_route=shape[0], n_comp=shape[1], d_value=shape[2])
+    w = gma.workload(1, **kw)
     inp = gma.make_inputs(w)
     t = {k: v.to(DEV) for k, v in inp.items()}
     prep = gma.decode_prepare(t["raw_var"], t["prior_logits"])
