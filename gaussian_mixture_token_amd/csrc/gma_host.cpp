@@ -16,6 +16,7 @@
 #include "gma_backward.hpp"
 #include "gma_decode.hpp"
 #include "gma_fixup.hpp"
+#include "gma_resp.hpp"
 #include "gma_registry.hpp"
 
 namespace gma {
@@ -81,6 +82,10 @@ struct Plan {
     size_t off_flags = 0, off_fix = 0;
     bool flags = false;
     int stat_segs = 0;                     // responsibility diagnostics: row segments per (batch, head)
+    // responsibilities through the token-split kernel (bf16 classes with token-split passes, d_r % 8 == 0):
+    // segments of resp_rows rows (whole 64-row blocks; seg_chunks chunks of the class for main_kernel)
+    bool resp_tok = false;
+    int64_t resp_rows = 0;
     size_t off_gamma = 0, off_part = 0;
     // Generic path (no compiled class covers the shape): fp32 responsibilities and products over
     // materialised Gamma_Q, Gamma_K.  Rows of tokens in entries of gen_step (a causal chunk or a
@@ -228,7 +233,27 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     const int wg_per_cu = tok ? plan->cls->tok_wg_per_cu : plan->cls->wg_per_cu;
     const int64_t BH = plan->B * plan->H;
     plan->n_chunks = (plan->N + C - 1) / C;
-    if (op == GMA_OP_RESPONSIBILITIES) {
+    // Token-split responsibilities (each wave alone on 16-row groups, every component's [a | b] in AGPRs,
+    // no LDS staging or barriers) against the main_kernel walk below, measured on MI355X: diagnostics
+    // 230 -> 152 us at B1 H16 N65536 d_r 128 K 128, 2.91 -> 1.87 ms at B1 H8 N1M d_r 64 K 256, 153 -> 46 us
+    // at B32 H8 N4096 d_r 64 K 32; Gamma written out 0.22 -> 0.19 ms and 0.073 -> 0.062 ms at the first and
+    // last shapes, but 2.23 -> 2.53 ms at K = 256 (8.6 GB of Gamma), which keeps the walk.
+    plan->resp_tok = resp && !tok && !plan->f32 && plan->d_r % 8 == 0 && 64 % C == 0 &&
+                     resp_tok_supported(plan->cls->kc, plan->cls->drc) &&
+                     (op == GMA_OP_RESPONSIBILITY_STATS || plan->cls->kc <= 128);
+    if (plan->resp_tok) {
+        // one round of workgroups, one per compute unit (four at K = 32, whose fragments leave room), each
+        // walking a segment of whole 64-row blocks
+        const int64_t wpc = plan->cls->kc <= 32 ? 4 : 1;
+        const int64_t blocks = (plan->N + 63) / 64;
+        int64_t P = (kComputeUnits * wpc + BH - 1) / BH;
+        if (P > blocks) P = blocks;
+        if (P < 1) P = 1;
+        const int64_t sb = (blocks + P - 1) / P;
+        plan->resp_rows = sb * 64;
+        plan->seg_chunks = (int)(sb * (64 / C));
+        plan->P = (int)((blocks + sb - 1) / sb);
+    } else if (op == GMA_OP_RESPONSIBILITIES) {
         // two workgroups' worth per compute unit slot, each walking consecutive chunks: a workgroup loads
         // the [a | b] fragments of its components once (32 KB per wave at K = d_r = 128) for all of its
         // chunks.  One chunk per workgroup measured 0.31 against 0.21 ms at B1 H16 N65536 K128 and 2.99
@@ -1598,7 +1623,14 @@ gma_status_t gma_responsibilities(const gma_problem_t* p, const void* x, const f
                      (pl.N + pl.cls->c) * pl.d_r * 2 < (int64_t(1) << 31);
     const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
     const int grid = (int)(pl.B * pl.H * pl.P);
-    st = timed_launch(K_RESP, s, [&] { f_resp(a, grid, s); });
+    if (pl.resp_tok && !misaligned(x, 16)) {
+        const bool vecg = pl.K % 4 == 0 && !misaligned(gamma, 16);
+        bool ok = false;
+        st = timed_launch(K_RESP, s, [&] { ok = launch_resp_tok(a, pl.cls->kc, pl.cls->drc, pl.resp_rows, vecg, grid, s); });
+        if (st == GMA_SUCCESS && !ok) return fail(GMA_ERROR_NOT_SUPPORTED, "no token-split responsibilities kernel");
+    } else {
+        st = timed_launch(K_RESP, s, [&] { f_resp(a, grid, s); });
+    }
     if (st != GMA_SUCCESS || !pl.flags) return st;
     FixArgs f = fix_args(pl, w);
     f.qx = x;
@@ -1662,7 +1694,15 @@ gma_status_t gma_responsibility_stats(const gma_problem_t* p, const void* x, con
         const bool dma = !pl.f32 && pl.cls->dma_resp && pl.d_r % 8 == 0 && !misaligned(x, 16) &&
                          (pl.N + pl.cls->c) * pl.d_r * 2 < (int64_t(1) << 31);
         const main_launch_t f_resp = dma ? pl.cls->dma_resp : pl.cls->resp;
-        st = timed_launch(K_STATS, s, [&] { f_resp(a, (int)(BH * pl.P), s); });
+        if (pl.resp_tok && !misaligned(x, 16)) {
+            bool ok = false;
+            st = timed_launch(K_STATS, s, [&] {
+                ok = launch_resp_tok(a, pl.cls->kc, pl.cls->drc, pl.resp_rows, false, (int)(BH * pl.P), s);
+            });
+            if (st == GMA_SUCCESS && !ok) return fail(GMA_ERROR_NOT_SUPPORTED, "no token-split responsibilities kernel");
+        } else {
+            st = timed_launch(K_STATS, s, [&] { f_resp(a, (int)(BH * pl.P), s); });
+        }
         if (st != GMA_SUCCESS) return st;
         if (pl.flags) {
             FixArgs f = fix_args(pl, w);
