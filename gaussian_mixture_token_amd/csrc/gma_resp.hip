@@ -28,6 +28,7 @@ resp_tok_kernel(const MainArgs a, int64_t rows_per_seg, int vec_gamma) {
     constexpr int W = kRespWaves;
     constexpr int NCT = KC / 16;    // component tiles
     constexpr int NKS2 = DRC / 32;  // fragment steps over d_r (x^2 part; the x part follows)
+    static_assert(KC <= 256, "component index in the low 8 bits of the argmax key");
     __shared__ __attribute__((aligned(16))) float s_c[KC];
     __shared__ float s_use[STATS ? W : 1][STATS ? KC : 1];
     __shared__ uint32_t s_cnt[STATS ? KC : 1];
@@ -130,40 +131,38 @@ resp_tok_kernel(const MainArgs a, int64_t rows_per_seg, int vec_gamma) {
         const int64_t row = g0 + lr;
         const bool valid = row < r1;
         // a row maximum of -inf or NaN (the maximum skips NaN logits), or a sum that is not finite
-        nonfin |= valid && !(m > -INFINITY && ssum < INFINITY);
+        const bool finite = m > -INFINITY && ssum < INFINITY;
+        nonfin |= valid && !finite;
         const float rs = valid ? fast_rcp(ssum) : 0.f;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[ct] *= rs;
 
         if constexpr (STATS) {
-            // usage sums of this lane's components; the row's largest gamma over its components, then over
-            // the lane groups (ties to the lowest component); a row whose gammas are not finite counts
-            // nowhere (its (batch, head) is flagged and recomputed)
-            float best = -1.f;
-            int bi = 0x7fffffff;
+            // usage sums of this lane's components (the normalisation folded into one multiply-add); the
+            // row's largest gamma: one 32-bit key per component, the top 24 bits of the non-negative
+            // 2^(l - max) (ordered as an integer, and in the same order as gamma) above 255 - k, so that an
+            // unsigned maximum over the lane's components and the four lane groups picks the largest (values
+            // equal in their top 24 bits, within about 2^-15 of each other, tie and go to the lowest
+            // component); pad components have 2^-inf = 0.
+            // A row whose gammas are not finite counts nowhere (its (batch, head) is flagged and recomputed).
+            uint32_t key = 0u;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                use[ct] += acc[ct];
+                use[ct] += acc[ct] * rs;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int c = 16 * ct + 4 * lg + i;
-                    if (c < K && acc[ct][i] > best) {
-                        best = acc[ct][i];
-                        bi = c;
-                    }
+                    const uint32_t kk = (__float_as_uint(acc[ct][i]) & 0xffffff00u) | (uint32_t)(255 - (16 * ct + 4 * lg + i));
+                    key = key > kk ? key : kk;
                 }
             }
 #pragma unroll
             for (int o = 16; o < 64; o <<= 1) {
-                const float ob = __shfl_xor(best, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (ob > best || (ob == best && oi < bi)) {
-                    best = ob;
-                    bi = oi;
-                }
+                const uint32_t ok = (uint32_t)__shfl_xor((int)key, o, 64);
+                key = key > ok ? key : ok;
             }
-            if (lg == 0 && valid && bi < K) atomicAdd(&s_cnt[bi], 1u);
+            const int bi = 255 - (int)(key & 0xffu);
+            if (lg == 0 && valid && finite && bi < K) atomicAdd(&s_cnt[bi], 1u);
         } else if (valid) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) acc[ct] *= rs;
             float* grow = a.gamma + (bh * N + row) * K;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {

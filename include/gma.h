@@ -114,8 +114,9 @@ gma_status_t gma_responsibilities(const gma_problem_t* problem, const void* x, c
  * row of x [B, H, N, d_r] under head h's mixture,
  *   usage [B, H, K] fp32         sum over the rows of gamma_k (each row of Gamma sums to 1);
  *   hard_counts [B, H, K] uint32 number of rows whose largest gamma is at component k (ties go to the
- *                                lowest k; decided on the library's fp32 Gamma, so rows whose two
- *                                largest responsibilities are within its rounding may go either way);
+ *                                lowest k; decided on the library's fp32 Gamma, where values within
+ *                                about 2^-15 of each other count as equal, so rows whose two largest
+ *                                responsibilities are that close may go either way);
  *   usage_entropy [B, H] fp32    -sum_k p_k ln p_k / ln K with p = usage / N (0 ln 0 = 0; 0 when
  *                                K = 1): the usage entropy as a fraction of its largest value, the
  *                                normalisation under which the page's interpretability figures (usage
