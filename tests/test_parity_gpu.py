@@ -85,6 +85,41 @@ def test_responsibilities_match_oracle(gma, cfg, shape):
     assert err <= TOL_GAMMA[w.dtype]
 
 
+@pytest.mark.parametrize("what", ["rows", "gamma"])
+def test_responsibilities_with_misaligned_buffers(gma, what):
+    # rows that are not 16-byte aligned take the register-staged kernel (against the oracle; the diagnostics
+    # against the aligned call); a Gamma buffer that is not 16-byte aligned takes element stores (bitwise the
+    # aligned call's Gamma)
+    w = gma.workload(3, batch=1, heads=2, seq_len=3000 + 7)
+    say("responsibilities, misaligned %s" % what)
+    inp = gma.make_inputs(w)
+    t = {k: v.to(DEV) for k, v in inp.items()}
+    args = (t["mu"], t["raw_var"], t["prior_logits"])
+    x = t["qx"]
+    ref = gma.responsibilities(x, *args)
+    if what == "rows":
+        buf = torch.empty(x.numel() + 8, dtype=x.dtype, device=DEV)
+        xs = buf[1:1 + x.numel()].view_as(x)
+        xs.copy_(x)
+        got = gma.responsibilities(xs, *args)
+        u0, c0, e0 = gma.responsibility_stats(x, *args)
+        u1, c1, e1 = gma.responsibility_stats(xs, *args)
+        torch.cuda.synchronize()
+        err = np.abs(got.cpu().numpy().astype(np.float64) -
+                     oracle.responsibilities(inp["qx"], inp["mu"], inp["raw_var"], inp["prior_logits"])).max()
+        say("  max |dGamma| = %.3e" % err)
+        assert err <= TOL_GAMMA[w.dtype]
+        assert torch.allclose(u1, u0, rtol=1e-3, atol=1e-2)
+        assert (c1.sum(-1) == w.seq_len).all() and (c1.long() - c0.long()).abs().sum() <= 0.01 * c0.numel() * w.seq_len / w.n_comp
+        assert torch.allclose(e1, e0, atol=1e-4)
+    else:
+        gb = torch.empty(ref.numel() + 4, dtype=torch.float32, device=DEV)
+        out = gb[1:1 + ref.numel()].view_as(ref)
+        got = gma.responsibilities(x, *args, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref)
+
+
 @pytest.mark.parametrize("cfg,heads,N,shape", [(3, 4, 65536 + 333, None), (4, 2, 65536 + 77, None),
                                                 (3, 2, 20000 + 5, (64, 7, 16)), (3, 2, 20000 + 5, (64, 100, 16))])
 def test_responsibilities_long_walks(gma, cfg, heads, N, shape):
