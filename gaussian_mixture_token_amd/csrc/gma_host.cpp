@@ -234,13 +234,13 @@ gma_status_t make_plan(const gma_problem_t* p, int op, Plan* plan, bool tok = fa
     const int64_t BH = plan->B * plan->H;
     plan->n_chunks = (plan->N + C - 1) / C;
     // Token-split responsibilities (each wave alone on 16-row groups, every component's [a | b] in AGPRs,
-    // no LDS staging or barriers) against the main_kernel walk below, measured on MI355X: diagnostics
-    // 230 -> 152 us at B1 H16 N65536 d_r 128 K 128, 2.91 -> 1.87 ms at B1 H8 N1M d_r 64 K 256, 153 -> 46 us
-    // at B32 H8 N4096 d_r 64 K 32; Gamma written out 0.22 -> 0.19 ms and 0.073 -> 0.062 ms at the first and
-    // last shapes, but 2.23 -> 2.53 ms at K = 256 (8.6 GB of Gamma), which keeps the walk.
+    // Gamma rows stored whole from a per-wave LDS staging area, no barriers) against the main_kernel walk
+    // below, measured on MI355X: diagnostics 230 -> 152 us at B1 H16 N65536 d_r 128 K 128, 2.91 -> 1.87 ms
+    // at B1 H8 N1M d_r 64 K 256, 153 -> 46 us at B32 H8 N4096 d_r 64 K 32 (then 126 us, 1.06 ms, 42 us with
+    // the packed argmax); Gamma written out 0.22 -> 0.19 ms, 2.22 -> 2.05 ms, 0.073 -> 0.059 ms.  The walk
+    // serves rows that are not 16-byte aligned.
     plan->resp_tok = resp && !tok && !plan->f32 && plan->d_r % 8 == 0 && 64 % C == 0 &&
-                     resp_tok_supported(plan->cls->kc, plan->cls->drc) &&
-                     (op == GMA_OP_RESPONSIBILITY_STATS || plan->cls->kc <= 128);
+                     resp_tok_supported(plan->cls->kc, plan->cls->drc);
     if (plan->resp_tok) {
         // one round of workgroups, one per compute unit (four at K = 32, whose fragments leave room), each
         // walking a segment of whole 64-row blocks

@@ -29,9 +29,13 @@ resp_tok_kernel(const MainArgs a, int64_t rows_per_seg, int vec_gamma) {
     constexpr int NCT = KC / 16;    // component tiles
     constexpr int NKS2 = DRC / 32;  // fragment steps over d_r (x^2 part; the x part follows)
     static_assert(KC <= 256, "component index in the low 8 bits of the argmax key");
+    static_assert((16 * KC / 4) % 64 == 0, "whole 16-byte units per lane in the row stores");
     __shared__ __attribute__((aligned(16))) float s_c[KC];
     __shared__ float s_use[STATS ? W : 1][STATS ? KC : 1];
     __shared__ uint32_t s_cnt[STATS ? KC : 1];
+    // Gamma rows out through LDS: each wave's 16 rows (row pitch KC fp32 + 16 bytes), stored as whole rows
+    constexpr int ROWB = KC * 4 + 16;
+    __shared__ __attribute__((aligned(16))) char s_rows[STATS ? 16 : W * 16 * ROWB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -160,16 +164,34 @@ resp_tok_kernel(const MainArgs a, int64_t rows_per_seg, int vec_gamma) {
             }
             const int bi = 255 - (int)(key & 0xffu);
             if (lg == 0 && valid && finite && bi < K) atomicAdd(&s_cnt[bi], 1u);
-        } else if (valid) {
+        } else {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) acc[ct] *= rs;
-            float* grow = a.gamma + (bh * N + row) * K;
+            if (vec_gamma) {
+                // lane (r, g) puts components 16 ct + 4 g .. + 3 of row r into the wave's staging area, then
+                // lane l stores 16 bytes (unit (64 j + l) % (KC / 4)) of row (64 j + l) / (KC / 4): each store
+                // instruction writes whole rows instead of 64-byte pieces of 16 rows.  The wave's LDS
+                // operations run in order; the empty asm statements keep the compiler from moving them
+                // across each other.
+                lds_char* sw = (lds_char*)s_rows + w * 16 * ROWB;
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int c0 = 16 * ct + 4 * lg;
-                if (vec_gamma && c0 + 4 <= K) {
-                    *reinterpret_cast<f32x4*>(grow + c0) = acc[ct];
-                } else {
+                for (int ct = 0; ct < NCT; ++ct) lds_st<f32x4>(sw + lr * ROWB + (16 * ct + 4 * lg) * 4, acc[ct]);
+                asm volatile("" ::: "memory");
+                constexpr int UPR = KC / 4;            // 16-byte units per row
+                constexpr int NU = 16 * UPR / 64;      // units per lane
+#pragma unroll
+                for (int j = 0; j < NU; ++j) {
+                    const int e = 64 * j + lane, rr = e / UPR, cu = e % UPR;
+                    const f32x4 v = lds_ld<f32x4>(sw + rr * ROWB + cu * 16);
+                    if (g0 + rr < r1 && 4 * cu < K)
+                        *reinterpret_cast<f32x4*>(a.gamma + (bh * N + g0 + rr) * K + 4 * cu) = v;
+                }
+                asm volatile("" ::: "memory");
+            } else if (valid) {
+                float* grow = a.gamma + (bh * N + row) * K;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const int c0 = 16 * ct + 4 * lg;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (c0 + i < K) grow[c0 + i] = acc[ct][i];
