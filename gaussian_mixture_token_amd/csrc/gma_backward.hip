@@ -1126,6 +1126,239 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
     }
 }
 
+// ---------------------------------------------------------------------------------- fused rows, small classes
+// The same three results for bf16 storage at K <= 64 and d_r <= 128 (K and d_r multiples of 4; padded to
+// KC in {32, 64} and DRC in {64, 128}): dl, then dx = dl [mu / s] - x (dl [1 / s]) and P += dl^T [x | x^2],
+// the sums of dl over tokens (the ones column) in fp32 on the vector units.  Workgroup: four wavefronts
+// over one (batch, head) and a segment of `seg` tokens, in chunks of 64; wave w loads rows 16 w .. 16 w +
+// 15 of each chunk into registers (lane (r, g): row r, components 32 ks + 8 g .. + 7 of gamma and dgamma,
+// dims 16 j + 4 g .. + 3 of x), the next chunk's while the current one is in the products.  dl stays in
+// registers as the B fragments of dx (split bf16 hi + lo, formed transposed: lane (r, g) then holds dx of
+// row r, dims 16 j + 4 g .. + 3); for P the chunk's dl and x go to LDS component- and dim-major (rows of
+// 64 tokens padded to 144 bytes, so a fragment's 16 rows fall in disjoint banks) and each wave takes a
+// quarter of the (component tile, dim tile) pairs over all 64 tokens.  The head's mu / s and 1 / s sit in
+// LDS as split bf16 images for the whole segment.  Waits are placed by the compiler (plain loads).
+template <int KC, int DRC>
+__global__ void __launch_bounds__(256) bwd_rows_small_kernel(const float* gamma, const float* dgamma, const void* x,
+                                                             const float* mw, void* dx, float* gp, int64_t N, int H,
+                                                             int K, int d_r, int seg, int64_t n_seg, int dxa) {
+    static_assert(KC == 32 || KC == 64, "component padding");
+    static_assert(DRC == 64 || DRC == 128, "dim padding");
+    constexpr int C = kFusedChunk;
+    constexpr int NKS = KC / 32;            // 32-component steps of dx's contraction
+    constexpr int NDT = DRC / 16;           // dim tiles
+    constexpr int NCT = KC / 16;            // component tiles
+    constexpr int UPW = NCT * NDT / 4;      // (component tile, dim tile) pairs per wave
+    constexpr int IS = 2 * C + 16;          // image row: 64 tokens of bf16 plus padding
+    constexpr int WS = 2 * KC + 16;         // mu / s and 1 / s image row: KC components of bf16 plus padding
+    __shared__ __attribute__((aligned(16))) char s_dl[2 * KC * IS];     // dl hi, dl lo: [component][token]
+    __shared__ __attribute__((aligned(16))) char s_x[DRC * IS];         // x: [dim][token]
+    __shared__ __attribute__((aligned(16))) char s_w[2 * 2 * DRC * WS]; // hi, lo: [part * DRC + dim][component]
+    __shared__ float s_one[4][KC];
+    lds_char* const LDH = (lds_char*)s_dl;
+    lds_char* const LDL = LDH + KC * IS;
+    lds_char* const LX = (lds_char*)s_x;
+    lds_char* const LWH = (lds_char*)s_w;
+    lds_char* const LWL = LWH + 2 * DRC * WS;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / n_seg;
+    const int64_t sg = blockIdx.x % n_seg;
+    const int h = (int)(bh % H);
+    const int64_t t0 = sg * seg;
+    const int64_t t1 = t0 + seg < N ? t0 + seg : N;
+    const int nch = (int)((t1 - t0 + C - 1) / C);
+
+    // mu / s (part 0) and 1 / s (part 1) of the head, zero past K and d_r
+    {
+        const float* mwh = mw + (int64_t)h * K * 2 * d_r;
+        for (int e = tid; e < 2 * DRC * KC; e += 256) {
+            const int k = e % KC, row = e / KC, p = row / DRC, d = row % DRC;
+            const float v = (k < K && d < d_r) ? mwh[(int64_t)k * 2 * d_r + 2 * d + p] : 0.f;
+            const __bf16 hi = (__bf16)v;
+            lds_st<__bf16>(LWH + row * WS + 2 * k, hi);
+            lds_st<__bf16>(LWL + row * WS + 2 * k, (__bf16)(v - (float)hi));
+        }
+    }
+
+    // descriptors over this (batch, head): rows past N load as zero and their stores are dropped, and so
+    // are components past K and dims past d_r (offsets with bit 31 set)
+    const __amdgpu_buffer_rsrc_t rs_g = make_rsrc(gamma + bh * N * K, (uint32_t)(N * K * 4));
+    const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(dgamma + bh * N * K, (uint32_t)(N * K * 4));
+    const __amdgpu_buffer_rsrc_t rs_x =
+        make_rsrc(reinterpret_cast<const uint16_t*>(x) + bh * N * d_r, (uint32_t)(N * d_r * 2));
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(reinterpret_cast<uint16_t*>(dx) + bh * N * d_r, (uint32_t)(N * d_r * 2));
+    constexpr uint32_t kOut = 0x80000000u;
+
+    // this lane's row of the chunk at n0: gamma and dgamma components 32 ks + 8 g .. + 7, x dims 16 j + 4 g .. + 3
+    f32x4 ga[NKS][2], da[NKS][2];
+    u32x2 xa[NDT];
+    auto load = [&](int64_t n0) {
+        const uint32_t t = (uint32_t)(n0 + 16 * w + r);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int k = 32 * ks + 8 * g + 4 * hf;
+                const uint32_t off = k < K ? (t * K + k) * 4 : kOut;
+                ga[ks][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, off, 0, 0));
+                da[ks][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_d, off, 0, 0));
+            }
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) {
+            const int d = 16 * j + 4 * g;
+            xa[j] = __builtin_amdgcn_raw_buffer_load_b64(rs_x, d < d_r ? (t * d_r + d) * 2 : kOut, 0, 0);
+        }
+    };
+
+    f32x4 px[UPW], p2[UPW];
+#pragma unroll
+    for (int q = 0; q < UPW; ++q) px[q] = p2[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float s1[NKS][8];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s1[ks][e] = 0.f;
+
+    if (nch > 0) load(t0);
+    for (int c = 0; c < nch; ++c) {
+        const int64_t n0 = t0 + (int64_t)c * C;
+        // dl of this lane's row; hi + lo split as dx's B fragments
+        bf16x8 bh8[NKS], bl8[NKS];
+        {
+            float dot = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dot += ga[ks][hf][e] * da[ks][hf][e];
+            dot += __shfl_xor(dot, 16, 64);
+            dot += __shfl_xor(dot, 32, 64);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                float v[8];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[4 * hf + e] = ga[ks][hf][e] * (da[ks][hf][e] - dot);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s1[ks][e] += v[e];
+                split_bf16x8(v, bh8[ks], bl8[ks]);
+            }
+        }
+        u32x2 xcur[NDT];
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) xcur[j] = xa[j];
+        // every wave is done with the previous chunk's images
+        lds_barrier();
+        {
+            const int t = 16 * w + r;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int k = 32 * ks + 8 * g + e;
+                    lds_st<__bf16>(LDH + k * IS + 2 * t, bh8[ks][e]);
+                    lds_st<__bf16>(LDL + k * IS + 2 * t, bl8[ks][e]);
+                }
+#pragma unroll
+            for (int j = 0; j < NDT; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int d = 16 * j + 4 * g + i;
+                    const uint16_t xv = (uint16_t)(xcur[j][i >> 1] >> (16 * (i & 1)));
+                    lds_st<uint16_t>(LX + d * IS + 2 * t, xv);
+                }
+        }
+        lds_barrier();   // the chunk's images are complete
+        if (c + 1 < nch) load(n0 + C);
+        // P += dl^T [x | x^2] for this wave's pairs over the chunk's 64 tokens
+#pragma unroll
+        for (int q = 0; q < UPW; ++q) {
+            const int u = w + 4 * q, ct = u % NCT, dt = u / NCT;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int off = (32 * kt + 8 * g) * 2;
+                const bf16x8 ah = lds_ld<bf16x8>(LDH + (16 * ct + r) * IS + off);
+                const bf16x8 al = lds_ld<bf16x8>(LDL + (16 * ct + r) * IS + off);
+                const bf16x8 xf = lds_ld<bf16x8>(LX + (16 * dt + r) * IS + off);
+                float sq[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sq[e] = (float)xf[e] * (float)xf[e];
+                bf16x8 sh, sl;
+                split_bf16x8(sq, sh, sl);
+                mma(px[q], al, xf);
+                mma(px[q], ah, xf);
+                mma(p2[q], al, sh);
+                mma(p2[q], ah, sl);
+                mma(p2[q], ah, sh);
+            }
+        }
+        // dx of this lane's row, dims 16 j + 4 g .. + 3
+        {
+            const uint32_t t = (uint32_t)(n0 + 16 * w + r);
+#pragma unroll
+            for (int j = 0; j < NDT; ++j) {
+                f32x4 aa = f32x4{0.f, 0.f, 0.f, 0.f}, ab = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int off = (32 * ks + 8 * g) * 2;
+                    const bf16x8 wah = lds_ld<bf16x8>(LWH + (16 * j + r) * WS + off);
+                    const bf16x8 wal = lds_ld<bf16x8>(LWL + (16 * j + r) * WS + off);
+                    const bf16x8 wbh = lds_ld<bf16x8>(LWH + (DRC + 16 * j + r) * WS + off);
+                    const bf16x8 wbl = lds_ld<bf16x8>(LWL + (DRC + 16 * j + r) * WS + off);
+                    mma(aa, wah, bl8[ks]);
+                    mma(aa, wal, bh8[ks]);
+                    mma(aa, wah, bh8[ks]);
+                    mma(ab, wbh, bl8[ks]);
+                    mma(ab, wbl, bh8[ks]);
+                    mma(ab, wbh, bh8[ks]);
+                }
+                const int d = 16 * j + 4 * g;
+                f32x4 val;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float xv = __uint_as_float((xcur[j][i >> 1] >> (16 * (i & 1))) << 16);
+                    val[i] = aa[i] - xv * ab[i];
+                }
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack4(val)), rs_o,
+                                                      d < d_r ? (t * d_r + d) * 2 : kOut, 0, 0);
+            }
+        }
+    }
+
+    // the segment's partial: gp [bh][sg][K][dxa], columns x | x^2 | 1
+    float* gpo = gp + (bh * n_seg + sg) * (int64_t)K * dxa;
+#pragma unroll
+    for (int q = 0; q < UPW; ++q) {
+        const int u = w + 4 * q, ct = u % NCT, dt = u / NCT;
+        const int d = 16 * dt + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = 16 * ct + 4 * g + i;
+            if (k < K && d < d_r) {
+                gpo[(int64_t)k * dxa + d] = px[q][i];
+                gpo[(int64_t)k * dxa + d_r + d] = p2[q][i];
+            }
+        }
+    }
+    // ones column: sum over the 16 rows of each lane group, then over the waves in order
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = s1[ks][e];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+            if (r == 0) s_one[w][32 * ks + 8 * g + e] = v;
+        }
+    __syncthreads();
+    if (tid < K) gpo[(int64_t)tid * dxa + 2 * d_r] = s_one[0][tid] + s_one[1][tid] + s_one[2][tid] + s_one[3][tid];
+}
+
 // ---------------------------------------------------------------------------------- chunk states
 // The causal prefix states from the chunk terms Gamma_K^T [V | 1] (64 tokens per chunk, bf16 storage,
 // K = d_v = 128), as [K][dva] records (columns d_v .. dva - 1: Z, then zeros), in two passes over segments
@@ -2522,11 +2755,20 @@ bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const v
     return true;
 }
 
-bool bwd_fused_rows_supported(int K, int d_r, bool f32) { return !f32 && K == 128 && d_r == 128; }
+namespace {
+bool fused_rows_small(int K, int d_r) { return K <= 64 && d_r <= 128 && K % 4 == 0 && d_r % 4 == 0; }
+}  // namespace
 
-int bwd_fused_rows_seg(int64_t BH, int64_t N, int min_seg) {
+bool bwd_fused_rows_supported(int K, int d_r, bool f32) {
+    return !f32 && ((K == 128 && d_r == 128) || fused_rows_small(K, d_r));
+}
+
+int bwd_fused_rows_seg(int64_t BH, int64_t N, int K, int d_r, int min_seg) {
+    // the K = d_r = 128 kernel holds one workgroup per compute unit; the small classes' hold three or
+    // more (their loads wait in registers), so they take shorter segments for more workgroups
+    const int64_t target = (K == 128 && d_r == 128) ? 256 : 1024;
     int seg = 4096;
-    while (seg / 2 >= min_seg && BH * ((N + seg - 1) / seg) < 256) seg /= 2;
+    while (seg / 2 >= min_seg && BH * ((N + seg - 1) / seg) < target) seg /= 2;
     return seg < min_seg ? min_seg : seg;
 }
 
@@ -2572,6 +2814,22 @@ bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* 
     if (!bwd_fused_rows_supported(K, d_r, false) || seg % kFusedChunk != 0 || dxa < 2 * d_r + 1) return false;
     const int64_t n_seg = (N + seg - 1) / seg;
     const dim3 grid((unsigned)(BH * n_seg));
+    if (!(K == 128 && d_r == 128)) {
+        if (dl_in) return false;
+        if (K <= 32 && d_r <= 64)
+            bwd_rows_small_kernel<32, 64><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K, d_r, seg,
+                                                                      n_seg, dxa);
+        else if (K <= 32)
+            bwd_rows_small_kernel<32, 128><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K, d_r, seg,
+                                                                       n_seg, dxa);
+        else if (d_r <= 64)
+            bwd_rows_small_kernel<64, 64><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K, d_r, seg,
+                                                                      n_seg, dxa);
+        else
+            bwd_rows_small_kernel<64, 128><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K, d_r, seg,
+                                                                       n_seg, dxa);
+        return true;
+    }
     if (dl_in)
         bwd_fused_rows_kernel<128, 128, true><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, seg, n_seg,
                                                                           dxa);

@@ -123,16 +123,17 @@ bool launch_bwd_chunk_k(const float* gq, const float* gk, const void* v, const v
 // row in place of dGamma (gamma as the chunk's split image holds it, about 16 significant bits).
 
 // Posterior gradient, routing-input gradient and parameter partials of one side in one kernel
-// (bf16 storage, K = d_r = 128; bwd_fused_rows_supported): from gamma and dgamma [BH, N, K] fp32, the
+// (bf16 storage, K = d_r = 128, or K <= 64 and d_r <= 128 with both multiples of 4;
+// bwd_fused_rows_supported): from gamma and dgamma [BH, N, K] fp32, the
 // routing input x [BH, N, d_r] bf16 and mw (launch_bwd_prep) it writes dx [BH, N, d_r] bf16 and the
 // partials gp [BH][n_seg][K][dxa] (columns x | x^2 | 1 of dl^T [x | x^2 | 1], rows dxa >= 2 d_r + 1
 // floats apart) over segments of
 // `seg` tokens (n_seg = ceil(N / seg)).  dl itself is not written.  Bases 16-byte aligned,
-// (N + 64) K 4 < 2^31.  false: no fused kernel for this shape.
+// (N + 64) K 4 < 2^31 and N d_r 2 < 2^31.  false: no fused kernel for this shape (dl_in only at K = d_r = 128).
 // bwd_fused_rows_seg: the segment length, a power of two in [min_seg, 4096] (min_seg a power of two
 // >= 64, at most 4096), long enough to keep n_seg within the partials buffer sized for min_seg.
 bool bwd_fused_rows_supported(int K, int d_r, bool f32);
-int bwd_fused_rows_seg(int64_t BH, int64_t N, int min_seg);
+int bwd_fused_rows_seg(int64_t BH, int64_t N, int K, int d_r, int min_seg);
 bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* x, const float* mw, void* dx, float* gp,
                            int64_t BH, int64_t N, int H, int K, int d_r, int dxa, int seg, bool dl_in, hipStream_t s);
 // dl_in: dgamma already holds dl (from the chunk kernels with emit_dl) and gamma is not read.

@@ -1295,11 +1295,11 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     // Per side, the posterior gradient, the routing-input gradient and the parameter partials in one fused
     // kernel where there is one for the shape.  The partials buffer holds n_sg segments of kBwdSeg tokens
     // per side: the fused segments are no shorter, so their count fits.
-    const int fseg = bwd_fused_rows_seg(BH, N, kBwdSeg);
+    const int fseg = bwd_fused_rows_seg(BH, N, K, d_r, kBwdSeg);
     const int64_t fn = (N + fseg - 1) / fseg;
     const bool fused = bwd_fused_rows_supported(K, d_r, f32) && !misaligned(qx, 16) && !misaligned(kx, 16) &&
                        !misaligned(dqx, 16) && !misaligned(dkx, 16) && (N + 64) * K * 4 < (int64_t(1) << 31) &&
-                       fn <= b.n_sg;
+                       N * d_r * 2 < (int64_t(1) << 31) && fn <= b.n_sg;
     // Causal bf16 at K = d_v = 128: fused chunk kernels for the state terms, the query side (read phase,
     // chunk terms of the suffix sums, dGamma_Q) and the key side (dGamma_K, dV).  With the fused row kernel
     // after them they write dl in place of dGamma.

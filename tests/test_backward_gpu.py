@@ -104,6 +104,20 @@ def test_backward_odd_shapes(gma, shape, dtype, causal):
     check(w, inp, dout, causal, run_gpu(gma, w, inp, dout, causal))
 
 
+@pytest.mark.parametrize("shape", [(64, 32, 64), (128, 32, 64), (64, 64, 32), (128, 64, 64), (36, 20, 40),
+                                   (100, 44, 24), (12, 4, 8)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_small_fused_row_classes(gma, shape, causal):
+    # bf16 storage with K <= 64 and d_r <= 128 (multiples of 4): the fused posterior / routing-input /
+    # parameter-partial row kernel of each padded class (K to 32 or 64, d_r to 64 or 128), over three
+    # segments of 1024 tokens with a ragged last chunk
+    d_r, K, d_v = shape
+    w = gma.workload(2).with_(batch=1, heads=2, seq_len=2500, d_route=d_r, n_comp=K, d_value=d_v)
+    say("backward small class shape=%s causal=%s" % (shape, causal))
+    inp, dout = inputs(gma, w, True)
+    check(w, inp, dout, causal, run_gpu(gma, w, inp, dout, causal))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_single_token_small_eps(gma, causal):
     # the degenerate case above at eps = 1e-6: dv = (gamma_Q . gamma_K) dO / (gamma_Q . gamma_K + eps) is
