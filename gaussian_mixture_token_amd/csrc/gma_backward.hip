@@ -1359,6 +1359,488 @@ __global__ void __launch_bounds__(256) bwd_rows_small_kernel(const float* gamma,
     if (tid < K) gpo[(int64_t)tid * dxa + 2 * d_r] = s_one[0][tid] + s_one[1][tid] + s_one[2][tid] + s_one[3][tid];
 }
 
+// ---------------------------------------------------------------------------------- bidirectional, small classes
+// The bidirectional backward's products for bf16 storage at K <= 64 and d_v <= 128 (multiples of 4; padded
+// to KC in {32, 64} and VC in {64, 128}), with the notation of the general path: the state
+// S = Gamma_K^T [V | 1] (its last column Z), per row num = Gamma_Q S_v, den = Gamma_Q Z, inv = 1 / (den +
+// eps), g = dO inv, h = -(dO . num) inv^2, then dGamma_Q = g S_v^T + h Z^T, R = Gamma_Q^T [g | h] summed
+// over all rows, dGamma_K = V R_v^T + R_1^T and dV = Gamma_K R_v.  Three kernels over segments of `seg`
+// tokens (a multiple of 64) of one (batch, head), four wavefronts in chunks of 64 tokens; wave w loads rows
+// 16 w .. 16 w + 15 of each chunk (lane (r, g): row r, components 32 ks + 8 g .. + 7 of the Gamma rows,
+// dims 16 j + 4 g .. + 3 of the bf16 rows), the next chunk's while the current one is in the products.
+// Row-wise products are formed with that lane's registers as the B operand (Gamma split into bf16 hi + lo;
+// dims in the permuted order 32 vs + 4 g .. + 3, 32 vs + 16 + 4 g .. + 3, the same order in both operands);
+// sums over tokens go through LDS images, component- or dim-major with rows of 64 tokens.  S and R (one
+// record per segment) are summed over the segments by the scan kernel (mode 2), in segment order; their
+// last column is summed on the vector units in fp32.  Where both operands are fp32 values a product is
+// hi hi + hi lo + lo hi, against exact bf16 values hi + lo.
+namespace {
+
+constexpr int kImgRow = 2 * 64 + 16;   // a 64-token bf16 image row plus padding (bytes)
+
+// Permuted 8-element fragment of an LDS row of bf16 values: elements 32 vs + 4 g .. + 3 and
+// 32 vs + 16 + 4 g .. + 3.
+__device__ __forceinline__ bf16x8 row_perm(const lds_char* row, int vs, int g) {
+    const u32x2 a = lds_ld<u32x2>(row + (32 * vs + 4 * g) * 2);
+    const u32x2 b = lds_ld<u32x2>(row + (32 * vs + 16 + 4 * g) * 2);
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+// A record [K][dva] (fp32) of this (batch, head) into split bf16 images, component-major [comp][dim]
+// (rows of 2 VC + 16 bytes) and dim-major [dim][comp] (rows of 2 KC + 16 bytes), zero past K and d_v;
+// its column d_v into last[comp].
+template <int KC, int VC>
+__device__ __forceinline__ void stage_record(const float* rec, int K, int d_v, int dva, lds_char* ch, lds_char* cl,
+                                             lds_char* dh, lds_char* dl, float* last) {
+    constexpr int WC = 2 * VC + 16, WD = 2 * KC + 16;
+    for (int e = threadIdx.x; e < KC * VC; e += 256) {
+        const int k = e / VC, d = e % VC;
+        const float v = (k < K && d < d_v) ? rec[(int64_t)k * dva + d] : 0.f;
+        const __bf16 hi = (__bf16)v, lo = (__bf16)(v - (float)hi);
+        lds_st<__bf16>(ch + k * WC + 2 * d, hi);
+        lds_st<__bf16>(cl + k * WC + 2 * d, lo);
+        lds_st<__bf16>(dh + d * WD + 2 * k, hi);
+        lds_st<__bf16>(dl + d * WD + 2 * k, lo);
+    }
+    for (int k = threadIdx.x; k < KC; k += 256) last[k] = k < K ? rec[(int64_t)k * dva + d_v] : 0.f;
+}
+
+// The record of a segment: the (component tile, dim tile) pairs of the wave (lane: components
+// 16 ct + 4 g + i, dim 16 dt + r), the last column from each lane's per-row sums `z` (components
+// 32 ks + 8 g + e) reduced over the rows and the waves in order, zeros after it.
+template <int KC, int VC, int UPW, int NKS>
+__device__ __forceinline__ void write_record(float* out, const f32x4 (&acc)[UPW], const float (&z)[NKS][8],
+                                             float (*s_z)[KC], int K, int d_v, int dva) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int q = 0; q < UPW; ++q) {
+        const int u = w + 4 * q, ct = u % (KC / 16), dt = u / (KC / 16);
+        const int d = 16 * dt + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = 16 * ct + 4 * g + i;
+            if (k < K && d < d_v) out[(int64_t)k * dva + d] = acc[q][i];
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = z[ks][e];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+            if (r == 0) s_z[w][32 * ks + 8 * g + e] = v;
+        }
+    __syncthreads();
+    const int pad = dva - d_v;
+    for (int e = threadIdx.x; e < K * pad; e += 256) {
+        const int k = e / pad, c = e % pad;
+        out[(int64_t)k * dva + d_v + c] = c == 0 ? s_z[0][k] + s_z[1][k] + s_z[2][k] + s_z[3][k] : 0.f;
+    }
+}
+
+}  // namespace
+
+// S per segment: st [BH][n_seg][K][dva].
+template <int KC, int VC>
+__global__ void __launch_bounds__(256) bwd_bidir_state_kernel(const float* gk, const void* v, float* st, int64_t N,
+                                                              int K, int d_v, int dva, int seg, int64_t n_seg) {
+    constexpr int C = kFusedChunk, NKS = KC / 32, NVT = VC / 16, NCT = KC / 16, UPW = NCT * NVT / 4;
+    constexpr int IS = kImgRow;
+    __shared__ __attribute__((aligned(16))) char s_g[2 * KC * IS];   // Gamma_K hi, lo: [comp][token]
+    __shared__ __attribute__((aligned(16))) char s_v[VC * IS];       // V: [dim][token]
+    __shared__ float s_z[4][KC];
+    lds_char* const LGH = (lds_char*)s_g;
+    lds_char* const LGL = LGH + KC * IS;
+    lds_char* const LV = (lds_char*)s_v;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / n_seg, sg = blockIdx.x % n_seg;
+    const int64_t t0 = sg * seg;
+    const int64_t t1 = t0 + seg < N ? t0 + seg : N;
+    const int nch = (int)((t1 - t0 + C - 1) / C);
+    const __amdgpu_buffer_rsrc_t rs_g = make_rsrc(gk + bh * N * K, (uint32_t)(N * K * 4));
+    const __amdgpu_buffer_rsrc_t rs_v =
+        make_rsrc(reinterpret_cast<const uint16_t*>(v) + bh * N * d_v, (uint32_t)(N * d_v * 2));
+    constexpr uint32_t kOut = 0x80000000u;
+
+    f32x4 ga[NKS][2];
+    u32x2 va[NVT];
+    auto load = [&](int64_t n0) {
+        const uint32_t t = (uint32_t)(n0 + 16 * w + r);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int k = 32 * ks + 8 * g + 4 * hf;
+                ga[ks][hf] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, k < K ? (t * K + k) * 4 : kOut, 0, 0));
+            }
+#pragma unroll
+        for (int j = 0; j < NVT; ++j) {
+            const int d = 16 * j + 4 * g;
+            va[j] = __builtin_amdgcn_raw_buffer_load_b64(rs_v, d < d_v ? (t * d_v + d) * 2 : kOut, 0, 0);
+        }
+    };
+
+    f32x4 acc[UPW];
+#pragma unroll
+    for (int q = 0; q < UPW; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float z[NKS][8];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[ks][e] = 0.f;
+
+    if (nch > 0) load(t0);
+    for (int c = 0; c < nch; ++c) {
+        const int64_t n0 = t0 + (int64_t)c * C;
+        bf16x8 gh8[NKS], gl8[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            float gv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                gv[e] = ga[ks][e >> 2][e & 3];
+                z[ks][e] += gv[e];
+            }
+            split_bf16x8(gv, gh8[ks], gl8[ks]);
+        }
+        u32x2 vcur[NVT];
+#pragma unroll
+        for (int j = 0; j < NVT; ++j) vcur[j] = va[j];
+        if (c + 1 < nch) load(n0 + C);
+        lds_barrier();   // every wave is done with the previous chunk's images
+        {
+            const int t = 16 * w + r;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int k = 32 * ks + 8 * g + e;
+                    lds_st<__bf16>(LGH + k * IS + 2 * t, gh8[ks][e]);
+                    lds_st<__bf16>(LGL + k * IS + 2 * t, gl8[ks][e]);
+                }
+#pragma unroll
+            for (int j = 0; j < NVT; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    lds_st<uint16_t>(LV + (16 * j + 4 * g + i) * IS + 2 * t,
+                                     (uint16_t)(vcur[j][i >> 1] >> (16 * (i & 1))));
+        }
+        lds_barrier();   // the chunk's images are complete
+#pragma unroll
+        for (int q = 0; q < UPW; ++q) {
+            const int u = w + 4 * q, ct = u % NCT, dt = u / NCT;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int off = (32 * kt + 8 * g) * 2;
+                const bf16x8 ah = lds_ld<bf16x8>(LGH + (16 * ct + r) * IS + off);
+                const bf16x8 al = lds_ld<bf16x8>(LGL + (16 * ct + r) * IS + off);
+                const bf16x8 vf = lds_ld<bf16x8>(LV + (16 * dt + r) * IS + off);
+                mma(acc[q], al, vf);
+                mma(acc[q], ah, vf);
+            }
+        }
+    }
+    write_record<KC, VC, UPW, NKS>(st + (bh * n_seg + sg) * (int64_t)K * dva, acc, z, s_z, K, d_v, dva);
+}
+
+// Query side: dGamma_Q [BH][N][K] and the segments' R records r_seg [BH][n_seg][K][dva], from the summed
+// state (entry 0 of st [BH][n_seg][K][dva]).
+template <int KC, int VC>
+__global__ void __launch_bounds__(256) bwd_bidir_q_kernel(const float* gq, const void* dout, const float* st,
+                                                          float* dgq, float* r_seg, int64_t N, int K, int d_v,
+                                                          int dva, int seg, int64_t n_seg, float eps) {
+    constexpr int C = kFusedChunk, NKS = KC / 32, NVT = VC / 16, NVS = VC / 32, NCT = KC / 16;
+    constexpr int UPW = NCT * NVT / 4, IS = kImgRow, WC = 2 * VC + 16, WD = 2 * KC + 16;
+    __shared__ __attribute__((aligned(16))) char s_sc[2 * KC * WC];   // S_v hi, lo: [comp][dim]
+    __shared__ __attribute__((aligned(16))) char s_sd[2 * VC * WD];   // S_v^T hi, lo: [dim][comp]
+    __shared__ __attribute__((aligned(16))) char s_g[2 * KC * IS];    // Gamma_Q hi, lo: [comp][token]
+    __shared__ __attribute__((aligned(16))) char s_x[2 * VC * IS];    // g hi, lo: [dim][token]
+    __shared__ float s_zt[KC];
+    __shared__ float s_z[4][KC];
+    lds_char* const SCH = (lds_char*)s_sc;
+    lds_char* const SCL = SCH + KC * WC;
+    lds_char* const SDH = (lds_char*)s_sd;
+    lds_char* const SDL = SDH + VC * WD;
+    lds_char* const LGH = (lds_char*)s_g;
+    lds_char* const LGL = LGH + KC * IS;
+    lds_char* const LXH = (lds_char*)s_x;
+    lds_char* const LXL = LXH + VC * IS;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / n_seg, sg = blockIdx.x % n_seg;
+    const int64_t t0 = sg * seg;
+    const int64_t t1 = t0 + seg < N ? t0 + seg : N;
+    const int nch = (int)((t1 - t0 + C - 1) / C);
+    const __amdgpu_buffer_rsrc_t rs_g = make_rsrc(gq + bh * N * K, (uint32_t)(N * K * 4));
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(dgq + bh * N * K, (uint32_t)(N * K * 4));
+    const __amdgpu_buffer_rsrc_t rs_d =
+        make_rsrc(reinterpret_cast<const uint16_t*>(dout) + bh * N * d_v, (uint32_t)(N * d_v * 2));
+    constexpr uint32_t kOut = 0x80000000u;
+
+    stage_record<KC, VC>(st + bh * n_seg * (int64_t)K * dva, K, d_v, dva, SCH, SCL, SDH, SDL, s_zt);
+
+    f32x4 ga[NKS][2];
+    u32x2 da[NVT];
+    auto load = [&](int64_t n0) {
+        const uint32_t t = (uint32_t)(n0 + 16 * w + r);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int k = 32 * ks + 8 * g + 4 * hf;
+                ga[ks][hf] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, k < K ? (t * K + k) * 4 : kOut, 0, 0));
+            }
+#pragma unroll
+        for (int j = 0; j < NVT; ++j) {
+            const int d = 16 * j + 4 * g;
+            da[j] = __builtin_amdgcn_raw_buffer_load_b64(rs_d, d < d_v ? (t * d_v + d) * 2 : kOut, 0, 0);
+        }
+    };
+
+    f32x4 acc[UPW];
+#pragma unroll
+    for (int q = 0; q < UPW; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float z[NKS][8];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[ks][e] = 0.f;
+
+    if (nch > 0) load(t0);
+    __syncthreads();   // the staged state
+    for (int c = 0; c < nch; ++c) {
+        const int64_t n0 = t0 + (int64_t)c * C;
+        const uint32_t t = (uint32_t)(n0 + 16 * w + r);
+        float gv[NKS][8];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gv[ks][e] = ga[ks][e >> 2][e & 3];
+        float dov[NVT][4];
+#pragma unroll
+        for (int j = 0; j < NVT; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dov[j][i] = __uint_as_float((da[j][i >> 1] >> (16 * (i & 1))) << 16);
+        if (c + 1 < nch) load(n0 + C);
+
+        // den and num of this lane's row (num: dims 16 j + 4 g .. + 3)
+        bf16x8 gh8[NKS], gl8[NKS];
+        float den = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) den += gv[ks][e] * s_zt[32 * ks + 8 * g + e];
+            split_bf16x8(gv[ks], gh8[ks], gl8[ks]);
+        }
+        den += __shfl_xor(den, 16, 64);
+        den += __shfl_xor(den, 32, 64);
+        const float inv = t < (uint32_t)t1 ? 1.f / (den + eps) : 0.f;
+        float dot = 0.f;
+#pragma unroll
+        for (int j = 0; j < NVT; ++j) {
+            f32x4 nm = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = (32 * ks + 8 * g) * 2;
+                const bf16x8 ah = lds_ld<bf16x8>(SDH + (16 * j + r) * WD + off);
+                const bf16x8 al = lds_ld<bf16x8>(SDL + (16 * j + r) * WD + off);
+                mma(nm, ah, gl8[ks]);
+                mma(nm, al, gh8[ks]);
+                mma(nm, ah, gh8[ks]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dot += dov[j][i] * (nm[i] * inv);
+        }
+        dot += __shfl_xor(dot, 16, 64);
+        dot += __shfl_xor(dot, 32, 64);
+        const float hv = -dot * inv;
+        // g in the permuted dim order, split
+        bf16x8 xh8[NVS], xl8[NVS];
+#pragma unroll
+        for (int vs = 0; vs < NVS; ++vs) {
+            float gg[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                gg[e] = dov[2 * vs][e] * inv;
+                gg[4 + e] = dov[2 * vs + 1][e] * inv;
+            }
+            split_bf16x8(gg, xh8[vs], xl8[vs]);
+        }
+        // dGamma_Q of this lane's row, components 16 ct + 4 g .. + 3
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 dg = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int vs = 0; vs < NVS; ++vs) {
+                const bf16x8 ah = row_perm(SCH + (16 * ct + r) * WC, vs, g);
+                const bf16x8 al = row_perm(SCL + (16 * ct + r) * WC, vs, g);
+                mma(dg, ah, xl8[vs]);
+                mma(dg, al, xh8[vs]);
+                mma(dg, ah, xh8[vs]);
+            }
+            const int k = 16 * ct + 4 * g;
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = dg[i] + hv * s_zt[k + i];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_o, k < K ? (t * K + k) * 4 : kOut,
+                                                   0, 0);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[ks][e] += gv[ks][e] * hv;
+
+        // R += Gamma_Q^T g over the chunk
+        lds_barrier();   // every wave is done with the previous chunk's images
+        {
+            const int tt = 16 * w + r;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int k = 32 * ks + 8 * g + e;
+                    lds_st<__bf16>(LGH + k * IS + 2 * tt, gh8[ks][e]);
+                    lds_st<__bf16>(LGL + k * IS + 2 * tt, gl8[ks][e]);
+                }
+#pragma unroll
+            for (int vs = 0; vs < NVS; ++vs)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int d = 32 * vs + (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
+                    lds_st<__bf16>(LXH + d * IS + 2 * tt, xh8[vs][e]);
+                    lds_st<__bf16>(LXL + d * IS + 2 * tt, xl8[vs][e]);
+                }
+        }
+        lds_barrier();   // the chunk's images are complete
+#pragma unroll
+        for (int q = 0; q < UPW; ++q) {
+            const int u = w + 4 * q, ct = u % NCT, dt = u / NCT;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int off = (32 * kt + 8 * g) * 2;
+                const bf16x8 ah = lds_ld<bf16x8>(LGH + (16 * ct + r) * IS + off);
+                const bf16x8 al = lds_ld<bf16x8>(LGL + (16 * ct + r) * IS + off);
+                const bf16x8 bh = lds_ld<bf16x8>(LXH + (16 * dt + r) * IS + off);
+                const bf16x8 bl = lds_ld<bf16x8>(LXL + (16 * dt + r) * IS + off);
+                mma(acc[q], ah, bl);
+                mma(acc[q], al, bh);
+                mma(acc[q], ah, bh);
+            }
+        }
+    }
+    write_record<KC, VC, UPW, NKS>(r_seg + (bh * n_seg + sg) * (int64_t)K * dva, acc, z, s_z, K, d_v, dva);
+}
+
+// Key side: dGamma_K [BH][N][K] fp32 and dV [BH][N][d_v] bf16 from the summed R (entry 0 of
+// r_seg [BH][n_seg][K][dva]).
+template <int KC, int VC>
+__global__ void __launch_bounds__(256) bwd_bidir_k_kernel(const float* gk, const void* v, const float* r_seg,
+                                                          float* dgk, void* dv, int64_t N, int K, int d_v, int dva,
+                                                          int seg, int64_t n_seg) {
+    constexpr int C = kFusedChunk, NKS = KC / 32, NVT = VC / 16, NVS = VC / 32, NCT = KC / 16;
+    constexpr int WC = 2 * VC + 16, WD = 2 * KC + 16;
+    __shared__ __attribute__((aligned(16))) char s_rc[2 * KC * WC];   // R_v hi, lo: [comp][dim]
+    __shared__ __attribute__((aligned(16))) char s_rd[2 * VC * WD];   // R_v^T hi, lo: [dim][comp]
+    __shared__ float s_r1[KC];
+    lds_char* const RCH = (lds_char*)s_rc;
+    lds_char* const RCL = RCH + KC * WC;
+    lds_char* const RDH = (lds_char*)s_rd;
+    lds_char* const RDL = RDH + VC * WD;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t bh = blockIdx.x / n_seg, sg = blockIdx.x % n_seg;
+    const int64_t t0 = sg * seg;
+    const int64_t t1 = t0 + seg < N ? t0 + seg : N;
+    const int nch = (int)((t1 - t0 + C - 1) / C);
+    const __amdgpu_buffer_rsrc_t rs_g = make_rsrc(gk + bh * N * K, (uint32_t)(N * K * 4));
+    const __amdgpu_buffer_rsrc_t rs_o = make_rsrc(dgk + bh * N * K, (uint32_t)(N * K * 4));
+    const __amdgpu_buffer_rsrc_t rs_v =
+        make_rsrc(reinterpret_cast<const uint16_t*>(v) + bh * N * d_v, (uint32_t)(N * d_v * 2));
+    const __amdgpu_buffer_rsrc_t rs_w = make_rsrc(reinterpret_cast<uint16_t*>(dv) + bh * N * d_v, (uint32_t)(N * d_v * 2));
+    constexpr uint32_t kOut = 0x80000000u;
+
+    stage_record<KC, VC>(r_seg + bh * n_seg * (int64_t)K * dva, K, d_v, dva, RCH, RCL, RDH, RDL, s_r1);
+
+    f32x4 ga[NKS][2];
+    u32x2 va[NVT];
+    auto load = [&](int64_t n0) {
+        const uint32_t t = (uint32_t)(n0 + 16 * w + r);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int k = 32 * ks + 8 * g + 4 * hf;
+                ga[ks][hf] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, k < K ? (t * K + k) * 4 : kOut, 0, 0));
+            }
+#pragma unroll
+        for (int j = 0; j < NVT; ++j) {
+            const int d = 16 * j + 4 * g;
+            va[j] = __builtin_amdgcn_raw_buffer_load_b64(rs_v, d < d_v ? (t * d_v + d) * 2 : kOut, 0, 0);
+        }
+    };
+
+    if (nch > 0) load(t0);
+    __syncthreads();   // the staged R
+    for (int c = 0; c < nch; ++c) {
+        const int64_t n0 = t0 + (int64_t)c * C;
+        const uint32_t t = (uint32_t)(n0 + 16 * w + r);
+        bf16x8 gh8[NKS], gl8[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            float gv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gv[e] = ga[ks][e >> 2][e & 3];
+            split_bf16x8(gv, gh8[ks], gl8[ks]);
+        }
+        bf16x8 vf[NVS];
+#pragma unroll
+        for (int vs = 0; vs < NVS; ++vs)
+            vf[vs] = __builtin_bit_cast(bf16x8, u32x4{va[2 * vs][0], va[2 * vs][1], va[2 * vs + 1][0], va[2 * vs + 1][1]});
+        if (c + 1 < nch) load(n0 + C);
+        // dGamma_K of this lane's row, components 16 ct + 4 g .. + 3
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 dg = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int vs = 0; vs < NVS; ++vs) {
+                mma(dg, row_perm(RCL + (16 * ct + r) * WC, vs, g), vf[vs]);
+                mma(dg, row_perm(RCH + (16 * ct + r) * WC, vs, g), vf[vs]);
+            }
+            const int k = 16 * ct + 4 * g;
+            f32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = dg[i] + s_r1[k + i];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_o, k < K ? (t * K + k) * 4 : kOut,
+                                                   0, 0);
+        }
+        // dV of this lane's row, dims 16 j + 4 g .. + 3
+#pragma unroll
+        for (int j = 0; j < NVT; ++j) {
+            f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = (32 * ks + 8 * g) * 2;
+                const bf16x8 ah = lds_ld<bf16x8>(RDH + (16 * j + r) * WD + off);
+                const bf16x8 al = lds_ld<bf16x8>(RDL + (16 * j + r) * WD + off);
+                mma(o, ah, gl8[ks]);
+                mma(o, al, gh8[ks]);
+                mma(o, ah, gh8[ks]);
+            }
+            const int d = 16 * j + 4 * g;
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack4(o)), rs_w,
+                                                  d < d_v ? (t * d_v + d) * 2 : kOut, 0, 0);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------- chunk states
 // The causal prefix states from the chunk terms Gamma_K^T [V | 1] (64 tokens per chunk, bf16 storage,
 // K = d_v = 128), as [K][dva] records (columns d_v .. dva - 1: Z, then zeros), in two passes over segments
@@ -2836,6 +3318,58 @@ bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* 
     else
         bwd_fused_rows_kernel<128, 128, false><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, seg, n_seg,
                                                                            dxa);
+    return true;
+}
+
+bool bwd_bidir_small_supported(int K, int d_v, bool f32) {
+    return !f32 && K <= 64 && d_v <= 128 && K % 4 == 0 && d_v % 4 == 0;
+}
+
+namespace {
+// Calls f(KC, VC) with the padded class of (K, d_v) as integral constants.
+template <class F>
+void bidir_class(int K, int d_v, F&& f) {
+    using I32 = std::integral_constant<int, 32>;
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    if (K <= 32 && d_v <= 64) f(I32{}, I64{});
+    else if (K <= 32) f(I32{}, I128{});
+    else if (d_v <= 64) f(I64{}, I64{});
+    else f(I64{}, I128{});
+}
+}  // namespace
+
+bool launch_bwd_bidir_state(const float* gk, const void* v, float* st, int64_t BH, int64_t N, int K, int d_v, int dva,
+                            int seg, hipStream_t s) {
+    if (!bwd_bidir_small_supported(K, d_v, false) || dva != d_v + 4 || seg % kFusedChunk != 0) return false;
+    const int64_t n_seg = (N + seg - 1) / seg;
+    bidir_class(K, d_v, [&](auto kc, auto vc) {
+        bwd_bidir_state_kernel<decltype(kc)::value, decltype(vc)::value>
+            <<<dim3((unsigned)(BH * n_seg)), dim3(256), 0, s>>>(gk, v, st, N, K, d_v, dva, seg, n_seg);
+    });
+    return true;
+}
+
+bool launch_bwd_bidir_q(const float* gq, const void* dout, const float* st, float* dgq, float* r_seg, int64_t BH,
+                        int64_t N, int K, int d_v, int dva, int seg, float eps, hipStream_t s) {
+    if (!bwd_bidir_small_supported(K, d_v, false) || dva != d_v + 4 || seg % kFusedChunk != 0) return false;
+    const int64_t n_seg = (N + seg - 1) / seg;
+    bidir_class(K, d_v, [&](auto kc, auto vc) {
+        bwd_bidir_q_kernel<decltype(kc)::value, decltype(vc)::value>
+            <<<dim3((unsigned)(BH * n_seg)), dim3(256), 0, s>>>(gq, dout, st, dgq, r_seg, N, K, d_v, dva, seg, n_seg,
+                                                               eps);
+    });
+    return true;
+}
+
+bool launch_bwd_bidir_k(const float* gk, const void* v, const float* r_seg, float* dgk, void* dv, int64_t BH, int64_t N,
+                        int K, int d_v, int dva, int seg, hipStream_t s) {
+    if (!bwd_bidir_small_supported(K, d_v, false) || dva != d_v + 4 || seg % kFusedChunk != 0) return false;
+    const int64_t n_seg = (N + seg - 1) / seg;
+    bidir_class(K, d_v, [&](auto kc, auto vc) {
+        bwd_bidir_k_kernel<decltype(kc)::value, decltype(vc)::value>
+            <<<dim3((unsigned)(BH * n_seg)), dim3(256), 0, s>>>(gk, v, r_seg, dgk, dv, N, K, d_v, dva, seg, n_seg);
+    });
     return true;
 }
 

@@ -137,6 +137,23 @@ int bwd_fused_rows_seg(int64_t BH, int64_t N, int K, int d_r, int min_seg);
 bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* x, const float* mw, void* dx, float* gp,
                            int64_t BH, int64_t N, int H, int K, int d_r, int dxa, int seg, bool dl_in, hipStream_t s);
 // dl_in: dgamma already holds dl (from the chunk kernels with emit_dl) and gamma is not read.
+// Bidirectional backward products in three fused kernels (bf16 storage, K <= 64 and d_v <= 128, both
+// multiples of 4, dva = d_v + 4; bwd_bidir_small_supported), over segments of `seg` tokens (a multiple
+// of 64; n_seg = ceil(N / seg) records per (batch, head), each [K][dva]):
+//   state: st [BH][n_seg] <- each segment's Gamma_K^T [V | 1] (columns past d_v: Z, then zeros);
+//   q: with the summed state in entry 0 of st, dGamma_Q [BH, N, K] = g S_v^T + h Z^T and r_seg [BH][n_seg]
+//      <- each segment's Gamma_Q^T [g | h], where g = dO / (Gamma_Q . Z + eps) and h = -(dO . num) g's
+//      scale squared per row;
+//   k: with the summed R in entry 0 of r_seg, dGamma_K [BH, N, K] = V R_v^T + R_1^T and dV [BH, N, d_v]
+//      = Gamma_K R_v (bf16).
+// V, dO and dV rows 8-byte aligned; (N + 64) K 4 and N d_v 2 below 2^31.  false: not supported.
+bool bwd_bidir_small_supported(int K, int d_v, bool f32);
+bool launch_bwd_bidir_state(const float* gk, const void* v, float* st, int64_t BH, int64_t N, int K, int d_v, int dva,
+                            int seg, hipStream_t s);
+bool launch_bwd_bidir_q(const float* gq, const void* dout, const float* st, float* dgq, float* r_seg, int64_t BH,
+                        int64_t N, int K, int d_v, int dva, int seg, float eps, hipStream_t s);
+bool launch_bwd_bidir_k(const float* gk, const void* v, const float* r_seg, float* dgk, void* dv, int64_t BH, int64_t N,
+                        int K, int d_v, int dva, int seg, hipStream_t s);
 // Chunk-state scans over [n_outer][n][rec]: mode 0 exclusive prefix in place, 1 exclusive suffix in
 // place, 2 the total into entry 0.  rec is a multiple of 4 (K times d_v + 1 rounded up to 4) and st
 // 16-byte aligned.

@@ -1305,6 +1305,12 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     // after them they write dl in place of dGamma.
     const bool qfused = b.fq;
     const bool emit_dl = qfused && fused;
+    // Bidirectional bf16 at K <= 64, d_v <= 128: fused kernels for the state, the query side (num, den, g,
+    // h, dGamma_Q and the segment sums of Gamma_Q^T [g | h]) and the key side (dGamma_K, dV), over the
+    // state segments of C tokens
+    const bool bq = !causal && bwd_bidir_small_supported(K, d_v, f32) && dva == d_v + 4 && !misaligned(v, 8) &&
+                    !misaligned(dout, 8) && !misaligned(dv, 8) && (N + 64) * K * 4 < (int64_t(1) << 31) &&
+                    (N + 64) * d_v * 2 < (int64_t(1) << 31);
     // the chunk kernels read and write whole 16-byte pieces of bf16 rows: rows that are not 16-byte aligned
     // go through aligned copies in the workspace
     const void* vq = v;
@@ -1339,6 +1345,22 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
             launch_bwd_chunk_state(gk, vq, stt, sgs, b.sper, false, BH, N, b.n_st, K, d_v, dva, s);
         }));
+    } else if (bq) {
+        bool ok = true;
+        GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
+            ok = launch_bwd_bidir_state(gk, v, stt, BH, N, K, d_v, dva, C, s);
+        }));
+        if (!ok) return fail(GMA_ERROR_LAUNCH, "no bidirectional state kernel for this shape");
+        GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, 2, s); }));
+        GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
+            ok = launch_bwd_bidir_q(gq, dout, stt, dgq, rt, BH, N, K, d_v, dva, C, b.eps, s);
+        }));
+        if (!ok) return fail(GMA_ERROR_LAUNCH, "no bidirectional query-side kernel for this shape");
+        GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(rt, BH, b.n_st, rec, 2, s); }));
+        GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
+            ok = launch_bwd_bidir_k(gk, v, rt, dgk, dv, BH, N, K, d_v, dva, C, s);
+        }));
+        if (!ok) return fail(GMA_ERROR_LAUNCH, "no bidirectional key-side kernel for this shape");
     } else {
         GMA_TRY(gemm(tok(gk, K), true, vv, false, all_st(stt), stt, false, K, dva, C, TK, 0, nullptr, false, BwdGen{},
                      gen_v));
@@ -1358,7 +1380,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
             launch_bwd_suffix_state(gq, dq, rs, rt, sgs, b.sper, BH, N, b.n_st, K, d_v, dva, s);
         }));
     }
-    if (!qfused) {
+    if (!qfused && !bq) {
         // read phase: [num | Gamma_Q . Z] = Gamma_Q state (+ tril(Gamma_Q Gamma_K^T) [V | 1]), then g, h
         GMA_TRY(gemm(tok(gq, K), false, cur_st(stt), false, tok(pp, dva), pp, false, C, dva, K, TM, 0, nullptr, false));
         if (causal) {
@@ -1385,7 +1407,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused key-side chunk kernel for this shape");
         if (dvq != dv && hipMemcpyAsync(dv, dvq, row_bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
             return fail(GMA_ERROR_LAUNCH, "copy of the staged dv failed");
-    } else {
+    } else if (!bq) {
         // dGamma_K = [V | 1] R^T (+ the same intra-chunk block transposed, times Gamma_Q)
         GMA_TRY(gemm(vv, false, cur_st(rt), true, tok(dgk, K), dgk, false, C, K, dva, TM, 0, nullptr, false, gen_v));
         if (causal)
