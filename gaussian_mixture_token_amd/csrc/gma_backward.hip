@@ -3008,42 +3008,52 @@ __global__ void __launch_bounds__(64) bwd_scan_kernel(float* st, int64_t n, int6
 }
 
 // ---------------------------------------------------------------------------------- parameters
-// gp [2][B * H][n_seg][K][dxa]; element (k, d) of head blockIdx.y sums its partials in a fixed order:
+// gp [2][B * H][n_seg][K][dxa]: the partial records of a head, nt = 2 B n_seg of them, summed per
+// element into gs [H][K][dxa]:
 //   G1 = sum dl x_d, G2 = sum dl x_d^2, G0 = sum dl
 //   dmu = (G1 - mu G0) / s, ds = ((G2 - 2 mu G1 + mu^2 G0) / s^2 - G0 / s) / 2, draw_var = ds sigmoid(rho)
 constexpr int kParamBatch = 16;  // partial loads in flight per thread in the parameter reductions
 
-__global__ void __launch_bounds__(256) bwd_param_kernel(const float* gp, const float* mu, const float* raw_var,
-                                                        float* dmu, float* draw_var, int64_t B, int H, int K, int d_r,
-                                                        int dxa, int64_t n_seg) {
+// Workgroup: 64 consecutive elements of one head; wave s sums records s nt / 4 .. (s + 1) nt / 4 - 1
+// in order (kParamBatch loads in flight), then the four slices are added in order.
+__global__ void __launch_bounds__(256) bwd_param_sum_kernel(const float* gp, float* gs, int64_t B, int H,
+                                                            int64_t part, int64_t n_seg) {
+    __shared__ float s_acc[4][64];
+    const int64_t per = (part + 63) / 64;   // element blocks per head
+    const int h = (int)(blockIdx.x / per);
+    const int l = threadIdx.x & 63, sl = threadIdx.x >> 6;
+    const int64_t e = (blockIdx.x % per) * 64 + l;
+    const int64_t nt = 2 * B * n_seg;
+    const int64_t a = nt * sl / 4, z = nt * (sl + 1) / 4;
+    float acc = 0.f;
+    if (e < part) {
+        for (int64_t t0 = a; t0 < z; t0 += kParamBatch) {
+            float v[kParamBatch];
+#pragma unroll
+            for (int j = 0; j < kParamBatch; ++j) {
+                const int64_t t = t0 + j < z ? t0 + j : z - 1;
+                const int64_t q = t / n_seg;
+                v[j] = gp[((q * H + h) * n_seg + (t - q * n_seg)) * part + e];
+            }
+#pragma unroll
+            for (int j = 0; j < kParamBatch; ++j)
+                if (t0 + j < z) acc += v[j];
+        }
+    }
+    s_acc[sl][l] = acc;
+    __syncthreads();
+    if (sl == 0 && e < part) gs[(int64_t)h * part + e] = ((s_acc[0][l] + s_acc[1][l]) + s_acc[2][l]) + s_acc[3][l];
+}
+
+__global__ void __launch_bounds__(256) bwd_param_kernel(const float* gs, const float* mu, const float* raw_var,
+                                                        float* dmu, float* draw_var, int H, int K, int d_r, int dxa) {
     const int per = (K * d_r + 255) / 256;   // workgroups per head
     const int h = blockIdx.x / per;
     const int e = (blockIdx.x % per) * 256 + threadIdx.x;
     if (e >= K * d_r) return;
     const int k = e / d_r, d = e % d_r;
-    const int64_t part = (int64_t)K * dxa;
-    // partial t = (side * B + b) * n_seg + sg, summed in that order; loads batched kParamBatch at a time
-    const int64_t nt = 2 * B * n_seg;
-    float g0 = 0.f, g1 = 0.f, g2 = 0.f;
-    for (int64_t t0 = 0; t0 < nt; t0 += kParamBatch) {
-        float a0[kParamBatch], a1[kParamBatch], a2[kParamBatch];
-#pragma unroll
-        for (int j = 0; j < kParamBatch; ++j) {
-            const int64_t t = t0 + j < nt ? t0 + j : nt - 1;
-            const int64_t q = t / n_seg;
-            const float* p = gp + ((q * H + h) * n_seg + (t - q * n_seg)) * part + (int64_t)k * dxa;
-            a1[j] = p[d];
-            a2[j] = p[d_r + d];
-            a0[j] = p[2 * d_r];
-        }
-#pragma unroll
-        for (int j = 0; j < kParamBatch; ++j)
-            if (t0 + j < nt) {
-                g1 += a1[j];
-                g2 += a2[j];
-                g0 += a0[j];
-            }
-    }
+    const float* p = gs + ((int64_t)h * K + k) * dxa;
+    const float g1 = p[d], g2 = p[d_r + d], g0 = p[2 * d_r];
     const int64_t pe = (int64_t)h * K * d_r + e;
     const float m = mu[pe], rv = raw_var[pe];
     const float s = fmaxf(rv, 0.f) + log1pf(expf(-fabsf(rv)));
@@ -3053,29 +3063,14 @@ __global__ void __launch_bounds__(256) bwd_param_kernel(const float* gp, const f
     draw_var[pe] = ds / (1.f + expf(-rv));
 }
 
-// dlog pi_k = G0_k summed like above; dprior_logits_k = G0_k - pi_k sum_j G0_j
-__global__ void __launch_bounds__(256) bwd_prior_kernel(const float* gp, const float* prior, float* dprior, int64_t B,
-                                                        int H, int K, int d_r, int dxa, int64_t n_seg) {
+// dlog pi_k = G0_k; dprior_logits_k = G0_k - pi_k sum_j G0_j
+__global__ void __launch_bounds__(256) bwd_prior_kernel(const float* gs, const float* prior, float* dprior, int H,
+                                                        int K, int d_r, int dxa) {
     const int h = blockIdx.x, tid = threadIdx.x;
     __shared__ float s_g[256];
     __shared__ float s_p[256];
-    const int64_t part = (int64_t)K * dxa;
     if (tid < K) {
-        const int64_t nt = 2 * B * n_seg;
-        float g0 = 0.f;
-        for (int64_t t0 = 0; t0 < nt; t0 += kParamBatch) {
-            float a0[kParamBatch];
-#pragma unroll
-            for (int j = 0; j < kParamBatch; ++j) {
-                const int64_t t = t0 + j < nt ? t0 + j : nt - 1;
-                const int64_t q = t / n_seg;
-                a0[j] = gp[((q * H + h) * n_seg + (t - q * n_seg)) * part + (int64_t)tid * dxa + 2 * d_r];
-            }
-#pragma unroll
-            for (int j = 0; j < kParamBatch; ++j)
-                if (t0 + j < nt) g0 += a0[j];
-        }
-        s_g[tid] = g0;
+        s_g[tid] = gs[((int64_t)h * K + tid) * dxa + 2 * d_r];
         s_p[tid] = prior[(int64_t)h * K + tid];
     }
     __syncthreads();
@@ -3377,12 +3372,14 @@ void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mod
     bwd_scan_kernel<<<dim3((unsigned)((rec / 4 + 63) / 64 * n_outer)), dim3(64), 0, s>>>(st, n, rec, mode);
 }
 
-void launch_bwd_param(const float* gp, const float* mu, const float* raw_var, const float* prior, float* dmu,
-                      float* draw_var, float* dprior, int64_t B, int H, int K, int d_r, int dxa, int64_t n_seg,
-                      hipStream_t s) {
-    bwd_param_kernel<<<dim3((unsigned)((K * d_r + 255) / 256 * H)), dim3(256), 0, s>>>(
-        gp, mu, raw_var, dmu, draw_var, B, H, K, d_r, dxa, n_seg);
-    bwd_prior_kernel<<<dim3((unsigned)H), dim3(256), 0, s>>>(gp, prior, dprior, B, H, K, d_r, dxa, n_seg);
+void launch_bwd_param(const float* gp, float* gs, const float* mu, const float* raw_var, const float* prior,
+                      float* dmu, float* draw_var, float* dprior, int64_t B, int H, int K, int d_r, int dxa,
+                      int64_t n_seg, hipStream_t s) {
+    const int64_t part = (int64_t)K * dxa;
+    bwd_param_sum_kernel<<<dim3((unsigned)((part + 63) / 64 * H)), dim3(256), 0, s>>>(gp, gs, B, H, part, n_seg);
+    bwd_param_kernel<<<dim3((unsigned)((K * d_r + 255) / 256 * H)), dim3(256), 0, s>>>(gs, mu, raw_var, dmu, draw_var,
+                                                                                   H, K, d_r, dxa);
+    bwd_prior_kernel<<<dim3((unsigned)H), dim3(256), 0, s>>>(gs, prior, dprior, H, K, d_r, dxa);
 }
 
 }  // namespace gma

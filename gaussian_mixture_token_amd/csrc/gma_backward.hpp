@@ -159,9 +159,9 @@ bool launch_bwd_bidir_k(const float* gk, const void* v, const float* r_seg, floa
 // 16-byte aligned.
 void launch_bwd_scan(float* st, int64_t n_outer, int64_t n, int64_t rec, int mode, hipStream_t s);
 // Mixture-parameter gradients from the partial sums gp [parts][K][dxa] (parts = 2 sides x B x
-// n_seg per head; columns x | x^2 | 1 of dl^T [x | x^2 | 1]).
-void launch_bwd_param(const float* gp, const float* mu, const float* raw_var, const float* prior, float* dmu,
-                      float* draw_var, float* dprior, int64_t B, int H, int K, int d_r, int dxa, int64_t n_seg,
-                      hipStream_t s);
+// n_seg per head; columns x | x^2 | 1 of dl^T [x | x^2 | 1]), first summed per head into gs [H][K][dxa].
+void launch_bwd_param(const float* gp, float* gs, const float* mu, const float* raw_var, const float* prior,
+                      float* dmu, float* draw_var, float* dprior, int64_t B, int H, int K, int d_r, int dxa,
+                      int64_t n_seg, hipStream_t s);
 
 }  // namespace gma

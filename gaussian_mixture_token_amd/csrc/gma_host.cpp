@@ -368,7 +368,7 @@ struct BwdPlan {
     int64_t n_st = 0, n_sg = 0;  // state entries and parameter segments per (batch, head)
     size_t off_bf = 0, off_cq = 0, off_mw = 0, off_gq = 0, off_gk = 0, off_dgq = 0, off_dgk = 0, off_gh = 0,
            off_pp = 0, off_st = 0, off_rt = 0, off_ac = 0, off_mt = 0, off_dvt = 0, off_gp = 0, off_sgs = 0,
-           off_vs = 0, off_ds = 0, off_dvs = 0, total = 0;
+           off_vs = 0, off_ds = 0, off_dvs = 0, off_gs = 0, total = 0;
     int sper = 1;   // causal: chunks per state segment (bwd_state_segment)
     // causal bf16 at K = d_v = 128: the fused chunk kernels, whose plan has no [num | den], no per-chunk
     // 64 x 64 blocks and no fp32 dV; the suffix states share the bytes of the prefix states (the query side
@@ -402,7 +402,7 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
     const int64_t widest = std::max<int64_t>(std::max<int64_t>(b->K, b->dva), std::max<int64_t>(2 * b->d_r, b->dxa));
     if (b->BH * std::max(b->n_st, b->n_sg) * ((kBwdSeg + 63) / 64) * ((widest + 63) / 64) > INT32_MAX ||
         rows / 4 + 1 > INT32_MAX || b->BH * ((rec + 255) / 256) > INT32_MAX ||
-        b->H * (((int64_t)b->K * b->d_r + 255) / 256) > INT32_MAX)
+        b->H * (((int64_t)b->K * b->d_r + 255) / 256) > INT32_MAX || b->H * (((int64_t)b->K * b->dxa + 63) / 64) > INT32_MAX)
         return fail(GMA_ERROR_NOT_SUPPORTED, "problem too large for the backward grids");
     const int64_t C = b->st_step;
     size_t off = 0;
@@ -433,6 +433,7 @@ gma_status_t make_bwd_plan(const gma_problem_t* p, bool causal, BwdPlan* b) {
     take(&b->off_dvs, b->fq ? stage : 0);
     take(&b->off_gp, std::max<int64_t>(2 * b->BH * b->n_sg * b->K * b->dxa, b->fq ? stage : 0));
     b->off_ds = b->off_gp;
+    take(&b->off_gs, b->H * b->K * b->dxa);   // the partials summed per head
     // causal: the state segments' totals, then their exclusive prefixes
     b->sper = causal ? bwd_state_segment(b->BH, b->n_st) : 1;
     take(&b->off_sgs, causal ? b->BH * ((b->n_st + b->sper - 1) / b->sper) * rec : 0);
@@ -1210,7 +1211,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     float *mw = F(b.off_mw), *gq = F(b.off_gq), *gk = F(b.off_gk), *dgq = F(b.off_dgq),
           *dgk = F(b.off_dgk), *rs = F(b.off_gh), *pp = F(b.off_pp), *stt = F(b.off_st),
           *rt = F(b.off_rt), *ac = F(b.off_ac), *mt = F(b.off_mt), *dvt = F(b.off_dvt),
-          *gp = F(b.off_gp);
+          *gp = F(b.off_gp), *gs = F(b.off_gs);
     const int64_t BH = b.BH, N = b.N, rows = BH * N, rec = (int64_t)b.K * b.dva;
     const int K = b.K, d_r = b.d_r, d_v = b.d_v, dva = b.dva, dxa = b.dxa, H = (int)b.H;
     const int C = b.st_step;
@@ -1432,7 +1433,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
             if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused backward row kernel for this shape");
         }
         return timed_launch(K_BWD_PARAM, s, [&] {
-            launch_bwd_param(gp, mu, rv, pr, dmu, drv, dpr, b.B, H, K, d_r, dxa, fn, s);
+            launch_bwd_param(gp, gs, mu, rv, pr, dmu, drv, dpr, b.B, H, K, d_r, dxa, fn, s);
         });
     }
     GMA_TRY(timed_launch(K_BWD_ROWS, s, [&] { launch_bwd_dl(gq, dgq, rows, K, s); }));
@@ -1453,7 +1454,7 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     }
 #undef GMA_TRY
     return timed_launch(K_BWD_PARAM, s, [&] {
-        launch_bwd_param(gp, mu, rv, pr, dmu, drv, dpr, b.B, H, K, d_r, dxa, b.n_sg, s);
+        launch_bwd_param(gp, gs, mu, rv, pr, dmu, drv, dpr, b.B, H, K, d_r, dxa, b.n_sg, s);
     });
 }
 
