@@ -1132,7 +1132,7 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
 // the sums of dl over tokens (the ones column) in fp32 on the vector units.  Workgroup: four wavefronts
 // over one (batch, head) and a segment of `seg` tokens, in chunks of 64; wave w loads rows 16 w .. 16 w +
 // 15 of each chunk into registers (lane (r, g): row r, components 32 ks + 8 g .. + 7 of gamma and dgamma,
-// dims 16 j + 4 g .. + 3 of x), the next chunk's while the current one is in the products.  dl stays in
+// dims 16 j + 4 g .. + 3 of x), the next chunk's as soon as the current one's dl is formed.  dl stays in
 // registers as the B fragments of dx (split bf16 hi + lo, formed transposed: lane (r, g) then holds dx of
 // row r, dims 16 j + 4 g .. + 3); for P the chunk's dl and x go to LDS component- and dim-major (rows of
 // 64 tokens padded to 144 bytes, so a fragment's 16 rows fall in disjoint banks) and each wave takes a
@@ -1252,6 +1252,7 @@ __global__ void __launch_bounds__(256) bwd_rows_small_kernel(const float* gamma,
         u32x2 xcur[NDT];
 #pragma unroll
         for (int j = 0; j < NDT; ++j) xcur[j] = xa[j];
+        if (c + 1 < nch) load(n0 + C);
         // every wave is done with the previous chunk's images
         lds_barrier();
         {
@@ -1274,7 +1275,6 @@ __global__ void __launch_bounds__(256) bwd_rows_small_kernel(const float* gamma,
                 }
         }
         lds_barrier();   // the chunk's images are complete
-        if (c + 1 < nch) load(n0 + C);
         // P += dl^T [x | x^2] for this wave's pairs over the chunk's 64 tokens
 #pragma unroll
         for (int q = 0; q < UPW; ++q) {
