@@ -79,7 +79,7 @@ def test_backward_matches_oracle(gma, cfg, N, causal, soft):
     check(w, inp, dout, causal, run_gpu(gma, w, inp, dout, causal))
 
 
-@pytest.mark.parametrize("base", [0, 3])
+@pytest.mark.parametrize("base", [0, 2, 3])
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 1023, 1024, 1025])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_tails_and_tiny_lengths(gma, base, N, causal):
@@ -225,3 +225,42 @@ def test_backward_fused_shape_with_misaligned_rows(gma, which):
     for name in NAMES:
         assert torch.equal(got[name], ref[name]), name
     check(w, inp, dout, True, got)
+
+
+def _offset(t, nbytes):
+    # the same values at an address nbytes past a 16-byte boundary
+    el = t.element_size()
+    buf = torch.empty(t.numel() + 16, dtype=t.dtype, device=t.device)
+    out = buf[nbytes // el:nbytes // el + t.numel()].view(t.shape)
+    out.copy_(t)
+    assert out.data_ptr() % 16 == nbytes
+    return out
+
+
+@pytest.mark.parametrize("nbytes", [8, 2])
+@pytest.mark.parametrize("which", ["v", "dout", "dv", "x", "all"])
+def test_backward_bidir_small_class_alignment(gma, nbytes, which):
+    # bidirectional bf16 at K = 32, d_v = 64: rows of v, dout or dv 8 bytes past a 16-byte boundary still
+    # take the fused bidirectional kernels (8-byte pieces) and give the aligned call's results bit for bit;
+    # 2 bytes past one, or routing inputs off 16 bytes, take the general kernels, held to the oracle
+    w = gma.workload(2).with_(batch=1, heads=2, seq_len=1500)
+    inp, dout = inputs(gma, w, True)
+    t = {k: x.to(DEV) for k, x in inp.items()}
+    d = dout.to(DEV)
+    say("backward bidir alignment which=%s offset=%d" % (which, nbytes))
+    ref = gma.backward(t["qx"], t["kx"], t["v"], t["mu"], t["raw_var"], t["prior_logits"], d, eps=w.eps,
+                       causal=False)
+    vv = _offset(t["v"], nbytes) if which in ("v", "all") else t["v"]
+    dd = _offset(d, nbytes) if which in ("dout", "all") else d
+    qx = _offset(t["qx"], nbytes) if which in ("x", "all") else t["qx"]
+    kx = _offset(t["kx"], nbytes) if which in ("x", "all") else t["kx"]
+    grads = {k: torch.empty_like(x) for k, x in ref.items()}
+    if which in ("dv", "all"):
+        grads["dv"] = _offset(torch.zeros_like(t["v"]), nbytes)
+    got = gma.backward(qx, kx, vv, t["mu"], t["raw_var"], t["prior_logits"], dd, eps=w.eps, causal=False,
+                       grads=grads)
+    torch.cuda.synchronize()
+    if nbytes == 8 and which != "x" and which != "all":
+        for name in NAMES:
+            assert torch.equal(got[name], ref[name]), name
+    check(w, inp, dout, False, got)
