@@ -1138,7 +1138,8 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
 // 64 tokens padded to 144 bytes, so a fragment's 16 rows fall in disjoint banks) and each wave takes a
 // quarter of the (component tile, dim tile) pairs over all 64 tokens.  The head's mu / s and 1 / s sit in
 // LDS as split bf16 images for the whole segment.  Waits are placed by the compiler (plain loads).
-template <int KC, int DRC>
+// DL_IN: `dgamma` already holds dl and `gamma` is not read.
+template <int KC, int DRC, bool DL_IN>
 __global__ void __launch_bounds__(256) bwd_rows_small_kernel(const float* gamma, const float* dgamma, const void* x,
                                                              const float* mw, void* dx, float* gp, int64_t N, int H,
                                                              int K, int d_r, int seg, int64_t n_seg, int dxa) {
@@ -1203,7 +1204,8 @@ __global__ void __launch_bounds__(256) bwd_rows_small_kernel(const float* gamma,
             for (int hf = 0; hf < 2; ++hf) {
                 const int k = 32 * ks + 8 * g + 4 * hf;
                 const uint32_t off = k < K ? (t * K + k) * 4 : kOut;
-                ga[ks][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, off, 0, 0));
+                if constexpr (!DL_IN)
+                    ga[ks][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, off, 0, 0));
                 da[ks][hf] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_d, off, 0, 0));
             }
 #pragma unroll
@@ -1229,21 +1231,24 @@ __global__ void __launch_bounds__(256) bwd_rows_small_kernel(const float* gamma,
         bf16x8 bh8[NKS], bl8[NKS];
         {
             float dot = 0.f;
+            if constexpr (!DL_IN) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
+                for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
+                    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) dot += ga[ks][hf][e] * da[ks][hf][e];
-            dot += __shfl_xor(dot, 16, 64);
-            dot += __shfl_xor(dot, 32, 64);
+                        for (int e = 0; e < 4; ++e) dot += ga[ks][hf][e] * da[ks][hf][e];
+                dot += __shfl_xor(dot, 16, 64);
+                dot += __shfl_xor(dot, 32, 64);
+            }
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 float v[8];
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[4 * hf + e] = ga[ks][hf][e] * (da[ks][hf][e] - dot);
+                    for (int e = 0; e < 4; ++e)
+                        v[4 * hf + e] = DL_IN ? da[ks][hf][e] : ga[ks][hf][e] * (da[ks][hf][e] - dot);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) s1[ks][e] += v[e];
                 split_bf16x8(v, bh8[ks], bl8[ks]);
@@ -1378,6 +1383,10 @@ namespace {
 
 constexpr int kImgRow = 2 * 64 + 16;   // a 64-token bf16 image row plus padding (bytes)
 
+// Element e of a lane's permuted 8-element group in step ks: 32 ks + 4 g + e for e < 4, then
+// 32 ks + 16 + 4 g + e - 4 (the order of an accumulator tile pair's rows 16 ct + 4 g + i, ct = 2 ks, 2 ks + 1).
+__device__ __forceinline__ int perm_comp(int ks, int g, int e) { return 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3); }
+
 // Permuted 8-element fragment of an LDS row of bf16 values: elements 32 vs + 4 g .. + 3 and
 // 32 vs + 16 + 4 g .. + 3.
 __device__ __forceinline__ bf16x8 row_perm(const lds_char* row, int vs, int g) {
@@ -1408,7 +1417,7 @@ __device__ __forceinline__ void stage_record(const float* rec, int K, int d_v, i
 // The record of a segment: the (component tile, dim tile) pairs of the wave (lane: components
 // 16 ct + 4 g + i, dim 16 dt + r), the last column from each lane's per-row sums `z` (components
 // 32 ks + 8 g + e) reduced over the rows and the waves in order, zeros after it.
-template <int KC, int VC, int UPW, int NKS>
+template <int KC, int VC, int UPW, int NKS, bool PERM = false>
 __device__ __forceinline__ void write_record(float* out, const f32x4 (&acc)[UPW], const float (&z)[NKS][8],
                                              float (*s_z)[KC], int K, int d_v, int dva) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
@@ -1429,7 +1438,7 @@ __device__ __forceinline__ void write_record(float* out, const f32x4 (&acc)[UPW]
             float v = z[ks][e];
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-            if (r == 0) s_z[w][32 * ks + 8 * g + e] = v;
+            if (r == 0) s_z[w][PERM ? perm_comp(ks, g, e) : 32 * ks + 8 * g + e] = v;
         }
     __syncthreads();
     const int pad = dva - d_v;
@@ -1547,9 +1556,11 @@ __global__ void __launch_bounds__(256) bwd_bidir_state_kernel(const float* gk, c
     write_record<KC, VC, UPW, NKS>(st + (bh * n_seg + sg) * (int64_t)K * dva, acc, z, s_z, K, d_v, dva);
 }
 
-// Query side: dGamma_Q [BH][N][K] and the segments' R records r_seg [BH][n_seg][K][dva], from the summed
-// state (entry 0 of st [BH][n_seg][K][dva]).
-template <int KC, int VC>
+// Query side: dGamma_Q [BH][N][K] (EMIT_DL: dl = Gamma_Q (dGamma_Q - Gamma_Q . dGamma_Q) in its place) and
+// the segments' R records r_seg [BH][n_seg][K][dva], from the summed state (entry 0 of st [BH][n_seg][K][dva]).
+// Gamma_Q is loaded in the permuted component order (perm_comp), which is the order of dGamma_Q's
+// accumulator rows, so that dl is formed in registers.
+template <int KC, int VC, bool EMIT_DL>
 __global__ void __launch_bounds__(256) bwd_bidir_q_kernel(const float* gq, const void* dout, const float* st,
                                                           float* dgq, float* r_seg, int64_t N, int K, int d_v,
                                                           int dva, int seg, int64_t n_seg, float eps) {
@@ -1592,7 +1603,7 @@ __global__ void __launch_bounds__(256) bwd_bidir_q_kernel(const float* gq, const
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const int k = 32 * ks + 8 * g + 4 * hf;
+                const int k = 32 * ks + 16 * hf + 4 * g;
                 ga[ks][hf] = __builtin_bit_cast(
                     f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, k < K ? (t * K + k) * 4 : kOut, 0, 0));
             }
@@ -1635,7 +1646,7 @@ __global__ void __launch_bounds__(256) bwd_bidir_q_kernel(const float* gq, const
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) den += gv[ks][e] * s_zt[32 * ks + 8 * g + e];
+            for (int e = 0; e < 8; ++e) den += gv[ks][e] * s_zt[perm_comp(ks, g, e)];
             split_bf16x8(gv[ks], gh8[ks], gl8[ks]);
         }
         den += __shfl_xor(den, 16, 64);
@@ -1647,9 +1658,8 @@ __global__ void __launch_bounds__(256) bwd_bidir_q_kernel(const float* gq, const
             f32x4 nm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const int off = (32 * ks + 8 * g) * 2;
-                const bf16x8 ah = lds_ld<bf16x8>(SDH + (16 * j + r) * WD + off);
-                const bf16x8 al = lds_ld<bf16x8>(SDL + (16 * j + r) * WD + off);
+                const bf16x8 ah = row_perm(SDH + (16 * j + r) * WD, ks, g);
+                const bf16x8 al = row_perm(SDL + (16 * j + r) * WD, ks, g);
                 mma(nm, ah, gl8[ks]);
                 mma(nm, al, gh8[ks]);
                 mma(nm, ah, gh8[ks]);
@@ -1672,7 +1682,9 @@ __global__ void __launch_bounds__(256) bwd_bidir_q_kernel(const float* gq, const
             }
             split_bf16x8(gg, xh8[vs], xl8[vs]);
         }
-        // dGamma_Q of this lane's row, components 16 ct + 4 g .. + 3
+        // dGamma_Q of this lane's row, components 16 ct + 4 g .. + 3 (ct = 2 ks + e / 4: the lane's own order)
+        f32x4 dgo[NCT];
+        float dot2 = 0.f;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4 dg = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1685,9 +1697,24 @@ __global__ void __launch_bounds__(256) bwd_bidir_q_kernel(const float* gq, const
                 mma(dg, ah, xh8[vs]);
             }
             const int k = 16 * ct + 4 * g;
-            f32x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = dg[i] + hv * s_zt[k + i];
+            for (int i = 0; i < 4; ++i) {
+                dgo[ct][i] = dg[i] + hv * s_zt[k + i];
+                dot2 += gv[ct >> 1][4 * (ct & 1) + i] * dgo[ct][i];
+            }
+        }
+        if constexpr (EMIT_DL) {
+            dot2 += __shfl_xor(dot2, 16, 64);
+            dot2 += __shfl_xor(dot2, 32, 64);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int k = 16 * ct + 4 * g;
+            f32x4 o = dgo[ct];
+            if constexpr (EMIT_DL) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = gv[ct >> 1][4 * (ct & 1) + i] * (dgo[ct][i] - dot2);
+            }
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_o, k < K ? (t * K + k) * 4 : kOut,
                                                    0, 0);
         }
@@ -1704,7 +1731,7 @@ __global__ void __launch_bounds__(256) bwd_bidir_q_kernel(const float* gq, const
             for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int k = 32 * ks + 8 * g + e;
+                    const int k = perm_comp(ks, g, e);
                     lds_st<__bf16>(LGH + k * IS + 2 * tt, gh8[ks][e]);
                     lds_st<__bf16>(LGL + k * IS + 2 * tt, gl8[ks][e]);
                 }
@@ -1734,12 +1761,12 @@ __global__ void __launch_bounds__(256) bwd_bidir_q_kernel(const float* gq, const
             }
         }
     }
-    write_record<KC, VC, UPW, NKS>(r_seg + (bh * n_seg + sg) * (int64_t)K * dva, acc, z, s_z, K, d_v, dva);
+    write_record<KC, VC, UPW, NKS, true>(r_seg + (bh * n_seg + sg) * (int64_t)K * dva, acc, z, s_z, K, d_v, dva);
 }
 
-// Key side: dGamma_K [BH][N][K] fp32 and dV [BH][N][d_v] bf16 from the summed R (entry 0 of
-// r_seg [BH][n_seg][K][dva]).
-template <int KC, int VC>
+// Key side: dGamma_K [BH][N][K] fp32 (EMIT_DL: dl in its place, as on the query side) and dV [BH][N][d_v]
+// bf16 from the summed R (entry 0 of r_seg [BH][n_seg][K][dva]); Gamma_K in the permuted component order.
+template <int KC, int VC, bool EMIT_DL>
 __global__ void __launch_bounds__(256) bwd_bidir_k_kernel(const float* gk, const void* v, const float* r_seg,
                                                           float* dgk, void* dv, int64_t N, int K, int d_v, int dva,
                                                           int seg, int64_t n_seg) {
@@ -1776,7 +1803,7 @@ __global__ void __launch_bounds__(256) bwd_bidir_k_kernel(const float* gk, const
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const int k = 32 * ks + 8 * g + 4 * hf;
+                const int k = 32 * ks + 16 * hf + 4 * g;
                 ga[ks][hf] = __builtin_bit_cast(
                     f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, k < K ? (t * K + k) * 4 : kOut, 0, 0));
             }
@@ -1793,19 +1820,21 @@ __global__ void __launch_bounds__(256) bwd_bidir_k_kernel(const float* gk, const
         const int64_t n0 = t0 + (int64_t)c * C;
         const uint32_t t = (uint32_t)(n0 + 16 * w + r);
         bf16x8 gh8[NKS], gl8[NKS];
+        float gv[NKS][8];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            float gv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) gv[e] = ga[ks][e >> 2][e & 3];
-            split_bf16x8(gv, gh8[ks], gl8[ks]);
+            for (int e = 0; e < 8; ++e) gv[ks][e] = ga[ks][e >> 2][e & 3];
+            split_bf16x8(gv[ks], gh8[ks], gl8[ks]);
         }
         bf16x8 vf[NVS];
 #pragma unroll
         for (int vs = 0; vs < NVS; ++vs)
             vf[vs] = __builtin_bit_cast(bf16x8, u32x4{va[2 * vs][0], va[2 * vs][1], va[2 * vs + 1][0], va[2 * vs + 1][1]});
         if (c + 1 < nch) load(n0 + C);
-        // dGamma_K of this lane's row, components 16 ct + 4 g .. + 3
+        // dGamma_K of this lane's row, components 16 ct + 4 g .. + 3 (the lane's own order)
+        f32x4 dgo[NCT];
+        float dot2 = 0.f;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4 dg = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1815,9 +1844,24 @@ __global__ void __launch_bounds__(256) bwd_bidir_k_kernel(const float* gk, const
                 mma(dg, row_perm(RCH + (16 * ct + r) * WC, vs, g), vf[vs]);
             }
             const int k = 16 * ct + 4 * g;
-            f32x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = dg[i] + s_r1[k + i];
+            for (int i = 0; i < 4; ++i) {
+                dgo[ct][i] = dg[i] + s_r1[k + i];
+                dot2 += gv[ct >> 1][4 * (ct & 1) + i] * dgo[ct][i];
+            }
+        }
+        if constexpr (EMIT_DL) {
+            dot2 += __shfl_xor(dot2, 16, 64);
+            dot2 += __shfl_xor(dot2, 32, 64);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int k = 16 * ct + 4 * g;
+            f32x4 o = dgo[ct];
+            if constexpr (EMIT_DL) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = gv[ct >> 1][4 * (ct & 1) + i] * (dgo[ct][i] - dot2);
+            }
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rs_o, k < K ? (t * K + k) * 4 : kOut,
                                                    0, 0);
         }
@@ -1827,9 +1871,8 @@ __global__ void __launch_bounds__(256) bwd_bidir_k_kernel(const float* gk, const
             f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const int off = (32 * ks + 8 * g) * 2;
-                const bf16x8 ah = lds_ld<bf16x8>(RDH + (16 * j + r) * WD + off);
-                const bf16x8 al = lds_ld<bf16x8>(RDL + (16 * j + r) * WD + off);
+                const bf16x8 ah = row_perm(RDH + (16 * j + r) * WD, ks, g);
+                const bf16x8 al = row_perm(RDL + (16 * j + r) * WD, ks, g);
                 mma(o, ah, gl8[ks]);
                 mma(o, al, gh8[ks]);
                 mma(o, ah, gh8[ks]);
@@ -3233,6 +3276,20 @@ bool launch_bwd_chunk_q(const float* gq, const float* gk, const void* v, const v
 }
 
 namespace {
+// Calls f(KC, DC) with the padded class of (K, d), d = d_v or d_r, as integral constants.
+template <class F>
+void bidir_class(int K, int d_v, F&& f) {
+    using I32 = std::integral_constant<int, 32>;
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    if (K <= 32 && d_v <= 64) f(I32{}, I64{});
+    else if (K <= 32) f(I32{}, I128{});
+    else if (d_v <= 64) f(I64{}, I64{});
+    else f(I64{}, I128{});
+}
+}  // namespace
+
+namespace {
 bool fused_rows_small(int K, int d_r) { return K <= 64 && d_r <= 128 && K % 4 == 0 && d_r % 4 == 0; }
 }  // namespace
 
@@ -3292,19 +3349,16 @@ bool launch_bwd_fused_rows(const float* gamma, const float* dgamma, const void* 
     const int64_t n_seg = (N + seg - 1) / seg;
     const dim3 grid((unsigned)(BH * n_seg));
     if (!(K == 128 && d_r == 128)) {
-        if (dl_in) return false;
-        if (K <= 32 && d_r <= 64)
-            bwd_rows_small_kernel<32, 64><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K, d_r, seg,
-                                                                      n_seg, dxa);
-        else if (K <= 32)
-            bwd_rows_small_kernel<32, 128><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K, d_r, seg,
-                                                                       n_seg, dxa);
-        else if (d_r <= 64)
-            bwd_rows_small_kernel<64, 64><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K, d_r, seg,
-                                                                      n_seg, dxa);
-        else
-            bwd_rows_small_kernel<64, 128><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K, d_r, seg,
-                                                                       n_seg, dxa);
+        // the small classes: (K, d_r) padded as the bidirectional kernels pad (K, d_v)
+        bidir_class(K, d_r, [&](auto kc, auto dc) {
+            constexpr int KC = decltype(kc)::value, DRC = decltype(dc)::value;
+            if (dl_in)
+                bwd_rows_small_kernel<KC, DRC, true><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K,
+                                                                               d_r, seg, n_seg, dxa);
+            else
+                bwd_rows_small_kernel<KC, DRC, false><<<grid, dim3(256), 0, s>>>(gamma, dgamma, x, mw, dx, gp, N, H, K,
+                                                                                d_r, seg, n_seg, dxa);
+        });
         return true;
     }
     if (dl_in)
@@ -3320,19 +3374,6 @@ bool bwd_bidir_small_supported(int K, int d_v, bool f32) {
     return !f32 && K <= 64 && d_v <= 128 && K % 4 == 0 && d_v % 4 == 0;
 }
 
-namespace {
-// Calls f(KC, VC) with the padded class of (K, d_v) as integral constants.
-template <class F>
-void bidir_class(int K, int d_v, F&& f) {
-    using I32 = std::integral_constant<int, 32>;
-    using I64 = std::integral_constant<int, 64>;
-    using I128 = std::integral_constant<int, 128>;
-    if (K <= 32 && d_v <= 64) f(I32{}, I64{});
-    else if (K <= 32) f(I32{}, I128{});
-    else if (d_v <= 64) f(I64{}, I64{});
-    else f(I64{}, I128{});
-}
-}  // namespace
 
 bool launch_bwd_bidir_state(const float* gk, const void* v, float* st, int64_t BH, int64_t N, int K, int d_v, int dva,
                             int seg, hipStream_t s) {
@@ -3346,24 +3387,34 @@ bool launch_bwd_bidir_state(const float* gk, const void* v, float* st, int64_t B
 }
 
 bool launch_bwd_bidir_q(const float* gq, const void* dout, const float* st, float* dgq, float* r_seg, int64_t BH,
-                        int64_t N, int K, int d_v, int dva, int seg, float eps, hipStream_t s) {
+                        int64_t N, int K, int d_v, int dva, int seg, float eps, bool emit_dl, hipStream_t s) {
     if (!bwd_bidir_small_supported(K, d_v, false) || dva != d_v + 4 || seg % kFusedChunk != 0) return false;
     const int64_t n_seg = (N + seg - 1) / seg;
+    const dim3 grid((unsigned)(BH * n_seg));
     bidir_class(K, d_v, [&](auto kc, auto vc) {
-        bwd_bidir_q_kernel<decltype(kc)::value, decltype(vc)::value>
-            <<<dim3((unsigned)(BH * n_seg)), dim3(256), 0, s>>>(gq, dout, st, dgq, r_seg, N, K, d_v, dva, seg, n_seg,
-                                                               eps);
+        constexpr int KC = decltype(kc)::value, VC = decltype(vc)::value;
+        if (emit_dl)
+            bwd_bidir_q_kernel<KC, VC, true><<<grid, dim3(256), 0, s>>>(gq, dout, st, dgq, r_seg, N, K, d_v, dva, seg,
+                                                                       n_seg, eps);
+        else
+            bwd_bidir_q_kernel<KC, VC, false><<<grid, dim3(256), 0, s>>>(gq, dout, st, dgq, r_seg, N, K, d_v, dva, seg,
+                                                                        n_seg, eps);
     });
     return true;
 }
 
 bool launch_bwd_bidir_k(const float* gk, const void* v, const float* r_seg, float* dgk, void* dv, int64_t BH, int64_t N,
-                        int K, int d_v, int dva, int seg, hipStream_t s) {
+                        int K, int d_v, int dva, int seg, bool emit_dl, hipStream_t s) {
     if (!bwd_bidir_small_supported(K, d_v, false) || dva != d_v + 4 || seg % kFusedChunk != 0) return false;
     const int64_t n_seg = (N + seg - 1) / seg;
+    const dim3 grid((unsigned)(BH * n_seg));
     bidir_class(K, d_v, [&](auto kc, auto vc) {
-        bwd_bidir_k_kernel<decltype(kc)::value, decltype(vc)::value>
-            <<<dim3((unsigned)(BH * n_seg)), dim3(256), 0, s>>>(gk, v, r_seg, dgk, dv, N, K, d_v, dva, seg, n_seg);
+        constexpr int KC = decltype(kc)::value, VC = decltype(vc)::value;
+        if (emit_dl)
+            bwd_bidir_k_kernel<KC, VC, true><<<grid, dim3(256), 0, s>>>(gk, v, r_seg, dgk, dv, N, K, d_v, dva, seg, n_seg);
+        else
+            bwd_bidir_k_kernel<KC, VC, false><<<grid, dim3(256), 0, s>>>(gk, v, r_seg, dgk, dv, N, K, d_v, dva, seg,
+                                                                        n_seg);
     });
     return true;
 }

@@ -129,7 +129,7 @@ bool launch_bwd_chunk_k(const float* gq, const float* gk, const void* v, const v
 // partials gp [BH][n_seg][K][dxa] (columns x | x^2 | 1 of dl^T [x | x^2 | 1], rows dxa >= 2 d_r + 1
 // floats apart) over segments of
 // `seg` tokens (n_seg = ceil(N / seg)).  dl itself is not written.  Bases 16-byte aligned,
-// (N + 64) K 4 < 2^31 and N d_r 2 < 2^31.  false: no fused kernel for this shape (dl_in only at K = d_r = 128).
+// (N + 64) K 4 < 2^31 and N d_r 2 < 2^31.  false: no fused kernel for this shape.
 // bwd_fused_rows_seg: the segment length, a power of two in [min_seg, 4096] (min_seg a power of two
 // >= 64, at most 4096), long enough to keep n_seg within the partials buffer sized for min_seg.
 bool bwd_fused_rows_supported(int K, int d_r, bool f32);
@@ -151,9 +151,10 @@ bool bwd_bidir_small_supported(int K, int d_v, bool f32);
 bool launch_bwd_bidir_state(const float* gk, const void* v, float* st, int64_t BH, int64_t N, int K, int d_v, int dva,
                             int seg, hipStream_t s);
 bool launch_bwd_bidir_q(const float* gq, const void* dout, const float* st, float* dgq, float* r_seg, int64_t BH,
-                        int64_t N, int K, int d_v, int dva, int seg, float eps, hipStream_t s);
+                        int64_t N, int K, int d_v, int dva, int seg, float eps, bool emit_dl, hipStream_t s);
 bool launch_bwd_bidir_k(const float* gk, const void* v, const float* r_seg, float* dgk, void* dv, int64_t BH, int64_t N,
-                        int K, int d_v, int dva, int seg, hipStream_t s);
+                        int K, int d_v, int dva, int seg, bool emit_dl, hipStream_t s);
+// emit_dl (q and k): dl = Gamma (dGamma - Gamma . dGamma) of each row in place of dGamma.
 // Chunk-state scans over [n_outer][n][rec]: mode 0 exclusive prefix in place, 1 exclusive suffix in
 // place, 2 the total into entry 0.  rec is a multiple of 4 (K times d_v + 1 rounded up to 4) and st
 // 16-byte aligned.

@@ -1312,6 +1312,8 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
     const bool bq = !causal && bwd_bidir_small_supported(K, d_v, f32) && dva == d_v + 4 && !misaligned(v, 8) &&
                     !misaligned(dout, 8) && !misaligned(dv, 8) && (N + 64) * K * 4 < (int64_t(1) << 31) &&
                     (N + 64) * d_v * 2 < (int64_t(1) << 31);
+    // with the fused row kernel after them they too write dl in place of dGamma
+    const bool bq_dl = bq && fused;
     // the chunk kernels read and write whole 16-byte pieces of bf16 rows: rows that are not 16-byte aligned
     // go through aligned copies in the workspace
     const void* vq = v;
@@ -1354,12 +1356,12 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no bidirectional state kernel for this shape");
         GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(stt, BH, b.n_st, rec, 2, s); }));
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            ok = launch_bwd_bidir_q(gq, dout, stt, dgq, rt, BH, N, K, d_v, dva, C, b.eps, s);
+            ok = launch_bwd_bidir_q(gq, dout, stt, dgq, rt, BH, N, K, d_v, dva, C, b.eps, bq_dl, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no bidirectional query-side kernel for this shape");
         GMA_TRY(timed_launch(K_BWD_SCAN, s, [&] { launch_bwd_scan(rt, BH, b.n_st, rec, 2, s); }));
         GMA_TRY(timed_launch(K_BWD_CHUNK, s, [&] {
-            ok = launch_bwd_bidir_k(gk, v, rt, dgk, dv, BH, N, K, d_v, dva, C, s);
+            ok = launch_bwd_bidir_k(gk, v, rt, dgk, dv, BH, N, K, d_v, dva, C, bq_dl, s);
         }));
         if (!ok) return fail(GMA_ERROR_LAUNCH, "no bidirectional key-side kernel for this shape");
     } else {
@@ -1427,8 +1429,8 @@ gma_status_t backward(const gma_problem_t* p, bool causal, const void* qx, const
             bool ok = true;
             GMA_TRY(timed_launch(K_BWD_FUSED, s, [&] {
                 ok = launch_bwd_fused_rows(side ? gk : gq, side ? dgk : dgq, side ? kx : qx, mw, side ? dkx : dqx,
-                                           gp + (size_t)side * BH * fn * K * dxa, BH, N, H, K, d_r, dxa, fseg, emit_dl,
-                                           s);
+                                           gp + (size_t)side * BH * fn * K * dxa, BH, N, H, K, d_r, dxa, fseg,
+                                           emit_dl || bq_dl, s);
             }));
             if (!ok) return fail(GMA_ERROR_LAUNCH, "no fused backward row kernel for this shape");
         }
