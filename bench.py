@@ -10,7 +10,7 @@ gradient, from a seeded dL/dO); its line carries the whole step against the peak
 cores its products run on (bf16 with split operands for bf16 storage, fp32 for fp32 storage).
 
 The forward line also carries `copy_reference`: the rate a plain 1 GiB device copy sustains on the
-same GPU (and, under `read_only`, the rate of a plain 1 GiB reduction, which only reads), beside the
+same GPU (and, under `read_only`, the rate of the library's plain 1 GiB read probe), beside the
 rate at which the step moves its measured HBM traffic; and `exp2_reference`: the
 measured rate of the hardware exponential and the time the step's 2 K exponentials per token-head
 take at it.
@@ -23,6 +23,7 @@ own bytes (read the rows, write Gamma in fp32).
     python bench.py [--steps K] [--warmup W] [--workload I] [--backward | --decode | --responsibilities] [--no-cpu-baseline]
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -355,7 +356,8 @@ def main():
     read_gbs = read_reference(dev)
     copy_ref = {"kernel": "torch copy_ of 1 GiB fp32 into 1 GiB, 20 back to back", "gbs": copy_gbs,
                 "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
-                "read_only": {"kernel": "torch amax over 1 GiB fp32, 20 back to back", "gbs": read_gbs,
+                "read_only": {"kernel": "gma_probe_read_rate over 1 GiB (plain 16-byte loads), 10 back to back",
+                              "gbs": read_gbs,
                               "frac_of_peak": read_gbs / HBM_PEAK_GBS},
                 "step_traffic_gbs": None if traffic is None else traffic / step_s / 1e9,
                 "step_traffic_over_copy": None if traffic is None else traffic / step_s / 1e9 / copy_gbs}
@@ -416,23 +418,20 @@ def copy_reference(dev, steps: int = 20) -> float:
     return gbs
 
 
-def read_reference(dev, steps: int = 20) -> float:
-    """GB/s of a plain device reduction over 1 GiB (torch's amax: reads only, writes one value), back to
-    back after three untimed runs: the rate a kernel that only reads sustains on this GPU, as context for
-    passes that read far more than they write."""
+def read_reference(dev) -> float:
+    """GB/s of the library's read-rate probe (gma_probe_read_rate: a plain grid-stride kernel of 16-byte
+    loads, ten launches back to back) over 1 GiB: the rate a kernel that only reads sustains on this GPU,
+    as context for passes that read far more than they write."""
     import torch
+    from gaussian_mixture_token_amd import _lib
+    lib = _lib.load()
     x = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    for _ in range(3):
-        x.amax()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        x.amax()
-    e1.record()
     torch.cuda.synchronize()
-    gbs = steps * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    rate = ctypes.c_double(0.0)
+    _lib.check(lib.gma_probe_read_rate(ctypes.c_void_p(x.data_ptr()), ctypes.c_size_t(x.numel() * 4),
+                                       ctypes.byref(rate), None))
     del x
-    return gbs
+    return rate.value / 1e9
 
 
 EXP2_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9   # CUs x SIMDs x lanes at a quarter of the full rate x clock

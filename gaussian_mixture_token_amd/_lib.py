@@ -64,6 +64,8 @@ _SIGS = [
     ("gma_kernel_count", ctypes.c_int, []),
     ("gma_kernel_name", ctypes.c_char_p, [ctypes.c_int]),
     ("gma_probe_exp2_rate", ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]),
+    ("gma_probe_read_rate", ctypes.c_int,
+     [ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]),
 ]
 
 

@@ -292,6 +292,15 @@ const char* gma_kernel_name(int kernel_id);
  * GMA_ERROR_LAUNCH if a HIP call fails (*per_second is then 0). */
 gma_status_t gma_probe_exp2_rate(double* per_second, void* stream);
 
+/* Measurement support: the rate at which the current device reads HBM, in bytes per second, written
+ * to *bytes_per_second.  Reads the first bytes / 16 16-byte pieces of the caller's device buffer `buf`
+ * (16-byte aligned; its contents do not matter and are not changed) with one untimed and ten timed
+ * launches of a plain grid-stride read kernel on `stream` (NULL: the null stream), and waits for them;
+ * allocates no device memory.  Pass a buffer well beyond the 256 MB last-level cache (1 GiB) to measure
+ * HBM.  GMA_ERROR_INVALID_VALUE if bytes_per_second or buf is NULL, bytes < 16 or buf is not 16-byte
+ * aligned; GMA_ERROR_LAUNCH if a HIP call fails (*bytes_per_second is then 0). */
+gma_status_t gma_probe_read_rate(const void* buf, size_t bytes, double* bytes_per_second, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -100,3 +100,27 @@ def test_exp2_rate_probe(gma):
     assert lib.gma_probe_exp2_rate(ctypes.byref(rate), None) == 0
     assert 1e11 < rate.value < 1e15
     assert lib.gma_probe_exp2_rate(None, None) == 1
+
+
+@pytest.mark.gpu
+def test_read_rate_probe(gma):
+    # reads a 256 MiB buffer: a positive rate of the order of the HBM's (bounded loosely), the buffer
+    # unchanged; NULL output, NULL or misaligned buffers and sizes below one piece rejected
+    import ctypes
+    import torch
+    from gaussian_mixture_token_amd import _lib
+    lib = _lib.load()
+    x = torch.arange(1 << 26, dtype=torch.float32, device="cuda:0")
+    y = x.clone()
+    rate = ctypes.c_double()
+    assert lib.gma_probe_read_rate(ctypes.c_void_p(x.data_ptr()), ctypes.c_size_t(x.numel() * 4),
+                                   ctypes.byref(rate), None) == 0
+    torch.cuda.synchronize()
+    assert 1e11 < rate.value < 1e14
+    assert torch.equal(x, y)
+    p = ctypes.c_void_p(x.data_ptr())
+    assert lib.gma_probe_read_rate(p, ctypes.c_size_t(1 << 20), None, None) == 1
+    assert lib.gma_probe_read_rate(None, ctypes.c_size_t(1 << 20), ctypes.byref(rate), None) == 1
+    assert lib.gma_probe_read_rate(ctypes.c_void_p(x.data_ptr() + 4), ctypes.c_size_t(1 << 20), ctypes.byref(rate),
+                                   None) == 1
+    assert lib.gma_probe_read_rate(p, ctypes.c_size_t(8), ctypes.byref(rate), None) == 1
