@@ -1137,8 +1137,9 @@ __global__ void __launch_bounds__(256) bwd_fused_rows_kernel(const float* gamma,
 // row r, dims 16 j + 4 g .. + 3); for P the chunk's dl and x go to LDS component- and dim-major (rows of
 // 64 tokens padded to 144 bytes, so a fragment's 16 rows fall in disjoint banks) and each wave takes a
 // quarter of the (component tile, dim tile) pairs over all 64 tokens.  The head's mu / s and 1 / s sit in
-// LDS as split bf16 images for the whole segment.  Waits are placed by the compiler (plain loads).
-// DL_IN: `dgamma` already holds dl and `gamma` is not read.
+// LDS as split bf16 images for the whole segment.  Loads and stores go through buffer descriptors
+// (rows past N, components past K and dims past d_r read as zero and are not written); their waits are
+// placed by the compiler.  DL_IN: `dgamma` already holds dl and `gamma` is not read.
 template <int KC, int DRC, bool DL_IN>
 __global__ void __launch_bounds__(256) bwd_rows_small_kernel(const float* gamma, const float* dgamma, const void* x,
                                                              const float* mw, void* dx, float* gp, int64_t N, int H,
